@@ -1,0 +1,159 @@
+"""Seeded synthetic inputs for the Mamba-3 SSM layer core.
+
+This module only draws random tensors; it holds none of the method's arithmetic.  Both the GPU
+library's callers and the fp64 oracle take their inputs from here, so both see the same rounded
+values (bf16 draws are rounded once, to nearest-even, and the oracle upcasts them exactly).
+
+The five workloads are the layer-level shapes of the Mamba-3 paper's latency study (1.5B model,
+batch 128, 512-16384 tokens, described on the bud-325 notes page, "Benchmarking Latencies"),
+with no trained weights or activations: every tensor is drawn from the distribution below.
+
+  x, B, C         ~ N(0, 1)
+  dt              = softplus(N(0, 1) - 1)              per (batch, step, head)
+  A               = -exp(U(0, ln 16))                  per head
+  lam             = sigmoid(N(0, 1))                   per (batch, step, head)
+  theta           ~ N(0, s^2), s = 1 (pi for the long-context workload), per rotation pair
+  bias_B, bias_C  ~ N(0, 0.1^2)                        per (head, rank, state index)
+  w_out           ~ N(0, 1) / sqrt(R)                  per (head, rank, head-dim index)
+  decode state    h ~ N(0, 1), phi ~ U(-pi, pi), Bbar_prev, x_prev ~ N(0, 1)
+
+Draw order (fixed, so a seed names one input set): A, bias_B, bias_C, w_out, x, B, C, dt, lam,
+theta, then the decode-state tensors.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int      # P
+    dstate: int       # N
+    rank: int         # R (1 = SISO)
+    chunk: int        # Q
+    io: str           # "f32" or "bf16"
+    bcnorm: bool
+    bias: bool
+    mix: bool         # per-head output mixing over the R ranks
+    theta_std: float = 1.0
+    decode_steps: int = 0
+    note: str = field(default="", compare=False)
+
+    @property
+    def torch_io(self):
+        return torch.float32 if self.io == "f32" else torch.bfloat16
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny_siso_f32": Workload("tiny_siso_f32", 1, 64, 1, 16, 16, 1, 16, "f32", False, False, False,
+                              note="b1 L64 H1 P16 N16 R1 Q16, fp32, rotation on, BCNorm off"),
+    "siso_b8_l2048": Workload("siso_b8_l2048", 8, 2048, 64, 64, 128, 1, 64, "bf16", True, True,
+                              False, note="b8 L2048 H64 P64 N128 R1 Q64, bf16 io, fp32 state"),
+    "mimo4_b8_l2048": Workload("mimo4_b8_l2048", 8, 2048, 64, 64, 128, 4, 16, "bf16", True, True,
+                               True, note="b8 L2048 H64 P64 N128 R4 Q16, bf16 io, mixing on"),
+    "decode_b128_r1": Workload("decode_b128_r1", 128, 1, 64, 64, 128, 1, 1, "bf16", True, True,
+                               False, decode_steps=256, note="b128 H64 P64 N128 R1, 256 steps"),
+    "decode_b128_r4": Workload("decode_b128_r4", 128, 1, 64, 64, 128, 4, 1, "bf16", True, True,
+                               True, decode_steps=256, note="b128 H64 P64 N128 R4, 256 steps"),
+    "long_mimo4_b1_l16384": Workload("long_mimo4_b1_l16384", 1, 16384, 64, 64, 128, 4, 16, "bf16",
+                                     True, True, True, theta_std=math.pi, decode_steps=512,
+                                     note="b1 L16384 H64 R4 Q16, theta std pi, then 512 decode steps"),
+}
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _normal(g, shape, device, std=1.0, mean=0.0):
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std + mean
+
+
+def _uniform(g, shape, device, lo, hi):
+    return torch.rand(shape, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo
+
+
+def make_params(w: Workload, g, device, normw: bool = False) -> dict:
+    """Per-head constants: A [H], bias_B/bias_C [H,R,N], w_out [H,R,P], optional normw [H,N]."""
+    H, R, N, P = w.nheads, w.rank, w.dstate, w.headdim
+    out = {"A": -torch.exp(_uniform(g, (H,), device, 0.0, math.log(16.0)))}
+    out["bias_B"] = _normal(g, (H, R, N), device, 0.1) if w.bias else None
+    out["bias_C"] = _normal(g, (H, R, N), device, 0.1) if w.bias else None
+    out["w_out"] = _normal(g, (H, R, P), device) / math.sqrt(R) if w.mix else None
+    if normw:
+        out["normw_B"] = 1.0 + _normal(g, (H, N), device, 0.1)
+        out["normw_C"] = 1.0 + _normal(g, (H, N), device, 0.1)
+    else:
+        out["normw_B"] = None
+        out["normw_C"] = None
+    return out
+
+
+def make_sequence(w: Workload, g, device, lead: tuple) -> dict:
+    """Per-step tensors with leading dims ``lead`` (e.g. (b, L) for prefill, (steps, b) for decode).
+
+    x [*lead, H, R, P], B, C [*lead, H, R, N], dt, lam [*lead, H], theta [*lead, H, N/2], all in
+    the workload's io dtype.
+    """
+    H, R, N, P = w.nheads, w.rank, w.dstate, w.headdim
+    io = w.torch_io
+    out = {}
+    out["x"] = _normal(g, (*lead, H, R, P), device).to(io)
+    out["B"] = _normal(g, (*lead, H, R, N), device).to(io)
+    out["C"] = _normal(g, (*lead, H, R, N), device).to(io)
+    out["dt"] = torch.nn.functional.softplus(_normal(g, (*lead, H), device) - 1.0).to(io)
+    out["lam"] = torch.sigmoid(_normal(g, (*lead, H), device)).to(io)
+    out["theta"] = _normal(g, (*lead, H, N // 2), device, w.theta_std).to(io)
+    return out
+
+
+def make_decode_state(w: Workload, g, device) -> dict:
+    """Resident decode state: h [b,H,N,P] f32, phi [b,H,N/2] f32, Bbar_prev, x_prev (io)."""
+    b, H, R, N, P = w.batch, w.nheads, w.rank, w.dstate, w.headdim
+    return {
+        "h": _normal(g, (b, H, N, P), device),
+        "phi": _uniform(g, (b, H, N // 2), device, -math.pi, math.pi),
+        "Bbar_prev": _normal(g, (b, H, R, N), device).to(w.torch_io),
+        "x_prev": _normal(g, (b, H, R, P), device).to(w.torch_io),
+    }
+
+
+def make_prefill_inputs(w: Workload, seed: int, device="cpu", normw: bool = False,
+                        carry: bool = False) -> dict:
+    """All inputs of one prefill call of workload ``w``.
+
+    With ``carry`` the call also receives a carried-in state (h_in, phi_in, Bbar_prev, x_prev)
+    drawn like the decode state, as a continuation of an earlier call would.
+    """
+    g = _gen(seed, device)
+    out = make_params(w, g, device, normw=normw)
+    out.update(make_sequence(w, g, device, (w.batch, w.seqlen)))
+    if carry:
+        st = make_decode_state(w, g, device)
+        out["h_in"] = st["h"]
+        out["phi_in"] = st["phi"]
+        out["Bbar_prev"] = st["Bbar_prev"]
+        out["x_prev"] = st["x_prev"]
+    return out
+
+
+def make_decode_inputs(w: Workload, seed: int, steps: int, device="cpu",
+                       normw: bool = False) -> dict:
+    """Constants, a starting state and ``steps`` tokens laid out step-major ([steps, b, H, ...])."""
+    g = _gen(seed, device)
+    out = make_params(w, g, device, normw=normw)
+    out["tokens"] = make_sequence(w, g, device, (steps, w.batch))
+    out["state"] = make_decode_state(w, g, device)
+    return out

@@ -1,0 +1,52 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutant is a copy of the oracle's C source with one plausible mistake (a dropped term, a
+wrong sign, a wrong index or operand), built on the CPU into a temporary library.  The pins in
+``pins.py`` are run against it; the test passes only if some pin rejects the mutant.  This shows
+the pins are sharp enough to catch each kind of mistake, not that the oracle is right (that is
+what ``test_oracle_pins.py`` checks).
+"""
+import pytest
+
+import oracle
+import pins
+
+# (name, text in m3_oracle.c, replacement)
+MUTANTS = [
+    ("beta_without_decay", "const double beta = (1.0 - lm) * d * alpha;",
+     "const double beta = (1.0 - lm) * d;"),
+    ("gamma_uses_one_minus_lambda", "const double gamma = lm * d;",
+     "const double gamma = (1.0 - lm) * d;"),
+    ("alpha_missing_dt", "const double alpha = exp(d * A[h]);", "const double alpha = exp(A[h]);"),
+    ("previous_input_not_kept", "uprev = u;\n            u = tmp;", "(void)tmp;"),
+    ("output_reads_B", "const double *ct = Cbar + (row * R + r) * N;",
+     "const double *ct = Bbar + (row * R + r) * N;"),
+    ("rotation_transposed",
+     "out[2 * k] = c * v[2 * k] + s * v[2 * k + 1];\n                        out[2 * k + 1] = -s * v[2 * k] + c * v[2 * k + 1];",
+     "out[2 * k] = c * v[2 * k] - s * v[2 * k + 1];\n                        out[2 * k + 1] = s * v[2 * k] + c * v[2 * k + 1];"),
+    ("angle_without_dt", "phi[k] += d * theta[row * K + k];", "phi[k] += theta[row * K + k];"),
+    ("angle_skips_current_step",
+     "for (int64_t k = 0; k < K; ++k)\n                phi[k] += d * theta[row * K + k];",
+     "for (int64_t k = 0; k < K && t > 0; ++k)\n                phi[k] += dt[row - H] * theta[(row - H) * K + k];"),
+    ("rms_not_mean", "ms /= (double)N;", ""),
+    ("bias_dropped", "v[n] += bias[(h * R + r) * N + n];", "(void)bias;"),
+    ("h_in_ignored", "g[i] = h_in ? h_in[(ib * H + h) * NP + i] : 0.0;", "g[i] = 0.0;"),
+    ("carried_input_ignored", "if (Bbar_prev && x_prev) {", "if (0) {"),
+    ("rank_sum_dropped", "u[n * P + p] += bt[n] * xt[p];", "u[n * P + p] = bt[n] * xt[p];"),
+    ("pair_swapped_in_rotation", "out[2 * k + 1] = -s * v[2 * k] + c * v[2 * k + 1];",
+     "out[2 * k + 1] = -s * v[2 * k + 1] + c * v[2 * k];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = oracle.source_text()
+    assert src.count(old) == 1, "mutation site not found exactly once: " + name
+    lib = oracle.build_variant(src.replace(old, new), str(tmp_path / ("m_" + name + ".so")))
+    failed = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(lib=lib)
+        except AssertionError:
+            failed.append(check.__name__)
+    assert failed, "no pin caught mutant " + name
