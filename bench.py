@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mamba-3 SSM layer core on one MI355X.
+
+One step = one pass of the layer core over one batch of the SISO workload (b=8, L=2048, H=64,
+P=64, N=128, R=1, chunk 64, bf16 io, fp32 state): m3_bcnorm_rope then m3_prefill.  `value` is
+prefill tokens/s (b * L tokens per step).  The same JSON line carries decode throughput on the
+B=128 decode workloads (R=1 and R=4: m3_bcnorm_rope with L=1 then m3_decode_step per token),
+the roofline of the dominant kernel measured live with HIP events on the launch stream, and the
+fp64 oracle's throughput on a bounded sample of the same prefill workload on the host cores.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from state_space_sequence_m3_amd import inputs, m3scan  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def prefill_bytes_per_token_head(w) -> int:
+    """Compulsory HBM bytes of m3_prefill per (token, head): x, Bbar, Cbar, dt, lam read once,
+    y written once (the final state is added per (b, h) separately)."""
+    es = 2 if w.io == "bf16" else 4
+    R, N, P = w.rank, w.dstate, w.headdim
+    y = P if w.mix else R * P
+    return es * (R * P + 2 * R * N + 2 + y)
+
+
+def bcnorm_bytes_per_token_head(w) -> int:
+    """m3_bcnorm_rope: B, C, theta, dt read once; Bbar, Cbar written once."""
+    es = 2 if w.io == "bf16" else 4
+    R, N = w.rank, w.dstate
+    return es * (4 * R * N + N // 2 + 1)
+
+
+def prefill_flops_per_token_head(w) -> int:
+    """Chunked form with full Q x Q blocks: 2 Q R^2 (N + P) + 4 R N P."""
+    Q, R, N, P = w.chunk, w.rank, w.dstate, w.headdim
+    return 2 * Q * R * R * (N + P) + 4 * R * N * P
+
+
+def decode_bytes_per_head(w) -> int:
+    """m3_decode_step per (b, h): fp32 state read + written, Bbar_prev, x_prev, x, Bbar, Cbar,
+    dt, lam read, y written."""
+    es = 2 if w.io == "bf16" else 4
+    R, N, P = w.rank, w.dstate, w.headdim
+    y = P if w.mix else R * P
+    return 2 * N * P * 4 + es * (3 * R * N + 2 * R * P + 2 + y)
+
+
+def time_prefill(w, steps, warmup, dev):
+    inp = inputs.make_prefill_inputs(w, seed=0, device=dev)
+    b, L, H, R, N, P = w.batch, w.seqlen, w.nheads, w.rank, w.dstate, w.headdim
+    io = w.torch_io
+    Bb = torch.empty((b, L, H, R, N), dtype=io, device=dev)
+    Cb = torch.empty_like(Bb)
+    phi = torch.empty((b, H, N // 2), dtype=torch.float32, device=dev)
+    y = torch.empty((b, L, H, P) if w.mix else (b, L, H, R, P), dtype=io, device=dev)
+    h = torch.empty((b, H, N, P), dtype=torch.float32, device=dev)
+    dims = m3scan.make_dims(b, L, H, P, N, R, w.chunk, m3scan.M3_BF16 if w.io == "bf16" else m3scan.M3_F32)
+    wsb = m3scan.bcnorm_rope_workspace_bytes(dims)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        m3scan.m3_bcnorm_rope(inp["B"], inp["C"], inp["dt"], inp["theta"], inp["normw_B"],
+                              inp["normw_C"], inp["bias_B"], inp["bias_C"], None, Bbar=Bb, Cbar=Cb,
+                              phi_out=phi, bcnorm=w.bcnorm, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        m3scan.m3_prefill(inp["x"], Bb, Cb, inp["dt"], inp["A"], inp["lam"],
+                          inp["w_out"] if w.mix else None, y=y, h_out=h, chunk=w.chunk)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-step timing: K steps between two events
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    # per-kernel timing on the same stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    ms_bc = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    ms_pf = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    return inp, ms_step, ms_bc, ms_pf
+
+
+def time_decode(w, steps, warmup, dev):
+    """`steps` consecutive decode tokens (bcnorm_rope L=1 + decode_step each), HIP-event timed."""
+    total = steps + warmup
+    dinp = inputs.make_decode_inputs(w, seed=0, steps=total, device=dev)
+    toks, st = dinp["tokens"], dinp["state"]
+    b, H, R, N, P = w.batch, w.nheads, w.rank, w.dstate, w.headdim
+    h, phi = st["h"], st["phi"]
+    bufs = [st["Bbar_prev"], torch.empty_like(st["Bbar_prev"])]
+    Cc = torch.empty_like(bufs[0])
+    y = torch.empty((b, H, P) if w.mix else (b, H, R, P), dtype=w.torch_io, device=dev)
+    stream = torch.cuda.current_stream()
+    xprev = st["x_prev"]
+
+    def tok(s, ev=None):
+        nonlocal xprev
+        Bprev, Bcur = bufs[s % 2], bufs[(s + 1) % 2]
+        if ev is not None:
+            ev[0].record(stream)
+        m3scan.m3_bcnorm_rope(toks["B"][s].unsqueeze(1), toks["C"][s].unsqueeze(1),
+                              toks["dt"][s].unsqueeze(1), toks["theta"][s].unsqueeze(1), None, None,
+                              dinp["bias_B"], dinp["bias_C"], phi, Bbar=Bcur.unsqueeze(1),
+                              Cbar=Cc.unsqueeze(1), phi_out=phi)
+        if ev is not None:
+            ev[1].record(stream)
+        m3scan.m3_decode_step(h, Bprev, xprev, toks["x"][s], Bcur, Cc, toks["dt"][s], dinp["A"],
+                              toks["lam"][s], dinp["w_out"] if w.mix else None, y=y)
+        if ev is not None:
+            ev[2].record(stream)
+        xprev = toks["x"][s]
+
+    for s in range(warmup):
+        tok(s)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for k in range(steps):
+        tok(warmup + k, evs[k])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_tok = t0.elapsed_time(t1) / steps
+    ms_bc = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    ms_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    return ms_tok, ms_bc, ms_dec
+
+
+def cpu_baseline(w, inp, nheads: int):
+    """The fp64 oracle (unchanged) on a bounded sample of the prefill workload: every batch row
+    and the first `nheads` heads, i.e. batch * nheads (batch, head) pairs over the full length."""
+    import oracle
+    host = {}
+    for k in ("x", "B", "C", "dt", "lam", "theta"):
+        host[k] = inp[k][:, :, :nheads].cpu()
+    host["A"] = inp["A"][:nheads].cpu()
+    for k in ("bias_B", "bias_C", "normw_B", "normw_C", "w_out"):
+        host[k] = None if inp[k] is None else inp[k][:nheads].cpu()
+    t_start = time.perf_counter()
+    oracle.layer(host, bcnorm=w.bcnorm, mix=w.mix)
+    secs = time.perf_counter() - t_start
+    pairs = w.batch * nheads
+    tokens = pairs * w.seqlen / w.nheads   # (batch, head) pairs -> whole-layer tokens
+    return {"value": tokens / secs, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d (batch, head) pairs (all %d batch rows x %d of %d heads) x %d steps of "
+                      "%s, fp64 bcnorm_rope + scan, %.2f s wall; tokens = pairs * L / H"
+                      % (pairs, w.batch, nheads, w.nheads, w.seqlen, w.name, secs)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the layer core has no cross-GPU step, and this build "
+              "runs on a single MI355X (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    m3scan.load()
+
+    w = inputs.WORKLOADS["siso_b8_l2048"]
+    inp, ms_step, ms_bc, ms_pf = time_prefill(w, args.steps, args.warmup, dev)
+    th = w.batch * w.seqlen * w.nheads
+    tokens = w.batch * w.seqlen
+    pf_bytes = th * prefill_bytes_per_token_head(w) + w.batch * w.nheads * w.dstate * w.headdim * 4
+    bc_bytes = th * bcnorm_bytes_per_token_head(w)
+    pf_flops = th * prefill_flops_per_token_head(w)
+    kernels = {
+        "m3_prefill": {"ms": ms_pf, "bytes": pf_bytes, "GB/s": pf_bytes / ms_pf / 1e6,
+                       "TFLOP/s": pf_flops / ms_pf / 1e9,
+                       "hbm_frac": pf_bytes / ms_pf / 1e6 / HBM_PEAK_GBS,
+                       "mfma_frac": pf_flops / ms_pf / 1e9 / BF16_MFMA_PEAK_TFLOPS},
+        "m3_bcnorm_rope": {"ms": ms_bc, "bytes": bc_bytes, "GB/s": bc_bytes / ms_bc / 1e6,
+                           "hbm_frac": bc_bytes / ms_bc / 1e6 / HBM_PEAK_GBS},
+    }
+    dom = "m3_prefill" if ms_pf >= ms_bc else "m3_bcnorm_rope"
+    kd = kernels[dom]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(kd["GB/s"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": kd["bytes"], "avg_launch_ms": round(kd["ms"], 5)}
+
+    decode = None
+    if not args.no_decode:
+        decode = {}
+        for name in ("decode_b128_r1", "decode_b128_r4"):
+            wd = inputs.WORKLOADS[name]
+            ms_tok, ms_dbc, ms_dec = time_decode(wd, args.decode_steps, args.warmup, dev)
+            dbytes = wd.batch * wd.nheads * decode_bytes_per_head(wd)
+            decode[name] = {"steps_per_s": 1e3 / ms_tok, "ms_per_step": ms_tok,
+                            "decode_step_ms": ms_dec, "bcnorm_rope_ms": ms_dbc,
+                            "decode_step_GB/s": dbytes / ms_dec / 1e6,
+                            "decode_step_hbm_frac": dbytes / ms_dec / 1e6 / HBM_PEAK_GBS,
+                            "decode_step_bytes": dbytes}
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp, args.cpu_heads)
+
+    line = {
+        "metric": "prefill tokens/s and B=128 decode steps/s per Mamba-3 layer; % of roofline",
+        "value": tokens / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the SISO b8 L2048 layer workload)",
+        "config": {"workload": "siso_b8_l2048: m3_bcnorm_rope + m3_prefill, b=8 L=2048 H=64 P=64 "
+                               "N=128 R=1 chunk=64, bf16 io, fp32 state",
+                   "batch": w.batch, "seq_len": w.seqlen, "nheads": w.nheads, "headdim": w.headdim,
+                   "dstate": w.dstate, "rank": w.rank, "chunk": w.chunk},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "decode": decode,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

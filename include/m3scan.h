@@ -1,0 +1,207 @@
+/*
+ * m3scan.h -- C ABI of libm3scan, the MI355X (gfx950) library for the Mamba-3 SSM layer core.
+ *
+ * The layer core is the exponential-trapezoidal selective recurrence with a data-dependent
+ * rotation of the state and MIMO rank R:
+ *
+ *   h_t = alpha_t R_t h_{t-1} + beta_t R_t B_{t-1} x_{t-1}^T + gamma_t B_t x_t^T,   y_t = C_t^T h_t
+ *   alpha_t = exp(dt_t A),  beta_t = (1 - lambda_t) dt_t exp(dt_t A),  gamma_t = lambda_t dt_t
+ *
+ * (aipaper.cc summary of "Mamba-3: Improved Sequence Modeling using State Space Principles",
+ * section 4.1 Proposition 1 for the recurrence, section 4.2 Propositions 2-3 for the rotation,
+ * section 4.3 for MIMO).  The rotation R_t is block-diagonal with 2x2 blocks of angle
+ * dt_t * theta_t[k] on the pairs (2k, 2k+1) (metaphor-xennon SSM comparison, section 2.2).  As
+ * Proposition 3 states, it is applied as a cumulative rotation of B and C, so the state
+ * recurrence itself stays real with a scalar decay:
+ *
+ *   m3_bcnorm_rope   BCNorm + bias + cumulative rotation:  Bbar_t = R(Phi_t)^T Btilde_t, same for C
+ *   m3_prefill       chunked scan over a whole sequence (structured-mask matrix form)
+ *   m3_decode_step   one new token for a batch of resident states
+ *
+ * Frame of the state.  The state the library keeps, returns and accepts is the rotated frame
+ * g_t = R(Phi_t)^T h_t.  Together with the angle Phi_t (returned by m3_bcnorm_rope) it fully
+ * determines h_t = R(Phi_t) g_t.  In this frame the previous-input term uses the rotated
+ * previous input: g_t = alpha_t g_{t-1} + beta_t Bbar_{t-1}^T x_{t-1} + gamma_t Bbar_t^T x_t.
+ *
+ * Conventions for every entry point:
+ *  - Memory.  All tensor pointers are device pointers, owned by the caller, dense row-major in
+ *    the layouts stated below, and must stay valid until the work queued on `stream` has run.
+ *    The library never allocates in these calls; a call that needs scratch memory takes a
+ *    caller-provided workspace whose size the matching *_workspace_bytes function returns.
+ *  - Alignment.  Pointers to x, B, C, Bbar, Cbar, theta, y, h, h_in, h_out must be 16-byte
+ *    aligned; every other pointer must be aligned to its element size.
+ *  - dtype.  "io" tensors have the element type dims->io (fp32 or bf16, bf16 stored as its
+ *    16-bit pattern).  The state h, the angle phi and every per-head constant are fp32.
+ *  - Asynchrony.  Every call only validates its arguments and enqueues kernels on `stream`.
+ *    M3_OK means "validated and enqueued"; faults during execution surface at the caller's
+ *    next synchronisation.  Calls on one stream run in order.
+ *  - Errors.  A non-OK status leaves every output untouched and sets a message readable with
+ *    m3_last_error() on the calling thread.  Numeric values are not validated (dt <= 0, A > 0,
+ *    NaN or Inf simply propagate).
+ *  - Device.  The current HIP device must be a gfx950 GPU, else M3_E_NODEVICE.
+ *  - Threads.  Calls from several host threads are safe; calls that write the same buffers
+ *    must be ordered by the caller.
+ */
+#ifndef M3SCAN_H
+#define M3SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    M3_OK = 0,
+    M3_E_NULL = 1,        /* a required pointer is NULL                                    */
+    M3_E_DIMS = 2,        /* a size is negative, odd where it must be even, or inconsistent */
+    M3_E_ALIGN = 3,       /* a pointer violates the alignment rule above                    */
+    M3_E_DTYPE = 4,       /* dims->io is not M3_F32 or M3_BF16                             */
+    M3_E_UNSUPPORTED = 5, /* valid, but outside the shapes this build has kernels for       */
+    M3_E_NODEVICE = 6,    /* no current HIP device, or it is not gfx950                     */
+    M3_E_LAUNCH = 7,      /* the HIP runtime refused a kernel launch                        */
+    M3_E_WORKSPACE = 8,   /* workspace NULL or smaller than *_workspace_bytes returned      */
+    M3_E_ALIAS = 9        /* outputs overlap inputs in a way the call does not allow        */
+} m3_status;
+
+typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
+
+/* dims->flags */
+#define M3_BCNORM 1u /* apply the RMS normalisation in m3_bcnorm_rope (else only bias + rotation) */
+
+typedef struct {
+    int64_t batch;   /* b                                                                    */
+    int64_t seqlen;  /* L: time steps in this call (1 for m3_decode_step)                    */
+    int64_t nheads;  /* H                                                                    */
+    int64_t headdim; /* P: width of x and y per rank                                         */
+    int64_t dstate;  /* N: state size per head dim (even: N/2 rotation pairs)                */
+    int64_t rank;    /* R: MIMO rank, 1 = SISO                                                */
+    int64_t chunk;   /* Q: time steps per chunk in m3_prefill; 0 = library default (64/R)    */
+    int32_t io;      /* m3_dtype of the io tensors                                            */
+    uint32_t flags;  /* M3_BCNORM                                                             */
+    float eps;       /* added to the mean square in BCNorm (e.g. 1e-5)                        */
+} m3_dims;
+
+/*
+ * m3_bcnorm_rope -- BCNorm, head bias and cumulative rotation of B and C.
+ *
+ * Defined by: papernotes.org summary of Mamba-3, key design 4 (RMSNorm on the B and C
+ * projections, "BCNorm", and a learnable head-specific B/C bias); aipaper.cc summary, section
+ * 4.2 Proposition 3 (B and C multiplied by the cumulative product of R_i^T, i = 0..t);
+ * metaphor-xennon section 2.2 (R_t has angle dt_t * theta_t).
+ *
+ * For every (b, t, h, r) and each of B and C (vector v of N entries):
+ *   vt = v / sqrt(mean(v^2) + eps) * normw[h, :]   if dims->flags & M3_BCNORM, else vt = v
+ *   vt = vt + bias[h, r, :]                         if bias is not NULL
+ *   Phi_t[k] = Phi_in[k] + sum_{i<=t} dt_i theta_i[k]       (k < N/2; the current step included)
+ *   out[2k] = cos(Phi_t[k]) vt[2k] + sin(Phi_t[k]) vt[2k+1]
+ *   out[2k+1] = -sin(Phi_t[k]) vt[2k] + cos(Phi_t[k]) vt[2k+1]
+ *
+ * Arguments (shapes use the dims fields; "io" = dims->io):
+ *   B, C        [b, L, H, R, N] io   raw projections                                  required
+ *   dt          [b, L, H] io         step size (positive; already passed through softplus) required
+ *   theta       [b, L, H, N/2] io    rotation rate per pair                            required
+ *   normw_B/C   [H, N] f32           BCNorm weight; NULL = 1                            optional
+ *   bias_B/C    [H, R, N] f32        head bias; NULL = 0                                optional
+ *   phi_in      [b, H, N/2] f32      angle carried in from earlier steps; NULL = 0      optional
+ *   Bbar, Cbar  [b, L, H, R, N] io   rotated outputs                                   required
+ *   phi_out     [b, H, N/2] f32      angle after the last step, reduced to [-pi, pi]    required
+ *   workspace   device scratch of m3_bcnorm_rope_workspace_bytes(dims) bytes (may be NULL
+ *               when that is 0)
+ * phi_out may be the same buffer as phi_in (decode carries the angle in place); no other
+ * output may overlap an input.  This build has kernels for N in {16, 32, 64, 128, 256} and
+ * 1 <= R <= 64; other shapes return M3_E_UNSUPPORTED.
+ */
+m3_status m3_bcnorm_rope(const m3_dims* dims, const void* B, const void* C, const void* dt,
+                         const void* theta, const float* normw_B, const float* normw_C,
+                         const float* bias_B, const float* bias_C, const float* phi_in,
+                         void* Bbar, void* Cbar, float* phi_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace m3_bcnorm_rope needs for these dims (0 for short sequences). */
+size_t m3_bcnorm_rope_workspace_bytes(const m3_dims* dims);
+
+/*
+ * m3_prefill -- the exponential-trapezoidal recurrence over a whole sequence, in chunks.
+ *
+ * Defined by: aipaper.cc summary, section 4.1 Proposition 1 (recurrence and alpha, beta,
+ * gamma), section 4.3 (MIMO update H_t = a_t H_{t-1} + B_t X_t^T); papernotes.org, key design 1
+ * (the structured mask of the recurrence is a 1-semiseparable decay times a 2-band matrix and
+ * still allows chunked matrix products).  Computed exactly (up to rounding) as, per (b, h):
+ *
+ *   g_{-1} = h_in,   u_{-1} = sum_r Bbar_prev[r]^T x_prev[r]
+ *   u_t = sum_r Bbar_t[r]^T x_t[r]                                   (N x P)
+ *   g_t = alpha_t g_{t-1} + beta_t u_{t-1} + gamma_t u_t,   alpha_t = exp(dt_t A[h])
+ *   Y_t[r] = Cbar_t[r] g_t                                           (R x P)
+ *   y_t[p] = sum_r w_out[h, r, p] Y_t[r, p] if w_out is given, else y_t = Y_t
+ *
+ * Arguments:
+ *   x           [b, L, H, R, P] io    inputs                                          required
+ *   Bbar, Cbar  [b, L, H, R, N] io    rotated B, C (from m3_bcnorm_rope)                required
+ *   dt, lam     [b, L, H] io          step size and trapezoid weight lambda             required
+ *   A           [H] f32               decay rate per head (<= 0)                        required
+ *   w_out       [H, R, P] f32         output mixing over ranks; NULL = no mixing         optional
+ *   h_in        [b, H, N, P] f32      state carried in; NULL = 0                         optional
+ *   Bbar_prev   [b, H, R, N] io       rotated Bbar of the step before this call; NULL = 0 optional
+ *   x_prev      [b, H, R, P] io       x of the step before this call; NULL = 0           optional
+ *   y           [b, L, H, P] io if w_out, else [b, L, H, R, P] io                      required
+ *   h_out       [b, H, N, P] f32      final state g_{L-1} (may be the same buffer as h_in) required
+ *   Bbar_last   [b, H, R, N] io       copy of Bbar at step L-1 (for a following decode)  optional
+ *   x_last      [b, H, R, P] io       copy of x at step L-1                              optional
+ *   workspace   m3_prefill_workspace_bytes(dims) bytes (may be NULL when that is 0)
+ * Any L >= 0 is accepted (L = 0 copies the carried state to the outputs).  dims->chunk * R
+ * must be 16, 32, 48 or 64.  This build has kernels for (N, P) in {(16,16), (64,64), (128,64)}
+ * and R in {1, 2, 4, 8, 16} dividing 16; other shapes return M3_E_UNSUPPORTED.
+ */
+m3_status m3_prefill(const m3_dims* dims, const void* x, const void* Bbar, const void* Cbar,
+                     const void* dt, const float* A, const void* lam, const float* w_out,
+                     const float* h_in, const void* Bbar_prev, const void* x_prev, void* y,
+                     float* h_out, void* Bbar_last, void* x_last, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace m3_prefill needs for these dims. */
+size_t m3_prefill_workspace_bytes(const m3_dims* dims);
+
+/*
+ * m3_decode_step -- one new token for each of b * H resident states, updated in place.
+ *
+ * Defined by: aipaper.cc summary, section 4.1 Proposition 1 and section 4.3 (the same
+ * recurrence as m3_prefill with L = 1); papernotes.org key design 3 (decode is bound by the
+ * memory traffic of the state; MIMO adds work per byte).  Per (b, h):
+ *
+ *   h    <- alpha h + beta Bbar_prev^T x_prev + gamma Bbar^T x      (rank-2R update, fp32)
+ *   Y[r] =  Cbar[r] h                                               (after the update)
+ *   y[p] =  sum_r w_out[h, r, p] Y[r, p] if w_out, else y = Y
+ *
+ * Arguments (dims->seqlen must be 1):
+ *   h           [b, H, N, P] f32      state, read and overwritten                       required
+ *   Bbar_prev   [b, H, R, N] io       rotated B of the previous token                   required
+ *   x_prev      [b, H, R, P] io       x of the previous token                           required
+ *   x           [b, H, R, P] io       x of this token                                   required
+ *   Bbar, Cbar  [b, H, R, N] io       rotated B, C of this token (m3_bcnorm_rope, L = 1) required
+ *   dt, lam     [b, H] io                                                               required
+ *   A           [H] f32                                                                 required
+ *   w_out       [H, R, P] f32 or NULL                                                   optional
+ *   y           [b, H, P] io if w_out, else [b, H, R, P] io                            required
+ * The caller keeps (Bbar, x) of this token as (Bbar_prev, x_prev) of the next one, e.g. by
+ * swapping buffers; nothing is copied.  P must be a power of two with 4 <= P <= 256, N <= 256,
+ * R <= 8.
+ */
+m3_status m3_decode_step(const m3_dims* dims, float* h, const void* Bbar_prev,
+                         const void* x_prev, const void* x, const void* Bbar, const void* Cbar,
+                         const void* dt, const float* A, const void* lam, const float* w_out,
+                         void* y, hipStream_t stream);
+
+/* Message describing the last non-OK status returned on the calling thread ("" if none). */
+const char* m3_last_error(void);
+
+/* Library version string. */
+const char* m3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M3SCAN_H */

@@ -1,0 +1,309 @@
+// api.hip -- the C ABI of libm3scan (declared in include/m3scan.h): argument validation, the
+// gfx950 device check, workspace sizing, and dispatch to the kernels.  Nothing here computes
+// any part of the method; every call validates, then only enqueues kernels on the caller's
+// stream.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "m3_device.h"
+#include "m3_launch.h"
+#include "m3scan.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+m3_status fail(m3_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+// 0 = not checked yet, 1 = gfx950, 2 = something else
+std::atomic<int> g_dev_ok[256];
+
+m3_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(M3_E_NODEVICE, "no current HIP device");
+    if (dev < 256) {
+        const int s = g_dev_ok[dev].load(std::memory_order_relaxed);
+        if (s == 1) return M3_OK;
+        if (s == 2) return fail(M3_E_NODEVICE, "HIP device %d is not a gfx950 GPU", dev);
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(M3_E_NODEVICE, "cannot query HIP device %d", dev);
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 256) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    if (!ok) return fail(M3_E_NODEVICE, "HIP device %d is %s, not gfx950", dev, prop.gcnArchName);
+    return M3_OK;
+}
+
+size_t io_size(const m3_dims* d) { return d->io == M3_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// [p, p + n) and [q, q + m) overlap (both non-empty)
+bool overlap(const void* p, size_t n, const void* q, size_t m) {
+    if (!p || !q || n == 0 || m == 0) return false;
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + m && b < a + n;
+}
+
+struct Buf {
+    const void* p;
+    size_t bytes;
+    const char* name;
+};
+
+m3_status check_common_dims(const m3_dims* d) {
+    if (!d) return fail(M3_E_NULL, "dims is NULL");
+    if (d->io != M3_F32 && d->io != M3_BF16) return fail(M3_E_DTYPE, "dims->io = %d is not M3_F32 or M3_BF16", d->io);
+    const int64_t lim = (int64_t)1 << 31;
+    if (d->batch < 0 || d->seqlen < 0 || d->nheads < 0 || d->headdim < 0 || d->dstate < 0 || d->rank < 1 ||
+        d->chunk < 0)
+        return fail(M3_E_DIMS, "negative size, or rank < 1");
+    if (d->batch >= lim || d->seqlen >= lim || d->nheads >= lim || d->headdim > 4096 || d->dstate > 4096 ||
+        d->rank > 64)
+        return fail(M3_E_DIMS, "size out of range");
+    if (d->dstate % 2 != 0) return fail(M3_E_DIMS, "dstate N = %lld must be even", (long long)d->dstate);
+    return M3_OK;
+}
+
+// outputs must not overlap inputs, nor each other
+m3_status check_alias(const Buf* outs, int nout, const Buf* ins, int nin) {
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlap(outs[i].p, outs[i].bytes, ins[j].p, ins[j].bytes))
+                return fail(M3_E_ALIAS, "output %s overlaps input %s", outs[i].name, ins[j].name);
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
+                return fail(M3_E_ALIAS, "outputs %s and %s overlap", outs[i].name, outs[j].name);
+    }
+    return M3_OK;
+}
+
+m3_status check_required(const Buf* bufs, int n) {
+    for (int i = 0; i < n; ++i)
+        if (!bufs[i].p && bufs[i].bytes > 0) return fail(M3_E_NULL, "%s is NULL", bufs[i].name);
+    return M3_OK;
+}
+
+m3_status check_align(const Buf* bufs, int n, size_t a) {
+    for (int i = 0; i < n; ++i)
+        if (bufs[i].p && !aligned(bufs[i].p, a))
+            return fail(M3_E_ALIGN, "%s is not %zu-byte aligned", bufs[i].name, a);
+    return M3_OK;
+}
+
+m3_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(M3_E_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return M3_OK;
+}
+
+// dst[i] = src ? src[i] : 0 over n 16-bit words (the sizes used here are all even in bytes)
+__global__ void copy_or_zero_kernel(uint16_t* dst, const uint16_t* src, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = src ? src[i] : (uint16_t)0;
+}
+
+__global__ void wrap_angle_kernel(float* dst, const float* src, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = src ? m3::wrap_angle(src[i]) : 0.0f;
+}
+
+hipError_t copy_or_zero(void* dst, const void* src, size_t bytes, hipStream_t s) {
+    if (!dst || bytes == 0) return hipSuccess;
+    const int64_t n = (int64_t)(bytes / 2);
+    const unsigned blocks = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    hipLaunchKernelGGL(copy_or_zero_kernel, dim3(blocks), dim3(256), 0, s, (uint16_t*)dst, (const uint16_t*)src, n);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* m3_last_error(void) { return g_err; }
+
+const char* m3_version(void) { return "libm3scan 0.1.0 gfx950"; }
+
+size_t m3_bcnorm_rope_workspace_bytes(const m3_dims* d) {
+    if (!d || d->batch <= 0 || d->nheads <= 0 || d->seqlen <= 0 || d->dstate <= 0) return 0;
+    const int64_t seg = m3::bcnorm_rope_seglen();
+    const int64_t nseg = (d->seqlen + seg - 1) / seg;
+    if (nseg <= 1) return 0;
+    return (size_t)(d->batch * d->nheads * nseg * (d->dstate / 2)) * sizeof(float);
+}
+
+size_t m3_prefill_workspace_bytes(const m3_dims* d) {
+    (void)d;
+    return 0;
+}
+
+m3_status m3_bcnorm_rope(const m3_dims* d, const void* B, const void* C, const void* dt, const void* theta,
+                         const float* normw_B, const float* normw_C, const float* bias_B, const float* bias_C,
+                         const float* phi_in, void* Bbar, void* Cbar, float* phi_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    m3_status s = check_common_dims(d);
+    if (s != M3_OK) return s;
+    const int64_t b = d->batch, L = d->seqlen, H = d->nheads, N = d->dstate, R = d->rank;
+    const size_t es = io_size(d);
+    const size_t nBC = (size_t)(b * L * H * R * N) * es, nStep = (size_t)(b * L * H) * es;
+    const size_t nTh = (size_t)(b * L * H * (N / 2)) * es, nPhi = (size_t)(b * H * (N / 2)) * 4;
+    const Buf req[] = {{B, nBC, "B"}, {C, nBC, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
+                       {Bbar, nBC, "Bbar"}, {Cbar, nBC, "Cbar"}, {phi_out, nPhi, "phi_out"}};
+    if ((s = check_required(req, 7)) != M3_OK) return s;
+    if (!m3::bcnorm_rope_supported((int)N, (int)R))
+        return fail(M3_E_UNSUPPORTED, "m3_bcnorm_rope: N = %lld (need 16, 32, 64, 128 or 256), R = %lld",
+                    (long long)N, (long long)R);
+    const Buf a16[] = {{B, 1, "B"}, {C, 1, "C"}, {theta, 1, "theta"}, {Bbar, 1, "Bbar"}, {Cbar, 1, "Cbar"}};
+    if ((s = check_align(a16, 5, 16)) != M3_OK) return s;
+    const Buf a4[] = {{normw_B, 1, "normw_B"}, {normw_C, 1, "normw_C"}, {bias_B, 1, "bias_B"},
+                      {bias_C, 1, "bias_C"}, {phi_in, 1, "phi_in"}, {phi_out, 1, "phi_out"},
+                      {workspace, 1, "workspace"}};
+    if ((s = check_align(a4, 7, 4)) != M3_OK) return s;
+    if ((s = check_align(&req[2], 1, es)) != M3_OK) return s;
+    if (normw_B && !aligned(normw_B, 16)) return fail(M3_E_ALIGN, "normw_B is not 16-byte aligned");
+    if (normw_C && !aligned(normw_C, 16)) return fail(M3_E_ALIGN, "normw_C is not 16-byte aligned");
+    if (bias_B && !aligned(bias_B, 16)) return fail(M3_E_ALIGN, "bias_B is not 16-byte aligned");
+    if (bias_C && !aligned(bias_C, 16)) return fail(M3_E_ALIGN, "bias_C is not 16-byte aligned");
+    const size_t nW = (size_t)(H * N) * 4, nBias = (size_t)(H * R * N) * 4;
+    const Buf ins[] = {{B, nBC, "B"}, {C, nBC, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
+                       {normw_B, nW, "normw_B"}, {normw_C, nW, "normw_C"}, {bias_B, nBias, "bias_B"},
+                       {bias_C, nBias, "bias_C"}};
+    const size_t need = m3_bcnorm_rope_workspace_bytes(d);
+    const Buf outs[] = {{Bbar, nBC, "Bbar"}, {Cbar, nBC, "Cbar"}, {phi_out, nPhi, "phi_out"},
+                        {workspace, need, "workspace"}};
+    if ((s = check_alias(outs, 4, ins, 8)) != M3_OK) return s;
+    if (phi_in && phi_in != phi_out && overlap(phi_in, nPhi, phi_out, nPhi))
+        return fail(M3_E_ALIAS, "phi_out partially overlaps phi_in");
+    if (overlap(phi_in, nPhi, Bbar, nBC) || overlap(phi_in, nPhi, Cbar, nBC) || overlap(phi_in, nPhi, workspace, need))
+        return fail(M3_E_ALIAS, "phi_in overlaps an output");
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(M3_E_WORKSPACE, "m3_bcnorm_rope needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    if ((s = check_device()) != M3_OK) return s;
+    if (b == 0 || H == 0 || N == 0) return M3_OK;
+    if (L == 0) {
+        const int64_t n = b * H * (N / 2);
+        hipLaunchKernelGGL(wrap_angle_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, phi_out,
+                           phi_in, n);
+        return launched(hipGetLastError(), "m3_bcnorm_rope");
+    }
+    const int64_t seg = m3::bcnorm_rope_seglen();
+    const int64_t nseg = (L + seg - 1) / seg;
+    if (b * H * nseg >= ((int64_t)1 << 31) / 256) return fail(M3_E_DIMS, "m3_bcnorm_rope: grid too large");
+    m3::BcnormRopeArgs a;
+    a.B = B; a.C = C; a.dt = dt; a.theta = theta;
+    a.normw_B = normw_B; a.normw_C = normw_C; a.bias_B = bias_B; a.bias_C = bias_C;
+    a.phi_in = phi_in;
+    a.seg_phi = nseg > 1 ? (float*)workspace : nullptr;
+    a.Bbar = Bbar; a.Cbar = Cbar; a.phi_out = phi_out;
+    a.b = b; a.L = L; a.H = (int)H; a.N = (int)N; a.R = (int)R;
+    a.seglen = seg; a.nseg = (int)nseg;
+    a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;
+    a.eps = d->eps;
+    return launched(m3::launch_bcnorm_rope(a, d->io == M3_BF16, stream), "m3_bcnorm_rope");
+}
+
+m3_status m3_prefill(const m3_dims* d, const void* x, const void* Bbar, const void* Cbar, const void* dt,
+                     const float* A, const void* lam, const float* w_out, const float* h_in, const void* Bbar_prev,
+                     const void* x_prev, void* y, float* h_out, void* Bbar_last, void* x_last, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    m3_status s = check_common_dims(d);
+    if (s != M3_OK) return s;
+    const int64_t b = d->batch, L = d->seqlen, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
+    const int64_t Q = d->chunk > 0 ? d->chunk : (64 / R > 0 ? 64 / R : 1);
+    const size_t es = io_size(d);
+    const size_t nX = (size_t)(b * L * H * R * P) * es, nBC = (size_t)(b * L * H * R * N) * es;
+    const size_t nStep = (size_t)(b * L * H) * es, nA = (size_t)H * 4;
+    const size_t nY = (size_t)(b * L * H * (w_out ? 1 : R) * P) * es, nH = (size_t)(b * H * N * P) * 4;
+    const size_t nBp = (size_t)(b * H * R * N) * es, nXp = (size_t)(b * H * R * P) * es;
+    const size_t nWo = (size_t)(H * R * P) * 4;
+    const Buf req[] = {{x, nX, "x"}, {Bbar, nBC, "Bbar"}, {Cbar, nBC, "Cbar"}, {dt, nStep, "dt"}, {A, nA, "A"},
+                       {lam, nStep, "lam"}, {y, nY, "y"}, {h_out, nH, "h_out"}};
+    if ((s = check_required(req, 8)) != M3_OK) return s;
+    if (Q * R > 64 || !m3::prefill_supported((int)N, (int)P, (int)R, (int)(Q * R), d->io == M3_BF16))
+        return fail(M3_E_UNSUPPORTED,
+                    "m3_prefill: no kernel for N = %lld, P = %lld, R = %lld, chunk*R = %lld (supported: (N,P) in "
+                    "{(16,16),(64,64),(128,64)}, R in {1,2,4,8,16}, chunk*R in {16,32,48,64})",
+                    (long long)N, (long long)P, (long long)R, (long long)(Q * R));
+    const Buf a16[] = {{x, 1, "x"}, {Bbar, 1, "Bbar"}, {Cbar, 1, "Cbar"}, {y, 1, "y"}, {h_out, 1, "h_out"},
+                       {h_in, 1, "h_in"}};
+    if ((s = check_align(a16, 6, 16)) != M3_OK) return s;
+    const Buf aes[] = {{dt, 1, "dt"}, {lam, 1, "lam"}, {Bbar_prev, 1, "Bbar_prev"}, {x_prev, 1, "x_prev"},
+                       {Bbar_last, 1, "Bbar_last"}, {x_last, 1, "x_last"}, {A, 1, "A"}, {w_out, 1, "w_out"}};
+    if ((s = check_align(aes, 8, es)) != M3_OK) return s;
+    const Buf ins[] = {{x, nX, "x"}, {Bbar, nBC, "Bbar"}, {Cbar, nBC, "Cbar"}, {dt, nStep, "dt"}, {A, nA, "A"},
+                       {lam, nStep, "lam"}, {w_out, nWo, "w_out"}, {Bbar_prev, nBp, "Bbar_prev"},
+                       {x_prev, nXp, "x_prev"}};
+    const Buf outs[] = {{y, nY, "y"}, {h_out, nH, "h_out"}, {Bbar_last, nBp, "Bbar_last"}, {x_last, nXp, "x_last"}};
+    if ((s = check_alias(outs, 4, ins, 9)) != M3_OK) return s;
+    if (h_in && h_in != h_out && overlap(h_in, nH, h_out, nH)) return fail(M3_E_ALIAS, "h_out partially overlaps h_in");
+    if (overlap(h_in, nH, y, nY) || overlap(h_in, nH, Bbar_last, nBp) || overlap(h_in, nH, x_last, nXp))
+        return fail(M3_E_ALIAS, "h_in overlaps an output");
+    if ((s = check_device()) != M3_OK) return s;
+    if (b == 0 || H == 0) return M3_OK;
+    if (L == 0) {
+        // nothing to scan: the carried state passes through unchanged
+        hipError_t e = copy_or_zero(h_out, h_in == h_out ? h_out : h_in, nH, stream);
+        if (e == hipSuccess) e = copy_or_zero(Bbar_last, Bbar_prev, nBp, stream);
+        if (e == hipSuccess) e = copy_or_zero(x_last, x_prev, nXp, stream);
+        return launched(e, "m3_prefill");
+    }
+    m3::PrefillArgs a;
+    a.x = x; a.Bbar = Bbar; a.Cbar = Cbar; a.dt = dt; a.A = A; a.lam = lam; a.w_out = w_out;
+    a.h_in = h_in; a.Bbar_prev = Bbar_prev; a.x_prev = x_prev;
+    a.y = y; a.h_out = h_out; a.Bbar_last = Bbar_last; a.x_last = x_last;
+    a.b = b; a.L = L; a.H = (int)H; a.N = (int)N; a.P = (int)P; a.R = (int)R; a.Q = (int)Q;
+    return launched(m3::launch_prefill(a, d->io == M3_BF16, stream), "m3_prefill");
+}
+
+m3_status m3_decode_step(const m3_dims* d, float* h, const void* Bbar_prev, const void* x_prev, const void* x,
+                         const void* Bbar, const void* Cbar, const void* dt, const float* A, const void* lam,
+                         const float* w_out, void* y, hipStream_t stream) {
+    m3_status s = check_common_dims(d);
+    if (s != M3_OK) return s;
+    if (d->seqlen != 1) return fail(M3_E_DIMS, "m3_decode_step: dims->seqlen must be 1, got %lld", (long long)d->seqlen);
+    const int64_t b = d->batch, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
+    const size_t es = io_size(d);
+    const size_t nH = (size_t)(b * H * N * P) * 4, nBp = (size_t)(b * H * R * N) * es;
+    const size_t nXp = (size_t)(b * H * R * P) * es, nStep = (size_t)(b * H) * es, nA = (size_t)H * 4;
+    const size_t nY = (size_t)(b * H * (w_out ? 1 : R) * P) * es, nWo = (size_t)(H * R * P) * 4;
+    const Buf req[] = {{h, nH, "h"}, {Bbar_prev, nBp, "Bbar_prev"}, {x_prev, nXp, "x_prev"}, {x, nXp, "x"},
+                       {Bbar, nBp, "Bbar"}, {Cbar, nBp, "Cbar"}, {dt, nStep, "dt"}, {A, nA, "A"},
+                       {lam, nStep, "lam"}, {y, nY, "y"}};
+    if ((s = check_required(req, 10)) != M3_OK) return s;
+    if (!m3::decode_supported((int)N, (int)P, (int)R))
+        return fail(M3_E_UNSUPPORTED,
+                    "m3_decode_step: no kernel for N = %lld, P = %lld, R = %lld (need P a power of two in [4, 256], "
+                    "N <= 256, R in {1,2,4,8})",
+                    (long long)N, (long long)P, (long long)R);
+    if (!aligned(h, 16)) return fail(M3_E_ALIGN, "h is not 16-byte aligned");
+    const Buf aes[] = {{Bbar_prev, 1, "Bbar_prev"}, {x_prev, 1, "x_prev"}, {x, 1, "x"}, {Bbar, 1, "Bbar"},
+                       {Cbar, 1, "Cbar"}, {dt, 1, "dt"}, {lam, 1, "lam"}, {y, 1, "y"}, {A, 1, "A"},
+                       {w_out, 1, "w_out"}};
+    if ((s = check_align(aes, 10, es)) != M3_OK) return s;
+    const Buf ins[] = {{Bbar_prev, nBp, "Bbar_prev"}, {x_prev, nXp, "x_prev"}, {x, nXp, "x"}, {Bbar, nBp, "Bbar"},
+                       {Cbar, nBp, "Cbar"}, {dt, nStep, "dt"}, {A, nA, "A"}, {lam, nStep, "lam"},
+                       {w_out, nWo, "w_out"}};
+    const Buf outs[] = {{h, nH, "h"}, {y, nY, "y"}};
+    if ((s = check_alias(outs, 2, ins, 9)) != M3_OK) return s;
+    if ((s = check_device()) != M3_OK) return s;
+    if (b == 0 || H == 0) return M3_OK;
+    if (b * H >= ((int64_t)1 << 31) / 256) return fail(M3_E_DIMS, "m3_decode_step: grid too large");
+    m3::DecodeArgs a;
+    a.h = h; a.Bbar_prev = Bbar_prev; a.x_prev = x_prev; a.x = x; a.Bbar = Bbar; a.Cbar = Cbar;
+    a.dt = dt; a.A = A; a.lam = lam; a.w_out = w_out; a.y = y;
+    a.b = b; a.H = (int)H; a.N = (int)N; a.P = (int)P; a.R = (int)R;
+    return launched(m3::launch_decode(a, d->io == M3_BF16, stream), "m3_decode_step");
+}
+
+}  // extern "C"

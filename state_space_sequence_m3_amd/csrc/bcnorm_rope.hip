@@ -1,0 +1,307 @@
+// bcnorm_rope.hip -- m3_bcnorm_rope: BCNorm + head bias + cumulative rotation of B and C.
+//
+// BCNorm (RMS normalisation of each projected B/C vector, with an optional weight) and the
+// head-specific bias: papernotes.org summary of Mamba-3, key design 4.  The rotation: aipaper.cc
+// summary, section 4.2 Proposition 3 -- B_t and C_t are multiplied by the cumulative product of
+// R_i^T over i = 0..t, where R_i is block-diagonal with 2x2 blocks of angle dt_i * theta_i[k]
+// (metaphor-xennon SSM comparison, section 2.2).  The blocks commute, so the product is one
+// rotation by Phi_t[k] = Phi_in[k] + sum_{i<=t} dt_i theta_i[k] on each pair (2k, 2k+1).
+//
+// The angle is a prefix sum along the sequence, the only sequential part.  Long sequences are
+// cut into segments of kSegLen steps: angle_partial_kernel sums dt*theta over every segment in
+// parallel, angle_scan_kernel turns those sums into segment start angles (a scan over a few
+// dozen segments per (b, h)), and bcnorm_rope_kernel does the elementwise work with one
+// workgroup per (b, h, segment).  Inside a workgroup each wave owns a quarter of the segment;
+// the waves first sum their quarter's angle increments and exchange them through LDS, then walk
+// their quarter, carrying the angle in registers.  Angles are kept reduced to [-pi, pi] so the
+// fp32 rounding of the running sum stays at the size of one ulp of pi.
+//
+// Lane mapping: each (t, r) row of N values is split over N/8 lanes, 8 values (4 rotation
+// pairs) per lane, so one wave instruction moves 512/N whole rows.  The RMS over N is a
+// shuffle reduction within a row's N/8 lanes.
+#include "m3_device.h"
+#include "m3_launch.h"
+
+namespace m3 {
+
+namespace {
+
+constexpr int64_t kSegLen = 512;
+
+__device__ __forceinline__ void load4(const float* p, float o[4]) {
+    const float4 v = *(const float4*)p;
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float o[4]) {
+    const uint2 v = *(const uint2*)p;
+    o[0] = __uint_as_float(v.x << 16);
+    o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16);
+    o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+__device__ __forceinline__ void load8(const float* p, float o[8]) {
+    load4(p, o);
+    load4(p + 4, o + 4);
+}
+__device__ __forceinline__ void load8(const bf16* p, float o[8]) {
+    const uint4 v = *(const uint4*)p;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(w[i] << 16);
+        o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+    ((float4*)p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    ((float4*)p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void store8(bf16* p, const float v[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)bf16_bits_rne(v[2 * i]) | ((uint32_t)bf16_bits_rne(v[2 * i + 1]) << 16);
+    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Sum of dt * theta over each segment: seg_phi[b, h, seg, :].
+template <typename T, int N>
+__global__ __launch_bounds__(256) void angle_partial_kernel(BcnormRopeArgs a) {
+    constexpr int LPR = N / 8, K = N / 2;
+    __shared__ float part[4][K];
+    const int64_t id = blockIdx.x;
+    const int seg = (int)(id % a.nseg);
+    const int64_t bh = id / a.nseg;
+    const int64_t b = bh / a.H;
+    const int h = (int)(bh % a.H);
+    const int tid = threadIdx.x, c = tid % LPR, j = tid / LPR;
+    const int64_t t0 = seg * a.seglen;
+    const int64_t t1 = t0 + a.seglen < a.L ? t0 + a.seglen : a.L;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t t = t0 + j; t < t1; t += 256 / LPR) {
+        const int64_t row = (b * a.L + t) * a.H + h;
+        const float d = load_f32((const T*)a.dt + row);
+        float th[4];
+        load4((const T*)a.theta + row * K + 4 * c, th);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] += d * th[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        for (int m = LPR; m < 64; m <<= 1) acc[q] += shfl_xor(acc[q], m);
+    const int wave = tid >> 6, lane = tid & 63;
+    if (lane < LPR) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) part[wave][4 * c + q] = acc[q];
+    }
+    __syncthreads();
+    if (tid < K)
+        a.seg_phi[(bh * a.nseg + seg) * K + tid] =
+            part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+}
+
+// Segment sums -> segment start angles (exclusive scan, phi_in added), in place.
+__global__ void angle_scan_kernel(BcnormRopeArgs a) {
+    const int K = a.N / 2;
+    const int64_t bh = blockIdx.x;
+    for (int k = threadIdx.x; k < K; k += blockDim.x) {
+        float run = a.phi_in ? wrap_angle(a.phi_in[bh * K + k]) : 0.0f;
+        for (int s = 0; s < a.nseg; ++s) {
+            float* p = a.seg_phi + (bh * a.nseg + s) * K + k;
+            const float v = *p;
+            *p = run;
+            run = wrap_angle(run + v);
+        }
+    }
+}
+
+template <typename T, int N, int NW>
+__global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) {
+    constexpr int LPR = N / 8, RPW = 64 / LPR, K = N / 2;
+    __shared__ float wsum[NW][K];
+    const int64_t id = blockIdx.x;
+    const int seg = (int)(id % a.nseg);
+    const int64_t bh = id / a.nseg;
+    const int64_t b = bh / a.H;
+    const int h = (int)(bh % a.H);
+    const int R = a.R;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int c = lane % LPR, j = lane / LPR;
+
+    const int64_t t0 = seg * a.seglen;
+    const int64_t t1 = t0 + a.seglen < a.L ? t0 + a.seglen : a.L;
+    const int64_t sub = (t1 - t0 + NW - 1) / NW;
+    const int64_t w0 = t0 + wave * sub < t1 ? t0 + wave * sub : t1;
+    const int64_t w1 = w0 + sub < t1 ? w0 + sub : t1;
+
+    // angle at the start of the segment, for this lane's 4 pairs
+    float phi[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (a.seg_phi)
+            phi[q] = a.seg_phi[(bh * a.nseg + seg) * K + 4 * c + q];
+        else
+            phi[q] = a.phi_in ? wrap_angle(a.phi_in[bh * K + 4 * c + q]) : 0.0f;
+    }
+
+    // each wave sums the angle increments of its quarter; waves before it shift its start
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t t = w0 + j; t < w1; t += RPW) {
+        const int64_t row = (b * a.L + t) * a.H + h;
+        const float d = load_f32((const T*)a.dt + row);
+        float th[4];
+        load4((const T*)a.theta + row * K + 4 * c, th);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] += d * th[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        for (int m = LPR; m < 64; m <<= 1) acc[q] += shfl_xor(acc[q], m);
+    if (j == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wsum[wave][4 * c + q] = acc[q];
+    }
+    __syncthreads();
+    float start[4], total[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float s = 0.0f, tot = 0.0f;
+        for (int w = 0; w < NW; ++w) {
+            const float v = wsum[w][4 * c + q];
+            if (w < wave) s += v;
+            tot += v;
+        }
+        start[q] = wrap_angle(phi[q] + s);
+        total[q] = wrap_angle(phi[q] + tot);
+    }
+    if (seg == a.nseg - 1 && wave == 0 && j == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a.phi_out[bh * K + 4 * c + q] = total[q];
+    }
+
+    // per-lane constants: BCNorm weights for this lane's 8 columns
+    float wB[8], wC[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        wB[e] = a.normw_B ? a.normw_B[h * N + 8 * c + e] : 1.0f;
+        wC[e] = a.normw_C ? a.normw_C[h * N + 8 * c + e] : 1.0f;
+    }
+    const float invN = 1.0f / (float)N;
+
+    // walk the quarter: rows rho = (t - w0) * R + r, RPW rows per iteration
+    const int64_t nrows = (w1 - w0) * R;
+    int64_t t_next = w0;   // first step whose angle increment is not yet in phi_acc
+    float phi_acc[4] = {start[0], start[1], start[2], start[3]};
+    for (int64_t rho0 = 0; rho0 < nrows; rho0 += RPW) {
+        const int64_t rho = rho0 + j;
+        const bool valid = rho < nrows;
+        const int64_t my_t = w0 + (valid ? rho : nrows - 1) / R;
+        const int r = (int)((valid ? rho : nrows - 1) % R);
+        const int64_t last = rho0 + RPW < nrows ? rho0 + RPW - 1 : nrows - 1;
+        const int64_t t_last = w0 + last / R;
+        float my_phi[4] = {phi_acc[0], phi_acc[1], phi_acc[2], phi_acc[3]};
+        for (int64_t t = t_next; t <= t_last; ++t) {
+            const int64_t row = (b * a.L + t) * a.H + h;
+            const float d = load_f32((const T*)a.dt + row);
+            float th[4];
+            load4((const T*)a.theta + row * K + 4 * c, th);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) phi_acc[q] = wrap_angle(phi_acc[q] + d * th[q]);
+            if (t == my_t) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) my_phi[q] = phi_acc[q];
+            }
+        }
+        t_next = t_last + 1;
+
+        const int64_t off = (((b * a.L + my_t) * a.H + h) * R + r) * N + 8 * c;
+        float vb[8], vc[8];
+        load8((const T*)a.B + off, vb);
+        load8((const T*)a.C + off, vc);
+        if (a.bcnorm) {
+            float sb = 0.f, sc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sb += vb[e] * vb[e];
+                sc += vc[e] * vc[e];
+            }
+            for (int m = 1; m < LPR; m <<= 1) {
+                sb += shfl_xor(sb, m);
+                sc += shfl_xor(sc, m);
+            }
+            const float ib = rsqrtf(sb * invN + a.eps), ic = rsqrtf(sc * invN + a.eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                vb[e] *= ib * wB[e];
+                vc[e] *= ic * wC[e];
+            }
+        }
+        if (a.bias_B) {
+            float bb[8];
+            load8(a.bias_B + (h * R + r) * N + 8 * c, bb);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vb[e] += bb[e];
+        }
+        if (a.bias_C) {
+            float bc[8];
+            load8(a.bias_C + (h * R + r) * N + 8 * c, bc);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vc[e] += bc[e];
+        }
+        float ob[8], oc[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float s, co;
+            sincosf(my_phi[q], &s, &co);
+            ob[2 * q] = co * vb[2 * q] + s * vb[2 * q + 1];
+            ob[2 * q + 1] = -s * vb[2 * q] + co * vb[2 * q + 1];
+            oc[2 * q] = co * vc[2 * q] + s * vc[2 * q + 1];
+            oc[2 * q + 1] = -s * vc[2 * q] + co * vc[2 * q + 1];
+        }
+        if (valid) {
+            store8((T*)a.Bbar + off, ob);
+            store8((T*)a.Cbar + off, oc);
+        }
+    }
+}
+
+template <typename T, int N>
+hipError_t launch_n(const BcnormRopeArgs& a, hipStream_t s) {
+    const unsigned nbh = (unsigned)(a.b * a.H);
+    if (a.nseg > 1) {
+        hipLaunchKernelGGL((angle_partial_kernel<T, N>), dim3(nbh * a.nseg), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(angle_scan_kernel, dim3(nbh), dim3(N / 2 < 64 ? 64 : N / 2), 0, s, a);
+    }
+    // a single-wave workgroup when the segment has too few rows to share among four waves
+    if (a.seglen * a.R >= 4 * (512 / N))
+        hipLaunchKernelGGL((bcnorm_rope_kernel<T, N, 4>), dim3(nbh * a.nseg), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((bcnorm_rope_kernel<T, N, 1>), dim3(nbh * a.nseg), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const BcnormRopeArgs& a, hipStream_t s) {
+    switch (a.N) {
+        case 16: return launch_n<T, 16>(a, s);
+        case 32: return launch_n<T, 32>(a, s);
+        case 64: return launch_n<T, 64>(a, s);
+        case 128: return launch_n<T, 128>(a, s);
+        case 256: return launch_n<T, 256>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool bcnorm_rope_supported(int N, int R) {
+    return (N == 16 || N == 32 || N == 64 || N == 128 || N == 256) && R >= 1 && R <= 64;
+}
+
+int64_t bcnorm_rope_seglen() { return kSegLen; }
+
+hipError_t launch_bcnorm_rope(const BcnormRopeArgs& a, bool bf16_io, hipStream_t s) {
+    return bf16_io ? launch_t<bf16>(a, s) : launch_t<float>(a, s);
+}
+
+}  // namespace m3

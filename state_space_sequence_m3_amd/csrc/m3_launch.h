@@ -1,0 +1,79 @@
+// m3_launch.h -- argument blocks and launchers shared between the C-ABI layer and the kernels.
+// Shapes and pointers are validated by the C-ABI layer (api.hip) before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace m3 {
+
+struct DecodeArgs {
+    float* h;
+    const void* Bbar_prev;
+    const void* x_prev;
+    const void* x;
+    const void* Bbar;
+    const void* Cbar;
+    const void* dt;
+    const float* A;
+    const void* lam;
+    const float* w_out;
+    void* y;
+    int64_t b;
+    int H, N, P, R;
+};
+
+struct BcnormRopeArgs {
+    const void* B;
+    const void* C;
+    const void* dt;
+    const void* theta;
+    const float* normw_B;
+    const float* normw_C;
+    const float* bias_B;
+    const float* bias_C;
+    const float* phi_in;
+    float* seg_phi;       // [b, H, nseg, N/2] segment start angles (nseg > 1), else nullptr
+    void* Bbar;
+    void* Cbar;
+    float* phi_out;
+    int64_t b, L;
+    int H, N, R;
+    int64_t seglen;       // time steps per segment
+    int nseg;             // segments per (b, h)
+    int bcnorm;
+    float eps;
+};
+
+struct PrefillArgs {
+    const void* x;
+    const void* Bbar;
+    const void* Cbar;
+    const void* dt;
+    const float* A;
+    const void* lam;
+    const float* w_out;
+    const float* h_in;
+    const void* Bbar_prev;
+    const void* x_prev;
+    void* y;
+    float* h_out;
+    void* Bbar_last;
+    void* x_last;
+    int64_t b, L;
+    int H, N, P, R;
+    int Q;                // time steps per chunk; Q * R rows per chunk tile (16..64)
+};
+
+bool decode_supported(int N, int P, int R);
+hipError_t launch_decode(const DecodeArgs& a, bool bf16_io, hipStream_t s);
+
+bool bcnorm_rope_supported(int N, int R);
+int64_t bcnorm_rope_seglen();
+hipError_t launch_bcnorm_rope(const BcnormRopeArgs& a, bool bf16_io, hipStream_t s);
+
+bool prefill_supported(int N, int P, int R, int QR, bool bf16_io);
+hipError_t launch_prefill(const PrefillArgs& a, bool bf16_io, hipStream_t s);
+
+}  // namespace m3

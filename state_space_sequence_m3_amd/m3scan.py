@@ -1,0 +1,232 @@
+"""ctypes binding of libm3scan with the same entry-point names as the C ABI (include/m3scan.h).
+
+This module only marshals arguments: it checks tensor placement, dtype, shape and contiguity,
+allocates outputs and workspaces with torch when the caller does not pass them, passes raw
+device pointers and the current HIP stream, and turns a non-OK status into an exception.  Every
+step of the computation runs in the library's HIP kernels.  There is no fallback: if
+``libm3scan.so`` is not built, or cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libm3scan.so")
+
+M3_OK, M3_E_NULL, M3_E_DIMS, M3_E_ALIGN, M3_E_DTYPE = 0, 1, 2, 3, 4
+M3_E_UNSUPPORTED, M3_E_NODEVICE, M3_E_LAUNCH, M3_E_WORKSPACE, M3_E_ALIAS = 5, 6, 7, 8, 9
+STATUS_NAMES = {0: "M3_OK", 1: "M3_E_NULL", 2: "M3_E_DIMS", 3: "M3_E_ALIGN", 4: "M3_E_DTYPE",
+                5: "M3_E_UNSUPPORTED", 6: "M3_E_NODEVICE", 7: "M3_E_LAUNCH", 8: "M3_E_WORKSPACE",
+                9: "M3_E_ALIAS"}
+M3_F32, M3_BF16 = 0, 1
+M3_BCNORM = 1
+
+EXPORTED = ["m3_bcnorm_rope", "m3_bcnorm_rope_workspace_bytes", "m3_prefill",
+            "m3_prefill_workspace_bytes", "m3_decode_step", "m3_last_error", "m3_version"]
+
+
+class M3Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("rank", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("io", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("eps", ctypes.c_float)]
+
+
+class M3Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, str(status)), message))
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.c_void_p
+_DIMS = ctypes.POINTER(M3Dims)
+
+
+def load(path: str = LIB_PATH):
+    """Load libm3scan.so (once) and declare the C signatures.  Raises if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError("libm3scan.so is not built (%s); run "
+                                   "`python -m state_space_sequence_m3_amd.build`" % path)
+            lib = ctypes.CDLL(path)
+            lib.m3_bcnorm_rope.restype = ctypes.c_int
+            lib.m3_bcnorm_rope.argtypes = [_DIMS] + [_P] * 13 + [ctypes.c_size_t, _P]
+            lib.m3_bcnorm_rope_workspace_bytes.restype = ctypes.c_size_t
+            lib.m3_bcnorm_rope_workspace_bytes.argtypes = [_DIMS]
+            lib.m3_prefill.restype = ctypes.c_int
+            lib.m3_prefill.argtypes = [_DIMS] + [_P] * 15 + [ctypes.c_size_t, _P]
+            lib.m3_prefill_workspace_bytes.restype = ctypes.c_size_t
+            lib.m3_prefill_workspace_bytes.argtypes = [_DIMS]
+            lib.m3_decode_step.restype = ctypes.c_int
+            lib.m3_decode_step.argtypes = [_DIMS] + [_P] * 11 + [_P]
+            lib.m3_last_error.restype = ctypes.c_char_p
+            lib.m3_last_error.argtypes = []
+            lib.m3_version.restype = ctypes.c_char_p
+            lib.m3_version.argtypes = []
+            _lib = lib
+    return _lib
+
+
+def version() -> str:
+    return load().m3_version().decode()
+
+
+def last_error() -> str:
+    return load().m3_last_error().decode()
+
+
+def _check(status: int):
+    if status != M3_OK:
+        raise M3Error(status, last_error())
+
+
+def _io_code(dtype) -> int:
+    if dtype == torch.float32:
+        return M3_F32
+    if dtype == torch.bfloat16:
+        return M3_BF16
+    raise ValueError("io tensors must be float32 or bfloat16, got %s" % dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _tensor(t, name, shape, dtype, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def make_dims(batch, seqlen, nheads, headdim, dstate, rank, chunk=0, io=M3_BF16, bcnorm=True,
+              eps=1e-5) -> M3Dims:
+    return M3Dims(batch, seqlen, nheads, headdim, dstate, rank, chunk, io,
+                  M3_BCNORM if bcnorm else 0, eps)
+
+
+def bcnorm_rope_workspace_bytes(dims: M3Dims) -> int:
+    return int(load().m3_bcnorm_rope_workspace_bytes(ctypes.byref(dims)))
+
+
+def prefill_workspace_bytes(dims: M3Dims) -> int:
+    return int(load().m3_prefill_workspace_bytes(ctypes.byref(dims)))
+
+
+def m3_bcnorm_rope(B, C, dt, theta, normw_B=None, normw_C=None, bias_B=None, bias_C=None,
+                   phi_in=None, Bbar=None, Cbar=None, phi_out=None, bcnorm=True, eps=1e-5,
+                   workspace=None, stream=None):
+    """BCNorm + bias + cumulative rotation.  B, C: [b, L, H, R, N]; returns (Bbar, Cbar, phi_out)."""
+    lib = load()
+    b, L, H, R, N = B.shape
+    dev, io = B.device, B.dtype
+    f32 = torch.float32
+    _tensor(B, "B", (b, L, H, R, N), io, dev)
+    _tensor(C, "C", (b, L, H, R, N), io, dev)
+    _tensor(dt, "dt", (b, L, H), io, dev)
+    _tensor(theta, "theta", (b, L, H, N // 2), io, dev)
+    _tensor(normw_B, "normw_B", (H, N), f32, dev)
+    _tensor(normw_C, "normw_C", (H, N), f32, dev)
+    _tensor(bias_B, "bias_B", (H, R, N), f32, dev)
+    _tensor(bias_C, "bias_C", (H, R, N), f32, dev)
+    _tensor(phi_in, "phi_in", (b, H, N // 2), f32, dev)
+    Bbar = torch.empty_like(B) if Bbar is None else _tensor(Bbar, "Bbar", B.shape, io, dev)
+    Cbar = torch.empty_like(C) if Cbar is None else _tensor(Cbar, "Cbar", C.shape, io, dev)
+    if phi_out is None:
+        phi_out = torch.empty((b, H, N // 2), dtype=f32, device=dev)
+    _tensor(phi_out, "phi_out", (b, H, N // 2), f32, dev)
+    dims = make_dims(b, L, H, 0, N, R, 0, _io_code(io), bcnorm, eps)
+    need = bcnorm_rope_workspace_bytes(dims)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.m3_bcnorm_rope(ctypes.byref(dims), _ptr(B), _ptr(C), _ptr(dt), _ptr(theta),
+                              _ptr(normw_B), _ptr(normw_C), _ptr(bias_B), _ptr(bias_C),
+                              _ptr(phi_in), _ptr(Bbar), _ptr(Cbar), _ptr(phi_out),
+                              _ptr(workspace), ws_bytes, _stream(stream)))
+    return Bbar, Cbar, phi_out
+
+
+def m3_prefill(x, Bbar, Cbar, dt, A, lam, w_out=None, h_in=None, Bbar_prev=None, x_prev=None,
+               y=None, h_out=None, Bbar_last=None, x_last=None, chunk=0, workspace=None,
+               stream=None):
+    """Chunked scan.  x: [b, L, H, R, P]; Bbar, Cbar: [b, L, H, R, N].  Returns (y, h_out)."""
+    lib = load()
+    b, L, H, R, P = x.shape
+    N = Bbar.shape[-1]
+    dev, io = x.device, x.dtype
+    f32 = torch.float32
+    _tensor(Bbar, "Bbar", (b, L, H, R, N), io, dev)
+    _tensor(Cbar, "Cbar", (b, L, H, R, N), io, dev)
+    _tensor(dt, "dt", (b, L, H), io, dev)
+    _tensor(lam, "lam", (b, L, H), io, dev)
+    _tensor(A, "A", (H,), f32, dev)
+    _tensor(w_out, "w_out", (H, R, P), f32, dev)
+    _tensor(h_in, "h_in", (b, H, N, P), f32, dev)
+    _tensor(Bbar_prev, "Bbar_prev", (b, H, R, N), io, dev)
+    _tensor(x_prev, "x_prev", (b, H, R, P), io, dev)
+    yshape = (b, L, H, P) if w_out is not None else (b, L, H, R, P)
+    y = torch.empty(yshape, dtype=io, device=dev) if y is None else _tensor(y, "y", yshape, io, dev)
+    if h_out is None:
+        h_out = torch.empty((b, H, N, P), dtype=f32, device=dev)
+    _tensor(h_out, "h_out", (b, H, N, P), f32, dev)
+    _tensor(Bbar_last, "Bbar_last", (b, H, R, N), io, dev)
+    _tensor(x_last, "x_last", (b, H, R, P), io, dev)
+    dims = make_dims(b, L, H, P, N, R, chunk, _io_code(io))
+    need = prefill_workspace_bytes(dims)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.m3_prefill(ctypes.byref(dims), _ptr(x), _ptr(Bbar), _ptr(Cbar), _ptr(dt), _ptr(A),
+                          _ptr(lam), _ptr(w_out), _ptr(h_in), _ptr(Bbar_prev), _ptr(x_prev),
+                          _ptr(y), _ptr(h_out), _ptr(Bbar_last), _ptr(x_last), _ptr(workspace),
+                          ws_bytes, _stream(stream)))
+    return y, h_out
+
+
+def m3_decode_step(h, Bbar_prev, x_prev, x, Bbar, Cbar, dt, A, lam, w_out=None, y=None,
+                   stream=None):
+    """One decode token, state h [b, H, N, P] updated in place.  Returns y."""
+    lib = load()
+    b, H, N, P = h.shape
+    R = x.shape[2]
+    dev, io = h.device, x.dtype
+    f32 = torch.float32
+    _tensor(h, "h", (b, H, N, P), f32, dev)
+    for name, t, shp in (("Bbar_prev", Bbar_prev, (b, H, R, N)), ("x_prev", x_prev, (b, H, R, P)),
+                         ("x", x, (b, H, R, P)), ("Bbar", Bbar, (b, H, R, N)),
+                         ("Cbar", Cbar, (b, H, R, N)), ("dt", dt, (b, H)), ("lam", lam, (b, H))):
+        _tensor(t, name, shp, io, dev)
+    _tensor(A, "A", (H,), f32, dev)
+    _tensor(w_out, "w_out", (H, R, P), f32, dev)
+    yshape = (b, H, P) if w_out is not None else (b, H, R, P)
+    y = torch.empty(yshape, dtype=io, device=dev) if y is None else _tensor(y, "y", yshape, io, dev)
+    dims = make_dims(b, 1, H, P, N, R, 0, _io_code(io))
+    _check(lib.m3_decode_step(ctypes.byref(dims), _ptr(h), _ptr(Bbar_prev), _ptr(x_prev), _ptr(x),
+                              _ptr(Bbar), _ptr(Cbar), _ptr(dt), _ptr(A), _ptr(lam), _ptr(w_out),
+                              _ptr(y), _stream(stream)))
+    return y

@@ -1,0 +1,361 @@
+"""GPU parity of libm3scan's three calls against the fp64 oracle, on small seeded inputs that span
+several chunks/segments and end in a ragged tail.  Every call goes through the C ABI (via the
+ctypes binding).  Tolerances are those of gpu_util.TOL."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, angle_err, per_head_rel_err, rel_err, to_dev, to_np
+from state_space_sequence_m3_amd import inputs, m3scan
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _wl(io, b, L, H, P, N, R, Q, bcnorm=True, bias=True, mix=False, theta_std=1.0):
+    return inputs.Workload("case", b, L, H, P, N, R, Q, io, bcnorm, bias, mix, theta_std)
+
+
+def _scan_inputs(w, seed, carry):
+    """Seeded prefill inputs where Bbar, Cbar are drawn directly (prefill in isolation)."""
+    inp = inputs.make_prefill_inputs(w, seed, "cpu", carry=carry)
+    inp["Bbar"] = inp.pop("B")
+    inp["Cbar"] = inp.pop("C")
+    return inp
+
+
+# ---------------------------------------------------------------------------------------------
+# m3_bcnorm_rope
+# ---------------------------------------------------------------------------------------------
+BCNORM_CASES = [
+    # io, b, L, H, N, R, bcnorm, normw, phi_in
+    ("f32", 1, 64, 1, 16, 1, False, False, False),        # the tiny SISO fp32 workload
+    ("f32", 2, 37, 3, 128, 4, True, True, True),
+    ("bf16", 2, 75, 3, 128, 1, True, True, True),
+    ("bf16", 1, 50, 2, 128, 4, True, False, True),
+    ("bf16", 1, 1300, 2, 128, 1, True, False, True),     # three segments, ragged tail
+    ("f32", 1, 1100, 2, 64, 2, True, True, False),       # three segments
+    ("bf16", 3, 1, 4, 128, 4, True, True, True),          # decode-shaped (L = 1)
+    ("f32", 2, 9, 2, 256, 1, True, True, True),
+    ("f32", 2, 9, 2, 32, 3, True, True, True),            # R does not divide the row group
+]
+
+
+@pytest.mark.parametrize("case", BCNORM_CASES, ids=lambda c: "%s-b%d-L%d-H%d-N%d-R%d" % c[:6])
+def test_bcnorm_rope_parity(case):
+    io, b, L, H, N, R, bcnorm, normw, with_phi = case
+    w = _wl(io, b, L, H, 16, N, R, 16, bcnorm=bcnorm, bias=True)
+    inp = inputs.make_prefill_inputs(w, seed=100 + L, normw=normw, carry=with_phi)
+    d = to_dev(inp, DEV)
+    Bb, Cb, phi = m3scan.m3_bcnorm_rope(d["B"], d["C"], d["dt"], d["theta"], d["normw_B"],
+                                        d["normw_C"], d["bias_B"], d["bias_C"], d.get("phi_in"),
+                                        bcnorm=bcnorm, eps=1e-5)
+    torch.cuda.synchronize()
+    rB, rC, rphi = oracle.bcnorm_rope(inp["B"], inp["C"], inp["dt"], inp["theta"], inp["normw_B"],
+                                      inp["normw_C"], inp["bias_B"], inp["bias_C"],
+                                      inp.get("phi_in"), bcnorm=bcnorm, eps=1e-5)
+    tol = TOL[io]
+    assert rel_err(Bb, rB) <= tol
+    assert rel_err(Cb, rC) <= tol
+    assert angle_err(phi, rphi) <= (1e-4 if io == "f32" else 2e-3) * max(1.0, math.sqrt(L))
+
+
+def test_bcnorm_rope_phi_in_place():
+    """Decode carries the angle in place: phi_out may be the phi_in buffer."""
+    w = _wl("bf16", 4, 1, 3, 16, 128, 4, 16)
+    inp = inputs.make_prefill_inputs(w, seed=7, carry=True)
+    d = to_dev(inp, DEV)
+    phi = d["phi_in"].clone()
+    m3scan.m3_bcnorm_rope(d["B"], d["C"], d["dt"], d["theta"], None, None, d["bias_B"],
+                          d["bias_C"], phi, phi_out=phi)
+    torch.cuda.synchronize()
+    _, _, rphi = oracle.bcnorm_rope(inp["B"], inp["C"], inp["dt"], inp["theta"], None, None,
+                                    inp["bias_B"], inp["bias_C"], inp["phi_in"])
+    assert angle_err(phi, rphi) <= 1e-5
+
+
+# ---------------------------------------------------------------------------------------------
+# m3_prefill
+# ---------------------------------------------------------------------------------------------
+PREFILL_CASES = [
+    # io, b, L, H, P, N, R, Q, mix, carry
+    ("f32", 1, 64, 1, 16, 16, 1, 16, False, False),       # the tiny SISO fp32 workload
+    ("f32", 1, 64, 1, 16, 16, 1, 16, False, True),
+    ("f32", 2, 83, 2, 64, 128, 1, 32, False, True),       # fp32 at full width, ragged tail
+    ("f32", 1, 45, 2, 64, 64, 4, 8, True, True),
+    ("bf16", 2, 200, 2, 64, 128, 1, 64, False, False),    # SISO layer shape, 4 chunks, ragged
+    ("bf16", 2, 200, 2, 64, 128, 1, 64, False, True),
+    ("bf16", 1, 150, 3, 64, 128, 4, 16, True, True),      # MIMO R=4 with output mixing
+    ("bf16", 1, 150, 3, 64, 128, 4, 16, False, True),     # MIMO unmixed
+    ("bf16", 2, 77, 2, 64, 64, 2, 32, True, True),
+    ("bf16", 1, 70, 2, 16, 16, 1, 16, False, True),
+    ("bf16", 1, 33, 2, 64, 128, 16, 4, True, True),
+    ("bf16", 1, 1, 2, 64, 128, 4, 16, True, True),        # a single step
+]
+
+
+def _run_prefill(d, chunk, mix, carry, y=None, h_out=None):
+    return m3scan.m3_prefill(d["x"], d["Bbar"], d["Cbar"], d["dt"], d["A"], d["lam"],
+                             d["w_out"] if mix else None, d.get("h_in") if carry else None,
+                             d.get("Bbar_prev") if carry else None,
+                             d.get("x_prev") if carry else None, y=y, h_out=h_out, chunk=chunk)
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES,
+                         ids=lambda c: "%s-b%d-L%d-H%d-P%d-N%d-R%d-Q%d-mix%d-carry%d" % c)
+def test_prefill_parity(case):
+    io, b, L, H, P, N, R, Q, mix, carry = case
+    w = _wl(io, b, L, H, P, N, R, Q, mix=mix)
+    inp = _scan_inputs(w, seed=200 + L + R, carry=carry)
+    d = to_dev(inp, DEV)
+    y, h = _run_prefill(d, Q, mix, carry)
+    torch.cuda.synchronize()
+    ry, rh = oracle.scan(inp["x"], inp["Bbar"], inp["Cbar"], inp["dt"], inp["A"], inp["lam"],
+                         inp["w_out"] if mix else None, inp.get("h_in") if carry else None,
+                         inp.get("Bbar_prev") if carry else None,
+                         inp.get("x_prev") if carry else None)
+    tol = TOL[io]
+    assert rel_err(y, ry) <= tol
+    assert rel_err(h, rh) <= tol
+    assert per_head_rel_err(h, rh, 3) <= tol
+
+
+def test_prefill_writes_every_output():
+    """Outputs pre-filled with NaN: every element must be overwritten."""
+    w = _wl("bf16", 2, 150, 2, 64, 128, 4, 16, mix=True)
+    d = to_dev(_scan_inputs(w, 5, carry=True), DEV)
+    y = torch.full((2, 150, 2, 64), float("nan"), dtype=torch.bfloat16, device=DEV)
+    h = torch.full((2, 2, 128, 64), float("nan"), dtype=torch.float32, device=DEV)
+    Bl = torch.full((2, 2, 4, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    xl = torch.full((2, 2, 4, 64), float("nan"), dtype=torch.bfloat16, device=DEV)
+    m3scan.m3_prefill(d["x"], d["Bbar"], d["Cbar"], d["dt"], d["A"], d["lam"], d["w_out"],
+                      d["h_in"], d["Bbar_prev"], d["x_prev"], y=y, h_out=h, Bbar_last=Bl,
+                      x_last=xl, chunk=16)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all() and torch.isfinite(h).all()
+    assert torch.equal(Bl, d["Bbar"][:, -1]) and torch.equal(xl, d["x"][:, -1])
+
+
+def test_prefill_guard_canaries():
+    """Outputs embedded in larger buffers: the bytes around them must stay untouched."""
+    w = _wl("bf16", 1, 130, 2, 64, 128, 1, 64)
+    d = to_dev(_scan_inputs(w, 6, carry=False), DEV)
+    pad = 4096
+    ny, nh = 130 * 2 * 64, 2 * 128 * 64
+    ybuf = torch.full((ny + 2 * pad,), 7.0, dtype=torch.bfloat16, device=DEV)
+    hbuf = torch.full((nh + 2 * pad,), 7.0, dtype=torch.float32, device=DEV)
+    y = ybuf[pad:pad + ny].view(1, 130, 2, 64)
+    h = hbuf[pad:pad + nh].view(1, 2, 128, 64)
+    _run_prefill(d, 64, False, False, y=y, h_out=h)
+    torch.cuda.synchronize()
+    assert (ybuf[:pad] == 7.0).all() and (ybuf[pad + ny:] == 7.0).all()
+    assert (hbuf[:pad] == 7.0).all() and (hbuf[pad + nh:] == 7.0).all()
+
+
+def test_prefill_chunk_size_invariance():
+    """The chunk length is a schedule choice: Q = 16, 32, 48, 64 give the oracle's result."""
+    w = _wl("bf16", 1, 190, 2, 64, 128, 1, 64)
+    inp = _scan_inputs(w, 8, carry=True)
+    d = to_dev(inp, DEV)
+    ry, rh = oracle.scan(inp["x"], inp["Bbar"], inp["Cbar"], inp["dt"], inp["A"], inp["lam"], None,
+                         inp["h_in"], inp["Bbar_prev"], inp["x_prev"])
+    for Q in (16, 32, 48, 64):
+        y, h = _run_prefill(d, Q, False, True)
+        torch.cuda.synchronize()
+        assert rel_err(y, ry) <= TOL["bf16"], Q
+        assert rel_err(h, rh) <= TOL["bf16"], Q
+
+
+def test_prefill_split_carry():
+    """Prefill of [0, t1) then [t1, L) with the carried state equals the oracle over [0, L)."""
+    w = _wl("bf16", 2, 211, 2, 64, 128, 4, 16, mix=True)
+    inp = _scan_inputs(w, 9, carry=True)
+    d = to_dev(inp, DEV)
+    t1 = 97
+    seq = ("x", "Bbar", "Cbar", "dt", "lam")
+    first = {k: (v[:, :t1].contiguous() if k in seq else v) for k, v in d.items()}
+    second = {k: (v[:, t1:].contiguous() if k in seq else v) for k, v in d.items()}
+    b, H, R, N, P = 2, 2, 4, 128, 64
+    Bl = torch.empty((b, H, R, N), dtype=torch.bfloat16, device=DEV)
+    xl = torch.empty((b, H, R, P), dtype=torch.bfloat16, device=DEV)
+    y1, h1 = m3scan.m3_prefill(first["x"], first["Bbar"], first["Cbar"], first["dt"], first["A"],
+                               first["lam"], first["w_out"], first["h_in"], first["Bbar_prev"],
+                               first["x_prev"], Bbar_last=Bl, x_last=xl, chunk=16)
+    y2, h2 = m3scan.m3_prefill(second["x"], second["Bbar"], second["Cbar"], second["dt"],
+                               second["A"], second["lam"], second["w_out"], h1, Bl, xl, chunk=16)
+    torch.cuda.synchronize()
+    ry, rh = oracle.scan(inp["x"], inp["Bbar"], inp["Cbar"], inp["dt"], inp["A"], inp["lam"],
+                         inp["w_out"], inp["h_in"], inp["Bbar_prev"], inp["x_prev"])
+    assert rel_err(torch.cat([y1, y2], 1), ry) <= TOL["bf16"]
+    assert rel_err(h2, rh) <= TOL["bf16"]
+
+
+def test_prefill_in_place_state():
+    """h_out may be the h_in buffer."""
+    w = _wl("f32", 1, 40, 2, 64, 128, 1, 16)
+    inp = _scan_inputs(w, 10, carry=True)
+    d = to_dev(inp, DEV)
+    h = d["h_in"].clone()
+    y, _ = m3scan.m3_prefill(d["x"], d["Bbar"], d["Cbar"], d["dt"], d["A"], d["lam"], None, h,
+                             d["Bbar_prev"], d["x_prev"], h_out=h, chunk=16)
+    torch.cuda.synchronize()
+    ry, rh = oracle.scan(inp["x"], inp["Bbar"], inp["Cbar"], inp["dt"], inp["A"], inp["lam"], None,
+                         inp["h_in"], inp["Bbar_prev"], inp["x_prev"])
+    assert rel_err(h, rh) <= TOL["f32"] and rel_err(y, ry) <= TOL["f32"]
+
+
+def test_prefill_empty_sequence():
+    """L = 0: the carried state passes through; no y is produced."""
+    w = _wl("bf16", 2, 0, 2, 64, 128, 4, 16, mix=True)
+    d = to_dev(_scan_inputs(w, 11, carry=True), DEV)
+    Bl = torch.empty((2, 2, 4, 128), dtype=torch.bfloat16, device=DEV)
+    xl = torch.empty((2, 2, 4, 64), dtype=torch.bfloat16, device=DEV)
+    y, h = m3scan.m3_prefill(d["x"], d["Bbar"], d["Cbar"], d["dt"], d["A"], d["lam"], d["w_out"],
+                             d["h_in"], d["Bbar_prev"], d["x_prev"], Bbar_last=Bl, x_last=xl,
+                             chunk=16)
+    torch.cuda.synchronize()
+    assert y.numel() == 0
+    assert torch.equal(h, d["h_in"]) and torch.equal(Bl, d["Bbar_prev"]) and torch.equal(xl, d["x_prev"])
+
+
+def test_prefill_empty_batch():
+    w = _wl("bf16", 0, 64, 2, 64, 128, 1, 64)
+    d = to_dev(_scan_inputs(w, 12, carry=False), DEV)
+    y, h = _run_prefill(d, 64, False, False)
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and h.numel() == 0
+
+
+def test_unsupported_shape_is_rejected():
+    w = _wl("bf16", 1, 32, 1, 32, 128, 1, 32)
+    d = to_dev(_scan_inputs(w, 13, carry=False), DEV)
+    with pytest.raises(m3scan.M3Error) as e:
+        _run_prefill(d, 32, False, False)
+    assert e.value.status == m3scan.M3_E_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------------------------
+# the layer core (rotation + scan) and decode
+# ---------------------------------------------------------------------------------------------
+def _layer_gpu(d, w, chunk):
+    Bb, Cb, phi = m3scan.m3_bcnorm_rope(d["B"], d["C"], d["dt"], d["theta"], d["normw_B"],
+                                        d["normw_C"], d["bias_B"], d["bias_C"], d.get("phi_in"),
+                                        bcnorm=w.bcnorm)
+    y, h = m3scan.m3_prefill(d["x"], Bb, Cb, d["dt"], d["A"], d["lam"], d["w_out"], d.get("h_in"),
+                             d.get("Bbar_prev"), d.get("x_prev"), chunk=chunk)
+    return y, h, phi
+
+
+@pytest.mark.parametrize("name", ["tiny_siso_f32", "siso", "mimo"])
+def test_layer_core_parity(name):
+    if name == "tiny_siso_f32":
+        w = inputs.WORKLOADS["tiny_siso_f32"]
+    elif name == "siso":
+        w = inputs.WORKLOADS["siso_b8_l2048"].with_(batch=2, seqlen=333, nheads=3)
+    else:
+        w = inputs.WORKLOADS["mimo4_b8_l2048"].with_(batch=1, seqlen=333, nheads=3)
+    inp = inputs.make_prefill_inputs(w, seed=21, normw=True, carry=True)
+    d = to_dev(inp, DEV)
+    y, h, phi = _layer_gpu(d, w, w.chunk)
+    torch.cuda.synchronize()
+    ref = oracle.layer(inp, bcnorm=w.bcnorm, mix=w.mix)
+    assert rel_err(y, ref["y"]) <= TOL[w.io]
+    assert rel_err(h, ref["h_out"]) <= TOL[w.io]
+    assert angle_err(phi, ref["phi_out"]) <= 1e-3
+
+
+def _decode_run(w, steps, seed, mix):
+    """GPU: steps x (m3_bcnorm_rope L=1 + m3_decode_step) with buffer swapping; oracle alongside."""
+    dinp = inputs.make_decode_inputs(w, seed, steps)
+    d = to_dev({k: v for k, v in dinp.items() if k not in ("tokens", "state")}, DEV)
+    toks = to_dev(dinp["tokens"], DEV)
+    st = to_dev(dinp["state"], DEV)
+    h = st["h"].clone()
+    phi = st["phi"].clone()
+    Bprev, xprev = st["Bbar_prev"].clone(), st["x_prev"].clone()
+    Bcur = torch.empty_like(Bprev)
+    Ccur = torch.empty_like(Bprev)
+    ys = []
+    for s in range(steps):
+        B = toks["B"][s].unsqueeze(1)
+        C = toks["C"][s].unsqueeze(1)
+        m3scan.m3_bcnorm_rope(B, C, toks["dt"][s].unsqueeze(1), toks["theta"][s].unsqueeze(1),
+                              None, None, d["bias_B"], d["bias_C"], phi,
+                              Bbar=Bcur.unsqueeze(1), Cbar=Ccur.unsqueeze(1), phi_out=phi)
+        x = toks["x"][s]
+        y = m3scan.m3_decode_step(h, Bprev, xprev, x, Bcur, Ccur, toks["dt"][s], d["A"],
+                                  toks["lam"][s], d["w_out"] if mix else None)
+        ys.append(y)
+        Bprev, Bcur = Bcur, Bprev
+        xprev = x
+    torch.cuda.synchronize()
+    # oracle
+    consts = {"A": dinp["A"], "bias_B": dinp["bias_B"], "bias_C": dinp["bias_C"],
+              "w_out": dinp["w_out"]}
+    state = {"h": dinp["state"]["h"], "phi": dinp["state"]["phi"],
+             "Bbar_prev": dinp["state"]["Bbar_prev"], "x_prev": dinp["state"]["x_prev"]}
+    rys = []
+    for s in range(steps):
+        tok = {k: dinp["tokens"][k][s] for k in ("x", "B", "C", "dt", "lam", "theta")}
+        ry, state = oracle.decode_step(state, tok, consts, mix=mix)
+        rys.append(ry)
+    return ys, h, phi, rys, state
+
+
+@pytest.mark.parametrize("R", [1, 4])
+def test_decode_parity(R):
+    w = inputs.WORKLOADS["decode_b128_r%d" % R].with_(batch=3, nheads=5)
+    ys, h, phi, rys, state = _decode_run(w, 12, seed=31 + R, mix=w.mix)
+    for y, ry in zip(ys, rys):
+        assert rel_err(y, ry) <= TOL["bf16"]
+    assert rel_err(h, state["h"]) <= TOL["bf16"]
+    assert angle_err(phi, state["phi"]) <= 1e-4
+
+
+def test_decode_fp32_parity():
+    w = inputs.WORKLOADS["decode_b128_r1"].with_(batch=2, nheads=3, io="f32")
+    ys, h, phi, rys, state = _decode_run(w, 10, seed=41, mix=False)
+    for y, ry in zip(ys, rys):
+        assert rel_err(y, ry) <= TOL["f32"]
+    assert rel_err(h, state["h"]) <= TOL["f32"]
+
+
+def test_prefill_then_decode_continues_the_sequence():
+    """prefill(L - k) followed by k decode steps equals the oracle's layer over L steps."""
+    w = inputs.WORKLOADS["mimo4_b8_l2048"].with_(batch=1, seqlen=100, nheads=2)
+    inp = inputs.make_prefill_inputs(w, seed=51, carry=False)
+    d = to_dev(inp, DEV)
+    k = 5
+    L0 = w.seqlen - k
+    seq = ("x", "B", "C", "dt", "lam", "theta")
+    head = {kk: (v[:, :L0].contiguous() if kk in seq else v) for kk, v in d.items()}
+    Bb, Cb, phi = m3scan.m3_bcnorm_rope(head["B"], head["C"], head["dt"], head["theta"], None, None,
+                                        d["bias_B"], d["bias_C"])
+    Bl = torch.empty((1, 2, 4, 128), dtype=torch.bfloat16, device=DEV)
+    xl = torch.empty((1, 2, 4, 64), dtype=torch.bfloat16, device=DEV)
+    y0, h = m3scan.m3_prefill(head["x"], Bb, Cb, head["dt"], d["A"], head["lam"], d["w_out"],
+                              Bbar_last=Bl, x_last=xl, chunk=16)
+    ys = [y0]
+    Bprev, xprev = Bl, xl
+    for s in range(L0, w.seqlen):
+        Bc, Cc, phi = m3scan.m3_bcnorm_rope(d["B"][:, s:s + 1].contiguous(),
+                                            d["C"][:, s:s + 1].contiguous(),
+                                            d["dt"][:, s:s + 1].contiguous(),
+                                            d["theta"][:, s:s + 1].contiguous(), None, None,
+                                            d["bias_B"], d["bias_C"], phi, phi_out=phi)
+        x = d["x"][:, s].contiguous()
+        y = m3scan.m3_decode_step(h, Bprev, xprev, x, Bc[:, 0].contiguous(), Cc[:, 0].contiguous(),
+                                  d["dt"][:, s].contiguous(), d["A"], d["lam"][:, s].contiguous(),
+                                  d["w_out"])
+        ys.append(y.unsqueeze(1))
+        Bprev, xprev = Bc[:, 0].contiguous(), x
+    torch.cuda.synchronize()
+    ref = oracle.layer(inp, mix=True)
+    assert rel_err(torch.cat(ys, 1), ref["y"]) <= TOL["bf16"]
+    assert rel_err(h, ref["h_out"]) <= TOL["bf16"]

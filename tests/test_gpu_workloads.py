@@ -1,0 +1,152 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py times.
+
+The GPU runs the whole batch; the fp64 oracle recomputes a few sampled (batch, head) pairs from
+the same inputs (every (batch, head) is independent, so a sampled pair is checked exactly, not
+approximately).  Inputs are drawn on the device with a seeded generator; the sampled slices are
+copied to the host for the oracle.
+"""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, angle_err, rel_err, to_np
+from state_space_sequence_m3_amd import inputs, m3scan
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+SEQ_KEYS = ("x", "B", "C", "dt", "lam", "theta")
+
+
+def _slice_pair(inp, bi, hi):
+    """Host copy of one (batch, head) pair's prefill inputs, with per-head constants."""
+    out = {}
+    for k, v in inp.items():
+        if v is None:
+            out[k] = None
+        elif k in SEQ_KEYS:
+            out[k] = v[bi:bi + 1, :, hi:hi + 1].cpu()
+        elif k == "A":
+            out[k] = v[hi:hi + 1].cpu()
+        elif k in ("bias_B", "bias_C", "w_out", "normw_B", "normw_C"):
+            out[k] = v[hi:hi + 1].cpu()
+        else:  # carried state [b, H, ...]
+            out[k] = v[bi:bi + 1, hi:hi + 1].cpu()
+    return out
+
+
+def _layer(d, w):
+    Bb, Cb, phi = m3scan.m3_bcnorm_rope(d["B"], d["C"], d["dt"], d["theta"], d["normw_B"],
+                                        d["normw_C"], d["bias_B"], d["bias_C"], d.get("phi_in"),
+                                        bcnorm=w.bcnorm)
+    y, h = m3scan.m3_prefill(d["x"], Bb, Cb, d["dt"], d["A"], d["lam"], d["w_out"] if w.mix else None,
+                             d.get("h_in"), d.get("Bbar_prev"), d.get("x_prev"), chunk=w.chunk)
+    return Bb, Cb, y, h, phi
+
+
+@pytest.mark.parametrize("name,pairs", [
+    ("siso_b8_l2048", [(0, 0), (3, 17), (7, 63)]),
+    ("mimo4_b8_l2048", [(0, 5), (6, 40)]),
+])
+def test_prefill_workload_sampled(name, pairs):
+    w = inputs.WORKLOADS[name]
+    print("workload", name, flush=True)
+    inp = inputs.make_prefill_inputs(w, seed=1, device=DEV)
+    Bb, Cb, y, h, phi = _layer(inp, w)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all() and torch.isfinite(h).all()
+    for bi, hi in pairs:
+        ref = oracle.layer(_slice_pair(inp, bi, hi), bcnorm=w.bcnorm, mix=w.mix)
+        ys = y[bi:bi + 1, :, hi:hi + 1]
+        assert rel_err(ys, ref["y"]) <= TOL[w.io], (bi, hi)
+        assert rel_err(h[bi:bi + 1, hi:hi + 1], ref["h_out"]) <= TOL[w.io], (bi, hi)
+        assert angle_err(phi[bi:bi + 1, hi:hi + 1], ref["phi_out"]) <= 1e-3
+
+
+def _decode_steps(w, dinp, steps, mix, h, phi, Bprev, xprev, consts_dev, toks):
+    Bcur = torch.empty_like(Bprev)
+    Ccur = torch.empty_like(Bprev)
+    ys = []
+    for s in range(steps):
+        m3scan.m3_bcnorm_rope(toks["B"][s].unsqueeze(1), toks["C"][s].unsqueeze(1),
+                              toks["dt"][s].unsqueeze(1), toks["theta"][s].unsqueeze(1), None, None,
+                              consts_dev["bias_B"], consts_dev["bias_C"], phi,
+                              Bbar=Bcur.unsqueeze(1), Cbar=Ccur.unsqueeze(1), phi_out=phi)
+        y = m3scan.m3_decode_step(h, Bprev, xprev, toks["x"][s], Bcur, Ccur, toks["dt"][s],
+                                  consts_dev["A"], toks["lam"][s],
+                                  consts_dev["w_out"] if mix else None)
+        ys.append(y)
+        Bprev, Bcur = Bcur, Bprev
+        xprev = toks["x"][s]
+    return ys, Bprev, xprev
+
+
+@pytest.mark.parametrize("name,pairs", [
+    ("decode_b128_r1", [(0, 0), (77, 31), (127, 63)]),
+    ("decode_b128_r4", [(5, 2), (120, 60)]),
+])
+def test_decode_workload_sampled(name, pairs):
+    w = inputs.WORKLOADS[name]
+    print("workload", name, flush=True)
+    steps = w.decode_steps
+    dinp = inputs.make_decode_inputs(w, seed=3, steps=steps, device=DEV)
+    st = dinp["state"]
+    h = st["h"].clone()
+    phi = st["phi"].clone()
+    ys, _, _ = _decode_steps(w, dinp, steps, w.mix, h, phi, st["Bbar_prev"].clone(),
+                             st["x_prev"].clone(), dinp, dinp["tokens"])
+    torch.cuda.synchronize()
+    for bi, hi in pairs:
+        consts = {"A": dinp["A"][hi:hi + 1].cpu(), "bias_B": dinp["bias_B"][hi:hi + 1].cpu(),
+                  "bias_C": dinp["bias_C"][hi:hi + 1].cpu(),
+                  "w_out": dinp["w_out"][hi:hi + 1].cpu() if w.mix else None}
+        state = {k: st[k][bi:bi + 1, hi:hi + 1].cpu() for k in ("phi", "Bbar_prev", "x_prev")}
+        state["h"] = st["h"][bi:bi + 1, hi:hi + 1].cpu()
+        worst = 0.0
+        for s in range(steps):
+            tok = {k: dinp["tokens"][k][s, bi:bi + 1, hi:hi + 1].cpu() for k in SEQ_KEYS}
+            ry, state = oracle.decode_step(state, tok, consts, mix=w.mix)
+            worst = max(worst, rel_err(ys[s][bi:bi + 1, hi:hi + 1], ry))
+        assert worst <= TOL[w.io], (bi, hi, worst)
+        assert rel_err(h[bi:bi + 1, hi:hi + 1], state["h"]) <= TOL[w.io]
+        assert angle_err(phi[bi:bi + 1, hi:hi + 1], state["phi"]) <= 1e-3
+
+
+def test_long_context_prefill_then_decode_sampled():
+    """b=1, L=16384, MIMO R=4, theta ~ N(0, pi^2); then 512 decode steps from the final state."""
+    w = inputs.WORKLOADS["long_mimo4_b1_l16384"]
+    print("workload", w.name, flush=True)
+    inp = inputs.make_prefill_inputs(w, seed=4, device=DEV)
+    b, H, R, N, P = w.batch, w.nheads, w.rank, w.dstate, w.headdim
+    Bb, Cb, phi = m3scan.m3_bcnorm_rope(inp["B"], inp["C"], inp["dt"], inp["theta"], None, None,
+                                        inp["bias_B"], inp["bias_C"])
+    Bl = torch.empty((b, H, R, N), dtype=torch.bfloat16, device=DEV)
+    xl = torch.empty((b, H, R, P), dtype=torch.bfloat16, device=DEV)
+    y, h = m3scan.m3_prefill(inp["x"], Bb, Cb, inp["dt"], inp["A"], inp["lam"], inp["w_out"],
+                             Bbar_last=Bl, x_last=xl, chunk=w.chunk)
+    torch.cuda.synchronize()
+    dsteps = w.decode_steps
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    toks = inputs.make_sequence(w, g, DEV, (dsteps, b))
+    ys, _, _ = _decode_steps(w, None, dsteps, True, h, phi, Bl, xl, inp, toks)
+    torch.cuda.synchronize()
+    for hi in (0, 41):
+        pair = _slice_pair(inp, 0, hi)
+        ref = oracle.layer(pair, mix=True)
+        assert rel_err(y[:, :, hi:hi + 1], ref["y"]) <= TOL["bf16"], hi
+        state = {"h": ref["h_out"], "phi": ref["phi_out"], "Bbar_prev": ref["Bbar_last"],
+                 "x_prev": ref["x_last"]}
+        consts = {"A": pair["A"], "bias_B": pair["bias_B"], "bias_C": pair["bias_C"],
+                  "w_out": pair["w_out"]}
+        worst = 0.0
+        for s in range(dsteps):
+            tok = {k: toks[k][s, 0:1, hi:hi + 1].cpu() for k in SEQ_KEYS}
+            ry, state = oracle.decode_step(state, tok, consts, mix=True)
+            worst = max(worst, rel_err(ys[s][:, hi:hi + 1], ry))
+        assert worst <= TOL["bf16"], (hi, worst)
+        assert rel_err(h[:, hi:hi + 1], state["h"]) <= TOL["bf16"]
+        assert angle_err(phi[:, hi:hi + 1], state["phi"]) <= 1e-3
