@@ -178,6 +178,27 @@ def cpu_baseline(w, inp, nheads: int):
                       % (pairs, w.batch, nheads, w.nheads, w.seqlen, w.name, secs)}
 
 
+def copy_probe(nbytes: int, steps: int, warmup: int, dev):
+    """A plain device-to-device copy of known size: the practical HBM ceiling on this machine, and
+    the reference against which the FETCH_SIZE / WRITE_SIZE counters are scaled."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).normal_()
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    moved = 2 * src.numel() * 4
+    return {"copy_bytes_read": src.numel() * 4, "copy_bytes_written": src.numel() * 4,
+            "ms": ms, "GB/s": moved / ms / 1e6, "hbm_frac": moved / ms / 1e6 / HBM_PEAK_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +208,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
+                    help="only time a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the layer core has no cross-GPU step, and this build "
@@ -196,6 +219,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.copy_only:
+        print(json.dumps({"copy_probe": copy_probe(args.copy_only, args.steps, args.warmup, dev)}))
+        return
     m3scan.load()
 
     w = inputs.WORKLOADS["siso_b8_l2048"]

@@ -57,11 +57,8 @@ __device__ __forceinline__ void store8(float* p, const float v[8]) {
     ((float4*)p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 __device__ __forceinline__ void store8(bf16* p, const float v[8]) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        w[i] = (uint32_t)bf16_bits_rne(v[2 * i]) | ((uint32_t)bf16_bits_rne(v[2 * i + 1]) << 16);
-    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+    *(uint4*)p = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                            pack_bf16x2(v[6], v[7]));
 }
 
 // Sum of dt * theta over each segment: seg_phi[b, h, seg, :].

@@ -14,26 +14,28 @@
 // i.e. the mask entry is exp(l_t - l_s) mu_s below the diagonal and gamma_t on it (the
 // "decay x 2-band" matrix), and the carried state is G.  The chunk then passes on
 //   G_end = exp(l_end) G_{t0-1} + sum_s exp(l_end - l_s) mu_s u_s.
-// At the call's last step c_{L} is taken as 0, so the returned G is the true state g_{L-1};
-// at the call's first step G_{-1} = h_in + c_0 Bbar_prev^T x_prev.  The trapezoid's link across
-// chunk boundaries is therefore one scalar (dt, lambda of the next step), not a B/x halo.
+// At the call's last step c_L is taken as 0, so the returned G is the true state g_{L-1}; at the
+// call's first step G_{-1} = h_in + c_0 Bbar_prev^T x_prev.  The trapezoid's link across chunk
+// boundaries is therefore one scalar (dt, lambda of the next step), not a B/x halo.
 //
-// Mapping on gfx950.  One workgroup per (b, h) walks the chunks in order and keeps the N x P
-// fp32 state in MFMA accumulator registers, so chunk states never travel through HBM.  The
-// chunk holds QR = Q * R rows (t, r).  Wave w owns the 16 columns [16w, 16w + 16) of P.
-//   1. S^T = Bbar Cbar^T (QR x QR, K = N) on MFMA, only the causal 16x16 tiles, shared out
-//      among the waves; the mask is applied in registers and M = L o S goes to LDS.
-//   2. Y^T (own 16 columns x QR) = state^T Cbar^T * exp(l) + X^T M^T: the state is the A
-//      operand straight from the accumulator registers (an MFMA D tile of S[n][p] is an A tile
-//      of S^T), M comes back from LDS.
+// Mapping on gfx950.  One workgroup per (b, h) walks the chunks in order and keeps the N x P fp32
+// state in MFMA accumulator registers, so chunk states never travel through HBM.  A chunk holds
+// QR = Q * R rows (t, r).  Wave w owns the 16 columns [16w, 16w + 16) of P.
+//   1. S^T = Bbar Cbar^T (QR x QR, K = N) on MFMA, only the causal 16x16 tiles, shared out among
+//      the waves; the mask is applied in registers and M = L o S goes to LDS.
+//   2. Y^T (own 16 columns x QR) = state^T Cbar^T * exp(l) + X^T M^T: the state is the A operand
+//      straight from the accumulator registers (an MFMA D tile of S[n][p] is an A tile of S^T).
 //   3. state = exp(l_end) state + (Bbar^T)(w o X), w_s = exp(l_end - l_s) mu_s.
-// Every MFMA operand read from LDS is four consecutive elements along K.  X and Bbar are
-// staged transposed so that holds for the products over s.  The next chunk's tiles are loaded
-// into registers while the current chunk computes.
+// The chunk's Bbar, Cbar and x tiles sit in LDS exactly as they are laid out in memory (rows
+// (t, r)), written with 16-byte stores.  Operands that need the other orientation (X^T and
+// Bbar^T, contracted over the rows) are read with gfx950's transposing LDS read
+// (ds_read_b64_tr_b16): in each group of 16 lanes, lane j points at 4 consecutive elements of
+// row k0 + j/4, columns c0 + 4 (j % 4); lane i then receives rows k0..k0+3 of column c0 + i.
+// The next chunk's tiles are loaded into registers while the current chunk computes.
 //
 // Operands: bf16 inputs run v_mfma_f32_16x16x16_bf16 (fp32 accumulate); fp32 inputs run
-// v_mfma_f32_16x16x4_f32 four times per 16-wide K block.  The same lane->K slot assignment is
-// used for both operands of every product, which is all the result depends on.
+// v_mfma_f32_16x16x4_f32 four times per 16-wide K block.  In every product the same lane -> K
+// slot assignment is used for both operands, which is all the result depends on.
 #include "m3_device.h"
 #include "m3_launch.h"
 
@@ -41,21 +43,28 @@ namespace m3 {
 
 namespace {
 
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef __attribute__((address_space(3))) char lds_char;
+
 template <typename T> struct Mma;
 
 template <> struct Mma<bf16> {
     typedef shortx4 frag;
-    static __device__ __forceinline__ frag lds(const bf16* p) { return *(const shortx4*)p; }
+    static constexpr int PAD = 16;  // elements of padding per LDS row (32 bytes)
+    // lane gets p[0..3] (4 consecutive elements along K)
+    static __device__ __forceinline__ frag ldk(const bf16* p) { return *(const shortx4*)p; }
+    // transposed read: `row` points at tile[k0 + 4g][c0] for this lane's group g; lane (l16, g)
+    // receives tile[k0 + 4g + m][c0 + l16], m = 0..3
+    static __device__ __forceinline__ frag ldt(const bf16* row, int ld, int l16) {
+        const bf16* p = row + (l16 >> 2) * ld + 4 * (l16 & 3);
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(lds_char*)p);
+    }
     static __device__ __forceinline__ floatx4 mma(frag a, frag b, floatx4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ frag pack(floatx4 v) {
-        frag f;
-        f[0] = (short)bf16_bits_rne(v[0]);
-        f[1] = (short)bf16_bits_rne(v[1]);
-        f[2] = (short)bf16_bits_rne(v[2]);
-        f[3] = (short)bf16_bits_rne(v[3]);
-        return f;
+        const uint2 u = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        return __builtin_bit_cast(frag, u);
     }
     static __device__ __forceinline__ floatx4 unpack(frag f) {
         floatx4 v;
@@ -70,7 +79,16 @@ template <> struct Mma<bf16> {
 
 template <> struct Mma<float> {
     typedef floatx4 frag;
-    static __device__ __forceinline__ frag lds(const float* p) { return *(const floatx4*)p; }
+    static constexpr int PAD = 4;
+    static __device__ __forceinline__ frag ldk(const float* p) { return *(const floatx4*)p; }
+    static __device__ __forceinline__ frag ldt(const float* row, int ld, int l16) {
+        frag f;
+        f[0] = row[l16];
+        f[1] = row[ld + l16];
+        f[2] = row[2 * ld + l16];
+        f[3] = row[3 * ld + l16];
+        return f;
+    }
     static __device__ __forceinline__ floatx4 mma(frag a, frag b, floatx4 c) {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
@@ -86,18 +104,15 @@ template <> struct Mma<float> {
 // four consecutive output values to global memory
 __device__ __forceinline__ void store4(float* p, floatx4 v) { *(floatx4*)p = v; }
 __device__ __forceinline__ void store4(bf16* p, floatx4 v) {
-    const uint32_t lo = (uint32_t)bf16_bits_rne(v[0]) | ((uint32_t)bf16_bits_rne(v[1]) << 16);
-    const uint32_t hi = (uint32_t)bf16_bits_rne(v[2]) | ((uint32_t)bf16_bits_rne(v[3]) << 16);
-    *(uint2*)p = make_uint2(lo, hi);
+    *(uint2*)p = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
-template <typename T, int N, int P>
-__global__ __launch_bounds__(P / 16 * 64) void prefill_kernel(PrefillArgs a) {
+template <typename T, int N, int P, int NIB>
+__global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) {
     using MM = Mma<T>;
     using F = typename MM::frag;
     constexpr int NW = P / 16, NT = NW * 64;
-    constexpr int PAD = 16 / sizeof(T);          // one 16-byte vector of padding per row
-    constexpr int LDN = N + PAD, LDQ = 64 + PAD;
+    constexpr int LDN = N + MM::PAD, LDP = P + MM::PAD, LDQ = 64 + MM::PAD;
     constexpr int VE = 16 / sizeof(T);           // elements per 16-byte vector
     constexpr int VPN = N / VE, VPP = P / VE;    // vectors per row of Bbar/Cbar and of x
     constexpr int MAXC = (64 * VPN + NT - 1) / NT;
@@ -106,93 +121,105 @@ __global__ __launch_bounds__(P / 16 * 64) void prefill_kernel(PrefillArgs a) {
 
     __shared__ __align__(16) T sC[64 * LDN];     // Cbar rows of the chunk  [i][n]
     __shared__ __align__(16) T sB[64 * LDN];     // Bbar rows               [s][n]
-    __shared__ __align__(16) T sBT[N * LDQ];     // Bbar transposed         [n][s]
-    __shared__ __align__(16) T sXT[P * LDQ];     // x transposed            [p][s]
+    __shared__ __align__(16) T sX[64 * LDP];     // x rows                  [s][p]
     __shared__ __align__(16) T sM[64 * LDQ];     // masked scores           [i][s]
-    __shared__ float sL2[64], sGam[64], sMu[64], sEl[64], sW[64];
+    // per-row (t, r) copies of the chunk's per-step scalars, rewritten every chunk: log2 decay
+    // l_t, gamma_t, mu_t, exp(l_t), w_t = exp(l_end - l_t) mu_t, and the row's step t
+    __shared__ __align__(16) float rL2[64], rGam[64], rMu[64], rEl[64], rW[64];
+    __shared__ __align__(16) int rT[64];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / a.H;
     const int h = (int)(bh % a.H);
-    const int H = a.H, R = a.R, Q = a.Q, QR = Q * R, nIB = QR / 16;
+    constexpr int QR = 16 * NIB;                 // rows (t, r) per chunk
+    const int H = a.H, R = a.R, Q = a.Q;
+    const int rl2 = __builtin_ctz((unsigned)R), rmask = R - 1;
     const int64_t L = a.L;
     const int64_t nchunk = (L + Q - 1) / Q;
     const float Alog2 = a.A[h] * kLog2e;
-    const T* Xg = (const T*)a.x;
-    const T* Bg = (const T*)a.Bbar;
-    const T* Cg = (const T*)a.Cbar;
-    const T* dtg = (const T*)a.dt;
-    const T* lamg = (const T*)a.lam;
+    // (b, t = 0, h) bases; step t of this (b, h) is t * H rows further
+    const int64_t row_bh = b * L * a.H + h;
+    const T* Xg = (const T*)a.x + row_bh * a.R * P;
+    const T* Bg = (const T*)a.Bbar + row_bh * a.R * N;
+    const T* Cg = (const T*)a.Cbar + row_bh * a.R * N;
+    const T* dtg = (const T*)a.dt + row_bh;
+    const T* lamg = (const T*)a.lam + row_bh;
     const int pcol = 16 * wave + l16;            // this lane's column of P in MFMA tiles
+    const int64_t HRN = (int64_t)H * R * N, HRP = (int64_t)H * R * P;
+
+    // ---- staging: this thread moves 16-byte vectors k = 0, 1, ... of each tile.  Vector k is
+    // chunk row i = i0 + k * (NT / VPN) (row (t, r) = (i >> rl2, i & rmask)), 16-byte column cv0.
+    static_assert(NT % VPN == 0 && NT % VPP == 0, "vectors per row must divide the block");
+    constexpr int RKC = NT / VPN, RKX = NT / VPP;            // chunk rows per k
+    const int iC0 = tid / VPN, cC0 = tid % VPN, iX0 = tid / VPP, cX0 = tid % VPP;
+    const int HRN32 = H * R * N, HRP32 = H * R * P;
+    auto offC = [&](int k) { const int i = iC0 + k * RKC; return (i >> rl2) * HRN32 + (i & rmask) * N + cC0 * VE; };
+    auto offX = [&](int k) { const int i = iX0 + k * RKX; return (i >> rl2) * HRP32 + (i & rmask) * P + cX0 * VE; };
 
     // ---- chunk prefetch into registers --------------------------------------------------
     uint4 rc[MAXC], rb[MAXC], rx[MAXX];
     float rd = 0.f, rl = 0.f, rdn = 0.f, rln = 0.f;
     auto load_chunk = [&](int64_t c) {
         const int64_t t0 = c * Q;
+        const T* cb = Cg + t0 * HRN32;
+        const T* bb = Bg + t0 * HRN32;
+        const T* xb = Xg + t0 * HRP32;
+        if (t0 + Q <= L) {   // a full chunk: every row exists
 #pragma unroll
-        for (int k = 0; k < MAXC; ++k) {
-            const int v = tid + k * NT;
-            rc[k] = make_uint4(0, 0, 0, 0);
-            rb[k] = make_uint4(0, 0, 0, 0);
-            if (v < QR * VPN) {
-                const int i = v / VPN, cv = v % VPN;
-                const int64_t t = t0 + i / R;
-                if (t < L) {
-                    const int64_t off = ((((b * L + t) * H + h) * R) + i % R) * N + cv * VE;
-                    rc[k] = *(const uint4*)(Cg + off);
-                    rb[k] = *(const uint4*)(Bg + off);
+            for (int k = 0; k < MAXC; ++k) {
+                if (iC0 + k * RKC < QR) {
+                    rc[k] = *(const uint4*)(cb + offC(k));
+                    rb[k] = *(const uint4*)(bb + offC(k));
                 }
             }
-        }
 #pragma unroll
-        for (int k = 0; k < MAXX; ++k) {
-            const int v = tid + k * NT;
-            rx[k] = make_uint4(0, 0, 0, 0);
-            if (v < QR * VPP) {
-                const int i = v / VPP, cv = v % VPP;
-                const int64_t t = t0 + i / R;
-                if (t < L) {
-                    const int64_t off = ((((b * L + t) * H + h) * R) + i % R) * P + cv * VE;
-                    rx[k] = *(const uint4*)(Xg + off);
+            for (int k = 0; k < MAXX; ++k)
+                if (iX0 + k * RKX < QR) rx[k] = *(const uint4*)(xb + offX(k));
+        } else {             // the ragged last chunk: rows past the sequence end are zero
+            const int nvalid = (int)(L - t0);
+#pragma unroll
+            for (int k = 0; k < MAXC; ++k) {
+                const int i = iC0 + k * RKC;
+                rc[k] = make_uint4(0, 0, 0, 0);
+                rb[k] = make_uint4(0, 0, 0, 0);
+                if (i < QR && (i >> rl2) < nvalid) {
+                    rc[k] = *(const uint4*)(cb + offC(k));
+                    rb[k] = *(const uint4*)(bb + offC(k));
                 }
+            }
+#pragma unroll
+            for (int k = 0; k < MAXX; ++k) {
+                const int i = iX0 + k * RKX;
+                rx[k] = make_uint4(0, 0, 0, 0);
+                if (i < QR && (i >> rl2) < nvalid) rx[k] = *(const uint4*)(xb + offX(k));
             }
         }
         if (wave == 0) {
             const int64_t t = t0 + lane;
             const bool in = lane < Q && t < L;
             const bool inn = lane < Q && t + 1 < L;
-            const int64_t row = (b * L + t) * H + h;
-            rd = in ? load_f32(dtg + row) : 0.f;
-            rl = in ? load_f32(lamg + row) : 0.f;
-            rdn = inn ? load_f32(dtg + row + H) : 0.f;
-            rln = inn ? load_f32(lamg + row + H) : 0.f;
+            rd = in ? load_f32(dtg + t * H) : 0.f;
+            rl = in ? load_f32(lamg + t * H) : 0.f;
+            rdn = inn ? load_f32(dtg + (t + 1) * H) : 0.f;
+            rln = inn ? load_f32(lamg + (t + 1) * H) : 0.f;
         }
     };
     auto store_chunk = [&]() {
 #pragma unroll
         for (int k = 0; k < MAXC; ++k) {
-            const int v = tid + k * NT;
-            if (v < QR * VPN) {
-                const int i = v / VPN, cv = v % VPN;
-                *(uint4*)(sC + i * LDN + cv * VE) = rc[k];
-                *(uint4*)(sB + i * LDN + cv * VE) = rb[k];
-                const T* e = (const T*)&rb[k];
-#pragma unroll
-                for (int q = 0; q < VE; ++q) sBT[(cv * VE + q) * LDQ + i] = e[q];
+            const int i = iC0 + k * RKC;
+            if (i < QR) {
+                *(uint4*)(sC + i * LDN + cC0 * VE) = rc[k];
+                *(uint4*)(sB + i * LDN + cC0 * VE) = rb[k];
             }
         }
 #pragma unroll
         for (int k = 0; k < MAXX; ++k) {
-            const int v = tid + k * NT;
-            if (v < QR * VPP) {
-                const int i = v / VPP, cv = v % VPP;
-                const T* e = (const T*)&rx[k];
-#pragma unroll
-                for (int q = 0; q < VE; ++q) sXT[(cv * VE + q) * LDQ + i] = e[q];
-            }
+            const int i = iX0 + k * RKX;
+            if (i < QR) *(uint4*)(sX + i * LDP + cX0 * VE) = rx[k];
         }
         if (wave == 0) {
             // l_t in log2 units: inclusive prefix sum of dt * A over the chunk
@@ -205,47 +232,56 @@ __global__ __launch_bounds__(P / 16 * 64) void prefill_kernel(PrefillArgs a) {
             const float gam = rl * rd;
             const float mu = gam + (1.0f - rln) * rdn;
             const float l2end = shfl(l2, Q - 1);
-            sL2[lane] = l2;
-            sGam[lane] = gam;
-            sMu[lane] = mu;
-            sEl[lane] = exp2f(l2);
-            sW[lane] = exp2f(l2end - l2) * mu;
+            const float el = fast_exp2(l2);
+            const float w = fast_exp2(fminf(l2end - l2, 0.f)) * mu;
+            // lane = chunk row s; its step is s >> rl2 (rows past Q * R are never read)
+            const int ts = lane >> rl2;
+            rL2[lane] = shfl(l2, ts);
+            rGam[lane] = shfl(gam, ts);
+            rMu[lane] = shfl(mu, ts);
+            rEl[lane] = shfl(el, ts);
+            rW[lane] = shfl(w, ts);
+            rT[lane] = ts;
         }
     };
 
     // ---- carried-in state: G_{-1} = h_in + c_0 Bbar_prev^T x_prev ------------------------
     floatx4 st[NB];
-    {
-        float c0 = 0.f;
-        if (L > 0) {
-            const int64_t row0 = (b * L) * H + h;
-            c0 = (1.0f - load_f32(lamg + row0)) * load_f32(dtg + row0);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            st[nb][m] = a.h_in ? a.h_in[(bh * N + 16 * nb + 4 * g + m) * P + pcol] : 0.f;
+    if (a.Bbar_prev && a.x_prev && L > 0) {
+        const float c0 = (1.0f - load_f32(lamg)) * load_f32(dtg);
+        const T* Bp = (const T*)a.Bbar_prev + bh * R * N;
+        const T* xp = (const T*)a.x_prev + bh * R * P;
+        for (int r = 0; r < R; ++r) {
+            const float xv = c0 * load_f32(xp + r * P + pcol);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) st[nb][m] += load_f32(Bp + r * N + 16 * nb + 4 * g + m) * xv;
         }
-        const T* Bp = (const T*)a.Bbar_prev;
-        const T* xp = (const T*)a.x_prev;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int n = 16 * nb + 4 * g + m;
-                float v = a.h_in ? a.h_in[(bh * N + n) * P + pcol] : 0.f;
-                if (Bp && xp) {
-                    float u = 0.f;
-                    for (int r = 0; r < R; ++r)
-                        u += load_f32(Bp + (bh * R + r) * N + n) * load_f32(xp + (bh * R + r) * P + pcol);
-                    v += c0 * u;
-                }
-                st[nb][m] = v;
-            }
     }
+
+    T* ymix = (T*)a.y + row_bh * P;            // [b, L, H, P] when mixing
+    T* yraw = (T*)a.y + row_bh * a.R * P;      // [b, L, H, R, P] otherwise
 
     // output mixing weights for this lane's (r, 4 columns)
     floatx4 wo = {1.f, 1.f, 1.f, 1.f};
     if (a.w_out) {
-        const int r = l16 % R;
+        const int r = l16 & rmask;
 #pragma unroll
         for (int m = 0; m < 4; ++m) wo[m] = a.w_out[(h * R + r) * P + 16 * wave + 4 * g + m];
     }
+
+    // loop-invariant LDS fragment addresses for this lane
+    const T* pB_k = sB + l16 * LDN + 4 * g;                 // + 16 sb LDN + 16 kb
+    const T* pC_k = sC + l16 * LDN + 4 * g;                 // + 16 ib LDN + 16 kb
+    const T* pM_k = sM + l16 * LDQ + 4 * g;                 // + 16 ib LDQ + 16 sb
+    const T* pX_t = sX + 4 * g * LDP + 16 * wave;           // + 16 sb LDP
+    const T* pB_t = sB + 4 * g * LDN;                       // + 16 sb LDN + 16 nb
 
     if (nchunk > 0) load_chunk(0);
     for (int64_t c = 0; c < nchunk; ++c) {
@@ -255,51 +291,59 @@ __global__ __launch_bounds__(P / 16 * 64) void prefill_kernel(PrefillArgs a) {
         const int64_t t0 = c * Q;
 
         // 1. masked scores M[i][s] = L(t_i, t_s) * Cbar_i . Bbar_s on the causal tiles
-        int tau = 0;
-        for (int ib = 0; ib < nIB; ++ib) {
-            for (int sb = 0; sb <= ib; ++sb, ++tau) {
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+            for (int sb = 0; sb <= ib; ++sb) {
+                const int tau = ib * (ib + 1) / 2 + sb;
                 if (tau % NW != wave) continue;
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < NB; ++kb) {
-                    const F fa = MM::lds(sB + (16 * sb + l16) * LDN + 16 * kb + 4 * g);
-                    const F fb = MM::lds(sC + (16 * ib + l16) * LDN + 16 * kb + 4 * g);
-                    acc = MM::mma(fa, fb, acc);
-                }
+                for (int kb = 0; kb < NB; ++kb)
+                    acc = MM::mma(MM::ldk(pB_k + 16 * sb * LDN + 16 * kb),
+                                  MM::ldk(pC_k + 16 * ib * LDN + 16 * kb), acc);
                 const int i = 16 * ib + l16;
-                const int ti = i / R;
-                const float l2i = sL2[ti], gi = sGam[ti];
+                const int ti = rT[i];
+                const float l2i = rL2[i], gi = rGam[i];
+                const floatx4 l2s = *(const floatx4*)(rL2 + 16 * sb + 4 * g);
+                const floatx4 mus = *(const floatx4*)(rMu + 16 * sb + 4 * g);
+                const int4 ts = *(const int4*)(rT + 16 * sb + 4 * g);
+                const int tsv[4] = {ts.x, ts.y, ts.z, ts.w};
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const int ts = (16 * sb + 4 * g + m) / R;
-                    const float f = ts < ti ? exp2f(l2i - sL2[ts]) * sMu[ts] : (ts == ti ? gi : 0.f);
+                    // below the diagonal exp(l_t - l_s) mu_s, on it gamma_t, above it 0
+                    const float e = fast_exp2(fminf(l2i - l2s[m], 0.f)) * mus[m];
+                    const float f = tsv[m] < ti ? e : (tsv[m] == ti ? gi : 0.f);
                     acc[m] *= f;
                 }
                 MM::st(sM + i * LDQ + 16 * sb + 4 * g, MM::pack(acc));
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         __syncthreads();
+
+        // X^T fragments of this wave's 16 columns, for every 16 rows of the chunk
+        F xf[NIB];
+#pragma unroll
+        for (int sb = 0; sb < NIB; ++sb) xf[sb] = MM::ldt(pX_t + 16 * sb * LDP, LDP, l16);
 
         // 2. Y^T for this wave's 16 columns: state part, scaled by exp(l_t), plus X^T M^T
         F sa[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) sa[nb] = MM::pack(st[nb]);
-        for (int ib = 0; ib < nIB; ++ib) {
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib) {
             floatx4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < NB; ++kb)
-                y = MM::mma(sa[kb], MM::lds(sC + (16 * ib + l16) * LDN + 16 * kb + 4 * g), y);
+            for (int kb = 0; kb < NB; ++kb) y = MM::mma(sa[kb], MM::ldk(pC_k + 16 * ib * LDN + 16 * kb), y);
             const int i = 16 * ib + l16;
-            const float el = sEl[i / R];
+            const float el = rEl[i];
 #pragma unroll
             for (int m = 0; m < 4; ++m) y[m] *= el;
-            for (int sb = 0; sb <= ib; ++sb) {
-                const F fa = MM::lds(sXT + pcol * LDQ + 16 * sb + 4 * g);
-                const F fb = MM::lds(sM + i * LDQ + 16 * sb + 4 * g);
-                y = MM::mma(fa, fb, y);
-            }
+#pragma unroll
+            for (int sb = 0; sb <= ib; ++sb) y = MM::mma(xf[sb], MM::ldk(pM_k + 16 * ib * LDQ + 16 * sb), y);
             // lane holds Y[(t, r) = i][p = 16 wave + 4 g + m]
-            const int tl = i / R, r = i % R;
+            const int tl = i >> rl2, r = i & rmask;
             const int64_t t = t0 + tl;
             const bool valid = t < L;
             const int p = 16 * wave + 4 * g;
@@ -310,26 +354,30 @@ __global__ __launch_bounds__(P / 16 * 64) void prefill_kernel(PrefillArgs a) {
                     for (int o = 1; o < R; o <<= 1) v += shfl_xor(v, o);
                     y[m] = v;
                 }
-                if (valid && r == 0) store4((T*)a.y + ((b * L + t) * H + h) * P + p, y);
+                if (valid && r == 0) store4(ymix + t * H * P + p, y);
             } else if (valid) {
-                store4((T*)a.y + (((b * L + t) * H + h) * R + r) * P + p, y);
+                store4(yraw + (t * H * R + r) * P + p, y);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // 3. state update: G = exp(l_end) G + Bbar^T (w o X)
-        const float dec = sEl[Q - 1];
+        const float dec = rEl[QR - 1];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int m = 0; m < 4; ++m) st[nb][m] *= dec;
-        for (int sb = 0; sb < nIB; ++sb) {
-            floatx4 xf = MM::unpack(MM::lds(sXT + pcol * LDQ + 16 * sb + 4 * g));
 #pragma unroll
-            for (int m = 0; m < 4; ++m) xf[m] *= sW[(16 * sb + 4 * g + m) / R];
-            const F fx = MM::pack(xf);
+        for (int sb = 0; sb < NIB; ++sb) {
+            floatx4 xs = MM::unpack(xf[sb]);
+            const floatx4 ws = *(const floatx4*)(rW + 16 * sb + 4 * g);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) xs[m] *= ws[m];
+            const F fx = MM::pack(xs);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                st[nb] = MM::mma(MM::lds(sBT + (16 * nb + l16) * LDQ + 16 * sb + 4 * g), fx, st[nb]);
+                st[nb] = MM::mma(MM::ldt(pB_t + 16 * sb * LDN + 16 * nb, LDN, l16), fx, st[nb]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
     }
@@ -340,26 +388,33 @@ __global__ __launch_bounds__(P / 16 * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) a.h_out[(bh * N + 16 * nb + 4 * g + m) * P + pcol] = st[nb][m];
     if (L > 0) {
-        const int64_t rowl = ((b * L + L - 1) * H + h) * R;
         if (a.Bbar_last)
-            for (int e = tid; e < R * N; e += NT) ((T*)a.Bbar_last)[bh * R * N + e] = Bg[rowl * N + e];
+            for (int e = tid; e < R * N; e += NT)
+                ((T*)a.Bbar_last)[bh * R * N + e] = Bg[(L - 1) * HRN32 + e];
         if (a.x_last)
-            for (int e = tid; e < R * P; e += NT) ((T*)a.x_last)[bh * R * P + e] = Xg[rowl * P + e];
+            for (int e = tid; e < R * P; e += NT) ((T*)a.x_last)[bh * R * P + e] = Xg[(L - 1) * HRP32 + e];
     }
+}
+
+template <typename T, int N, int P>
+hipError_t launch_np(const PrefillArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)(a.b * a.H)), block(P / 16 * 64);
+    switch (a.Q * a.R) {
+        case 16: hipLaunchKernelGGL((prefill_kernel<T, N, P, 1>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((prefill_kernel<T, N, P, 2>), grid, block, 0, s, a); break;
+        case 48: hipLaunchKernelGGL((prefill_kernel<T, N, P, 3>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((prefill_kernel<T, N, P, 4>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)(a.b * a.H));
-    if (a.N == 16 && a.P == 16)
-        hipLaunchKernelGGL((prefill_kernel<T, 16, 16>), grid, dim3(64), 0, s, a);
-    else if (a.N == 64 && a.P == 64)
-        hipLaunchKernelGGL((prefill_kernel<T, 64, 64>), grid, dim3(256), 0, s, a);
-    else if (a.N == 128 && a.P == 64)
-        hipLaunchKernelGGL((prefill_kernel<T, 128, 64>), grid, dim3(256), 0, s, a);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (a.N == 16 && a.P == 16) return launch_np<T, 16, 16>(a, s);
+    if (a.N == 64 && a.P == 64) return launch_np<T, 64, 64>(a, s);
+    if (a.N == 128 && a.P == 64) return launch_np<T, 128, 64>(a, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -4,9 +4,15 @@ The GPU runs the whole batch; the fp64 oracle recomputes a few sampled (batch, h
 the same inputs (every (batch, head) is independent, so a sampled pair is checked exactly, not
 approximately).  Inputs are drawn on the device with a seeded generator; the sampled slices are
 copied to the host for the oracle.
+
+Errors are normwise per output tensor, max|gpu - ref| / max|ref|; for decode the output tensor is
+y over all decode steps of the run.  (A single step's y can be far below its typical size when
+Cbar_t . Bbar_t nearly cancels; its absolute error is then the usual one, set by the bf16 rounding
+of Bbar and Cbar, so a per-step ratio is not a meaningful measure there.)
 """
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
@@ -105,12 +111,15 @@ def test_decode_workload_sampled(name, pairs):
                   "w_out": dinp["w_out"][hi:hi + 1].cpu() if w.mix else None}
         state = {k: st[k][bi:bi + 1, hi:hi + 1].cpu() for k in ("phi", "Bbar_prev", "x_prev")}
         state["h"] = st["h"][bi:bi + 1, hi:hi + 1].cpu()
-        worst = 0.0
+        rys = []
         for s in range(steps):
             tok = {k: dinp["tokens"][k][s, bi:bi + 1, hi:hi + 1].cpu() for k in SEQ_KEYS}
             ry, state = oracle.decode_step(state, tok, consts, mix=w.mix)
-            worst = max(worst, rel_err(ys[s][bi:bi + 1, hi:hi + 1], ry))
-        assert worst <= TOL[w.io], (bi, hi, worst)
+            rys.append(ry)
+        # y over all decode steps is one output tensor: normwise error over the whole of it
+        yg = torch.stack([y[bi:bi + 1, hi:hi + 1] for y in ys], 0)
+        err = rel_err(yg, np.stack(rys, 0))
+        assert err <= TOL[w.io], (bi, hi, err)
         assert rel_err(h[bi:bi + 1, hi:hi + 1], state["h"]) <= TOL[w.io]
         assert angle_err(phi[bi:bi + 1, hi:hi + 1], state["phi"]) <= 1e-3
 
@@ -142,11 +151,12 @@ def test_long_context_prefill_then_decode_sampled():
                  "x_prev": ref["x_last"]}
         consts = {"A": pair["A"], "bias_B": pair["bias_B"], "bias_C": pair["bias_C"],
                   "w_out": pair["w_out"]}
-        worst = 0.0
+        rys = []
         for s in range(dsteps):
             tok = {k: toks[k][s, 0:1, hi:hi + 1].cpu() for k in SEQ_KEYS}
             ry, state = oracle.decode_step(state, tok, consts, mix=True)
-            worst = max(worst, rel_err(ys[s][:, hi:hi + 1], ry))
-        assert worst <= TOL["bf16"], (hi, worst)
+            rys.append(ry)
+        err = rel_err(torch.stack([y[:, hi:hi + 1] for y in ys], 0), np.stack(rys, 0))
+        assert err <= TOL["bf16"], (hi, err)
         assert rel_err(h[:, hi:hi + 1], state["h"]) <= TOL["bf16"]
         assert angle_err(phi[:, hi:hi + 1], state["phi"]) <= 1e-3
