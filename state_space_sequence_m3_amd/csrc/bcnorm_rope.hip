@@ -61,6 +61,40 @@ __device__ __forceinline__ void store8(bf16* p, const float v[8]) {
                             pack_bf16x2(v[6], v[7]));
 }
 
+// Raw (still packed) 8- and 4-element loads, so a prefetched block costs few registers.
+template <typename T> struct Raw;
+template <> struct Raw<bf16> {
+    typedef uint4 v8;
+    typedef uint2 v4;
+    static __device__ __forceinline__ v8 ld8(const bf16* p) { return *(const uint4*)p; }
+    static __device__ __forceinline__ v4 ld4(const bf16* p) { return *(const uint2*)p; }
+    static __device__ __forceinline__ void un8(v8 v, float o[8]) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void un4(v4 v, float o[4]) {
+        o[0] = __uint_as_float(v.x << 16);
+        o[1] = __uint_as_float(v.x & 0xffff0000u);
+        o[2] = __uint_as_float(v.y << 16);
+        o[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+};
+template <> struct Raw<float> {
+    struct v8 { float4 a, b; };
+    typedef float4 v4;
+    static __device__ __forceinline__ v8 ld8(const float* p) { return v8{((const float4*)p)[0], ((const float4*)p)[1]}; }
+    static __device__ __forceinline__ v4 ld4(const float* p) { return *(const float4*)p; }
+    static __device__ __forceinline__ void un8(v8 v, float o[8]) {
+        o[0] = v.a.x; o[1] = v.a.y; o[2] = v.a.z; o[3] = v.a.w;
+        o[4] = v.b.x; o[5] = v.b.y; o[6] = v.b.z; o[7] = v.b.w;
+    }
+    static __device__ __forceinline__ void un4(v4 v, float o[4]) { o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; }
+};
+
 // Sum of dt * theta over each segment: seg_phi[b, h, seg, :].
 template <typename T, int N>
 __global__ __launch_bounds__(256) void angle_partial_kernel(BcnormRopeArgs a) {
@@ -75,6 +109,7 @@ __global__ __launch_bounds__(256) void angle_partial_kernel(BcnormRopeArgs a) {
     const int64_t t0 = seg * a.seglen;
     const int64_t t1 = t0 + a.seglen < a.L ? t0 + a.seglen : a.L;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
     for (int64_t t = t0 + j; t < t1; t += 256 / LPR) {
         const int64_t row = (b * a.L + t) * a.H + h;
         const float d = load_f32((const T*)a.dt + row);
@@ -143,6 +178,7 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
 
     // each wave sums the angle increments of its quarter; waves before it shift its start
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
     for (int64_t t = w0 + j; t < w1; t += RPW) {
         const int64_t row = (b * a.L + t) * a.H + h;
         const float d = load_f32((const T*)a.dt + row);
@@ -184,37 +220,70 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
         wC[e] = a.normw_C ? a.normw_C[h * N + 8 * c + e] : 1.0f;
     }
     const float invN = 1.0f / (float)N;
+    // when R divides the rows per wave instruction, row group j always holds rank j % R, so its
+    // bias is fixed for the whole walk
+    const bool bias_fixed = RPW % R == 0;
+    float bB[8], bC[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        bB[e] = (bias_fixed && a.bias_B) ? a.bias_B[(h * R + j % R) * N + 8 * c + e] : 0.0f;
+        bC[e] = (bias_fixed && a.bias_C) ? a.bias_C[(h * R + j % R) * N + 8 * c + e] : 0.0f;
+    }
 
-    // walk the quarter: rows rho = (t - w0) * R + r, RPW rows per iteration
+    // walk the quarter, RPW rows rho = (t - w0) * R + r at a time; row rho of this wave lives at
+    // (rho / R) * H * R * N + (rho % R) * N past the (b, w0, h) row
     const int64_t nrows = (w1 - w0) * R;
-    int64_t t_next = w0;   // first step whose angle increment is not yet in phi_acc
+    const int64_t row_w0 = (b * a.L + w0) * a.H + h;
+    const int64_t HRN = (int64_t)a.H * R * N, HK = (int64_t)a.H * K;
+    const T* Bq = (const T*)a.B + row_w0 * R * N + 8 * c;
+    const T* Cq = (const T*)a.C + row_w0 * R * N + 8 * c;
+    T* Bo = (T*)a.Bbar + row_w0 * R * N + 8 * c;
+    T* Co = (T*)a.Cbar + row_w0 * R * N + 8 * c;
+    const T* thq = (const T*)a.theta + row_w0 * K + 4 * c;
+    const T* dtq = (const T*)a.dt + row_w0;
+
+    // one block of this lane's row, prefetched (still packed) while the previous block computes
+    using RW = Raw<T>;
+    typename RW::v8 nB, nC;
+    typename RW::v4 nT;
+    T nD;
+    auto load_block = [&](int64_t rho0) {
+        int64_t rho = rho0 + j;
+        if (rho >= nrows) rho = nrows - 1;   // past the end: reload the last row, result unused
+        const int64_t tl = rho / R;
+        const int r = (int)(rho % R);
+        nB = RW::ld8(Bq + tl * HRN + r * N);
+        nC = RW::ld8(Cq + tl * HRN + r * N);
+        nT = RW::ld4(thq + tl * HK);
+        nD = dtq[tl * a.H];
+    };
     float phi_acc[4] = {start[0], start[1], start[2], start[3]};
+    if (nrows > 0) load_block(0);
     for (int64_t rho0 = 0; rho0 < nrows; rho0 += RPW) {
+        float vb[8], vc[8], th[4];
+        RW::un8(nB, vb);
+        RW::un8(nC, vc);
+        RW::un4(nT, th);
+        const float d = to_f32(nD);
+        if (rho0 + RPW < nrows) load_block(rho0 + RPW);
+
         const int64_t rho = rho0 + j;
         const bool valid = rho < nrows;
-        const int64_t my_t = w0 + (valid ? rho : nrows - 1) / R;
-        const int r = (int)((valid ? rho : nrows - 1) % R);
-        const int64_t last = rho0 + RPW < nrows ? rho0 + RPW - 1 : nrows - 1;
-        const int64_t t_last = w0 + last / R;
-        float my_phi[4] = {phi_acc[0], phi_acc[1], phi_acc[2], phi_acc[3]};
-        for (int64_t t = t_next; t <= t_last; ++t) {
-            const int64_t row = (b * a.L + t) * a.H + h;
-            const float d = load_f32((const T*)a.dt + row);
-            float th[4];
-            load4((const T*)a.theta + row * K + 4 * c, th);
+        const int r = (int)(rho % R);
+        // angle: each step's increment enters once, on the step's first row (r == 0); an
+        // inclusive prefix over the row groups gives every row the angle of its own step
+        float my_phi[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) phi_acc[q] = wrap_angle(phi_acc[q] + d * th[q]);
-            if (t == my_t) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) my_phi[q] = phi_acc[q];
+        for (int q = 0; q < 4; ++q) {
+            float inc = (valid && r == 0) ? d * th[q] : 0.0f;
+            for (int o = LPR; o < 64; o <<= 1) {
+                const float v = shfl_up(inc, o);
+                if (lane >= o) inc += v;
             }
+            my_phi[q] = wrap_angle(phi_acc[q] + inc);
+            phi_acc[q] = wrap_angle(phi_acc[q] + shfl(inc, (RPW - 1) * LPR + c));
         }
-        t_next = t_last + 1;
 
-        const int64_t off = (((b * a.L + my_t) * a.H + h) * R + r) * N + 8 * c;
-        float vb[8], vc[8];
-        load8((const T*)a.B + off, vb);
-        load8((const T*)a.C + off, vc);
         if (a.bcnorm) {
             float sb = 0.f, sc = 0.f;
 #pragma unroll
@@ -233,31 +302,40 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
                 vc[e] *= ic * wC[e];
             }
         }
-        if (a.bias_B) {
-            float bb[8];
-            load8(a.bias_B + (h * R + r) * N + 8 * c, bb);
+        if (bias_fixed) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vb[e] += bb[e];
-        }
-        if (a.bias_C) {
-            float bc[8];
-            load8(a.bias_C + (h * R + r) * N + 8 * c, bc);
+            for (int e = 0; e < 8; ++e) {
+                vb[e] += bB[e];
+                vc[e] += bC[e];
+            }
+        } else {
+            if (a.bias_B) {
+                float bb[8];
+                load8(a.bias_B + (h * R + r) * N + 8 * c, bb);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vc[e] += bc[e];
+                for (int e = 0; e < 8; ++e) vb[e] += bb[e];
+            }
+            if (a.bias_C) {
+                float bc[8];
+                load8(a.bias_C + (h * R + r) * N + 8 * c, bc);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vc[e] += bc[e];
+            }
         }
         float ob[8], oc[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             float s, co;
-            sincosf(my_phi[q], &s, &co);
+            __sincosf(my_phi[q], &s, &co);   // |angle| <= pi after reduction
             ob[2 * q] = co * vb[2 * q] + s * vb[2 * q + 1];
             ob[2 * q + 1] = -s * vb[2 * q] + co * vb[2 * q + 1];
             oc[2 * q] = co * vc[2 * q] + s * vc[2 * q + 1];
             oc[2 * q + 1] = -s * vc[2 * q] + co * vc[2 * q + 1];
         }
         if (valid) {
-            store8((T*)a.Bbar + off, ob);
-            store8((T*)a.Cbar + off, oc);
+            const int64_t off = (rho / R) * HRN + r * N;
+            store8(Bo + off, ob);
+            store8(Co + off, oc);
         }
     }
 }
@@ -270,7 +348,8 @@ hipError_t launch_n(const BcnormRopeArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(angle_scan_kernel, dim3(nbh), dim3(N / 2 < 64 ? 64 : N / 2), 0, s, a);
     }
     // a single-wave workgroup when the segment has too few rows to share among four waves
-    if (a.seglen * a.R >= 4 * (512 / N))
+    const int64_t steps = a.L < a.seglen ? a.L : a.seglen;
+    if (steps * a.R >= 4 * (512 / N))
         hipLaunchKernelGGL((bcnorm_rope_kernel<T, N, 4>), dim3(nbh * a.nseg), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL((bcnorm_rope_kernel<T, N, 1>), dim3(nbh * a.nseg), dim3(64), 0, s, a);
