@@ -62,6 +62,13 @@ template <> struct Mma<bf16> {
     static __device__ __forceinline__ floatx4 mma(frag a, frag b, floatx4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
     }
+    // two 16-wide K blocks.  They could run as one v_mfma_f32_16x16x32_bf16 (its K slots pair up
+    // symmetrically for A and B), but with this toolchain a VALU write that follows that
+    // instruction can clobber its A/B registers while later passes still read them, so the pair
+    // runs as two 16x16x16 instructions.
+    static __device__ __forceinline__ floatx4 mma2(frag a0, frag a1, frag b0, frag b1, floatx4 c) {
+        return mma(a1, b1, mma(a0, b0, c));
+    }
     static __device__ __forceinline__ frag pack(floatx4 v) {
         const uint2 u = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         return __builtin_bit_cast(frag, u);
@@ -96,10 +103,23 @@ template <> struct Mma<float> {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
         return c;
     }
+    static __device__ __forceinline__ floatx4 mma2(frag a0, frag a1, frag b0, frag b1, floatx4 c) {
+        return mma(a1, b1, mma(a0, b0, c));
+    }
     static __device__ __forceinline__ frag pack(floatx4 v) { return v; }
     static __device__ __forceinline__ floatx4 unpack(frag f) { return f; }
     static __device__ __forceinline__ void st(float* p, frag f) { *(floatx4*)p = f; }
 };
+
+// acc += sum over K blocks k < NK of A_k B_k, two blocks per instruction where possible.
+// fa(k), fb(k) return the fragments of 16-wide K block k.
+template <typename MM, int NK, typename FA, typename FB>
+__device__ __forceinline__ floatx4 kchain(FA fa, FB fb, floatx4 acc) {
+#pragma unroll
+    for (int k = 0; k + 1 < NK; k += 2) acc = MM::mma2(fa(k), fa(k + 1), fb(k), fb(k + 1), acc);
+    if (NK & 1) acc = MM::mma(fa(NK - 1), fb(NK - 1), acc);
+    return acc;
+}
 
 // four consecutive output values to global memory
 __device__ __forceinline__ void store4(float* p, floatx4 v) { *(floatx4*)p = v; }
@@ -297,11 +317,11 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             for (int sb = 0; sb <= ib; ++sb) {
                 const int tau = ib * (ib + 1) / 2 + sb;
                 if (tau % NW != wave) continue;
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < NB; ++kb)
-                    acc = MM::mma(MM::ldk(pB_k + 16 * sb * LDN + 16 * kb),
-                                  MM::ldk(pC_k + 16 * ib * LDN + 16 * kb), acc);
+                const T* pb = pB_k + 16 * sb * LDN;
+                const T* pc = pC_k + 16 * ib * LDN;
+                floatx4 acc = kchain<MM, NB>([&](int k) { return MM::ldk(pb + 16 * k); },
+                                             [&](int k) { return MM::ldk(pc + 16 * k); },
+                                             floatx4{0.f, 0.f, 0.f, 0.f});
                 const int i = 16 * ib + l16;
                 const int ti = rT[i];
                 const float l2i = rL2[i], gi = rGam[i];
@@ -313,8 +333,9 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
                 for (int m = 0; m < 4; ++m) {
                     // below the diagonal exp(l_t - l_s) mu_s, on it gamma_t, above it 0
                     const float e = fast_exp2(fminf(l2i - l2s[m], 0.f)) * mus[m];
-                    const float f = tsv[m] < ti ? e : (tsv[m] == ti ? gi : 0.f);
-                    acc[m] *= f;
+                    const float below = tsv[m] < ti ? 1.f : 0.f;
+                    const float diag = tsv[m] == ti ? gi : 0.f;
+                    acc[m] *= fmaf(e, below, diag);
                 }
                 MM::st(sM + i * LDQ + 16 * sb + 4 * g, MM::pack(acc));
                 __builtin_amdgcn_sched_barrier(0);
@@ -333,15 +354,22 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         for (int nb = 0; nb < NB; ++nb) sa[nb] = MM::pack(st[nb]);
 #pragma unroll
         for (int ib = 0; ib < NIB; ++ib) {
-            floatx4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NB; ++kb) y = MM::mma(sa[kb], MM::ldk(pC_k + 16 * ib * LDN + 16 * kb), y);
+            const T* pc = pC_k + 16 * ib * LDN;
+            floatx4 y = kchain<MM, NB>([&](int k) { return sa[k]; }, [&](int k) { return MM::ldk(pc + 16 * k); },
+                                       floatx4{0.f, 0.f, 0.f, 0.f});
             const int i = 16 * ib + l16;
             const float el = rEl[i];
 #pragma unroll
             for (int m = 0; m < 4; ++m) y[m] *= el;
+            const T* pm = pM_k + 16 * ib * LDQ;
+            // K = s over the causal blocks 0..ib (pairs in one instruction, an odd last block alone)
 #pragma unroll
-            for (int sb = 0; sb <= ib; ++sb) y = MM::mma(xf[sb], MM::ldk(pM_k + 16 * ib * LDQ + 16 * sb), y);
+            for (int k = 0; k < NIB; k += 2) {
+                if (k + 1 <= ib)
+                    y = MM::mma2(xf[k], xf[k + 1], MM::ldk(pm + 16 * k), MM::ldk(pm + 16 * (k + 1)), y);
+                else if (k <= ib)
+                    y = MM::mma(xf[k], MM::ldk(pm + 16 * k), y);
+            }
             // lane holds Y[(t, r) = i][p = 16 wave + 4 g + m]
             const int tl = i >> rl2, r = i & rmask;
             const int64_t t = t0 + tl;
@@ -367,17 +395,20 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int m = 0; m < 4; ++m) st[nb][m] *= dec;
+        F xw[NIB];
 #pragma unroll
         for (int sb = 0; sb < NIB; ++sb) {
             floatx4 xs = MM::unpack(xf[sb]);
             const floatx4 ws = *(const floatx4*)(rW + 16 * sb + 4 * g);
 #pragma unroll
             for (int m = 0; m < 4; ++m) xs[m] *= ws[m];
-            const F fx = MM::pack(xs);
+            xw[sb] = MM::pack(xs);
+        }
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                st[nb] = MM::mma(MM::ldt(pB_t + 16 * sb * LDN + 16 * nb, LDN, l16), fx, st[nb]);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int nb = 0; nb < NB; ++nb) {
+            const T* pt = pB_t + 16 * nb;
+            st[nb] = kchain<MM, NIB>([&](int k) { return MM::ldt(pt + 16 * k * LDN, LDN, l16); },
+                                     [&](int k) { return xw[k]; }, st[nb]);
         }
         __syncthreads();
     }
