@@ -13,6 +13,7 @@ fp64 oracle's throughput on a bounded sample of the same prefill workload on the
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +28,37 @@ from state_space_sequence_m3_amd import inputs, m3scan  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 MFMA, TFLOP/s
+
+
+KERNEL_SOURCES = {
+    "prefill_kernel<bf16,128,64,4>": ("prefill.hip", "m3_device.h", "m3_launch.h"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_core_siso_b8_l2048_hbm_traffic.md")
+
+
+def source_digest(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "state_space_sequence_m3_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE record of this kernel, or
+    None if there is none or the kernel's sources changed since the counters were taken."""
+    if kernel not in KERNEL_SOURCES or not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = source_digest(KERNEL_SOURCES[kernel])
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            line = line.strip()
+            if not line.startswith("traffic-record "):
+                continue
+            kv = dict(item.split("=", 1) for item in line.split()[1:])
+            if kv.get("kernel") == kernel and kv.get("workload") == workload and kv.get("digest") == want:
+                return int(kv["fetch_bytes"]) + int(kv["write_bytes"])
+    return None
 
 
 def prefill_bytes_per_token_head(w) -> int:
@@ -239,11 +271,15 @@ def main():
         "m3_bcnorm_rope": {"ms": ms_bc, "bytes": bc_bytes, "GB/s": bc_bytes / ms_bc / 1e6,
                            "hbm_frac": bc_bytes / ms_bc / 1e6 / HBM_PEAK_GBS},
     }
-    dom = "m3_prefill" if ms_pf >= ms_bc else "m3_bcnorm_rope"
-    kd = kernels[dom]
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(kd["GB/s"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
-                "algorithmic_bytes_per_launch": kd["bytes"], "avg_launch_ms": round(kd["ms"], 5)}
+    # the dominant single kernel of the step: m3_prefill is one kernel; m3_bcnorm_rope is three
+    # (segment sums, segment scan, main pass) whose largest is below the prefill kernel
+    kd = kernels["m3_prefill"]
+    kname = "prefill_kernel<bf16,128,64,4>"
+    roofline = {"kernel": "m3_prefill (%s)" % kname, "bound": "hbm", "achieved": round(kd["GB/s"], 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4),
+                "traffic": recorded_traffic(kname, w.name),
+                "algorithmic_bytes_per_launch": kd["bytes"], "avg_launch_ms": round(kd["ms"], 5),
+                "mfma_tflops": round(kd["TFLOP/s"], 1), "mfma_frac_of_bf16_peak": round(kd["mfma_frac"], 4)}
 
     decode = None
     if not args.no_decode:

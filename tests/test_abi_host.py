@@ -1,0 +1,170 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function that
+include/m3scan.h declares, and each validation error is reported with its status and message.
+Validation runs before any device access, so every call here returns before touching a GPU."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from state_space_sequence_m3_amd import m3scan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "m3scan.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(m3_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("m3_bcnorm_rope", "m3_prefill", "m3_decode_step", "m3_last_error",
+              "m3_bcnorm_rope_workspace_bytes", "m3_prefill_workspace_bytes", "m3_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = m3scan.load()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", m3scan.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(m3_[a-z_]+)\b", out))
+    assert set(declared_functions()) <= exported
+    assert set(m3scan.EXPORTED) == set(declared_functions())
+
+
+def test_version():
+    assert "gfx950" in m3scan.version()
+
+
+def _dims(**kw):
+    d = dict(batch=2, seqlen=8, nheads=3, headdim=64, dstate=128, rank=1, chunk=0, io=m3scan.M3_BF16,
+             bcnorm=True, eps=1e-5)
+    d.update(kw)
+    return m3scan.make_dims(**d)
+
+
+P = ctypes.c_void_p
+ALIGNED = 0x10000        # fake, aligned device addresses: validation never dereferences them
+
+
+def _ptrs(n, base=ALIGNED, stride=1 << 24):
+    return [P(base + i * stride) for i in range(n)]
+
+
+def _prefill(dims, ptrs):
+    lib = m3scan.load()
+    return lib.m3_prefill(ctypes.byref(dims), *ptrs, 0, None)
+
+
+def _prefill_args():
+    # x, Bbar, Cbar, dt, A, lam, w_out, h_in, Bbar_prev, x_prev, y, h_out, Bbar_last, x_last, ws
+    p = _ptrs(15)
+    for i in (6, 7, 8, 9, 12, 13, 14):
+        p[i] = None
+    return p
+
+
+def test_prefill_null_pointer():
+    p = _prefill_args()
+    p[0] = None
+    assert _prefill(_dims(), p) == m3scan.M3_E_NULL
+    assert "x is NULL" in m3scan.last_error()
+
+
+def test_prefill_bad_dims():
+    assert _prefill(_dims(dstate=127), _prefill_args()) == m3scan.M3_E_DIMS
+    assert _prefill(_dims(batch=-1), _prefill_args()) == m3scan.M3_E_DIMS
+    assert _prefill(_dims(rank=0), _prefill_args()) == m3scan.M3_E_DIMS
+
+
+def test_prefill_bad_dtype():
+    assert _prefill(_dims(io=7), _prefill_args()) == m3scan.M3_E_DTYPE
+
+
+def test_prefill_unsupported_shape():
+    assert _prefill(_dims(headdim=32), _prefill_args()) == m3scan.M3_E_UNSUPPORTED
+    assert _prefill(_dims(rank=3, chunk=16), _prefill_args()) == m3scan.M3_E_UNSUPPORTED
+    assert _prefill(_dims(chunk=128), _prefill_args()) == m3scan.M3_E_UNSUPPORTED
+    assert "no kernel" in m3scan.last_error()
+
+
+def test_prefill_misaligned():
+    p = _prefill_args()
+    p[1] = P(ALIGNED + (1 << 24) + 8)
+    assert _prefill(_dims(), p) == m3scan.M3_E_ALIGN
+
+
+def test_prefill_output_overlapping_input():
+    p = _prefill_args()
+    p[10] = p[0]    # y on top of x
+    assert _prefill(_dims(), p) == m3scan.M3_E_ALIAS
+
+
+def test_prefill_valid_call_without_gpu_reports_no_device():
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU driver is present; this checks the no-device path")
+    assert _prefill(_dims(), _prefill_args()) == m3scan.M3_E_NODEVICE
+
+
+def test_bcnorm_rope_errors():
+    lib = m3scan.load()
+    # B, C, dt, theta, normw_B, normw_C, bias_B, bias_C, phi_in, Bbar, Cbar, phi_out, ws
+    p = _ptrs(13)
+    for i in (4, 5, 6, 7, 8, 12):
+        p[i] = None
+    d = _dims()
+    call = lambda dims, q, wsb=0: lib.m3_bcnorm_rope(ctypes.byref(dims), *q, wsb, None)
+    q = list(p)
+    q[3] = None
+    assert call(d, q) == m3scan.M3_E_NULL
+    assert call(_dims(dstate=96), p) == m3scan.M3_E_UNSUPPORTED
+    long = _dims(seqlen=4096)
+    assert m3scan.bcnorm_rope_workspace_bytes(long) == 2 * 3 * 8 * 64 * 4
+    assert call(long, p) == m3scan.M3_E_WORKSPACE
+    q = list(p)
+    q[9] = q[0]
+    assert call(d, q) == m3scan.M3_E_ALIAS
+    # phi_out may be the phi_in buffer (angle carried in place) but not partly overlap it.  The
+    # call without its workspace stops at the workspace check, after the alias check, so it
+    # never reaches a device.
+    q = list(p)
+    q[8] = q[11]
+    assert call(long, q) == m3scan.M3_E_WORKSPACE
+    q[8] = P(q[11].value + 8)
+    assert call(long, q) == m3scan.M3_E_ALIAS
+
+
+def test_decode_errors():
+    lib = m3scan.load()
+    # h, Bbar_prev, x_prev, x, Bbar, Cbar, dt, A, lam, w_out, y
+    p = _ptrs(11)
+    p[9] = None
+    call = lambda dims, q: lib.m3_decode_step(ctypes.byref(dims), *q, None)
+    assert call(_dims(seqlen=2), p) == m3scan.M3_E_DIMS
+    assert call(_dims(seqlen=1, headdim=48), p) == m3scan.M3_E_UNSUPPORTED
+    q = list(p)
+    q[0] = P(ALIGNED + 4)
+    assert call(_dims(seqlen=1), q) == m3scan.M3_E_ALIGN
+    q = list(p)
+    q[10] = q[0]
+    assert call(_dims(seqlen=1), q) == m3scan.M3_E_ALIAS
+
+
+def test_workspace_sizes():
+    assert m3scan.prefill_workspace_bytes(_dims()) == 0
+    assert m3scan.bcnorm_rope_workspace_bytes(_dims(seqlen=512)) == 0
+    assert m3scan.bcnorm_rope_workspace_bytes(_dims(seqlen=513)) == 2 * 3 * 2 * 64 * 4
+
+
+def test_binding_raises_without_the_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(m3scan, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        m3scan.load(str(tmp_path / "missing.so"))
