@@ -44,6 +44,59 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTwoPi = 6.283185307179586f;
 constexpr float kInvTwoPi = 0.15915494309189535f;
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS crossbar): a
+// Hillis-Steele scan inside each row of 16 lanes (row_shr 1, 2, 4, 8; lanes with no source get 0),
+// then row 15's total is broadcast into rows 1 and 3 and row 31's into rows 2 and 3.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float wave_scan_add(float v) {
+    v += dpp_move<0x111, 0xf>(v);   // row_shr:1
+    v += dpp_move<0x112, 0xf>(v);   // row_shr:2
+    v += dpp_move<0x114, 0xf>(v);   // row_shr:4
+    v += dpp_move<0x118, 0xf>(v);   // row_shr:8
+    v += dpp_move<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_move<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
+// Sum over aligned groups of R lanes (R = 1, 2, 4, 8 or 16) inside each row of 16 lanes, with DPP
+// moves only: quad_perm swaps inside quads, then half-row and row mirrors, each of which pairs two
+// groups that already hold uniform partial sums.
+__device__ __forceinline__ float group_sum(float v, int R) {
+    if (R >= 2) v += dpp_move<0xB1, 0xf>(v);    // quad_perm [1, 0, 3, 2]
+    if (R >= 4) v += dpp_move<0x4E, 0xf>(v);    // quad_perm [2, 3, 0, 1]
+    if (R >= 8) v += dpp_move<0x141, 0xf>(v);   // row_half_mirror
+    if (R >= 16) v += dpp_move<0x140, 0xf>(v);  // row_mirror
+    return v;
+}
+__device__ __forceinline__ float lane_value(float v, int src_lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_lane));
+}
+
+// Raw buffer access (stride 0): loads at or past `bytes` return zero and stores there are
+// dropped, so the tail of a sequence needs no branches.  The fourth descriptor word is the gfx9
+// default data format.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buffer_store8(rsrc_t r, uint32_t off, uint2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buffer_store16(rsrc_t r, uint32_t off, uint4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
+}
+// bytes of `n` elements, clamped to what a descriptor can hold
+__device__ __forceinline__ uint32_t clamp_bytes(int64_t n) {
+    return n <= 0 ? 0u : (n >= 0xffffffffLL ? 0xffffffffu : (uint32_t)n);
+}
+
 // Reduce an angle to [-pi, pi] (any representative gives the same rotation).
 __device__ __forceinline__ float wrap_angle(float a) { return a - kTwoPi * rintf(a * kInvTwoPi); }
 

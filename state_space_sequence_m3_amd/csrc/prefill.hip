@@ -20,18 +20,27 @@
 //
 // Mapping on gfx950.  One workgroup per (b, h) walks the chunks in order and keeps the N x P fp32
 // state in MFMA accumulator registers, so chunk states never travel through HBM.  A chunk holds
-// QR = Q * R rows (t, r).  Wave w owns the 16 columns [16w, 16w + 16) of P.
-//   1. S^T = Bbar Cbar^T (QR x QR, K = N) on MFMA, only the causal 16x16 tiles, shared out among
-//      the waves; the mask is applied in registers and M = L o S goes to LDS.
-//   2. Y^T (own 16 columns x QR) = state^T Cbar^T * exp(l) + X^T M^T: the state is the A operand
-//      straight from the accumulator registers (an MFMA D tile of S[n][p] is an A tile of S^T).
-//   3. state = exp(l_end) state + (Bbar^T)(w o X), w_s = exp(l_end - l_s) mu_s.
-// The chunk's Bbar, Cbar and x tiles sit in LDS exactly as they are laid out in memory (rows
-// (t, r)), written with 16-byte stores.  Operands that need the other orientation (X^T and
-// Bbar^T, contracted over the rows) are read with gfx950's transposing LDS read
-// (ds_read_b64_tr_b16): in each group of 16 lanes, lane j points at 4 consecutive elements of
-// row k0 + j/4, columns c0 + 4 (j % 4); lane i then receives rows k0..k0+3 of column c0 + i.
-// The next chunk's tiles are loaded into registers while the current chunk computes.
+// QR = Q * R rows (t, r).  Wave w owns the 16 columns [16w, 16w + 16) of P.  Per chunk:
+//   stage  the chunk's Bbar, Cbar and x rows (loaded into registers during the previous chunk) go to
+//          LDS, the next chunk's loads are issued, wave 0 turns dt and lambda into per-row scalars;
+//          barrier.
+//   part 1 everything that needs only this chunk's tiles and the carried state, as independent MFMA
+//          chains interleaved along K: the state part of Y^T (state^T Cbar^T, the state is the A
+//          operand straight from its accumulator registers: an MFMA D tile of S[n][p] is an A tile
+//          of S^T), this wave's share of the causal 16x16 tiles of S^T = Bbar Cbar^T, and the state
+//          update  state = exp(l_end) state + (Bbar^T)(w o X), w_s = exp(l_end - l_s) mu_s.  The
+//          score tiles are masked in registers and M = L o S goes to LDS; barrier.
+//   part 2 Y^T += X^T M^T, then output mixing and the stores.
+// Two barriers per chunk: nothing reads the staged tiles after the second, so the next chunk's
+// staging may overwrite them, and M is rewritten only after the next chunk's first barrier.
+// Operands that need the other orientation (X^T and Bbar^T, contracted over the rows) are read
+// with gfx950's transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane j
+// points at 4 consecutive elements of row k0 + j/4, columns c0 + 4 (j % 4); lane i then receives
+// rows k0..k0+3 of column c0 + i.  LDS rows are padded so that the 32 lanes one cycle serves land
+// on distinct banks (64 banks of 4 bytes): rows read along K get 8 extra elements, rows read with
+// the transposing read 16.
+// Global traffic goes through raw buffer descriptors that end at the sequence's last row: loads
+// past it return zero and stores past it are dropped, so the ragged last chunk needs no branches.
 //
 // Operands: bf16 inputs run v_mfma_f32_16x16x16_bf16 (fp32 accumulate); fp32 inputs run
 // v_mfma_f32_16x16x4_f32 four times per 16-wide K block.  In every product the same lane -> K
@@ -50,7 +59,8 @@ template <typename T> struct Mma;
 
 template <> struct Mma<bf16> {
     typedef shortx4 frag;
-    static constexpr int PAD = 16;  // elements of padding per LDS row (32 bytes)
+    // LDS row padding in elements: tiles read along K (8 bytes a lane), tiles read transposed
+    static constexpr int PADK = 8, PADT = 16;
     // lane gets p[0..3] (4 consecutive elements along K)
     static __device__ __forceinline__ frag ldk(const bf16* p) { return *(const shortx4*)p; }
     // transposed read: `row` points at tile[k0 + 4g][c0] for this lane's group g; lane (l16, g)
@@ -61,13 +71,6 @@ template <> struct Mma<bf16> {
     }
     static __device__ __forceinline__ floatx4 mma(frag a, frag b, floatx4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-    }
-    // two 16-wide K blocks.  They could run as one v_mfma_f32_16x16x32_bf16 (its K slots pair up
-    // symmetrically for A and B), but with this toolchain a VALU write that follows that
-    // instruction can clobber its A/B registers while later passes still read them, so the pair
-    // runs as two 16x16x16 instructions.
-    static __device__ __forceinline__ floatx4 mma2(frag a0, frag a1, frag b0, frag b1, floatx4 c) {
-        return mma(a1, b1, mma(a0, b0, c));
     }
     static __device__ __forceinline__ frag pack(floatx4 v) {
         const uint2 u = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -86,7 +89,7 @@ template <> struct Mma<bf16> {
 
 template <> struct Mma<float> {
     typedef floatx4 frag;
-    static constexpr int PAD = 4;
+    static constexpr int PADK = 8, PADT = 8;
     static __device__ __forceinline__ frag ldk(const float* p) { return *(const floatx4*)p; }
     static __device__ __forceinline__ frag ldt(const float* row, int ld, int l16) {
         frag f;
@@ -103,50 +106,45 @@ template <> struct Mma<float> {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
         return c;
     }
-    static __device__ __forceinline__ floatx4 mma2(frag a0, frag a1, frag b0, frag b1, floatx4 c) {
-        return mma(a1, b1, mma(a0, b0, c));
-    }
     static __device__ __forceinline__ frag pack(floatx4 v) { return v; }
     static __device__ __forceinline__ floatx4 unpack(frag f) { return f; }
     static __device__ __forceinline__ void st(float* p, frag f) { *(floatx4*)p = f; }
 };
 
-// acc += sum over K blocks k < NK of A_k B_k, two blocks per instruction where possible.
-// fa(k), fb(k) return the fragments of 16-wide K block k.
-template <typename MM, int NK, typename FA, typename FB>
-__device__ __forceinline__ floatx4 kchain(FA fa, FB fb, floatx4 acc) {
-#pragma unroll
-    for (int k = 0; k + 1 < NK; k += 2) acc = MM::mma2(fa(k), fa(k + 1), fb(k), fb(k + 1), acc);
-    if (NK & 1) acc = MM::mma(fa(NK - 1), fb(NK - 1), acc);
-    return acc;
+// four consecutive output values through a buffer descriptor
+__device__ __forceinline__ void store4(rsrc_t r, uint32_t off, floatx4 v, float) {
+    buffer_store16(r, off, __builtin_bit_cast(uint4, v));
+}
+__device__ __forceinline__ void store4(rsrc_t r, uint32_t off, floatx4 v, bf16) {
+    buffer_store8(r, off, make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
 }
 
-// four consecutive output values to global memory
-__device__ __forceinline__ void store4(float* p, floatx4 v) { *(floatx4*)p = v; }
-__device__ __forceinline__ void store4(bf16* p, floatx4 v) {
-    *(uint2*)p = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-}
+// causal 16x16 tile number tau = ib (ib + 1) / 2 + sb (sb <= ib < 4) -> row block ib
+__device__ __forceinline__ int tile_ib(int tau) { return (tau >= 1) + (tau >= 3) + (tau >= 6); }
 
 template <typename T, int N, int P, int NIB>
 __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) {
     using MM = Mma<T>;
     using F = typename MM::frag;
     constexpr int NW = P / 16, NT = NW * 64;
-    constexpr int LDN = N + MM::PAD, LDP = P + MM::PAD, LDQ = 64 + MM::PAD;
+    constexpr int QR = 16 * NIB;                 // rows (t, r) per chunk
+    constexpr int NB = N / 16;
+    constexpr int LDC = N + MM::PADK, LDB = N + MM::PADT, LDX = P + MM::PADT, LDM = QR + MM::PADK;
     constexpr int VE = 16 / sizeof(T);           // elements per 16-byte vector
     constexpr int VPN = N / VE, VPP = P / VE;    // vectors per row of Bbar/Cbar and of x
-    constexpr int MAXC = (64 * VPN + NT - 1) / NT;
-    constexpr int MAXX = (64 * VPP + NT - 1) / NT;
-    constexpr int NB = N / 16;
+    static_assert(NT % VPN == 0 && NT % VPP == 0, "vectors per row must divide the block");
+    constexpr int RKC = NT / VPN, RKX = NT / VPP;                // chunk rows per staging step
+    constexpr int MAXC = (QR + RKC - 1) / RKC, MAXX = (QR + RKX - 1) / RKX;
+    constexpr bool FULLC = MAXC * RKC == QR, FULLX = MAXX * RKX == QR;
+    constexpr int NTILE = NIB * (NIB + 1) / 2, NSLOT = (NTILE + NW - 1) / NW;
 
-    __shared__ __align__(16) T sC[64 * LDN];     // Cbar rows of the chunk  [i][n]
-    __shared__ __align__(16) T sB[64 * LDN];     // Bbar rows               [s][n]
-    __shared__ __align__(16) T sX[64 * LDP];     // x rows                  [s][p]
-    __shared__ __align__(16) T sM[64 * LDQ];     // masked scores           [i][s]
+    __shared__ __align__(16) T sC[QR * LDC];     // Cbar rows of the chunk  [i][n]
+    __shared__ __align__(16) T sB[QR * LDB];     // Bbar rows               [s][n]
+    __shared__ __align__(16) T sX[QR * LDX];     // x rows                  [s][p]
+    __shared__ __align__(16) T sM[QR * LDM];     // masked scores           [i][s]
     // per-row (t, r) copies of the chunk's per-step scalars, rewritten every chunk: log2 decay
-    // l_t, gamma_t, mu_t, exp(l_t), w_t = exp(l_end - l_t) mu_t, and the row's step t
+    // l_t, gamma_t, mu_t, exp(l_t) and w_t = exp(l_end - l_t) mu_t
     __shared__ __align__(16) float rL2[64], rGam[64], rMu[64], rEl[64], rW[64];
-    __shared__ __align__(16) int rT[64];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -154,114 +152,103 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / a.H;
     const int h = (int)(bh % a.H);
-    constexpr int QR = 16 * NIB;                 // rows (t, r) per chunk
     const int H = a.H, R = a.R, Q = a.Q;
     const int rl2 = __builtin_ctz((unsigned)R), rmask = R - 1;
     const int64_t L = a.L;
     const int64_t nchunk = (L + Q - 1) / Q;
     const float Alog2 = a.A[h] * kLog2e;
     // (b, t = 0, h) bases; step t of this (b, h) is t * H rows further
-    const int64_t row_bh = b * L * a.H + h;
-    const T* Xg = (const T*)a.x + row_bh * a.R * P;
-    const T* Bg = (const T*)a.Bbar + row_bh * a.R * N;
-    const T* Cg = (const T*)a.Cbar + row_bh * a.R * N;
+    const int64_t row_bh = b * L * H + h;
+    const int64_t HRN = (int64_t)H * R * N, HRP = (int64_t)H * R * P;
+    const T* Xg = (const T*)a.x + row_bh * R * P;
+    const T* Bg = (const T*)a.Bbar + row_bh * R * N;
+    const T* Cg = (const T*)a.Cbar + row_bh * R * N;
     const T* dtg = (const T*)a.dt + row_bh;
     const T* lamg = (const T*)a.lam + row_bh;
     const int pcol = 16 * wave + l16;            // this lane's column of P in MFMA tiles
-    const int64_t HRN = (int64_t)H * R * N, HRP = (int64_t)H * R * P;
+    // bytes from a chunk's first row to the end of the sequence's last row (t = L - 1)
+    auto tail_bytes = [&](int64_t t0, int64_t step, int64_t row) {
+        return clamp_bytes(((L - t0 - 1) * step + row) * (int64_t)sizeof(T));
+    };
 
     // ---- staging: this thread moves 16-byte vectors k = 0, 1, ... of each tile.  Vector k is
-    // chunk row i = i0 + k * (NT / VPN) (row (t, r) = (i >> rl2, i & rmask)), 16-byte column cv0.
-    static_assert(NT % VPN == 0 && NT % VPP == 0, "vectors per row must divide the block");
-    constexpr int RKC = NT / VPN, RKX = NT / VPP;            // chunk rows per k
+    // chunk row i = i0 + k * RK (row (t, r) = (i >> rl2, i & rmask)), 16-byte column c0.
     const int iC0 = tid / VPN, cC0 = tid % VPN, iX0 = tid / VPP, cX0 = tid % VPP;
-    const int HRN32 = H * R * N, HRP32 = H * R * P;
-    auto offC = [&](int k) { const int i = iC0 + k * RKC; return (i >> rl2) * HRN32 + (i & rmask) * N + cC0 * VE; };
-    auto offX = [&](int k) { const int i = iX0 + k * RKX; return (i >> rl2) * HRP32 + (i & rmask) * P + cX0 * VE; };
+    const int HRN32 = (int)HRN, HRP32 = (int)HRP;
+    auto offC = [&](int k) {
+        const int i = iC0 + k * RKC;
+        return (uint32_t)(((i >> rl2) * HRN32 + (i & rmask) * N + cC0 * VE) * (int)sizeof(T));
+    };
+    auto offX = [&](int k) {
+        const int i = iX0 + k * RKX;
+        return (uint32_t)(((i >> rl2) * HRP32 + (i & rmask) * P + cX0 * VE) * (int)sizeof(T));
+    };
 
     // ---- chunk prefetch into registers --------------------------------------------------
     uint4 rc[MAXC], rb[MAXC], rx[MAXX];
-    float rd = 0.f, rl = 0.f, rdn = 0.f, rln = 0.f;
+    float nd = 0.f, nl = 0.f, ndn = 0.f, nln = 0.f;   // wave 0: dt, lambda at t and t + 1
     auto load_chunk = [&](int64_t c) {
         const int64_t t0 = c * Q;
-        const T* cb = Cg + t0 * HRN32;
-        const T* bb = Bg + t0 * HRN32;
-        const T* xb = Xg + t0 * HRP32;
-        if (t0 + Q <= L) {   // a full chunk: every row exists
+        const uint32_t nbc = tail_bytes(t0, HRN, (int64_t)R * N), nbx = tail_bytes(t0, HRP, (int64_t)R * P);
+        const rsrc_t dC = make_rsrc(Cg + t0 * HRN, nbc), dB = make_rsrc(Bg + t0 * HRN, nbc);
+        const rsrc_t dX = make_rsrc(Xg + t0 * HRP, nbx);
 #pragma unroll
-            for (int k = 0; k < MAXC; ++k) {
-                if (iC0 + k * RKC < QR) {
-                    rc[k] = *(const uint4*)(cb + offC(k));
-                    rb[k] = *(const uint4*)(bb + offC(k));
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < MAXX; ++k)
-                if (iX0 + k * RKX < QR) rx[k] = *(const uint4*)(xb + offX(k));
-        } else {             // the ragged last chunk: rows past the sequence end are zero
-            const int nvalid = (int)(L - t0);
-#pragma unroll
-            for (int k = 0; k < MAXC; ++k) {
-                const int i = iC0 + k * RKC;
-                rc[k] = make_uint4(0, 0, 0, 0);
-                rb[k] = make_uint4(0, 0, 0, 0);
-                if (i < QR && (i >> rl2) < nvalid) {
-                    rc[k] = *(const uint4*)(cb + offC(k));
-                    rb[k] = *(const uint4*)(bb + offC(k));
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < MAXX; ++k) {
-                const int i = iX0 + k * RKX;
-                rx[k] = make_uint4(0, 0, 0, 0);
-                if (i < QR && (i >> rl2) < nvalid) rx[k] = *(const uint4*)(xb + offX(k));
+        for (int k = 0; k < MAXC; ++k) {
+            if (FULLC || iC0 + k * RKC < QR) {
+                rc[k] = buffer_load16(dC, offC(k));
+                rb[k] = buffer_load16(dB, offC(k));
             }
         }
+#pragma unroll
+        for (int k = 0; k < MAXX; ++k)
+            if (FULLX || iX0 + k * RKX < QR) rx[k] = buffer_load16(dX, offX(k));
         if (wave == 0) {
             const int64_t t = t0 + lane;
             const bool in = lane < Q && t < L;
             const bool inn = lane < Q && t + 1 < L;
-            rd = in ? load_f32(dtg + t * H) : 0.f;
-            rl = in ? load_f32(lamg + t * H) : 0.f;
-            rdn = inn ? load_f32(dtg + (t + 1) * H) : 0.f;
-            rln = inn ? load_f32(lamg + (t + 1) * H) : 0.f;
+            nd = in ? load_f32(dtg + t * H) : 0.f;
+            nl = in ? load_f32(lamg + t * H) : 0.f;
+            ndn = inn ? load_f32(dtg + (t + 1) * H) : 0.f;
+            nln = inn ? load_f32(lamg + (t + 1) * H) : 0.f;
         }
     };
-    auto store_chunk = [&]() {
+    auto store_tiles = [&]() {
 #pragma unroll
         for (int k = 0; k < MAXC; ++k) {
             const int i = iC0 + k * RKC;
-            if (i < QR) {
-                *(uint4*)(sC + i * LDN + cC0 * VE) = rc[k];
-                *(uint4*)(sB + i * LDN + cC0 * VE) = rb[k];
+            if (FULLC || i < QR) {
+                *(uint4*)(sC + i * LDC + cC0 * VE) = rc[k];
+                *(uint4*)(sB + i * LDB + cC0 * VE) = rb[k];
             }
         }
 #pragma unroll
         for (int k = 0; k < MAXX; ++k) {
             const int i = iX0 + k * RKX;
-            if (i < QR) *(uint4*)(sX + i * LDP + cX0 * VE) = rx[k];
+            if (FULLX || i < QR) *(uint4*)(sX + i * LDX + cX0 * VE) = rx[k];
         }
-        if (wave == 0) {
-            // l_t in log2 units: inclusive prefix sum of dt * A over the chunk
-            float l2 = rd * Alog2;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float n = shfl_up(l2, o);
-                if (lane >= o) l2 += n;
-            }
-            const float gam = rl * rd;
-            const float mu = gam + (1.0f - rln) * rdn;
-            const float l2end = shfl(l2, Q - 1);
-            const float el = fast_exp2(l2);
-            const float w = fast_exp2(fminf(l2end - l2, 0.f)) * mu;
-            // lane = chunk row s; its step is s >> rl2 (rows past Q * R are never read)
+    };
+    // wave 0: the chunk's per-step scalars (lane = step) -> per-row copies in LDS.  Lanes past
+    // the chunk only add to later lanes of the scan, which are never read.
+    auto stage_scalars = [&](float d, float lm, float dn, float lmn) {
+        const float l2 = wave_scan_add(d * Alog2);   // l_t in log2 units, inclusive over the chunk
+        const float gam = lm * d;
+        const float mu = gam + (1.0f - lmn) * dn;
+        const float l2end = lane_value(l2, Q - 1);
+        const float el = fast_exp2(l2);
+        const float w = fast_exp2(fminf(l2end - l2, 0.f)) * mu;
+        if (R == 1) {
+            rL2[lane] = l2;
+            rGam[lane] = gam;
+            rMu[lane] = mu;
+            rEl[lane] = el;
+            rW[lane] = w;
+        } else {   // row s holds step s >> rl2 (rows past Q * R are never read)
             const int ts = lane >> rl2;
             rL2[lane] = shfl(l2, ts);
             rGam[lane] = shfl(gam, ts);
             rMu[lane] = shfl(mu, ts);
             rEl[lane] = shfl(el, ts);
             rW[lane] = shfl(w, ts);
-            rT[lane] = ts;
         }
     };
 
@@ -285,117 +272,54 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         }
     }
 
-    T* ymix = (T*)a.y + row_bh * P;            // [b, L, H, P] when mixing
-    T* yraw = (T*)a.y + row_bh * a.R * P;      // [b, L, H, R, P] otherwise
-
-    // output mixing weights for this lane's (r, 4 columns)
-    floatx4 wo = {1.f, 1.f, 1.f, 1.f};
-    if (a.w_out) {
+    // outputs: mixed [b, L, H, P] with w_out, else [b, L, H, R, P]
+    const bool mix = a.w_out != nullptr;
+    T* yg = (T*)a.y + row_bh * (mix ? P : (int64_t)R * P);
+    const int64_t ystep = mix ? (int64_t)H * P : HRP, yrow = mix ? P : (int64_t)R * P;
+    floatx4 wo = {1.f, 1.f, 1.f, 1.f};          // mixing weights for this lane's (r, 4 columns)
+    if (mix) {
         const int r = l16 & rmask;
 #pragma unroll
         for (int m = 0; m < 4; ++m) wo[m] = a.w_out[(h * R + r) * P + 16 * wave + 4 * g + m];
     }
 
     // loop-invariant LDS fragment addresses for this lane
-    const T* pB_k = sB + l16 * LDN + 4 * g;                 // + 16 sb LDN + 16 kb
-    const T* pC_k = sC + l16 * LDN + 4 * g;                 // + 16 ib LDN + 16 kb
-    const T* pM_k = sM + l16 * LDQ + 4 * g;                 // + 16 ib LDQ + 16 sb
-    const T* pX_t = sX + 4 * g * LDP + 16 * wave;           // + 16 sb LDP
-    const T* pB_t = sB + 4 * g * LDN;                       // + 16 sb LDN + 16 nb
+    const T* pC_k = sC + l16 * LDC + 4 * g;                 // + 16 ib LDC + 16 kb
+    const T* pB_k = sB + l16 * LDB + 4 * g;                 // + 16 sb LDB + 16 kb
+    const T* pM_k = sM + l16 * LDM + 4 * g;                 // + 16 ib LDM + 16 sb
+    const T* pX_t = sX + 4 * g * LDX + 16 * wave;           // + 16 sb LDX
+    const T* pB_t = sB + 4 * g * LDB;                       // + 16 sb LDB + 16 nb
+    // this wave's score tiles: tau = wave, wave + NW, ...; a wave with fewer tiles than NSLOT
+    // recomputes tile NTILE - 1 in its spare slot and drops the copy
+    int sIb[NSLOT], sSb[NSLOT];
+    bool sOn[NSLOT];
+    const T* pSB[NSLOT];
+    const T* pSC[NSLOT];
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j) {
+        const int tau0 = wave + NW * j;
+        sOn[j] = tau0 < NTILE;
+        const int tau = sOn[j] ? tau0 : NTILE - 1;
+        sIb[j] = tile_ib(tau);
+        sSb[j] = tau - sIb[j] * (sIb[j] + 1) / 2;
+        pSB[j] = pB_k + 16 * sSb[j] * LDB;
+        pSC[j] = pC_k + 16 * sIb[j] * LDC;
+    }
 
     if (nchunk > 0) load_chunk(0);
     for (int64_t c = 0; c < nchunk; ++c) {
-        store_chunk();
+        const float cd = nd, cl = nl, cdn = ndn, cln = nln;
+        store_tiles();
+        if (c + 1 < nchunk) load_chunk(c + 1);   // the next chunk's loads fly during this one
+        if (wave == 0) stage_scalars(cd, cl, cdn, cln);
         __syncthreads();
-        if (c + 1 < nchunk) load_chunk(c + 1);
         const int64_t t0 = c * Q;
 
-        // 1. masked scores M[i][s] = L(t_i, t_s) * Cbar_i . Bbar_s on the causal tiles
+        // ---- part 1 -------------------------------------------------------------------------
+        // X^T fragments of this wave's 16 columns, and w o X for the state update
+        F xf[NIB], xw[NIB];
 #pragma unroll
-        for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-            for (int sb = 0; sb <= ib; ++sb) {
-                const int tau = ib * (ib + 1) / 2 + sb;
-                if (tau % NW != wave) continue;
-                const T* pb = pB_k + 16 * sb * LDN;
-                const T* pc = pC_k + 16 * ib * LDN;
-                floatx4 acc = kchain<MM, NB>([&](int k) { return MM::ldk(pb + 16 * k); },
-                                             [&](int k) { return MM::ldk(pc + 16 * k); },
-                                             floatx4{0.f, 0.f, 0.f, 0.f});
-                const int i = 16 * ib + l16;
-                const int ti = rT[i];
-                const float l2i = rL2[i], gi = rGam[i];
-                const floatx4 l2s = *(const floatx4*)(rL2 + 16 * sb + 4 * g);
-                const floatx4 mus = *(const floatx4*)(rMu + 16 * sb + 4 * g);
-                const int4 ts = *(const int4*)(rT + 16 * sb + 4 * g);
-                const int tsv[4] = {ts.x, ts.y, ts.z, ts.w};
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    // below the diagonal exp(l_t - l_s) mu_s, on it gamma_t, above it 0
-                    const float e = fast_exp2(fminf(l2i - l2s[m], 0.f)) * mus[m];
-                    const float below = tsv[m] < ti ? 1.f : 0.f;
-                    const float diag = tsv[m] == ti ? gi : 0.f;
-                    acc[m] *= fmaf(e, below, diag);
-                }
-                MM::st(sM + i * LDQ + 16 * sb + 4 * g, MM::pack(acc));
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        __syncthreads();
-
-        // X^T fragments of this wave's 16 columns, for every 16 rows of the chunk
-        F xf[NIB];
-#pragma unroll
-        for (int sb = 0; sb < NIB; ++sb) xf[sb] = MM::ldt(pX_t + 16 * sb * LDP, LDP, l16);
-
-        // 2. Y^T for this wave's 16 columns: state part, scaled by exp(l_t), plus X^T M^T
-        F sa[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sa[nb] = MM::pack(st[nb]);
-#pragma unroll
-        for (int ib = 0; ib < NIB; ++ib) {
-            const T* pc = pC_k + 16 * ib * LDN;
-            floatx4 y = kchain<MM, NB>([&](int k) { return sa[k]; }, [&](int k) { return MM::ldk(pc + 16 * k); },
-                                       floatx4{0.f, 0.f, 0.f, 0.f});
-            const int i = 16 * ib + l16;
-            const float el = rEl[i];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) y[m] *= el;
-            const T* pm = pM_k + 16 * ib * LDQ;
-            // K = s over the causal blocks 0..ib (pairs in one instruction, an odd last block alone)
-#pragma unroll
-            for (int k = 0; k < NIB; k += 2) {
-                if (k + 1 <= ib)
-                    y = MM::mma2(xf[k], xf[k + 1], MM::ldk(pm + 16 * k), MM::ldk(pm + 16 * (k + 1)), y);
-                else if (k <= ib)
-                    y = MM::mma(xf[k], MM::ldk(pm + 16 * k), y);
-            }
-            // lane holds Y[(t, r) = i][p = 16 wave + 4 g + m]
-            const int tl = i >> rl2, r = i & rmask;
-            const int64_t t = t0 + tl;
-            const bool valid = t < L;
-            const int p = 16 * wave + 4 * g;
-            if (a.w_out) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    float v = y[m] * wo[m];
-                    for (int o = 1; o < R; o <<= 1) v += shfl_xor(v, o);
-                    y[m] = v;
-                }
-                if (valid && r == 0) store4(ymix + t * H * P + p, y);
-            } else if (valid) {
-                store4(yraw + (t * H * R + r) * P + p, y);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // 3. state update: G = exp(l_end) G + Bbar^T (w o X)
-        const float dec = rEl[QR - 1];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) st[nb][m] *= dec;
-        F xw[NIB];
+        for (int sb = 0; sb < NIB; ++sb) xf[sb] = MM::ldt(pX_t + 16 * sb * LDX, LDX, l16);
 #pragma unroll
         for (int sb = 0; sb < NIB; ++sb) {
             floatx4 xs = MM::unpack(xf[sb]);
@@ -404,13 +328,101 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             for (int m = 0; m < 4; ++m) xs[m] *= ws[m];
             xw[sb] = MM::pack(xs);
         }
+        const float dec = rEl[QR - 1];
+        floatx4 y[NIB], acc[NSLOT];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const T* pt = pB_t + 16 * nb;
-            st[nb] = kchain<MM, NIB>([&](int k) { return MM::ldt(pt + 16 * k * LDN, LDN, l16); },
-                                     [&](int k) { return xw[k]; }, st[nb]);
+        for (int ib = 0; ib < NIB; ++ib) y[ib] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // Fragments of K block k: Cbar for every row block, the score tiles' Bbar and Cbar, and
+        // Bbar^T for state rows 16k..16k+15.  Block k + 1 is read while block k computes; the
+        // scheduling barriers keep each read one block ahead of its use and the live registers at
+        // two blocks' worth.
+        F fc[2][NIB], fsb[2][NSLOT], fsc[2][NSLOT], fbt[2][NIB];
+        auto fetch = [&](int k, int s) {
+#pragma unroll
+            for (int ib = 0; ib < NIB; ++ib) fc[s][ib] = MM::ldk(pC_k + 16 * ib * LDC + 16 * k);
+#pragma unroll
+            for (int j = 0; j < NSLOT; ++j) {
+                fsb[s][j] = MM::ldk(pSB[j] + 16 * k);
+                fsc[s][j] = MM::ldk(pSC[j] + 16 * k);
+            }
+#pragma unroll
+            for (int sb = 0; sb < NIB; ++sb) fbt[s][sb] = MM::ldt(pB_t + 16 * sb * LDB + 16 * k, LDB, l16);
+        };
+        fetch(0, 0);
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int s = k & 1;
+            __builtin_amdgcn_sched_barrier(0);
+            if (k + 1 < NB) fetch(k + 1, s ^ 1);
+            // state part of Y^T, K block k (state rows 16k.., before the update)
+            const F sa = MM::pack(st[k]);
+#pragma unroll
+            for (int ib = 0; ib < NIB; ++ib) y[ib] = MM::mma(sa, fc[s][ib], y[ib]);
+            // this wave's S^T tiles
+#pragma unroll
+            for (int j = 0; j < NSLOT; ++j) acc[j] = MM::mma(fsb[s][j], fsc[s][j], acc[j]);
+            // state rows of N block k
+#pragma unroll
+            for (int m = 0; m < 4; ++m) st[k][m] *= dec;
+#pragma unroll
+            for (int sb = 0; sb < NIB; ++sb) st[k] = MM::mma(fbt[s][sb], xw[sb], st[k]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // mask the score tiles: lane holds S^T[s = 16 sb + 4 g + m][i = 16 ib + l16]
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) {
+            if (!sOn[j]) continue;
+            const int i = 16 * sIb[j] + l16, s0 = 16 * sSb[j] + 4 * g;
+            const int ti = i >> rl2;
+            const float l2i = rL2[i], gi = rGam[i];
+            const floatx4 l2s = *(const floatx4*)(rL2 + s0);
+            const floatx4 mus = *(const floatx4*)(rMu + s0);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                // below the diagonal exp(l_t - l_s) mu_s, on it gamma_t, above it 0
+                const int ts = (s0 + m) >> rl2;
+                const float e = fast_exp2(fminf(l2i - l2s[m], 0.f)) * mus[m];
+                const float below = ts < ti ? 1.f : 0.f;
+                const float diag = ts == ti ? gi : 0.f;
+                acc[j][m] *= fmaf(e, below, diag);
+            }
+            MM::st(sM + i * LDM + s0, MM::pack(acc[j]));
+        }
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib) {
+            const float el = rEl[16 * ib + l16];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) y[ib][m] *= el;
         }
         __syncthreads();
+
+        // ---- part 2: Y^T += X^T M^T, mixing, stores ------------------------------------------
+#pragma unroll
+        for (int sb = 0; sb < NIB; ++sb)
+#pragma unroll
+            for (int ib = sb; ib < NIB; ++ib)
+                y[ib] = MM::mma(xf[sb], MM::ldk(pM_k + 16 * ib * LDM + 16 * sb), y[ib]);
+        const rsrc_t dY = make_rsrc(yg + t0 * ystep, tail_bytes(t0, ystep, yrow));
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib) {
+            // lane holds Y[(t, r) = i][p = 16 wave + 4 g + m]
+            const int i = 16 * ib + l16;
+            const int tl = i >> rl2, r = i & rmask;
+            const int p = 16 * wave + 4 * g;
+            floatx4 yv = y[ib];
+            uint32_t off;
+            if (mix) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) yv[m] = group_sum(yv[m] * wo[m], R);
+                // one lane per step stores the mixed row; the others aim past the descriptor
+                off = r == 0 ? (uint32_t)((tl * H * P + p) * (int)sizeof(T)) : 0x80000000u;
+            } else {
+                off = (uint32_t)(((tl * H * R + r) * P + p) * (int)sizeof(T));
+            }
+            store4(dY, off, yv, T{});
+        }
     }
 
     // ---- outputs: final state and the last step's (Bbar, x) ------------------------------
@@ -421,9 +433,9 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     if (L > 0) {
         if (a.Bbar_last)
             for (int e = tid; e < R * N; e += NT)
-                ((T*)a.Bbar_last)[bh * R * N + e] = Bg[(L - 1) * HRN32 + e];
+                ((T*)a.Bbar_last)[bh * R * N + e] = Bg[(L - 1) * HRN + e];
         if (a.x_last)
-            for (int e = tid; e < R * P; e += NT) ((T*)a.x_last)[bh * R * P + e] = Xg[(L - 1) * HRP32 + e];
+            for (int e = tid; e < R * P; e += NT) ((T*)a.x_last)[bh * R * P + e] = Xg[(L - 1) * HRP + e];
     }
 }
 
