@@ -16,6 +16,7 @@
  *
  *   m3_bcnorm_rope   BCNorm + bias + cumulative rotation:  Bbar_t = R(Phi_t)^T Btilde_t, same for C
  *   m3_prefill       chunked scan over a whole sequence (structured-mask matrix form)
+ *   m3_layer_prefill the two above in one pass (rotation applied while staging each chunk)
  *   m3_decode_step   one new token for a batch of resident states
  *
  * Frame of the state.  The state the library keeps, returns and accepts is the rotated frame
@@ -163,6 +164,36 @@ m3_status m3_prefill(const m3_dims* dims, const void* x, const void* Bbar, const
 
 /* Bytes of device workspace m3_prefill needs for these dims. */
 size_t m3_prefill_workspace_bytes(const m3_dims* dims);
+
+/*
+ * m3_layer_prefill -- m3_bcnorm_rope followed by m3_prefill, in one pass over the sequence.
+ *
+ * Defined by: the two calls it stands for (see them above).  papernotes.org, key design 4, notes
+ * that BCNorm, the bias and the rotation only change the projections the scan consumes; here
+ * they are applied while each chunk of raw B and C is staged on chip, so the rotated Bbar and
+ * Cbar never travel through device memory.  The results are those of
+ *
+ *   m3_bcnorm_rope(dims, B, C, dt, theta, normw_B, normw_C, bias_B, bias_C, phi_in,
+ *                  Bbar, Cbar, phi_out)
+ *   m3_prefill(dims, x, Bbar, Cbar, dt, A, lam, w_out, h_in, Bbar_prev, x_prev,
+ *              y, h_out, Bbar_last, x_last)
+ *
+ * up to rounding order (the rotated values are rounded to the io type at the same point).
+ * Arguments are those of the two calls, with the same shapes, optionality and meaning; Bbar_last
+ * receives the rotated Bbar of the last step, as m3_prefill would return it.  dims->chunk = 0
+ * picks 32 / R steps per chunk.  h_out may be the h_in buffer and phi_out the phi_in buffer;
+ * no other output may overlap an input.  This build has kernels for (N, P) in {(16, 16),
+ * (64, 64), (128, 64)}, R in {1, 2, 4, 8, 16} and chunk * R in {16, 32}, or 64 when R <= 4;
+ * other shapes return M3_E_UNSUPPORTED.  No workspace is needed (pass NULL, 0).
+ */
+m3_status m3_layer_prefill(const m3_dims* dims, const void* x, const void* B, const void* C,
+                           const void* dt, const void* theta, const float* normw_B,
+                           const float* normw_C, const float* bias_B, const float* bias_C,
+                           const float* A, const void* lam, const float* w_out,
+                           const float* phi_in, const float* h_in, const void* Bbar_prev,
+                           const void* x_prev, void* y, float* h_out, float* phi_out,
+                           void* Bbar_last, void* x_last, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /*
  * m3_decode_step -- one new token for each of b * H resident states, updated in place.

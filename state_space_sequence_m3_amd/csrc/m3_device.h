@@ -68,6 +68,23 @@ __device__ __forceinline__ float group_sum(float v, int R) {
     if (R >= 4) v += dpp_move<0x4E, 0xf>(v);    // quad_perm [2, 3, 0, 1]
     if (R >= 8) v += dpp_move<0x141, 0xf>(v);   // row_half_mirror
     if (R >= 16) v += dpp_move<0x140, 0xf>(v);  // row_mirror
+    if (R >= 32) v += __shfl_xor(v, 16, 64);
+    if (R >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+// Inclusive prefix sum inside aligned groups of W lanes (W a power of two, at most 64).  Inside a
+// row of 16 lanes it is the Hillis-Steele steps of wave_scan_add, with the steps that would reach
+// across a group of fewer than 16 lanes masked off.
+template <int W>
+__device__ __forceinline__ float seg_scan_add(float v, int lane) {
+    static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+    const int j = lane & (W - 1);
+    if (W >= 2) { const float u = dpp_move<0x111, 0xf>(v); v += (W >= 16 || j >= 1) ? u : 0.f; }
+    if (W >= 4) { const float u = dpp_move<0x112, 0xf>(v); v += (W >= 16 || j >= 2) ? u : 0.f; }
+    if (W >= 8) { const float u = dpp_move<0x114, 0xf>(v); v += (W >= 16 || j >= 4) ? u : 0.f; }
+    if (W >= 16) v += dpp_move<0x118, 0xf>(v);
+    if (W >= 32) v += dpp_move<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    if (W >= 64) v += dpp_move<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
     return v;
 }
 __device__ __forceinline__ float lane_value(float v, int src_lane) {

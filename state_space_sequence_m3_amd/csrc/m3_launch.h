@@ -64,6 +64,17 @@ struct PrefillArgs {
     int64_t b, L;
     int H, N, P, R;
     int Q;                // time steps per chunk; Q * R rows per chunk tile (16..64)
+    // fused layer only (launch_layer): Bbar and Cbar above then point at the raw B and C, which
+    // the kernel normalises, biases and rotates while staging each chunk
+    const void* theta = nullptr;
+    const float* normw_B = nullptr;
+    const float* normw_C = nullptr;
+    const float* bias_B = nullptr;
+    const float* bias_C = nullptr;
+    const float* phi_in = nullptr;
+    float* phi_out = nullptr;
+    int bcnorm = 0;
+    float eps = 0.f;
 };
 
 bool decode_supported(int N, int P, int R);
@@ -75,5 +86,8 @@ hipError_t launch_bcnorm_rope(const BcnormRopeArgs& a, bool bf16_io, hipStream_t
 
 bool prefill_supported(int N, int P, int R, int QR, bool bf16_io);
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16_io, hipStream_t s);
+
+bool layer_supported(int N, int P, int R, int QR, bool bf16_io);
+hipError_t launch_layer(const PrefillArgs& a, bool bf16_io, hipStream_t s);
 
 }  // namespace m3

@@ -122,7 +122,30 @@ __device__ __forceinline__ void store4(rsrc_t r, uint32_t off, floatx4 v, bf16) 
 // causal 16x16 tile number tau = ib (ib + 1) / 2 + sb (sb <= ib < 4) -> row block ib
 __device__ __forceinline__ int tile_ib(int tau) { return (tau >= 1) + (tau >= 3) + (tau >= 6); }
 
-template <typename T, int N, int P, int NIB>
+// unpack one 16-byte vector of io elements to floats
+__device__ __forceinline__ void unpack16(uint4 v, float (&o)[4], float) {
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ void unpack16(uint4 v, float (&o)[8], bf16) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(w[i] << 16);
+        o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ uint4 pack16(const float (&v)[4], float) {
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+}
+__device__ __forceinline__ uint4 pack16(const float (&v)[8], bf16) {
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+
+// FUSED: the chunk's B and C arrive raw and are normalised (BCNorm), biased and rotated by the
+// cumulative angle while they are staged (papernotes.org, key design 4; aipaper.cc section 4.2
+// Proposition 3), so the rotated Bbar and Cbar never go through HBM.
+template <typename T, int N, int P, int NIB, bool FUSED>
 __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) {
     using MM = Mma<T>;
     using F = typename MM::frag;
@@ -137,6 +160,14 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     constexpr int MAXC = (QR + RKC - 1) / RKC, MAXX = (QR + RKX - 1) / RKX;
     constexpr bool FULLC = MAXC * RKC == QR, FULLX = MAXX * RKX == QR;
     constexpr int NTILE = NIB * (NIB + 1) / 2, NSLOT = (NTILE + NW - 1) / NW;
+    // fused angle scan: K rotation pairs, VT angle increments per 16-byte theta vector, NVT vectors
+    // per step; thread tau scans column v = tau / TPV over steps j * SPT .. j * SPT + SPT - 1
+    constexpr int K = N / 2, VT = VE, NVT = K / VT;
+    constexpr int SPT = NVT * QR > NT ? NVT * QR / NT : 1, TPV = FUSED ? QR / SPT : 16;
+    static_assert(!FUSED || (TPV <= 64 && NVT * TPV <= NT && (QR & (QR - 1)) == 0), "angle scan layout");
+    constexpr int LDPHI = K + 8;                 // padded angle rows (fp32)
+    constexpr int RB = NIB > 2 ? 4 : 16;         // ranks whose bias fits in LDS
+    constexpr int FZ = FUSED ? 1 : 0;            // sizes the fused-only LDS arrays
 
     __shared__ __align__(16) T sC[QR * LDC];     // Cbar rows of the chunk  [i][n]
     __shared__ __align__(16) T sB[QR * LDB];     // Bbar rows               [s][n]
@@ -145,6 +176,10 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // per-row (t, r) copies of the chunk's per-step scalars, rewritten every chunk: log2 decay
     // l_t, gamma_t, mu_t, exp(l_t) and w_t = exp(l_end - l_t) mu_t
     __shared__ __align__(16) float rL2[64], rGam[64], rMu[64], rEl[64], rW[64];
+    // fused only: the chunk's angles Phi[t][k], BCNorm weights [B, C][n], biases [B, C][r][n]
+    __shared__ __align__(16) float sPhi[FZ * QR * LDPHI + 1];
+    __shared__ __align__(16) float sWt[FZ * 2 * N + 1];
+    __shared__ __align__(16) float sBias[FZ * 2 * RB * N + 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -212,13 +247,113 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             nln = inn ? load_f32(lamg + (t + 1) * H) : 0.f;
         }
     };
+    // ---- fused: angle increments of a chunk and their prefix scan ----------------------
+    const int tau = tid, tv = tau / TPV, tj = tau % TPV;
+    const bool scanner = FUSED && tau < NVT * TPV;
+    uint4 rth[SPT];
+    float rdt[SPT];
+    const T* thg = (const T*)a.theta + row_bh * K;
+    const int64_t HK = (int64_t)H * K;
+    auto load_theta = [&](int64_t c) {
+        if (!scanner) return;
+        const int64_t t0 = c * Q;
+        const rsrc_t dT = make_rsrc(thg + t0 * HK, tail_bytes(t0, HK, K));
+#pragma unroll
+        for (int s = 0; s < SPT; ++s) {
+            const int t = tj * SPT + s;
+            const bool in = t < Q;   // steps past the chunk (R > 1 leaves rows of the tile unused)
+            rth[s] = in ? buffer_load16(dT, (uint32_t)((t * (int)HK + tv * VT) * (int)sizeof(T)))
+                        : make_uint4(0, 0, 0, 0);
+            rdt[s] = in && t0 + t < L ? load_f32(dtg + (t0 + t) * H) : 0.f;
+        }
+    };
+    // Phi[t] = Phi[t0 - 1] + sum_{t0 <= i <= t} dt_i theta_i for the chunk starting at c * Q, into
+    // sPhi.  The carried angle is the previous chunk's last row, read by the same wave that
+    // rewrites it (reads come before writes in one wave's LDS order); chunk 0 starts from phi_in.
+    auto scan = [&](int64_t c) {
+        if (!scanner) return;
+        float acc[SPT][VT];
+#pragma unroll
+        for (int s = 0; s < SPT; ++s) {
+            float f[VT];
+            unpack16(rth[s], f, T{});
+#pragma unroll
+            for (int e = 0; e < VT; ++e) acc[s][e] = (s ? acc[s - 1][e] : 0.f) + rdt[s] * f[e];
+        }
+        float base[VT];
+#pragma unroll
+        for (int e = 0; e < VT; ++e) {
+            const int k = tv * VT + e;
+            const float carry = c == 0 ? (a.phi_in ? wrap_angle(a.phi_in[bh * K + k]) : 0.f)
+                                       : sPhi[(Q - 1) * LDPHI + k];
+            const float tot = acc[SPT - 1][e];
+            base[e] = carry + seg_scan_add<TPV>(tot, lane) - tot;
+        }
+#pragma unroll
+        for (int s = 0; s < SPT; ++s) {
+            float* dst = sPhi + (tj * SPT + s) * LDPHI + tv * VT;
+#pragma unroll
+            for (int e = 0; e < VT; e += 4)
+                *(floatx4*)(dst + e) = floatx4{wrap_angle(base[e] + acc[s][e]), wrap_angle(base[e + 1] + acc[s][e + 1]),
+                                               wrap_angle(base[e + 2] + acc[s][e + 2]), wrap_angle(base[e + 3] + acc[s][e + 3])};
+        }
+    };
+    // fused: raw B and C rows of this thread -> BCNorm, weight, bias, rotation -> LDS
+    const float invN = 1.0f / (float)N;
+    auto stage_bc = [&](int k, int i) {
+        const int t = i >> rl2, r = i & rmask;
+        float xb[VE], xc[VE];
+        unpack16(rb[k], xb, T{});
+        unpack16(rc[k], xc, T{});
+        float sb = 1.f, sc = 1.f;
+        if (a.bcnorm) {   // RMS over the row's N values, spread over VPN consecutive lanes
+            float qb = 0.f, qc = 0.f;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                qb = fmaf(xb[e], xb[e], qb);
+                qc = fmaf(xc[e], xc[e], qc);
+            }
+            qb = group_sum(qb, VPN);
+            qc = group_sum(qc, VPN);
+            sb = rsqrtf(fmaf(qb, invN, a.eps));
+            sc = rsqrtf(fmaf(qc, invN, a.eps));
+        }
+        const int n0 = cC0 * VE;
+        const float* wB = sWt + n0;
+        const float* wC = sWt + N + n0;
+        const float* bB = sBias + r * N + n0;
+        const float* bC = sBias + (RB + r) * N + n0;
+        const float* ph = sPhi + t * LDPHI + n0 / 2;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            xb[e] = fmaf(xb[e] * sb, wB[e], bB[e]);
+            xc[e] = fmaf(xc[e] * sc, wC[e], bC[e]);
+        }
+#pragma unroll
+        for (int q = 0; q < VE / 2; ++q) {
+            float sn, cs;
+            __sincosf(ph[q], &sn, &cs);   // |angle| <= pi
+            const float b0 = xb[2 * q], b1 = xb[2 * q + 1], c0 = xc[2 * q], c1 = xc[2 * q + 1];
+            xb[2 * q] = fmaf(cs, b0, sn * b1);
+            xb[2 * q + 1] = fmaf(cs, b1, -sn * b0);
+            xc[2 * q] = fmaf(cs, c0, sn * c1);
+            xc[2 * q + 1] = fmaf(cs, c1, -sn * c0);
+        }
+        *(uint4*)(sC + i * LDC + n0) = pack16(xc, T{});
+        *(uint4*)(sB + i * LDB + n0) = pack16(xb, T{});
+    };
+
     auto store_tiles = [&]() {
 #pragma unroll
         for (int k = 0; k < MAXC; ++k) {
             const int i = iC0 + k * RKC;
             if (FULLC || i < QR) {
-                *(uint4*)(sC + i * LDC + cC0 * VE) = rc[k];
-                *(uint4*)(sB + i * LDB + cC0 * VE) = rb[k];
+                if (FUSED) {
+                    stage_bc(k, i);
+                } else {
+                    *(uint4*)(sC + i * LDC + cC0 * VE) = rc[k];
+                    *(uint4*)(sB + i * LDB + cC0 * VE) = rb[k];
+                }
             }
         }
 #pragma unroll
@@ -306,10 +441,28 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         pSC[j] = pC_k + 16 * sIb[j] * LDC;
     }
 
+    if (FUSED) {
+        // BCNorm weights (1 without BCNorm or without weights) and biases (0 when absent)
+        for (int e = tid; e < 2 * N; e += NT) {
+            const float* w = e < N ? a.normw_B : a.normw_C;
+            sWt[e] = a.bcnorm && w ? w[h * N + (e % N)] : 1.f;
+        }
+        for (int e = tid; e < 2 * RB * N; e += NT) {
+            const int which = e / (RB * N), r = (e / N) % RB;
+            const float* bias = which == 0 ? a.bias_B : a.bias_C;
+            sBias[e] = bias && r < R ? bias[(h * R + r) * N + (e % N)] : 0.f;
+        }
+        if (nchunk > 0) {
+            load_theta(0);
+            scan(0);
+        }
+        __syncthreads();
+    }
     if (nchunk > 0) load_chunk(0);
     for (int64_t c = 0; c < nchunk; ++c) {
         const float cd = nd, cl = nl, cdn = ndn, cln = nln;
         store_tiles();
+        if (FUSED && c + 1 < nchunk) load_theta(c + 1);   // scanned at the end of this chunk's part 1
         if (c + 1 < nchunk) load_chunk(c + 1);   // the next chunk's loads fly during this one
         if (wave == 0) stage_scalars(cd, cl, cdn, cln);
         __syncthreads();
@@ -370,6 +523,8 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             for (int sb = 0; sb < NIB; ++sb) st[k] = MM::mma(fbt[s][sb], xw[sb], st[k]);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // fused: angles of the next chunk (its staging reads them after the coming barrier)
+        if (FUSED && c + 1 < nchunk) scan(c + 1);
         // mask the score tiles: lane holds S^T[s = 16 sb + 4 g + m][i = 16 ib + l16]
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
@@ -431,32 +586,44 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
         for (int m = 0; m < 4; ++m) a.h_out[(bh * N + 16 * nb + 4 * g + m) * P + pcol] = st[nb][m];
     if (L > 0) {
-        if (a.Bbar_last)
-            for (int e = tid; e < R * N; e += NT)
-                ((T*)a.Bbar_last)[bh * R * N + e] = Bg[(L - 1) * HRN + e];
+        // the last chunk's tiles are still in LDS (nothing is staged after it)
+        const int tlast = (int)(L - 1 - (nchunk - 1) * Q);
+        if (a.Bbar_last) {
+            for (int e = tid; e < R * N; e += NT) {
+                T v;
+                if (FUSED) v = sB[(tlast * R + e / N) * LDB + e % N];   // rotated here, never in HBM
+                else v = Bg[(L - 1) * HRN + e];
+                ((T*)a.Bbar_last)[bh * R * N + e] = v;
+            }
+        }
         if (a.x_last)
             for (int e = tid; e < R * P; e += NT) ((T*)a.x_last)[bh * R * P + e] = Xg[(L - 1) * HRP + e];
+        if (FUSED && a.phi_out)
+            for (int k = tid; k < K; k += NT) a.phi_out[bh * K + k] = sPhi[(Q - 1) * LDPHI + k];
     }
 }
 
-template <typename T, int N, int P>
+template <typename T, int N, int P, bool FUSED>
 hipError_t launch_np(const PrefillArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)(a.b * a.H)), block(P / 16 * 64);
     switch (a.Q * a.R) {
-        case 16: hipLaunchKernelGGL((prefill_kernel<T, N, P, 1>), grid, block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((prefill_kernel<T, N, P, 2>), grid, block, 0, s, a); break;
-        case 48: hipLaunchKernelGGL((prefill_kernel<T, N, P, 3>), grid, block, 0, s, a); break;
-        case 64: hipLaunchKernelGGL((prefill_kernel<T, N, P, 4>), grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((prefill_kernel<T, N, P, 1, FUSED>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((prefill_kernel<T, N, P, 2, FUSED>), grid, block, 0, s, a); break;
+        case 48:
+            if (FUSED) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((prefill_kernel<T, N, P, 3, false>), grid, block, 0, s, a);
+            break;
+        case 64: hipLaunchKernelGGL((prefill_kernel<T, N, P, 4, FUSED>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool FUSED>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
-    if (a.N == 16 && a.P == 16) return launch_np<T, 16, 16>(a, s);
-    if (a.N == 64 && a.P == 64) return launch_np<T, 64, 64>(a, s);
-    if (a.N == 128 && a.P == 64) return launch_np<T, 128, 64>(a, s);
+    if (a.N == 16 && a.P == 16) return launch_np<T, 16, 16, FUSED>(a, s);
+    if (a.N == 64 && a.P == 64) return launch_np<T, 64, 64, FUSED>(a, s);
+    if (a.N == 128 && a.P == 64) return launch_np<T, 128, 64, FUSED>(a, s);
     return hipErrorInvalidValue;
 }
 
@@ -470,7 +637,17 @@ bool prefill_supported(int N, int P, int R, int QR, bool /*bf16_io*/) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16_io, hipStream_t s) {
-    return bf16_io ? launch_t<bf16>(a, s) : launch_t<float>(a, s);
+    return bf16_io ? launch_t<bf16, false>(a, s) : launch_t<float, false>(a, s);
+}
+
+bool layer_supported(int N, int P, int R, int QR, bool bf16_io) {
+    // chunk rows 16, 32 or 64 (the angle scan wants a power-of-two step count); the 64-row tile
+    // keeps the biases of at most 4 ranks in LDS
+    return prefill_supported(N, P, R, QR, bf16_io) && QR != 48 && (QR < 48 || R <= 4);
+}
+
+hipError_t launch_layer(const PrefillArgs& a, bool bf16_io, hipStream_t s) {
+    return bf16_io ? launch_t<bf16, true>(a, s) : launch_t<float, true>(a, s);
 }
 
 }  // namespace m3

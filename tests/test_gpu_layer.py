@@ -1,0 +1,147 @@
+"""GPU parity of m3_layer_prefill (BCNorm, bias and rotation applied while each chunk is staged,
+then the chunked scan) against the fp64 oracle's layer core (oracle.layer = bcnorm_rope then
+scan), on seeded inputs that span several chunks and end in a ragged tail.  Every call goes
+through the C ABI (via the ctypes binding).  Tolerances are those of gpu_util.TOL."""
+from __future__ import annotations
+
+import math
+
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, angle_err, per_head_rel_err, rel_err, to_dev
+from state_space_sequence_m3_amd import inputs, m3scan
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _wl(io, b, L, H, P, N, R, Q, bcnorm=True, bias=True, mix=False, theta_std=1.0):
+    return inputs.Workload("case", b, L, H, P, N, R, Q, io, bcnorm, bias, mix, theta_std)
+
+
+def _run(d, w, chunk, mix, **kw):
+    return m3scan.m3_layer_prefill(d["x"], d["B"], d["C"], d["dt"], d["theta"], d["A"], d["lam"],
+                                   d.get("normw_B"), d.get("normw_C"), d.get("bias_B"), d.get("bias_C"),
+                                   d["w_out"] if mix else None, d.get("phi_in"), d.get("h_in"),
+                                   d.get("Bbar_prev"), d.get("x_prev"), chunk=chunk, bcnorm=w.bcnorm,
+                                   **kw)
+
+
+LAYER_CASES = [
+    # io, b, L, H, P, N, R, chunk, bcnorm, normw, bias, mix, carry, theta_std
+    ("f32", 1, 64, 1, 16, 16, 1, 16, False, False, False, False, False, 1.0),  # tiny SISO fp32
+    ("f32", 2, 75, 2, 16, 16, 2, 8, True, True, True, True, True, 1.0),
+    ("bf16", 2, 333, 3, 64, 128, 1, 32, True, True, True, False, True, 1.0),
+    ("bf16", 2, 200, 3, 64, 128, 1, 16, True, False, True, False, True, 1.0),
+    ("bf16", 1, 333, 3, 64, 128, 1, 64, True, True, True, False, True, 1.0),
+    ("bf16", 1, 150, 3, 64, 128, 4, 8, True, True, True, True, True, 1.0),
+    ("bf16", 1, 150, 2, 64, 128, 4, 16, True, True, True, True, False, 1.0),
+    ("bf16", 1, 90, 2, 64, 128, 2, 16, True, False, True, False, True, 1.0),
+    ("f32", 1, 70, 2, 64, 64, 1, 32, True, True, True, False, True, 1.0),
+    ("bf16", 1, 70, 2, 64, 64, 8, 2, True, True, True, True, True, 1.0),
+    ("bf16", 1, 100, 2, 64, 128, 16, 2, True, True, True, True, True, 1.0),
+    ("bf16", 1, 257, 2, 64, 128, 1, 32, True, True, True, False, True, math.pi),
+    ("bf16", 2, 129, 2, 64, 128, 1, 32, False, False, False, False, False, 1.0),
+    ("f32", 1, 45, 2, 64, 128, 4, 8, True, True, True, True, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", LAYER_CASES,
+                         ids=lambda c: "%s-b%d-L%d-H%d-P%d-N%d-R%d-Q%d" % c[:8])
+def test_layer_parity(case):
+    io, b, L, H, P, N, R, Q, bcnorm, normw, bias, mix, carry, tstd = case
+    w = _wl(io, b, L, H, P, N, R, Q, bcnorm, bias, mix, tstd)
+    inp = inputs.make_prefill_inputs(w, seed=31, normw=normw, carry=carry)
+    d = to_dev(inp, DEV)
+    Blast = torch.empty((b, H, R, N), dtype=w.torch_io, device=DEV)
+    xlast = torch.empty((b, H, R, P), dtype=w.torch_io, device=DEV)
+    y, h, phi = _run(d, w, Q, mix, Bbar_last=Blast, x_last=xlast)
+    torch.cuda.synchronize()
+    ref = oracle.layer(inp, bcnorm=bcnorm, mix=mix)
+    tol = TOL[io]
+    assert rel_err(y, ref["y"]) <= tol
+    assert per_head_rel_err(y, ref["y"], 2 if mix else 3) <= 2 * tol
+    assert rel_err(h, ref["h_out"]) <= tol
+    assert angle_err(phi, ref["phi_out"]) <= (1e-3 if io == "bf16" else 1e-4)
+    assert rel_err(Blast, ref["Bbar_last"]) <= tol
+    assert rel_err(xlast, ref["x_last"]) == 0.0
+
+
+def test_layer_default_chunk():
+    w = _wl("bf16", 1, 100, 2, 64, 128, 4, 0, mix=True)
+    inp = inputs.make_prefill_inputs(w, seed=32, carry=True)
+    d = to_dev(inp, DEV)
+    y, h, phi = _run(d, w, 0, True)
+    torch.cuda.synchronize()
+    ref = oracle.layer(inp, bcnorm=True, mix=True)
+    assert rel_err(y, ref["y"]) <= TOL["bf16"]
+    assert rel_err(h, ref["h_out"]) <= TOL["bf16"]
+
+
+def test_layer_split_carry():
+    """layer(0..t1) then layer(t1..L) with every carry passed on equals the oracle over 0..L."""
+    w = _wl("bf16", 2, 300, 2, 64, 128, 2, 16, mix=True)
+    inp = inputs.make_prefill_inputs(w, seed=33, normw=True, carry=True)
+    d = to_dev(inp, DEV)
+    t1 = 113
+    first = {k: (v[:, :t1] if k in ("x", "B", "C", "dt", "lam", "theta") else v) for k, v in d.items()}
+    second = {k: (v[:, t1:] if k in ("x", "B", "C", "dt", "lam", "theta") else v) for k, v in d.items()}
+    b, H, R, N, P = 2, 2, 2, 128, 64
+    Blast = torch.empty((b, H, R, N), dtype=torch.bfloat16, device=DEV)
+    xlast = torch.empty((b, H, R, P), dtype=torch.bfloat16, device=DEV)
+    y1, h1, phi1 = _run({k: v.contiguous() for k, v in first.items()}, w, 16, True,
+                        Bbar_last=Blast, x_last=xlast)
+    second = {k: v.contiguous() for k, v in second.items()}
+    second.update(h_in=h1, phi_in=phi1, Bbar_prev=Blast, x_prev=xlast)
+    y2, h2, phi2 = _run(second, w, 16, True)
+    torch.cuda.synchronize()
+    ref = oracle.layer(inp, bcnorm=True, mix=True)
+    y = torch.cat([y1, y2], dim=1)
+    assert rel_err(y, ref["y"]) <= TOL["bf16"]
+    assert rel_err(h2, ref["h_out"]) <= TOL["bf16"]
+    assert angle_err(phi2, ref["phi_out"]) <= 1e-3
+
+
+def test_layer_in_place_state_and_angle():
+    w = _wl("bf16", 1, 97, 2, 64, 128, 1, 32)
+    inp = inputs.make_prefill_inputs(w, seed=34, carry=True)
+    d = to_dev(inp, DEV)
+    h = d["h_in"].clone()
+    phi = d["phi_in"].clone()
+    d2 = dict(d, h_in=h, phi_in=phi)
+    _run(d2, w, 32, False, h_out=h, phi_out=phi)
+    torch.cuda.synchronize()
+    ref = oracle.layer(inp, bcnorm=True, mix=False)
+    assert rel_err(h, ref["h_out"]) <= TOL["bf16"]
+    assert angle_err(phi, ref["phi_out"]) <= 1e-3
+
+
+def test_layer_empty_sequence_passes_the_carry_through():
+    w = _wl("bf16", 2, 0, 2, 64, 128, 1, 32)
+    inp = inputs.make_prefill_inputs(w, seed=35, carry=True)
+    d = to_dev(inp, DEV)
+    Blast = torch.full_like(d["Bbar_prev"], 7.0)
+    xlast = torch.full_like(d["x_prev"], 7.0)
+    y, h, phi = _run(d, w, 32, False, Bbar_last=Blast, x_last=xlast)
+    torch.cuda.synchronize()
+    assert y.numel() == 0
+    assert torch.equal(h, d["h_in"])
+    assert torch.equal(Blast, d["Bbar_prev"])
+    assert torch.equal(xlast, d["x_prev"])
+    assert angle_err(phi, inp["phi_in"].double().numpy()) <= 1e-6
+
+
+def test_layer_unsupported_chunk_is_rejected():
+    w = _wl("bf16", 1, 48, 1, 64, 128, 1, 48)
+    d = to_dev(inputs.make_prefill_inputs(w, seed=36), DEV)
+    with pytest.raises(m3scan.M3Error) as e:
+        _run(d, w, 48, False)
+    assert e.value.status == m3scan.M3_E_UNSUPPORTED
+    w = _wl("bf16", 1, 48, 1, 64, 128, 8, 8)
+    d = to_dev(inputs.make_prefill_inputs(w, seed=36), DEV)
+    with pytest.raises(m3scan.M3Error) as e:
+        _run(d, w, 8, False)
+    assert e.value.status == m3scan.M3_E_UNSUPPORTED
