@@ -1,12 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the Mamba-3 SSM layer core on one MI355X.
 
-One step = one pass of the layer core over one batch of the SISO workload (b=8, L=2048, H=64,
-P=64, N=128, R=1, chunk 64, bf16 io, fp32 state): m3_bcnorm_rope then m3_prefill.  `value` is
-prefill tokens/s (b * L tokens per step).  The same JSON line carries decode throughput on the
-B=128 decode workloads (R=1 and R=4: m3_bcnorm_rope with L=1 then m3_decode_step per token),
-the roofline of the dominant kernel measured live with HIP events on the launch stream, and the
-fp64 oracle's throughput on a bounded sample of the same prefill workload on the host cores.
+One step = one pass of the layer core (BCNorm + bias + rotation, then the chunked scan) over one
+batch of the SISO workload (b=8, L=2048, H=64, P=64, N=128, R=1, bf16 io, fp32 state) through
+m3_layer_prefill, which does both in one kernel (chunk 32).  `value` is prefill tokens/s (b * L
+tokens per step).  The same line times the two-call path (m3_bcnorm_rope then m3_prefill, chunk
+64) for comparison, the MIMO R=4 workload through both paths, decode throughput on the B=128
+decode workloads (R=1 and R=4: m3_bcnorm_rope with L=1 then m3_decode_step per token), the
+roofline of the dominant kernel measured live with HIP events on the launch stream, and the fp64
+oracle's throughput on a bounded sample of the same prefill workload on the host cores.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
 """
@@ -32,7 +34,9 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 MFMA, TFLOP/s
 
 KERNEL_SOURCES = {
     "prefill_kernel<bf16,128,64,4>": ("prefill.hip", "m3_device.h", "m3_launch.h"),
+    "prefill_kernel<bf16,128,64,2,fused>": ("prefill.hip", "m3_device.h", "m3_launch.h"),
 }
+LAYER_CHUNK_ROWS = 32   # chunk * R rows per tile of the fused kernel
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_core_siso_b8_l2048_hbm_traffic.md")
 
 
@@ -77,6 +81,14 @@ def bcnorm_bytes_per_token_head(w) -> int:
     return es * (4 * R * N + N // 2 + 1)
 
 
+def layer_bytes_per_token_head(w) -> int:
+    """m3_layer_prefill: x, raw B and C, theta, dt, lam read once, y written once."""
+    es = 2 if w.io == "bf16" else 4
+    R, N, P = w.rank, w.dstate, w.headdim
+    y = P if w.mix else R * P
+    return es * (R * P + 2 * R * N + N // 2 + 2 + y)
+
+
 def prefill_flops_per_token_head(w) -> int:
     """Chunked form with full Q x Q blocks: 2 Q R^2 (N + P) + 4 R N P."""
     Q, R, N, P = w.chunk, w.rank, w.dstate, w.headdim
@@ -92,8 +104,10 @@ def decode_bytes_per_head(w) -> int:
     return 2 * N * P * 4 + es * (3 * R * N + 2 * R * P + 2 + y)
 
 
-def time_prefill(w, steps, warmup, dev):
-    inp = inputs.make_prefill_inputs(w, seed=0, device=dev)
+def time_prefill(w, steps, warmup, dev, inp=None):
+    """The two-call path: m3_bcnorm_rope then m3_prefill (chunk w.chunk)."""
+    if inp is None:
+        inp = inputs.make_prefill_inputs(w, seed=0, device=dev)
     b, L, H, R, N, P = w.batch, w.seqlen, w.nheads, w.rank, w.dstate, w.headdim
     io = w.torch_io
     Bb = torch.empty((b, L, H, R, N), dtype=io, device=dev)
@@ -139,6 +153,33 @@ def time_prefill(w, steps, warmup, dev):
     ms_bc = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     ms_pf = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     return inp, ms_step, ms_bc, ms_pf
+
+
+def time_layer(w, inp, chunk, steps, warmup, dev):
+    """`steps` fused layer passes (m3_layer_prefill) between two HIP events on the launch stream."""
+    b, L, H, R, N, P = w.batch, w.seqlen, w.nheads, w.rank, w.dstate, w.headdim
+    y = torch.empty((b, L, H, P) if w.mix else (b, L, H, R, P), dtype=w.torch_io, device=dev)
+    h = torch.empty((b, H, N, P), dtype=torch.float32, device=dev)
+    phi = torch.empty((b, H, N // 2), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        m3scan.m3_layer_prefill(inp["x"], inp["B"], inp["C"], inp["dt"], inp["theta"], inp["A"],
+                                inp["lam"], inp["normw_B"], inp["normw_C"], inp["bias_B"],
+                                inp["bias_C"], inp["w_out"] if w.mix else None, y=y, h_out=h,
+                                phi_out=phi, chunk=chunk, bcnorm=w.bcnorm)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
 
 
 def time_decode(w, steps, warmup, dev):
@@ -240,6 +281,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-mimo", action="store_true")
     ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
                     help="only time a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -256,26 +298,51 @@ def main():
         return
     m3scan.load()
 
+    def path_stats(w, inp, chunk_rows):
+        """Both paths on workload w: the fused call (the step) and the two calls."""
+        th = w.batch * w.seqlen * w.nheads
+        tokens = w.batch * w.seqlen
+        state = w.batch * w.nheads * w.dstate * w.headdim * 4
+        angle = w.batch * w.nheads * (w.dstate // 2) * 4
+        ms_layer = time_layer(w, inp, chunk_rows // w.rank, args.steps, args.warmup, dev)
+        wl = w.with_(chunk=chunk_rows // w.rank)
+        ly_bytes = th * layer_bytes_per_token_head(w) + state + angle
+        ly_flops = th * prefill_flops_per_token_head(wl)
+        _, ms_two, ms_bc, ms_pf = time_prefill(w, args.steps, args.warmup, dev, inp)
+        pf_bytes = th * prefill_bytes_per_token_head(w) + state
+        bc_bytes = th * bcnorm_bytes_per_token_head(w) + angle
+        pf_flops = th * prefill_flops_per_token_head(w)
+        return {
+            "m3_layer_prefill": {"ms": ms_layer, "tokens/s": tokens / (ms_layer / 1e3), "chunk": wl.chunk,
+                                 "bytes": ly_bytes, "GB/s": ly_bytes / ms_layer / 1e6,
+                                 "TFLOP/s": ly_flops / ms_layer / 1e9,
+                                 "hbm_frac": ly_bytes / ms_layer / 1e6 / HBM_PEAK_GBS,
+                                 "mfma_frac": ly_flops / ms_layer / 1e9 / BF16_MFMA_PEAK_TFLOPS},
+            "two_calls": {"ms": ms_two, "tokens/s": tokens / (ms_two / 1e3), "chunk": w.chunk},
+            "m3_prefill": {"ms": ms_pf, "bytes": pf_bytes, "GB/s": pf_bytes / ms_pf / 1e6,
+                           "TFLOP/s": pf_flops / ms_pf / 1e9,
+                           "hbm_frac": pf_bytes / ms_pf / 1e6 / HBM_PEAK_GBS,
+                           "mfma_frac": pf_flops / ms_pf / 1e9 / BF16_MFMA_PEAK_TFLOPS},
+            "m3_bcnorm_rope": {"ms": ms_bc, "bytes": bc_bytes, "GB/s": bc_bytes / ms_bc / 1e6,
+                               "hbm_frac": bc_bytes / ms_bc / 1e6 / HBM_PEAK_GBS},
+        }
+
     w = inputs.WORKLOADS["siso_b8_l2048"]
-    inp, ms_step, ms_bc, ms_pf = time_prefill(w, args.steps, args.warmup, dev)
-    th = w.batch * w.seqlen * w.nheads
+    inp = inputs.make_prefill_inputs(w, seed=0, device=dev)
+    kernels = path_stats(w, inp, LAYER_CHUNK_ROWS)
+    ms_step = kernels["m3_layer_prefill"]["ms"]
     tokens = w.batch * w.seqlen
-    pf_bytes = th * prefill_bytes_per_token_head(w) + w.batch * w.nheads * w.dstate * w.headdim * 4
-    bc_bytes = th * bcnorm_bytes_per_token_head(w)
-    pf_flops = th * prefill_flops_per_token_head(w)
-    kernels = {
-        "m3_prefill": {"ms": ms_pf, "bytes": pf_bytes, "GB/s": pf_bytes / ms_pf / 1e6,
-                       "TFLOP/s": pf_flops / ms_pf / 1e9,
-                       "hbm_frac": pf_bytes / ms_pf / 1e6 / HBM_PEAK_GBS,
-                       "mfma_frac": pf_flops / ms_pf / 1e9 / BF16_MFMA_PEAK_TFLOPS},
-        "m3_bcnorm_rope": {"ms": ms_bc, "bytes": bc_bytes, "GB/s": bc_bytes / ms_bc / 1e6,
-                           "hbm_frac": bc_bytes / ms_bc / 1e6 / HBM_PEAK_GBS},
-    }
-    # the dominant single kernel of the step: m3_prefill is one kernel; m3_bcnorm_rope is three
-    # (segment sums, segment scan, main pass) whose largest is below the prefill kernel
-    kd = kernels["m3_prefill"]
-    kname = "prefill_kernel<bf16,128,64,4>"
-    roofline = {"kernel": "m3_prefill (%s)" % kname, "bound": "hbm", "achieved": round(kd["GB/s"], 1),
+    mimo = None
+    if not args.no_mimo:
+        wm = inputs.WORKLOADS["mimo4_b8_l2048"]
+        inpm = inputs.make_prefill_inputs(wm, seed=0, device=dev)
+        mimo = path_stats(wm, inpm, LAYER_CHUNK_ROWS)
+        del inpm
+        torch.cuda.empty_cache()
+    # the step is one kernel: the fused layer kernel
+    kd = kernels["m3_layer_prefill"]
+    kname = "prefill_kernel<bf16,128,64,2,fused>"
+    roofline = {"kernel": "m3_layer_prefill (%s)" % kname, "bound": "hbm", "achieved": round(kd["GB/s"], 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4),
                 "traffic": recorded_traffic(kname, w.name),
                 "algorithmic_bytes_per_launch": kd["bytes"], "avg_launch_ms": round(kd["ms"], 5),
@@ -312,13 +379,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; shapes and distributions of the SISO b8 L2048 layer workload)",
-        "config": {"workload": "siso_b8_l2048: m3_bcnorm_rope + m3_prefill, b=8 L=2048 H=64 P=64 "
-                               "N=128 R=1 chunk=64, bf16 io, fp32 state",
+        "config": {"workload": "siso_b8_l2048: m3_layer_prefill (BCNorm + bias + rotation + chunked "
+                               "scan in one kernel), b=8 L=2048 H=64 P=64 N=128 R=1 chunk=%d, bf16 io, "
+                               "fp32 state" % kernels["m3_layer_prefill"]["chunk"],
                    "batch": w.batch, "seq_len": w.seqlen, "nheads": w.nheads, "headdim": w.headdim,
-                   "dstate": w.dstate, "rank": w.rank, "chunk": w.chunk},
+                   "dstate": w.dstate, "rank": w.rank, "chunk": kernels["m3_layer_prefill"]["chunk"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "mimo4_b8_l2048": mimo,
         "decode": decode,
     }
     print(json.dumps(line))

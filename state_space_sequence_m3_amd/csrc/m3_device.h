@@ -21,9 +21,11 @@ __device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float((uint32
 __device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
-// two floats -> packed bf16 pair (lo in bits 0..15)
+// two floats -> packed bf16 pair (lo in bits 0..15), one v_cvt_pk_bf16_f32
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float floatx2_v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)bf16_bits_rne(lo) | ((uint32_t)bf16_bits_rne(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2_v){lo, hi}, bf16x2_v));
 }
 // 2^x with the hardware instruction (no denormal fix-up; tiny results flush to zero)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

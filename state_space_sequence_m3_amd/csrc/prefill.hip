@@ -298,8 +298,12 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
                                                wrap_angle(base[e + 2] + acc[s][e + 2]), wrap_angle(base[e + 3] + acc[s][e + 3])};
         }
     };
-    // fused: raw B and C rows of this thread -> BCNorm, weight, bias, rotation -> LDS
+    // fused: raw B and C rows of this thread -> BCNorm, weight, bias, rotation -> LDS.  When the
+    // staging step RKC is a multiple of every supported R, all rows of a thread have the same
+    // rank, and the thread's weights and biases stay in registers (loaded after the prologue).
     const float invN = 1.0f / (float)N;
+    constexpr bool WREG = FUSED && RKC % 16 == 0;
+    float cwB[WREG ? VE : 1], cwC[WREG ? VE : 1], cbB[WREG ? VE : 1], cbC[WREG ? VE : 1];
     auto stage_bc = [&](int k, int i) {
         const int t = i >> rl2, r = i & rmask;
         float xb[VE], xc[VE];
@@ -315,19 +319,29 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             }
             qb = group_sum(qb, VPN);
             qc = group_sum(qc, VPN);
-            sb = rsqrtf(fmaf(qb, invN, a.eps));
-            sc = rsqrtf(fmaf(qc, invN, a.eps));
+            // hardware 1/sqrt; the clamp keeps its argument out of the denormal range (an all-zero
+            // row stays zero either way)
+            sb = __builtin_amdgcn_rsqf(fmaxf(fmaf(qb, invN, a.eps), 1e-30f));
+            sc = __builtin_amdgcn_rsqf(fmaxf(fmaf(qc, invN, a.eps), 1e-30f));
         }
         const int n0 = cC0 * VE;
-        const float* wB = sWt + n0;
-        const float* wC = sWt + N + n0;
-        const float* bB = sBias + r * N + n0;
-        const float* bC = sBias + (RB + r) * N + n0;
         const float* ph = sPhi + t * LDPHI + n0 / 2;
+        if (WREG) {
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            xb[e] = fmaf(xb[e] * sb, wB[e], bB[e]);
-            xc[e] = fmaf(xc[e] * sc, wC[e], bC[e]);
+            for (int e = 0; e < VE; ++e) {
+                xb[e] = fmaf(xb[e] * sb, cwB[e % (WREG ? VE : 1)], cbB[e % (WREG ? VE : 1)]);
+                xc[e] = fmaf(xc[e] * sc, cwC[e % (WREG ? VE : 1)], cbC[e % (WREG ? VE : 1)]);
+            }
+        } else {
+            const float* wB = sWt + n0;
+            const float* wC = sWt + N + n0;
+            const float* bB = sBias + r * N + n0;
+            const float* bC = sBias + (RB + r) * N + n0;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                xb[e] = fmaf(xb[e] * sb, wB[e], bB[e]);
+                xc[e] = fmaf(xc[e] * sc, wC[e], bC[e]);
+            }
         }
 #pragma unroll
         for (int q = 0; q < VE / 2; ++q) {
@@ -457,6 +471,16 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             scan(0);
         }
         __syncthreads();
+        if (WREG) {
+            const int n0 = cC0 * VE, r0 = iC0 & rmask;
+#pragma unroll
+            for (int e = 0; e < (WREG ? VE : 1); ++e) {
+                cwB[e] = sWt[n0 + e];
+                cwC[e] = sWt[N + n0 + e];
+                cbB[e] = sBias[r0 * N + n0 + e];
+                cbC[e] = sBias[(RB + r0) * N + n0 + e];
+            }
+        }
     }
     if (nchunk > 0) load_chunk(0);
     for (int64_t c = 0; c < nchunk; ++c) {
