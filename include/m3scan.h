@@ -183,7 +183,7 @@ size_t m3_prefill_workspace_bytes(const m3_dims* dims);
  * receives the rotated Bbar of the last step, as m3_prefill would return it.  dims->chunk = 0
  * picks 32 / R steps per chunk.  h_out may be the h_in buffer and phi_out the phi_in buffer;
  * no other output may overlap an input.  This build has kernels for (N, P) in {(16, 16),
- * (64, 64), (128, 64)}, R in {1, 2, 4, 8, 16} and chunk * R in {16, 32}, or 64 when R <= 4;
+ * (64, 64), (128, 64)}, R in {1, 2, 4, 8, 16} and chunk * R in {16, 32, 64};
  * other shapes return M3_E_UNSUPPORTED.  No workspace is needed (pass NULL, 0).
  */
 m3_status m3_layer_prefill(const m3_dims* dims, const void* x, const void* B, const void* C,

@@ -295,7 +295,7 @@ m3_status m3_layer_prefill(const m3_dims* d, const void* x, const void* B, const
     if (Q * R > 64 || !m3::layer_supported((int)N, (int)P, (int)R, (int)(Q * R), d->io == M3_BF16))
         return fail(M3_E_UNSUPPORTED,
                     "m3_layer_prefill: no kernel for N = %lld, P = %lld, R = %lld, chunk*R = %lld (supported: (N,P) "
-                    "in {(16,16),(64,64),(128,64)}, R in {1,2,4,8,16}, chunk*R in {16,32} or 64 with R <= 4)",
+                    "in {(16,16),(64,64),(128,64)}, R in {1,2,4,8,16}, chunk*R in {16,32,64})",
                     (long long)N, (long long)P, (long long)R, (long long)(Q * R));
     if (Q * H * R * (N > P ? N : P) * (int64_t)es >= ((int64_t)1 << 31))
         return fail(M3_E_DIMS, "m3_layer_prefill: nheads * rank = %lld is too large for one chunk", (long long)(H * R));

@@ -111,6 +111,19 @@ __device__ __forceinline__ void buffer_store8(rsrc_t r, uint32_t off, uint2 v) {
 __device__ __forceinline__ void buffer_store16(rsrc_t r, uint32_t off, uint4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
 }
+// one io element as raw bits (loaded now, converted where it is used, so the load need not be
+// waited for at once); past the descriptor's end it reads as zero
+template <typename T> struct IoBits;
+template <> struct IoBits<float> { typedef uint32_t type; };
+template <> struct IoBits<bf16> { typedef uint16_t type; };
+__device__ __forceinline__ uint32_t buffer_load_bits(rsrc_t r, uint32_t off, float) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint16_t buffer_load_bits(rsrc_t r, uint32_t off, bf16) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ float bits_to_f32(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ float bits_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 // bytes of `n` elements, clamped to what a descriptor can hold
 __device__ __forceinline__ uint32_t clamp_bytes(int64_t n) {
     return n <= 0 ? 0u : (n >= 0xffffffffLL ? 0xffffffffu : (uint32_t)n);

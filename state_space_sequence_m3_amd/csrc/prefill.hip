@@ -45,6 +45,8 @@
 // Operands: bf16 inputs run v_mfma_f32_16x16x16_bf16 (fp32 accumulate); fp32 inputs run
 // v_mfma_f32_16x16x4_f32 four times per 16-wide K block.  In every product the same lane -> K
 // slot assignment is used for both operands, which is all the result depends on.
+#include <type_traits>
+
 #include "m3_device.h"
 #include "m3_launch.h"
 
@@ -145,6 +147,13 @@ __device__ __forceinline__ uint4 pack16(const float (&v)[8], bf16) {
 // FUSED: the chunk's B and C arrive raw and are normalised (BCNorm), biased and rotated by the
 // cumulative angle while they are staged (papernotes.org, key design 4; aipaper.cc section 4.2
 // Proposition 3), so the rotated Bbar and Cbar never go through HBM.
+//
+// Chunk tiles of 16 or 32 rows are software-pipelined: the LDS tiles, per-row scalars, scores and
+// angles are double-buffered by chunk parity, chunk c + 1 is staged (and, fused, normalised and
+// rotated) in slices between the MFMA K blocks of chunk c's part 1, and one barrier per chunk
+// remains.  The raw loads of chunk c + 2 are issued at the start of chunk c into the register set
+// of that parity, so they have a whole chunk to arrive.  Tiles of 48 or 64 rows do not fit twice
+// in LDS and run the same steps with two barriers per chunk.
 template <typename T, int N, int P, int NIB, bool FUSED>
 __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) {
     using MM = Mma<T>;
@@ -152,6 +161,8 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     constexpr int NW = P / 16, NT = NW * 64;
     constexpr int QR = 16 * NIB;                 // rows (t, r) per chunk
     constexpr int NB = N / 16;
+    constexpr bool PIPE = NIB <= 2;
+    constexpr int NBUF = PIPE ? 2 : 1;
     constexpr int LDC = N + MM::PADK, LDB = N + MM::PADT, LDX = P + MM::PADT, LDM = QR + MM::PADK;
     constexpr int VE = 16 / sizeof(T);           // elements per 16-byte vector
     constexpr int VPN = N / VE, VPP = P / VE;    // vectors per row of Bbar/Cbar and of x
@@ -166,20 +177,24 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     constexpr int SPT = NVT * QR > NT ? NVT * QR / NT : 1, TPV = FUSED ? QR / SPT : 16;
     static_assert(!FUSED || (TPV <= 64 && NVT * TPV <= NT && (QR & (QR - 1)) == 0), "angle scan layout");
     constexpr int LDPHI = K + 8;                 // padded angle rows (fp32)
-    constexpr int RB = NIB > 2 ? 4 : 16;         // ranks whose bias fits in LDS
     constexpr int FZ = FUSED ? 1 : 0;            // sizes the fused-only LDS arrays
+    constexpr int TC = QR * LDC, TB = QR * LDB, TX = QR * LDX, TM = QR * LDM, TPH = QR * LDPHI;
 
-    __shared__ __align__(16) T sC[QR * LDC];     // Cbar rows of the chunk  [i][n]
-    __shared__ __align__(16) T sB[QR * LDB];     // Bbar rows               [s][n]
-    __shared__ __align__(16) T sX[QR * LDX];     // x rows                  [s][p]
-    __shared__ __align__(16) T sM[QR * LDM];     // masked scores           [i][s]
-    // per-row (t, r) copies of the chunk's per-step scalars, rewritten every chunk: log2 decay
-    // l_t, gamma_t, mu_t, exp(l_t) and w_t = exp(l_end - l_t) mu_t
-    __shared__ __align__(16) float rL2[64], rGam[64], rMu[64], rEl[64], rW[64];
-    // fused only: the chunk's angles Phi[t][k], BCNorm weights [B, C][n], biases [B, C][r][n]
-    __shared__ __align__(16) float sPhi[FZ * QR * LDPHI + 1];
-    __shared__ __align__(16) float sWt[FZ * 2 * N + 1];
-    __shared__ __align__(16) float sBias[FZ * 2 * RB * N + 1];
+    // buffer b of each (b = chunk parity when pipelined)
+    __shared__ __align__(16) T sC[NBUF * TC];    // Cbar rows of the chunk  [i][n]
+    __shared__ __align__(16) T sB[NBUF * TB];    // Bbar rows               [s][n]
+    __shared__ __align__(16) T sX[NBUF * TX];    // x rows                  [s][p]
+    __shared__ __align__(16) T sM[NBUF * TM];    // masked scores           [i][s]
+    // per-row (t, r) copies of the chunk's per-step scalars: log2 decay l_t, gamma_t, mu_t,
+    // exp(l_t) and w_t = exp(l_end - l_t) mu_t
+    __shared__ __align__(16) float rL2[NBUF * 64], rGam[NBUF * 64], rMu[NBUF * 64], rEl[NBUF * 64],
+        rW[NBUF * 64];
+    // fused only: the chunk's angles Phi[t][k]; in the dynamic LDS the BCNorm weights [B, C][n]
+    // and the biases [B, C][r][n] ((2 N + 2 R N) floats, sized at launch)
+    __shared__ __align__(16) float sPhi[FZ * NBUF * TPH + 1];
+    extern __shared__ __align__(16) float dyn_lds[];
+    float* sWt = dyn_lds;
+    float* sBias = dyn_lds + 2 * N;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -219,10 +234,11 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         return (uint32_t)(((i >> rl2) * HRP32 + (i & rmask) * P + cX0 * VE) * (int)sizeof(T));
     };
 
-    // ---- chunk prefetch into registers --------------------------------------------------
-    uint4 rc[MAXC], rb[MAXC], rx[MAXX];
-    float nd = 0.f, nl = 0.f, ndn = 0.f, nln = 0.f;   // wave 0: dt, lambda at t and t + 1
-    auto load_chunk = [&](int64_t c) {
+    // ---- chunk prefetch into registers (set = chunk parity when pipelined) ----------------
+    uint4 rc[NBUF][MAXC], rb[NBUF][MAXC], rx[NBUF][MAXX];
+    typedef typename IoBits<T>::type Bits;
+    Bits nd[NBUF], nl[NBUF], ndn[NBUF], nln[NBUF];   // dt, lambda at t and t + 1 (io bits; wave 0 uses them)
+    auto load_chunk = [&](int64_t c, int set) {
         const int64_t t0 = c * Q;
         const uint32_t nbc = tail_bytes(t0, HRN, (int64_t)R * N), nbx = tail_bytes(t0, HRP, (int64_t)R * P);
         const rsrc_t dC = make_rsrc(Cg + t0 * HRN, nbc), dB = make_rsrc(Bg + t0 * HRN, nbc);
@@ -230,174 +246,172 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
         for (int k = 0; k < MAXC; ++k) {
             if (FULLC || iC0 + k * RKC < QR) {
-                rc[k] = buffer_load16(dC, offC(k));
-                rb[k] = buffer_load16(dB, offC(k));
+                rc[set][k] = buffer_load16(dC, offC(k));
+                rb[set][k] = buffer_load16(dB, offC(k));
             }
         }
 #pragma unroll
         for (int k = 0; k < MAXX; ++k)
-            if (FULLX || iX0 + k * RKX < QR) rx[k] = buffer_load16(dX, offX(k));
-        if (wave == 0) {
-            const int64_t t = t0 + lane;
-            const bool in = lane < Q && t < L;
-            const bool inn = lane < Q && t + 1 < L;
-            nd = in ? load_f32(dtg + t * H) : 0.f;
-            nl = in ? load_f32(lamg + t * H) : 0.f;
-            ndn = inn ? load_f32(dtg + (t + 1) * H) : 0.f;
-            nln = inn ? load_f32(lamg + (t + 1) * H) : 0.f;
+            if (FULLX || iX0 + k * RKX < QR) rx[set][k] = buffer_load16(dX, offX(k));
+        {
+            // steps t0 + lane and t0 + lane + 1; zero past the sequence end.  Lanes at or past Q
+            // read the next chunk's values, which only reach scan lanes that are never read.  Only
+            // wave 0 uses them; every wave loads them so that the number of loads in flight is the
+            // same on every path (the compiler's wait counts stay exact).
+            const uint32_t nbs = tail_bytes(t0, H, 1);
+            const rsrc_t dD = make_rsrc(dtg + t0 * H, nbs), dL = make_rsrc(lamg + t0 * H, nbs);
+            const uint32_t o0 = (uint32_t)(lane * H * (int)sizeof(T)), o1 = o0 + (uint32_t)(H * (int)sizeof(T));
+            nd[set] = buffer_load_bits(dD, o0, T{});
+            nl[set] = buffer_load_bits(dL, o0, T{});
+            ndn[set] = buffer_load_bits(dD, o1, T{});
+            nln[set] = buffer_load_bits(dL, o1, T{});
         }
     };
     // ---- fused: angle increments of a chunk and their prefix scan ----------------------
     const int tau = tid, tv = tau / TPV, tj = tau % TPV;
     const bool scanner = FUSED && tau < NVT * TPV;
     uint4 rth[SPT];
-    float rdt[SPT];
+    Bits rdt[SPT];
     const T* thg = (const T*)a.theta + row_bh * K;
     const int64_t HK = (int64_t)H * K;
     auto load_theta = [&](int64_t c) {
-        if (!scanner) return;
+        if (!FUSED) return;
         const int64_t t0 = c * Q;
         const rsrc_t dT = make_rsrc(thg + t0 * HK, tail_bytes(t0, HK, K));
+        const rsrc_t dD = make_rsrc(dtg + t0 * H, tail_bytes(t0, H, 1));
 #pragma unroll
         for (int s = 0; s < SPT; ++s) {
+            // steps past the chunk (R > 1 leaves rows of the tile unused) aim past the descriptor
             const int t = tj * SPT + s;
-            const bool in = t < Q;   // steps past the chunk (R > 1 leaves rows of the tile unused)
-            rth[s] = in ? buffer_load16(dT, (uint32_t)((t * (int)HK + tv * VT) * (int)sizeof(T)))
-                        : make_uint4(0, 0, 0, 0);
-            rdt[s] = in && t0 + t < L ? load_f32(dtg + (t0 + t) * H) : 0.f;
+            const bool in = t < Q;
+            rth[s] = buffer_load16(dT, in ? (uint32_t)((t * (int)HK + tv * VT) * (int)sizeof(T)) : 0x80000000u);
+            rdt[s] = buffer_load_bits(dD, in ? (uint32_t)(t * H * (int)sizeof(T)) : 0x80000000u, T{});
         }
     };
     // Phi[t] = Phi[t0 - 1] + sum_{t0 <= i <= t} dt_i theta_i for the chunk starting at c * Q, into
-    // sPhi.  The carried angle is the previous chunk's last row, read by the same wave that
-    // rewrites it (reads come before writes in one wave's LDS order); chunk 0 starts from phi_in.
-    auto scan = [&](int64_t c) {
+    // angle buffer `out`.  The carried angle is the last row of buffer `prev` (the previous
+    // chunk), read by the same wave that wrote it and, when prev == out, before it is rewritten
+    // (one wave's LDS operations complete in order); chunk 0 starts from phi_in.
+    auto scan = [&](int64_t c, int out, int prev) {
         if (!scanner) return;
         float acc[SPT][VT];
 #pragma unroll
         for (int s = 0; s < SPT; ++s) {
             float f[VT];
             unpack16(rth[s], f, T{});
+            const float d = bits_to_f32(rdt[s]);
 #pragma unroll
-            for (int e = 0; e < VT; ++e) acc[s][e] = (s ? acc[s - 1][e] : 0.f) + rdt[s] * f[e];
+            for (int e = 0; e < VT; ++e) acc[s][e] = (s ? acc[s - 1][e] : 0.f) + d * f[e];
         }
         float base[VT];
 #pragma unroll
         for (int e = 0; e < VT; ++e) {
             const int k = tv * VT + e;
             const float carry = c == 0 ? (a.phi_in ? wrap_angle(a.phi_in[bh * K + k]) : 0.f)
-                                       : sPhi[(Q - 1) * LDPHI + k];
+                                       : sPhi[prev * TPH + (Q - 1) * LDPHI + k];
             const float tot = acc[SPT - 1][e];
             base[e] = carry + seg_scan_add<TPV>(tot, lane) - tot;
         }
 #pragma unroll
         for (int s = 0; s < SPT; ++s) {
-            float* dst = sPhi + (tj * SPT + s) * LDPHI + tv * VT;
+            float* dst = sPhi + out * TPH + (tj * SPT + s) * LDPHI + tv * VT;
 #pragma unroll
             for (int e = 0; e < VT; e += 4)
                 *(floatx4*)(dst + e) = floatx4{wrap_angle(base[e] + acc[s][e]), wrap_angle(base[e + 1] + acc[s][e + 1]),
                                                wrap_angle(base[e + 2] + acc[s][e + 2]), wrap_angle(base[e + 3] + acc[s][e + 3])};
         }
     };
-    // fused: raw B and C rows of this thread -> BCNorm, weight, bias, rotation -> LDS.  When the
-    // staging step RKC is a multiple of every supported R, all rows of a thread have the same
-    // rank, and the thread's weights and biases stay in registers (loaded after the prologue).
+    // fused: raw B and C rows -> BCNorm, weight, bias, rotation -> tile buffer `buf`.  B and C go
+    // one after the other to keep few values live; they share the row's angles.
     const float invN = 1.0f / (float)N;
-    constexpr bool WREG = FUSED && RKC % 16 == 0;
-    float cwB[WREG ? VE : 1], cwC[WREG ? VE : 1], cbB[WREG ? VE : 1], cbC[WREG ? VE : 1];
-    auto stage_bc = [&](int k, int i) {
+    const bool has_w = a.bcnorm && (a.normw_B || a.normw_C);
+    auto stage_bc = [&](int set, int k, int i, int buf) {
         const int t = i >> rl2, r = i & rmask;
-        float xb[VE], xc[VE];
-        unpack16(rb[k], xb, T{});
-        unpack16(rc[k], xc, T{});
-        float sb = 1.f, sc = 1.f;
-        if (a.bcnorm) {   // RMS over the row's N values, spread over VPN consecutive lanes
-            float qb = 0.f, qc = 0.f;
-#pragma unroll
-            for (int e = 0; e < VE; ++e) {
-                qb = fmaf(xb[e], xb[e], qb);
-                qc = fmaf(xc[e], xc[e], qc);
-            }
-            qb = group_sum(qb, VPN);
-            qc = group_sum(qc, VPN);
-            // hardware 1/sqrt; the clamp keeps its argument out of the denormal range (an all-zero
-            // row stays zero either way)
-            sb = __builtin_amdgcn_rsqf(fmaxf(fmaf(qb, invN, a.eps), 1e-30f));
-            sc = __builtin_amdgcn_rsqf(fmaxf(fmaf(qc, invN, a.eps), 1e-30f));
-        }
         const int n0 = cC0 * VE;
-        const float* ph = sPhi + t * LDPHI + n0 / 2;
-        if (WREG) {
+        float cs[VE / 2], sn[VE / 2];
+        {
+            const float* ph = sPhi + buf * TPH + t * LDPHI + n0 / 2;
 #pragma unroll
-            for (int e = 0; e < VE; ++e) {
-                xb[e] = fmaf(xb[e] * sb, cwB[e % (WREG ? VE : 1)], cbB[e % (WREG ? VE : 1)]);
-                xc[e] = fmaf(xc[e] * sc, cwC[e % (WREG ? VE : 1)], cbC[e % (WREG ? VE : 1)]);
-            }
-        } else {
-            const float* wB = sWt + n0;
-            const float* wC = sWt + N + n0;
-            const float* bB = sBias + r * N + n0;
-            const float* bC = sBias + (RB + r) * N + n0;
-#pragma unroll
-            for (int e = 0; e < VE; ++e) {
-                xb[e] = fmaf(xb[e] * sb, wB[e], bB[e]);
-                xc[e] = fmaf(xc[e] * sc, wC[e], bC[e]);
-            }
+            for (int q = 0; q < VE / 2; ++q) __sincosf(ph[q], &sn[q], &cs[q]);   // |angle| <= pi
         }
 #pragma unroll
-        for (int q = 0; q < VE / 2; ++q) {
-            float sn, cs;
-            __sincosf(ph[q], &sn, &cs);   // |angle| <= pi
-            const float b0 = xb[2 * q], b1 = xb[2 * q + 1], c0 = xc[2 * q], c1 = xc[2 * q + 1];
-            xb[2 * q] = fmaf(cs, b0, sn * b1);
-            xb[2 * q + 1] = fmaf(cs, b1, -sn * b0);
-            xc[2 * q] = fmaf(cs, c0, sn * c1);
-            xc[2 * q + 1] = fmaf(cs, c1, -sn * c0);
-        }
-        *(uint4*)(sC + i * LDC + n0) = pack16(xc, T{});
-        *(uint4*)(sB + i * LDB + n0) = pack16(xb, T{});
-    };
-
-    auto store_tiles = [&]() {
+        for (int which = 0; which < 2; ++which) {
+            float x[VE];
+            unpack16(which == 0 ? rb[set][k] : rc[set][k], x, T{});
+            float sc = 1.f;
+            if (a.bcnorm) {   // RMS over the row's N values, spread over VPN consecutive lanes
+                float qs = 0.f;
 #pragma unroll
-        for (int k = 0; k < MAXC; ++k) {
-            const int i = iC0 + k * RKC;
-            if (FULLC || i < QR) {
-                if (FUSED) {
-                    stage_bc(k, i);
-                } else {
-                    *(uint4*)(sC + i * LDC + cC0 * VE) = rc[k];
-                    *(uint4*)(sB + i * LDB + cC0 * VE) = rb[k];
-                }
+                for (int e = 0; e < VE; ++e) qs = fmaf(x[e], x[e], qs);
+                qs = group_sum(qs, VPN);
+                // hardware 1/sqrt; the clamp keeps its argument out of the denormal range (an
+                // all-zero row stays zero either way)
+                sc = __builtin_amdgcn_rsqf(fmaxf(fmaf(qs, invN, a.eps), 1e-30f));
             }
-        }
+            const float* bw = sBias + (which * R + r) * N + n0;
+            if (has_w) {
+                const float* ww = sWt + which * N + n0;
 #pragma unroll
-        for (int k = 0; k < MAXX; ++k) {
-            const int i = iX0 + k * RKX;
-            if (FULLX || i < QR) *(uint4*)(sX + i * LDX + cX0 * VE) = rx[k];
+                for (int e = 0; e < VE; ++e) x[e] = fmaf(x[e] * sc, ww[e], bw[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < VE; ++e) x[e] = fmaf(x[e], sc, bw[e]);
+            }
+#pragma unroll
+            for (int q = 0; q < VE / 2; ++q) {
+                const float x0 = x[2 * q], x1 = x[2 * q + 1];
+                x[2 * q] = fmaf(cs[q], x0, sn[q] * x1);
+                x[2 * q + 1] = fmaf(cs[q], x1, -sn[q] * x0);
+            }
+            if (which == 0) *(uint4*)(sB + buf * TB + i * LDB + n0) = pack16(x, T{});
+            else *(uint4*)(sC + buf * TC + i * LDC + n0) = pack16(x, T{});
         }
     };
     // wave 0: the chunk's per-step scalars (lane = step) -> per-row copies in LDS.  Lanes past
     // the chunk only add to later lanes of the scan, which are never read.
-    auto stage_scalars = [&](float d, float lm, float dn, float lmn) {
+    auto stage_scalars = [&](float d, float lm, float dn, float lmn, int buf) {
         const float l2 = wave_scan_add(d * Alog2);   // l_t in log2 units, inclusive over the chunk
         const float gam = lm * d;
         const float mu = gam + (1.0f - lmn) * dn;
         const float l2end = lane_value(l2, Q - 1);
         const float el = fast_exp2(l2);
         const float w = fast_exp2(fminf(l2end - l2, 0.f)) * mu;
+        float* o = rL2 + buf * 64;
         if (R == 1) {
-            rL2[lane] = l2;
-            rGam[lane] = gam;
-            rMu[lane] = mu;
-            rEl[lane] = el;
-            rW[lane] = w;
+            o[lane] = l2;
+            rGam[buf * 64 + lane] = gam;
+            rMu[buf * 64 + lane] = mu;
+            rEl[buf * 64 + lane] = el;
+            rW[buf * 64 + lane] = w;
         } else {   // row s holds step s >> rl2 (rows past Q * R are never read)
             const int ts = lane >> rl2;
-            rL2[lane] = shfl(l2, ts);
-            rGam[lane] = shfl(gam, ts);
-            rMu[lane] = shfl(mu, ts);
-            rEl[lane] = shfl(el, ts);
-            rW[lane] = shfl(w, ts);
+            o[lane] = shfl(l2, ts);
+            rGam[buf * 64 + lane] = shfl(gam, ts);
+            rMu[buf * 64 + lane] = shfl(mu, ts);
+            rEl[buf * 64 + lane] = shfl(el, ts);
+            rW[buf * 64 + lane] = shfl(w, ts);
+        }
+    };
+    // staging item j of register set `set` into buffer `buf`: the B/C row vectors, then the x
+    // vectors, then (wave 0) the scalars
+    constexpr int NITEM = MAXC + MAXX + 1;
+    auto stage_item = [&](int j, int set, int buf) {
+        if (j < MAXC) {
+            const int i = iC0 + j * RKC;
+            if (FULLC || i < QR) {
+                if (FUSED) {
+                    stage_bc(set, j, i, buf);
+                } else {
+                    *(uint4*)(sC + buf * TC + i * LDC + cC0 * VE) = rc[set][j];
+                    *(uint4*)(sB + buf * TB + i * LDB + cC0 * VE) = rb[set][j];
+                }
+            }
+        } else if (j < MAXC + MAXX) {
+            const int k = j - MAXC, i = iX0 + k * RKX;
+            if (FULLX || i < QR) *(uint4*)(sX + buf * TX + i * LDX + cX0 * VE) = rx[set][k];
+        } else if (wave == 0) {
+            stage_scalars(bits_to_f32(nd[set]), bits_to_f32(nl[set]), bits_to_f32(ndn[set]),
+                          bits_to_f32(nln[set]), buf);
         }
     };
 
@@ -432,7 +446,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         for (int m = 0; m < 4; ++m) wo[m] = a.w_out[(h * R + r) * P + 16 * wave + 4 * g + m];
     }
 
-    // loop-invariant LDS fragment addresses for this lane
+    // loop-invariant LDS fragment addresses for this lane (buffer 0; buffer b is b * T? further)
     const T* pC_k = sC + l16 * LDC + 4 * g;                 // + 16 ib LDC + 16 kb
     const T* pB_k = sB + l16 * LDB + 4 * g;                 // + 16 sb LDB + 16 kb
     const T* pM_k = sM + l16 * LDM + 4 * g;                 // + 16 ib LDM + 16 sb
@@ -455,57 +469,30 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         pSC[j] = pC_k + 16 * sIb[j] * LDC;
     }
 
-    if (FUSED) {
-        // BCNorm weights (1 without BCNorm or without weights) and biases (0 when absent)
-        for (int e = tid; e < 2 * N; e += NT) {
-            const float* w = e < N ? a.normw_B : a.normw_C;
-            sWt[e] = a.bcnorm && w ? w[h * N + (e % N)] : 1.f;
-        }
-        for (int e = tid; e < 2 * RB * N; e += NT) {
-            const int which = e / (RB * N), r = (e / N) % RB;
-            const float* bias = which == 0 ? a.bias_B : a.bias_C;
-            sBias[e] = bias && r < R ? bias[(h * R + r) * N + (e % N)] : 0.f;
-        }
-        if (nchunk > 0) {
-            load_theta(0);
-            scan(0);
-        }
-        __syncthreads();
-        if (WREG) {
-            const int n0 = cC0 * VE, r0 = iC0 & rmask;
-#pragma unroll
-            for (int e = 0; e < (WREG ? VE : 1); ++e) {
-                cwB[e] = sWt[n0 + e];
-                cwC[e] = sWt[N + n0 + e];
-                cbB[e] = sBias[r0 * N + n0 + e];
-                cbC[e] = sBias[(RB + r0) * N + n0 + e];
-            }
-        }
-    }
-    if (nchunk > 0) load_chunk(0);
-    for (int64_t c = 0; c < nchunk; ++c) {
-        const float cd = nd, cl = nl, cdn = ndn, cln = nln;
-        store_tiles();
-        if (FUSED && c + 1 < nchunk) load_theta(c + 1);   // scanned at the end of this chunk's part 1
-        if (c + 1 < nchunk) load_chunk(c + 1);   // the next chunk's loads fly during this one
-        if (wave == 0) stage_scalars(cd, cl, cdn, cln);
-        __syncthreads();
+    // ---- one chunk on buffer `buf`: part 1 (calling hook(k) in K block k), after_part1(),
+    // masks, a barrier, part 2 ------------------------------------------------------------
+    auto chunk_compute = [&](int buf, int64_t c, auto hook, auto after_part1) {
         const int64_t t0 = c * Q;
-
-        // ---- part 1 -------------------------------------------------------------------------
+        const T* tC = pC_k + buf * TC;
+        const T* tBt = pB_t + buf * TB;
+        const float* sL2 = rL2 + buf * 64;
+        const float* sGm = rGam + buf * 64;
+        const float* sMu = rMu + buf * 64;
+        const float* sEl = rEl + buf * 64;
+        const float* sW = rW + buf * 64;
         // X^T fragments of this wave's 16 columns, and w o X for the state update
         F xf[NIB], xw[NIB];
 #pragma unroll
-        for (int sb = 0; sb < NIB; ++sb) xf[sb] = MM::ldt(pX_t + 16 * sb * LDX, LDX, l16);
+        for (int sb = 0; sb < NIB; ++sb) xf[sb] = MM::ldt(pX_t + buf * TX + 16 * sb * LDX, LDX, l16);
 #pragma unroll
         for (int sb = 0; sb < NIB; ++sb) {
             floatx4 xs = MM::unpack(xf[sb]);
-            const floatx4 ws = *(const floatx4*)(rW + 16 * sb + 4 * g);
+            const floatx4 ws = *(const floatx4*)(sW + 16 * sb + 4 * g);
 #pragma unroll
             for (int m = 0; m < 4; ++m) xs[m] *= ws[m];
             xw[sb] = MM::pack(xs);
         }
-        const float dec = rEl[QR - 1];
+        const float dec = sEl[QR - 1];
         floatx4 y[NIB], acc[NSLOT];
 #pragma unroll
         for (int ib = 0; ib < NIB; ++ib) y[ib] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -518,14 +505,14 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         F fc[2][NIB], fsb[2][NSLOT], fsc[2][NSLOT], fbt[2][NIB];
         auto fetch = [&](int k, int s) {
 #pragma unroll
-            for (int ib = 0; ib < NIB; ++ib) fc[s][ib] = MM::ldk(pC_k + 16 * ib * LDC + 16 * k);
+            for (int ib = 0; ib < NIB; ++ib) fc[s][ib] = MM::ldk(tC + 16 * ib * LDC + 16 * k);
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) {
-                fsb[s][j] = MM::ldk(pSB[j] + 16 * k);
-                fsc[s][j] = MM::ldk(pSC[j] + 16 * k);
+                fsb[s][j] = MM::ldk(pSB[j] + buf * TB + 16 * k);
+                fsc[s][j] = MM::ldk(pSC[j] + buf * TC + 16 * k);
             }
 #pragma unroll
-            for (int sb = 0; sb < NIB; ++sb) fbt[s][sb] = MM::ldt(pB_t + 16 * sb * LDB + 16 * k, LDB, l16);
+            for (int sb = 0; sb < NIB; ++sb) fbt[s][sb] = MM::ldt(tBt + 16 * sb * LDB + 16 * k, LDB, l16);
         };
         fetch(0, 0);
 #pragma unroll
@@ -533,6 +520,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             const int s = k & 1;
             __builtin_amdgcn_sched_barrier(0);
             if (k + 1 < NB) fetch(k + 1, s ^ 1);
+            hook(k);
             // state part of Y^T, K block k (state rows 16k.., before the update)
             const F sa = MM::pack(st[k]);
 #pragma unroll
@@ -547,17 +535,16 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             for (int sb = 0; sb < NIB; ++sb) st[k] = MM::mma(fbt[s][sb], xw[sb], st[k]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // fused: angles of the next chunk (its staging reads them after the coming barrier)
-        if (FUSED && c + 1 < nchunk) scan(c + 1);
+        after_part1();
         // mask the score tiles: lane holds S^T[s = 16 sb + 4 g + m][i = 16 ib + l16]
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
             if (!sOn[j]) continue;
             const int i = 16 * sIb[j] + l16, s0 = 16 * sSb[j] + 4 * g;
             const int ti = i >> rl2;
-            const float l2i = rL2[i], gi = rGam[i];
-            const floatx4 l2s = *(const floatx4*)(rL2 + s0);
-            const floatx4 mus = *(const floatx4*)(rMu + s0);
+            const float l2i = sL2[i], gi = sGm[i];
+            const floatx4 l2s = *(const floatx4*)(sL2 + s0);
+            const floatx4 mus = *(const floatx4*)(sMu + s0);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 // below the diagonal exp(l_t - l_s) mu_s, on it gamma_t, above it 0
@@ -567,22 +554,22 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
                 const float diag = ts == ti ? gi : 0.f;
                 acc[j][m] *= fmaf(e, below, diag);
             }
-            MM::st(sM + i * LDM + s0, MM::pack(acc[j]));
+            MM::st(sM + buf * TM + i * LDM + s0, MM::pack(acc[j]));
         }
 #pragma unroll
         for (int ib = 0; ib < NIB; ++ib) {
-            const float el = rEl[16 * ib + l16];
+            const float el = sEl[16 * ib + l16];
 #pragma unroll
             for (int m = 0; m < 4; ++m) y[ib][m] *= el;
         }
         __syncthreads();
 
-        // ---- part 2: Y^T += X^T M^T, mixing, stores ------------------------------------------
+        // ---- part 2: Y^T += X^T M^T, mixing, stores --------------------------------------
 #pragma unroll
         for (int sb = 0; sb < NIB; ++sb)
 #pragma unroll
             for (int ib = sb; ib < NIB; ++ib)
-                y[ib] = MM::mma(xf[sb], MM::ldk(pM_k + 16 * ib * LDM + 16 * sb), y[ib]);
+                y[ib] = MM::mma(xf[sb], MM::ldk(pM_k + buf * TM + 16 * ib * LDM + 16 * sb), y[ib]);
         const rsrc_t dY = make_rsrc(yg + t0 * ystep, tail_bytes(t0, ystep, yrow));
 #pragma unroll
         for (int ib = 0; ib < NIB; ++ib) {
@@ -602,6 +589,85 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             }
             store4(dY, off, yv, T{});
         }
+    };
+
+    // ---- prologue ---------------------------------------------------------------------
+    // Chunk loads are issued on every path, also for chunks past the end (their descriptors hold
+    // zero bytes, so nothing is read), and every thread loads its angle increments; the compiler's
+    // wait counts then match the loads actually in flight.
+    if (FUSED) {
+        // BCNorm weights (1 without BCNorm or without weights) and biases (0 when absent)
+        for (int e = tid; e < 2 * N; e += NT) {
+            const float* w = e < N ? a.normw_B : a.normw_C;
+            sWt[e] = a.bcnorm && w ? w[h * N + (e % N)] : 1.f;
+        }
+        for (int e = tid; e < 2 * R * N; e += NT) {
+            const int which = e / (R * N), rn = e % (R * N);
+            const float* bias = which == 0 ? a.bias_B : a.bias_C;
+            sBias[e] = bias ? bias[h * R * N + rn] : 0.f;
+        }
+        if (nchunk > 0) {
+            load_theta(0);
+            scan(0, 0, 0);
+        }
+        if (PIPE && nchunk > 1) {
+            load_theta(1);
+            scan(1, 1, 0);
+        }
+        if (PIPE) load_theta(2);
+        __syncthreads();
+    }
+    if (nchunk > 0) load_chunk(0, 0);
+    auto no_hook = [&](int) {};
+
+    if constexpr (PIPE) {
+        if (nchunk > 0) {
+#pragma unroll
+            for (int j = 0; j < NITEM; ++j) stage_item(j, 0, 0);
+        }
+        load_chunk(1, 1);
+        __builtin_amdgcn_s_waitcnt(0);   // nothing from the prologue stays in flight into the loop
+        __syncthreads();
+        // chunk c on buffer p = c & 1 (p compile-time in each half of the unrolled pair)
+        auto iter = [&](auto PB, int64_t c) {
+            constexpr int p = decltype(PB)::value, q = p ^ 1;
+            const bool has1 = c + 1 < nchunk, has2 = c + 2 < nchunk;
+            load_chunk(c + 2, p);
+            // stage chunk c + 1 (register set q) into buffer q, item j after K block
+            // (2 j + 1) NB / (2 NITEM)
+            auto hook = [&](int k) {
+                if (!has1) return;
+#pragma unroll
+                for (int j = 0; j < NITEM; ++j)
+                    if ((2 * j + 1) * NB / (2 * NITEM) == k) stage_item(j, q, q);
+            };
+            auto after = [&]() {
+                if (FUSED) {
+                    if (has2) scan(c + 2, p, q);
+                    load_theta(c + 3);
+                }
+            };
+            chunk_compute(p, c, hook, after);
+        };
+        for (int64_t c = 0; c < nchunk; c += 2) {
+            iter(std::integral_constant<int, 0>{}, c);
+            if (c + 1 < nchunk) iter(std::integral_constant<int, 1>{}, c + 1);
+        }
+    } else {
+        for (int64_t c = 0; c < nchunk; ++c) {
+#pragma unroll
+            for (int j = 0; j < MAXC + MAXX; ++j) stage_item(j, 0, 0);
+            const float cd = bits_to_f32(nd[0]), cl = bits_to_f32(nl[0]);
+            const float cdn = bits_to_f32(ndn[0]), cln = bits_to_f32(nln[0]);
+            load_theta(c + 1);    // scanned at the end of this chunk's part 1
+            load_chunk(c + 1, 0);   // the next chunk's loads fly during this one
+            if (wave == 0) stage_scalars(cd, cl, cdn, cln, 0);
+            __syncthreads();
+            auto after = [&]() {
+                if (FUSED && c + 1 < nchunk) scan(c + 1, 0, 0);
+            };
+            chunk_compute(0, c, no_hook, after);
+        }
     }
 
     // ---- outputs: final state and the last step's (Bbar, x) ------------------------------
@@ -610,12 +676,13 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
         for (int m = 0; m < 4; ++m) a.h_out[(bh * N + 16 * nb + 4 * g + m) * P + pcol] = st[nb][m];
     if (L > 0) {
-        // the last chunk's tiles are still in LDS (nothing is staged after it)
+        // the last chunk's tiles and angles are still in LDS (nothing is staged after it)
+        const int lb = PIPE ? (int)((nchunk - 1) & 1) : 0;
         const int tlast = (int)(L - 1 - (nchunk - 1) * Q);
         if (a.Bbar_last) {
             for (int e = tid; e < R * N; e += NT) {
                 T v;
-                if (FUSED) v = sB[(tlast * R + e / N) * LDB + e % N];   // rotated here, never in HBM
+                if (FUSED) v = sB[lb * TB + (tlast * R + e / N) * LDB + e % N];   // rotated here only
                 else v = Bg[(L - 1) * HRN + e];
                 ((T*)a.Bbar_last)[bh * R * N + e] = v;
             }
@@ -623,21 +690,23 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         if (a.x_last)
             for (int e = tid; e < R * P; e += NT) ((T*)a.x_last)[bh * R * P + e] = Xg[(L - 1) * HRP + e];
         if (FUSED && a.phi_out)
-            for (int k = tid; k < K; k += NT) a.phi_out[bh * K + k] = sPhi[(Q - 1) * LDPHI + k];
+            for (int k = tid; k < K; k += NT) a.phi_out[bh * K + k] = sPhi[lb * TPH + (Q - 1) * LDPHI + k];
     }
 }
 
 template <typename T, int N, int P, bool FUSED>
 hipError_t launch_np(const PrefillArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)(a.b * a.H)), block(P / 16 * 64);
+    // fused: BCNorm weights and biases in dynamic LDS
+    const size_t dyn = FUSED ? (size_t)(2 * N + 2 * a.R * N) * sizeof(float) : 0;
     switch (a.Q * a.R) {
-        case 16: hipLaunchKernelGGL((prefill_kernel<T, N, P, 1, FUSED>), grid, block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((prefill_kernel<T, N, P, 2, FUSED>), grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((prefill_kernel<T, N, P, 1, FUSED>), grid, block, dyn, s, a); break;
+        case 32: hipLaunchKernelGGL((prefill_kernel<T, N, P, 2, FUSED>), grid, block, dyn, s, a); break;
         case 48:
             if (FUSED) return hipErrorInvalidValue;
             hipLaunchKernelGGL((prefill_kernel<T, N, P, 3, false>), grid, block, 0, s, a);
             break;
-        case 64: hipLaunchKernelGGL((prefill_kernel<T, N, P, 4, FUSED>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((prefill_kernel<T, N, P, 4, FUSED>), grid, block, dyn, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -665,9 +734,8 @@ hipError_t launch_prefill(const PrefillArgs& a, bool bf16_io, hipStream_t s) {
 }
 
 bool layer_supported(int N, int P, int R, int QR, bool bf16_io) {
-    // chunk rows 16, 32 or 64 (the angle scan wants a power-of-two step count); the 64-row tile
-    // keeps the biases of at most 4 ranks in LDS
-    return prefill_supported(N, P, R, QR, bf16_io) && QR != 48 && (QR < 48 || R <= 4);
+    // chunk rows 16, 32 or 64 (the angle scan wants a power-of-two step count)
+    return prefill_supported(N, P, R, QR, bf16_io) && QR != 48;
 }
 
 hipError_t launch_layer(const PrefillArgs& a, bool bf16_io, hipStream_t s) {

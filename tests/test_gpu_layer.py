@@ -46,6 +46,7 @@ LAYER_CASES = [
     ("bf16", 1, 257, 2, 64, 128, 1, 32, True, True, True, False, True, math.pi),
     ("bf16", 2, 129, 2, 64, 128, 1, 32, False, False, False, False, False, 1.0),
     ("f32", 1, 45, 2, 64, 128, 4, 8, True, True, True, True, True, 1.0),
+    ("bf16", 1, 70, 2, 64, 128, 8, 8, True, True, True, True, True, 1.0),    # 64 rows, R = 8
 ]
 
 
@@ -140,8 +141,8 @@ def test_layer_unsupported_chunk_is_rejected():
     with pytest.raises(m3scan.M3Error) as e:
         _run(d, w, 48, False)
     assert e.value.status == m3scan.M3_E_UNSUPPORTED
-    w = _wl("bf16", 1, 48, 1, 64, 128, 8, 8)
+    w = _wl("bf16", 1, 48, 1, 32, 128, 1, 32)      # no kernel for P = 32
     d = to_dev(inputs.make_prefill_inputs(w, seed=36), DEV)
     with pytest.raises(m3scan.M3Error) as e:
-        _run(d, w, 8, False)
+        _run(d, w, 32, False)
     assert e.value.status == m3scan.M3_E_UNSUPPORTED
