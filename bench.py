@@ -6,7 +6,8 @@ batch of the SISO workload (b=8, L=2048, H=64, P=64, N=128, R=1, bf16 io, fp32 s
 m3_layer_prefill, which does both in one kernel (chunk 32).  `value` is prefill tokens/s (b * L
 tokens per step).  The same line times the two-call path (m3_bcnorm_rope then m3_prefill, chunk
 64) for comparison, the MIMO R=4 workload through both paths, decode throughput on the B=128
-decode workloads (R=1 and R=4: m3_bcnorm_rope with L=1 then m3_decode_step per token), the
+decode workloads (R=1 and R=4: m3_layer_decode_step per token, and the two-call path
+m3_bcnorm_rope with L=1 then m3_decode_step), the
 roofline of the dominant kernel measured live with HIP events on the launch stream, and the fp64
 oracle's throughput on a bounded sample of the same prefill workload on the host cores.
 
@@ -104,6 +105,15 @@ def decode_bytes_per_head(w) -> int:
     return 2 * N * P * 4 + es * (3 * R * N + 2 * R * P + 2 + y)
 
 
+def layer_decode_bytes_per_head(w) -> int:
+    """m3_layer_decode_step per (b, h): fp32 state read + written, angle read + written, Bbar_prev,
+    x_prev, x, raw B and C, dt, lam, theta read, the rotated B and y written."""
+    es = 2 if w.io == "bf16" else 4
+    R, N, P = w.rank, w.dstate, w.headdim
+    y = P if w.mix else R * P
+    return 2 * N * P * 4 + 2 * (N // 2) * 4 + es * (4 * R * N + 2 * R * P + 2 + N // 2 + y)
+
+
 def time_prefill(w, steps, warmup, dev, inp=None):
     """The two-call path: m3_bcnorm_rope then m3_prefill (chunk w.chunk)."""
     if inp is None:
@@ -177,6 +187,41 @@ def time_layer(w, inp, chunk, steps, warmup, dev):
     t0.record(stream)
     for _ in range(steps):
         step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def time_layer_decode(w, steps, warmup, dev):
+    """`steps` consecutive decode tokens through m3_layer_decode_step (rotation + decode in one
+    launch), HIP-event timed on the launch stream."""
+    total = steps + warmup
+    dinp = inputs.make_decode_inputs(w, seed=0, steps=total, device=dev)
+    toks, st = dinp["tokens"], dinp["state"]
+    b, H, R, N, P = w.batch, w.nheads, w.rank, w.dstate, w.headdim
+    h, phi = st["h"], st["phi"]
+    bufs = [st["Bbar_prev"], torch.empty_like(st["Bbar_prev"])]
+    y = torch.empty((b, H, P) if w.mix else (b, H, R, P), dtype=w.torch_io, device=dev)
+    stream = torch.cuda.current_stream()
+    xprev = st["x_prev"]
+
+    def tok(s):
+        nonlocal xprev
+        Bprev, Bcur = bufs[s % 2], bufs[(s + 1) % 2]
+        m3scan.m3_layer_decode_step(h, phi, Bprev, xprev, toks["x"][s], toks["B"][s], toks["C"][s],
+                                    toks["dt"][s], toks["theta"][s], dinp["A"], toks["lam"][s], None,
+                                    None, dinp["bias_B"], dinp["bias_C"],
+                                    dinp["w_out"] if w.mix else None, y=y, Bbar_out=Bcur)
+        xprev = toks["x"][s]
+
+    for s in range(warmup):
+        tok(s)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for k in range(steps):
+        tok(warmup + k)
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
@@ -353,13 +398,19 @@ def main():
         decode = {}
         for name in ("decode_b128_r1", "decode_b128_r4"):
             wd = inputs.WORKLOADS[name]
+            ms_fused = time_layer_decode(wd, args.decode_steps, args.warmup, dev)
             ms_tok, ms_dbc, ms_dec = time_decode(wd, args.decode_steps, args.warmup, dev)
             dbytes = wd.batch * wd.nheads * decode_bytes_per_head(wd)
-            decode[name] = {"steps_per_s": 1e3 / ms_tok, "ms_per_step": ms_tok,
-                            "decode_step_ms": ms_dec, "bcnorm_rope_ms": ms_dbc,
-                            "decode_step_GB/s": dbytes / ms_dec / 1e6,
-                            "decode_step_hbm_frac": dbytes / ms_dec / 1e6 / HBM_PEAK_GBS,
-                            "decode_step_bytes": dbytes}
+            fbytes = wd.batch * wd.nheads * layer_decode_bytes_per_head(wd)
+            decode[name] = {"steps_per_s": 1e3 / ms_fused, "ms_per_step": ms_fused,
+                            "layer_decode_step_GB/s": fbytes / ms_fused / 1e6,
+                            "layer_decode_step_hbm_frac": fbytes / ms_fused / 1e6 / HBM_PEAK_GBS,
+                            "layer_decode_step_bytes": fbytes,
+                            "two_calls": {"steps_per_s": 1e3 / ms_tok, "ms_per_step": ms_tok,
+                                          "decode_step_ms": ms_dec, "bcnorm_rope_ms": ms_dbc,
+                                          "decode_step_GB/s": dbytes / ms_dec / 1e6,
+                                          "decode_step_hbm_frac": dbytes / ms_dec / 1e6 / HBM_PEAK_GBS,
+                                          "decode_step_bytes": dbytes}}
             torch.cuda.empty_cache()
 
     cpu = None

@@ -18,6 +18,7 @@
  *   m3_prefill       chunked scan over a whole sequence (structured-mask matrix form)
  *   m3_layer_prefill the two above in one pass (rotation applied while staging each chunk)
  *   m3_decode_step   one new token for a batch of resident states
+ *   m3_layer_decode_step  the rotation and one decode step in one launch
  *
  * Frame of the state.  The state the library keeps, returns and accepts is the rotated frame
  * g_t = R(Phi_t)^T h_t.  Together with the angle Phi_t (returned by m3_bcnorm_rope) it fully
@@ -230,6 +231,37 @@ const char* m3_last_error(void);
 
 /* Library version string. */
 const char* m3_version(void);
+
+/*
+ * m3_layer_decode_step -- m3_bcnorm_rope (L = 1) followed by m3_decode_step, in one launch.
+ *
+ * Defined by: the two calls it stands for (see them above); papernotes.org, key design 4 (the
+ * normalisation, bias and rotation only change what the recurrence consumes).  The token's raw B
+ * and C are normalised, biased and rotated by Phi + dt * theta inside the decode kernel; the
+ * results are those of
+ *
+ *   m3_bcnorm_rope(dims, B, C, dt, theta, normw_B, normw_C, bias_B, bias_C, phi,
+ *                  Bbar_out, Cbar, phi)
+ *   m3_decode_step(dims, h, Bbar_prev, x_prev, x, Bbar_out, Cbar, dt, A, lam, w_out, y)
+ *
+ * up to rounding order.  Arguments (dims->seqlen must be 1):
+ *   h           [b, H, N, P] f32     state, updated in place                            required
+ *   phi         [b, H, N/2] f32      carried angle, advanced in place                   required
+ *   Bbar_prev, x_prev                as in m3_decode_step (the previous token's rotated B and x)
+ *   x           [b, H, R, P] io      the token's input                                  required
+ *   B, C        [b, H, R, N] io      the token's raw projections                        required
+ *   dt, lam     [b, H] io; theta [b, H, N/2] io; A, normw_*, bias_*, w_out as before
+ *   y           [b, H, P] io (with w_out) or [b, H, R, P]                               required
+ *   Bbar_out    [b, H, R, N] io      the token's rotated B: the next step's Bbar_prev   required
+ * The caller swaps the Bbar_prev / Bbar_out buffers (and passes x as the next x_prev) between
+ * steps.  No output may overlap an input or another output.  Shapes as m3_decode_step.
+ */
+m3_status m3_layer_decode_step(const m3_dims* dims, float* h, float* phi, const void* Bbar_prev,
+                               const void* x_prev, const void* x, const void* B, const void* C,
+                               const void* dt, const void* theta, const float* normw_B,
+                               const float* normw_C, const float* bias_B, const float* bias_C,
+                               const float* A, const void* lam, const float* w_out, void* y,
+                               void* Bbar_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

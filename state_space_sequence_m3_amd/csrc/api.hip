@@ -392,4 +392,61 @@ m3_status m3_decode_step(const m3_dims* d, float* h, const void* Bbar_prev, cons
     return launched(m3::launch_decode(a, d->io == M3_BF16, stream), "m3_decode_step");
 }
 
+m3_status m3_layer_decode_step(const m3_dims* d, float* h, float* phi, const void* Bbar_prev, const void* x_prev,
+                               const void* x, const void* B, const void* C, const void* dt, const void* theta,
+                               const float* normw_B, const float* normw_C, const float* bias_B,
+                               const float* bias_C, const float* A, const void* lam, const float* w_out, void* y,
+                               void* Bbar_out, hipStream_t stream) {
+    m3_status s = check_common_dims(d);
+    if (s != M3_OK) return s;
+    if (d->seqlen != 1)
+        return fail(M3_E_DIMS, "m3_layer_decode_step: dims->seqlen must be 1, got %lld", (long long)d->seqlen);
+    const int64_t b = d->batch, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
+    const size_t es = io_size(d);
+    const size_t nH = (size_t)(b * H * N * P) * 4, nBp = (size_t)(b * H * R * N) * es;
+    const size_t nXp = (size_t)(b * H * R * P) * es, nStep = (size_t)(b * H) * es, nA = (size_t)H * 4;
+    const size_t nY = (size_t)(b * H * (w_out ? 1 : R) * P) * es, nWo = (size_t)(H * R * P) * 4;
+    const size_t nTh = (size_t)(b * H * (N / 2)) * es, nPhi = (size_t)(b * H * (N / 2)) * 4;
+    const size_t nW = (size_t)(H * N) * 4, nBias = (size_t)(H * R * N) * 4;
+    const Buf req[] = {{h, nH, "h"}, {phi, nPhi, "phi"}, {Bbar_prev, nBp, "Bbar_prev"}, {x_prev, nXp, "x_prev"},
+                       {x, nXp, "x"}, {B, nBp, "B"}, {C, nBp, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
+                       {A, nA, "A"}, {lam, nStep, "lam"}, {y, nY, "y"}, {Bbar_out, nBp, "Bbar_out"}};
+    if ((s = check_required(req, 13)) != M3_OK) return s;
+    if (!m3::decode_supported((int)N, (int)P, (int)R))
+        return fail(M3_E_UNSUPPORTED,
+                    "m3_layer_decode_step: no kernel for N = %lld, P = %lld, R = %lld (need P a power of two in "
+                    "[4, 256], N <= 256, R in {1,2,4,8})",
+                    (long long)N, (long long)P, (long long)R);
+    if (!aligned(h, 16)) return fail(M3_E_ALIGN, "h is not 16-byte aligned");
+    const Buf aes[] = {{Bbar_prev, 1, "Bbar_prev"}, {x_prev, 1, "x_prev"}, {x, 1, "x"}, {B, 1, "B"},
+                       {C, 1, "C"}, {dt, 1, "dt"}, {theta, 1, "theta"}, {lam, 1, "lam"}, {y, 1, "y"},
+                       {Bbar_out, 1, "Bbar_out"}};
+    if ((s = check_align(aes, 10, es)) != M3_OK) return s;
+    const Buf a4[] = {{A, 1, "A"}, {w_out, 1, "w_out"}, {phi, 1, "phi"}, {normw_B, 1, "normw_B"},
+                      {normw_C, 1, "normw_C"}, {bias_B, 1, "bias_B"}, {bias_C, 1, "bias_C"}};
+    if ((s = check_align(a4, 7, 4)) != M3_OK) return s;
+    const Buf ins[] = {{Bbar_prev, nBp, "Bbar_prev"}, {x_prev, nXp, "x_prev"}, {x, nXp, "x"}, {B, nBp, "B"},
+                       {C, nBp, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"}, {A, nA, "A"}, {lam, nStep, "lam"},
+                       {w_out, nWo, "w_out"}, {normw_B, nW, "normw_B"}, {normw_C, nW, "normw_C"},
+                       {bias_B, nBias, "bias_B"}, {bias_C, nBias, "bias_C"}};
+    const Buf outs[] = {{h, nH, "h"}, {phi, nPhi, "phi"}, {y, nY, "y"}, {Bbar_out, nBp, "Bbar_out"}};
+    if ((s = check_alias(outs, 4, ins, 14)) != M3_OK) return s;
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
+                return fail(M3_E_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+    if ((s = check_device()) != M3_OK) return s;
+    if (b == 0 || H == 0) return M3_OK;
+    if (b * H >= ((int64_t)1 << 31) / 256) return fail(M3_E_DIMS, "m3_layer_decode_step: grid too large");
+    m3::DecodeArgs a;
+    a.h = h; a.Bbar_prev = Bbar_prev; a.x_prev = x_prev; a.x = x; a.Bbar = B; a.Cbar = C;
+    a.dt = dt; a.A = A; a.lam = lam; a.w_out = w_out; a.y = y;
+    a.b = b; a.H = (int)H; a.N = (int)N; a.P = (int)P; a.R = (int)R;
+    a.theta = theta; a.normw_B = normw_B; a.normw_C = normw_C; a.bias_B = bias_B; a.bias_C = bias_C;
+    a.phi = phi; a.Bbar_out = Bbar_out;
+    a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;
+    a.eps = d->eps;
+    return launched(m3::launch_layer_decode(a, d->io == M3_BF16, stream), "m3_layer_decode_step");
+}
+
 }  // extern "C"

@@ -22,6 +22,17 @@ struct DecodeArgs {
     void* y;
     int64_t b;
     int H, N, P, R;
+    // fused step only (launch_layer_decode): Bbar and Cbar above then point at the raw B and C of
+    // the token, which the kernel normalises, biases and rotates by the carried angle first
+    const void* theta = nullptr;
+    const float* normw_B = nullptr;
+    const float* normw_C = nullptr;
+    const float* bias_B = nullptr;
+    const float* bias_C = nullptr;
+    float* phi = nullptr;        // [b, H, N/2] in/out
+    void* Bbar_out = nullptr;    // [b, H, R, N] the token's rotated B (next step's Bbar_prev)
+    int bcnorm = 0;
+    float eps = 0.f;
 };
 
 struct BcnormRopeArgs {
@@ -79,6 +90,7 @@ struct PrefillArgs {
 
 bool decode_supported(int N, int P, int R);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16_io, hipStream_t s);
+hipError_t launch_layer_decode(const DecodeArgs& a, bool bf16_io, hipStream_t s);
 
 bool bcnorm_rope_supported(int N, int R);
 int64_t bcnorm_rope_seglen();

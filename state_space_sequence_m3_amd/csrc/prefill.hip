@@ -571,23 +571,37 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             for (int ib = sb; ib < NIB; ++ib)
                 y[ib] = MM::mma(xf[sb], MM::ldk(pM_k + buf * TM + 16 * ib * LDM + 16 * sb), y[ib]);
         const rsrc_t dY = make_rsrc(yg + t0 * ystep, tail_bytes(t0, ystep, yrow));
+        // lane holds Y[(t, r) = i][p = 16 wave + 4 g + m] of row block ib
+        const int p = 16 * wave + 4 * g;
+        auto store_mixed = [&](auto RW) {   // RW: the rank as a compile-time width
+            constexpr int RR = decltype(RW)::value;
 #pragma unroll
-        for (int ib = 0; ib < NIB; ++ib) {
-            // lane holds Y[(t, r) = i][p = 16 wave + 4 g + m]
-            const int i = 16 * ib + l16;
-            const int tl = i >> rl2, r = i & rmask;
-            const int p = 16 * wave + 4 * g;
-            floatx4 yv = y[ib];
-            uint32_t off;
-            if (mix) {
+            for (int ib = 0; ib < NIB; ++ib) {
+                const int i = 16 * ib + l16;
+                floatx4 yv = y[ib];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) yv[m] = group_sum(yv[m] * wo[m], R);
+                for (int m = 0; m < 4; ++m) yv[m] = group_sum(yv[m] * wo[m], RR);
                 // one lane per step stores the mixed row; the others aim past the descriptor
-                off = r == 0 ? (uint32_t)((tl * H * P + p) * (int)sizeof(T)) : 0x80000000u;
-            } else {
-                off = (uint32_t)(((tl * H * R + r) * P + p) * (int)sizeof(T));
+                const uint32_t off = (i & (RR - 1)) == 0 ? (uint32_t)(((i / RR) * H * P + p) * (int)sizeof(T))
+                                                         : 0x80000000u;
+                store4(dY, off, yv, T{});
             }
-            store4(dY, off, yv, T{});
+        };
+        if (!mix) {
+#pragma unroll
+            for (int ib = 0; ib < NIB; ++ib) {
+                const int i = 16 * ib + l16;
+                const int tl = i >> rl2, r = i & rmask;
+                store4(dY, (uint32_t)(((tl * H * R + r) * P + p) * (int)sizeof(T)), y[ib], T{});
+            }
+        } else {
+            switch (R) {
+                case 1: store_mixed(std::integral_constant<int, 1>{}); break;
+                case 2: store_mixed(std::integral_constant<int, 2>{}); break;
+                case 4: store_mixed(std::integral_constant<int, 4>{}); break;
+                case 8: store_mixed(std::integral_constant<int, 8>{}); break;
+                default: store_mixed(std::integral_constant<int, 16>{}); break;
+            }
         }
     };
 

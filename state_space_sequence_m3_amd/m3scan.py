@@ -26,8 +26,8 @@ M3_F32, M3_BF16 = 0, 1
 M3_BCNORM = 1
 
 EXPORTED = ["m3_bcnorm_rope", "m3_bcnorm_rope_workspace_bytes", "m3_prefill",
-            "m3_prefill_workspace_bytes", "m3_layer_prefill", "m3_decode_step", "m3_last_error",
-            "m3_version"]
+            "m3_prefill_workspace_bytes", "m3_layer_prefill", "m3_decode_step",
+            "m3_layer_decode_step", "m3_last_error", "m3_version"]
 
 
 class M3Dims(ctypes.Structure):
@@ -69,6 +69,8 @@ def load(path: str = LIB_PATH):
             lib.m3_prefill_workspace_bytes.argtypes = [_DIMS]
             lib.m3_layer_prefill.restype = ctypes.c_int
             lib.m3_layer_prefill.argtypes = [_DIMS] + [_P] * 22 + [ctypes.c_size_t, _P]
+            lib.m3_layer_decode_step.restype = ctypes.c_int
+            lib.m3_layer_decode_step.argtypes = [_DIMS] + [_P] * 18 + [_P]
             lib.m3_decode_step.restype = ctypes.c_int
             lib.m3_decode_step.argtypes = [_DIMS] + [_P] * 11 + [_P]
             lib.m3_last_error.restype = ctypes.c_char_p
@@ -278,3 +280,39 @@ def m3_decode_step(h, Bbar_prev, x_prev, x, Bbar, Cbar, dt, A, lam, w_out=None, 
                               _ptr(Bbar), _ptr(Cbar), _ptr(dt), _ptr(A), _ptr(lam), _ptr(w_out),
                               _ptr(y), _stream(stream)))
     return y
+
+
+def m3_layer_decode_step(h, phi, Bbar_prev, x_prev, x, B, C, dt, theta, A, lam, normw_B=None,
+                         normw_C=None, bias_B=None, bias_C=None, w_out=None, y=None, Bbar_out=None,
+                         bcnorm=True, eps=1e-5, stream=None):
+    """Rotation + one decode token: h [b, H, N, P] and phi [b, H, N/2] updated in place.
+    Returns (y, Bbar_out); Bbar_out is the next step's Bbar_prev."""
+    lib = load()
+    b, H, N, P = h.shape
+    R = x.shape[2]
+    dev, io = h.device, x.dtype
+    f32 = torch.float32
+    _tensor(h, "h", (b, H, N, P), f32, dev)
+    _tensor(phi, "phi", (b, H, N // 2), f32, dev)
+    for name, t, shp in (("Bbar_prev", Bbar_prev, (b, H, R, N)), ("x_prev", x_prev, (b, H, R, P)),
+                         ("x", x, (b, H, R, P)), ("B", B, (b, H, R, N)), ("C", C, (b, H, R, N)),
+                         ("dt", dt, (b, H)), ("theta", theta, (b, H, N // 2)), ("lam", lam, (b, H))):
+        _tensor(t, name, shp, io, dev)
+    _tensor(A, "A", (H,), f32, dev)
+    _tensor(normw_B, "normw_B", (H, N), f32, dev)
+    _tensor(normw_C, "normw_C", (H, N), f32, dev)
+    _tensor(bias_B, "bias_B", (H, R, N), f32, dev)
+    _tensor(bias_C, "bias_C", (H, R, N), f32, dev)
+    _tensor(w_out, "w_out", (H, R, P), f32, dev)
+    yshape = (b, H, P) if w_out is not None else (b, H, R, P)
+    y = torch.empty(yshape, dtype=io, device=dev) if y is None else _tensor(y, "y", yshape, io, dev)
+    if Bbar_out is None:
+        Bbar_out = torch.empty((b, H, R, N), dtype=io, device=dev)
+    _tensor(Bbar_out, "Bbar_out", (b, H, R, N), io, dev)
+    dims = make_dims(b, 1, H, P, N, R, 0, _io_code(io), bcnorm, eps)
+    _check(lib.m3_layer_decode_step(ctypes.byref(dims), _ptr(h), _ptr(phi), _ptr(Bbar_prev),
+                                    _ptr(x_prev), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(theta),
+                                    _ptr(normw_B), _ptr(normw_C), _ptr(bias_B), _ptr(bias_C),
+                                    _ptr(A), _ptr(lam), _ptr(w_out), _ptr(y), _ptr(Bbar_out),
+                                    _stream(stream)))
+    return y, Bbar_out

@@ -6,6 +6,7 @@ from __future__ import annotations
 
 import math
 
+import numpy as np
 import pytest
 import torch
 
@@ -146,3 +147,90 @@ def test_layer_unsupported_chunk_is_rejected():
     with pytest.raises(m3scan.M3Error) as e:
         _run(d, w, 32, False)
     assert e.value.status == m3scan.M3_E_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------------------------
+# m3_layer_decode_step: rotation + decode in one launch
+# ---------------------------------------------------------------------------------------------
+def _fused_decode_run(w, steps, seed, mix, normw):
+    dinp = inputs.make_decode_inputs(w, seed, steps, normw=normw)
+    d = to_dev({k: v for k, v in dinp.items() if k not in ("tokens", "state")}, DEV)
+    toks = to_dev(dinp["tokens"], DEV)
+    st = to_dev(dinp["state"], DEV)
+    h, phi = st["h"].clone(), st["phi"].clone()
+    Bprev, xprev = st["Bbar_prev"].clone(), st["x_prev"].clone()
+    Bcur = torch.empty_like(Bprev)
+    ys = []
+    for s in range(steps):
+        x = toks["x"][s]
+        y, _ = m3scan.m3_layer_decode_step(h, phi, Bprev, xprev, x, toks["B"][s], toks["C"][s],
+                                           toks["dt"][s], toks["theta"][s], d["A"], toks["lam"][s],
+                                           d.get("normw_B"), d.get("normw_C"), d["bias_B"], d["bias_C"],
+                                           d["w_out"] if mix else None, Bbar_out=Bcur)
+        ys.append(y)
+        Bprev, Bcur = Bcur, Bprev
+        xprev = x
+    torch.cuda.synchronize()
+    consts = {k: dinp.get(k) for k in ("A", "bias_B", "bias_C", "w_out", "normw_B", "normw_C")}
+    state = dict(dinp["state"])
+    rys = []
+    for s in range(steps):
+        tok = {k: dinp["tokens"][k][s] for k in ("x", "B", "C", "dt", "lam", "theta")}
+        ry, state = oracle.decode_step(state, tok, consts, mix=mix)
+        rys.append(ry)
+    return ys, h, phi, Bprev, rys, state
+
+
+@pytest.mark.parametrize("R,io,normw", [(1, "bf16", False), (4, "bf16", True), (2, "f32", True),
+                                        (8, "bf16", False)])
+def test_layer_decode_parity(R, io, normw):
+    base = inputs.WORKLOADS["decode_b128_r4" if R > 1 else "decode_b128_r1"]
+    w = base.with_(batch=3, nheads=5, rank=R, io=io)
+    ys, h, phi, Blast, rys, state = _fused_decode_run(w, 12, seed=51 + R, mix=w.mix, normw=normw)
+    assert rel_err(torch.stack(ys, 0), np.stack(rys, 0)) <= TOL[io]
+    assert rel_err(h, state["h"]) <= TOL[io]
+    assert angle_err(phi, state["phi"]) <= (1e-4 if io == "f32" else 1e-3)
+    assert rel_err(Blast, state["Bbar_prev"]) <= TOL[io]
+
+
+def test_layer_prefill_then_layer_decode_continue_the_sequence():
+    """m3_layer_prefill over 0..L-k then k m3_layer_decode_step calls equal the oracle's layer
+    core over 0..L, token by token."""
+    w = _wl("bf16", 2, 150, 3, 64, 128, 4, 8, mix=True)
+    inp = inputs.make_prefill_inputs(w, seed=52, normw=True)
+    d = to_dev(inp, DEV)
+    k = 6
+    L0 = w.seqlen - k
+    head = {kk: (v[:, :L0].contiguous() if kk in ("x", "B", "C", "dt", "lam", "theta") else v)
+            for kk, v in d.items()}
+    Blast = torch.empty((2, 3, 4, 128), dtype=torch.bfloat16, device=DEV)
+    xlast = torch.empty((2, 3, 4, 64), dtype=torch.bfloat16, device=DEV)
+    y0, h, phi = _run(head, w, 8, True, Bbar_last=Blast, x_last=xlast)
+    Bprev, xprev, Bcur = Blast, xlast, torch.empty_like(Blast)
+    ys = [y0]
+    for t in range(L0, w.seqlen):
+        x = d["x"][:, t].contiguous()
+        y, _ = m3scan.m3_layer_decode_step(h, phi, Bprev, xprev, x, d["B"][:, t].contiguous(),
+                                           d["C"][:, t].contiguous(), d["dt"][:, t].contiguous(),
+                                           d["theta"][:, t].contiguous(), d["A"], d["lam"][:, t].contiguous(),
+                                           d["normw_B"], d["normw_C"], d["bias_B"], d["bias_C"], d["w_out"],
+                                           Bbar_out=Bcur)
+        ys.append(y.unsqueeze(1))
+        Bprev, Bcur = Bcur, Bprev
+        xprev = x
+    torch.cuda.synchronize()
+    ref = oracle.layer(inp, bcnorm=True, mix=True)
+    assert rel_err(torch.cat(ys, 1), ref["y"]) <= TOL["bf16"]
+    assert rel_err(h, ref["h_out"]) <= TOL["bf16"]
+    assert angle_err(phi, ref["phi_out"]) <= 1e-3
+
+
+def test_layer_decode_rejects_aliased_rotated_b():
+    w = inputs.WORKLOADS["decode_b128_r1"].with_(batch=1, nheads=2)
+    dinp = inputs.make_decode_inputs(w, 53, 1, device=DEV)
+    st, tk = dinp["state"], dinp["tokens"]
+    with pytest.raises(m3scan.M3Error) as e:
+        m3scan.m3_layer_decode_step(st["h"], st["phi"], st["Bbar_prev"], st["x_prev"], tk["x"][0], tk["B"][0],
+                                    tk["C"][0], tk["dt"][0], tk["theta"][0], dinp["A"], tk["lam"][0],
+                                    Bbar_out=st["Bbar_prev"])
+    assert e.value.status == m3scan.M3_E_ALIAS

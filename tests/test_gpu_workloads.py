@@ -72,18 +72,27 @@ def test_prefill_workload_sampled(name, pairs):
         assert angle_err(phi[bi:bi + 1, hi:hi + 1], ref["phi_out"]) <= 1e-3
 
 
-def _decode_steps(w, dinp, steps, mix, h, phi, Bprev, xprev, consts_dev, toks):
+def _decode_steps(w, dinp, steps, mix, h, phi, Bprev, xprev, consts_dev, toks, fused=False):
+    """`steps` tokens, each m3_bcnorm_rope (L = 1) + m3_decode_step, or with `fused` one
+    m3_layer_decode_step; the rotated-B buffers are swapped between steps."""
     Bcur = torch.empty_like(Bprev)
     Ccur = torch.empty_like(Bprev)
     ys = []
     for s in range(steps):
-        m3scan.m3_bcnorm_rope(toks["B"][s].unsqueeze(1), toks["C"][s].unsqueeze(1),
-                              toks["dt"][s].unsqueeze(1), toks["theta"][s].unsqueeze(1), None, None,
-                              consts_dev["bias_B"], consts_dev["bias_C"], phi,
-                              Bbar=Bcur.unsqueeze(1), Cbar=Ccur.unsqueeze(1), phi_out=phi)
-        y = m3scan.m3_decode_step(h, Bprev, xprev, toks["x"][s], Bcur, Ccur, toks["dt"][s],
-                                  consts_dev["A"], toks["lam"][s],
-                                  consts_dev["w_out"] if mix else None)
+        if fused:
+            y, _ = m3scan.m3_layer_decode_step(h, phi, Bprev, xprev, toks["x"][s], toks["B"][s],
+                                               toks["C"][s], toks["dt"][s], toks["theta"][s],
+                                               consts_dev["A"], toks["lam"][s], None, None,
+                                               consts_dev["bias_B"], consts_dev["bias_C"],
+                                               consts_dev["w_out"] if mix else None, Bbar_out=Bcur)
+        else:
+            m3scan.m3_bcnorm_rope(toks["B"][s].unsqueeze(1), toks["C"][s].unsqueeze(1),
+                                  toks["dt"][s].unsqueeze(1), toks["theta"][s].unsqueeze(1), None, None,
+                                  consts_dev["bias_B"], consts_dev["bias_C"], phi,
+                                  Bbar=Bcur.unsqueeze(1), Cbar=Ccur.unsqueeze(1), phi_out=phi)
+            y = m3scan.m3_decode_step(h, Bprev, xprev, toks["x"][s], Bcur, Ccur, toks["dt"][s],
+                                      consts_dev["A"], toks["lam"][s],
+                                      consts_dev["w_out"] if mix else None)
         ys.append(y)
         Bprev, Bcur = Bcur, Bprev
         xprev = toks["x"][s]
@@ -94,16 +103,17 @@ def _decode_steps(w, dinp, steps, mix, h, phi, Bprev, xprev, consts_dev, toks):
     ("decode_b128_r1", [(0, 0), (77, 31), (127, 63)]),
     ("decode_b128_r4", [(5, 2), (120, 60)]),
 ])
-def test_decode_workload_sampled(name, pairs):
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
+def test_decode_workload_sampled(name, pairs, fused):
     w = inputs.WORKLOADS[name]
-    print("workload", name, flush=True)
+    print("workload", name, "fused" if fused else "two calls", flush=True)
     steps = w.decode_steps
     dinp = inputs.make_decode_inputs(w, seed=3, steps=steps, device=DEV)
     st = dinp["state"]
     h = st["h"].clone()
     phi = st["phi"].clone()
     ys, _, _ = _decode_steps(w, dinp, steps, w.mix, h, phi, st["Bbar_prev"].clone(),
-                             st["x_prev"].clone(), dinp, dinp["tokens"])
+                             st["x_prev"].clone(), dinp, dinp["tokens"], fused=fused)
     torch.cuda.synchronize()
     for bi, hi in pairs:
         consts = {"A": dinp["A"][hi:hi + 1].cpu(), "bias_B": dinp["bias_B"][hi:hi + 1].cpu(),
