@@ -168,3 +168,43 @@ def test_binding_raises_without_the_library(tmp_path, monkeypatch):
     monkeypatch.setattr(m3scan, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         m3scan.load(str(tmp_path / "missing.so"))
+
+
+def test_layer_prefill_errors():
+    lib = m3scan.load()
+    # x, B, C, dt, theta, normw_B, normw_C, bias_B, bias_C, A, lam, w_out, phi_in, h_in,
+    # Bbar_prev, x_prev, y, h_out, phi_out, Bbar_last, x_last, ws
+    p = _ptrs(22)
+    for i in (5, 6, 7, 8, 11, 12, 13, 14, 15, 19, 20, 21):
+        p[i] = None
+    call = lambda dims, q: lib.m3_layer_prefill(ctypes.byref(dims), *q, 0, None)
+    q = list(p)
+    q[4] = None                                   # theta is required
+    assert call(_dims(chunk=32), q) == m3scan.M3_E_NULL
+    assert "theta is NULL" in m3scan.last_error()
+    assert call(_dims(chunk=48), p) == m3scan.M3_E_UNSUPPORTED   # 48-row tiles are two-call only
+    assert call(_dims(headdim=32), p) == m3scan.M3_E_UNSUPPORTED
+    q = list(p)
+    q[18] = q[4]                                  # phi_out on top of theta
+    assert call(_dims(chunk=32), q) == m3scan.M3_E_ALIAS
+    q = list(p)
+    q[12], q[18] = P(q[18].value + 4), q[18]      # phi_in partly overlapping phi_out
+    assert call(_dims(chunk=32), q) == m3scan.M3_E_ALIAS
+
+
+def test_layer_decode_step_errors():
+    lib = m3scan.load()
+    # h, phi, Bbar_prev, x_prev, x, B, C, dt, theta, normw_B, normw_C, bias_B, bias_C, A, lam,
+    # w_out, y, Bbar_out
+    p = _ptrs(18)
+    for i in (9, 10, 11, 12, 15):
+        p[i] = None
+    call = lambda dims, q: lib.m3_layer_decode_step(ctypes.byref(dims), *q, None)
+    assert call(_dims(seqlen=3), p) == m3scan.M3_E_DIMS
+    q = list(p)
+    q[17] = None
+    assert call(_dims(seqlen=1), q) == m3scan.M3_E_NULL
+    q = list(p)
+    q[17] = q[2]                                  # rotated B written over Bbar_prev
+    assert call(_dims(seqlen=1), q) == m3scan.M3_E_ALIAS
+    assert call(_dims(seqlen=1, rank=16), p) == m3scan.M3_E_UNSUPPORTED
