@@ -114,8 +114,9 @@ def layer_decode_bytes_per_head(w) -> int:
     return 2 * N * P * 4 + 2 * (N // 2) * 4 + es * (4 * R * N + 2 * R * P + 2 + N // 2 + y)
 
 
-def time_prefill(w, steps, warmup, dev, inp=None):
-    """The two-call path: m3_bcnorm_rope then m3_prefill (chunk w.chunk)."""
+def time_prefill(w, steps, warmup, dev, inp=None, scan_only=False):
+    """The two-call path: m3_bcnorm_rope then m3_prefill (chunk w.chunk).  With scan_only the
+    rotation call is left out and m3_prefill reads the raw B and C (Mamba-2 mode)."""
     if inp is None:
         inp = inputs.make_prefill_inputs(w, seed=0, device=dev)
     b, L, H, R, N, P = w.batch, w.seqlen, w.nheads, w.rank, w.dstate, w.headdim
@@ -133,12 +134,14 @@ def time_prefill(w, steps, warmup, dev, inp=None):
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        m3scan.m3_bcnorm_rope(inp["B"], inp["C"], inp["dt"], inp["theta"], inp["normw_B"],
-                              inp["normw_C"], inp["bias_B"], inp["bias_C"], None, Bbar=Bb, Cbar=Cb,
-                              phi_out=phi, bcnorm=w.bcnorm, workspace=ws)
+        if not scan_only:
+            m3scan.m3_bcnorm_rope(inp["B"], inp["C"], inp["dt"], inp["theta"], inp["normw_B"],
+                                  inp["normw_C"], inp["bias_B"], inp["bias_C"], None, Bbar=Bb, Cbar=Cb,
+                                  phi_out=phi, bcnorm=w.bcnorm, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
-        m3scan.m3_prefill(inp["x"], Bb, Cb, inp["dt"], inp["A"], inp["lam"],
+        m3scan.m3_prefill(inp["x"], inp["B"] if scan_only else Bb, inp["C"] if scan_only else Cb,
+                          inp["dt"], inp["A"], inp["lam"],
                           inp["w_out"] if w.mix else None, y=y, h_out=h, chunk=w.chunk)
         if ev is not None:
             ev[2].record(stream)
@@ -384,6 +387,28 @@ def main():
         mimo = path_stats(wm, inpm, LAYER_CHUNK_ROWS)
         del inpm
         torch.cuda.empty_cache()
+    # Mamba-2 mode (lambda = 1, theta = 0, no BCNorm/bias) and the d_state = 64 variant, on the
+    # same kernels: the fused call (chunk 32) and the plain scan (chunk 64; in Mamba-2 mode the raw
+    # B and C are already Bbar and Cbar, so the scan alone is the whole layer core)
+    variants = None
+    if not args.no_mimo:
+        variants = {}
+        for vname in ("mamba2_siso_b8_l2048", "siso_n64_b8_l2048"):
+            wv = inputs.WORKLOADS[vname]
+            inpv = inputs.make_prefill_inputs(wv, seed=0, device=dev)
+            thv = wv.batch * wv.seqlen * wv.nheads
+            ms_l = time_layer(wv, inpv, LAYER_CHUNK_ROWS // wv.rank, args.steps, args.warmup, dev)
+            lb = thv * layer_bytes_per_token_head(wv) + wv.batch * wv.nheads * wv.dstate * (wv.headdim + 1) * 4
+            entry = {"m3_layer_prefill": {"ms": ms_l, "tokens/s": wv.batch * wv.seqlen / (ms_l / 1e3),
+                                          "GB/s": lb / ms_l / 1e6, "hbm_frac": lb / ms_l / 1e6 / HBM_PEAK_GBS}}
+            if wv.mamba2:
+                _, _, _, ms_p = time_prefill(wv, args.steps, args.warmup, dev, inpv, scan_only=True)
+                pb = thv * prefill_bytes_per_token_head(wv) + wv.batch * wv.nheads * wv.dstate * wv.headdim * 4
+                entry["m3_prefill"] = {"ms": ms_p, "tokens/s": wv.batch * wv.seqlen / (ms_p / 1e3),
+                                       "GB/s": pb / ms_p / 1e6, "hbm_frac": pb / ms_p / 1e6 / HBM_PEAK_GBS}
+            variants[vname] = entry
+            del inpv
+            torch.cuda.empty_cache()
     # the step is one kernel: the fused layer kernel
     kd = kernels["m3_layer_prefill"]
     kname = "prefill_kernel<bf16,128,64,2,fused>"
@@ -439,6 +464,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "mimo4_b8_l2048": mimo,
+        "variants": variants,
         "decode": decode,
     }
     print(json.dumps(line))

@@ -19,6 +19,9 @@ with no trained weights or activations: every tensor is drawn from the distribut
 
 Draw order (fixed, so a seed names one input set): A, bias_B, bias_C, w_out, x, B, C, dt, lam,
 theta, then the decode-state tensors.
+
+Mamba-2 mode (the ``mamba2`` workloads) sets lam = 1 and theta = 0 after the draws, with BCNorm
+and biases off: the same kernels then run the exponential-Euler recurrence without rotation.
 """
 from __future__ import annotations
 
@@ -44,6 +47,7 @@ class Workload:
     mix: bool         # per-head output mixing over the R ranks
     theta_std: float = 1.0
     decode_steps: int = 0
+    mamba2: bool = False  # Mamba-2 mode: lambda = 1 (exponential-Euler step) and theta = 0
     note: str = field(default="", compare=False)
 
     @property
@@ -61,6 +65,11 @@ WORKLOADS = {
                               False, note="b8 L2048 H64 P64 N128 R1 Q64, bf16 io, fp32 state"),
     "mimo4_b8_l2048": Workload("mimo4_b8_l2048", 8, 2048, 64, 64, 128, 4, 16, "bf16", True, True,
                                True, note="b8 L2048 H64 P64 N128 R4 Q16, bf16 io, mixing on"),
+    "mamba2_siso_b8_l2048": Workload("mamba2_siso_b8_l2048", 8, 2048, 64, 64, 128, 1, 64, "bf16", False,
+                                     False, False, mamba2=True,
+                                     note="Mamba-2 mode: lambda = 1, theta = 0, no BCNorm/bias; b8 L2048 N128"),
+    "siso_n64_b8_l2048": Workload("siso_n64_b8_l2048", 8, 2048, 64, 64, 64, 1, 64, "bf16", True, True,
+                                  False, note="b8 L2048 H64 P64 N64 R1: the d_state = 64 variant"),
     "decode_b128_r1": Workload("decode_b128_r1", 128, 1, 64, 64, 128, 1, 1, "bf16", True, True,
                                False, decode_steps=256, note="b128 H64 P64 N128 R1, 256 steps"),
     "decode_b128_r4": Workload("decode_b128_r4", 128, 1, 64, 64, 128, 4, 1, "bf16", True, True,
@@ -116,6 +125,9 @@ def make_sequence(w: Workload, g, device, lead: tuple) -> dict:
     out["dt"] = torch.nn.functional.softplus(_normal(g, (*lead, H), device) - 1.0).to(io)
     out["lam"] = torch.sigmoid(_normal(g, (*lead, H), device)).to(io)
     out["theta"] = _normal(g, (*lead, H, N // 2), device, w.theta_std).to(io)
+    if w.mamba2:   # drawn first, so the other tensors of a seed are the same in both modes
+        out["lam"] = torch.ones_like(out["lam"])
+        out["theta"] = torch.zeros_like(out["theta"])
     return out
 
 

@@ -234,3 +234,28 @@ def test_layer_decode_rejects_aliased_rotated_b():
                                     tk["C"][0], tk["dt"][0], tk["theta"][0], dinp["A"], tk["lam"][0],
                                     Bbar_out=st["Bbar_prev"])
     assert e.value.status == m3scan.M3_E_ALIAS
+
+
+# ---------------------------------------------------------------------------------------------
+# Mamba-2 mode (lambda = 1, theta = 0, no BCNorm or bias) on the same kernels
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("N,R,chunk", [(128, 1, 64), (128, 1, 32), (64, 1, 32), (128, 4, 8)])
+def test_mamba2_mode_parity(N, R, chunk):
+    w = inputs.Workload("m2", 2, 150, 3, 64, N, R, chunk, "bf16", False, False, R > 1, mamba2=True)
+    inp = inputs.make_prefill_inputs(w, seed=61, carry=True)
+    d = to_dev(inp, DEV)
+    ref = oracle.layer(inp, bcnorm=False, mix=w.mix)
+    # fused call, with a carried-in state and angle (theta = 0 keeps the angle where it was)
+    y, h, phi = _run(d, w, chunk, w.mix)
+    # the plain scan straight on the raw B and C: with theta = 0, no BCNorm and no bias they are
+    # Bbar and Cbar (up to the carried angle, so this call starts from zero)
+    y2, h2 = m3scan.m3_prefill(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"],
+                               d["w_out"] if w.mix else None, chunk=chunk)
+    torch.cuda.synchronize()
+    assert rel_err(y, ref["y"]) <= TOL["bf16"]
+    assert rel_err(h, ref["h_out"]) <= TOL["bf16"]
+    assert angle_err(phi, ref["phi_out"]) <= 1e-3
+    ref2 = oracle.layer({k: v for k, v in inp.items() if k not in ("h_in", "phi_in", "Bbar_prev", "x_prev")},
+                        bcnorm=False, mix=w.mix)
+    assert rel_err(y2, ref2["y"]) <= TOL["bf16"]
+    assert rel_err(h2, ref2["h_out"]) <= TOL["bf16"]

@@ -53,15 +53,30 @@ def _layer(d, w):
     return Bb, Cb, y, h, phi
 
 
+def _fused_layer(d, w):
+    """m3_layer_prefill in the launch configuration bench.py times (chunk * R = 32)."""
+    return m3scan.m3_layer_prefill(d["x"], d["B"], d["C"], d["dt"], d["theta"], d["A"], d["lam"],
+                                   d["normw_B"], d["normw_C"], d["bias_B"], d["bias_C"],
+                                   d["w_out"] if w.mix else None, d.get("phi_in"), d.get("h_in"),
+                                   d.get("Bbar_prev"), d.get("x_prev"), chunk=32 // w.rank,
+                                   bcnorm=w.bcnorm)
+
+
 @pytest.mark.parametrize("name,pairs", [
     ("siso_b8_l2048", [(0, 0), (3, 17), (7, 63)]),
     ("mimo4_b8_l2048", [(0, 5), (6, 40)]),
+    ("mamba2_siso_b8_l2048", [(1, 2), (7, 60)]),
+    ("siso_n64_b8_l2048", [(2, 9), (5, 33)]),
 ])
-def test_prefill_workload_sampled(name, pairs):
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
+def test_prefill_workload_sampled(name, pairs, fused):
     w = inputs.WORKLOADS[name]
-    print("workload", name, flush=True)
+    print("workload", name, "fused" if fused else "two calls", flush=True)
     inp = inputs.make_prefill_inputs(w, seed=1, device=DEV)
-    Bb, Cb, y, h, phi = _layer(inp, w)
+    if fused:
+        y, h, phi = _fused_layer(inp, w)
+    else:
+        _, _, y, h, phi = _layer(inp, w)
     torch.cuda.synchronize()
     assert torch.isfinite(y).all() and torch.isfinite(h).all()
     for bi, hi in pairs:
