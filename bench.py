@@ -230,6 +230,97 @@ def time_layer_decode(w, steps, warmup, dev):
     return t0.elapsed_time(t1) / steps
 
 
+VARLEN_LENGTHS = (512, 1024, 2048, 3072, 4096, 1536, 2560, 1536)   # 16384 tokens, 8 prompts
+
+
+def time_varlen(w, steps, warmup, dev):
+    """m3_layer_prefill_varlen on a packed batch of prompts of mixed lengths (the SISO layer's
+    shapes, as many tokens as its b * L), HIP-event timed."""
+    T = sum(VARLEN_LENGTHS)
+    wp = w.with_(batch=1, seqlen=T)
+    inp = inputs.make_prefill_inputs(wp, seed=0, device=dev)
+    offs = [0]
+    for n in VARLEN_LENGTHS:
+        offs.append(offs[-1] + n)
+    cu = torch.tensor(offs, dtype=torch.int32, device=dev)
+    packed = {k: inp[k][0] for k in ("x", "B", "C", "dt", "lam", "theta")}
+    y = torch.empty((T, w.nheads, w.headdim), dtype=w.torch_io, device=dev)
+
+    def step():
+        m3scan.m3_layer_prefill_varlen(cu, packed["x"], packed["B"], packed["C"], packed["dt"], packed["theta"],
+                                       inp["A"], packed["lam"], inp["normw_B"], inp["normw_C"], inp["bias_B"],
+                                       inp["bias_C"], None, y=y.view(T, w.nheads, w.rank, w.headdim),
+                                       chunk=LAYER_CHUNK_ROWS // w.rank)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    return {"ms": ms, "tokens/s": T / (ms / 1e3), "lengths": list(VARLEN_LENGTHS),
+            "how": "m3_layer_prefill_varlen, one packed batch, chunk %d" % (LAYER_CHUNK_ROWS // w.rank)}
+
+
+def time_small_batch_decode(w, steps, dev, graph_steps=16):
+    """Decode at small batch, where launches rather than bytes bound a step: `steps` tokens of
+    m3_layer_decode_step launched one by one, and the same tokens replayed from HIP graphs that
+    each hold `graph_steps` steps.  Returns (eager ms/step, graph ms/step)."""
+    dinp = inputs.make_decode_inputs(w, seed=0, steps=graph_steps, device=dev)
+    toks, st = dinp["tokens"], dinp["state"]
+    b, H, R, N, P = w.batch, w.nheads, w.rank, w.dstate, w.headdim
+    h, phi = st["h"].clone(), st["phi"].clone()
+    bufs = [st["Bbar_prev"].clone(), torch.empty_like(st["Bbar_prev"])]
+    ys = torch.empty((graph_steps, b, H, P) if w.mix else (graph_steps, b, H, R, P), dtype=w.torch_io,
+                     device=dev)
+    x0 = st["x_prev"]
+
+    def run():
+        xprev = x0
+        for s in range(graph_steps):
+            m3scan.m3_layer_decode_step(h, phi, bufs[s % 2], xprev, toks["x"][s], toks["B"][s], toks["C"][s],
+                                        toks["dt"][s], toks["theta"][s], dinp["A"], toks["lam"][s], None,
+                                        None, dinp["bias_B"], dinp["bias_C"],
+                                        dinp["w_out"] if w.mix else None, y=ys[s],
+                                        Bbar_out=bufs[(s + 1) % 2])
+            xprev = toks["x"][s]
+
+    reps = max(1, steps // graph_steps)
+    run()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_eager = t0.elapsed_time(t1) / (reps * graph_steps)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_graph = t0.elapsed_time(t1) / (reps * graph_steps)
+    return ms_eager, ms_graph
+
+
 def time_decode(w, steps, warmup, dev):
     """`steps` consecutive decode tokens (bcnorm_rope L=1 + decode_step each), HIP-event timed."""
     total = steps + warmup
@@ -409,6 +500,7 @@ def main():
             variants[vname] = entry
             del inpv
             torch.cuda.empty_cache()
+        variants["siso_varlen_packed"] = time_varlen(w, args.steps, args.warmup, dev)
     # the step is one kernel: the fused layer kernel
     kd = kernels["m3_layer_prefill"]
     kname = "prefill_kernel<bf16,128,64,2,fused>"
@@ -437,6 +529,12 @@ def main():
                                           "decode_step_hbm_frac": dbytes / ms_dec / 1e6 / HBM_PEAK_GBS,
                                           "decode_step_bytes": dbytes}}
             torch.cuda.empty_cache()
+        # small batch (the long-context workload's decode tail: b = 1, H = 64, R = 4)
+        wl = inputs.WORKLOADS["long_mimo4_b1_l16384"]
+        ms_e, ms_g = time_small_batch_decode(wl, args.decode_steps, dev)
+        decode["decode_b1_r4"] = {"steps_per_s": 1e3 / ms_g, "ms_per_step": ms_g,
+                                  "how": "m3_layer_decode_step, 16 steps per HIP graph replay",
+                                  "eager": {"steps_per_s": 1e3 / ms_e, "ms_per_step": ms_e}}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -233,6 +233,31 @@ const char* m3_last_error(void);
 const char* m3_version(void);
 
 /*
+ * m3_layer_prefill_varlen -- m3_layer_prefill over a packed batch of sequences of different
+ * lengths (serving: prompts of mixed lengths without padding).
+ *
+ * Defined by: m3_layer_prefill, applied to each sequence separately.  Sequence s (s < b =
+ * dims->batch) is tokens cu_seqlens[s] .. cu_seqlens[s+1] - 1 of T = dims->seqlen packed tokens:
+ *   cu_seqlens  [b + 1] int32 (device), cu_seqlens[0] = 0, non-decreasing, cu_seqlens[b] = T
+ *   x [T, H, R, P], B, C [T, H, R, N], dt, lam [T, H], theta [T, H, N/2] io; y [T, H, P] (with
+ *   w_out) or [T, H, R, P]
+ *   per-sequence tensors as in m3_layer_prefill: h_in, h_out [b, H, N, P], phi_in, phi_out
+ *   [b, H, N/2], Bbar_prev, Bbar_last [b, H, R, N], x_prev, x_last [b, H, R, P]
+ * An empty sequence passes its carry through (h_out = h_in, phi_out = phi_in reduced, Bbar_last
+ * = Bbar_prev, x_last = x_prev).  cu_seqlens is read on the device; offsets outside [0, T] are
+ * clamped into it, so no access leaves the packed arrays.  Shapes, aliasing and errors as
+ * m3_layer_prefill (cu_seqlens NULL: M3_E_NULL).
+ */
+m3_status m3_layer_prefill_varlen(const m3_dims* dims, const int32_t* cu_seqlens, const void* x,
+                                  const void* B, const void* C, const void* dt, const void* theta,
+                                  const float* normw_B, const float* normw_C, const float* bias_B,
+                                  const float* bias_C, const float* A, const void* lam,
+                                  const float* w_out, const float* phi_in, const float* h_in,
+                                  const void* Bbar_prev, const void* x_prev, void* y, float* h_out,
+                                  float* phi_out, void* Bbar_last, void* x_last,
+                                  hipStream_t stream);
+
+/*
  * m3_layer_decode_step -- m3_bcnorm_rope (L = 1) followed by m3_decode_step, in one launch.
  *
  * Defined by: the two calls it stands for (see them above); papernotes.org, key design 4 (the

@@ -127,6 +127,105 @@ hipError_t copy_or_zero(void* dst, const void* src, size_t bytes, hipStream_t s)
 
 }  // namespace
 
+namespace {
+
+// m3_layer_prefill and its packed form: with cu_seqlens the sequence tensors are [T, H, ...] with
+// T = dims->seqlen tokens, and dims->batch sequences; per-sequence tensors stay [b, H, ...]
+m3_status layer_prefill(const m3_dims* d, bool packed, const int32_t* cu_seqlens, const void* x, const void* B,
+                        const void* C, const void* dt, const void* theta, const float* normw_B, const float* normw_C,
+                        const float* bias_B, const float* bias_C, const float* A, const void* lam,
+                        const float* w_out, const float* phi_in, const float* h_in, const void* Bbar_prev,
+                        const void* x_prev, void* y, float* h_out, float* phi_out, void* Bbar_last, void* x_last,
+                        hipStream_t stream, const char* fn) {
+    m3_status s = check_common_dims(d);
+    if (s != M3_OK) return s;
+    const int64_t b = d->batch, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
+    // tokens per sequence tensor: b * L dense, T packed
+    const int64_t L = d->seqlen, BL = packed ? L : b * L;
+    const int64_t Q = d->chunk > 0 ? d->chunk : (32 / R > 0 ? 32 / R : 1);
+    const size_t es = io_size(d);
+    const size_t nX = (size_t)(BL * H * R * P) * es, nBC = (size_t)(BL * H * R * N) * es;
+    const size_t nStep = (size_t)(BL * H) * es, nA = (size_t)H * 4;
+    const size_t nTh = (size_t)(BL * H * (N / 2)) * es, nPhi = (size_t)(b * H * (N / 2)) * 4;
+    const size_t nY = (size_t)(BL * H * (w_out ? 1 : R) * P) * es, nH = (size_t)(b * H * N * P) * 4;
+    const size_t nBp = (size_t)(b * H * R * N) * es, nXp = (size_t)(b * H * R * P) * es;
+    const size_t nWo = (size_t)(H * R * P) * 4, nW = (size_t)(H * N) * 4, nBias = (size_t)(H * R * N) * 4;
+    const Buf req[] = {{x, nX, "x"}, {B, nBC, "B"}, {C, nBC, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
+                       {A, nA, "A"}, {lam, nStep, "lam"}, {y, nY, "y"}, {h_out, nH, "h_out"},
+                       {phi_out, nPhi, "phi_out"}};
+    if ((s = check_required(req, 10)) != M3_OK) return s;
+    if (packed && cu_seqlens == nullptr) return fail(M3_E_NULL, "cu_seqlens is NULL");
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(M3_E_ALIGN, "cu_seqlens is not 4-byte aligned");
+    if (Q * R > 64 || !m3::layer_supported((int)N, (int)P, (int)R, (int)(Q * R), d->io == M3_BF16))
+        return fail(M3_E_UNSUPPORTED,
+                    "%s: no kernel for N = %lld, P = %lld, R = %lld, chunk*R = %lld (supported: (N,P) "
+                    "in {(16,16),(64,64),(128,64)}, R in {1,2,4,8,16}, chunk*R in {16,32,64})",
+                    fn, (long long)N, (long long)P, (long long)R, (long long)(Q * R));
+    if (Q * H * R * (N > P ? N : P) * (int64_t)es >= ((int64_t)1 << 31))
+        return fail(M3_E_DIMS, "%s: nheads * rank = %lld is too large for one chunk", fn, (long long)(H * R));
+    const Buf a16[] = {{x, 1, "x"}, {B, 1, "B"}, {C, 1, "C"}, {theta, 1, "theta"}, {y, 1, "y"},
+                       {h_out, 1, "h_out"}, {h_in, 1, "h_in"}};
+    if ((s = check_align(a16, 7, 16)) != M3_OK) return s;
+    const Buf aes[] = {{dt, 1, "dt"}, {lam, 1, "lam"}, {Bbar_prev, 1, "Bbar_prev"}, {x_prev, 1, "x_prev"},
+                       {Bbar_last, 1, "Bbar_last"}, {x_last, 1, "x_last"}};
+    if ((s = check_align(aes, 6, es)) != M3_OK) return s;
+    const Buf a4[] = {{A, 1, "A"}, {w_out, 1, "w_out"}, {normw_B, 1, "normw_B"}, {normw_C, 1, "normw_C"},
+                      {bias_B, 1, "bias_B"}, {bias_C, 1, "bias_C"}, {phi_in, 1, "phi_in"}, {phi_out, 1, "phi_out"}};
+    if ((s = check_align(a4, 8, 4)) != M3_OK) return s;
+    const Buf ins[] = {{x, nX, "x"}, {B, nBC, "B"}, {C, nBC, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
+                       {A, nA, "A"}, {lam, nStep, "lam"}, {w_out, nWo, "w_out"}, {normw_B, nW, "normw_B"},
+                       {normw_C, nW, "normw_C"}, {bias_B, nBias, "bias_B"}, {bias_C, nBias, "bias_C"},
+                       {Bbar_prev, nBp, "Bbar_prev"}, {x_prev, nXp, "x_prev"}};
+    const Buf outs[] = {{y, nY, "y"}, {h_out, nH, "h_out"}, {phi_out, nPhi, "phi_out"},
+                        {Bbar_last, nBp, "Bbar_last"}, {x_last, nXp, "x_last"}};
+    if ((s = check_alias(outs, 5, ins, 14)) != M3_OK) return s;
+    for (int o = 0; o < 5; ++o)
+        if (overlap(cu_seqlens, (size_t)(b + 1) * 4, outs[o].p, outs[o].bytes))
+            return fail(M3_E_ALIAS, "cu_seqlens overlaps %s", outs[o].name);
+    if (h_in && h_in != h_out && overlap(h_in, nH, h_out, nH)) return fail(M3_E_ALIAS, "h_out partially overlaps h_in");
+    if (phi_in && phi_in != phi_out && overlap(phi_in, nPhi, phi_out, nPhi))
+        return fail(M3_E_ALIAS, "phi_out partially overlaps phi_in");
+    const Buf carried[] = {{h_in, nH, "h_in"}, {phi_in, nPhi, "phi_in"}};
+    for (int i = 0; i < 2; ++i)
+        for (int o = 0; o < 5; ++o) {
+            const bool same_buffer = (i == 0 && o == 1 && h_in == h_out) || (i == 1 && o == 2 && phi_in == phi_out);
+            if (!same_buffer && overlap(carried[i].p, carried[i].bytes, outs[o].p, outs[o].bytes))
+                return fail(M3_E_ALIAS, "%s overlaps %s", carried[i].name, outs[o].name);
+        }
+    if ((s = check_device()) != M3_OK) return s;
+    if (b == 0 || H == 0) return M3_OK;
+    if (L == 0) {   // no tokens at all (dense L = 0, or a packed batch of empty sequences)
+        // nothing to scan: the carried state and angle pass through unchanged
+        hipError_t e = copy_or_zero(h_out, h_in == h_out ? h_out : h_in, nH, stream);
+        if (e == hipSuccess) e = copy_or_zero(Bbar_last, Bbar_prev, nBp, stream);
+        if (e == hipSuccess) e = copy_or_zero(x_last, x_prev, nXp, stream);
+        if (e == hipSuccess) {
+            const int64_t n = b * H * (N / 2);
+            hipLaunchKernelGGL(wrap_angle_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, phi_out,
+                               phi_in, n);
+            e = hipGetLastError();
+        }
+        return launched(e, fn);
+    }
+    m3::PrefillArgs a;
+    a.x = x; a.Bbar = B; a.Cbar = C; a.dt = dt; a.A = A; a.lam = lam; a.w_out = w_out;
+    a.h_in = h_in; a.Bbar_prev = Bbar_prev; a.x_prev = x_prev;
+    a.y = y; a.h_out = h_out; a.Bbar_last = Bbar_last; a.x_last = x_last;
+    a.b = b; a.L = L; a.H = (int)H; a.N = (int)N; a.P = (int)P; a.R = (int)R; a.Q = (int)Q;
+    a.theta = theta; a.normw_B = normw_B; a.normw_C = normw_C; a.bias_B = bias_B; a.bias_C = bias_C;
+    a.phi_in = phi_in; a.phi_out = phi_out;
+    a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;
+    a.eps = d->eps;
+    if (packed) {
+        a.cu_seqlens = cu_seqlens;
+        a.T = L;
+        a.L = 0;
+    }
+    return launched(m3::launch_layer(a, d->io == M3_BF16, stream), fn);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* m3_last_error(void) { return g_err; }
@@ -277,79 +376,19 @@ m3_status m3_layer_prefill(const m3_dims* d, const void* x, const void* B, const
                            size_t workspace_bytes, hipStream_t stream) {
     (void)workspace;
     (void)workspace_bytes;
-    m3_status s = check_common_dims(d);
-    if (s != M3_OK) return s;
-    const int64_t b = d->batch, L = d->seqlen, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
-    const int64_t Q = d->chunk > 0 ? d->chunk : (32 / R > 0 ? 32 / R : 1);
-    const size_t es = io_size(d);
-    const size_t nX = (size_t)(b * L * H * R * P) * es, nBC = (size_t)(b * L * H * R * N) * es;
-    const size_t nStep = (size_t)(b * L * H) * es, nA = (size_t)H * 4;
-    const size_t nTh = (size_t)(b * L * H * (N / 2)) * es, nPhi = (size_t)(b * H * (N / 2)) * 4;
-    const size_t nY = (size_t)(b * L * H * (w_out ? 1 : R) * P) * es, nH = (size_t)(b * H * N * P) * 4;
-    const size_t nBp = (size_t)(b * H * R * N) * es, nXp = (size_t)(b * H * R * P) * es;
-    const size_t nWo = (size_t)(H * R * P) * 4, nW = (size_t)(H * N) * 4, nBias = (size_t)(H * R * N) * 4;
-    const Buf req[] = {{x, nX, "x"}, {B, nBC, "B"}, {C, nBC, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
-                       {A, nA, "A"}, {lam, nStep, "lam"}, {y, nY, "y"}, {h_out, nH, "h_out"},
-                       {phi_out, nPhi, "phi_out"}};
-    if ((s = check_required(req, 10)) != M3_OK) return s;
-    if (Q * R > 64 || !m3::layer_supported((int)N, (int)P, (int)R, (int)(Q * R), d->io == M3_BF16))
-        return fail(M3_E_UNSUPPORTED,
-                    "m3_layer_prefill: no kernel for N = %lld, P = %lld, R = %lld, chunk*R = %lld (supported: (N,P) "
-                    "in {(16,16),(64,64),(128,64)}, R in {1,2,4,8,16}, chunk*R in {16,32,64})",
-                    (long long)N, (long long)P, (long long)R, (long long)(Q * R));
-    if (Q * H * R * (N > P ? N : P) * (int64_t)es >= ((int64_t)1 << 31))
-        return fail(M3_E_DIMS, "m3_layer_prefill: nheads * rank = %lld is too large for one chunk", (long long)(H * R));
-    const Buf a16[] = {{x, 1, "x"}, {B, 1, "B"}, {C, 1, "C"}, {theta, 1, "theta"}, {y, 1, "y"},
-                       {h_out, 1, "h_out"}, {h_in, 1, "h_in"}};
-    if ((s = check_align(a16, 7, 16)) != M3_OK) return s;
-    const Buf aes[] = {{dt, 1, "dt"}, {lam, 1, "lam"}, {Bbar_prev, 1, "Bbar_prev"}, {x_prev, 1, "x_prev"},
-                       {Bbar_last, 1, "Bbar_last"}, {x_last, 1, "x_last"}};
-    if ((s = check_align(aes, 6, es)) != M3_OK) return s;
-    const Buf a4[] = {{A, 1, "A"}, {w_out, 1, "w_out"}, {normw_B, 1, "normw_B"}, {normw_C, 1, "normw_C"},
-                      {bias_B, 1, "bias_B"}, {bias_C, 1, "bias_C"}, {phi_in, 1, "phi_in"}, {phi_out, 1, "phi_out"}};
-    if ((s = check_align(a4, 8, 4)) != M3_OK) return s;
-    const Buf ins[] = {{x, nX, "x"}, {B, nBC, "B"}, {C, nBC, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
-                       {A, nA, "A"}, {lam, nStep, "lam"}, {w_out, nWo, "w_out"}, {normw_B, nW, "normw_B"},
-                       {normw_C, nW, "normw_C"}, {bias_B, nBias, "bias_B"}, {bias_C, nBias, "bias_C"},
-                       {Bbar_prev, nBp, "Bbar_prev"}, {x_prev, nXp, "x_prev"}};
-    const Buf outs[] = {{y, nY, "y"}, {h_out, nH, "h_out"}, {phi_out, nPhi, "phi_out"},
-                        {Bbar_last, nBp, "Bbar_last"}, {x_last, nXp, "x_last"}};
-    if ((s = check_alias(outs, 5, ins, 14)) != M3_OK) return s;
-    if (h_in && h_in != h_out && overlap(h_in, nH, h_out, nH)) return fail(M3_E_ALIAS, "h_out partially overlaps h_in");
-    if (phi_in && phi_in != phi_out && overlap(phi_in, nPhi, phi_out, nPhi))
-        return fail(M3_E_ALIAS, "phi_out partially overlaps phi_in");
-    const Buf carried[] = {{h_in, nH, "h_in"}, {phi_in, nPhi, "phi_in"}};
-    for (int i = 0; i < 2; ++i)
-        for (int o = 0; o < 5; ++o) {
-            const bool same_buffer = (i == 0 && o == 1 && h_in == h_out) || (i == 1 && o == 2 && phi_in == phi_out);
-            if (!same_buffer && overlap(carried[i].p, carried[i].bytes, outs[o].p, outs[o].bytes))
-                return fail(M3_E_ALIAS, "%s overlaps %s", carried[i].name, outs[o].name);
-        }
-    if ((s = check_device()) != M3_OK) return s;
-    if (b == 0 || H == 0) return M3_OK;
-    if (L == 0) {
-        // nothing to scan: the carried state and angle pass through unchanged
-        hipError_t e = copy_or_zero(h_out, h_in == h_out ? h_out : h_in, nH, stream);
-        if (e == hipSuccess) e = copy_or_zero(Bbar_last, Bbar_prev, nBp, stream);
-        if (e == hipSuccess) e = copy_or_zero(x_last, x_prev, nXp, stream);
-        if (e == hipSuccess) {
-            const int64_t n = b * H * (N / 2);
-            hipLaunchKernelGGL(wrap_angle_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, phi_out,
-                               phi_in, n);
-            e = hipGetLastError();
-        }
-        return launched(e, "m3_layer_prefill");
-    }
-    m3::PrefillArgs a;
-    a.x = x; a.Bbar = B; a.Cbar = C; a.dt = dt; a.A = A; a.lam = lam; a.w_out = w_out;
-    a.h_in = h_in; a.Bbar_prev = Bbar_prev; a.x_prev = x_prev;
-    a.y = y; a.h_out = h_out; a.Bbar_last = Bbar_last; a.x_last = x_last;
-    a.b = b; a.L = L; a.H = (int)H; a.N = (int)N; a.P = (int)P; a.R = (int)R; a.Q = (int)Q;
-    a.theta = theta; a.normw_B = normw_B; a.normw_C = normw_C; a.bias_B = bias_B; a.bias_C = bias_C;
-    a.phi_in = phi_in; a.phi_out = phi_out;
-    a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;
-    a.eps = d->eps;
-    return launched(m3::launch_layer(a, d->io == M3_BF16, stream), "m3_layer_prefill");
+    return layer_prefill(d, false, nullptr, x, B, C, dt, theta, normw_B, normw_C, bias_B, bias_C, A, lam, w_out, phi_in,
+                         h_in, Bbar_prev, x_prev, y, h_out, phi_out, Bbar_last, x_last, stream, "m3_layer_prefill");
+}
+
+m3_status m3_layer_prefill_varlen(const m3_dims* d, const int32_t* cu_seqlens, const void* x, const void* B,
+                                  const void* C, const void* dt, const void* theta, const float* normw_B,
+                                  const float* normw_C, const float* bias_B, const float* bias_C, const float* A,
+                                  const void* lam, const float* w_out, const float* phi_in, const float* h_in,
+                                  const void* Bbar_prev, const void* x_prev, void* y, float* h_out, float* phi_out,
+                                  void* Bbar_last, void* x_last, hipStream_t stream) {
+    return layer_prefill(d, true, cu_seqlens, x, B, C, dt, theta, normw_B, normw_C, bias_B, bias_C, A, lam, w_out,
+                         phi_in, h_in, Bbar_prev, x_prev, y, h_out, phi_out, Bbar_last, x_last, stream,
+                         "m3_layer_prefill_varlen");
 }
 
 m3_status m3_decode_step(const m3_dims* d, float* h, const void* Bbar_prev, const void* x_prev, const void* x,

@@ -86,6 +86,10 @@ struct PrefillArgs {
     float* phi_out = nullptr;
     int bcnorm = 0;
     float eps = 0.f;
+    // packed variable-length batch: sequence s holds tokens [cu_seqlens[s], cu_seqlens[s+1]) of
+    // T packed tokens (b = number of sequences); nullptr = dense [b, L, ...]
+    const int32_t* cu_seqlens = nullptr;
+    int64_t T = 0;
 };
 
 bool decode_supported(int N, int P, int R);

@@ -204,11 +204,19 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const int h = (int)(bh % a.H);
     const int H = a.H, R = a.R, Q = a.Q;
     const int rl2 = __builtin_ctz((unsigned)R), rmask = R - 1;
-    const int64_t L = a.L;
+    // dense: sequence b is steps [0, L) of [b, L, ...]; packed: tokens [cu[b], cu[b+1]) of T,
+    // clamped into [0, T) so that any offsets stay inside the packed arrays
+    int64_t L = a.L, t_first = b * a.L;
+    if (a.cu_seqlens) {
+        const int64_t s0 = min(max((int64_t)a.cu_seqlens[b], (int64_t)0), a.T);
+        const int64_t s1 = min(max((int64_t)a.cu_seqlens[b + 1], s0), a.T);
+        t_first = s0;
+        L = s1 - s0;
+    }
     const int64_t nchunk = (L + Q - 1) / Q;
     const float Alog2 = a.A[h] * kLog2e;
     // (b, t = 0, h) bases; step t of this (b, h) is t * H rows further
-    const int64_t row_bh = b * L * H + h;
+    const int64_t row_bh = t_first * H + h;
     const int64_t HRN = (int64_t)H * R * N, HRP = (int64_t)H * R * P;
     const T* Xg = (const T*)a.x + row_bh * R * P;
     const T* Bg = (const T*)a.Bbar + row_bh * R * N;
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // ---- chunk prefetch into registers (set = chunk parity when pipelined) ----------------
     uint4 rc[NBUF][MAXC], rb[NBUF][MAXC], rx[NBUF][MAXX];
     typedef typename IoBits<T>::type Bits;
-    Bits nd[NBUF], nl[NBUF], ndn[NBUF], nln[NBUF];   // dt, lambda at t and t + 1 (io bits; wave 0 uses them)
+    Bits nd[NBUF], nl[NBUF], ndn[NBUF], nln[NBUF];   // dt, lambda at t and t + 1 (io bits; the last wave uses them)
     auto load_chunk = [&](int64_t c, int set) {
         const int64_t t0 = c * Q;
         const uint32_t nbc = tail_bytes(t0, HRN, (int64_t)R * N), nbx = tail_bytes(t0, HRP, (int64_t)R * P);
@@ -256,8 +264,8 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         {
             // steps t0 + lane and t0 + lane + 1; zero past the sequence end.  Lanes at or past Q
             // read the next chunk's values, which only reach scan lanes that are never read.  Only
-            // wave 0 uses them; every wave loads them so that the number of loads in flight is the
-            // same on every path (the compiler's wait counts stay exact).
+            // the last wave uses them; every wave loads them so that the number of loads in flight
+            // is the same on every path (the compiler's wait counts stay exact).
             const uint32_t nbs = tail_bytes(t0, H, 1);
             const rsrc_t dD = make_rsrc(dtg + t0 * H, nbs), dL = make_rsrc(lamg + t0 * H, nbs);
             const uint32_t o0 = (uint32_t)(lane * H * (int)sizeof(T)), o1 = o0 + (uint32_t)(H * (int)sizeof(T));
@@ -328,34 +336,46 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     auto stage_bc = [&](int set, int k, int i, int buf) {
         const int t = i >> rl2, r = i & rmask;
         const int n0 = cC0 * VE;
+        // angles first (LDS read + hardware sin/cos, independent of the rest)
         float cs[VE / 2], sn[VE / 2];
         {
             const float* ph = sPhi + buf * TPH + t * LDPHI + n0 / 2;
 #pragma unroll
-            for (int q = 0; q < VE / 2; ++q) __sincosf(ph[q], &sn[q], &cs[q]);   // |angle| <= pi
+            for (int q = 0; q < VE / 2; ++q) __sincosf(ph[q], &sn[q], &cs[q]);   // |angle| < 256 turns
+        }
+        float sc[2] = {1.f, 1.f};
+        if (a.bcnorm) {   // RMS over the row's N values, spread over VPN consecutive lanes
+            float q2[2];
+#pragma unroll
+            for (int which = 0; which < 2; ++which) {
+                float x[VE];
+                unpack16(which == 0 ? rb[set][k] : rc[set][k], x, T{});
+                float part[4] = {0.f, 0.f, 0.f, 0.f};   // a tree, not one long chain
+#pragma unroll
+                for (int e = 0; e < VE; ++e) part[e & 3] = fmaf(x[e], x[e], part[e & 3]);
+                q2[which] = (part[0] + part[1]) + (part[2] + part[3]);
+            }
+            // the two rows' lane sums interleave
+            q2[0] = group_sum(q2[0], VPN);
+            q2[1] = group_sum(q2[1], VPN);
+#pragma unroll
+            for (int which = 0; which < 2; ++which)
+                // hardware 1/sqrt; the clamp keeps its argument out of the denormal range (an
+                // all-zero row stays zero either way)
+                sc[which] = __builtin_amdgcn_rsqf(fmaxf(fmaf(q2[which], invN, a.eps), 1e-30f));
         }
 #pragma unroll
         for (int which = 0; which < 2; ++which) {
             float x[VE];
             unpack16(which == 0 ? rb[set][k] : rc[set][k], x, T{});
-            float sc = 1.f;
-            if (a.bcnorm) {   // RMS over the row's N values, spread over VPN consecutive lanes
-                float qs = 0.f;
-#pragma unroll
-                for (int e = 0; e < VE; ++e) qs = fmaf(x[e], x[e], qs);
-                qs = group_sum(qs, VPN);
-                // hardware 1/sqrt; the clamp keeps its argument out of the denormal range (an
-                // all-zero row stays zero either way)
-                sc = __builtin_amdgcn_rsqf(fmaxf(fmaf(qs, invN, a.eps), 1e-30f));
-            }
             const float* bw = sBias + (which * R + r) * N + n0;
             if (has_w) {
                 const float* ww = sWt + which * N + n0;
 #pragma unroll
-                for (int e = 0; e < VE; ++e) x[e] = fmaf(x[e] * sc, ww[e], bw[e]);
+                for (int e = 0; e < VE; ++e) x[e] = fmaf(x[e] * sc[which], ww[e], bw[e]);
             } else {
 #pragma unroll
-                for (int e = 0; e < VE; ++e) x[e] = fmaf(x[e], sc, bw[e]);
+                for (int e = 0; e < VE; ++e) x[e] = fmaf(x[e], sc[which], bw[e]);
             }
 #pragma unroll
             for (int q = 0; q < VE / 2; ++q) {
@@ -367,8 +387,9 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             else *(uint4*)(sC + buf * TC + i * LDC + n0) = pack16(x, T{});
         }
     };
-    // wave 0: the chunk's per-step scalars (lane = step) -> per-row copies in LDS.  Lanes past
-    // the chunk only add to later lanes of the scan, which are never read.
+    // the last wave (the one with the fewest score tiles): the chunk's per-step scalars (lane =
+    // step) -> per-row copies in LDS.  Lanes past the chunk only add to later lanes of the scan,
+    // which are never read.
     auto stage_scalars = [&](float d, float lm, float dn, float lmn, int buf) {
         const float l2 = wave_scan_add(d * Alog2);   // l_t in log2 units, inclusive over the chunk
         const float gam = lm * d;
@@ -409,7 +430,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         } else if (j < MAXC + MAXX) {
             const int k = j - MAXC, i = iX0 + k * RKX;
             if (FULLX || i < QR) *(uint4*)(sX + buf * TX + i * LDX + cX0 * VE) = rx[set][k];
-        } else if (wave == 0) {
+        } else if (wave == NW - 1) {
             stage_scalars(bits_to_f32(nd[set]), bits_to_f32(nl[set]), bits_to_f32(ndn[set]),
                           bits_to_f32(nln[set]), buf);
         }
@@ -648,19 +669,19 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             const bool has1 = c + 1 < nchunk, has2 = c + 2 < nchunk;
             load_chunk(c + 2, p);
             // stage chunk c + 1 (register set q) into buffer q, item j after K block
-            // (2 j + 1) NB / (2 NITEM)
+            // (2 j + 1) NB / (2 NITEM); fused: the angles of chunk c + 2 in K block NB / 2
             auto hook = [&](int k) {
-                if (!has1) return;
+                if (has1) {
 #pragma unroll
-                for (int j = 0; j < NITEM; ++j)
-                    if ((2 * j + 1) * NB / (2 * NITEM) == k) stage_item(j, q, q);
-            };
-            auto after = [&]() {
-                if (FUSED) {
+                    for (int j = 0; j < NITEM; ++j)
+                        if ((2 * j + 1) * NB / (2 * NITEM) == k) stage_item(j, q, q);
+                }
+                if (FUSED && k == NB / 2) {
                     if (has2) scan(c + 2, p, q);
                     load_theta(c + 3);
                 }
             };
+            auto after = [&]() {};
             chunk_compute(p, c, hook, after);
         };
         for (int64_t c = 0; c < nchunk; c += 2) {
@@ -675,7 +696,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             const float cdn = bits_to_f32(ndn[0]), cln = bits_to_f32(nln[0]);
             load_theta(c + 1);    // scanned at the end of this chunk's part 1
             load_chunk(c + 1, 0);   // the next chunk's loads fly during this one
-            if (wave == 0) stage_scalars(cd, cl, cdn, cln, 0);
+            if (wave == NW - 1) stage_scalars(cd, cl, cdn, cln, 0);
             __syncthreads();
             auto after = [&]() {
                 if (FUSED && c + 1 < nchunk) scan(c + 1, 0, 0);
@@ -705,6 +726,16 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             for (int e = tid; e < R * P; e += NT) ((T*)a.x_last)[bh * R * P + e] = Xg[(L - 1) * HRP + e];
         if (FUSED && a.phi_out)
             for (int k = tid; k < K; k += NT) a.phi_out[bh * K + k] = sPhi[lb * TPH + (Q - 1) * LDPHI + k];
+    } else {
+        // an empty sequence of a packed batch: the carry passes through unchanged
+        if (a.Bbar_last)
+            for (int e = tid; e < R * N; e += NT)
+                ((T*)a.Bbar_last)[bh * R * N + e] = a.Bbar_prev ? ((const T*)a.Bbar_prev)[bh * R * N + e] : T{};
+        if (a.x_last)
+            for (int e = tid; e < R * P; e += NT)
+                ((T*)a.x_last)[bh * R * P + e] = a.x_prev ? ((const T*)a.x_prev)[bh * R * P + e] : T{};
+        if (FUSED && a.phi_out)
+            for (int k = tid; k < K; k += NT) a.phi_out[bh * K + k] = a.phi_in ? wrap_angle(a.phi_in[bh * K + k]) : 0.f;
     }
 }
 

@@ -26,7 +26,8 @@ M3_F32, M3_BF16 = 0, 1
 M3_BCNORM = 1
 
 EXPORTED = ["m3_bcnorm_rope", "m3_bcnorm_rope_workspace_bytes", "m3_prefill",
-            "m3_prefill_workspace_bytes", "m3_layer_prefill", "m3_decode_step",
+            "m3_prefill_workspace_bytes", "m3_layer_prefill", "m3_layer_prefill_varlen",
+            "m3_decode_step",
             "m3_layer_decode_step", "m3_last_error", "m3_version"]
 
 
@@ -69,6 +70,8 @@ def load(path: str = LIB_PATH):
             lib.m3_prefill_workspace_bytes.argtypes = [_DIMS]
             lib.m3_layer_prefill.restype = ctypes.c_int
             lib.m3_layer_prefill.argtypes = [_DIMS] + [_P] * 22 + [ctypes.c_size_t, _P]
+            lib.m3_layer_prefill_varlen.restype = ctypes.c_int
+            lib.m3_layer_prefill_varlen.argtypes = [_DIMS] + [_P] * 22 + [_P]
             lib.m3_layer_decode_step.restype = ctypes.c_int
             lib.m3_layer_decode_step.argtypes = [_DIMS] + [_P] * 18 + [_P]
             lib.m3_decode_step.restype = ctypes.c_int
@@ -316,3 +319,51 @@ def m3_layer_decode_step(h, phi, Bbar_prev, x_prev, x, B, C, dt, theta, A, lam, 
                                     _ptr(A), _ptr(lam), _ptr(w_out), _ptr(y), _ptr(Bbar_out),
                                     _stream(stream)))
     return y, Bbar_out
+
+
+def m3_layer_prefill_varlen(cu_seqlens, x, B, C, dt, theta, A, lam, normw_B=None, normw_C=None,
+                            bias_B=None, bias_C=None, w_out=None, phi_in=None, h_in=None,
+                            Bbar_prev=None, x_prev=None, y=None, h_out=None, phi_out=None,
+                            Bbar_last=None, x_last=None, chunk=0, bcnorm=True, eps=1e-5, stream=None):
+    """m3_layer_prefill over a packed batch: x [T, H, R, P], B, C [T, H, R, N], ...; sequence s is
+    tokens cu_seqlens[s]:cu_seqlens[s+1] (int32 device tensor of b + 1 offsets).
+    Returns (y, h_out, phi_out)."""
+    lib = load()
+    T, H, R, P = x.shape
+    N = B.shape[-1]
+    b = cu_seqlens.numel() - 1
+    dev, io = x.device, x.dtype
+    f32 = torch.float32
+    _tensor(cu_seqlens, "cu_seqlens", (b + 1,), torch.int32, dev)
+    _tensor(B, "B", (T, H, R, N), io, dev)
+    _tensor(C, "C", (T, H, R, N), io, dev)
+    _tensor(dt, "dt", (T, H), io, dev)
+    _tensor(theta, "theta", (T, H, N // 2), io, dev)
+    _tensor(lam, "lam", (T, H), io, dev)
+    _tensor(A, "A", (H,), f32, dev)
+    _tensor(normw_B, "normw_B", (H, N), f32, dev)
+    _tensor(normw_C, "normw_C", (H, N), f32, dev)
+    _tensor(bias_B, "bias_B", (H, R, N), f32, dev)
+    _tensor(bias_C, "bias_C", (H, R, N), f32, dev)
+    _tensor(w_out, "w_out", (H, R, P), f32, dev)
+    _tensor(phi_in, "phi_in", (b, H, N // 2), f32, dev)
+    _tensor(h_in, "h_in", (b, H, N, P), f32, dev)
+    _tensor(Bbar_prev, "Bbar_prev", (b, H, R, N), io, dev)
+    _tensor(x_prev, "x_prev", (b, H, R, P), io, dev)
+    yshape = (T, H, P) if w_out is not None else (T, H, R, P)
+    y = torch.empty(yshape, dtype=io, device=dev) if y is None else _tensor(y, "y", yshape, io, dev)
+    if h_out is None:
+        h_out = torch.empty((b, H, N, P), dtype=f32, device=dev)
+    _tensor(h_out, "h_out", (b, H, N, P), f32, dev)
+    if phi_out is None:
+        phi_out = torch.empty((b, H, N // 2), dtype=f32, device=dev)
+    _tensor(phi_out, "phi_out", (b, H, N // 2), f32, dev)
+    _tensor(Bbar_last, "Bbar_last", (b, H, R, N), io, dev)
+    _tensor(x_last, "x_last", (b, H, R, P), io, dev)
+    dims = make_dims(b, T, H, P, N, R, chunk, _io_code(io), bcnorm, eps)
+    _check(lib.m3_layer_prefill_varlen(ctypes.byref(dims), _ptr(cu_seqlens), _ptr(x), _ptr(B), _ptr(C),
+                                       _ptr(dt), _ptr(theta), _ptr(normw_B), _ptr(normw_C), _ptr(bias_B),
+                                       _ptr(bias_C), _ptr(A), _ptr(lam), _ptr(w_out), _ptr(phi_in),
+                                       _ptr(h_in), _ptr(Bbar_prev), _ptr(x_prev), _ptr(y), _ptr(h_out),
+                                       _ptr(phi_out), _ptr(Bbar_last), _ptr(x_last), _stream(stream)))
+    return y, h_out, phi_out

@@ -208,3 +208,22 @@ def test_layer_decode_step_errors():
     q[17] = q[2]                                  # rotated B written over Bbar_prev
     assert call(_dims(seqlen=1), q) == m3scan.M3_E_ALIAS
     assert call(_dims(seqlen=1, rank=16), p) == m3scan.M3_E_UNSUPPORTED
+
+
+def test_layer_prefill_varlen_needs_offsets():
+    lib = m3scan.load()
+    # cu_seqlens, then the m3_layer_prefill pointers without the workspace
+    p = _ptrs(22)
+    for i in (6, 7, 8, 9, 12, 13, 14, 15, 16, 20, 21):
+        p[i] = None
+    call = lambda dims, q: lib.m3_layer_prefill_varlen(ctypes.byref(dims), *q, None)
+    q = list(p)
+    q[0] = None
+    assert call(_dims(chunk=32), q) == m3scan.M3_E_NULL
+    assert "cu_seqlens" in m3scan.last_error()
+    q = list(p)
+    q[0] = P(ALIGNED + 2)
+    assert call(_dims(chunk=32), q) == m3scan.M3_E_ALIGN
+    q = list(p)
+    q[0] = q[17]                                  # offsets inside y
+    assert call(_dims(chunk=32), q) == m3scan.M3_E_ALIAS

@@ -259,3 +259,120 @@ def test_mamba2_mode_parity(N, R, chunk):
                         bcnorm=False, mix=w.mix)
     assert rel_err(y2, ref2["y"]) <= TOL["bf16"]
     assert rel_err(h2, ref2["h_out"]) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------------------------
+# decode captured in a HIP graph (small-batch serving: launches, not bytes, bound the step)
+# ---------------------------------------------------------------------------------------------
+def test_layer_decode_graph_replays_match_eager():
+    """K fused decode steps captured once and replayed three times, with eager work and
+    synchronisation between replays, give exactly the eager steps' y, state, angle and rotated
+    B every time (and the eager steps match the oracle)."""
+    K = 8
+    w = inputs.WORKLOADS["decode_b128_r4"].with_(batch=1, nheads=8)
+    dinp = inputs.make_decode_inputs(w, 71, K, device=DEV)
+    toks, st = dinp["tokens"], dinp["state"]
+    b, H, R, N, P = w.batch, w.nheads, w.rank, w.dstate, w.headdim
+    bufs = [torch.empty_like(st["Bbar_prev"]) for _ in range(2)]
+    ys = torch.empty((K, b, H, P), dtype=torch.bfloat16, device=DEV)
+    h = torch.empty_like(st["h"])
+    phi = torch.empty_like(st["phi"])
+    x0 = st["x_prev"].clone()
+
+    def reset():
+        h.copy_(st["h"])
+        phi.copy_(st["phi"])
+        bufs[0].copy_(st["Bbar_prev"])
+
+    def steps():
+        xprev = x0
+        for s in range(K):
+            m3scan.m3_layer_decode_step(h, phi, bufs[s % 2], xprev, toks["x"][s], toks["B"][s], toks["C"][s],
+                                        toks["dt"][s], toks["theta"][s], dinp["A"], toks["lam"][s], None, None,
+                                        dinp["bias_B"], dinp["bias_C"], dinp["w_out"], y=ys[s],
+                                        Bbar_out=bufs[(s + 1) % 2])
+            xprev = toks["x"][s]
+
+    reset()
+    steps()
+    torch.cuda.synchronize()
+    eager = [ys.clone(), h.clone(), phi.clone(), bufs[K % 2].clone()]
+    # oracle on the eager run
+    consts = {k: dinp.get(k) for k in ("A", "bias_B", "bias_C", "w_out")}
+    state = {k: v.cpu() for k, v in st.items()}
+    rys = []
+    for s in range(K):
+        tok = {k: toks[k][s].cpu() for k in ("x", "B", "C", "dt", "lam", "theta")}
+        ry, state = oracle.decode_step(state, tok, {k: (v.cpu() if v is not None else None)
+                                                    for k, v in consts.items()}, mix=True)
+        rys.append(ry)
+    assert rel_err(eager[0], np.stack(rys, 0)) <= TOL["bf16"]
+    assert rel_err(eager[1], state["h"]) <= TOL["bf16"]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # one warm run on the capture stream
+        reset()
+        steps()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        steps()
+    for rep in range(3):
+        ys.fill_(float("nan"))
+        reset()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ys, eager[0]), rep
+        assert torch.equal(h, eager[1]), rep
+        assert torch.equal(phi, eager[2]), rep
+        assert torch.equal(bufs[K % 2], eager[3]), rep
+
+
+# ---------------------------------------------------------------------------------------------
+# packed variable-length batch (serving: prompts of mixed lengths, no padding)
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("R,chunk,io", [(1, 32, "bf16"), (4, 8, "bf16"), (2, 8, "f32")])
+def test_layer_prefill_varlen_matches_each_sequence(R, chunk, io):
+    lens = [100, 1, 0, 257, 33]
+    T = sum(lens)
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=DEV)
+    nseq, H, P, N = len(lens), 3, 64, 128
+    w = _wl(io, 1, T, H, P, N, R, chunk, mix=R > 1)
+    inp = inputs.make_prefill_inputs(w, seed=81, normw=True)
+    # per-sequence carries drawn like the decode state
+    carry = inputs.make_decode_state(w.with_(batch=nseq), inputs._gen(82, "cpu"), "cpu")
+    d = to_dev(inp, DEV)
+    dc = to_dev(carry, DEV)
+    packed = {k: d[k][0] for k in ("x", "B", "C", "dt", "lam", "theta")}
+    Blast = torch.full((nseq, H, R, N), 7.0, dtype=w.torch_io, device=DEV)
+    xlast = torch.full((nseq, H, R, P), 7.0, dtype=w.torch_io, device=DEV)
+    y, h, phi = m3scan.m3_layer_prefill_varlen(
+        cu, packed["x"], packed["B"], packed["C"], packed["dt"], packed["theta"], d["A"], packed["lam"],
+        d["normw_B"], d["normw_C"], d["bias_B"], d["bias_C"], d["w_out"] if w.mix else None,
+        phi_in=dc["phi"], h_in=dc["h"], Bbar_prev=dc["Bbar_prev"], x_prev=dc["x_prev"],
+        Bbar_last=Blast, x_last=xlast, chunk=chunk)
+    torch.cuda.synchronize()
+    off = 0
+    for s, n in enumerate(lens):
+        if n == 0:   # the carry passes through
+            assert torch.equal(h[s], dc["h"][s])
+            assert torch.equal(Blast[s], dc["Bbar_prev"][s])
+            assert torch.equal(xlast[s], dc["x_prev"][s])
+            assert angle_err(phi[s], carry["phi"][s].double().numpy()) <= 1e-6
+            continue
+        seq = {k: inp[k][:, off:off + n] for k in ("x", "B", "C", "dt", "lam", "theta")}
+        seq.update({k: inp[k] for k in ("A", "bias_B", "bias_C", "w_out", "normw_B", "normw_C")})
+        seq.update(h_in=carry["h"][s:s + 1], phi_in=carry["phi"][s:s + 1],
+                   Bbar_prev=carry["Bbar_prev"][s:s + 1], x_prev=carry["x_prev"][s:s + 1])
+        ref = oracle.layer(seq, bcnorm=True, mix=w.mix)
+        assert rel_err(y[off:off + n].unsqueeze(0), ref["y"]) <= TOL[io], s
+        assert rel_err(h[s:s + 1], ref["h_out"]) <= TOL[io], s
+        assert angle_err(phi[s:s + 1], ref["phi_out"]) <= (1e-3 if io == "bf16" else 1e-4), s
+        assert rel_err(Blast[s:s + 1], ref["Bbar_last"]) <= TOL[io], s
+        assert rel_err(xlast[s:s + 1], ref["x_last"]) == 0.0, s
+        off += n
