@@ -16,6 +16,10 @@ composes them.  Every function cites the passage it follows:
 * ``layer``         the two composed: the layer core from raw B and C to y and the final state.
 * ``decode_step``   the same composition for one new token, with the state, the angle and the
                     previous-token factors carried in.
+* ``scan_backward``, ``bcnorm_rope_backward``, ``layer_backward``
+                    exact gradients of the three forward functions above (reverse-mode through
+                    the same steps in reverse order; the pages define no backward pass, so the
+                    gradient of the forward definition is the definition followed).
 """
 from __future__ import annotations
 
@@ -53,6 +57,10 @@ def _bind(path: str):
     lib.m3o_bcnorm_rope.argtypes = [_I64] * 5 + [ctypes.c_int, ctypes.c_double] + [_D] * 12
     lib.m3o_scan.restype = None
     lib.m3o_scan.argtypes = [_I64] * 6 + [_D] * 12
+    lib.m3o_scan_backward.restype = None
+    lib.m3o_scan_backward.argtypes = [_I64] * 6 + [_D] * 22
+    lib.m3o_bcnorm_rope_backward.restype = None
+    lib.m3o_bcnorm_rope_backward.argtypes = [_I64] * 5 + [ctypes.c_int, ctypes.c_double] + [_D] * 21
     lib.m3o_num_threads.restype = ctypes.c_int
     lib.m3o_num_threads.argtypes = []
     return lib
@@ -177,6 +185,84 @@ def decode_step(state: dict, tok: dict, consts: dict, bcnorm=True, eps=1e-5, mix
     new_state = {"h": out["h_out"], "phi": out["phi_out"], "Bbar_prev": out["Bbar_last"],
                  "x_prev": out["x_last"]}
     return out["y"][:, 0], new_state
+
+
+def scan_backward(x, Bbar, Cbar, dt, A, lam, dy, w_out=None, h_in=None, Bbar_prev=None,
+                  x_prev=None, dh_out=None, lib=None):
+    """Gradients of ``scan`` for the cotangents dy (layout of y) and dh_out (layout of h_out,
+    None = 0).  Returns a dict: x, Bbar, Cbar, dt, lam (layouts of those inputs), A [H], w_out
+    [H, R, P] (None without mixing), h_in [b, H, N, P], and Bbar_prev, x_prev (None unless both
+    were given).  Gradients of per-head parameters are summed over the batch."""
+    x, Bbar, Cbar, dt, A, lam, dy = map(_f64, (x, Bbar, Cbar, dt, A, lam, dy))
+    nb, L, H, R, P = x.shape
+    N = Bbar.shape[-1]
+    w_out, h_in, Bbar_prev, x_prev, dh_out = map(_f64, (w_out, h_in, Bbar_prev, x_prev, dh_out))
+    assert dy.shape == ((nb, L, H, P) if w_out is not None else (nb, L, H, R, P))
+    assert dh_out is None or dh_out.shape == (nb, H, N, P)
+    carry = Bbar_prev is not None and x_prev is not None
+    g = {"x": np.empty_like(x), "Bbar": np.empty_like(Bbar), "Cbar": np.empty_like(Cbar),
+         "dt": np.empty_like(dt), "lam": np.empty_like(lam), "A": np.empty_like(A),
+         "w_out": np.empty_like(w_out) if w_out is not None else None,
+         "h_in": np.empty((nb, H, N, P)),
+         "Bbar_prev": np.empty((nb, H, R, N)) if carry else None,
+         "x_prev": np.empty((nb, H, R, P)) if carry else None}
+    (lib or _load()).m3o_scan_backward(
+        nb, L, H, R, P, N, _ptr(x), _ptr(Bbar), _ptr(Cbar), _ptr(dt), _ptr(A), _ptr(lam),
+        _ptr(w_out), _ptr(h_in), _ptr(Bbar_prev), _ptr(x_prev), _ptr(dy), _ptr(dh_out),
+        _ptr(g["x"]), _ptr(g["Bbar"]), _ptr(g["Cbar"]), _ptr(g["dt"]), _ptr(g["A"]),
+        _ptr(g["lam"]), _ptr(g["w_out"]), _ptr(g["h_in"]), _ptr(g["Bbar_prev"]),
+        _ptr(g["x_prev"]))
+    return g
+
+
+def bcnorm_rope_backward(B, C, dt, theta, dBbar, dCbar, normw_B=None, normw_C=None, bias_B=None,
+                         bias_C=None, phi_in=None, dphi_out=None, bcnorm=True, eps=1e-5, lib=None):
+    """Gradients of ``bcnorm_rope`` for the cotangents dBbar, dCbar (layout of Bbar) and dphi_out
+    ([b, H, N/2], None = 0).  Returns a dict: B, C, dt (the rotation's share only), theta,
+    phi_in, and normw_B, normw_C [H, N], bias_B, bias_C [H, R, N] summed over the batch (zero
+    for normw without BCNorm)."""
+    B, C, dt, theta, dBbar, dCbar = map(_f64, (B, C, dt, theta, dBbar, dCbar))
+    nb, L, H, R, N = B.shape
+    normw_B, normw_C, bias_B, bias_C, phi_in, dphi_out = map(
+        _f64, (normw_B, normw_C, bias_B, bias_C, phi_in, dphi_out))
+    assert dBbar.shape == B.shape and dCbar.shape == B.shape
+    assert dphi_out is None or dphi_out.shape == (nb, H, N // 2)
+    g = {"B": np.empty_like(B), "C": np.empty_like(C), "dt": np.empty_like(dt),
+         "theta": np.empty_like(theta), "phi_in": np.empty((nb, H, N // 2)),
+         "normw_B": np.empty((H, N)), "normw_C": np.empty((H, N)),
+         "bias_B": np.empty((H, R, N)), "bias_C": np.empty((H, R, N))}
+    (lib or _load()).m3o_bcnorm_rope_backward(
+        nb, L, H, R, N, int(bool(bcnorm)), float(eps), _ptr(B), _ptr(C), _ptr(dt), _ptr(theta),
+        _ptr(normw_B), _ptr(normw_C), _ptr(bias_B), _ptr(bias_C), _ptr(phi_in), _ptr(dBbar),
+        _ptr(dCbar), _ptr(dphi_out), _ptr(g["B"]), _ptr(g["C"]), _ptr(g["dt"]), _ptr(g["theta"]),
+        _ptr(g["phi_in"]), _ptr(g["normw_B"]), _ptr(g["normw_C"]), _ptr(g["bias_B"]),
+        _ptr(g["bias_C"]))
+    return g
+
+
+def layer_backward(inp: dict, dy, dh_out=None, dphi_out=None, bcnorm=True, eps=1e-5, mix=True,
+                   lib=None):
+    """Gradients of ``layer`` for the cotangents dy, dh_out and dphi_out (None = 0): the forward
+    rotation is recomputed, ``scan_backward`` gives the gradients of the rotated B and C, and
+    ``bcnorm_rope_backward`` carries them back to the raw inputs.  dt reaches both the scan and
+    the rotation angle, so its gradient is the sum of the two shares.  Returns a dict keyed by
+    input name (x, B, C, dt, A, lam, theta, normw_B, normw_C, bias_B, bias_C, w_out, phi_in, h_in,
+    Bbar_prev, x_prev)."""
+    g = inp.get
+    Bbar, Cbar, _ = bcnorm_rope(g("B"), g("C"), g("dt"), g("theta"), g("normw_B"), g("normw_C"),
+                                g("bias_B"), g("bias_C"), g("phi_in"), bcnorm=bcnorm, eps=eps,
+                                lib=lib)
+    gs = scan_backward(g("x"), Bbar, Cbar, g("dt"), g("A"), g("lam"), dy,
+                       g("w_out") if mix else None, g("h_in"), g("Bbar_prev"), g("x_prev"),
+                       dh_out, lib=lib)
+    gr = bcnorm_rope_backward(g("B"), g("C"), g("dt"), g("theta"), gs["Bbar"], gs["Cbar"],
+                              g("normw_B"), g("normw_C"), g("bias_B"), g("bias_C"), g("phi_in"),
+                              dphi_out, bcnorm=bcnorm, eps=eps, lib=lib)
+    return {"x": gs["x"], "B": gr["B"], "C": gr["C"], "dt": gs["dt"] + gr["dt"], "A": gs["A"],
+            "lam": gs["lam"], "theta": gr["theta"], "normw_B": gr["normw_B"],
+            "normw_C": gr["normw_C"], "bias_B": gr["bias_B"], "bias_C": gr["bias_C"],
+            "w_out": gs["w_out"], "phi_in": gr["phi_in"], "h_in": gs["h_in"],
+            "Bbar_prev": gs["Bbar_prev"], "x_prev": gs["x_prev"]}
 
 
 def build_variant(src_text: str, out_path: str):

@@ -410,6 +410,64 @@ def check_split_carry(lib=None):
     assert np.abs(o2["phi_out"] - full["phi_out"]).max() < 1e-12
 
 
+# ---------------------------------------------------------------------------------------------
+# 11. Gradients: central finite differences of the forward oracle.  The pages define no backward
+#     pass; the gradient of the forward definition is what the backward computes, and a central
+#     difference of the forward (O(h^2) truncation, h = 1e-5) reaches it by another route.
+# ---------------------------------------------------------------------------------------------
+def _grad_case(seed, R, mix, bcnorm, carry, weights):
+    c = _rand_case(seed, L=6, R=R, N=4, P=3, H=2, b=2, carry=carry)
+    r = _rng(seed + 1000)
+    H, N, P = 2, 4, 3
+    if weights:
+        c["normw_B"] = 1.0 + 0.3 * r.standard_normal((H, N))
+        c["normw_C"] = 1.0 + 0.3 * r.standard_normal((H, N))
+    c["bias_B"] = 0.5 * r.standard_normal((H, R, N))
+    c["bias_C"] = 0.5 * r.standard_normal((H, R, N))
+    if mix:
+        c["w_out"] = r.standard_normal((H, R, P))
+    return c
+
+
+def _objective(c, cot, mix, bcnorm, lib):
+    out = oracle.layer(c, bcnorm=bcnorm, mix=mix, lib=lib)
+    return (float(np.sum(cot["y"] * out["y"])) + float(np.sum(cot["h"] * out["h_out"]))
+            + float(np.sum(cot["phi"] * out["phi_out"])))
+
+
+def check_layer_gradients_fd(lib=None):
+    step = 1e-5
+    for seed, R, mix, bcnorm, carry, weights in [(91, 2, True, True, True, True),
+                                                 (92, 1, False, False, False, False),
+                                                 (93, 3, False, True, True, False)]:
+        c = _grad_case(seed, R, mix, bcnorm, carry, weights)
+        b, L, H, _, P = c["x"].shape
+        N = c["B"].shape[-1]
+        r = _rng(seed + 2000)
+        cot = {"y": r.standard_normal((b, L, H, P) if mix else (b, L, H, R, P)),
+               "h": r.standard_normal((b, H, N, P)), "phi": r.standard_normal((b, H, N // 2))}
+        grads = oracle.layer_backward(c, cot["y"], cot["h"], cot["phi"], bcnorm=bcnorm, mix=mix,
+                                      lib=lib)
+        for name, val in c.items():
+            if name == "w_out" and not mix:
+                continue
+            got = grads[name]
+            assert got is not None and got.shape == val.shape, name
+            fd = np.empty_like(val)
+            flat = val.reshape(-1)
+            for i in range(flat.size):
+                keep = flat[i]
+                flat[i] = keep + step
+                fp = _objective(c, cot, mix, bcnorm, lib)
+                flat[i] = keep - step
+                fm = _objective(c, cot, mix, bcnorm, lib)
+                flat[i] = keep
+                fd.reshape(-1)[i] = (fp - fm) / (2 * step)
+            scale = max(1.0, float(np.abs(fd).max()))
+            err = float(np.abs(got - fd).max())
+            assert err <= 1e-6 * scale, (seed, name, err, scale)
+
+
 ALL_CHECKS = [
     check_masked_matrix_form,
     check_lambda_one_is_euler,
@@ -423,4 +481,5 @@ ALL_CHECKS = [
     check_mimo_is_sum_of_siso,
     check_bcnorm_invariants,
     check_split_carry,
+    check_layer_gradients_fd,
 ]

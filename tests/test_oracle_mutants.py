@@ -11,6 +11,8 @@ import pytest
 import oracle
 import pins
 
+GRAD_MARKER = "/*\n * Gradients of m3o_scan"
+
 # (name, text in m3_oracle.c, replacement)
 MUTANTS = [
     ("beta_without_decay", "const double beta = (1.0 - lm) * d * alpha;",
@@ -35,14 +37,40 @@ MUTANTS = [
     ("rank_sum_dropped", "u[n * P + p] += bt[n] * xt[p];", "u[n * P + p] = bt[n] * xt[p];"),
     ("pair_swapped_in_rotation", "out[2 * k + 1] = -s * v[2 * k] + c * v[2 * k + 1];",
      "out[2 * k + 1] = -s * v[2 * k + 1] + c * v[2 * k];"),
+    # gradients
+    ("grad_beta_carry_dropped", "dU[i] = gamma * dg[i] + dcarry[i];", "dU[i] = gamma * dg[i];"),
+    ("grad_alpha_uses_current_state", "dal += dg[i] * gp[i];", "dal += dg[i] * gt[i];"),
+    ("grad_A_beta_term_dropped",
+     "dA_part[bh] += dal * d * alpha + dbe * (1.0 - lm) * d * d * alpha;",
+     "dA_part[bh] += dal * d * alpha;"),
+    ("grad_mix_weight_dropped", "dw_part[(bh * R + r) * P + p] += acc * dyp;", "(void)acc;"),
+    ("grad_angle_sign", "dphi[k] += dout[2 * k] * o1 - dout[2 * k + 1] * o0;",
+     "dphi[k] += dout[2 * k + 1] * o0 - dout[2 * k] * o1;"),
+    ("grad_rotation_not_inverted", "dvb[2 * k] = c * dout[2 * k] - s * dout[2 * k + 1];",
+     "dvb[2 * k] = c * dout[2 * k] + s * dout[2 * k + 1];"),
+    ("grad_rms_projection_dropped",
+     "dsrc[n] = wn * inv * dvb[n] - inv * inv * inv * v[n] / (double)N * sdot;",
+     "dsrc[n] = wn * inv * dvb[n];"),
+    ("grad_angle_suffix_skips_current_step",
+     "S[k] += dphi[k];\n                dtheta[row * K + k] = S[k] * dt[row];",
+     "dtheta[row * K + k] = S[k] * dt[row];\n                S[k] += dphi[k];"),
 ]
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(tmp_path, name, old, new):
     src = oracle.source_text()
-    assert src.count(old) == 1, "mutation site not found exactly once: " + name
-    lib = oracle.build_variant(src.replace(old, new), str(tmp_path / ("m_" + name + ".so")))
+    # forward mutants edit the forward functions, gradient mutants the backward ones (the
+    # backward recomputes the forward, so some statements appear in both)
+    cut = src.index(GRAD_MARKER)
+    fwd, bwd = src[:cut], src[cut:]
+    if name.startswith("grad_"):
+        assert bwd.count(old) == 1, "mutation site not found exactly once: " + name
+        src = fwd + bwd.replace(old, new)
+    else:
+        assert fwd.count(old) == 1, "mutation site not found exactly once: " + name
+        src = fwd.replace(old, new) + bwd
+    lib = oracle.build_variant(src, str(tmp_path / ("m_" + name + ".so")))
     failed = []
     for check in pins.ALL_CHECKS:
         try:
