@@ -19,6 +19,8 @@
  *   m3_layer_prefill the two above in one pass (rotation applied while staging each chunk)
  *   m3_decode_step   one new token for a batch of resident states
  *   m3_layer_decode_step  the rotation and one decode step in one launch
+ *   m3_layer_backward     gradients of m3_layer_prefill (with m3_layer_chunk_states, the
+ *                         forward pass that saves what the backward pass reads)
  *
  * Frame of the state.  The state the library keeps, returns and accepts is the rotated frame
  * g_t = R(Phi_t)^T h_t.  Together with the angle Phi_t (returned by m3_bcnorm_rope) it fully
@@ -287,6 +289,87 @@ m3_status m3_layer_decode_step(const m3_dims* dims, float* h, float* phi, const 
                                const float* normw_C, const float* bias_B, const float* bias_C,
                                const float* A, const void* lam, const float* w_out, void* y,
                                void* Bbar_out, hipStream_t stream);
+
+/*
+ * m3_layer_backward_chunk -- time steps per chunk of the backward pass for these dims (the
+ * chunk of the states m3_layer_chunk_states saves), or 0 when no backward kernel covers them.
+ * Chunks are 64 rows (step, rank) for bf16 io and 32 rows for fp32 io at P = 64, 16 rows at
+ * P = 16; steps per chunk = rows / R.
+ */
+int64_t m3_layer_backward_chunk(const m3_dims* dims);
+
+/*
+ * m3_layer_chunk_states -- the state and angle at the entry of every backward chunk.
+ *
+ * Defined by: the recurrence of m3_prefill on the rotated B of m3_bcnorm_rope (aipaper.cc
+ * summary, section 4.1 Proposition 1, section 4.2 Proposition 3, section 4.3), with the chunk
+ * Q = m3_layer_backward_chunk(dims).  For chunk c (steps cQ .. cQ + Q - 1), per (b, h):
+ *
+ *   states[b, h, c] = (G_{cQ-1})^T,  G_{t} = g_t + c_{t+1} Bbar_t^T x_t  (the shifted state)
+ *   phis[b, h, c]   = Phi_{cQ-1} (reduced to [-pi, pi]),  Phi_{-1} = phi_in
+ *
+ * where c_{t} = (1 - lambda_t) dt_t, g_t is m3_prefill's state (g_{-1} = h_in) and the shifted
+ * state is the one the chunked form carries between chunks (its G_{-1} = h_in + c_0 u_{-1}).
+ * Arguments are those of m3_layer_prefill with the same meaning (only the B side is used), plus:
+ *   states  [b, H, nchunk, P, N] io   entry states, transposed              required
+ *   phis    [b, H, nchunk, N/2] f32   entry angles                         required
+ * with nchunk = ceil(L / Q).  Neither output may overlap an input or the other.  Shapes: (N, P)
+ * in {(16,16), (64,64), (128,64)}, R in {1, 2, 4}; dense batches only.  m3_layer_backward calls
+ * this itself; it is exported for checkpointing and for tests.
+ */
+m3_status m3_layer_chunk_states(const m3_dims* dims, const void* x, const void* B, const void* dt,
+                                const void* theta, const float* normw_B, const float* bias_B,
+                                const float* A, const void* lam, const float* phi_in,
+                                const float* h_in, const void* Bbar_prev, const void* x_prev,
+                                void* states, float* phis, hipStream_t stream);
+
+/* Bytes of device workspace m3_layer_backward needs for these dims (0 when unsupported). */
+size_t m3_layer_backward_workspace_bytes(const m3_dims* dims);
+
+/*
+ * m3_layer_backward -- gradients of m3_layer_prefill with respect to all of its inputs.
+ *
+ * Defined by: the derivative of the computation m3_layer_prefill defines (the pages give the
+ * forward only: aipaper.cc summary, sections 4.1-4.3; papernotes.org, key design 4; the
+ * cumulative angle of section 4.2 Proposition 3).  Given the cotangents dy (of y), dh_out (of
+ * h_out) and dphi_out (of phi_out), it returns, up to rounding, the exact gradient of
+ *   <dy, y> + <dh_out, h_out> + <dphi_out, phi_out>
+ * with respect to every input, computed by the reverse chunked pass (the gradient of each
+ * chunk's matrix products, the state cotangent carried from the last chunk to the first, the
+ * rotation and BCNorm undone per row, the angle cotangent summed from the end).  Arguments:
+ *   x .. x_prev   the forward inputs of m3_layer_prefill, same shapes and optionality
+ *   dy            [b, L, H, P] io with w_out, else [b, L, H, R, P] io             required
+ *   dh_out        [b, H, N, P] f32; NULL = 0                                      optional
+ *   dphi_out      [b, H, N/2] f32; NULL = 0                                       optional
+ *   dx            [b, L, H, R, P] io                                              required
+ *   dB, dC        [b, L, H, R, N] io   (of the raw B and C)                       required
+ *   ddt, dlam     [b, L, H] io   (ddt includes the angle's share)                 required
+ *   dtheta        [b, L, H, N/2] io                                               required
+ *   dA            [H] f32   summed over the batch                                 required
+ *   dnormw_B, dnormw_C [H, N] f32   summed over the batch; 0 without M3_BCNORM   optional
+ *   dbias_B, dbias_C   [H, R, N] f32 summed over the batch                        optional
+ *   dw_out        [H, R, P] f32 summed over the batch (only with w_out)           optional
+ *   dphi_in       [b, H, N/2] f32                                                 required
+ *   dh_in         [b, H, N, P] f32                                                required
+ *   dBbar_prev    [b, H, R, N] io; 0 when Bbar_prev or x_prev is NULL             optional
+ *   dx_prev       [b, H, R, P] io; 0 when Bbar_prev or x_prev is NULL             optional
+ *   workspace     m3_layer_backward_workspace_bytes(dims) bytes, 16-byte aligned  required
+ * Gradients of per-head parameters are reduced over the batch in a fixed order (results do not
+ * depend on scheduling).  Outputs may not overlap inputs, the workspace or each other.  dims->chunk
+ * must be 0 or m3_layer_backward_chunk(dims); dense batches only.  Shapes: (N, P) in {(16,16),
+ * (64,64), (128,64)}, R in {1, 2, 4}; others return M3_E_UNSUPPORTED.
+ */
+m3_status m3_layer_backward(const m3_dims* dims, const void* x, const void* B, const void* C,
+                            const void* dt, const void* theta, const float* normw_B,
+                            const float* normw_C, const float* bias_B, const float* bias_C,
+                            const float* A, const void* lam, const float* w_out,
+                            const float* phi_in, const float* h_in, const void* Bbar_prev,
+                            const void* x_prev, const void* dy, const float* dh_out,
+                            const float* dphi_out, void* dx, void* dB, void* dC, void* ddt,
+                            void* dtheta, float* dA, void* dlam, float* dnormw_B, float* dnormw_C,
+                            float* dbias_B, float* dbias_C, float* dw_out, float* dphi_in,
+                            float* dh_in, void* dBbar_prev, void* dx_prev, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

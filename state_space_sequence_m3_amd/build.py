@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build", "m3scan")
 LIB = os.path.join(PKG, "libm3scan.so")
-SOURCES = ["api.hip", "bcnorm_rope.hip", "prefill.hip", "decode.hip"]
+SOURCES = ["api.hip", "bcnorm_rope.hip", "prefill.hip", "decode.hip", "backward.hip"]
 ARCH = "gfx950"
 
 

@@ -224,6 +224,36 @@ m3_status layer_prefill(const m3_dims* d, bool packed, const int32_t* cu_seqlens
     return launched(m3::launch_layer(a, d->io == M3_BF16, stream), fn);
 }
 
+
+// backward pass: chunk and workspace layout (states, angles, per-(b, h) partial sums, each
+// starting on a 256-byte boundary)
+struct BwdLayout {
+    int64_t Q = 0, nchunk = 0;
+    int rec = 0;
+    size_t st_bytes = 0, phi_off = 0, phi_bytes = 0, part_off = 0, part_bytes = 0, total = 0;
+};
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+bool bwd_layout(const m3_dims* d, BwdLayout* o) {
+    if (!d || (d->io != M3_F32 && d->io != M3_BF16) || d->rank < 1 || d->batch < 0 || d->seqlen < 0 ||
+        d->nheads < 0)
+        return false;
+    if (!m3::backward_supported((int)d->dstate, (int)d->headdim, (int)d->rank)) return false;
+    const int64_t rows = m3::backward_chunk_rows((int)d->headdim, d->io == M3_BF16);
+    o->Q = rows / d->rank;
+    o->nchunk = (d->seqlen + o->Q - 1) / o->Q;
+    const int64_t b = d->batch, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
+    o->rec = (int)(1 + R * P + 2 * N + 2 * R * N);
+    o->st_bytes = (size_t)(b * H * o->nchunk * P * N) * io_size(d);
+    o->phi_off = round256(o->st_bytes);
+    o->phi_bytes = (size_t)(b * H * o->nchunk * (N / 2)) * 4;
+    o->part_off = o->phi_off + round256(o->phi_bytes);
+    o->part_bytes = (size_t)(b * H * o->rec) * 4;
+    o->total = o->part_off + round256(o->part_bytes);
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -486,6 +516,150 @@ m3_status m3_layer_decode_step(const m3_dims* d, float* h, float* phi, const voi
     a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;
     a.eps = d->eps;
     return launched(m3::launch_layer_decode(a, d->io == M3_BF16, stream), "m3_layer_decode_step");
+}
+
+int64_t m3_layer_backward_chunk(const m3_dims* d) {
+    BwdLayout lay;
+    return bwd_layout(d, &lay) ? lay.Q : 0;
+}
+
+size_t m3_layer_backward_workspace_bytes(const m3_dims* d) {
+    BwdLayout lay;
+    return bwd_layout(d, &lay) ? lay.total : 0;
+}
+
+m3_status m3_layer_chunk_states(const m3_dims* d, const void* x, const void* B, const void* dt, const void* theta,
+                                const float* normw_B, const float* bias_B, const float* A, const void* lam,
+                                const float* phi_in, const float* h_in, const void* Bbar_prev, const void* x_prev,
+                                void* states, float* phis, hipStream_t stream) {
+    m3_status s = check_common_dims(d);
+    if (s != M3_OK) return s;
+    const int64_t b = d->batch, L = d->seqlen, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
+    BwdLayout lay;
+    if (!bwd_layout(d, &lay))
+        return fail(M3_E_UNSUPPORTED,
+                    "m3_layer_chunk_states: no kernel for N = %lld, P = %lld, R = %lld (supported: (N,P) in "
+                    "{(16,16),(64,64),(128,64)}, R in {1,2,4})", (long long)N, (long long)P, (long long)R);
+    const size_t es = io_size(d);
+    const size_t nX = (size_t)(b * L * H * R * P) * es, nBC = (size_t)(b * L * H * R * N) * es;
+    const size_t nStep = (size_t)(b * L * H) * es, nA = (size_t)H * 4;
+    const size_t nTh = (size_t)(b * L * H * (N / 2)) * es, nPhi = (size_t)(b * H * (N / 2)) * 4;
+    const size_t nH = (size_t)(b * H * N * P) * 4, nBp = (size_t)(b * H * R * N) * es;
+    const size_t nXp = (size_t)(b * H * R * P) * es, nW = (size_t)(H * N) * 4, nBias = (size_t)(H * R * N) * 4;
+    const Buf req[] = {{x, nX, "x"}, {B, nBC, "B"}, {dt, nStep, "dt"}, {theta, nTh, "theta"}, {A, nA, "A"},
+                       {lam, nStep, "lam"}, {states, lay.st_bytes, "states"}, {phis, lay.phi_bytes, "phis"}};
+    if ((s = check_required(req, 8)) != M3_OK) return s;
+    if (lay.Q * H * R * (N > P ? N : P) * (int64_t)es >= ((int64_t)1 << 31))
+        return fail(M3_E_DIMS, "m3_layer_chunk_states: nheads * rank = %lld is too large for one chunk",
+                    (long long)(H * R));
+    const Buf a16[] = {{x, 1, "x"}, {B, 1, "B"}, {theta, 1, "theta"}, {states, 1, "states"}};
+    if ((s = check_align(a16, 4, 16)) != M3_OK) return s;
+    const Buf aes[] = {{dt, 1, "dt"}, {lam, 1, "lam"}, {Bbar_prev, 1, "Bbar_prev"}, {x_prev, 1, "x_prev"}};
+    if ((s = check_align(aes, 4, es)) != M3_OK) return s;
+    const Buf a4[] = {{A, 1, "A"}, {normw_B, 1, "normw_B"}, {bias_B, 1, "bias_B"}, {phi_in, 1, "phi_in"},
+                      {h_in, 1, "h_in"}, {phis, 1, "phis"}};
+    if ((s = check_align(a4, 6, 4)) != M3_OK) return s;
+    const Buf ins[] = {{x, nX, "x"}, {B, nBC, "B"}, {dt, nStep, "dt"}, {theta, nTh, "theta"}, {A, nA, "A"},
+                       {lam, nStep, "lam"}, {normw_B, nW, "normw_B"}, {bias_B, nBias, "bias_B"},
+                       {phi_in, nPhi, "phi_in"}, {h_in, nH, "h_in"}, {Bbar_prev, nBp, "Bbar_prev"},
+                       {x_prev, nXp, "x_prev"}};
+    const Buf outs[] = {{states, lay.st_bytes, "states"}, {phis, lay.phi_bytes, "phis"}};
+    if ((s = check_alias(outs, 2, ins, 12)) != M3_OK) return s;
+    if ((s = check_device()) != M3_OK) return s;
+    if (b == 0 || H == 0 || L == 0) return M3_OK;
+    m3::BackwardArgs a = {};
+    a.x = x; a.B = B; a.dt = dt; a.theta = theta; a.A = A; a.lam = lam; a.normw_B = normw_B; a.bias_B = bias_B;
+    a.phi_in = phi_in; a.h_in = h_in; a.Bbar_prev = Bbar_prev; a.x_prev = x_prev;
+    a.ws_states = states; a.ws_phi = phis;
+    a.b = b; a.L = L; a.H = (int)H; a.N = (int)N; a.P = (int)P; a.R = (int)R;
+    a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;
+    a.eps = d->eps;
+    return launched(m3::launch_chunk_states(a, d->io == M3_BF16, stream), "m3_layer_chunk_states");
+}
+
+m3_status m3_layer_backward(const m3_dims* d, const void* x, const void* B, const void* C, const void* dt,
+                            const void* theta, const float* normw_B, const float* normw_C, const float* bias_B,
+                            const float* bias_C, const float* A, const void* lam, const float* w_out,
+                            const float* phi_in, const float* h_in, const void* Bbar_prev, const void* x_prev,
+                            const void* dy, const float* dh_out, const float* dphi_out, void* dx, void* dB,
+                            void* dC, void* ddt, void* dtheta, float* dA, void* dlam, float* dnormw_B,
+                            float* dnormw_C, float* dbias_B, float* dbias_C, float* dw_out, float* dphi_in,
+                            float* dh_in, void* dBbar_prev, void* dx_prev, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    m3_status s = check_common_dims(d);
+    if (s != M3_OK) return s;
+    const int64_t b = d->batch, L = d->seqlen, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
+    BwdLayout lay;
+    if (!bwd_layout(d, &lay))
+        return fail(M3_E_UNSUPPORTED,
+                    "m3_layer_backward: no kernel for N = %lld, P = %lld, R = %lld (supported: (N,P) in "
+                    "{(16,16),(64,64),(128,64)}, R in {1,2,4})", (long long)N, (long long)P, (long long)R);
+    if (d->chunk != 0 && d->chunk != lay.Q)
+        return fail(M3_E_UNSUPPORTED, "m3_layer_backward: chunk must be 0 or %lld for these dims",
+                    (long long)lay.Q);
+    const size_t es = io_size(d);
+    const size_t nX = (size_t)(b * L * H * R * P) * es, nBC = (size_t)(b * L * H * R * N) * es;
+    const size_t nStep = (size_t)(b * L * H) * es, nA = (size_t)H * 4;
+    const size_t nTh = (size_t)(b * L * H * (N / 2)) * es, nPhi = (size_t)(b * H * (N / 2)) * 4;
+    const size_t nY = (size_t)(b * L * H * (w_out ? 1 : R) * P) * es, nH = (size_t)(b * H * N * P) * 4;
+    const size_t nBp = (size_t)(b * H * R * N) * es, nXp = (size_t)(b * H * R * P) * es;
+    const size_t nWo = (size_t)(H * R * P) * 4, nW = (size_t)(H * N) * 4, nBias = (size_t)(H * R * N) * 4;
+    const Buf req[] = {{x, nX, "x"}, {B, nBC, "B"}, {C, nBC, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
+                       {A, nA, "A"}, {lam, nStep, "lam"}, {dy, nY, "dy"}, {dx, nX, "dx"}, {dB, nBC, "dB"},
+                       {dC, nBC, "dC"}, {ddt, nStep, "ddt"}, {dtheta, nTh, "dtheta"}, {dA, nA, "dA"},
+                       {dlam, nStep, "dlam"}, {dphi_in, nPhi, "dphi_in"}, {dh_in, nH, "dh_in"}};
+    if ((s = check_required(req, 17)) != M3_OK) return s;
+    if (!workspace && lay.total > 0) return fail(M3_E_WORKSPACE, "m3_layer_backward: workspace is NULL");
+    if (workspace_bytes < lay.total)
+        return fail(M3_E_WORKSPACE, "m3_layer_backward: workspace has %zu bytes, needs %zu", workspace_bytes,
+                    lay.total);
+    if (lay.Q * H * R * (N > P ? N : P) * (int64_t)es >= ((int64_t)1 << 31))
+        return fail(M3_E_DIMS, "m3_layer_backward: nheads * rank = %lld is too large for one chunk",
+                    (long long)(H * R));
+    const Buf a16[] = {{x, 1, "x"}, {B, 1, "B"}, {C, 1, "C"}, {theta, 1, "theta"}, {dy, 1, "dy"},
+                       {dx, 1, "dx"}, {dB, 1, "dB"}, {dC, 1, "dC"}, {dtheta, 1, "dtheta"},
+                       {workspace, 1, "workspace"}};
+    if ((s = check_align(a16, 10, 16)) != M3_OK) return s;
+    const Buf aes[] = {{dt, 1, "dt"}, {lam, 1, "lam"}, {Bbar_prev, 1, "Bbar_prev"}, {x_prev, 1, "x_prev"},
+                       {ddt, 1, "ddt"}, {dlam, 1, "dlam"}, {dBbar_prev, 1, "dBbar_prev"}, {dx_prev, 1, "dx_prev"}};
+    if ((s = check_align(aes, 8, es)) != M3_OK) return s;
+    const Buf a4[] = {{A, 1, "A"}, {w_out, 1, "w_out"}, {normw_B, 1, "normw_B"}, {normw_C, 1, "normw_C"},
+                      {bias_B, 1, "bias_B"}, {bias_C, 1, "bias_C"}, {phi_in, 1, "phi_in"}, {h_in, 1, "h_in"},
+                      {dh_out, 1, "dh_out"}, {dphi_out, 1, "dphi_out"}, {dA, 1, "dA"}, {dnormw_B, 1, "dnormw_B"},
+                      {dnormw_C, 1, "dnormw_C"}, {dbias_B, 1, "dbias_B"}, {dbias_C, 1, "dbias_C"},
+                      {dw_out, 1, "dw_out"}, {dphi_in, 1, "dphi_in"}, {dh_in, 1, "dh_in"}};
+    if ((s = check_align(a4, 18, 4)) != M3_OK) return s;
+    const Buf ins[] = {{x, nX, "x"}, {B, nBC, "B"}, {C, nBC, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
+                       {A, nA, "A"}, {lam, nStep, "lam"}, {w_out, nWo, "w_out"}, {normw_B, nW, "normw_B"},
+                       {normw_C, nW, "normw_C"}, {bias_B, nBias, "bias_B"}, {bias_C, nBias, "bias_C"},
+                       {phi_in, nPhi, "phi_in"}, {h_in, nH, "h_in"}, {Bbar_prev, nBp, "Bbar_prev"},
+                       {x_prev, nXp, "x_prev"}, {dy, nY, "dy"}, {dh_out, nH, "dh_out"},
+                       {dphi_out, nPhi, "dphi_out"}, {workspace, lay.total, "workspace"}};
+    const Buf outs[] = {{dx, nX, "dx"}, {dB, nBC, "dB"}, {dC, nBC, "dC"}, {ddt, nStep, "ddt"},
+                        {dtheta, nTh, "dtheta"}, {dA, nA, "dA"}, {dlam, nStep, "dlam"}, {dnormw_B, nW, "dnormw_B"},
+                        {dnormw_C, nW, "dnormw_C"}, {dbias_B, nBias, "dbias_B"}, {dbias_C, nBias, "dbias_C"},
+                        {dw_out, w_out ? nWo : 0, "dw_out"}, {dphi_in, nPhi, "dphi_in"}, {dh_in, nH, "dh_in"},
+                        {dBbar_prev, nBp, "dBbar_prev"}, {dx_prev, nXp, "dx_prev"}};
+    if ((s = check_alias(outs, 16, ins, 20)) != M3_OK) return s;
+    if ((s = check_device()) != M3_OK) return s;
+    if (b == 0 || H == 0) return M3_OK;
+    m3::BackwardArgs a = {};
+    a.x = x; a.B = B; a.C = C; a.dt = dt; a.theta = theta; a.A = A; a.lam = lam;
+    a.normw_B = normw_B; a.normw_C = normw_C; a.bias_B = bias_B; a.bias_C = bias_C; a.w_out = w_out;
+    a.phi_in = phi_in; a.h_in = h_in; a.Bbar_prev = Bbar_prev; a.x_prev = x_prev;
+    a.dy = dy; a.dh_out = dh_out; a.dphi_out = dphi_out;
+    a.dx = dx; a.dB = dB; a.dC = dC; a.ddt = ddt; a.dtheta = dtheta; a.dlam = dlam; a.dA = dA;
+    a.dnormw_B = dnormw_B; a.dnormw_C = dnormw_C; a.dbias_B = dbias_B; a.dbias_C = dbias_C;
+    a.dw_out = w_out ? dw_out : nullptr;
+    a.dphi_in = dphi_in; a.dh_in = dh_in; a.dBbar_prev = dBbar_prev; a.dx_prev = dx_prev;
+    a.ws_states = workspace;
+    a.ws_phi = (float*)((char*)workspace + lay.phi_off);
+    a.ws_part = (float*)((char*)workspace + lay.part_off);
+    a.rec = lay.rec;
+    a.b = b; a.L = L; a.H = (int)H; a.N = (int)N; a.P = (int)P; a.R = (int)R;
+    a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;
+    a.eps = d->eps;
+    return launched(m3::launch_backward(a, d->io == M3_BF16, stream), "m3_layer_backward");
 }
 
 }  // extern "C"

@@ -92,6 +92,63 @@ struct PrefillArgs {
     int64_t T = 0;
 };
 
+// Gradients of the fused layer core (m3_layer_chunk_states / m3_layer_backward).  B and C are raw
+// (before BCNorm and rotation), as m3_layer_prefill takes them.
+struct BackwardArgs {
+    const void* x;
+    const void* B;
+    const void* C;
+    const void* dt;
+    const void* theta;
+    const float* A;
+    const void* lam;
+    const float* normw_B;
+    const float* normw_C;
+    const float* bias_B;
+    const float* bias_C;
+    const float* w_out;
+    const float* phi_in;
+    const float* h_in;
+    const void* Bbar_prev;
+    const void* x_prev;
+    // cotangents of y, h_out, phi_out (the last two nullable: zero)
+    const void* dy;
+    const float* dh_out;
+    const float* dphi_out;
+    // gradients
+    void* dx;
+    void* dB;
+    void* dC;
+    void* ddt;
+    void* dtheta;
+    void* dlam;
+    float* dA;
+    float* dnormw_B;
+    float* dnormw_C;
+    float* dbias_B;
+    float* dbias_C;
+    float* dw_out;
+    float* dphi_in;
+    float* dh_in;
+    void* dBbar_prev;
+    void* dx_prev;
+    // workspace: chunk-entry states [b, H, nchunk, P, N] (io type), entry angles
+    // [b, H, nchunk, N/2], per-(b, h) partial sums [b, H, rec]
+    void* ws_states;
+    float* ws_phi;
+    float* ws_part;
+    int rec;              // 1 + R P + 2 N + 2 R N
+    int64_t b, L;
+    int H, N, P, R;
+    int bcnorm;
+    float eps;
+};
+
+bool backward_supported(int N, int P, int R);
+int backward_chunk_rows(int P, bool bf16_io);   // rows (step, rank) per chunk; steps = rows / R
+hipError_t launch_chunk_states(const BackwardArgs& a, bool bf16_io, hipStream_t s);
+hipError_t launch_backward(const BackwardArgs& a, bool bf16_io, hipStream_t s);
+
 bool decode_supported(int N, int P, int R);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16_io, hipStream_t s);
 hipError_t launch_layer_decode(const DecodeArgs& a, bool bf16_io, hipStream_t s);

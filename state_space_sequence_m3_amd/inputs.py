@@ -161,6 +161,18 @@ def make_prefill_inputs(w: Workload, seed: int, device="cpu", normw: bool = Fals
     return out
 
 
+def make_cotangents(w: Workload, seed: int, device="cpu") -> dict:
+    """Seeded cotangents for a backward call of workload ``w``: dy with y's shape ([b, L, H, P]
+    with output mixing, else [b, L, H, R, P]) in the io dtype, dh_out [b, H, N, P] and
+    dphi_out [b, H, N/2] in fp32, all ~ N(0, 1)."""
+    g = _gen(seed, device)
+    b, L, H, R, N, P = w.batch, w.seqlen, w.nheads, w.rank, w.dstate, w.headdim
+    yshape = (b, L, H, P) if w.mix else (b, L, H, R, P)
+    return {"dy": _normal(g, yshape, device).to(w.torch_io),
+            "dh_out": _normal(g, (b, H, N, P), device),
+            "dphi_out": _normal(g, (b, H, N // 2), device)}
+
+
 def make_decode_inputs(w: Workload, seed: int, steps: int, device="cpu",
                        normw: bool = False) -> dict:
     """Constants, a starting state and ``steps`` tokens laid out step-major ([steps, b, H, ...])."""

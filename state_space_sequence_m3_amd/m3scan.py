@@ -28,7 +28,8 @@ M3_BCNORM = 1
 EXPORTED = ["m3_bcnorm_rope", "m3_bcnorm_rope_workspace_bytes", "m3_prefill",
             "m3_prefill_workspace_bytes", "m3_layer_prefill", "m3_layer_prefill_varlen",
             "m3_decode_step",
-            "m3_layer_decode_step", "m3_last_error", "m3_version"]
+            "m3_layer_decode_step", "m3_layer_backward_chunk", "m3_layer_chunk_states",
+            "m3_layer_backward_workspace_bytes", "m3_layer_backward", "m3_last_error", "m3_version"]
 
 
 class M3Dims(ctypes.Structure):
@@ -76,6 +77,14 @@ def load(path: str = LIB_PATH):
             lib.m3_layer_decode_step.argtypes = [_DIMS] + [_P] * 18 + [_P]
             lib.m3_decode_step.restype = ctypes.c_int
             lib.m3_decode_step.argtypes = [_DIMS] + [_P] * 11 + [_P]
+            lib.m3_layer_backward_chunk.restype = ctypes.c_int64
+            lib.m3_layer_backward_chunk.argtypes = [_DIMS]
+            lib.m3_layer_chunk_states.restype = ctypes.c_int
+            lib.m3_layer_chunk_states.argtypes = [_DIMS] + [_P] * 14 + [_P]
+            lib.m3_layer_backward_workspace_bytes.restype = ctypes.c_size_t
+            lib.m3_layer_backward_workspace_bytes.argtypes = [_DIMS]
+            lib.m3_layer_backward.restype = ctypes.c_int
+            lib.m3_layer_backward.argtypes = [_DIMS] + [_P] * 36 + [ctypes.c_size_t, _P]
             lib.m3_last_error.restype = ctypes.c_char_p
             lib.m3_last_error.argtypes = []
             lib.m3_version.restype = ctypes.c_char_p
@@ -367,3 +376,121 @@ def m3_layer_prefill_varlen(cu_seqlens, x, B, C, dt, theta, A, lam, normw_B=None
                                        _ptr(h_in), _ptr(Bbar_prev), _ptr(x_prev), _ptr(y), _ptr(h_out),
                                        _ptr(phi_out), _ptr(Bbar_last), _ptr(x_last), _stream(stream)))
     return y, h_out, phi_out
+
+
+def layer_backward_chunk(dims: M3Dims) -> int:
+    """Time steps per chunk of the backward pass (0 when unsupported)."""
+    return int(load().m3_layer_backward_chunk(ctypes.byref(dims)))
+
+
+def layer_backward_workspace_bytes(dims: M3Dims) -> int:
+    return int(load().m3_layer_backward_workspace_bytes(ctypes.byref(dims)))
+
+
+def m3_layer_chunk_states(x, B, dt, theta, A, lam, normw_B=None, bias_B=None, phi_in=None, h_in=None,
+                          Bbar_prev=None, x_prev=None, states=None, phis=None, bcnorm=True, eps=1e-5,
+                          stream=None):
+    """Entry state and angle of every backward chunk.  Returns (states [b, H, nchunk, P, N] io,
+    phis [b, H, nchunk, N/2] f32) and the chunk length in steps."""
+    lib = load()
+    b, L, H, R, P = x.shape
+    N = B.shape[-1]
+    dev, io = x.device, x.dtype
+    f32 = torch.float32
+    _tensor(B, "B", (b, L, H, R, N), io, dev)
+    _tensor(dt, "dt", (b, L, H), io, dev)
+    _tensor(theta, "theta", (b, L, H, N // 2), io, dev)
+    _tensor(lam, "lam", (b, L, H), io, dev)
+    _tensor(A, "A", (H,), f32, dev)
+    _tensor(normw_B, "normw_B", (H, N), f32, dev)
+    _tensor(bias_B, "bias_B", (H, R, N), f32, dev)
+    _tensor(phi_in, "phi_in", (b, H, N // 2), f32, dev)
+    _tensor(h_in, "h_in", (b, H, N, P), f32, dev)
+    _tensor(Bbar_prev, "Bbar_prev", (b, H, R, N), io, dev)
+    _tensor(x_prev, "x_prev", (b, H, R, P), io, dev)
+    dims = make_dims(b, L, H, P, N, R, 0, _io_code(io), bcnorm, eps)
+    Q = layer_backward_chunk(dims)
+    if Q == 0:
+        raise M3Error(M3_E_UNSUPPORTED, "no backward kernel for N=%d P=%d R=%d" % (N, P, R))
+    nc = (L + Q - 1) // Q
+    if states is None:
+        states = torch.empty((b, H, nc, P, N), dtype=io, device=dev)
+    _tensor(states, "states", (b, H, nc, P, N), io, dev)
+    if phis is None:
+        phis = torch.empty((b, H, nc, N // 2), dtype=f32, device=dev)
+    _tensor(phis, "phis", (b, H, nc, N // 2), f32, dev)
+    _check(lib.m3_layer_chunk_states(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(dt), _ptr(theta),
+                                     _ptr(normw_B), _ptr(bias_B), _ptr(A), _ptr(lam), _ptr(phi_in),
+                                     _ptr(h_in), _ptr(Bbar_prev), _ptr(x_prev), _ptr(states),
+                                     _ptr(phis), _stream(stream)))
+    return states, phis, Q
+
+
+def m3_layer_backward(x, B, C, dt, theta, A, lam, dy, normw_B=None, normw_C=None, bias_B=None,
+                      bias_C=None, w_out=None, phi_in=None, h_in=None, Bbar_prev=None, x_prev=None,
+                      dh_out=None, dphi_out=None, grads=None, bcnorm=True, eps=1e-5, workspace=None,
+                      stream=None):
+    """Gradients of m3_layer_prefill.  ``dy`` has y's shape; dh_out [b, H, N, P] and dphi_out
+    [b, H, N/2] are optional (zero).  Returns a dict keyed by input name (x, B, C, dt, theta, A,
+    lam, normw_B, normw_C, bias_B, bias_C, w_out, phi_in, h_in, Bbar_prev, x_prev); ``grads`` may
+    supply preallocated output tensors under those names."""
+    lib = load()
+    b, L, H, R, P = x.shape
+    N = B.shape[-1]
+    dev, io = x.device, x.dtype
+    f32 = torch.float32
+    _tensor(B, "B", (b, L, H, R, N), io, dev)
+    _tensor(C, "C", (b, L, H, R, N), io, dev)
+    _tensor(dt, "dt", (b, L, H), io, dev)
+    _tensor(theta, "theta", (b, L, H, N // 2), io, dev)
+    _tensor(lam, "lam", (b, L, H), io, dev)
+    _tensor(A, "A", (H,), f32, dev)
+    _tensor(normw_B, "normw_B", (H, N), f32, dev)
+    _tensor(normw_C, "normw_C", (H, N), f32, dev)
+    _tensor(bias_B, "bias_B", (H, R, N), f32, dev)
+    _tensor(bias_C, "bias_C", (H, R, N), f32, dev)
+    _tensor(w_out, "w_out", (H, R, P), f32, dev)
+    _tensor(phi_in, "phi_in", (b, H, N // 2), f32, dev)
+    _tensor(h_in, "h_in", (b, H, N, P), f32, dev)
+    _tensor(Bbar_prev, "Bbar_prev", (b, H, R, N), io, dev)
+    _tensor(x_prev, "x_prev", (b, H, R, P), io, dev)
+    yshape = (b, L, H, P) if w_out is not None else (b, L, H, R, P)
+    _tensor(dy, "dy", yshape, io, dev)
+    _tensor(dh_out, "dh_out", (b, H, N, P), f32, dev)
+    _tensor(dphi_out, "dphi_out", (b, H, N // 2), f32, dev)
+    carry = Bbar_prev is not None and x_prev is not None
+    spec = {"x": ((b, L, H, R, P), io), "B": ((b, L, H, R, N), io), "C": ((b, L, H, R, N), io),
+            "dt": ((b, L, H), io), "theta": ((b, L, H, N // 2), io), "A": ((H,), f32),
+            "lam": ((b, L, H), io), "normw_B": ((H, N), f32), "normw_C": ((H, N), f32),
+            "bias_B": ((H, R, N), f32), "bias_C": ((H, R, N), f32), "phi_in": ((b, H, N // 2), f32),
+            "h_in": ((b, H, N, P), f32)}
+    if w_out is not None:
+        spec["w_out"] = ((H, R, P), f32)
+    if carry:
+        spec["Bbar_prev"] = ((b, H, R, N), io)
+        spec["x_prev"] = ((b, H, R, P), io)
+    grads = dict(grads or {})
+    for k, (shape, dtype) in spec.items():
+        if grads.get(k) is None:
+            grads[k] = torch.empty(shape, dtype=dtype, device=dev)
+        _tensor(grads[k], "grad " + k, shape, dtype, dev)
+    grads.setdefault("w_out", None)
+    grads.setdefault("Bbar_prev", None)
+    grads.setdefault("x_prev", None)
+    dims = make_dims(b, L, H, P, N, R, 0, _io_code(io), bcnorm, eps)
+    need = layer_backward_workspace_bytes(dims)
+    if need == 0:
+        raise M3Error(M3_E_UNSUPPORTED, "no backward kernel for N=%d P=%d R=%d" % (N, P, R))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    g = grads
+    _check(lib.m3_layer_backward(
+        ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(theta), _ptr(normw_B),
+        _ptr(normw_C), _ptr(bias_B), _ptr(bias_C), _ptr(A), _ptr(lam), _ptr(w_out), _ptr(phi_in),
+        _ptr(h_in), _ptr(Bbar_prev), _ptr(x_prev), _ptr(dy), _ptr(dh_out), _ptr(dphi_out),
+        _ptr(g["x"]), _ptr(g["B"]), _ptr(g["C"]), _ptr(g["dt"]), _ptr(g["theta"]), _ptr(g["A"]),
+        _ptr(g["lam"]), _ptr(g["normw_B"]), _ptr(g["normw_C"]), _ptr(g["bias_B"]),
+        _ptr(g["bias_C"]), _ptr(g["w_out"]), _ptr(g["phi_in"]), _ptr(g["h_in"]),
+        _ptr(g["Bbar_prev"]), _ptr(g["x_prev"]), _ptr(workspace), ws_bytes, _stream(stream)))
+    return grads

@@ -227,3 +227,77 @@ def test_layer_prefill_varlen_needs_offsets():
     q = list(p)
     q[0] = q[17]                                  # offsets inside y
     assert call(_dims(chunk=32), q) == m3scan.M3_E_ALIAS
+
+
+def _bwd_args(ws_bytes_ok=True):
+    # x B C dt theta normw_B normw_C bias_B bias_C A lam w_out phi_in h_in Bbar_prev x_prev
+    # dy dh_out dphi_out | dx dB dC ddt dtheta dA dlam dnormw_B dnormw_C dbias_B dbias_C dw_out
+    # dphi_in dh_in dBbar_prev dx_prev | workspace
+    p = _ptrs(36)
+    for i in (5, 6, 7, 8, 11, 12, 13, 14, 15, 17, 18, 26, 27, 28, 29, 30, 33, 34):
+        p[i] = None
+    return p
+
+
+def _bwd(dims, p, ws_bytes):
+    return m3scan.load().m3_layer_backward(ctypes.byref(dims), *p, ws_bytes, None)
+
+
+def test_layer_backward_sizes():
+    d = _dims(seqlen=130)
+    assert m3scan.layer_backward_chunk(d) == 64
+    assert m3scan.layer_backward_chunk(_dims(rank=4)) == 16
+    assert m3scan.layer_backward_chunk(_dims(io=m3scan.M3_F32)) == 32
+    assert m3scan.layer_backward_chunk(_dims(rank=8)) == 0
+    # states (3 chunks) + angles + per-(b, h) partial sums, each rounded up to 256 bytes
+    st = 2 * 3 * 3 * 64 * 128 * 2
+    ph = 2 * 3 * 3 * 64 * 4
+    part = 2 * 3 * (1 + 64 + 2 * 128 + 2 * 128) * 4
+    r = lambda n: (n + 255) // 256 * 256
+    assert m3scan.layer_backward_workspace_bytes(d) == r(st) + r(ph) + r(part)
+    assert m3scan.layer_backward_workspace_bytes(_dims(rank=8)) == 0
+
+
+def test_layer_backward_errors():
+    d = _dims()
+    need = m3scan.layer_backward_workspace_bytes(d)
+    assert _bwd(d, _bwd_args(), need) == m3scan.M3_E_NODEVICE   # valid: stops at the device check
+    p = _bwd_args()
+    p[0] = None
+    assert _bwd(d, p, need) == m3scan.M3_E_NULL and "x is NULL" in m3scan.last_error()
+    p = _bwd_args()
+    p[16] = None
+    assert _bwd(d, p, need) == m3scan.M3_E_NULL and "dy is NULL" in m3scan.last_error()
+    assert _bwd(d, _bwd_args(), need - 1) == m3scan.M3_E_WORKSPACE
+    p = _bwd_args()
+    p[35] = None
+    assert _bwd(d, p, need) == m3scan.M3_E_WORKSPACE
+    assert _bwd(_dims(rank=8), _bwd_args(), 1 << 30) == m3scan.M3_E_UNSUPPORTED
+    assert _bwd(_dims(chunk=5), _bwd_args(), need) == m3scan.M3_E_UNSUPPORTED
+    assert _bwd(_dims(chunk=64), _bwd_args(), need) == m3scan.M3_E_NODEVICE
+    p = _bwd_args()
+    p[19] = P(p[19].value + 2)
+    assert _bwd(d, p, need) == m3scan.M3_E_ALIGN and "dx" in m3scan.last_error()
+    p = _bwd_args()
+    p[19] = p[0]
+    assert _bwd(d, p, need) == m3scan.M3_E_ALIAS
+    p = _bwd_args()
+    p[20] = p[35]
+    assert _bwd(d, p, need) == m3scan.M3_E_ALIAS and "workspace" in m3scan.last_error()
+
+
+def test_layer_chunk_states_errors():
+    lib = m3scan.load()
+    d = _dims()
+    # x B dt theta normw_B bias_B A lam phi_in h_in Bbar_prev x_prev states phis
+    p = _ptrs(14)
+    for i in (4, 5, 8, 9, 10, 11):
+        p[i] = None
+    assert lib.m3_layer_chunk_states(ctypes.byref(d), *p, None) == m3scan.M3_E_NODEVICE
+    q = list(p)
+    q[12] = None
+    assert lib.m3_layer_chunk_states(ctypes.byref(d), *q, None) == m3scan.M3_E_NULL
+    assert lib.m3_layer_chunk_states(ctypes.byref(_dims(headdim=32)), *p, None) == m3scan.M3_E_UNSUPPORTED
+    q = list(p)
+    q[12] = q[0]
+    assert lib.m3_layer_chunk_states(ctypes.byref(d), *q, None) == m3scan.M3_E_ALIAS

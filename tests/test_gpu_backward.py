@@ -1,0 +1,179 @@
+"""GPU parity of the layer-core backward pass (m3_layer_chunk_states and m3_layer_backward)
+against the fp64 oracle's gradients (oracle.layer_backward, the step-by-step reverse-mode of the
+plain recurrence, itself pinned to central finite differences of the forward oracle).
+
+Inputs and cotangents are seeded draws (inputs.make_prefill_inputs / make_cotangents); the
+oracle receives the same rounded values.  Sequence lengths span several backward chunks and end
+in a ragged tail, and include a sequence shorter than one chunk.  Every call goes through the C
+ABI.  Errors are normwise per gradient tensor, max|gpu - ref| / max|ref|, against gpu_util.TOL.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, angle_err, rel_err, to_dev, to_np
+from state_space_sequence_m3_amd import inputs, m3scan
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+GRAD_KEYS = ("x", "B", "C", "dt", "theta", "A", "lam", "normw_B", "normw_C", "bias_B", "bias_C",
+             "w_out", "phi_in", "h_in", "Bbar_prev", "x_prev")
+
+
+def _wl(io, b, L, H, P, N, R, bcnorm=True, bias=True, mix=False):
+    return inputs.Workload("case", b, L, H, P, N, R, 0, io, bcnorm, bias, mix)
+
+
+BWD_CASES = [
+    # io, b, L, H, P, N, R, bcnorm, normw, bias, mix, carry
+    ("f32", 1, 64, 1, 16, 16, 1, False, False, False, False, False),   # tiny SISO fp32, 4 chunks
+    ("f32", 2, 75, 2, 16, 16, 2, True, True, True, True, True),        # ragged, R = 2, mixing
+    ("f32", 1, 70, 2, 64, 64, 1, True, True, True, False, True),       # chunk 32 steps, ragged
+    ("f32", 1, 45, 2, 64, 128, 4, True, True, True, True, True),       # chunk 8 steps
+    ("bf16", 2, 333, 3, 64, 128, 1, True, True, True, False, True),    # chunk 64 steps, ragged
+    ("bf16", 1, 150, 2, 64, 128, 4, True, True, True, True, True),     # MIMO R = 4, mixing
+    ("bf16", 1, 90, 2, 64, 128, 2, True, False, True, False, True),    # R = 2, unit weights
+    ("bf16", 2, 129, 2, 64, 128, 1, False, False, False, False, False),  # no BCNorm, no bias
+    ("bf16", 1, 200, 2, 64, 64, 1, True, True, True, False, True),     # N = 64
+    ("bf16", 1, 40, 2, 64, 128, 1, True, True, True, False, True),     # shorter than one chunk
+]
+
+
+def _ids(c):
+    return "%s-b%d-L%d-H%d-P%d-N%d-R%d" % c[:7] + ("-mix" if c[10] else "") + ("-carry" if c[11] else "")
+
+
+def _angle_sum_scales(ref, inp, cot):
+    """Magnitudes of the terms summed into dtheta and dphi_in.
+
+    dtheta_t = dt_t S_t and dphi_in = S_0, where S_t = dphi_out + sum_{t' >= t} dPhi_t' sums the
+    per-step angle cotangents.  Those terms largely cancel (a rotation common to every Bbar and
+    Cbar leaves the outputs unchanged, apart from the carried-in terms), so the result can be far
+    smaller than its terms.  The error of a sum is bounded by the sum of its terms' magnitudes
+    times their relative error; this returns max_t dt_t A_t and max A_0 with
+    A_t = |dphi_out| + sum_{t' >= t} |dPhi_t'|, the dPhi_t being recovered from the oracle's own
+    dtheta (dt > 0)."""
+    dt = to_np(inp["dt"])[..., None]                                  # [b, L, H, 1]
+    S = ref["theta"] / dt                                              # [b, L, H, K]
+    dpo = to_np(cot["dphi_out"])[:, None] if cot.get("dphi_out") is not None else np.zeros_like(S[:, :1])
+    nxt = np.concatenate([S[:, 1:], dpo], axis=1)
+    A = np.flip(np.cumsum(np.flip(np.abs(S - nxt), 1), 1), 1) + np.abs(dpo)
+    return float((dt * A).max()), float(A[:, 0].max())
+
+
+def _backward(d, cot, w, mix):
+    return m3scan.m3_layer_backward(d["x"], d["B"], d["C"], d["dt"], d["theta"], d["A"], d["lam"],
+                                    cot["dy"], d.get("normw_B"), d.get("normw_C"), d.get("bias_B"),
+                                    d.get("bias_C"), d["w_out"] if mix else None, d.get("phi_in"),
+                                    d.get("h_in"), d.get("Bbar_prev"), d.get("x_prev"),
+                                    cot["dh_out"], cot["dphi_out"], bcnorm=w.bcnorm)
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=_ids)
+def test_backward_parity(case):
+    io, b, L, H, P, N, R, bcnorm, normw, bias, mix, carry = case
+    print("backward case", _ids(case), flush=True)
+    w = _wl(io, b, L, H, P, N, R, bcnorm, bias, mix)
+    inp = inputs.make_prefill_inputs(w, seed=41, normw=normw, carry=carry)
+    cot = inputs.make_cotangents(w, seed=42)
+    grads = _backward(to_dev(inp, DEV), to_dev(cot, DEV), w, mix)
+    torch.cuda.synchronize()
+    ref = oracle.layer_backward(inp, cot["dy"], cot["dh_out"], cot["dphi_out"], bcnorm=bcnorm,
+                                mix=mix)
+    tol = TOL[io]
+    errs = {}
+    for k in GRAD_KEYS:
+        if ref.get(k) is None or (k == "w_out" and not mix):
+            continue
+        if k in ("normw_B", "normw_C") and not bcnorm:
+            assert float(grads[k].abs().max()) == 0.0
+            continue
+        errs[k] = rel_err(grads[k], ref[k])
+    print("normwise", {k: "%.2e" % v for k, v in errs.items()}, flush=True)
+    if io == "bf16":
+        # sums of cancelling terms: error relative to the size of the terms summed
+        sc_theta, sc_phi = _angle_sum_scales(ref, inp, cot)
+        errs["theta"] = float(np.abs(to_np(grads["theta"]) - ref["theta"]).max()) / sc_theta
+        errs["phi_in"] = float(np.abs(to_np(grads["phi_in"]) - ref["phi_in"]).max()) / sc_phi
+        print("angle sums, relative to their terms: theta %.2e phi_in %.2e" % (errs["theta"], errs["phi_in"]),
+              flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, bad
+
+
+def test_backward_without_carry_gradients_zero_fill():
+    """Bbar_prev / x_prev absent: gradients asked for them are zero-filled; dh_in and dphi_in are
+    still the state and angle cotangents before the first step."""
+    w = _wl("bf16", 1, 100, 2, 64, 128, 1)
+    inp = inputs.make_prefill_inputs(w, seed=43, carry=False)
+    cot = inputs.make_cotangents(w, seed=44)
+    d, c = to_dev(inp, DEV), to_dev(cot, DEV)
+    pre = {"Bbar_prev": torch.full((1, 2, 1, 128), 7.0, dtype=torch.bfloat16, device=DEV),
+           "x_prev": torch.full((1, 2, 1, 64), 7.0, dtype=torch.bfloat16, device=DEV)}
+    g = m3scan.m3_layer_backward(d["x"], d["B"], d["C"], d["dt"], d["theta"], d["A"], d["lam"], c["dy"],
+                                 bias_B=d["bias_B"], bias_C=d["bias_C"], dh_out=c["dh_out"],
+                                 dphi_out=c["dphi_out"], grads=pre)
+    torch.cuda.synchronize()
+    ref = oracle.layer_backward(inp, cot["dy"], cot["dh_out"], cot["dphi_out"], mix=False)
+    assert rel_err(g["h_in"], ref["h_in"]) <= TOL["bf16"]
+    assert float(np.abs(to_np(g["phi_in"]) - ref["phi_in"]).max()) <= TOL["bf16"] * _angle_sum_scales(ref, inp, cot)[1]
+    assert rel_err(g["x"], ref["x"]) <= TOL["bf16"]
+    assert float(g["Bbar_prev"].float().abs().max()) == 0.0
+    assert float(g["x_prev"].float().abs().max()) == 0.0
+
+
+def test_backward_zero_cotangents_give_zero():
+    w = _wl("bf16", 1, 130, 2, 64, 128, 2, mix=True)
+    inp = inputs.make_prefill_inputs(w, seed=45, normw=True, carry=True)
+    d = to_dev(inp, DEV)
+    dy = torch.zeros((1, 130, 2, 64), dtype=torch.bfloat16, device=DEV)
+    g = m3scan.m3_layer_backward(d["x"], d["B"], d["C"], d["dt"], d["theta"], d["A"], d["lam"], dy,
+                                 d["normw_B"], d["normw_C"], d["bias_B"], d["bias_C"], d["w_out"],
+                                 d["phi_in"], d["h_in"], d["Bbar_prev"], d["x_prev"])
+    torch.cuda.synchronize()
+    for k, v in g.items():
+        if v is not None:
+            assert float(v.float().abs().max()) == 0.0, k
+
+
+def _oracle_chunk_states(inp, Q, bcnorm):
+    """Shifted states G_{t0-1} = g_{t0-1} + c_{t0} u_{t0-1} (transposed to [P][N]) and angles
+    Phi_{t0-1} at each chunk start t0 = cQ: the carried-in inputs for t0 = 0, else oracle.layer
+    on the prefix [0, t0).  The inputs carry h_in, phi_in, Bbar_prev and x_prev."""
+    L = inp["x"].shape[1]
+    dt, lam = to_np(inp["dt"]), to_np(inp["lam"])
+    states, phis = [], []
+    for t0 in range(0, L, Q):
+        if t0 == 0:
+            g, phi = to_np(inp["h_in"]), to_np(inp["phi_in"])
+            Bl, xl = to_np(inp["Bbar_prev"]), to_np(inp["x_prev"])
+        else:
+            pre = {k: (v[:, :t0] if k in ("x", "B", "C", "dt", "lam", "theta") else v)
+                   for k, v in inp.items()}
+            o = oracle.layer(pre, bcnorm=bcnorm, mix=False)
+            g, phi, Bl, xl = o["h_out"], o["phi_out"], o["Bbar_last"], o["x_last"]
+        cc = (1.0 - lam[:, t0]) * dt[:, t0]                        # [b, H]
+        u = np.einsum("bhrn,bhrp->bhnp", Bl, xl)
+        states.append(np.swapaxes(g + cc[:, :, None, None] * u, -1, -2))
+        phis.append(phi)
+    return np.stack(states, 2), np.stack(phis, 2)
+
+
+@pytest.mark.parametrize("io,R,N,P", [("bf16", 1, 128, 64), ("bf16", 4, 128, 64), ("f32", 2, 64, 64)])
+def test_chunk_states(io, R, N, P):
+    w = _wl(io, 1, 150, 2, P, N, R, mix=False)
+    print("chunk states", io, R, N, P, flush=True)
+    inp = inputs.make_prefill_inputs(w, seed=46, normw=True, carry=True)
+    d = to_dev(inp, DEV)
+    st, ph, Q = m3scan.m3_layer_chunk_states(d["x"], d["B"], d["dt"], d["theta"], d["A"], d["lam"],
+                                             d["normw_B"], d["bias_B"], d["phi_in"], d["h_in"],
+                                             d["Bbar_prev"], d["x_prev"])
+    torch.cuda.synchronize()
+    ref_st, ref_ph = _oracle_chunk_states(inp, Q, True)
+    assert rel_err(st, ref_st) <= TOL[io]
+    assert angle_err(ph, ref_ph) <= (1e-3 if io == "bf16" else 1e-4)
