@@ -7,7 +7,8 @@ m3_layer_prefill, which does both in one kernel (chunk 32).  `value` is prefill 
 tokens per step).  The same line times the two-call path (m3_bcnorm_rope then m3_prefill, chunk
 64) for comparison, the MIMO R=4 workload through both paths, decode throughput on the B=128
 decode workloads (R=1 and R=4: m3_layer_decode_step per token, and the two-call path
-m3_bcnorm_rope with L=1 then m3_decode_step), the
+m3_bcnorm_rope with L=1 then m3_decode_step), the backward pass (m3_layer_backward: gradients of
+every input) on the SISO and MIMO workloads, the
 roofline of the dominant kernel measured live with HIP events on the launch stream, and the fp64
 oracle's throughput on a bounded sample of the same prefill workload on the host cores.
 
@@ -368,6 +369,70 @@ def time_decode(w, steps, warmup, dev):
     return ms_tok, ms_bc, ms_dec
 
 
+def backward_bytes_per_token_head(w) -> int:
+    """Compulsory HBM bytes of m3_layer_backward per (token, head): the forward inputs x, B, C, dt,
+    lam, theta and the cotangent dy read once, the gradients dx, dB, dC, ddt, dlam, dtheta written
+    once.  The chunk states the call saves and reads back are its own intermediates (excluded)."""
+    es = 2 if w.io == "bf16" else 4
+    R, N, P = w.rank, w.dstate, w.headdim
+    io = R * P + 2 * R * N + 2 + N // 2
+    return es * (2 * io + (P if w.mix else R * P))
+
+
+def backward_flops_per_token_head(w, chunk_rows) -> int:
+    """MFMA flops of m3_layer_backward per (token, head), counting full chunk-square blocks: per
+    chunk of QR rows, S and dP (QR^2 N, QR^2 P), dX, dBbar, dCbar (QR^2 P, 2 QR^2 N plus three
+    QR N P state products), the state cotangent and the saved-state recompute (2 QR N P), the
+    recomputed Y for the mixing gradient (QR N P + QR^2 P), 2 flops per multiply-add."""
+    R, N, P, QR = w.rank, w.dstate, w.headdim, chunk_rows
+    per_chunk = 2 * (QR * QR * (3 * N + 2 * P) + 5 * QR * N * P)
+    if w.mix:
+        per_chunk += 2 * (QR * N * P + QR * QR * P)
+    return per_chunk * R // QR
+
+
+def time_backward(w, steps, warmup, dev):
+    """m3_layer_backward on workload w (inputs, cotangents, gradients and workspace allocated
+    once), HIP-event timed on the launch stream; also m3_layer_chunk_states alone (the first of the
+    call's kernels) for the split."""
+    inp = inputs.make_prefill_inputs(w, seed=0, device=dev)
+    cot = inputs.make_cotangents(w, seed=1, device=dev)
+    mixw = inp["w_out"] if w.mix else None
+    grads = m3scan.m3_layer_backward(inp["x"], inp["B"], inp["C"], inp["dt"], inp["theta"], inp["A"],
+                                     inp["lam"], cot["dy"], inp["normw_B"], inp["normw_C"], inp["bias_B"],
+                                     inp["bias_C"], mixw, bcnorm=w.bcnorm)
+    dims = m3scan.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, 0,
+                            m3scan._io_code(w.torch_io), w.bcnorm)
+    ws = torch.empty(m3scan.layer_backward_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        m3scan.m3_layer_backward(inp["x"], inp["B"], inp["C"], inp["dt"], inp["theta"], inp["A"], inp["lam"],
+                                 cot["dy"], inp["normw_B"], inp["normw_C"], inp["bias_B"], inp["bias_C"], mixw,
+                                 grads=grads, bcnorm=w.bcnorm, workspace=ws)
+
+    def states():
+        m3scan.m3_layer_chunk_states(inp["x"], inp["B"], inp["dt"], inp["theta"], inp["A"], inp["lam"],
+                                     inp["normw_B"], inp["bias_B"], bcnorm=w.bcnorm)
+
+    out = {}
+    for name, fn in (("m3_layer_backward", step), ("m3_layer_chunk_states", states)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = t0.elapsed_time(t1) / steps
+    del inp, cot, grads, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, inp, nheads: int):
     """The fp64 oracle (unchanged) on a bounded sample of the prefill workload: every batch row
     and the first `nheads` heads, i.e. batch * nheads (batch, head) pairs over the full length."""
@@ -421,6 +486,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-mimo", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
                     help="only time a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -536,6 +602,24 @@ def main():
                                   "how": "m3_layer_decode_step, 16 steps per HIP graph replay",
                                   "eager": {"steps_per_s": 1e3 / ms_e, "ms_per_step": ms_e}}
 
+    # backward pass of the layer core (gradients of every input), SISO and MIMO workloads
+    backward = None
+    if not args.no_backward:
+        backward = {}
+        for bname in ("siso_b8_l2048",) + (() if args.no_mimo else ("mimo4_b8_l2048",)):
+            wb = inputs.WORKLOADS[bname]
+            t = time_backward(wb, args.steps, args.warmup, dev)
+            thb = wb.batch * wb.seqlen * wb.nheads
+            rows = 64 if wb.io == "bf16" else 32
+            bb = thb * backward_bytes_per_token_head(wb) + 3 * wb.batch * wb.nheads * wb.dstate * wb.headdim * 4
+            bf = thb * backward_flops_per_token_head(wb, rows)
+            ms = t["m3_layer_backward"]
+            backward[bname] = {"ms": ms, "tokens/s": wb.batch * wb.seqlen / (ms / 1e3),
+                               "chunk_states_ms": t["m3_layer_chunk_states"],
+                               "bytes": bb, "GB/s": bb / ms / 1e6, "hbm_frac": bb / ms / 1e6 / HBM_PEAK_GBS,
+                               "TFLOP/s": bf / ms / 1e9, "mfma_frac": bf / ms / 1e9 / BF16_MFMA_PEAK_TFLOPS,
+                               "chunk_rows": rows}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, inp, args.cpu_heads)
@@ -564,6 +648,7 @@ def main():
         "mimo4_b8_l2048": mimo,
         "variants": variants,
         "decode": decode,
+        "backward": backward,
     }
     print(json.dumps(line))
 

@@ -185,3 +185,41 @@ def test_long_context_prefill_then_decode_sampled():
         assert err <= TOL["bf16"], (hi, err)
         assert rel_err(h[:, hi:hi + 1], state["h"]) <= TOL["bf16"]
         assert angle_err(phi[:, hi:hi + 1], state["phi"]) <= 1e-3
+
+
+@pytest.mark.parametrize("name,head", [("siso_b8_l2048", 17), ("mimo4_b8_l2048", 40)])
+def test_backward_workload_sampled(name, head):
+    """m3_layer_backward over the whole b8 L2048 batch (the configuration bench.py times); the
+    oracle recomputes every batch element of one head, which gives that head's per-sequence
+    gradients and its batch-summed parameter gradients exactly."""
+    w = inputs.WORKLOADS[name]
+    print("backward workload", name, "head", head, flush=True)
+    inp = inputs.make_prefill_inputs(w, seed=5, device=DEV)
+    cot = inputs.make_cotangents(w, seed=6, device=DEV)
+    g = m3scan.m3_layer_backward(inp["x"], inp["B"], inp["C"], inp["dt"], inp["theta"], inp["A"],
+                                 inp["lam"], cot["dy"], inp["normw_B"], inp["normw_C"], inp["bias_B"],
+                                 inp["bias_C"], inp["w_out"] if w.mix else None, bcnorm=w.bcnorm)
+    torch.cuda.synchronize()
+    hs = slice(head, head + 1)
+    pair = {}
+    for k, v in inp.items():
+        if v is None:
+            pair[k] = None
+        elif k in SEQ_KEYS:
+            pair[k] = v[:, :, hs].cpu()
+        else:   # per-head constants
+            pair[k] = v[hs].cpu()
+    c = {"dy": cot["dy"][:, :, hs].cpu(), "dh_out": None, "dphi_out": None}
+    ref = oracle.layer_backward(pair, c["dy"], bcnorm=w.bcnorm, mix=w.mix)
+    for k in ("x", "B", "C", "dt", "lam", "h_in"):
+        got = g[k][:, :, hs] if k in SEQ_KEYS else g[k][:, hs]
+        assert rel_err(got, ref[k]) <= TOL[w.io], k
+    for k in ("A", "bias_B", "bias_C", "normw_B", "normw_C") + (("w_out",) if w.mix else ()):
+        assert rel_err(g[k][hs], ref[k]) <= TOL[w.io], k
+    # dtheta and dphi_in sum cancelling terms: error against the size of the terms summed
+    dt = to_np(pair["dt"])[..., None]
+    S = ref["theta"] / dt
+    nxt = np.concatenate([S[:, 1:], np.zeros_like(S[:, :1])], axis=1)
+    A = np.flip(np.cumsum(np.flip(np.abs(S - nxt), 1), 1), 1)
+    assert np.abs(to_np(g["theta"][:, :, hs]) - ref["theta"]).max() <= TOL[w.io] * (dt * A).max()
+    assert np.abs(to_np(g["phi_in"][:, hs]) - ref["phi_in"]).max() <= TOL[w.io] * A[:, 0].max()
