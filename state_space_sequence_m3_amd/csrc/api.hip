@@ -161,8 +161,13 @@ m3_status layer_prefill(const m3_dims* d, bool packed, const int32_t* cu_seqlens
                     "%s: no kernel for N = %lld, P = %lld, R = %lld, chunk*R = %lld (supported: (N,P) "
                     "in {(16,16),(64,64),(128,64)}, R in {1,2,4,8,16}, chunk*R in {16,32,64})",
                     fn, (long long)N, (long long)P, (long long)R, (long long)(Q * R));
-    if (Q * H * R * (N > P ? N : P) * (int64_t)es >= ((int64_t)1 << 31))
-        return fail(M3_E_DIMS, "%s: nheads * rank = %lld is too large for one chunk", fn, (long long)(H * R));
+    // the kernel addresses a sequence's rows with 32-bit byte offsets (a packed sequence is at most
+    // the L = T packed tokens long)
+    if ((L + 3 * Q) * H * R * (N > P ? N : P) * (int64_t)es >= ((int64_t)1 << 31))
+        return fail(M3_E_DIMS,
+                    "%s: one sequence spans %lld bytes per tensor, the limit is 2^31 (split the sequence: the "
+                    "carried state, angle and last step make the split exact)",
+                    fn, (long long)(L * H * R * (N > P ? N : P) * (int64_t)es));
     const Buf a16[] = {{x, 1, "x"}, {B, 1, "B"}, {C, 1, "C"}, {theta, 1, "theta"}, {y, 1, "y"},
                        {h_out, 1, "h_out"}, {h_in, 1, "h_in"}};
     if ((s = check_align(a16, 7, 16)) != M3_OK) return s;
@@ -364,9 +369,12 @@ m3_status m3_prefill(const m3_dims* d, const void* x, const void* Bbar, const vo
                     "m3_prefill: no kernel for N = %lld, P = %lld, R = %lld, chunk*R = %lld (supported: (N,P) in "
                     "{(16,16),(64,64),(128,64)}, R in {1,2,4,8,16}, chunk*R in {16,32,48,64})",
                     (long long)N, (long long)P, (long long)R, (long long)(Q * R));
-    // the kernel addresses one chunk's rows with 32-bit byte offsets
-    if (Q * H * R * (N > P ? N : P) * (int64_t)es >= ((int64_t)1 << 31))
-        return fail(M3_E_DIMS, "m3_prefill: nheads * rank = %lld is too large for one chunk", (long long)(H * R));
+    // the kernel addresses a sequence's rows with 32-bit byte offsets
+    if ((L + 3 * Q) * H * R * (N > P ? N : P) * (int64_t)es >= ((int64_t)1 << 31))
+        return fail(M3_E_DIMS,
+                    "m3_prefill: one sequence spans %lld bytes per tensor, the limit is 2^31 (split the sequence: "
+                    "the carried state and last step make the split exact)",
+                    (long long)(L * H * R * (N > P ? N : P) * (int64_t)es));
     const Buf a16[] = {{x, 1, "x"}, {Bbar, 1, "Bbar"}, {Cbar, 1, "Cbar"}, {y, 1, "y"}, {h_out, 1, "h_out"},
                        {h_in, 1, "h_in"}};
     if ((s = check_align(a16, 6, 16)) != M3_OK) return s;

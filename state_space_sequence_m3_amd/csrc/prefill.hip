@@ -135,10 +135,15 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const T* dtg = (const T*)a.dt + row_bh;
     const T* lamg = (const T*)a.lam + row_bh;
     const int pcol = 16 * wave + l16;            // this lane's column of P in MFMA tiles
-    // bytes from a chunk's first row to the end of the sequence's last row (t = L - 1)
-    auto tail_bytes = [&](int64_t t0, int64_t step, int64_t row) {
-        return clamp_bytes(((L - t0 - 1) * step + row) * (int64_t)sizeof(T));
+    // One buffer descriptor per stream over this sequence: from step 0 of this (b, h) to the end
+    // of its last row (t = L - 1).  A chunk adds its byte offset (32 bits: the whole sequence
+    // spans less than 2^31 bytes, which the host checks) to the per-lane offsets; loads past the
+    // last row read zero and stores there are dropped, so the ragged last chunk needs no branches.
+    auto seq_bytes = [&](int64_t step, int64_t row) {
+        return L > 0 ? clamp_bytes(((L - 1) * step + row) * (int64_t)sizeof(T)) : 0u;
     };
+    constexpr uint32_t ES = sizeof(T);
+    auto step_off = [&](int64_t t0, int64_t step) { return (uint32_t)t0 * (uint32_t)(step * ES); };
 
     // ---- staging: this thread moves 16-byte vectors k = 0, 1, ... of each tile.  Vector k is
     // chunk row i = i0 + k * RK (row (t, r) = (i >> rl2, i & rmask)), 16-byte column c0.
@@ -157,33 +162,45 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     uint4 rc[NBUF][MAXC], rb[NBUF][MAXC], rx[NBUF][MAXX];
     typedef typename IoBits<T>::type Bits;
     Bits nd[NBUF], nl[NBUF], ndn[NBUF], nln[NBUF];   // dt, lambda at t and t + 1 (io bits; the last wave uses them)
-    auto load_chunk = [&](int64_t c, int set) {
+    const rsrc_t dCs = make_rsrc(Cg, seq_bytes(HRN, (int64_t)R * N));
+    const rsrc_t dBs = make_rsrc(Bg, seq_bytes(HRN, (int64_t)R * N));
+    const rsrc_t dXs = make_rsrc(Xg, seq_bytes(HRP, (int64_t)R * P));
+    const rsrc_t dDs = make_rsrc(dtg, seq_bytes(H, 1));
+    const rsrc_t dLs = make_rsrc(lamg, seq_bytes(H, 1));
+    // part: 0 = Cbar rows, 1 = Bbar rows, 2 = x rows, 3 = step scalars; -1 = all
+    auto load_chunk = [&](int64_t c, int set, int part = -1) {
         const int64_t t0 = c * Q;
-        const uint32_t nbc = tail_bytes(t0, HRN, (int64_t)R * N), nbx = tail_bytes(t0, HRP, (int64_t)R * P);
-        const rsrc_t dC = make_rsrc(Cg + t0 * HRN, nbc), dB = make_rsrc(Bg + t0 * HRN, nbc);
-        const rsrc_t dX = make_rsrc(Xg + t0 * HRP, nbx);
+        if (part < 0 || part == 0) {
+            const uint32_t o = step_off(t0, HRN);
 #pragma unroll
-        for (int k = 0; k < MAXC; ++k) {
-            if (FULLC || iC0 + k * RKC < QR) {
-                rc[set][k] = buffer_load16(dC, offC(k));
-                rb[set][k] = buffer_load16(dB, offC(k));
-            }
+            for (int k = 0; k < MAXC; ++k)
+                if (FULLC || iC0 + k * RKC < QR) rc[set][k] = buffer_load16(dCs, offC(k) + o);
         }
+        if (part < 0 || part == 1) {
+            const uint32_t o = step_off(t0, HRN);
 #pragma unroll
-        for (int k = 0; k < MAXX; ++k)
-            if (FULLX || iX0 + k * RKX < QR) rx[set][k] = buffer_load16(dX, offX(k));
-        {
+            for (int k = 0; k < MAXC; ++k)
+                if (FULLC || iC0 + k * RKC < QR) rb[set][k] = buffer_load16(dBs, offC(k) + o);
+        }
+        if (part < 0 || part == 2) {
+            const uint32_t o = step_off(t0, HRP);
+#pragma unroll
+            for (int k = 0; k < MAXX; ++k)
+                if (FULLX || iX0 + k * RKX < QR) rx[set][k] = buffer_load16(dXs, offX(k) + o);
+        }
+        if (part < 0 || part == 3) {
             // steps t0 + lane and t0 + lane + 1; zero past the sequence end.  Lanes at or past Q
             // read the next chunk's values, which only reach scan lanes that are never read.  Only
-            // the last wave uses them; every wave loads them so that the number of loads in flight
-            // is the same on every path (the compiler's wait counts stay exact).
-            const uint32_t nbs = tail_bytes(t0, H, 1);
-            const rsrc_t dD = make_rsrc(dtg + t0 * H, nbs), dL = make_rsrc(lamg + t0 * H, nbs);
-            const uint32_t o0 = (uint32_t)(lane * H * (int)sizeof(T)), o1 = o0 + (uint32_t)(H * (int)sizeof(T));
-            nd[set] = buffer_load_bits(dD, o0, T{});
-            nl[set] = buffer_load_bits(dL, o0, T{});
-            ndn[set] = buffer_load_bits(dD, o1, T{});
-            nln[set] = buffer_load_bits(dL, o1, T{});
+            // the last wave uses them; the other waves issue the same loads aimed past the
+            // descriptor (no memory access), so that the number of loads in flight is the same on
+            // every path and the compiler's wait counts stay exact.
+            // Step t0 + lane + 1 is the next lane's value; only lane 63 loads it.
+            const uint32_t o0 = wave == NW - 1 ? (uint32_t)(lane * H * (int)sizeof(T)) + step_off(t0, H) : 0x80000000u;
+            const uint32_t o1 = wave == NW - 1 && lane == 63 ? o0 + (uint32_t)(H * (int)sizeof(T)) : 0x80000000u;
+            nd[set] = buffer_load_bits(dDs, o0, T{});
+            nl[set] = buffer_load_bits(dLs, o0, T{});
+            ndn[set] = buffer_load_bits(dDs, o1, T{});
+            nln[set] = buffer_load_bits(dLs, o1, T{});
         }
     };
     // ---- fused: angle increments of a chunk and their prefix scan ----------------------
@@ -193,18 +210,21 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     Bits rdt[SPT];
     const T* thg = (const T*)a.theta + row_bh * K;
     const int64_t HK = (int64_t)H * K;
+    const rsrc_t dTs = make_rsrc(thg, FUSED ? seq_bytes(HK, K) : 0u);
     auto load_theta = [&](int64_t c) {
         if (!FUSED) return;
         const int64_t t0 = c * Q;
-        const rsrc_t dT = make_rsrc(thg + t0 * HK, tail_bytes(t0, HK, K));
-        const rsrc_t dD = make_rsrc(dtg + t0 * H, tail_bytes(t0, H, 1));
+        const uint32_t ot = step_off(t0, HK), od = step_off(t0, H);
 #pragma unroll
         for (int s = 0; s < SPT; ++s) {
-            // steps past the chunk (R > 1 leaves rows of the tile unused) aim past the descriptor
+            // steps past the chunk (R > 1 leaves rows of the tile unused) and threads that do not
+            // scan aim past the descriptor; with 32 steps per column the upper half of a wave
+            // repeats the lower half's steps and takes their dt by a shuffle in the scan
             const int t = tj * SPT + s;
-            const bool in = t < Q;
-            rth[s] = buffer_load16(dT, in ? (uint32_t)((t * (int)HK + tv * VT) * (int)sizeof(T)) : 0x80000000u);
-            rdt[s] = buffer_load_bits(dD, in ? (uint32_t)(t * H * (int)sizeof(T)) : 0x80000000u, T{});
+            const bool in = scanner && t < Q;
+            rth[s] = buffer_load16(dTs, in ? (uint32_t)((t * (int)HK + tv * VT) * (int)sizeof(T)) + ot : 0x80000000u);
+            const bool dt_lane = in && !(TPV == 32 && lane >= 32);
+            rdt[s] = buffer_load_bits(dDs, dt_lane ? (uint32_t)(t * H * (int)sizeof(T)) + od : 0x80000000u, T{});
         }
     };
     // Phi[t] = Phi[t0 - 1] + sum_{t0 <= i <= t} dt_i theta_i for the chunk starting at c * Q, into
@@ -218,7 +238,8 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         for (int s = 0; s < SPT; ++s) {
             float f[VT];
             unpack16(rth[s], f, T{});
-            const float d = bits_to_f32(rdt[s]);
+            float d = bits_to_f32(rdt[s]);
+            if (TPV == 32) d = shfl(d, lane & 31);
 #pragma unroll
             for (int e = 0; e < VT; ++e) acc[s][e] = (s ? acc[s - 1][e] : 0.f) + d * f[e];
         }
@@ -301,7 +322,12 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // the last wave (the one with the fewest score tiles): the chunk's per-step scalars (lane =
     // step) -> per-row copies in LDS.  Lanes past the chunk only add to later lanes of the scan,
     // which are never read.
-    auto stage_scalars = [&](float d, float lm, float dn, float lmn, int buf) {
+    auto stage_scalars = [&](float d, float lm, float dn63, float lmn63, int buf) {
+        // dt, lambda of step t + 1: the next lane's, lane 63's own load (the shuffles run in every
+        // lane: a lane reading an inactive lane would get zero)
+        const float dsh = __shfl_down(d, 1, 64), lsh = __shfl_down(lm, 1, 64);
+        const float dn = lane < 63 ? dsh : dn63;
+        const float lmn = lane < 63 ? lsh : lmn63;
         const float l2 = wave_scan_add(d * Alog2);   // l_t in log2 units, inclusive over the chunk
         const float gam = lm * d;
         const float mu = gam + (1.0f - lmn) * dn;
@@ -371,6 +397,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const bool mix = a.w_out != nullptr;
     T* yg = (T*)a.y + row_bh * (mix ? P : (int64_t)R * P);
     const int64_t ystep = mix ? (int64_t)H * P : HRP, yrow = mix ? P : (int64_t)R * P;
+    const rsrc_t dYs = make_rsrc(yg, seq_bytes(ystep, yrow));
     floatx4 wo = {1.f, 1.f, 1.f, 1.f};          // mixing weights for this lane's (r, 4 columns)
     if (mix) {
         const int r = l16 & rmask;
@@ -502,7 +529,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
             for (int ib = sb; ib < NIB; ++ib)
                 y[ib] = MM::mma(xf[sb], MM::ldk(pM_k + buf * TM + 16 * ib * LDM + 16 * sb), y[ib]);
-        const rsrc_t dY = make_rsrc(yg + t0 * ystep, tail_bytes(t0, ystep, yrow));
+        const uint32_t oy = step_off(t0, ystep);
         // lane holds Y[(t, r) = i][p = 16 wave + 4 g + m] of row block ib
         const int p = 16 * wave + 4 * g;
         auto store_mixed = [&](auto RW) {   // RW: the rank as a compile-time width
@@ -514,9 +541,9 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
                 for (int m = 0; m < 4; ++m) yv[m] = group_sum(yv[m] * wo[m], RR);
                 // one lane per step stores the mixed row; the others aim past the descriptor
-                const uint32_t off = (i & (RR - 1)) == 0 ? (uint32_t)(((i / RR) * H * P + p) * (int)sizeof(T))
+                const uint32_t off = (i & (RR - 1)) == 0 ? (uint32_t)(((i / RR) * H * P + p) * (int)sizeof(T)) + oy
                                                          : 0x80000000u;
-                store4(dY, off, yv, T{});
+                store4(dYs, off, yv, T{});
             }
         };
         if (!mix) {
@@ -524,7 +551,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             for (int ib = 0; ib < NIB; ++ib) {
                 const int i = 16 * ib + l16;
                 const int tl = i >> rl2, r = i & rmask;
-                store4(dY, (uint32_t)(((tl * H * R + r) * P + p) * (int)sizeof(T)), y[ib], T{});
+                store4(dYs, (uint32_t)(((tl * H * R + r) * P + p) * (int)sizeof(T)) + oy, y[ib], T{});
             }
         } else {
             switch (R) {
@@ -578,10 +605,14 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         auto iter = [&](auto PB, int64_t c) {
             constexpr int p = decltype(PB)::value, q = p ^ 1;
             const bool has1 = c + 1 < nchunk, has2 = c + 2 < nchunk;
-            load_chunk(c + 2, p);
             // stage chunk c + 1 (register set q) into buffer q, item j after K block
-            // (2 j + 1) NB / (2 NITEM); fused: the angles of chunk c + 2 in K block NB / 2
+            // (2 j + 1) NB / (2 NITEM); fused: the angles of chunk c + 2 in K block NB / 2.  The
+            // loads of chunk c + 2 go out in four parts over the K blocks, so that their issue
+            // does not stall the wave in one burst.
             auto hook = [&](int k) {
+#pragma unroll
+                for (int part = 0; part < 4; ++part)
+                    if (part * NB / 4 == k) load_chunk(c + 2, p, part);
                 if (has1) {
 #pragma unroll
                     for (int j = 0; j < NITEM; ++j)

@@ -96,6 +96,13 @@ def test_prefill_unsupported_shape():
     assert "no kernel" in m3scan.last_error()
 
 
+def test_prefill_sequence_span_limit():
+    """A sequence whose rows span 2^31 bytes or more per tensor is rejected (32-bit offsets)."""
+    # 2^31 / (64 heads * 128 * 2 bytes) = 131072 steps; the 3 chunks of margin push it over
+    assert _prefill(_dims(seqlen=131072 - 64, nheads=64), _prefill_args()) == m3scan.M3_E_DIMS
+    assert "2^31" in m3scan.last_error()
+
+
 def test_prefill_misaligned():
     p = _prefill_args()
     p[1] = P(ALIGNED + (1 << 24) + 8)
