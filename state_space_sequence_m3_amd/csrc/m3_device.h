@@ -131,5 +131,7 @@ __device__ __forceinline__ uint32_t clamp_bytes(int64_t n) {
 
 // Reduce an angle to [-pi, pi] (any representative gives the same rotation).
 __device__ __forceinline__ float wrap_angle(float a) { return a - kTwoPi * rintf(a * kInvTwoPi); }
+// The same for an angle in turns (revolutions): reduced to [-1/2, 1/2].
+__device__ __forceinline__ float wrap_turns(float a) { return a - rintf(a); }
 
 }  // namespace m3

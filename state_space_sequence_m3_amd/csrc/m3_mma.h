@@ -93,6 +93,19 @@ __device__ __forceinline__ void unpack16(uint4 v, float (&o)[8], bf16) {
         o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
 }
+// sum of the squares of one 16-byte vector of io elements (bf16 pairs: v_dot2_f32_bf16, whose
+// products of two bf16 values are exact in fp32), as a tree rather than one chain
+__device__ __forceinline__ float sumsq16(uint4 v, float) {
+    const float a = __uint_as_float(v.x), b = __uint_as_float(v.y), c = __uint_as_float(v.z), d = __uint_as_float(v.w);
+    return fmaf(a, a, b * b) + fmaf(c, c, d * d);
+}
+__device__ __forceinline__ float sumsq16(uint4 v, bf16) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t p = __builtin_bit_cast(bf16x2_t, v.x), q = __builtin_bit_cast(bf16x2_t, v.y);
+    const bf16x2_t r = __builtin_bit_cast(bf16x2_t, v.z), s = __builtin_bit_cast(bf16x2_t, v.w);
+    return __builtin_amdgcn_fdot2_f32_bf16(q, q, __builtin_amdgcn_fdot2_f32_bf16(p, p, 0.f, false), false) +
+           __builtin_amdgcn_fdot2_f32_bf16(s, s, __builtin_amdgcn_fdot2_f32_bf16(r, r, 0.f, false), false);
+}
 __device__ __forceinline__ uint4 pack16(const float (&v)[4], float) {
     return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
 }

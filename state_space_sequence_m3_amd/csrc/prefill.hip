@@ -228,9 +228,12 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         }
     };
     // Phi[t] = Phi[t0 - 1] + sum_{t0 <= i <= t} dt_i theta_i for the chunk starting at c * Q, into
-    // angle buffer `out`.  The carried angle is the last row of buffer `prev` (the previous
-    // chunk), read by the same wave that wrote it and, when prev == out, before it is rewritten
-    // (one wave's LDS operations complete in order); chunk 0 starts from phi_in.
+    // angle buffer `out`, in turns (revolutions: the unit of the hardware sine and cosine).  Only
+    // the carried angle is reduced to [-1/2, 1/2]; inside a chunk the rows stay within a few turns
+    // of it, well inside the hardware sine's input range.  The carried angle is the last row of
+    // buffer `prev` (the previous chunk), read by the same wave that wrote it and, when prev ==
+    // out, before it is rewritten (one wave's LDS operations complete in order); chunk 0 starts
+    // from phi_in (radians).
     auto scan = [&](int64_t c, int out, int prev) {
         if (!scanner) return;
         float acc[SPT][VT];
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         for (int s = 0; s < SPT; ++s) {
             float f[VT];
             unpack16(rth[s], f, T{});
-            float d = bits_to_f32(rdt[s]);
+            float d = bits_to_f32(rdt[s]) * kInvTwoPi;
             if (TPV == 32) d = shfl(d, lane & 31);
 #pragma unroll
             for (int e = 0; e < VT; ++e) acc[s][e] = (s ? acc[s - 1][e] : 0.f) + d * f[e];
@@ -247,8 +250,8 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
         for (int e = 0; e < VT; ++e) {
             const int k = tv * VT + e;
-            const float carry = c == 0 ? (a.phi_in ? wrap_angle(a.phi_in[bh * K + k]) : 0.f)
-                                       : sPhi[prev * TPH + (Q - 1) * LDPHI + k];
+            const float carry = c == 0 ? (a.phi_in ? wrap_turns(a.phi_in[bh * K + k] * kInvTwoPi) : 0.f)
+                                       : wrap_turns(sPhi[prev * TPH + (Q - 1) * LDPHI + k]);
             const float tot = acc[SPT - 1][e];
             base[e] = carry + seg_scan_add<TPV>(tot, lane) - tot;
         }
@@ -257,8 +260,8 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             float* dst = sPhi + out * TPH + (tj * SPT + s) * LDPHI + tv * VT;
 #pragma unroll
             for (int e = 0; e < VT; e += 4)
-                *(floatx4*)(dst + e) = floatx4{wrap_angle(base[e] + acc[s][e]), wrap_angle(base[e + 1] + acc[s][e + 1]),
-                                               wrap_angle(base[e + 2] + acc[s][e + 2]), wrap_angle(base[e + 3] + acc[s][e + 3])};
+                *(floatx4*)(dst + e) = floatx4{base[e] + acc[s][e], base[e + 1] + acc[s][e + 1],
+                                               base[e + 2] + acc[s][e + 2], base[e + 3] + acc[s][e + 3]};
         }
     };
     // fused: raw B and C rows -> BCNorm, weight, bias, rotation -> tile buffer `buf`.  B and C go
@@ -273,20 +276,16 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         {
             const float* ph = sPhi + buf * TPH + t * LDPHI + n0 / 2;
 #pragma unroll
-            for (int q = 0; q < VE / 2; ++q) __sincosf(ph[q], &sn[q], &cs[q]);   // |angle| < 256 turns
+            for (int q = 0; q < VE / 2; ++q) {   // angles in turns
+                sn[q] = __builtin_amdgcn_sinf(ph[q]);
+                cs[q] = __builtin_amdgcn_cosf(ph[q]);
+            }
         }
         float sc[2] = {1.f, 1.f};
         if (a.bcnorm) {   // RMS over the row's N values, spread over VPN consecutive lanes
             float q2[2];
 #pragma unroll
-            for (int which = 0; which < 2; ++which) {
-                float x[VE];
-                unpack16(which == 0 ? rb[set][k] : rc[set][k], x, T{});
-                float part[4] = {0.f, 0.f, 0.f, 0.f};   // a tree, not one long chain
-#pragma unroll
-                for (int e = 0; e < VE; ++e) part[e & 3] = fmaf(x[e], x[e], part[e & 3]);
-                q2[which] = (part[0] + part[1]) + (part[2] + part[3]);
-            }
+            for (int which = 0; which < 2; ++which) q2[which] = sumsq16(which == 0 ? rb[set][k] : rc[set][k], T{});
             // the two rows' lane sums interleave
             q2[0] = group_sum(q2[0], VPN);
             q2[1] = group_sum(q2[1], VPN);
@@ -667,7 +666,8 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         if (a.x_last)
             for (int e = tid; e < R * P; e += NT) ((T*)a.x_last)[bh * R * P + e] = Xg[(L - 1) * HRP + e];
         if (FUSED && a.phi_out)
-            for (int k = tid; k < K; k += NT) a.phi_out[bh * K + k] = sPhi[lb * TPH + (Q - 1) * LDPHI + k];
+            for (int k = tid; k < K; k += NT)
+                a.phi_out[bh * K + k] = wrap_turns(sPhi[lb * TPH + (Q - 1) * LDPHI + k]) * kTwoPi;
     } else {
         // an empty sequence of a packed batch: the carry passes through unchanged
         if (a.Bbar_last)
