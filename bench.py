@@ -435,7 +435,8 @@ def time_backward(w, steps, warmup, dev):
 
 def cpu_baseline(w, inp, nheads: int):
     """The fp64 oracle (unchanged) on a bounded sample of the prefill workload: every batch row
-    and the first `nheads` heads, i.e. batch * nheads (batch, head) pairs over the full length."""
+    and the first `nheads` heads, i.e. batch * nheads (batch, head) pairs over the full length
+    (by default all heads: the whole workload, about a second of host work)."""
     import oracle
     host = {}
     for k in ("x", "B", "C", "dt", "lam", "theta"):
@@ -482,7 +483,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=256)
-    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-mimo", action="store_true")
