@@ -155,9 +155,13 @@ size_t m3_bcnorm_rope_workspace_bytes(const m3_dims* dims);
  *   Bbar_last   [b, H, R, N] io       copy of Bbar at step L-1 (for a following decode)  optional
  *   x_last      [b, H, R, P] io       copy of x at step L-1                              optional
  *   workspace   m3_prefill_workspace_bytes(dims) bytes (may be NULL when that is 0)
- * Any L >= 0 is accepted (L = 0 copies the carried state to the outputs).  dims->chunk * R
- * must be 16, 32, 48 or 64.  This build has kernels for (N, P) in {(16,16), (64,64), (128,64)}
- * and R in {1, 2, 4, 8, 16} dividing 16; other shapes return M3_E_UNSUPPORTED.
+ * Any L >= 0 is accepted (L = 0 copies the carried state to the outputs), as long as one
+ * sequence's rows of a tensor span less than 2^31 bytes: (L + 3 chunk) * H * R * max(N, P) * io
+ * size < 2^31, else M3_E_DIMS (the kernel addresses a sequence with 32-bit offsets; a longer
+ * sequence is split into calls, which the carried state and last step make exact).
+ * dims->chunk * R must be 16, 32, 48 or 64.  This build has kernels for (N, P) in {(16,16),
+ * (64,64), (128,64)} and R in {1, 2, 4, 8, 16} dividing 16; other shapes return
+ * M3_E_UNSUPPORTED.
  */
 m3_status m3_prefill(const m3_dims* dims, const void* x, const void* Bbar, const void* Cbar,
                      const void* dt, const float* A, const void* lam, const float* w_out,
@@ -187,7 +191,9 @@ size_t m3_prefill_workspace_bytes(const m3_dims* dims);
  * picks 32 / R steps per chunk.  h_out may be the h_in buffer and phi_out the phi_in buffer;
  * no other output may overlap an input.  This build has kernels for (N, P) in {(16, 16),
  * (64, 64), (128, 64)}, R in {1, 2, 4, 8, 16} and chunk * R in {16, 32, 64};
- * other shapes return M3_E_UNSUPPORTED.  No workspace is needed (pass NULL, 0).
+ * other shapes return M3_E_UNSUPPORTED.  The sequence length limit of m3_prefill applies (with
+ * the angle carried as phi_in / phi_out when a sequence is split).  No workspace is needed
+ * (pass NULL, 0).
  */
 m3_status m3_layer_prefill(const m3_dims* dims, const void* x, const void* B, const void* C,
                            const void* dt, const void* theta, const float* normw_B,
