@@ -272,7 +272,7 @@ size_t m3_bcnorm_rope_workspace_bytes(const m3_dims* d) {
     const int64_t seg = m3::bcnorm_rope_seglen();
     const int64_t nseg = (d->seqlen + seg - 1) / seg;
     if (nseg <= 1) return 0;
-    return (size_t)(d->batch * d->nheads * nseg * (d->dstate / 2)) * sizeof(float);
+    return (size_t)(d->batch * d->nheads * nseg * m3::bcnorm_rope_parts() * (d->dstate / 2)) * sizeof(float);
 }
 
 size_t m3_prefill_workspace_bytes(const m3_dims* d) {

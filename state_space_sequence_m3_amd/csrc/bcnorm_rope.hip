@@ -8,13 +8,13 @@
 // rotation by Phi_t[k] = Phi_in[k] + sum_{i<=t} dt_i theta_i[k] on each pair (2k, 2k+1).
 //
 // The angle is a prefix sum along the sequence, the only sequential part.  Long sequences are
-// cut into segments of kSegLen steps: angle_partial_kernel sums dt*theta over every segment in
-// parallel, angle_scan_kernel turns those sums into segment start angles (a scan over a few
-// dozen segments per (b, h)), and bcnorm_rope_kernel does the elementwise work with one
-// workgroup per (b, h, segment).  Inside a workgroup each wave owns a quarter of the segment;
-// the waves first sum their quarter's angle increments and exchange them through LDS, then walk
-// their quarter, carrying the angle in registers.  Angles are kept reduced to [-pi, pi] so the
-// fp32 rounding of the running sum stays at the size of one ulp of pi.
+// cut into segments of kSegLen steps, one workgroup of four waves per (b, h, segment), each wave
+// walking a quarter of the segment: angle_partial_kernel sums dt*theta over every quarter in
+// parallel, angle_scan_kernel turns those sums into quarter start angles (a scan over a few dozen
+// quarters per (b, h)) and the final angle, and bcnorm_rope_kernel does the elementwise work, each
+// wave carrying its quarter's angle in registers.  A sequence of one segment has no partial pass:
+// its waves sum their quarters' increments first and exchange them through LDS.  Angles are kept
+// reduced to [-pi, pi] so the fp32 rounding of the running sum stays at the size of one ulp of pi.
 //
 // Lane mapping: each (t, r) row of N values is split over N/8 lanes, 8 values (4 rotation
 // pairs) per lane, so one wave instruction moves 512/N whole rows.  The RMS over N is a
@@ -27,6 +27,7 @@ namespace m3 {
 namespace {
 
 constexpr int64_t kSegLen = 512;
+constexpr int kParts = 4;   // waves (quarters) per segment in the partial pass and the main pass
 
 __device__ __forceinline__ void load4(const float* p, float o[4]) {
     const float4 v = *(const float4*)p;
@@ -95,22 +96,27 @@ template <> struct Raw<float> {
     static __device__ __forceinline__ void un4(v4 v, float o[4]) { o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; }
 };
 
-// Sum of dt * theta over each segment: seg_phi[b, h, seg, :].
+// Sum of dt * theta over each quarter of each segment: seg_phi[b, h, seg, quarter, :].  Wave w
+// sums steps [t0 + w sub, t0 + (w + 1) sub) with sub = ceil(segment length / 4), the quarter the
+// main pass's wave w walks.
 template <typename T, int N>
-__global__ __launch_bounds__(256) void angle_partial_kernel(BcnormRopeArgs a) {
-    constexpr int LPR = N / 8, K = N / 2;
-    __shared__ float part[4][K];
+__global__ __launch_bounds__(64 * kParts) void angle_partial_kernel(BcnormRopeArgs a) {
+    constexpr int LPR = N / 8, RPW = 64 / LPR, K = N / 2;
     const int64_t id = blockIdx.x;
     const int seg = (int)(id % a.nseg);
     const int64_t bh = id / a.nseg;
     const int64_t b = bh / a.H;
     const int h = (int)(bh % a.H);
-    const int tid = threadIdx.x, c = tid % LPR, j = tid / LPR;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int c = lane % LPR, j = lane / LPR;
     const int64_t t0 = seg * a.seglen;
     const int64_t t1 = t0 + a.seglen < a.L ? t0 + a.seglen : a.L;
+    const int64_t sub = (t1 - t0 + kParts - 1) / kParts;
+    const int64_t w0 = t0 + wave * sub < t1 ? t0 + wave * sub : t1;
+    const int64_t w1 = w0 + sub < t1 ? w0 + sub : t1;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-    for (int64_t t = t0 + j; t < t1; t += 256 / LPR) {
+    for (int64_t t = w0 + j; t < w1; t += RPW) {
         const int64_t row = (b * a.L + t) * a.H + h;
         const float d = load_f32((const T*)a.dt + row);
         float th[4];
@@ -121,29 +127,28 @@ __global__ __launch_bounds__(256) void angle_partial_kernel(BcnormRopeArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
         for (int m = LPR; m < 64; m <<= 1) acc[q] += shfl_xor(acc[q], m);
-    const int wave = tid >> 6, lane = tid & 63;
-    if (lane < LPR) {
+    if (j == 0) {
+        float* dst = a.seg_phi + ((bh * a.nseg + seg) * kParts + wave) * K + 4 * c;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) part[wave][4 * c + q] = acc[q];
+        for (int q = 0; q < 4; ++q) dst[q] = acc[q];
     }
-    __syncthreads();
-    if (tid < K)
-        a.seg_phi[(bh * a.nseg + seg) * K + tid] =
-            part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
 }
 
-// Segment sums -> segment start angles (exclusive scan, phi_in added), in place.
+// Quarter sums -> quarter start angles (exclusive scan, phi_in added), in place; the inclusive
+// total is the final angle phi_out.
 __global__ void angle_scan_kernel(BcnormRopeArgs a) {
     const int K = a.N / 2;
     const int64_t bh = blockIdx.x;
+    const int64_t nq = (int64_t)a.nseg * kParts;
     for (int k = threadIdx.x; k < K; k += blockDim.x) {
         float run = a.phi_in ? wrap_angle(a.phi_in[bh * K + k]) : 0.0f;
-        for (int s = 0; s < a.nseg; ++s) {
-            float* p = a.seg_phi + (bh * a.nseg + s) * K + k;
+        for (int64_t s = 0; s < nq; ++s) {
+            float* p = a.seg_phi + (bh * nq + s) * K + k;
             const float v = *p;
             *p = run;
             run = wrap_angle(run + v);
         }
+        a.phi_out[bh * K + k] = run;
     }
 }
 
@@ -166,15 +171,18 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
     const int64_t w0 = t0 + wave * sub < t1 ? t0 + wave * sub : t1;
     const int64_t w1 = w0 + sub < t1 ? w0 + sub : t1;
 
-    // angle at the start of the segment, for this lane's 4 pairs
+    // angle at the start of this wave's quarter, for this lane's 4 pairs: from the partial pass
+    // (several segments), else phi_in shifted by the waves before it
+    float start[4];
+    if (a.seg_phi) {
+        static_assert(NW == 1 || NW == kParts, "quarters");
+        const float* src = a.seg_phi + ((bh * a.nseg + seg) * kParts + wave) * K + 4 * c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) start[q] = src[q];
+    } else {
     float phi[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (a.seg_phi)
-            phi[q] = a.seg_phi[(bh * a.nseg + seg) * K + 4 * c + q];
-        else
-            phi[q] = a.phi_in ? wrap_angle(a.phi_in[bh * K + 4 * c + q]) : 0.0f;
-    }
+    for (int q = 0; q < 4; ++q) phi[q] = a.phi_in ? wrap_angle(a.phi_in[bh * K + 4 * c + q]) : 0.0f;
 
     // each wave sums the angle increments of its quarter; waves before it shift its start
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
         for (int q = 0; q < 4; ++q) wsum[wave][4 * c + q] = acc[q];
     }
     __syncthreads();
-    float start[4], total[4];
+    float total[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         float s = 0.0f, tot = 0.0f;
@@ -207,9 +215,10 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
         start[q] = wrap_angle(phi[q] + s);
         total[q] = wrap_angle(phi[q] + tot);
     }
-    if (seg == a.nseg - 1 && wave == 0 && j == 0) {
+    if (wave == 0 && j == 0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) a.phi_out[bh * K + 4 * c + q] = total[q];
+    }
     }
 
     // per-lane constants: BCNorm weights for this lane's 8 columns
@@ -242,34 +251,58 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
     const T* thq = (const T*)a.theta + row_w0 * K + 4 * c;
     const T* dtq = (const T*)a.dt + row_w0;
 
-    // one block of this lane's row, prefetched (still packed) while the previous block computes
+    // blocks of RPW rows, kDepth in flight (still packed) ahead of the one being computed; slot s
+    // of the register ring holds blocks s, s + kDepth, ...
     using RW = Raw<T>;
-    typename RW::v8 nB, nC;
-    typename RW::v4 nT;
-    T nD;
-    auto load_block = [&](int64_t rho0) {
-        int64_t rho = rho0 + j;
-        if (rho >= nrows) rho = nrows - 1;   // past the end: reload the last row, result unused
-        const int64_t tl = rho / R;
-        const int r = (int)(rho % R);
-        nB = RW::ld8(Bq + tl * HRN + r * N);
-        nC = RW::ld8(Cq + tl * HRN + r * N);
-        nT = RW::ld4(thq + tl * HK);
-        nD = dtq[tl * a.H];
+    constexpr int kDepth = 3;
+    typename RW::v8 nB[kDepth], nC[kDepth];
+    typename RW::v4 nT[kDepth];
+    T nD[kDepth];
+    // A lane's row rho = rho0 + j is step tl = rho / R, rank r = rho % R of the quarter; both are
+    // carried from block to block (RPW rows further: RPW / R steps and RPW % R ranks, with a carry)
+    // instead of dividing.  Rows past the end reload the quarter's last row (result unused).
+    struct Pos { int tl, r; };
+    const int qadv = RPW / R, madv = RPW % R;
+    auto advance = [&](Pos p) {
+        p.tl += qadv;
+        p.r += madv;
+        if (p.r >= R) { p.r -= R; p.tl += 1; }
+        return p;
+    };
+    const int nrows32 = (int)nrows;   // at most kSegLen * R
+    const Pos plast = {nrows32 > 0 ? (nrows32 - 1) / R : 0, nrows32 > 0 ? (nrows32 - 1) % R : 0};
+    auto load_block = [&](int rho0, Pos p, int slot) {
+        const Pos u = rho0 + j < nrows32 ? p : plast;
+        const int64_t o = (int64_t)u.tl * HRN + u.r * N;
+        nB[slot] = RW::ld8(Bq + o);
+        nC[slot] = RW::ld8(Cq + o);
+        nT[slot] = RW::ld4(thq + (int64_t)u.tl * HK);
+        nD[slot] = dtq[(int64_t)u.tl * a.H];
     };
     float phi_acc[4] = {start[0], start[1], start[2], start[3]};
-    if (nrows > 0) load_block(0);
-    for (int64_t rho0 = 0; rho0 < nrows; rho0 += RPW) {
+    Pos pcur = {j / R, j % R}, pld = pcur;
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) {
+        if (s * RPW < nrows32) load_block(s * RPW, pld, s);
+        pld = advance(pld);
+    }
+    for (int rho_base = 0; rho_base < nrows32; rho_base += kDepth * RPW)
+#pragma unroll
+    for (int slot = 0; slot < kDepth; ++slot) {
+        const int rho0 = rho_base + slot * RPW;
+        if (rho0 >= nrows32) break;
         float vb[8], vc[8], th[4];
-        RW::un8(nB, vb);
-        RW::un8(nC, vc);
-        RW::un4(nT, th);
-        const float d = to_f32(nD);
-        if (rho0 + RPW < nrows) load_block(rho0 + RPW);
+        RW::un8(nB[slot], vb);
+        RW::un8(nC[slot], vc);
+        RW::un4(nT[slot], th);
+        const float d = to_f32(nD[slot]);
+        if (rho0 + kDepth * RPW < nrows32) load_block(rho0 + kDepth * RPW, pld, slot);
+        pld = advance(pld);
 
-        const int64_t rho = rho0 + j;
-        const bool valid = rho < nrows;
-        const int r = (int)(rho % R);
+        const Pos pc = pcur;
+        pcur = advance(pcur);
+        const bool valid = rho0 + j < nrows32;
+        const int r = pc.r;
         // angle: each step's increment enters once, on the step's first row (r == 0); an
         // inclusive prefix over the row groups gives every row the angle of its own step
         float my_phi[4];
@@ -280,7 +313,7 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
                 const float v = shfl_up(inc, o);
                 if (lane >= o) inc += v;
             }
-            my_phi[q] = wrap_angle(phi_acc[q] + inc);
+            my_phi[q] = phi_acc[q] + inc;   // within a few radians of the reduced carry
             phi_acc[q] = wrap_angle(phi_acc[q] + shfl(inc, (RPW - 1) * LPR + c));
         }
 
@@ -291,22 +324,30 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
                 sb += vb[e] * vb[e];
                 sc += vc[e] * vc[e];
             }
-            for (int m = 1; m < LPR; m <<= 1) {
-                sb += shfl_xor(sb, m);
-                sc += shfl_xor(sc, m);
-            }
+            sb = group_sum(sb, LPR);   // DPP inside the row's lanes
+            sc = group_sum(sc, LPR);
             const float ib = rsqrtf(sb * invN + a.eps), ic = rsqrtf(sc * invN + a.eps);
+            if (bias_fixed) {   // norm, weight and bias in one multiply-add
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                vb[e] *= ib * wB[e];
-                vc[e] *= ic * wC[e];
+                for (int e = 0; e < 8; ++e) {
+                    vb[e] = fmaf(vb[e], ib * wB[e], bB[e]);
+                    vc[e] = fmaf(vc[e], ic * wC[e], bC[e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    vb[e] *= ib * wB[e];
+                    vc[e] *= ic * wC[e];
+                }
             }
         }
         if (bias_fixed) {
+            if (!a.bcnorm) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                vb[e] += bB[e];
-                vc[e] += bC[e];
+                for (int e = 0; e < 8; ++e) {
+                    vb[e] += bB[e];
+                    vc[e] += bC[e];
+                }
             }
         } else {
             if (a.bias_B) {
@@ -326,14 +367,14 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             float s, co;
-            __sincosf(my_phi[q], &s, &co);   // |angle| <= pi after reduction
+            __sincosf(my_phi[q], &s, &co);
             ob[2 * q] = co * vb[2 * q] + s * vb[2 * q + 1];
             ob[2 * q + 1] = -s * vb[2 * q] + co * vb[2 * q + 1];
             oc[2 * q] = co * vc[2 * q] + s * vc[2 * q + 1];
             oc[2 * q + 1] = -s * vc[2 * q] + co * vc[2 * q + 1];
         }
         if (valid) {
-            const int64_t off = (rho / R) * HRN + r * N;
+            const int64_t off = (int64_t)pc.tl * HRN + pc.r * N;
             store8(Bo + off, ob);
             store8(Co + off, oc);
         }
@@ -344,7 +385,7 @@ template <typename T, int N>
 hipError_t launch_n(const BcnormRopeArgs& a, hipStream_t s) {
     const unsigned nbh = (unsigned)(a.b * a.H);
     if (a.nseg > 1) {
-        hipLaunchKernelGGL((angle_partial_kernel<T, N>), dim3(nbh * a.nseg), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((angle_partial_kernel<T, N>), dim3(nbh * a.nseg), dim3(64 * kParts), 0, s, a);
         hipLaunchKernelGGL(angle_scan_kernel, dim3(nbh), dim3(N / 2 < 64 ? 64 : N / 2), 0, s, a);
     }
     // a single-wave workgroup when the segment has too few rows to share among four waves
@@ -375,6 +416,7 @@ bool bcnorm_rope_supported(int N, int R) {
 }
 
 int64_t bcnorm_rope_seglen() { return kSegLen; }
+int bcnorm_rope_parts() { return kParts; }
 
 hipError_t launch_bcnorm_rope(const BcnormRopeArgs& a, bool bf16_io, hipStream_t s) {
     return bf16_io ? launch_t<bf16>(a, s) : launch_t<float>(a, s);

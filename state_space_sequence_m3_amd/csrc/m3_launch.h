@@ -45,7 +45,7 @@ struct BcnormRopeArgs {
     const float* bias_B;
     const float* bias_C;
     const float* phi_in;
-    float* seg_phi;       // [b, H, nseg, N/2] segment start angles (nseg > 1), else nullptr
+    float* seg_phi;       // [b, H, nseg, parts, N/2] quarter start angles (nseg > 1), else nullptr
     void* Bbar;
     void* Cbar;
     float* phi_out;
@@ -155,6 +155,7 @@ hipError_t launch_layer_decode(const DecodeArgs& a, bool bf16_io, hipStream_t s)
 
 bool bcnorm_rope_supported(int N, int R);
 int64_t bcnorm_rope_seglen();
+int bcnorm_rope_parts();   // quarters per segment: the workspace holds one angle row per quarter
 hipError_t launch_bcnorm_rope(const BcnormRopeArgs& a, bool bf16_io, hipStream_t s);
 
 bool prefill_supported(int N, int P, int R, int QR, bool bf16_io);

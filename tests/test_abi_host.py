@@ -134,7 +134,8 @@ def test_bcnorm_rope_errors():
     assert call(d, q) == m3scan.M3_E_NULL
     assert call(_dims(dstate=96), p) == m3scan.M3_E_UNSUPPORTED
     long = _dims(seqlen=4096)
-    assert m3scan.bcnorm_rope_workspace_bytes(long) == 2 * 3 * 8 * 64 * 4
+    # one angle row of N/2 floats per quarter of each 512-step segment
+    assert m3scan.bcnorm_rope_workspace_bytes(long) == 2 * 3 * 8 * 4 * 64 * 4
     assert call(long, p) == m3scan.M3_E_WORKSPACE
     q = list(p)
     q[9] = q[0]
@@ -168,7 +169,7 @@ def test_decode_errors():
 def test_workspace_sizes():
     assert m3scan.prefill_workspace_bytes(_dims()) == 0
     assert m3scan.bcnorm_rope_workspace_bytes(_dims(seqlen=512)) == 0
-    assert m3scan.bcnorm_rope_workspace_bytes(_dims(seqlen=513)) == 2 * 3 * 2 * 64 * 4
+    assert m3scan.bcnorm_rope_workspace_bytes(_dims(seqlen=513)) == 2 * 3 * 2 * 4 * 64 * 4
 
 
 def test_binding_raises_without_the_library(tmp_path, monkeypatch):
