@@ -193,6 +193,20 @@ def test_layer_decode_parity(R, io, normw):
     assert rel_err(Blast, state["Bbar_prev"]) <= TOL[io]
 
 
+@pytest.mark.parametrize("R,io,dstate", [(1, "bf16", 128), (4, "bf16", 128), (2, "f32", 64)])
+def test_layer_decode_many_pairs_per_workgroup(R, io, dstate):
+    """More (batch, head) pairs than the GPU holds decode workgroups at once, with an odd head
+    count: the grid is then a multiple of H below the pair count and every workgroup serves
+    several pairs of one head in turn, loading the next pair while it updates the current one."""
+    base = inputs.WORKLOADS["decode_b128_r4" if R > 1 else "decode_b128_r1"]
+    w = base.with_(batch=300, nheads=7, rank=R, io=io, dstate=dstate)
+    ys, h, phi, Blast, rys, state = _fused_decode_run(w, 3, seed=61 + R, mix=w.mix, normw=True)
+    assert rel_err(torch.stack(ys, 0), np.stack(rys, 0)) <= TOL[io]
+    assert rel_err(h, state["h"]) <= TOL[io]
+    assert angle_err(phi, state["phi"]) <= (1e-4 if io == "f32" else 1e-3)
+    assert rel_err(Blast, state["Bbar_prev"]) <= TOL[io]
+
+
 def test_layer_prefill_then_layer_decode_continue_the_sequence():
     """m3_layer_prefill over 0..L-k then k m3_layer_decode_step calls equal the oracle's layer
     core over 0..L, token by token."""

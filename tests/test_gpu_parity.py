@@ -318,6 +318,15 @@ def test_decode_parity(R):
     assert angle_err(phi, state["phi"]) <= 1e-4
 
 
+def test_decode_many_pairs_per_workgroup():
+    """m3_decode_step with more (batch, head) pairs than resident workgroups and an odd H (each
+    workgroup updates several pairs of one head in turn)."""
+    w = inputs.WORKLOADS["decode_b128_r4"].with_(batch=300, nheads=7)
+    ys, h, phi, rys, state = _decode_run(w, 3, seed=71, mix=w.mix)
+    assert rel_err(torch.stack(ys, 0), np.stack(rys, 0)) <= TOL["bf16"]
+    assert rel_err(h, state["h"]) <= TOL["bf16"]
+
+
 def test_decode_fp32_parity():
     w = inputs.WORKLOADS["decode_b128_r1"].with_(batch=2, nheads=3, io="f32")
     ys, h, phi, rys, state = _decode_run(w, 10, seed=41, mix=False)
