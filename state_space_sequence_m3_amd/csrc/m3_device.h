@@ -89,6 +89,36 @@ __device__ __forceinline__ float seg_scan_add(float v, int lane) {
     if (W >= 64) v += dpp_move<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
     return v;
 }
+// Exclusive sum over runs of W lanes (run r = lanes [r W, (r + 1) W), column j = lane % W): the
+// sum of v over runs r' < r in lane (r, j).  W = 64, 32, 16 or 8.  Inside a 16-lane row by DPP
+// shifts; across rows by gfx950's swaps, all in VALU (no LDS crossbar): v_permlane16_swap applied
+// to (v, v) gives rows (0, 0, 2, 2) and (1, 1, 3, 3) of v, v_permlane32_swap rows (0, 1, 0, 1) and
+// (2, 3, 2, 3).
+__device__ __forceinline__ float rows_exclusive_sum(float v, int lane) {   // runs = rows (W = 16)
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float below = __uint_as_float(p[0]);                       // row r - 1 in odd rows
+    const float pair = below + __uint_as_float(p[1]);                // rows 2q + 2q+1, in both
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+    return ((lane & 16) ? below : 0.f) + (lane >= 32 ? __uint_as_float(h[0]) : 0.f);
+}
+template <int W>
+__device__ __forceinline__ float run_exclusive_sum(float v, int lane) {
+    static_assert(W == 8 || W == 16 || W == 32 || W == 64, "run width");
+    if constexpr (W == 64) {
+        return 0.f;
+    } else if constexpr (W == 32) {
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return lane >= 32 ? __uint_as_float(h[0]) : 0.f;
+    } else if constexpr (W == 16) {
+        return rows_exclusive_sum(v, lane);
+    } else {
+        // two runs per row: the upper run takes the lower one's value (row_shr:8), and the row's
+        // total for each column is v plus its partner (row_shr:8 + row_shl:8, zero outside the row)
+        const float lo = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+        const float hi = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x108, 0xf, 0xf, true));
+        return lo + rows_exclusive_sum(v + lo + hi, lane);
+    }
+}
 __device__ __forceinline__ float lane_value(float v, int src_lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_lane));
 }
@@ -104,6 +134,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 __device__ __forceinline__ uint4 buffer_load16(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+// The same for data read exactly once (a streamed input): non-temporal, so that it does not
+// displace lines that stay in use in L2 (among them the output rows being written back).
+__device__ __forceinline__ uint4 buffer_load16_stream(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
 }
 __device__ __forceinline__ void buffer_store8(rsrc_t r, uint32_t off, uint2 v) {
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, 0);

@@ -87,7 +87,14 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     constexpr int K = N / 2, VT = VE, NVT = K / VT;
     constexpr int SPT = NVT * QR > NT ? NVT * QR / NT : 1, TPV = FUSED ? QR / SPT : 16;
     static_assert(!FUSED || (TPV <= 64 && NVT * TPV <= NT && (QR & (QR - 1)) == 0), "angle scan layout");
-    constexpr int LDPHI = K + 8;                 // padded angle rows (fp32)
+    // padded angle rows (fp32): with K + 12 the column walk of the scan (runs of 2 or 8 steps)
+    // and the row writes of its first phase reach distinct banks
+    constexpr int LDPHI = K + 12;
+    // the scan's column walk: wave w owns angle columns [w KWL, (w + 1) KWL) (the columns its
+    // lanes load), lane = column j + KWL * run r, run r covers steps r SRUN .. r SRUN + SRUN - 1
+    constexpr int KWL = FUSED ? (VT * 64 / TPV < K ? VT * 64 / TPV : K) : 64;
+    constexpr int NW2 = FUSED ? K / KWL : 0, SEGW = 64 / KWL, SRUN = (QR + SEGW - 1) / SEGW;
+    static_assert(!FUSED || (NW2 <= NW && KWL >= 8 && KWL * SEGW == 64 && SRUN * SEGW <= QR), "column walk layout");
     constexpr int FZ = FUSED ? 1 : 0;            // sizes the fused-only LDS arrays
     constexpr int TC = QR * LDC, TB = QR * LDB, TX = QR * LDX, TM = QR * LDM, TPH = QR * LDPHI;
 
@@ -174,19 +181,19 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             const uint32_t o = step_off(t0, HRN);
 #pragma unroll
             for (int k = 0; k < MAXC; ++k)
-                if (FULLC || iC0 + k * RKC < QR) rc[set][k] = buffer_load16(dCs, offC(k) + o);
+                if (FULLC || iC0 + k * RKC < QR) rc[set][k] = buffer_load16_stream(dCs, offC(k) + o);
         }
         if (part < 0 || part == 1) {
             const uint32_t o = step_off(t0, HRN);
 #pragma unroll
             for (int k = 0; k < MAXC; ++k)
-                if (FULLC || iC0 + k * RKC < QR) rb[set][k] = buffer_load16(dBs, offC(k) + o);
+                if (FULLC || iC0 + k * RKC < QR) rb[set][k] = buffer_load16_stream(dBs, offC(k) + o);
         }
         if (part < 0 || part == 2) {
             const uint32_t o = step_off(t0, HRP);
 #pragma unroll
             for (int k = 0; k < MAXX; ++k)
-                if (FULLX || iX0 + k * RKX < QR) rx[set][k] = buffer_load16(dXs, offX(k) + o);
+                if (FULLX || iX0 + k * RKX < QR) rx[set][k] = buffer_load16_stream(dXs, offX(k) + o);
         }
         if (part < 0 || part == 3) {
             // steps t0 + lane and t0 + lane + 1; zero past the sequence end.  Lanes at or past Q
@@ -230,38 +237,47 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // Phi[t] = Phi[t0 - 1] + sum_{t0 <= i <= t} dt_i theta_i for the chunk starting at c * Q, into
     // angle buffer `out`, in turns (revolutions: the unit of the hardware sine and cosine).  Only
     // the carried angle is reduced to [-1/2, 1/2]; inside a chunk the rows stay within a few turns
-    // of it, well inside the hardware sine's input range.  The carried angle is the last row of
-    // buffer `prev` (the previous chunk), read by the same wave that wrote it and, when prev ==
-    // out, before it is rewritten (one wave's LDS operations complete in order); chunk 0 starts
-    // from phi_in (radians).
+    // of it, well inside the hardware sine's input range.  Two phases, both inside each wave's
+    // own columns (so no barrier): the loading lanes write the increments dt_t theta_t[k] to the
+    // rows, then lane (j, r) walks run r of column j, a serial sum of SRUN rows, and the runs'
+    // totals are chained across the wave's runs by lane swaps.  Rows past the chunk's steps
+    // hold zero increments (their loads aim past the descriptor), so a run that covers them ends
+    // on the last step's angle.  The carried angle is the last row of buffer `prev` (the previous
+    // chunk), read first: without pipelining prev == out.  Chunk 0 starts from phi_in (radians).
+    const int kcol = wave * KWL + (lane & (KWL - 1)), run = lane / KWL;
     auto scan = [&](int64_t c, int out, int prev) {
-        if (!scanner) return;
-        float acc[SPT][VT];
+        if (!FUSED) return;
+        const bool colwave = wave < NW2;
+        float carry = 0.f;
+        if (colwave)
+            carry = c == 0 ? (a.phi_in ? wrap_turns(a.phi_in[bh * K + kcol] * kInvTwoPi) : 0.f)
+                           : wrap_turns(sPhi[prev * TPH + (Q - 1) * LDPHI + kcol]);
+        float* ph = sPhi + out * TPH;
+        if (scanner) {
 #pragma unroll
-        for (int s = 0; s < SPT; ++s) {
-            float f[VT];
-            unpack16(rth[s], f, T{});
-            float d = bits_to_f32(rdt[s]) * kInvTwoPi;
-            if (TPV == 32) d = shfl(d, lane & 31);
+            for (int s = 0; s < SPT; ++s) {
+                float f[VT];
+                unpack16(rth[s], f, T{});
+                float d = bits_to_f32(rdt[s]) * kInvTwoPi;
+                if (TPV == 32) d = shfl(d, lane & 31);
+                float* dst = ph + (tj * SPT + s) * LDPHI + tv * VT;
 #pragma unroll
-            for (int e = 0; e < VT; ++e) acc[s][e] = (s ? acc[s - 1][e] : 0.f) + d * f[e];
+                for (int e = 0; e < VT; e += 4)
+                    *(floatx4*)(dst + e) = floatx4{d * f[e], d * f[e + 1], d * f[e + 2], d * f[e + 3]};
+            }
         }
-        float base[VT];
+        if (colwave) {
+            float* col = ph + run * SRUN * LDPHI + kcol;
+            // every read goes out before the first sum waits on one
+            float acc[SRUN];
 #pragma unroll
-        for (int e = 0; e < VT; ++e) {
-            const int k = tv * VT + e;
-            const float carry = c == 0 ? (a.phi_in ? wrap_turns(a.phi_in[bh * K + k] * kInvTwoPi) : 0.f)
-                                       : wrap_turns(sPhi[prev * TPH + (Q - 1) * LDPHI + k]);
-            const float tot = acc[SPT - 1][e];
-            base[e] = carry + seg_scan_add<TPV>(tot, lane) - tot;
-        }
+            for (int s = 0; s < SRUN; ++s) acc[s] = col[s * LDPHI];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < SPT; ++s) {
-            float* dst = sPhi + out * TPH + (tj * SPT + s) * LDPHI + tv * VT;
+            for (int s = 1; s < SRUN; ++s) acc[s] += acc[s - 1];
+            const float base = carry + run_exclusive_sum<KWL>(acc[SRUN - 1], lane);
 #pragma unroll
-            for (int e = 0; e < VT; e += 4)
-                *(floatx4*)(dst + e) = floatx4{base[e] + acc[s][e], base[e + 1] + acc[s][e + 1],
-                                               base[e + 2] + acc[s][e + 2], base[e + 3] + acc[s][e + 3]};
+            for (int s = 0; s < SRUN; ++s) col[s * LDPHI] = base + acc[s];
         }
     };
     // fused: raw B and C rows -> BCNorm, weight, bias, rotation -> tile buffer `buf`.  B and C go
@@ -625,10 +641,15 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             auto after = [&]() {};
             chunk_compute(p, c, hook, after);
         };
-        for (int64_t c = 0; c < nchunk; c += 2) {
+        // whole pairs in the loop and an odd last chunk after it: a pair whose second half could be
+        // skipped would give the loop head a path on which the compiler must assume few memory
+        // operations since the last half's loads, and it would wait for nearly all of them there
+        int64_t c = 0;
+        for (; c + 1 < nchunk; c += 2) {
             iter(std::integral_constant<int, 0>{}, c);
-            if (c + 1 < nchunk) iter(std::integral_constant<int, 1>{}, c + 1);
+            iter(std::integral_constant<int, 1>{}, c + 1);
         }
+        if (c < nchunk) iter(std::integral_constant<int, 0>{}, c);
     } else {
         for (int64_t c = 0; c < nchunk; ++c) {
 #pragma unroll
