@@ -212,10 +212,10 @@ __global__ __launch_bounds__(NIB * 64, 1) void chunk_states_kernel(BackwardArgs 
             const rsrc_t dX = make_rsrc(Xg + t0 * HRP, tail_bytes(t0, HRP, (int64_t)R * P));
 #pragma unroll
             for (int k = 0; k < MAXC; ++k)
-                rb[k] = buffer_load16(dB, S::FULLC || iC0 + k * RKC < QR ? offC(k) : 0x80000000u);
+                rb[k] = buffer_load16_stream(dB, S::FULLC || iC0 + k * RKC < QR ? offC(k) : 0x80000000u);
 #pragma unroll
             for (int k = 0; k < MAXX; ++k)
-                rx[k] = buffer_load16(dX, S::FULLX || iX0 + k * RKX < QR ? offX(k) : 0x80000000u);
+                rx[k] = buffer_load16_stream(dX, S::FULLX || iX0 + k * RKX < QR ? offX(k) : 0x80000000u);
         }
         uint4 rth[SPT];
         Bits rdt[SPT];
@@ -500,14 +500,14 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
 #pragma unroll
             for (int k = 0; k < MAXC; ++k) {
                 const bool in = S::FULLC || iC0 + k * RKC < QR;
-                rb[k] = buffer_load16(dB, in ? offC(k) : 0x80000000u);
-                rc[k] = buffer_load16(dC, in ? offC(k) : 0x80000000u);
+                rb[k] = buffer_load16_stream(dB, in ? offC(k) : 0x80000000u);
+                rc[k] = buffer_load16_stream(dC, in ? offC(k) : 0x80000000u);
             }
 #pragma unroll
             for (int k = 0; k < MAXX; ++k) {
                 const bool in = S::FULLX || iX0 + k * RKX < QR;
-                rx[k] = buffer_load16(dX, in ? offX(k) : 0x80000000u);
-                ry[k] = buffer_load16(dYr, in ? offY(k) : 0x80000000u);
+                rx[k] = buffer_load16_stream(dX, in ? offX(k) : 0x80000000u);
+                ry[k] = buffer_load16_stream(dYr, in ? offY(k) : 0x80000000u);
             }
 #pragma unroll
             for (int k = 0; k < MAXS; ++k) {

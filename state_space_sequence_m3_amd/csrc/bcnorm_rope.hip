@@ -68,7 +68,15 @@ template <> struct Raw<bf16> {
     typedef uint4 v8;
     typedef uint2 v4;
     static __device__ __forceinline__ v8 ld8(const bf16* p) { return *(const uint4*)p; }
+    // read-once rows (B, C): non-temporal, so that they do not displace the output rows in L2
+    static __device__ __forceinline__ v8 ld8s(const bf16* p) {
+        return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)p));
+    }
     static __device__ __forceinline__ v4 ld4(const bf16* p) { return *(const uint2*)p; }
+    static __device__ __forceinline__ v4 ld4s(const bf16* p) {
+        typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint2, __builtin_nontemporal_load((const u32x2v*)p));
+    }
     static __device__ __forceinline__ void un8(v8 v, float o[8]) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -88,7 +96,12 @@ template <> struct Raw<float> {
     struct v8 { float4 a, b; };
     typedef float4 v4;
     static __device__ __forceinline__ v8 ld8(const float* p) { return v8{((const float4*)p)[0], ((const float4*)p)[1]}; }
+    static __device__ __forceinline__ v8 ld8s(const float* p) {
+        return v8{__builtin_bit_cast(float4, __builtin_nontemporal_load((const floatx4*)p)),
+                  __builtin_bit_cast(float4, __builtin_nontemporal_load((const floatx4*)p + 1))};
+    }
     static __device__ __forceinline__ v4 ld4(const float* p) { return *(const float4*)p; }
+    static __device__ __forceinline__ v4 ld4s(const float* p) { return __builtin_bit_cast(float4, __builtin_nontemporal_load((const floatx4*)p)); }
     static __device__ __forceinline__ void un8(v8 v, float o[8]) {
         o[0] = v.a.x; o[1] = v.a.y; o[2] = v.a.z; o[3] = v.a.w;
         o[4] = v.b.x; o[5] = v.b.y; o[6] = v.b.z; o[7] = v.b.w;
@@ -274,9 +287,9 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
     auto load_block = [&](int rho0, Pos p, int slot) {
         const Pos u = rho0 + j < nrows32 ? p : plast;
         const int64_t o = (int64_t)u.tl * HRN + u.r * N;
-        nB[slot] = RW::ld8(Bq + o);
-        nC[slot] = RW::ld8(Cq + o);
-        nT[slot] = RW::ld4(thq + (int64_t)u.tl * HK);
+        nB[slot] = RW::ld8s(Bq + o);
+        nC[slot] = RW::ld8s(Cq + o);
+        nT[slot] = RW::ld4s(thq + (int64_t)u.tl * HK);
         nD[slot] = dtq[(int64_t)u.tl * a.H];
     };
     float phi_acc[4] = {start[0], start[1], start[2], start[3]};

@@ -196,14 +196,14 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
                 if (FULLX || iX0 + k * RKX < QR) rx[set][k] = buffer_load16_stream(dXs, offX(k) + o);
         }
         if (part < 0 || part == 3) {
-            // steps t0 + lane and t0 + lane + 1; zero past the sequence end.  Lanes at or past Q
-            // read the next chunk's values, which only reach scan lanes that are never read.  Only
-            // the last wave uses them; the other waves issue the same loads aimed past the
-            // descriptor (no memory access), so that the number of loads in flight is the same on
-            // every path and the compiler's wait counts stay exact.
-            // Step t0 + lane + 1 is the next lane's value; only lane 63 loads it.
-            const uint32_t o0 = wave == NW - 1 ? (uint32_t)(lane * H * (int)sizeof(T)) + step_off(t0, H) : 0x80000000u;
-            const uint32_t o1 = wave == NW - 1 && lane == 63 ? o0 + (uint32_t)(H * (int)sizeof(T)) : 0x80000000u;
+            // steps t0 + lane and t0 + lane + 1; zero past the sequence end.  Only lanes 0..Q are
+            // read (lane Q holds the step after the chunk); the other lanes, and the waves other
+            // than the last, issue the same loads aimed past the descriptor (no memory access),
+            // so that the number of loads in flight is the same on every path and the
+            // compiler's wait counts stay exact.  Step t0 + lane + 1 is the next lane's value;
+            // lane 63 loads its own only for 64-step chunks.
+            const uint32_t o0 = wave == NW - 1 && lane <= Q ? (uint32_t)(lane * H * (int)sizeof(T)) + step_off(t0, H) : 0x80000000u;
+            const uint32_t o1 = wave == NW - 1 && lane == 63 && Q == 64 ? o0 + (uint32_t)(H * (int)sizeof(T)) : 0x80000000u;
             nd[set] = buffer_load_bits(dDs, o0, T{});
             nl[set] = buffer_load_bits(dLs, o0, T{});
             ndn[set] = buffer_load_bits(dDs, o1, T{});
