@@ -206,8 +206,12 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             const uint32_t o1 = wave == NW - 1 && lane == 63 && Q == 64 ? o0 + (uint32_t)(H * (int)sizeof(T)) : 0x80000000u;
             nd[set] = buffer_load_bits(dDs, o0, T{});
             nl[set] = buffer_load_bits(dLs, o0, T{});
-            ndn[set] = buffer_load_bits(dDs, o1, T{});
-            nln[set] = buffer_load_bits(dLs, o1, T{});
+            if constexpr (QR == 64) {   // only a 64-step chunk reads past lane 63
+                ndn[set] = buffer_load_bits(dDs, o1, T{});
+                nln[set] = buffer_load_bits(dLs, o1, T{});
+            } else {
+                ndn[set] = nln[set] = Bits{};
+            }
         }
     };
     // ---- fused: angle increments of a chunk and their prefix scan ----------------------
