@@ -154,7 +154,16 @@ size_t m3_bcnorm_rope_workspace_bytes(const m3_dims* dims);
  *   h_out       [b, H, N, P] f32      final state g_{L-1} (may be the same buffer as h_in) required
  *   Bbar_last   [b, H, R, N] io       copy of Bbar at step L-1 (for a following decode)  optional
  *   x_last      [b, H, R, P] io       copy of x at step L-1                              optional
- *   workspace   m3_prefill_workspace_bytes(dims) bytes (may be NULL when that is 0)
+ *   workspace   m3_prefill_workspace_bytes(dims) bytes, 16-byte aligned, or NULL        optional
+ * With a workspace, a call with few (b, h) pairs (fewer than two per compute unit) and long
+ * sequences splits each sequence into segments of a multiple of 512 steps that run in parallel:
+ * pass 1 gives every segment's end state from a zero carry (segment 0 from the call's carry),
+ * a small kernel chains them (the recurrence is linear in its carry: the end state of segment s
+ * is its own end state plus the incoming state decayed by exp(A sum of dt over the segment)),
+ * and pass 2 reruns segments 1, 2, ... from their true carries.  The results are those of one
+ * pass up to rounding order.  m3_prefill_workspace_bytes returns 0 when no split would be used;
+ * with NULL the call always runs one pass per sequence.  A non-NULL workspace smaller than the
+ * returned size is M3_E_WORKSPACE; one that overlaps any argument is M3_E_ALIAS.
  * Any L >= 0 is accepted (L = 0 copies the carried state to the outputs), as long as one
  * sequence's rows of a tensor span less than 2^31 bytes: (L + 3 chunk) * H * R * max(N, P) * io
  * size < 2^31, else M3_E_DIMS (the kernel addresses a sequence with 32-bit offsets; a longer
@@ -169,7 +178,8 @@ m3_status m3_prefill(const m3_dims* dims, const void* x, const void* Bbar, const
                      float* h_out, void* Bbar_last, void* x_last, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of device workspace m3_prefill needs for these dims. */
+/* Bytes of device workspace m3_prefill uses for these dims on the current device (0: it does
+ * not split them).  The split depends on the device's compute-unit count. */
 size_t m3_prefill_workspace_bytes(const m3_dims* dims);
 
 /*
@@ -192,8 +202,10 @@ size_t m3_prefill_workspace_bytes(const m3_dims* dims);
  * no other output may overlap an input.  This build has kernels for (N, P) in {(16, 16),
  * (64, 64), (128, 64)}, R in {1, 2, 4, 8, 16} and chunk * R in {16, 32, 64};
  * other shapes return M3_E_UNSUPPORTED.  The sequence length limit of m3_prefill applies (with
- * the angle carried as phi_in / phi_out when a sequence is split).  No workspace is needed
- * (pass NULL, 0).
+ * the angle carried as phi_in / phi_out when a sequence is split).  The workspace (optional,
+ * m3_layer_prefill_workspace_bytes(dims) bytes, 16-byte aligned) enables the sequence split of
+ * m3_prefill; the segments' start angles then come from the sums of dt * theta per 512 steps, as
+ * m3_bcnorm_rope computes them.  Workspace errors as m3_prefill.
  */
 m3_status m3_layer_prefill(const m3_dims* dims, const void* x, const void* B, const void* C,
                            const void* dt, const void* theta, const float* normw_B,
@@ -203,6 +215,10 @@ m3_status m3_layer_prefill(const m3_dims* dims, const void* x, const void* B, co
                            const void* x_prev, void* y, float* h_out, float* phi_out,
                            void* Bbar_last, void* x_last, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace m3_layer_prefill uses for these dims on the current device (0: it
+ * does not split them). */
+size_t m3_layer_prefill_workspace_bytes(const m3_dims* dims);
 
 /*
  * m3_decode_step -- one new token for each of b * H resident states, updated in place.

@@ -125,6 +125,107 @@ hipError_t copy_or_zero(void* dst, const void* src, size_t bytes, hipStream_t s)
     return hipGetLastError();
 }
 
+// Compute units of the current device (256 when there is none to ask), cached per device.
+std::atomic<int> g_cus[256];
+int device_cus() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return 256;
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Sequence split of a prefill call (m3_prefill, m3_layer_prefill): when the (b, h) pairs are too
+// few to give every compute unit two workgroups, each sequence is cut into segments of a
+// multiple of 512 steps (at least 1024 each) that run in parallel, then are chained (see
+// PrefillArgs).  Workspace: the segments' end states, the rotated Bbar of their last steps and,
+// fused, the start angles of every 512-step angle segment and a final-angle scratch row.
+struct SplitPlan {
+    int nseg = 1;
+    int64_t seglen = 0, nsegA = 0;
+    size_t off_state = 0, off_bbar = 0, off_phi = 0, off_phiend = 0, total = 0;
+};
+constexpr int64_t kSplitAlign = 512, kSplitMin = 1024;
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+SplitPlan split_plan(const m3_dims* d, int64_t Q, bool fused, bool packed) {
+    SplitPlan sp;
+    const int64_t b = d->batch, L = d->seqlen, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
+    const int64_t pairs = b * H, target = 2 * (int64_t)device_cus();
+    if (packed || pairs <= 0 || pairs >= target || Q <= 0 || kSplitAlign % Q != 0) return sp;
+    int64_t nseg = (target + pairs - 1) / pairs;
+    if (nseg > L / kSplitMin) nseg = L / kSplitMin;
+    if (nseg < 2) return sp;
+    int64_t seglen = (L + nseg - 1) / nseg;
+    seglen = (seglen + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+    nseg = (L + seglen - 1) / seglen;
+    if (nseg < 2) return sp;
+    sp.nseg = (int)nseg;
+    sp.seglen = seglen;
+    const size_t es = d->io == M3_BF16 ? 2 : 4;
+    sp.off_state = 0;
+    sp.off_bbar = align256((size_t)(pairs * nseg * N * P) * 4);
+    sp.total = sp.off_bbar + align256((size_t)(pairs * nseg * R * N) * es);
+    if (fused) {
+        sp.nsegA = (L + m3::bcnorm_rope_seglen() - 1) / m3::bcnorm_rope_seglen();
+        sp.off_phi = sp.total;
+        sp.off_phiend = sp.off_phi + align256((size_t)(pairs * sp.nsegA * m3::bcnorm_rope_parts() * (N / 2)) * 4);
+        sp.total = sp.off_phiend + align256((size_t)(pairs * (N / 2)) * 4);
+    }
+    return sp;
+}
+
+// The workspace a split call uses: NULL (or a split that does not pay) runs one pass; otherwise it
+// must hold the plan's bytes, be 16-byte aligned and overlap none of the call's buffers.
+m3_status check_split_workspace(const SplitPlan& sp, const void* ws, size_t ws_bytes, const Buf* bufs, int n,
+                                const char* fn) {
+    if (!ws || sp.nseg < 2) return M3_OK;
+    if (ws_bytes < sp.total)
+        return fail(M3_E_WORKSPACE, "%s needs %zu workspace bytes, got %zu", fn, sp.total, ws_bytes);
+    if (!aligned(ws, 16)) return fail(M3_E_ALIGN, "workspace is not 16-byte aligned");
+    for (int i = 0; i < n; ++i)
+        if (overlap(ws, sp.total, bufs[i].p, bufs[i].bytes)) return fail(M3_E_ALIAS, "workspace overlaps %s", bufs[i].name);
+    return M3_OK;
+}
+
+// pass 1, chaining, pass 2 of a split prefill (fused: after the angle pass)
+hipError_t run_split(m3::PrefillArgs a, const SplitPlan& sp, void* ws, bool fused, bool bf16, hipStream_t s) {
+    char* w = (char*)ws;
+    a.nseg = sp.nseg;
+    a.seglen = sp.seglen;
+    a.ws_state = (float*)(w + sp.off_state);
+    a.ws_bbar = w + sp.off_bbar;
+    hipError_t e = hipSuccess;
+    if (fused) {
+        m3::BcnormRopeArgs g{};
+        g.dt = a.dt;
+        g.theta = a.theta;
+        g.phi_in = a.phi_in;
+        g.seg_phi = (float*)(w + sp.off_phi);
+        g.phi_out = (float*)(w + sp.off_phiend);
+        g.b = a.b;
+        g.L = a.L;
+        g.H = a.H;
+        g.N = a.N;
+        g.R = a.R;
+        g.seglen = m3::bcnorm_rope_seglen();
+        g.nseg = (int)sp.nsegA;
+        e = m3::launch_segment_angles(g, bf16, s);
+        a.seg_phi = g.seg_phi;
+        a.angle_seglen = g.seglen;
+        a.angle_parts = m3::bcnorm_rope_parts();
+    }
+    a.pass = 1;
+    if (e == hipSuccess) e = fused ? m3::launch_layer(a, bf16, s) : m3::launch_prefill(a, bf16, s);
+    if (e == hipSuccess && sp.nseg > 2) e = m3::launch_segment_combine(a, bf16, s);
+    a.pass = 2;
+    if (e == hipSuccess) e = fused ? m3::launch_layer(a, bf16, s) : m3::launch_prefill(a, bf16, s);
+    return e;
+}
+
 }  // namespace
 
 namespace {
@@ -136,7 +237,7 @@ m3_status layer_prefill(const m3_dims* d, bool packed, const int32_t* cu_seqlens
                         const float* bias_B, const float* bias_C, const float* A, const void* lam,
                         const float* w_out, const float* phi_in, const float* h_in, const void* Bbar_prev,
                         const void* x_prev, void* y, float* h_out, float* phi_out, void* Bbar_last, void* x_last,
-                        hipStream_t stream, const char* fn) {
+                        void* workspace, size_t workspace_bytes, hipStream_t stream, const char* fn) {
     m3_status s = check_common_dims(d);
     if (s != M3_OK) return s;
     const int64_t b = d->batch, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
@@ -226,6 +327,15 @@ m3_status layer_prefill(const m3_dims* d, bool packed, const int32_t* cu_seqlens
         a.T = L;
         a.L = 0;
     }
+    const SplitPlan sp = split_plan(d, Q, true, packed);
+    const Buf all[] = {{x, nX, "x"}, {B, nBC, "B"}, {C, nBC, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
+                       {A, nA, "A"}, {lam, nStep, "lam"}, {w_out, nWo, "w_out"}, {normw_B, nW, "normw_B"},
+                       {normw_C, nW, "normw_C"}, {bias_B, nBias, "bias_B"}, {bias_C, nBias, "bias_C"},
+                       {Bbar_prev, nBp, "Bbar_prev"}, {x_prev, nXp, "x_prev"}, {y, nY, "y"}, {h_out, nH, "h_out"},
+                       {phi_out, nPhi, "phi_out"}, {Bbar_last, nBp, "Bbar_last"}, {x_last, nXp, "x_last"},
+                       {h_in, nH, "h_in"}, {phi_in, nPhi, "phi_in"}};
+    if ((s = check_split_workspace(sp, workspace, workspace_bytes, all, 21, fn)) != M3_OK) return s;
+    if (workspace && sp.nseg >= 2) return launched(run_split(a, sp, workspace, true, d->io == M3_BF16, stream), fn);
     return launched(m3::launch_layer(a, d->io == M3_BF16, stream), fn);
 }
 
@@ -276,8 +386,15 @@ size_t m3_bcnorm_rope_workspace_bytes(const m3_dims* d) {
 }
 
 size_t m3_prefill_workspace_bytes(const m3_dims* d) {
-    (void)d;
-    return 0;
+    if (check_common_dims(d) != M3_OK) return 0;
+    const int64_t R = d->rank, Q = d->chunk > 0 ? d->chunk : (64 / R > 0 ? 64 / R : 1);
+    return split_plan(d, Q, false, false).total;
+}
+
+size_t m3_layer_prefill_workspace_bytes(const m3_dims* d) {
+    if (check_common_dims(d) != M3_OK) return 0;
+    const int64_t R = d->rank, Q = d->chunk > 0 ? d->chunk : (32 / R > 0 ? 32 / R : 1);
+    return split_plan(d, Q, true, false).total;
 }
 
 m3_status m3_bcnorm_rope(const m3_dims* d, const void* B, const void* C, const void* dt, const void* theta,
@@ -349,8 +466,6 @@ m3_status m3_prefill(const m3_dims* d, const void* x, const void* Bbar, const vo
                      const float* A, const void* lam, const float* w_out, const float* h_in, const void* Bbar_prev,
                      const void* x_prev, void* y, float* h_out, void* Bbar_last, void* x_last, void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     m3_status s = check_common_dims(d);
     if (s != M3_OK) return s;
     const int64_t b = d->batch, L = d->seqlen, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
@@ -403,6 +518,14 @@ m3_status m3_prefill(const m3_dims* d, const void* x, const void* Bbar, const vo
     a.h_in = h_in; a.Bbar_prev = Bbar_prev; a.x_prev = x_prev;
     a.y = y; a.h_out = h_out; a.Bbar_last = Bbar_last; a.x_last = x_last;
     a.b = b; a.L = L; a.H = (int)H; a.N = (int)N; a.P = (int)P; a.R = (int)R; a.Q = (int)Q;
+    const SplitPlan sp = split_plan(d, Q, false, false);
+    const Buf all[] = {{x, nX, "x"}, {Bbar, nBC, "Bbar"}, {Cbar, nBC, "Cbar"}, {dt, nStep, "dt"}, {A, nA, "A"},
+                       {lam, nStep, "lam"}, {w_out, nWo, "w_out"}, {Bbar_prev, nBp, "Bbar_prev"},
+                       {x_prev, nXp, "x_prev"}, {y, nY, "y"}, {h_out, nH, "h_out"}, {Bbar_last, nBp, "Bbar_last"},
+                       {x_last, nXp, "x_last"}, {h_in, nH, "h_in"}};
+    if ((s = check_split_workspace(sp, workspace, workspace_bytes, all, 14, "m3_prefill")) != M3_OK) return s;
+    if (workspace && sp.nseg >= 2)
+        return launched(run_split(a, sp, workspace, false, d->io == M3_BF16, stream), "m3_prefill");
     return launched(m3::launch_prefill(a, d->io == M3_BF16, stream), "m3_prefill");
 }
 
@@ -412,10 +535,9 @@ m3_status m3_layer_prefill(const m3_dims* d, const void* x, const void* B, const
                            const float* phi_in, const float* h_in, const void* Bbar_prev, const void* x_prev,
                            void* y, float* h_out, float* phi_out, void* Bbar_last, void* x_last, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     return layer_prefill(d, false, nullptr, x, B, C, dt, theta, normw_B, normw_C, bias_B, bias_C, A, lam, w_out, phi_in,
-                         h_in, Bbar_prev, x_prev, y, h_out, phi_out, Bbar_last, x_last, stream, "m3_layer_prefill");
+                         h_in, Bbar_prev, x_prev, y, h_out, phi_out, Bbar_last, x_last, workspace, workspace_bytes,
+                         stream, "m3_layer_prefill");
 }
 
 m3_status m3_layer_prefill_varlen(const m3_dims* d, const int32_t* cu_seqlens, const void* x, const void* B,
@@ -425,8 +547,8 @@ m3_status m3_layer_prefill_varlen(const m3_dims* d, const int32_t* cu_seqlens, c
                                   const void* Bbar_prev, const void* x_prev, void* y, float* h_out, float* phi_out,
                                   void* Bbar_last, void* x_last, hipStream_t stream) {
     return layer_prefill(d, true, cu_seqlens, x, B, C, dt, theta, normw_B, normw_C, bias_B, bias_C, A, lam, w_out,
-                         phi_in, h_in, Bbar_prev, x_prev, y, h_out, phi_out, Bbar_last, x_last, stream,
-                         "m3_layer_prefill_varlen");
+                         phi_in, h_in, Bbar_prev, x_prev, y, h_out, phi_out, Bbar_last, x_last, nullptr, 0,
+                         stream, "m3_layer_prefill_varlen");
 }
 
 m3_status m3_decode_step(const m3_dims* d, float* h, const void* Bbar_prev, const void* x_prev, const void* x,

@@ -422,6 +422,26 @@ hipError_t launch_t(const BcnormRopeArgs& a, hipStream_t s) {
     }
 }
 
+template <typename T, int N>
+hipError_t launch_angles_n(const BcnormRopeArgs& a, hipStream_t s) {
+    const unsigned nbh = (unsigned)(a.b * a.H);
+    hipLaunchKernelGGL((angle_partial_kernel<T, N>), dim3(nbh * a.nseg), dim3(64 * kParts), 0, s, a);
+    hipLaunchKernelGGL(angle_scan_kernel, dim3(nbh), dim3(N / 2 < 64 ? 64 : N / 2), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_angles_t(const BcnormRopeArgs& a, hipStream_t s) {
+    switch (a.N) {
+        case 16: return launch_angles_n<T, 16>(a, s);
+        case 32: return launch_angles_n<T, 32>(a, s);
+        case 64: return launch_angles_n<T, 64>(a, s);
+        case 128: return launch_angles_n<T, 128>(a, s);
+        case 256: return launch_angles_n<T, 256>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 bool bcnorm_rope_supported(int N, int R) {
@@ -433,6 +453,10 @@ int bcnorm_rope_parts() { return kParts; }
 
 hipError_t launch_bcnorm_rope(const BcnormRopeArgs& a, bool bf16_io, hipStream_t s) {
     return bf16_io ? launch_t<bf16>(a, s) : launch_t<float>(a, s);
+}
+
+hipError_t launch_segment_angles(const BcnormRopeArgs& a, bool bf16_io, hipStream_t s) {
+    return bf16_io ? launch_angles_t<bf16>(a, s) : launch_angles_t<float>(a, s);
 }
 
 }  // namespace m3

@@ -90,6 +90,20 @@ struct PrefillArgs {
     // T packed tokens (b = number of sequences); nullptr = dense [b, L, ...]
     const int32_t* cu_seqlens = nullptr;
     int64_t T = 0;
+    // Sequence split (few (b, h) pairs, long sequences): each sequence is cut into nseg segments
+    // of seglen steps.  pass 1 runs every segment at once, segment 0 from the call's carry and
+    // the others from zero (they read no C and store no y): their end states and the rotated
+    // Bbar of their last steps go to the workspace.  segment_combine then turns the end states
+    // into true ones, and pass 2 runs segments 1 .. nseg-1 from them, writing y and, in the last
+    // segment, the call's outputs.  pass 0 = no split.
+    int pass = 0;
+    int nseg = 1;
+    int64_t seglen = 0;
+    float* ws_state = nullptr;       // [b, H, nseg, N, P] end state of each segment
+    void* ws_bbar = nullptr;         // [b, H, nseg, R, N] io, rotated Bbar of each segment's last step
+    const float* seg_phi = nullptr;  // fused: angle-segment start angles [b, H, nsegA, parts, N/2] (radians)
+    int64_t angle_seglen = 0;        // steps per angle segment (a divisor of seglen)
+    int angle_parts = 0;             // start angles per angle segment
 };
 
 // Gradients of the fused layer core (m3_layer_chunk_states / m3_layer_backward).  B and C are raw
@@ -163,5 +177,10 @@ hipError_t launch_prefill(const PrefillArgs& a, bool bf16_io, hipStream_t s);
 
 bool layer_supported(int N, int P, int R, int QR, bool bf16_io);
 hipError_t launch_layer(const PrefillArgs& a, bool bf16_io, hipStream_t s);
+// between the two passes of a split sequence: true end states of segments 1 .. nseg-2
+hipError_t launch_segment_combine(const PrefillArgs& a, bool bf16_io, hipStream_t s);
+// the start angle of every angle segment (seg_phi) and the final angle: the first two kernels of
+// m3_bcnorm_rope alone
+hipError_t launch_segment_angles(const BcnormRopeArgs& a, bool bf16_io, hipStream_t s);
 
 }  // namespace m3

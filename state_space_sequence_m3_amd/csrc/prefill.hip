@@ -117,13 +117,17 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
-    const int64_t bh = blockIdx.x;
+    // a split sequence: pass 1 runs every segment of each (b, h), pass 2 segments 1 .. nseg-1
+    const int segs = a.pass == 2 ? a.nseg - 1 : a.nseg;
+    const int64_t bh = a.pass ? (int64_t)blockIdx.x / segs : (int64_t)blockIdx.x;
+    const int seg = a.pass ? (int)(blockIdx.x % (unsigned)segs) + (a.pass == 2 ? 1 : 0) : 0;
     const int64_t b = bh / a.H;
     const int h = (int)(bh % a.H);
     const int H = a.H, R = a.R, Q = a.Q;
     const int rl2 = __builtin_ctz((unsigned)R), rmask = R - 1;
     // dense: sequence b is steps [0, L) of [b, L, ...]; packed: tokens [cu[b], cu[b+1]) of T,
-    // clamped into [0, T) so that any offsets stay inside the packed arrays
+    // clamped into [0, T) so that any offsets stay inside the packed arrays; split: the segment's
+    // steps (never empty: the host makes the last segment hold the tail)
     int64_t L = a.L, t_first = b * a.L;
     if (a.cu_seqlens) {
         const int64_t s0 = min(max((int64_t)a.cu_seqlens[b], (int64_t)0), a.T);
@@ -131,6 +135,15 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         t_first = s0;
         L = s1 - s0;
     }
+    if (a.pass) {
+        t_first += seg * a.seglen;
+        L = min(a.seglen, a.L - seg * a.seglen);
+    }
+    // pass 1 beyond segment 0 needs only the segment's end state: no C is read and no y stored
+    const bool states_only = a.pass == 1 && seg > 0;
+    // carried in: the call's carry (no split, or segment 0 of pass 1), none (the later segments of
+    // pass 1), or the previous segment's combined end state and its last step (pass 2)
+    const bool own_carry = a.pass == 0 || (a.pass == 1 && seg == 0);
     const int64_t nchunk = (L + Q - 1) / Q;
     const float Alog2 = a.A[h] * kLog2e;
     // (b, t = 0, h) bases; step t of this (b, h) is t * H rows further
@@ -141,6 +154,18 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const T* Cg = (const T*)a.Cbar + row_bh * R * N;
     const T* dtg = (const T*)a.dt + row_bh;
     const T* lamg = (const T*)a.lam + row_bh;
+    const float* hin = nullptr;
+    const T* Bprev = nullptr;
+    const T* xprev = nullptr;
+    if (own_carry) {
+        hin = a.h_in ? a.h_in + bh * (int64_t)(N * P) : nullptr;
+        Bprev = a.Bbar_prev ? (const T*)a.Bbar_prev + bh * (int64_t)(R * N) : nullptr;
+        xprev = a.x_prev ? (const T*)a.x_prev + bh * (int64_t)(R * P) : nullptr;
+    } else if (a.pass == 2) {
+        hin = a.ws_state + (bh * a.nseg + seg - 1) * (int64_t)(N * P);
+        Bprev = (const T*)a.ws_bbar + (bh * a.nseg + seg - 1) * (int64_t)(R * N);
+        xprev = Xg - HRP;   // step t_first - 1 of this head
+    }
     const int pcol = 16 * wave + l16;            // this lane's column of P in MFMA tiles
     // One buffer descriptor per stream over this sequence: from step 0 of this (b, h) to the end
     // of its last row (t = L - 1).  A chunk adds its byte offset (32 bits: the whole sequence
@@ -169,7 +194,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     uint4 rc[NBUF][MAXC], rb[NBUF][MAXC], rx[NBUF][MAXX];
     typedef typename IoBits<T>::type Bits;
     Bits nd[NBUF], nl[NBUF], ndn[NBUF], nln[NBUF];   // dt, lambda at t and t + 1 (io bits; the last wave uses them)
-    const rsrc_t dCs = make_rsrc(Cg, seq_bytes(HRN, (int64_t)R * N));
+    const rsrc_t dCs = make_rsrc(Cg, states_only ? 0u : seq_bytes(HRN, (int64_t)R * N));
     const rsrc_t dBs = make_rsrc(Bg, seq_bytes(HRN, (int64_t)R * N));
     const rsrc_t dXs = make_rsrc(Xg, seq_bytes(HRP, (int64_t)R * P));
     const rsrc_t dDs = make_rsrc(dtg, seq_bytes(H, 1));
@@ -249,12 +274,22 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // on the last step's angle.  The carried angle is the last row of buffer `prev` (the previous
     // chunk), read first: without pipelining prev == out.  Chunk 0 starts from phi_in (radians).
     const int kcol = wave * KWL + (lane & (KWL - 1)), run = lane / KWL;
+    // angle carried in (radians): the call's, or the segment's start angle from the angle pass
+    const float* phin = nullptr;
+    if (FUSED) {
+        if (own_carry) {
+            phin = a.phi_in ? a.phi_in + bh * K : nullptr;
+        } else {
+            const int64_t nsegA = (a.L + a.angle_seglen - 1) / a.angle_seglen;
+            phin = a.seg_phi + (bh * nsegA + seg * (a.seglen / a.angle_seglen)) * a.angle_parts * (int64_t)K;
+        }
+    }
     auto scan = [&](int64_t c, int out, int prev) {
         if (!FUSED) return;
         const bool colwave = wave < NW2;
         float carry = 0.f;
         if (colwave)
-            carry = c == 0 ? (a.phi_in ? wrap_turns(a.phi_in[bh * K + kcol] * kInvTwoPi) : 0.f)
+            carry = c == 0 ? (phin ? wrap_turns(phin[kcol] * kInvTwoPi) : 0.f)
                            : wrap_turns(sPhi[prev * TPH + (Q - 1) * LDPHI + kcol]);
         float* ph = sPhi + out * TPH;
         if (scanner) {
@@ -398,17 +433,15 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-            st[nb][m] = a.h_in ? a.h_in[(bh * N + 16 * nb + 4 * g + m) * P + pcol] : 0.f;
-    if (a.Bbar_prev && a.x_prev && L > 0) {
+            st[nb][m] = hin ? hin[(16 * nb + 4 * g + m) * P + pcol] : 0.f;
+    if (Bprev && xprev && L > 0) {
         const float c0 = (1.0f - load_f32(lamg)) * load_f32(dtg);
-        const T* Bp = (const T*)a.Bbar_prev + bh * R * N;
-        const T* xp = (const T*)a.x_prev + bh * R * P;
         for (int r = 0; r < R; ++r) {
-            const float xv = c0 * load_f32(xp + r * P + pcol);
+            const float xv = c0 * load_f32(xprev + r * P + pcol);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) st[nb][m] += load_f32(Bp + r * N + 16 * nb + 4 * g + m) * xv;
+                for (int m = 0; m < 4; ++m) st[nb][m] += load_f32(Bprev + r * N + 16 * nb + 4 * g + m) * xv;
         }
     }
 
@@ -416,7 +449,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const bool mix = a.w_out != nullptr;
     T* yg = (T*)a.y + row_bh * (mix ? P : (int64_t)R * P);
     const int64_t ystep = mix ? (int64_t)H * P : HRP, yrow = mix ? P : (int64_t)R * P;
-    const rsrc_t dYs = make_rsrc(yg, seq_bytes(ystep, yrow));
+    const rsrc_t dYs = make_rsrc(yg, states_only ? 0u : seq_bytes(ystep, yrow));
     floatx4 wo = {1.f, 1.f, 1.f, 1.f};          // mixing weights for this lane's (r, 4 columns)
     if (mix) {
         const int r = l16 & rmask;
@@ -672,43 +705,93 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     }
 
     // ---- outputs: final state and the last step's (Bbar, x) ------------------------------
+    // no split: the call's; pass 1: the segment's end state and last Bbar row, into the
+    // workspace; pass 2: the call's, from the last segment only
+    const bool last_seg = a.pass != 2 || seg == a.nseg - 1;
+    float* hout = a.pass == 1 ? a.ws_state + (bh * a.nseg + seg) * (int64_t)(N * P)
+                              : (last_seg ? a.h_out + bh * (int64_t)(N * P) : nullptr);
+    T* Blast = a.pass == 1 ? (T*)a.ws_bbar + (bh * a.nseg + seg) * (int64_t)(R * N)
+                           : (last_seg && a.Bbar_last ? (T*)a.Bbar_last + bh * (int64_t)(R * N) : nullptr);
+    T* xlast = a.pass != 1 && last_seg && a.x_last ? (T*)a.x_last + bh * (int64_t)(R * P) : nullptr;
+    float* phout = FUSED && a.pass != 1 && last_seg && a.phi_out ? a.phi_out + bh * K : nullptr;
+    if (hout) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) a.h_out[(bh * N + 16 * nb + 4 * g + m) * P + pcol] = st[nb][m];
+            for (int m = 0; m < 4; ++m) hout[(16 * nb + 4 * g + m) * P + pcol] = st[nb][m];
+    }
     if (L > 0) {
         // the last chunk's tiles and angles are still in LDS (nothing is staged after it)
         const int lb = PIPE ? (int)((nchunk - 1) & 1) : 0;
         const int tlast = (int)(L - 1 - (nchunk - 1) * Q);
-        if (a.Bbar_last) {
+        if (Blast) {
             for (int e = tid; e < R * N; e += NT) {
                 T v;
                 if (FUSED) v = sB[lb * TB + (tlast * R + e / N) * LDB + e % N];   // rotated here only
                 else v = Bg[(L - 1) * HRN + e];
-                ((T*)a.Bbar_last)[bh * R * N + e] = v;
+                Blast[e] = v;
             }
         }
-        if (a.x_last)
-            for (int e = tid; e < R * P; e += NT) ((T*)a.x_last)[bh * R * P + e] = Xg[(L - 1) * HRP + e];
-        if (FUSED && a.phi_out)
-            for (int k = tid; k < K; k += NT)
-                a.phi_out[bh * K + k] = wrap_turns(sPhi[lb * TPH + (Q - 1) * LDPHI + k]) * kTwoPi;
+        if (xlast)
+            for (int e = tid; e < R * P; e += NT) xlast[e] = Xg[(L - 1) * HRP + e];
+        if (phout)
+            for (int k = tid; k < K; k += NT) phout[k] = wrap_turns(sPhi[lb * TPH + (Q - 1) * LDPHI + k]) * kTwoPi;
     } else {
         // an empty sequence of a packed batch: the carry passes through unchanged
-        if (a.Bbar_last)
-            for (int e = tid; e < R * N; e += NT)
-                ((T*)a.Bbar_last)[bh * R * N + e] = a.Bbar_prev ? ((const T*)a.Bbar_prev)[bh * R * N + e] : T{};
-        if (a.x_last)
-            for (int e = tid; e < R * P; e += NT)
-                ((T*)a.x_last)[bh * R * P + e] = a.x_prev ? ((const T*)a.x_prev)[bh * R * P + e] : T{};
-        if (FUSED && a.phi_out)
-            for (int k = tid; k < K; k += NT) a.phi_out[bh * K + k] = a.phi_in ? wrap_angle(a.phi_in[bh * K + k]) : 0.f;
+        if (Blast)
+            for (int e = tid; e < R * N; e += NT) Blast[e] = Bprev ? Bprev[e] : T{};
+        if (xlast)
+            for (int e = tid; e < R * P; e += NT) xlast[e] = xprev ? xprev[e] : T{};
+        if (phout)
+            for (int k = tid; k < K; k += NT) phout[k] = phin ? wrap_angle(phin[k]) : 0.f;
+    }
+}
+
+// Between the passes of a split sequence, one workgroup per (b, h): the true end state of
+// segment s (1 <= s <= nseg - 2) is its local end state (from zero) plus the carried state that
+// enters it, decayed over the segment:
+//   g_end(s) = g_local(s) + exp(A sum_{t in s} dt_t) (g_end(s - 1) + c_{t0} Bbar_{t0-1}^T x_{t0-1})
+// with t0 the segment's first step and c_{t0} = (1 - lambda_{t0}) dt_{t0}: the recurrence is linear
+// in its carry, and the carry term is the one the scan adds for a carried (Bbar_prev, x_prev).
+template <typename T>
+__global__ __launch_bounds__(256) void segment_combine_kernel(PrefillArgs a) {
+    __shared__ float red[4];
+    extern __shared__ __align__(16) float cl_lds[];   // Bbar row [R][N], x row [R][P] (fp32)
+    const int64_t bh = blockIdx.x, b = bh / a.H;
+    const int h = (int)(bh % a.H), tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int N = a.N, P = a.P, R = a.R, H = a.H;
+    const int64_t NP = (int64_t)N * P;
+    float* sBr = cl_lds;
+    float* sXr = cl_lds + R * N;
+    for (int s = 1; s + 1 < a.nseg; ++s) {
+        const int64_t t0 = s * a.seglen, t1 = min(t0 + a.seglen, a.L);
+        float acc = 0.f;
+        for (int64_t t = t0 + tid; t < t1; t += 256) acc += load_f32((const T*)a.dt + (b * a.L + t) * H + h);
+        for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+        if (lane == 0) red[wave] = acc;
+        const int64_t row0 = (b * a.L + t0) * H + h;   // step t0 of this head
+        for (int e = tid; e < R * N; e += 256)
+            sBr[e] = load_f32((const T*)a.ws_bbar + (bh * a.nseg + s - 1) * (int64_t)(R * N) + e);
+        for (int e = tid; e < R * P; e += 256) sXr[e] = load_f32((const T*)a.x + (row0 - H) * R * P + e);
+        __syncthreads();
+        const float decay = expf(a.A[h] * (red[0] + red[1] + red[2] + red[3]));
+        const float c0 = (1.0f - load_f32((const T*)a.lam + row0)) * load_f32((const T*)a.dt + row0);
+        const float* gprev = a.ws_state + (bh * a.nseg + s - 1) * NP;
+        float* gcur = a.ws_state + (bh * a.nseg + s) * NP;
+        for (int64_t e = tid; e < NP; e += 256) {
+            const int n = (int)(e / P), p = (int)(e % P);
+            float u = 0.f;
+            for (int r = 0; r < R; ++r) u = fmaf(sBr[r * N + n], sXr[r * P + p], u);
+            gcur[e] = fmaf(decay, fmaf(c0, u, gprev[e]), gcur[e]);
+        }
+        __syncthreads();   // the next segment reuses red and the LDS rows
     }
 }
 
 template <typename T, int N, int P, bool FUSED>
 hipError_t launch_np(const PrefillArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)(a.b * a.H)), block(P / 16 * 64);
+    const int64_t per_bh = a.pass == 0 ? 1 : (a.pass == 1 ? a.nseg : a.nseg - 1);
+    const dim3 grid((unsigned)(a.b * a.H * per_bh)), block(P / 16 * 64);
     // fused: BCNorm weights and biases in dynamic LDS
     const size_t dyn = FUSED ? (size_t)(2 * N + 2 * a.R * N) * sizeof(float) : 0;
     switch (a.Q * a.R) {
@@ -752,6 +835,15 @@ bool layer_supported(int N, int P, int R, int QR, bool bf16_io) {
 
 hipError_t launch_layer(const PrefillArgs& a, bool bf16_io, hipStream_t s) {
     return bf16_io ? launch_t<bf16, true>(a, s) : launch_t<float, true>(a, s);
+}
+
+hipError_t launch_segment_combine(const PrefillArgs& a, bool bf16_io, hipStream_t s) {
+    const size_t lds = (size_t)(a.R * a.N + a.R * a.P) * sizeof(float);
+    if (bf16_io)
+        hipLaunchKernelGGL(segment_combine_kernel<bf16>, dim3((unsigned)(a.b * a.H)), dim3(256), lds, s, a);
+    else
+        hipLaunchKernelGGL(segment_combine_kernel<float>, dim3((unsigned)(a.b * a.H)), dim3(256), lds, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace m3

@@ -26,7 +26,8 @@ M3_F32, M3_BF16 = 0, 1
 M3_BCNORM = 1
 
 EXPORTED = ["m3_bcnorm_rope", "m3_bcnorm_rope_workspace_bytes", "m3_prefill",
-            "m3_prefill_workspace_bytes", "m3_layer_prefill", "m3_layer_prefill_varlen",
+            "m3_prefill_workspace_bytes", "m3_layer_prefill", "m3_layer_prefill_workspace_bytes",
+            "m3_layer_prefill_varlen",
             "m3_decode_step",
             "m3_layer_decode_step", "m3_layer_backward_chunk", "m3_layer_chunk_states",
             "m3_layer_backward_workspace_bytes", "m3_layer_backward", "m3_last_error", "m3_version"]
@@ -69,6 +70,8 @@ def load(path: str = LIB_PATH):
             lib.m3_prefill.argtypes = [_DIMS] + [_P] * 15 + [ctypes.c_size_t, _P]
             lib.m3_prefill_workspace_bytes.restype = ctypes.c_size_t
             lib.m3_prefill_workspace_bytes.argtypes = [_DIMS]
+            lib.m3_layer_prefill_workspace_bytes.restype = ctypes.c_size_t
+            lib.m3_layer_prefill_workspace_bytes.argtypes = [_DIMS]
             lib.m3_layer_prefill.restype = ctypes.c_int
             lib.m3_layer_prefill.argtypes = [_DIMS] + [_P] * 22 + [ctypes.c_size_t, _P]
             lib.m3_layer_prefill_varlen.restype = ctypes.c_int
@@ -154,6 +157,10 @@ def prefill_workspace_bytes(dims: M3Dims) -> int:
     return int(load().m3_prefill_workspace_bytes(ctypes.byref(dims)))
 
 
+def layer_prefill_workspace_bytes(dims: M3Dims) -> int:
+    return load().m3_layer_prefill_workspace_bytes(ctypes.byref(dims))
+
+
 def m3_bcnorm_rope(B, C, dt, theta, normw_B=None, normw_C=None, bias_B=None, bias_C=None,
                    phi_in=None, Bbar=None, Cbar=None, phi_out=None, bcnorm=True, eps=1e-5,
                    workspace=None, stream=None):
@@ -188,6 +195,19 @@ def m3_bcnorm_rope(B, C, dt, theta, normw_B=None, normw_C=None, bias_B=None, bia
     return Bbar, Cbar, phi_out
 
 
+def _workspace(workspace, need, dev):
+    """A prefill call's workspace: None allocates the bytes the library asks for (it then splits
+    few long sequences into segments), False passes none (one pass per sequence), a tensor is
+    used as given.  Returns (tensor or None, bytes)."""
+    if workspace is False:
+        return None, 0
+    if workspace is None:
+        if not need:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def m3_prefill(x, Bbar, Cbar, dt, A, lam, w_out=None, h_in=None, Bbar_prev=None, x_prev=None,
                y=None, h_out=None, Bbar_last=None, x_last=None, chunk=0, workspace=None,
                stream=None):
@@ -214,10 +234,7 @@ def m3_prefill(x, Bbar, Cbar, dt, A, lam, w_out=None, h_in=None, Bbar_prev=None,
     _tensor(Bbar_last, "Bbar_last", (b, H, R, N), io, dev)
     _tensor(x_last, "x_last", (b, H, R, P), io, dev)
     dims = make_dims(b, L, H, P, N, R, chunk, _io_code(io))
-    need = prefill_workspace_bytes(dims)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(workspace, prefill_workspace_bytes(dims), dev)
     _check(lib.m3_prefill(ctypes.byref(dims), _ptr(x), _ptr(Bbar), _ptr(Cbar), _ptr(dt), _ptr(A),
                           _ptr(lam), _ptr(w_out), _ptr(h_in), _ptr(Bbar_prev), _ptr(x_prev),
                           _ptr(y), _ptr(h_out), _ptr(Bbar_last), _ptr(x_last), _ptr(workspace),
@@ -228,9 +245,10 @@ def m3_prefill(x, Bbar, Cbar, dt, A, lam, w_out=None, h_in=None, Bbar_prev=None,
 def m3_layer_prefill(x, B, C, dt, theta, A, lam, normw_B=None, normw_C=None, bias_B=None,
                      bias_C=None, w_out=None, phi_in=None, h_in=None, Bbar_prev=None, x_prev=None,
                      y=None, h_out=None, phi_out=None, Bbar_last=None, x_last=None, chunk=0,
-                     bcnorm=True, eps=1e-5, stream=None):
+                     bcnorm=True, eps=1e-5, workspace=None, stream=None):
     """m3_bcnorm_rope + m3_prefill in one pass.  x: [b, L, H, R, P]; raw B, C: [b, L, H, R, N].
-    Returns (y, h_out, phi_out)."""
+    A workspace of layer_prefill_workspace_bytes is allocated when none is given (it lets few
+    long sequences run split into segments).  Returns (y, h_out, phi_out)."""
     lib = load()
     b, L, H, R, P = x.shape
     N = B.shape[-1]
@@ -262,11 +280,12 @@ def m3_layer_prefill(x, B, C, dt, theta, A, lam, normw_B=None, normw_C=None, bia
     _tensor(Bbar_last, "Bbar_last", (b, H, R, N), io, dev)
     _tensor(x_last, "x_last", (b, H, R, P), io, dev)
     dims = make_dims(b, L, H, P, N, R, chunk, _io_code(io), bcnorm, eps)
+    workspace, ws_bytes = _workspace(workspace, layer_prefill_workspace_bytes(dims), dev)
     _check(lib.m3_layer_prefill(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(theta),
                                 _ptr(normw_B), _ptr(normw_C), _ptr(bias_B), _ptr(bias_C), _ptr(A),
                                 _ptr(lam), _ptr(w_out), _ptr(phi_in), _ptr(h_in), _ptr(Bbar_prev),
                                 _ptr(x_prev), _ptr(y), _ptr(h_out), _ptr(phi_out), _ptr(Bbar_last),
-                                _ptr(x_last), None, 0, _stream(stream)))
+                                _ptr(x_last), _ptr(workspace), ws_bytes, _stream(stream)))
     return y, h_out, phi_out
 
 

@@ -1,0 +1,119 @@
+"""GPU parity of the sequence split of m3_prefill and m3_layer_prefill: with few (b, h) pairs and
+long sequences, and a workspace, each sequence runs as segments in parallel (pass 1 from zero
+carries, a chaining kernel, pass 2 from the true carries).  Checked against the fp64 oracle's
+layer core over the whole sequence, with carries in, ragged last segments and 2-4 segments (so
+that the chaining runs); the same call run in one pass is checked against the oracle too.
+Every call goes through the C ABI (via the ctypes binding).  Tolerances are those of
+gpu_util.TOL."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, angle_err, rel_err, to_dev
+from state_space_sequence_m3_amd import inputs, m3scan
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+SPLIT_CASES = [
+    # io, b, L, H, P, N, R, chunk (fused), chunk (m3_prefill), mix, carry
+    ("bf16", 1, 3000, 2, 64, 128, 1, 32, 64, False, True),   # 2 segments, ragged tail
+    ("bf16", 1, 5000, 2, 64, 128, 4, 8, 16, True, True),     # 4 segments: chaining runs twice
+    ("f32", 1, 4100, 1, 16, 16, 2, 8, 16, True, True),       # 3 segments, fp32
+    ("bf16", 1, 4096, 2, 64, 64, 1, 32, 32, False, False),   # N = 64, segments of 1024
+]
+
+
+def _wl(io, b, L, H, P, N, R, Q, mix):
+    return inputs.Workload("split", b, L, H, P, N, R, Q, io, True, True, mix, 1.0)
+
+
+def _layer(d, w, chunk, mix, **kw):
+    return m3scan.m3_layer_prefill(d["x"], d["B"], d["C"], d["dt"], d["theta"], d["A"], d["lam"],
+                                   d.get("normw_B"), d.get("normw_C"), d.get("bias_B"), d.get("bias_C"),
+                                   d["w_out"] if mix else None, d.get("phi_in"), d.get("h_in"),
+                                   d.get("Bbar_prev"), d.get("x_prev"), chunk=chunk, **kw)
+
+
+def _dims(w, chunk):
+    return m3scan.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, chunk,
+                            m3scan.M3_BF16 if w.io == "bf16" else m3scan.M3_F32)
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "%s-b%d-L%d-H%d-P%d-N%d-R%d" % c[:7])
+def test_split_layer_prefill(case):
+    io, b, L, H, P, N, R, Qf, Qp, mix, carry = case
+    w = _wl(io, b, L, H, P, N, R, Qf, mix)
+    assert m3scan.layer_prefill_workspace_bytes(_dims(w, Qf)) > 0, "the split is not used"
+    inp = inputs.make_prefill_inputs(w, seed=81, normw=True, carry=carry)
+    d = to_dev(inp, DEV)
+    Blast = torch.empty((b, H, R, N), dtype=w.torch_io, device=DEV)
+    xlast = torch.empty((b, H, R, P), dtype=w.torch_io, device=DEV)
+    y, h, phi = _layer(d, w, Qf, mix, Bbar_last=Blast, x_last=xlast)
+    y1, h1, phi1 = _layer(d, w, Qf, mix, workspace=False)
+    torch.cuda.synchronize()
+    ref = oracle.layer(inp, bcnorm=True, mix=mix)
+    tol = TOL[io]
+    assert rel_err(y, ref["y"]) <= tol
+    assert rel_err(h, ref["h_out"]) <= tol
+    assert angle_err(phi, ref["phi_out"]) <= (1e-3 if io == "bf16" else 1e-4)
+    assert rel_err(Blast, ref["Bbar_last"]) <= tol
+    assert rel_err(xlast, ref["x_last"]) == 0.0
+    # the same call in one pass (no workspace) meets the same bar
+    assert rel_err(y1, ref["y"]) <= tol
+    assert rel_err(h1, ref["h_out"]) <= tol
+    assert angle_err(phi1, ref["phi_out"]) <= (1e-3 if io == "bf16" else 1e-4)
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "%s-b%d-L%d-H%d-P%d-N%d-R%d" % c[:7])
+def test_split_prefill_two_calls(case):
+    io, b, L, H, P, N, R, Qf, Qp, mix, carry = case
+    w = _wl(io, b, L, H, P, N, R, Qp, mix)
+    assert m3scan.prefill_workspace_bytes(_dims(w, Qp)) > 0, "the split is not used"
+    inp = inputs.make_prefill_inputs(w, seed=82, normw=True, carry=carry)
+    d = to_dev(inp, DEV)
+    Bb, Cb, phi = m3scan.m3_bcnorm_rope(d["B"], d["C"], d["dt"], d["theta"], d.get("normw_B"),
+                                        d.get("normw_C"), d.get("bias_B"), d.get("bias_C"), d.get("phi_in"))
+    Blast = torch.empty((b, H, R, N), dtype=w.torch_io, device=DEV)
+    xlast = torch.empty((b, H, R, P), dtype=w.torch_io, device=DEV)
+    y, h = m3scan.m3_prefill(d["x"], Bb, Cb, d["dt"], d["A"], d["lam"], d["w_out"] if mix else None,
+                             d.get("h_in"), d.get("Bbar_prev"), d.get("x_prev"), Bbar_last=Blast,
+                             x_last=xlast, chunk=Qp)
+    torch.cuda.synchronize()
+    ref = oracle.layer(inp, bcnorm=True, mix=mix)
+    tol = TOL[io]
+    assert rel_err(y, ref["y"]) <= tol
+    assert rel_err(h, ref["h_out"]) <= tol
+    assert rel_err(Blast, ref["Bbar_last"]) <= tol
+    assert rel_err(xlast, ref["x_last"]) == 0.0
+
+
+def test_split_layer_prefill_in_place_carry():
+    """h_out = h_in and phi_out = phi_in on the split path (the angle pass must not clobber the
+    carried angle before segment 0 reads it)."""
+    w = _wl("bf16", 1, 4500, 2, 64, 128, 2, 16, True)
+    inp = inputs.make_prefill_inputs(w, seed=83, normw=True, carry=True)
+    d = to_dev(inp, DEV)
+    h = d["h_in"].clone()
+    phi = d["phi_in"].clone()
+    y, _, _ = _layer(dict(d, h_in=h, phi_in=phi), w, 16, True, h_out=h, phi_out=phi)
+    torch.cuda.synchronize()
+    ref = oracle.layer(inp, bcnorm=True, mix=True)
+    assert rel_err(y, ref["y"]) <= TOL["bf16"]
+    assert rel_err(h, ref["h_out"]) <= TOL["bf16"]
+    assert angle_err(phi, ref["phi_out"]) <= 1e-3
+
+
+def test_split_workspace_too_small_is_rejected():
+    w = _wl("bf16", 1, 3000, 2, 64, 128, 1, 32, False)
+    inp = inputs.make_prefill_inputs(w, seed=84)
+    d = to_dev(inp, DEV)
+    need = m3scan.layer_prefill_workspace_bytes(_dims(w, 32))
+    assert need > 0
+    small = torch.empty(need - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(m3scan.M3Error) as e:
+        _layer(d, w, 32, False, workspace=small)
+    assert e.value.status == m3scan.M3_E_WORKSPACE

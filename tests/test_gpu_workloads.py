@@ -187,6 +187,24 @@ def test_long_context_prefill_then_decode_sampled():
         assert angle_err(phi[:, hi:hi + 1], state["phi"]) <= 1e-3
 
 
+def test_long_context_layer_prefill_sampled():
+    """m3_layer_prefill on b=1, L=16384, MIMO R=4 (64 (b, h) pairs: the call splits each sequence
+    into segments that run in parallel), sampled heads against the oracle."""
+    w = inputs.WORKLOADS["long_mimo4_b1_l16384"]
+    print("workload", w.name, "fused", flush=True)
+    inp = inputs.make_prefill_inputs(w, seed=6, device=DEV)
+    dims = m3scan.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, 0, m3scan.M3_BF16)
+    assert m3scan.layer_prefill_workspace_bytes(dims) > 0
+    y, h, phi = m3scan.m3_layer_prefill(inp["x"], inp["B"], inp["C"], inp["dt"], inp["theta"], inp["A"],
+                                        inp["lam"], None, None, inp["bias_B"], inp["bias_C"], inp["w_out"])
+    torch.cuda.synchronize()
+    for hi in (3, 58):
+        ref = oracle.layer(_slice_pair(inp, 0, hi), mix=True)
+        assert rel_err(y[:, :, hi:hi + 1], ref["y"]) <= TOL["bf16"], hi
+        assert rel_err(h[:, hi:hi + 1], ref["h_out"]) <= TOL["bf16"], hi
+        assert angle_err(phi[:, hi:hi + 1], ref["phi_out"]) <= 1e-3, hi
+
+
 @pytest.mark.parametrize("name,head", [("siso_b8_l2048", 17), ("mimo4_b8_l2048", 40)])
 def test_backward_workload_sampled(name, head):
     """m3_layer_backward over the whole b8 L2048 batch (the configuration bench.py times); the
