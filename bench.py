@@ -130,6 +130,8 @@ def time_prefill(w, steps, warmup, dev, inp=None, scan_only=False):
     dims = m3scan.make_dims(b, L, H, P, N, R, w.chunk, m3scan.M3_BF16 if w.io == "bf16" else m3scan.M3_F32)
     wsb = m3scan.bcnorm_rope_workspace_bytes(dims)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    pneed = m3scan.prefill_workspace_bytes(dims)
+    pws = torch.empty(pneed, dtype=torch.uint8, device=dev) if pneed else False
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -143,7 +145,7 @@ def time_prefill(w, steps, warmup, dev, inp=None, scan_only=False):
             ev[1].record(stream)
         m3scan.m3_prefill(inp["x"], inp["B"] if scan_only else Bb, inp["C"] if scan_only else Cb,
                           inp["dt"], inp["A"], inp["lam"],
-                          inp["w_out"] if w.mix else None, y=y, h_out=h, chunk=w.chunk)
+                          inp["w_out"] if w.mix else None, y=y, h_out=h, chunk=w.chunk, workspace=pws)
         if ev is not None:
             ev[2].record(stream)
 
@@ -176,12 +178,17 @@ def time_layer(w, inp, chunk, steps, warmup, dev):
     h = torch.empty((b, H, N, P), dtype=torch.float32, device=dev)
     phi = torch.empty((b, H, N // 2), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    # the sequence-split workspace (few long sequences), allocated once outside the timed region
+    dims = m3scan.make_dims(b, L, H, P, N, R, chunk, m3scan.M3_BF16 if w.io == "bf16" else m3scan.M3_F32,
+                            w.bcnorm)
+    need = m3scan.layer_prefill_workspace_bytes(dims)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else False
 
     def step():
         m3scan.m3_layer_prefill(inp["x"], inp["B"], inp["C"], inp["dt"], inp["theta"], inp["A"],
                                 inp["lam"], inp["normw_B"], inp["normw_C"], inp["bias_B"],
                                 inp["bias_C"], inp["w_out"] if w.mix else None, y=y, h_out=h,
-                                phi_out=phi, chunk=chunk, bcnorm=w.bcnorm)
+                                phi_out=phi, chunk=chunk, bcnorm=w.bcnorm, workspace=ws)
 
     for _ in range(warmup):
         step()
@@ -568,6 +575,26 @@ def main():
             del inpv
             torch.cuda.empty_cache()
         variants["siso_varlen_packed"] = time_varlen(w, args.steps, args.warmup, dev)
+        # the long-context workload's prefill: b = 1, L = 16384, MIMO R = 4, i.e. 64 (b, h) pairs,
+        # so both paths split each sequence into segments that run in parallel
+        wl4 = inputs.WORKLOADS["long_mimo4_b1_l16384"]
+        inp4 = inputs.make_prefill_inputs(wl4, seed=0, device=dev)
+        th4 = wl4.batch * wl4.seqlen * wl4.nheads
+        ms_l4 = time_layer(wl4, inp4, LAYER_CHUNK_ROWS // wl4.rank, args.steps, args.warmup, dev)
+        lb4 = th4 * layer_bytes_per_token_head(wl4) + wl4.batch * wl4.nheads * wl4.dstate * (wl4.headdim + 1) * 4
+        _, ms_s4, ms_b4, ms_p4 = time_prefill(wl4, args.steps, args.warmup, dev, inp4)
+        pb4 = th4 * prefill_bytes_per_token_head(wl4) + wl4.batch * wl4.nheads * wl4.dstate * wl4.headdim * 4
+        toks4 = wl4.batch * wl4.seqlen
+        variants["long_mimo4_b1_l16384"] = {
+            "m3_layer_prefill": {"ms": ms_l4, "tokens/s": toks4 / (ms_l4 / 1e3), "GB/s": lb4 / ms_l4 / 1e6,
+                                 "hbm_frac": lb4 / ms_l4 / 1e6 / HBM_PEAK_GBS,
+                                 "chunk": LAYER_CHUNK_ROWS // wl4.rank},
+            "two_calls": {"ms": ms_s4, "tokens/s": toks4 / (ms_s4 / 1e3), "bcnorm_rope_ms": ms_b4,
+                          "chunk": wl4.chunk},
+            "m3_prefill": {"ms": ms_p4, "GB/s": pb4 / ms_p4 / 1e6, "hbm_frac": pb4 / ms_p4 / 1e6 / HBM_PEAK_GBS},
+            "how": "sequence split into segments run in parallel (64 (b, h) pairs)"}
+        del inp4
+        torch.cuda.empty_cache()
     # the step is one kernel: the fused layer kernel
     kd = kernels["m3_layer_prefill"]
     kname = "prefill_kernel<bf16,128,64,2,fused>"

@@ -91,11 +91,11 @@ struct PrefillArgs {
     const int32_t* cu_seqlens = nullptr;
     int64_t T = 0;
     // Sequence split (few (b, h) pairs, long sequences): each sequence is cut into nseg segments
-    // of seglen steps.  pass 1 runs every segment at once, segment 0 from the call's carry and
-    // the others from zero (they read no C and store no y): their end states and the rotated
-    // Bbar of their last steps go to the workspace.  segment_combine then turns the end states
-    // into true ones, and pass 2 runs segments 1 .. nseg-1 from them, writing y and, in the last
-    // segment, the call's outputs.  pass 0 = no split.
+    // of seglen steps.  pass 1 runs segments 0 .. nseg-2 at once for their end states only
+    // (segment 0 from the call's carry, the others from zero; no C is read, no y computed): the
+    // end states and the rotated Bbar of their last steps go to the workspace.  segment_combine
+    // turns the end states into true ones, and pass 2 runs every segment from its true carry,
+    // writing y and, in the last segment, the call's outputs.  pass 0 = no split.
     int pass = 0;
     int nseg = 1;
     int64_t seglen = 0;

@@ -65,7 +65,10 @@ namespace {
 // remains.  The raw loads of chunk c + 2 are issued at the start of chunk c into the register set
 // of that parity, so they have a whole chunk to arrive.  Tiles of 48 or 64 rows do not fit twice
 // in LDS and run the same steps with two barriers per chunk.
-template <typename T, int N, int P, int NIB, bool FUSED>
+// STATES: pass 1 of a split sequence, which needs only each segment's end state: no C is read
+// or staged, and the score tiles, masks, outputs and stores of y are left out (the chunk's
+// barrier stays, it orders the staging buffers).
+template <typename T, int N, int P, int NIB, bool FUSED, bool STATES = false>
 __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) {
     using MM = Mma<T>;
     using F = typename MM::frag;
@@ -117,10 +120,11 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
-    // a split sequence: pass 1 runs every segment of each (b, h), pass 2 segments 1 .. nseg-1
-    const int segs = a.pass == 2 ? a.nseg - 1 : a.nseg;
+    // a split sequence: pass 1 runs segments 0 .. nseg-2 of each (b, h) (end states only), pass 2
+    // all of them
+    const int segs = a.pass == 1 ? a.nseg - 1 : a.nseg;
     const int64_t bh = a.pass ? (int64_t)blockIdx.x / segs : (int64_t)blockIdx.x;
-    const int seg = a.pass ? (int)(blockIdx.x % (unsigned)segs) + (a.pass == 2 ? 1 : 0) : 0;
+    const int seg = a.pass ? (int)(blockIdx.x % (unsigned)segs) : 0;
     const int64_t b = bh / a.H;
     const int h = (int)(bh % a.H);
     const int H = a.H, R = a.R, Q = a.Q;
@@ -139,11 +143,12 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         t_first += seg * a.seglen;
         L = min(a.seglen, a.L - seg * a.seglen);
     }
-    // pass 1 beyond segment 0 needs only the segment's end state: no C is read and no y stored
-    const bool states_only = a.pass == 1 && seg > 0;
-    // carried in: the call's carry (no split, or segment 0 of pass 1), none (the later segments of
-    // pass 1), or the previous segment's combined end state and its last step (pass 2)
-    const bool own_carry = a.pass == 0 || (a.pass == 1 && seg == 0);
+    // pass 1 needs only the segment's end state: no C is read and no y stored
+    const bool states_only = STATES || a.pass == 1;
+    // carried in: the call's carry (no split, or segment 0), none (the later segments in pass 1),
+    // or the previous segment's combined end state and its last step (the later segments in
+    // pass 2)
+    const bool own_carry = seg == 0;
     const int64_t nchunk = (L + Q - 1) / Q;
     const float Alog2 = a.A[h] * kLog2e;
     // (b, t = 0, h) bases; step t of this (b, h) is t * H rows further
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // part: 0 = Cbar rows, 1 = Bbar rows, 2 = x rows, 3 = step scalars; -1 = all
     auto load_chunk = [&](int64_t c, int set, int part = -1) {
         const int64_t t0 = c * Q;
-        if (part < 0 || part == 0) {
+        if (!STATES && (part < 0 || part == 0)) {
             const uint32_t o = step_off(t0, HRN);
 #pragma unroll
             for (int k = 0; k < MAXC; ++k)
@@ -338,20 +343,21 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         }
         float sc[2] = {1.f, 1.f};
         if (a.bcnorm) {   // RMS over the row's N values, spread over VPN consecutive lanes
-            float q2[2];
+            constexpr int NR = STATES ? 1 : 2;   // rows normalised: B (and C)
+            float q2[2] = {0.f, 0.f};
 #pragma unroll
-            for (int which = 0; which < 2; ++which) q2[which] = sumsq16(which == 0 ? rb[set][k] : rc[set][k], T{});
+            for (int which = 0; which < NR; ++which) q2[which] = sumsq16(which == 0 ? rb[set][k] : rc[set][k], T{});
             // the two rows' lane sums interleave
-            q2[0] = group_sum(q2[0], VPN);
-            q2[1] = group_sum(q2[1], VPN);
 #pragma unroll
-            for (int which = 0; which < 2; ++which)
+            for (int which = 0; which < NR; ++which) q2[which] = group_sum(q2[which], VPN);
+#pragma unroll
+            for (int which = 0; which < NR; ++which)
                 // hardware 1/sqrt; the clamp keeps its argument out of the denormal range (an
                 // all-zero row stays zero either way)
                 sc[which] = __builtin_amdgcn_rsqf(fmaxf(fmaf(q2[which], invN, a.eps), 1e-30f));
         }
 #pragma unroll
-        for (int which = 0; which < 2; ++which) {
+        for (int which = 0; which < (STATES ? 1 : 2); ++which) {
             float x[VE];
             unpack16(which == 0 ? rb[set][k] : rc[set][k], x, T{});
             const float* bw = sBias + (which * R + r) * N + n0;
@@ -414,7 +420,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
                 if (FUSED) {
                     stage_bc(set, j, i, buf);
                 } else {
-                    *(uint4*)(sC + buf * TC + i * LDC + cC0 * VE) = rc[set][j];
+                    if (!STATES) *(uint4*)(sC + buf * TC + i * LDC + cC0 * VE) = rc[set][j];
                     *(uint4*)(sB + buf * TB + i * LDB + cC0 * VE) = rb[set][j];
                 }
             }
@@ -515,12 +521,14 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         // two blocks' worth.
         F fc[2][NIB], fsb[2][NSLOT], fsc[2][NSLOT], fbt[2][NIB];
         auto fetch = [&](int k, int s) {
+            if constexpr (!STATES) {
 #pragma unroll
-            for (int ib = 0; ib < NIB; ++ib) fc[s][ib] = MM::ldk(tC + 16 * ib * LDC + 16 * k);
+                for (int ib = 0; ib < NIB; ++ib) fc[s][ib] = MM::ldk(tC + 16 * ib * LDC + 16 * k);
 #pragma unroll
-            for (int j = 0; j < NSLOT; ++j) {
-                fsb[s][j] = MM::ldk(pSB[j] + buf * TB + 16 * k);
-                fsc[s][j] = MM::ldk(pSC[j] + buf * TC + 16 * k);
+                for (int j = 0; j < NSLOT; ++j) {
+                    fsb[s][j] = MM::ldk(pSB[j] + buf * TB + 16 * k);
+                    fsc[s][j] = MM::ldk(pSC[j] + buf * TC + 16 * k);
+                }
             }
 #pragma unroll
             for (int sb = 0; sb < NIB; ++sb) fbt[s][sb] = MM::ldt(tBt + 16 * sb * LDB + 16 * k, LDB, l16);
@@ -532,13 +540,15 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             __builtin_amdgcn_sched_barrier(0);
             if (k + 1 < NB) fetch(k + 1, s ^ 1);
             hook(k);
-            // state part of Y^T, K block k (state rows 16k.., before the update)
-            const F sa = MM::pack(st[k]);
+            if constexpr (!STATES) {
+                // state part of Y^T, K block k (state rows 16k.., before the update)
+                const F sa = MM::pack(st[k]);
 #pragma unroll
-            for (int ib = 0; ib < NIB; ++ib) y[ib] = MM::mma(sa, fc[s][ib], y[ib]);
-            // this wave's S^T tiles
+                for (int ib = 0; ib < NIB; ++ib) y[ib] = MM::mma(sa, fc[s][ib], y[ib]);
+                // this wave's S^T tiles
 #pragma unroll
-            for (int j = 0; j < NSLOT; ++j) acc[j] = MM::mma(fsb[s][j], fsc[s][j], acc[j]);
+                for (int j = 0; j < NSLOT; ++j) acc[j] = MM::mma(fsb[s][j], fsc[s][j], acc[j]);
+            }
             // state rows of N block k
 #pragma unroll
             for (int m = 0; m < 4; ++m) st[k][m] *= dec;
@@ -547,6 +557,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         }
         __builtin_amdgcn_sched_barrier(0);
         after_part1();
+        if constexpr (!STATES) {
         // mask the score tiles: lane holds S^T[s = 16 sb + 4 g + m][i = 16 ib + l16]
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
@@ -573,7 +584,9 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
             for (int m = 0; m < 4; ++m) y[ib][m] *= el;
         }
+        }
         __syncthreads();
+        if constexpr (STATES) return;
 
         // ---- part 2: Y^T += X^T M^T, mixing, stores --------------------------------------
 #pragma unroll
@@ -748,8 +761,8 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 }
 
 // Between the passes of a split sequence, one workgroup per (b, h): the true end state of
-// segment s (1 <= s <= nseg - 2) is its local end state (from zero) plus the carried state that
-// enters it, decayed over the segment:
+// segment s (1 <= s <= nseg - 2) is its local end state (from zero, pass 1) plus the carried
+// state that enters it, decayed over the segment:
 //   g_end(s) = g_local(s) + exp(A sum_{t in s} dt_t) (g_end(s - 1) + c_{t0} Bbar_{t0-1}^T x_{t0-1})
 // with t0 the segment's first step and c_{t0} = (1 - lambda_{t0}) dt_{t0}: the recurrence is linear
 // in its carry, and the carry term is the one the scan adds for a carried (Bbar_prev, x_prev).
@@ -788,23 +801,28 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(PrefillArgs a) {
     }
 }
 
-template <typename T, int N, int P, bool FUSED>
-hipError_t launch_np(const PrefillArgs& a, hipStream_t s) {
-    const int64_t per_bh = a.pass == 0 ? 1 : (a.pass == 1 ? a.nseg : a.nseg - 1);
+template <typename T, int N, int P, bool FUSED, bool STATES>
+hipError_t launch_nps(const PrefillArgs& a, hipStream_t s) {
+    const int64_t per_bh = a.pass == 0 ? 1 : (a.pass == 1 ? a.nseg - 1 : a.nseg);
     const dim3 grid((unsigned)(a.b * a.H * per_bh)), block(P / 16 * 64);
     // fused: BCNorm weights and biases in dynamic LDS
     const size_t dyn = FUSED ? (size_t)(2 * N + 2 * a.R * N) * sizeof(float) : 0;
     switch (a.Q * a.R) {
-        case 16: hipLaunchKernelGGL((prefill_kernel<T, N, P, 1, FUSED>), grid, block, dyn, s, a); break;
-        case 32: hipLaunchKernelGGL((prefill_kernel<T, N, P, 2, FUSED>), grid, block, dyn, s, a); break;
+        case 16: hipLaunchKernelGGL((prefill_kernel<T, N, P, 1, FUSED, STATES>), grid, block, dyn, s, a); break;
+        case 32: hipLaunchKernelGGL((prefill_kernel<T, N, P, 2, FUSED, STATES>), grid, block, dyn, s, a); break;
         case 48:
-            if (FUSED) return hipErrorInvalidValue;
+            if (FUSED || STATES) return hipErrorInvalidValue;   // never split (48 does not divide 512)
             hipLaunchKernelGGL((prefill_kernel<T, N, P, 3, false>), grid, block, 0, s, a);
             break;
-        case 64: hipLaunchKernelGGL((prefill_kernel<T, N, P, 4, FUSED>), grid, block, dyn, s, a); break;
+        case 64: hipLaunchKernelGGL((prefill_kernel<T, N, P, 4, FUSED, STATES>), grid, block, dyn, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <typename T, int N, int P, bool FUSED>
+hipError_t launch_np(const PrefillArgs& a, hipStream_t s) {
+    return a.pass == 1 ? launch_nps<T, N, P, FUSED, true>(a, s) : launch_nps<T, N, P, FUSED, false>(a, s);
 }
 
 template <typename T, bool FUSED>
