@@ -140,12 +140,13 @@ int device_cus() {
 // Sequence split of a prefill call (m3_prefill, m3_layer_prefill): when the (b, h) pairs are too
 // few to give every compute unit two workgroups, each sequence is cut into segments of a
 // multiple of 512 steps (at least 1024 each) that run in parallel, then are chained (see
-// PrefillArgs).  Workspace: the segments' end states, the rotated Bbar of their last steps and,
-// fused, the start angles of every 512-step angle segment and a final-angle scratch row.
+// PrefillArgs).  Workspace: the segments' end states, the rotated Bbar of their last steps, their
+// log2 decays and, fused, the start angles of every 512-step angle segment and a final-angle
+// scratch row.
 struct SplitPlan {
     int nseg = 1;
     int64_t seglen = 0, nsegA = 0;
-    size_t off_state = 0, off_bbar = 0, off_phi = 0, off_phiend = 0, total = 0;
+    size_t off_state = 0, off_bbar = 0, off_l2 = 0, off_phi = 0, off_phiend = 0, total = 0;
 };
 constexpr int64_t kSplitAlign = 512, kSplitMin = 1024;
 
@@ -168,7 +169,8 @@ SplitPlan split_plan(const m3_dims* d, int64_t Q, bool fused, bool packed) {
     const size_t es = d->io == M3_BF16 ? 2 : 4;
     sp.off_state = 0;
     sp.off_bbar = align256((size_t)(pairs * nseg * N * P) * 4);
-    sp.total = sp.off_bbar + align256((size_t)(pairs * nseg * R * N) * es);
+    sp.off_l2 = sp.off_bbar + align256((size_t)(pairs * nseg * R * N) * es);
+    sp.total = sp.off_l2 + align256((size_t)(pairs * nseg) * 4);
     if (fused) {
         sp.nsegA = (L + m3::bcnorm_rope_seglen() - 1) / m3::bcnorm_rope_seglen();
         sp.off_phi = sp.total;
@@ -198,6 +200,7 @@ hipError_t run_split(m3::PrefillArgs a, const SplitPlan& sp, void* ws, bool fuse
     a.seglen = sp.seglen;
     a.ws_state = (float*)(w + sp.off_state);
     a.ws_bbar = w + sp.off_bbar;
+    a.ws_l2 = (float*)(w + sp.off_l2);
     hipError_t e = hipSuccess;
     if (fused) {
         m3::BcnormRopeArgs g{};

@@ -382,6 +382,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // the last wave (the one with the fewest score tiles): the chunk's per-step scalars (lane =
     // step) -> per-row copies in LDS.  Lanes past the chunk only add to later lanes of the scan,
     // which are never read.
+    float l2sum = 0.f;   // STATES: the segment's log2 decay, sum of the chunks' (last wave)
     auto stage_scalars = [&](float d, float lm, float dn63, float lmn63, int buf) {
         // dt, lambda of step t + 1: the next lane's, lane 63's own load (the shuffles run in every
         // lane: a lane reading an inactive lane would get zero)
@@ -392,6 +393,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         const float gam = lm * d;
         const float mu = gam + (1.0f - lmn) * dn;
         const float l2end = lane_value(l2, Q - 1);
+        if (STATES) l2sum += l2end;
         const float el = fast_exp2(l2);
         const float w = fast_exp2(fminf(l2end - l2, 0.f)) * mu;
         float* o = rL2 + buf * 64;
@@ -727,6 +729,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
                            : (last_seg && a.Bbar_last ? (T*)a.Bbar_last + bh * (int64_t)(R * N) : nullptr);
     T* xlast = a.pass != 1 && last_seg && a.x_last ? (T*)a.x_last + bh * (int64_t)(R * P) : nullptr;
     float* phout = FUSED && a.pass != 1 && last_seg && a.phi_out ? a.phi_out + bh * K : nullptr;
+    if (STATES && wave == NW - 1 && lane == 0) a.ws_l2[bh * a.nseg + seg] = l2sum;
     if (hout) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -760,44 +763,45 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     }
 }
 
-// Between the passes of a split sequence, one workgroup per (b, h): the true end state of
-// segment s (1 <= s <= nseg - 2) is its local end state (from zero, pass 1) plus the carried
-// state that enters it, decayed over the segment:
-//   g_end(s) = g_local(s) + exp(A sum_{t in s} dt_t) (g_end(s - 1) + c_{t0} Bbar_{t0-1}^T x_{t0-1})
-// with t0 the segment's first step and c_{t0} = (1 - lambda_{t0}) dt_{t0}: the recurrence is linear
-// in its carry, and the carry term is the one the scan adds for a carried (Bbar_prev, x_prev).
+// Between the passes of a split sequence: the true end state of segment s (1 <= s <= nseg - 2)
+// is its local end state (from zero, pass 1) plus the carried state that enters it, decayed over
+// the segment:
+//   g_end(s) = g_local(s) + 2^{l2(s)} (g_end(s - 1) + c_{t0} Bbar_{t0-1}^T x_{t0-1})
+// with l2(s) = log2 e * A * sum_{t in s} dt_t (saved by pass 1), t0 the segment's first step and
+// c_{t0} = (1 - lambda_{t0}) dt_{t0}: the recurrence is linear in its carry, and the carry term is
+// the one the scan adds for a carried (Bbar_prev, x_prev).  kCombineElems state elements per
+// workgroup (4 per thread, kept in registers along the chain).
+constexpr int kCombineElems = 1024;
 template <typename T>
 __global__ __launch_bounds__(256) void segment_combine_kernel(PrefillArgs a) {
-    __shared__ float red[4];
-    extern __shared__ __align__(16) float cl_lds[];   // Bbar row [R][N], x row [R][P] (fp32)
-    const int64_t bh = blockIdx.x, b = bh / a.H;
-    const int h = (int)(bh % a.H), tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int N = a.N, P = a.P, R = a.R, H = a.H;
     const int64_t NP = (int64_t)N * P;
-    float* sBr = cl_lds;
-    float* sXr = cl_lds + R * N;
+    const int G = (int)((NP + kCombineElems - 1) / kCombineElems);
+    const int64_t bh = blockIdx.x / G, b = bh / H;
+    const int h = (int)(bh % H), part = (int)(blockIdx.x % G);
+    float gp[4];
+    int64_t el[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        el[j] = (int64_t)part * kCombineElems + threadIdx.x + 256 * j;
+        gp[j] = el[j] < NP ? a.ws_state[bh * a.nseg * NP + el[j]] : 0.f;   // segment 0: already true
+    }
     for (int s = 1; s + 1 < a.nseg; ++s) {
-        const int64_t t0 = s * a.seglen, t1 = min(t0 + a.seglen, a.L);
-        float acc = 0.f;
-        for (int64_t t = t0 + tid; t < t1; t += 256) acc += load_f32((const T*)a.dt + (b * a.L + t) * H + h);
-        for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-        if (lane == 0) red[wave] = acc;
-        const int64_t row0 = (b * a.L + t0) * H + h;   // step t0 of this head
-        for (int e = tid; e < R * N; e += 256)
-            sBr[e] = load_f32((const T*)a.ws_bbar + (bh * a.nseg + s - 1) * (int64_t)(R * N) + e);
-        for (int e = tid; e < R * P; e += 256) sXr[e] = load_f32((const T*)a.x + (row0 - H) * R * P + e);
-        __syncthreads();
-        const float decay = expf(a.A[h] * (red[0] + red[1] + red[2] + red[3]));
+        const float decay = exp2f(a.ws_l2[bh * a.nseg + s]);
+        const int64_t row0 = (b * a.L + s * a.seglen) * H + h;   // step t0 of this head
         const float c0 = (1.0f - load_f32((const T*)a.lam + row0)) * load_f32((const T*)a.dt + row0);
-        const float* gprev = a.ws_state + (bh * a.nseg + s - 1) * NP;
-        float* gcur = a.ws_state + (bh * a.nseg + s) * NP;
-        for (int64_t e = tid; e < NP; e += 256) {
-            const int n = (int)(e / P), p = (int)(e % P);
+        const T* Bp = (const T*)a.ws_bbar + (bh * a.nseg + s - 1) * (int64_t)(R * N);
+        const T* xp = (const T*)a.x + (row0 - H) * R * P;
+        float* gs = a.ws_state + (bh * a.nseg + s) * NP;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (el[j] >= NP) continue;
+            const int n = (int)(el[j] / P), p = (int)(el[j] % P);
             float u = 0.f;
-            for (int r = 0; r < R; ++r) u = fmaf(sBr[r * N + n], sXr[r * P + p], u);
-            gcur[e] = fmaf(decay, fmaf(c0, u, gprev[e]), gcur[e]);
+            for (int r = 0; r < R; ++r) u = fmaf(load_f32(Bp + r * N + n), load_f32(xp + r * P + p), u);
+            gp[j] = fmaf(decay, fmaf(c0, u, gp[j]), gs[el[j]]);
+            gs[el[j]] = gp[j];
         }
-        __syncthreads();   // the next segment reuses red and the LDS rows
     }
 }
 
@@ -856,11 +860,12 @@ hipError_t launch_layer(const PrefillArgs& a, bool bf16_io, hipStream_t s) {
 }
 
 hipError_t launch_segment_combine(const PrefillArgs& a, bool bf16_io, hipStream_t s) {
-    const size_t lds = (size_t)(a.R * a.N + a.R * a.P) * sizeof(float);
+    const int64_t G = ((int64_t)a.N * a.P + kCombineElems - 1) / kCombineElems;
+    const dim3 grid((unsigned)(a.b * a.H * G));
     if (bf16_io)
-        hipLaunchKernelGGL(segment_combine_kernel<bf16>, dim3((unsigned)(a.b * a.H)), dim3(256), lds, s, a);
+        hipLaunchKernelGGL(segment_combine_kernel<bf16>, grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(segment_combine_kernel<float>, dim3((unsigned)(a.b * a.H)), dim3(256), lds, s, a);
+        hipLaunchKernelGGL(segment_combine_kernel<float>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -177,12 +177,13 @@ def test_sequence_split_workspace_sizes():
     are assumed, so the split aims at 512 workgroups)."""
     kw = dict(batch=1, seqlen=16384, nheads=64, rank=4, chunk=16)
     # 64 pairs -> 8 segments of 2048 steps: end states [64, 8, 128, 64] f32, last Bbar rows
-    # [64, 8, 4, 128] bf16
-    state, bbar = 64 * 8 * 128 * 64 * 4, 64 * 8 * 4 * 128 * 2
-    assert m3scan.prefill_workspace_bytes(_dims(**kw)) == state + bbar
+    # [64, 8, 4, 128] bf16, log2 decays [64, 8] f32
+    state, bbar, decay = 64 * 8 * 128 * 64 * 4, 64 * 8 * 4 * 128 * 2, 64 * 8 * 4
+    assert m3scan.prefill_workspace_bytes(_dims(**kw)) == state + bbar + decay
     # fused, chunk 8 (32 rows): plus 32 angle segments x 4 quarters x 64 angles and one final row
     fused = dict(kw, chunk=8)
-    assert m3scan.layer_prefill_workspace_bytes(_dims(**fused)) == state + bbar + 64 * 32 * 4 * 64 * 4 + 64 * 64 * 4
+    assert m3scan.layer_prefill_workspace_bytes(_dims(**fused)) == \
+        state + bbar + decay + 64 * 32 * 4 * 64 * 4 + 64 * 64 * 4
     # enough pairs, too short a sequence, or a chunk that does not divide 512: no split
     assert m3scan.prefill_workspace_bytes(_dims(batch=8, seqlen=2048, nheads=64)) == 0
     assert m3scan.prefill_workspace_bytes(_dims(batch=1, seqlen=2047, nheads=64)) == 0
@@ -192,7 +193,7 @@ def test_sequence_split_workspace_sizes():
     # 1536 steps (a multiple of 512); workspace sections are padded to 256 bytes
     r = lambda n: (n + 255) // 256 * 256
     assert m3scan.prefill_workspace_bytes(_dims(batch=1, seqlen=3000, nheads=2, rank=1, chunk=32)) == \
-        r(2 * 2 * 128 * 64 * 4) + r(2 * 2 * 1 * 128 * 2)
+        r(2 * 2 * 128 * 64 * 4) + r(2 * 2 * 1 * 128 * 2) + r(2 * 2 * 4)
 
 
 def test_binding_raises_without_the_library(tmp_path, monkeypatch):
