@@ -141,8 +141,8 @@ int device_cus() {
 // few to give every compute unit two workgroups, each sequence is cut into segments of a
 // multiple of 512 steps (at least 1024 each) that run in parallel, then are chained (see
 // PrefillArgs).  Workspace: the segments' end states, the rotated Bbar of their last steps, their
-// log2 decays and, fused, the start angles of every 512-step angle segment and a final-angle
-// scratch row.
+// log2 decays and, fused, the start angles of each segment's quarters (m3_bcnorm_rope's angle
+// kernels over the same segments) and a final-angle scratch row.
 struct SplitPlan {
     int nseg = 1;
     int64_t seglen = 0, nsegA = 0;
@@ -172,7 +172,7 @@ SplitPlan split_plan(const m3_dims* d, int64_t Q, bool fused, bool packed) {
     sp.off_l2 = sp.off_bbar + align256((size_t)(pairs * nseg * R * N) * es);
     sp.total = sp.off_l2 + align256((size_t)(pairs * nseg) * 4);
     if (fused) {
-        sp.nsegA = (L + m3::bcnorm_rope_seglen() - 1) / m3::bcnorm_rope_seglen();
+        sp.nsegA = nseg;   // the angle pass sums dt * theta over the same segments
         sp.off_phi = sp.total;
         sp.off_phiend = sp.off_phi + align256((size_t)(pairs * sp.nsegA * m3::bcnorm_rope_parts() * (N / 2)) * 4);
         sp.total = sp.off_phiend + align256((size_t)(pairs * (N / 2)) * 4);
@@ -214,7 +214,7 @@ hipError_t run_split(m3::PrefillArgs a, const SplitPlan& sp, void* ws, bool fuse
         g.H = a.H;
         g.N = a.N;
         g.R = a.R;
-        g.seglen = m3::bcnorm_rope_seglen();
+        g.seglen = sp.seglen;
         g.nseg = (int)sp.nsegA;
         e = m3::launch_segment_angles(g, bf16, s);
         a.seg_phi = g.seg_phi;

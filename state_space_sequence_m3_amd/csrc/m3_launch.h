@@ -103,7 +103,7 @@ struct PrefillArgs {
     void* ws_bbar = nullptr;         // [b, H, nseg, R, N] io, rotated Bbar of each segment's last step
     float* ws_l2 = nullptr;          // [b, H, nseg] log2 decay of each segment (log2 e A sum of dt)
     const float* seg_phi = nullptr;  // fused: angle-segment start angles [b, H, nsegA, parts, N/2] (radians)
-    int64_t angle_seglen = 0;        // steps per angle segment (a divisor of seglen)
+    int64_t angle_seglen = 0;        // steps per angle segment (seglen or a divisor of it)
     int angle_parts = 0;             // start angles per angle segment
 };
 

@@ -180,10 +180,11 @@ def test_sequence_split_workspace_sizes():
     # [64, 8, 4, 128] bf16, log2 decays [64, 8] f32
     state, bbar, decay = 64 * 8 * 128 * 64 * 4, 64 * 8 * 4 * 128 * 2, 64 * 8 * 4
     assert m3scan.prefill_workspace_bytes(_dims(**kw)) == state + bbar + decay
-    # fused, chunk 8 (32 rows): plus 32 angle segments x 4 quarters x 64 angles and one final row
+    # fused, chunk 8 (32 rows): plus the start angles of each segment's 4 quarters (64 angles)
+    # and one final row
     fused = dict(kw, chunk=8)
     assert m3scan.layer_prefill_workspace_bytes(_dims(**fused)) == \
-        state + bbar + decay + 64 * 32 * 4 * 64 * 4 + 64 * 64 * 4
+        state + bbar + decay + 64 * 8 * 4 * 64 * 4 + 64 * 64 * 4
     # enough pairs, too short a sequence, or a chunk that does not divide 512: no split
     assert m3scan.prefill_workspace_bytes(_dims(batch=8, seqlen=2048, nheads=64)) == 0
     assert m3scan.prefill_workspace_bytes(_dims(batch=1, seqlen=2047, nheads=64)) == 0
