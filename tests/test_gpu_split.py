@@ -24,6 +24,8 @@ SPLIT_CASES = [
     ("bf16", 1, 5000, 2, 64, 128, 4, 8, 16, True, True),     # 4 segments: chaining runs twice
     ("f32", 1, 4100, 1, 16, 16, 2, 8, 16, True, True),       # 3 segments, fp32
     ("bf16", 1, 4096, 2, 64, 64, 1, 32, 32, False, False),   # N = 64, segments of 1024
+    ("bf16", 2, 3500, 1, 64, 128, 2, 8, 32, True, True),     # b = 2, 16-row fused chunks
+    ("bf16", 3, 2100, 1, 64, 128, 1, 16, 16, False, True),   # b = 3, chunk 16 in both calls
 ]
 
 
