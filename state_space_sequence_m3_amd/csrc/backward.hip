@@ -421,21 +421,10 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
     }
     for (int e = tid; e < NW * 64; e += NT) pMu[e] = pLi[e] = pGam[e] = 0.f;
 
-    // ---- staging layout (B, C, state rows: vectors of rows iC0 + k RKC; x, dY: iX0 + k RKX)
+    // ---- staging layout (B, C, state rows: vectors of rows iC0 + k RKC; x, dY: iX0 + k RKX); the
+    // chunk loop recomputes these and its row offsets from the thread index
     const int iC0 = tid / VPN, cC0 = tid % VPN, iX0 = tid / VPP, cX0 = tid % VPP;
     const int rC = iC0 & (R - 1), rX = iX0 & (R - 1);
-    auto offC = [&](int k) {
-        const int i = iC0 + k * RKC;
-        return (uint32_t)(((i >> RL2) * (int)HRN + (i & (R - 1)) * N + cC0 * VE) * (int)sizeof(T));
-    };
-    auto offX = [&](int k) {
-        const int i = iX0 + k * RKX;
-        return (uint32_t)(((i >> RL2) * (int)HRP + (i & (R - 1)) * P + cX0 * VE) * (int)sizeof(T));
-    };
-    auto offY = [&](int k) {   // dy: mixed rows are per step
-        const int i = iX0 + k * RKX;
-        return mix ? (uint32_t)(((i >> RL2) * H * P + cX0 * VE) * (int)sizeof(T)) : offX(k);
-    };
     float wmix[VE];   // w_out of this thread's (r, columns) for the dY staging
 #pragma unroll
     for (int e = 0; e < VE; ++e) wmix[e] = mix ? a.w_out[(h * R + rX) * P + cX0 * VE + e] : 1.f;
@@ -484,9 +473,32 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
         sIb[j] = tile_ib(tau);
         sSb[j] = tau - sIb[j] * (sIb[j] + 1) / 2;
     }
-    const int wrow = 16 * wave + l16;   // this lane's chunk row in the wave-owned row block
 
     for (int64_t c = nchunk - 1; c >= 0; --c) {
+        // The thread-index arithmetic is redone each chunk from an opaque copy of the index (a
+        // register move the compiler cannot look through): hoisted out of the loop, the offsets
+        // were kept in scratch memory and reloaded every chunk, a memory round trip per use that
+        // one wave per SIMD cannot hide; recomputed, each costs a few VALU instructions.
+        int tid_o;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(tid_o) : "v"(tid));
+        const int tid = tid_o, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+        const int iC0 = tid / VPN, cC0 = tid % VPN, iX0 = tid / VPP, cX0 = tid % VPP;
+        const int rC = iC0 & (R - 1);
+        const int tv = tid / TPV, tj = tid % TPV;
+        const bool scanner = tid < NVT * TPV;
+        const int wrow = 16 * wave + l16;   // this lane's chunk row in the wave-owned row block
+        auto offC = [&](int k) {
+            const int i = iC0 + k * RKC;
+            return (uint32_t)(((i >> RL2) * (int)HRN + (i & (R - 1)) * N + cC0 * VE) * (int)sizeof(T));
+        };
+        auto offX = [&](int k) {
+            const int i = iX0 + k * RKX;
+            return (uint32_t)(((i >> RL2) * (int)HRP + (i & (R - 1)) * P + cX0 * VE) * (int)sizeof(T));
+        };
+        auto offY = [&](int k) {   // dy: mixed rows are per step
+            const int i = iX0 + k * RKX;
+            return mix ? (uint32_t)(((i >> RL2) * H * P + cX0 * VE) * (int)sizeof(T)) : offX(k);
+        };
         const int64_t t0 = c * Q;
         // ================= S1: loads ===================================================
         uint4 rb[MAXC], rc[MAXC], rx[MAXX], ry[MAXX], rs[MAXS];
