@@ -377,7 +377,7 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
     __shared__ __align__(16) float pMu[NW * 64], pLi[NW * 64], pGam[NW * 64], rDw[64], rDlo[64];
     __shared__ float pSS[NW], red[NW];
     __shared__ __align__(16) float rotdd[NVT * 64];
-    __shared__ __align__(16) float sWt[2 * N], sBias[2 * R * N];
+    __shared__ __align__(16) float sWt[2 * N], sBias[2 * R * N], sWo[R * P];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -422,12 +422,13 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
     for (int e = tid; e < NW * 64; e += NT) pMu[e] = pLi[e] = pGam[e] = 0.f;
 
     // ---- staging layout (B, C, state rows: vectors of rows iC0 + k RKC; x, dY: iX0 + k RKX); the
-    // chunk loop recomputes these and its row offsets from the thread index
-    const int iC0 = tid / VPN, cC0 = tid % VPN, iX0 = tid / VPP, cX0 = tid % VPP;
-    const int rC = iC0 & (R - 1), rX = iX0 & (R - 1);
-    float wmix[VE];   // w_out of this thread's (r, columns) for the dY staging
-#pragma unroll
-    for (int e = 0; e < VE; ++e) wmix[e] = mix ? a.w_out[(h * R + rX) * P + cX0 * VE + e] : 1.f;
+    // chunk loop derives it and its row offsets from the thread index itself, the sums after the
+    // loop use the B/C rows' part
+    const int iC0 = tid / VPN, cC0 = tid % VPN;
+    const int rC = iC0 & (R - 1);
+    // w_out of this head for the dY staging, read from LDS in the chunk loop (kept in registers,
+    // the compiler spilled it)
+    for (int e = tid; e < R * P; e += NT) sWo[e] = mix ? a.w_out[h * R * P + e] : 1.f;
 
     // ---- angle layout and the running angle cotangent (starts at dphi_out)
     const int tv = tid / TPV, tj = tid % TPV;
@@ -598,7 +599,7 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
                 float f[VE];
                 unpack16(ry[k], f, T{});
 #pragma unroll
-                for (int e = 0; e < VE; ++e) f[e] *= wmix[e];
+                for (int e = 0; e < VE; ++e) f[e] *= sWo[(i & (R - 1)) * P + cX0 * VE + e];
                 *(uint4*)(sDY + i * LDX + cX0 * VE) = pack16(f, T{});
             } else {
                 *(uint4*)(sDY + i * LDX + cX0 * VE) = ry[k];
