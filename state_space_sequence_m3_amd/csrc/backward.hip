@@ -513,8 +513,8 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
 #pragma unroll
             for (int k = 0; k < MAXC; ++k) {
                 const bool in = S::FULLC || iC0 + k * RKC < QR;
-                rb[k] = buffer_load16_stream(dB, in ? offC(k) : 0x80000000u);
-                rc[k] = buffer_load16_stream(dC, in ? offC(k) : 0x80000000u);
+                rb[k] = buffer_load16(dB, in ? offC(k) : 0x80000000u);
+                rc[k] = buffer_load16(dC, in ? offC(k) : 0x80000000u);
             }
 #pragma unroll
             for (int k = 0; k < MAXX; ++k) {
@@ -899,6 +899,18 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
         __syncthreads();   // (4)
 
         // ================= S6: gradient rows to LDS (fp32) ==============================
+        // The raw B and C rows are read again for the adjoint below (the first read left them in
+        // L2): holding them from S1 through the products took registers that then spilled.
+        {
+            const uint32_t nbc = tail_bytes(t0, HRN, (int64_t)R * N);
+            const rsrc_t dB = make_rsrc(Bg + t0 * HRN, nbc), dC = make_rsrc(Cg + t0 * HRN, nbc);
+#pragma unroll
+            for (int k = 0; k < MAXC; ++k) {
+                const bool in = S::FULLC || iC0 + k * RKC < QR;
+                rb[k] = buffer_load16_stream(dB, in ? offC(k) : 0x80000000u);
+                rc[k] = buffer_load16_stream(dC, in ? offC(k) : 0x80000000u);
+            }
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             *(floatx4*)(fB + wrow * LDF + 16 * nb + 4 * g) = dba[nb];
