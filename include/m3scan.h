@@ -86,7 +86,24 @@ typedef struct {
     int32_t io;      /* m3_dtype of the io tensors                                            */
     uint32_t flags;  /* M3_BCNORM                                                             */
     float eps;       /* added to the mean square in BCNorm (e.g. 1e-5)                        */
+    int64_t ngroups; /* G: raw B and C shared by groups of H / G heads; 0 = one per head (G = H) */
 } m3_dims;
+
+/*
+ * Head groups (dims->ngroups).  The calls that take the raw projections B and C
+ * (m3_bcnorm_rope, m3_layer_prefill, m3_layer_prefill_varlen, m3_layer_decode_step,
+ * m3_layer_chunk_states, m3_layer_backward) accept them with G <= H head slots instead of H: head
+ * h reads slot h / (H / G), so the H / G consecutive heads of a group share one B and one C row.
+ * Each head still applies its own BCNorm weight, bias and rotation, and everything else (x, dt,
+ * theta, lambda, the state, the outputs, the rotated Bbar and Cbar) stays per head: the result
+ * is that of the same call with each group's rows repeated for every head of the group.  The
+ * pages define B and C per head; sharing them across heads is a layout option of this library
+ * that cuts the bytes of B and C read by H / G.  G must divide H (else M3_E_DIMS); 0 means H.
+ * m3_prefill and m3_decode_step take rotated, per-head Bbar and Cbar and require G = H (or 0).
+ * The layouts below write B and C as [.., H, R, N]; with groups read [.., G, R, N].  In
+ * m3_layer_backward the gradients dB and dC have the grouped layout: the sums over each group's
+ * heads.
+ */
 
 /*
  * m3_bcnorm_rope -- BCNorm, head bias and cumulative rotation of B and C.

@@ -20,6 +20,11 @@ composes them.  Every function cites the passage it follows:
                     exact gradients of the three forward functions above (reverse-mode through
                     the same steps in reverse order; the pages define no backward pass, so the
                     gradient of the forward definition is the definition followed).
+* ``heads_from_groups``, ``groups_from_heads``
+                    raw B and C with G < H head slots, shared by groups of H / G consecutive
+                    heads.  The pages define B and C per head; the shared layout is defined here
+                    as its expansion (head h reads slot h // (H / G)), and the gradient of a
+                    shared row is the sum of the gradients of the heads that read it.
 """
 from __future__ import annotations
 
@@ -93,15 +98,34 @@ def num_threads() -> int:
     return int(_load().m3o_num_threads())
 
 
+def heads_from_groups(v, H):
+    """Raw B or C [b, L, G, R, N] with G head slots -> [b, L, H, R, N]: head h reads slot
+    h // (H // G), so each slot serves the H / G consecutive heads of its group."""
+    v = _f64(v)
+    G = v.shape[2]
+    assert G >= 1 and H % G == 0
+    return np.repeat(v, H // G, axis=2)
+
+
+def groups_from_heads(g, G):
+    """Gradient of ``heads_from_groups``: [b, L, H, R, N] -> [b, L, G, R, N], each slot's
+    gradient the sum over the heads of its group."""
+    b, L, H, R, N = g.shape
+    return g.reshape(b, L, G, H // G, R, N).sum(axis=3)
+
+
 def bcnorm_rope(B, C, dt, theta, normw_B=None, normw_C=None, bias_B=None, bias_C=None,
                 phi_in=None, bcnorm=True, eps=1e-5, lib=None):
-    """BCNorm, bias and cumulative rotation for B, C of shape [b, L, H, R, N].
+    """BCNorm, bias and cumulative rotation for B, C of shape [b, L, H, R, N] (or [b, L, G, R, N]
+    with head slots shared by groups of heads: expanded by ``heads_from_groups``).
 
     dt is [b, L, H], theta is [b, L, H, N/2], normw_* are [H, N], bias_* are [H, R, N] and phi_in
     is [b, H, N/2] (each optional except B, C, dt, theta).  Returns (Bbar, Cbar, phi_out) with
-    phi_out the final cumulative angle, not reduced modulo 2*pi.
+    Bbar, Cbar [b, L, H, R, N] and phi_out the final cumulative angle, not reduced modulo 2*pi.
     """
     B, C, dt, theta = _f64(B), _f64(C), _f64(dt), _f64(theta)
+    if B.shape[2] != dt.shape[2]:
+        B, C = heads_from_groups(B, dt.shape[2]), heads_from_groups(C, dt.shape[2])
     nb, L, H, R, N = B.shape
     assert C.shape == B.shape and dt.shape == (nb, L, H) and theta.shape == (nb, L, H, N // 2)
     assert N % 2 == 0
@@ -170,7 +194,7 @@ def decode_step(state: dict, tok: dict, consts: dict, bcnorm=True, eps=1e-5, mix
     """One decode step = the layer core with L = 1 and everything carried.
 
     ``state`` holds h [b, H, N, P], phi [b, H, N/2], Bbar_prev [b, H, R, N], x_prev [b, H, R, P];
-    ``tok`` holds the new token's x [b, H, R, P], B, C [b, H, R, N], dt, lam [b, H] and
+    ``tok`` holds the new token's x [b, H, R, P], B, C [b, H, R, N] (or [b, G, R, N]), dt, lam [b, H] and
     theta [b, H, N/2]; ``consts`` holds A and optionally normw_B, normw_C, bias_B, bias_C, w_out.
     Returns (y, new_state) with y [b, H, P] (mixed) or [b, H, R, P].
     """
@@ -247,18 +271,27 @@ def layer_backward(inp: dict, dy, dh_out=None, dphi_out=None, bcnorm=True, eps=1
     ``bcnorm_rope_backward`` carries them back to the raw inputs.  dt reaches both the scan and
     the rotation angle, so its gradient is the sum of the two shares.  Returns a dict keyed by
     input name (x, B, C, dt, A, lam, theta, normw_B, normw_C, bias_B, bias_C, w_out, phi_in, h_in,
-    Bbar_prev, x_prev)."""
+    Bbar_prev, x_prev).  With raw B and C in G < H head slots, their gradients are summed over
+    each group's heads (``groups_from_heads``)."""
     g = inp.get
-    Bbar, Cbar, _ = bcnorm_rope(g("B"), g("C"), g("dt"), g("theta"), g("normw_B"), g("normw_C"),
+    H = _f64(g("dt")).shape[2]
+    B, C = _f64(g("B")), _f64(g("C"))
+    G = B.shape[2]
+    if G != H:
+        B, C = heads_from_groups(B, H), heads_from_groups(C, H)
+    Bbar, Cbar, _ = bcnorm_rope(B, C, g("dt"), g("theta"), g("normw_B"), g("normw_C"),
                                 g("bias_B"), g("bias_C"), g("phi_in"), bcnorm=bcnorm, eps=eps,
                                 lib=lib)
     gs = scan_backward(g("x"), Bbar, Cbar, g("dt"), g("A"), g("lam"), dy,
                        g("w_out") if mix else None, g("h_in"), g("Bbar_prev"), g("x_prev"),
                        dh_out, lib=lib)
-    gr = bcnorm_rope_backward(g("B"), g("C"), g("dt"), g("theta"), gs["Bbar"], gs["Cbar"],
+    gr = bcnorm_rope_backward(B, C, g("dt"), g("theta"), gs["Bbar"], gs["Cbar"],
                               g("normw_B"), g("normw_C"), g("bias_B"), g("bias_C"), g("phi_in"),
                               dphi_out, bcnorm=bcnorm, eps=eps, lib=lib)
-    return {"x": gs["x"], "B": gr["B"], "C": gr["C"], "dt": gs["dt"] + gr["dt"], "A": gs["A"],
+    dB, dC = gr["B"], gr["C"]
+    if G != H:
+        dB, dC = groups_from_heads(dB, G), groups_from_heads(dC, G)
+    return {"x": gs["x"], "B": dB, "C": dC, "dt": gs["dt"] + gr["dt"], "A": gs["A"],
             "lam": gs["lam"], "theta": gr["theta"], "normw_B": gr["normw_B"],
             "normw_C": gr["normw_C"], "bias_B": gr["bias_B"], "bias_C": gr["bias_C"],
             "w_out": gs["w_out"], "phi_in": gr["phi_in"], "h_in": gs["h_in"],

@@ -72,6 +72,21 @@ m3_status check_common_dims(const m3_dims* d) {
         d->rank > 64)
         return fail(M3_E_DIMS, "size out of range");
     if (d->dstate % 2 != 0) return fail(M3_E_DIMS, "dstate N = %lld must be even", (long long)d->dstate);
+    if (d->ngroups < 0 || d->ngroups > d->nheads || (d->ngroups > 0 && d->nheads % d->ngroups != 0))
+        return fail(M3_E_DIMS, "ngroups G = %lld must be 0 or divide nheads H = %lld", (long long)d->ngroups,
+                    (long long)d->nheads);
+    return M3_OK;
+}
+
+// head slots of raw B and C (G; H when every head has its own), and the kernels' group field
+// (0 for one slot per head)
+int64_t bc_groups(const m3_dims* d) { return d->ngroups > 0 ? d->ngroups : d->nheads; }
+int kernel_groups(const m3_dims* d) { return d->ngroups > 0 && d->ngroups < d->nheads ? (int)d->ngroups : 0; }
+
+// the calls that take rotated, per-head Bbar and Cbar
+m3_status check_per_head(const m3_dims* d, const char* fn) {
+    if (bc_groups(d) != d->nheads)
+        return fail(M3_E_DIMS, "%s takes per-head Bbar and Cbar: dims->ngroups must be 0 or nheads", fn);
     return M3_OK;
 }
 
@@ -248,7 +263,7 @@ m3_status layer_prefill(const m3_dims* d, bool packed, const int32_t* cu_seqlens
     const int64_t L = d->seqlen, BL = packed ? L : b * L;
     const int64_t Q = d->chunk > 0 ? d->chunk : (32 / R > 0 ? 32 / R : 1);
     const size_t es = io_size(d);
-    const size_t nX = (size_t)(BL * H * R * P) * es, nBC = (size_t)(BL * H * R * N) * es;
+    const size_t nX = (size_t)(BL * H * R * P) * es, nBC = (size_t)(BL * bc_groups(d) * R * N) * es;
     const size_t nStep = (size_t)(BL * H) * es, nA = (size_t)H * 4;
     const size_t nTh = (size_t)(BL * H * (N / 2)) * es, nPhi = (size_t)(b * H * (N / 2)) * 4;
     const size_t nY = (size_t)(BL * H * (w_out ? 1 : R) * P) * es, nH = (size_t)(b * H * N * P) * 4;
@@ -325,6 +340,7 @@ m3_status layer_prefill(const m3_dims* d, bool packed, const int32_t* cu_seqlens
     a.phi_in = phi_in; a.phi_out = phi_out;
     a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;
     a.eps = d->eps;
+    a.G = kernel_groups(d);
     if (packed) {
         a.cu_seqlens = cu_seqlens;
         a.T = L;
@@ -349,13 +365,16 @@ struct BwdLayout {
     int64_t Q = 0, nchunk = 0;
     int rec = 0;
     size_t st_bytes = 0, phi_off = 0, phi_bytes = 0, part_off = 0, part_bytes = 0, total = 0;
+    // head groups: per-head dB and dC rows (H / G planes of the grouped layout each)
+    size_t gB_off = 0, gC_off = 0, g_bytes = 0;
 };
 
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 bool bwd_layout(const m3_dims* d, BwdLayout* o) {
     if (!d || (d->io != M3_F32 && d->io != M3_BF16) || d->rank < 1 || d->batch < 0 || d->seqlen < 0 ||
-        d->nheads < 0)
+        d->nheads < 0 || d->ngroups < 0 || d->ngroups > d->nheads ||
+        (d->ngroups > 0 && d->nheads % d->ngroups != 0))
         return false;
     if (!m3::backward_supported((int)d->dstate, (int)d->headdim, (int)d->rank)) return false;
     const int64_t rows = m3::backward_chunk_rows((int)d->headdim, d->io == M3_BF16);
@@ -369,6 +388,12 @@ bool bwd_layout(const m3_dims* d, BwdLayout* o) {
     o->part_off = o->phi_off + round256(o->phi_bytes);
     o->part_bytes = (size_t)(b * H * o->rec) * 4;
     o->total = o->part_off + round256(o->part_bytes);
+    if (kernel_groups(d) > 0) {
+        o->g_bytes = (size_t)(b * d->seqlen * H * R * N) * io_size(d);
+        o->gB_off = o->total;
+        o->gC_off = o->gB_off + round256(o->g_bytes);
+        o->total = o->gC_off + round256(o->g_bytes);
+    }
     return true;
 }
 
@@ -378,7 +403,7 @@ extern "C" {
 
 const char* m3_last_error(void) { return g_err; }
 
-const char* m3_version(void) { return "libm3scan 0.1.0 gfx950"; }
+const char* m3_version(void) { return "libm3scan 0.2.0 gfx950"; }
 
 size_t m3_bcnorm_rope_workspace_bytes(const m3_dims* d) {
     if (!d || d->batch <= 0 || d->nheads <= 0 || d->seqlen <= 0 || d->dstate <= 0) return 0;
@@ -409,8 +434,9 @@ m3_status m3_bcnorm_rope(const m3_dims* d, const void* B, const void* C, const v
     const int64_t b = d->batch, L = d->seqlen, H = d->nheads, N = d->dstate, R = d->rank;
     const size_t es = io_size(d);
     const size_t nBC = (size_t)(b * L * H * R * N) * es, nStep = (size_t)(b * L * H) * es;
+    const size_t nIn = (size_t)(b * L * bc_groups(d) * R * N) * es;   // raw B, C: G head slots
     const size_t nTh = (size_t)(b * L * H * (N / 2)) * es, nPhi = (size_t)(b * H * (N / 2)) * 4;
-    const Buf req[] = {{B, nBC, "B"}, {C, nBC, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
+    const Buf req[] = {{B, nIn, "B"}, {C, nIn, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
                        {Bbar, nBC, "Bbar"}, {Cbar, nBC, "Cbar"}, {phi_out, nPhi, "phi_out"}};
     if ((s = check_required(req, 7)) != M3_OK) return s;
     if (!m3::bcnorm_rope_supported((int)N, (int)R))
@@ -428,7 +454,7 @@ m3_status m3_bcnorm_rope(const m3_dims* d, const void* B, const void* C, const v
     if (bias_B && !aligned(bias_B, 16)) return fail(M3_E_ALIGN, "bias_B is not 16-byte aligned");
     if (bias_C && !aligned(bias_C, 16)) return fail(M3_E_ALIGN, "bias_C is not 16-byte aligned");
     const size_t nW = (size_t)(H * N) * 4, nBias = (size_t)(H * R * N) * 4;
-    const Buf ins[] = {{B, nBC, "B"}, {C, nBC, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
+    const Buf ins[] = {{B, nIn, "B"}, {C, nIn, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
                        {normw_B, nW, "normw_B"}, {normw_C, nW, "normw_C"}, {bias_B, nBias, "bias_B"},
                        {bias_C, nBias, "bias_C"}};
     const size_t need = m3_bcnorm_rope_workspace_bytes(d);
@@ -462,6 +488,7 @@ m3_status m3_bcnorm_rope(const m3_dims* d, const void* B, const void* C, const v
     a.seglen = seg; a.nseg = (int)nseg;
     a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;
     a.eps = d->eps;
+    a.G = kernel_groups(d);
     return launched(m3::launch_bcnorm_rope(a, d->io == M3_BF16, stream), "m3_bcnorm_rope");
 }
 
@@ -471,6 +498,7 @@ m3_status m3_prefill(const m3_dims* d, const void* x, const void* Bbar, const vo
                      size_t workspace_bytes, hipStream_t stream) {
     m3_status s = check_common_dims(d);
     if (s != M3_OK) return s;
+    if ((s = check_per_head(d, "m3_prefill")) != M3_OK) return s;
     const int64_t b = d->batch, L = d->seqlen, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
     const int64_t Q = d->chunk > 0 ? d->chunk : (64 / R > 0 ? 64 / R : 1);
     const size_t es = io_size(d);
@@ -560,6 +588,7 @@ m3_status m3_decode_step(const m3_dims* d, float* h, const void* Bbar_prev, cons
     m3_status s = check_common_dims(d);
     if (s != M3_OK) return s;
     if (d->seqlen != 1) return fail(M3_E_DIMS, "m3_decode_step: dims->seqlen must be 1, got %lld", (long long)d->seqlen);
+    if ((s = check_per_head(d, "m3_decode_step")) != M3_OK) return s;
     const int64_t b = d->batch, H = d->nheads, N = d->dstate, P = d->headdim, R = d->rank;
     const size_t es = io_size(d);
     const size_t nH = (size_t)(b * H * N * P) * 4, nBp = (size_t)(b * H * R * N) * es;
@@ -610,8 +639,9 @@ m3_status m3_layer_decode_step(const m3_dims* d, float* h, float* phi, const voi
     const size_t nY = (size_t)(b * H * (w_out ? 1 : R) * P) * es, nWo = (size_t)(H * R * P) * 4;
     const size_t nTh = (size_t)(b * H * (N / 2)) * es, nPhi = (size_t)(b * H * (N / 2)) * 4;
     const size_t nW = (size_t)(H * N) * 4, nBias = (size_t)(H * R * N) * 4;
+    const size_t nIn = (size_t)(b * bc_groups(d) * R * N) * es;   // raw B, C: G head slots
     const Buf req[] = {{h, nH, "h"}, {phi, nPhi, "phi"}, {Bbar_prev, nBp, "Bbar_prev"}, {x_prev, nXp, "x_prev"},
-                       {x, nXp, "x"}, {B, nBp, "B"}, {C, nBp, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
+                       {x, nXp, "x"}, {B, nIn, "B"}, {C, nIn, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"},
                        {A, nA, "A"}, {lam, nStep, "lam"}, {y, nY, "y"}, {Bbar_out, nBp, "Bbar_out"}};
     if ((s = check_required(req, 13)) != M3_OK) return s;
     if (!m3::decode_supported((int)N, (int)P, (int)R))
@@ -627,8 +657,8 @@ m3_status m3_layer_decode_step(const m3_dims* d, float* h, float* phi, const voi
     const Buf a4[] = {{A, 1, "A"}, {w_out, 1, "w_out"}, {phi, 1, "phi"}, {normw_B, 1, "normw_B"},
                       {normw_C, 1, "normw_C"}, {bias_B, 1, "bias_B"}, {bias_C, 1, "bias_C"}};
     if ((s = check_align(a4, 7, 4)) != M3_OK) return s;
-    const Buf ins[] = {{Bbar_prev, nBp, "Bbar_prev"}, {x_prev, nXp, "x_prev"}, {x, nXp, "x"}, {B, nBp, "B"},
-                       {C, nBp, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"}, {A, nA, "A"}, {lam, nStep, "lam"},
+    const Buf ins[] = {{Bbar_prev, nBp, "Bbar_prev"}, {x_prev, nXp, "x_prev"}, {x, nXp, "x"}, {B, nIn, "B"},
+                       {C, nIn, "C"}, {dt, nStep, "dt"}, {theta, nTh, "theta"}, {A, nA, "A"}, {lam, nStep, "lam"},
                        {w_out, nWo, "w_out"}, {normw_B, nW, "normw_B"}, {normw_C, nW, "normw_C"},
                        {bias_B, nBias, "bias_B"}, {bias_C, nBias, "bias_C"}};
     const Buf outs[] = {{h, nH, "h"}, {phi, nPhi, "phi"}, {y, nY, "y"}, {Bbar_out, nBp, "Bbar_out"}};
@@ -648,6 +678,7 @@ m3_status m3_layer_decode_step(const m3_dims* d, float* h, float* phi, const voi
     a.phi = phi; a.Bbar_out = Bbar_out;
     a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;
     a.eps = d->eps;
+    a.G = kernel_groups(d);
     return launched(m3::launch_layer_decode(a, d->io == M3_BF16, stream), "m3_layer_decode_step");
 }
 
@@ -674,7 +705,7 @@ m3_status m3_layer_chunk_states(const m3_dims* d, const void* x, const void* B, 
                     "m3_layer_chunk_states: no kernel for N = %lld, P = %lld, R = %lld (supported: (N,P) in "
                     "{(16,16),(64,64),(128,64)}, R in {1,2,4})", (long long)N, (long long)P, (long long)R);
     const size_t es = io_size(d);
-    const size_t nX = (size_t)(b * L * H * R * P) * es, nBC = (size_t)(b * L * H * R * N) * es;
+    const size_t nX = (size_t)(b * L * H * R * P) * es, nBC = (size_t)(b * L * bc_groups(d) * R * N) * es;
     const size_t nStep = (size_t)(b * L * H) * es, nA = (size_t)H * 4;
     const size_t nTh = (size_t)(b * L * H * (N / 2)) * es, nPhi = (size_t)(b * H * (N / 2)) * 4;
     const size_t nH = (size_t)(b * H * N * P) * 4, nBp = (size_t)(b * H * R * N) * es;
@@ -707,6 +738,7 @@ m3_status m3_layer_chunk_states(const m3_dims* d, const void* x, const void* B, 
     a.b = b; a.L = L; a.H = (int)H; a.N = (int)N; a.P = (int)P; a.R = (int)R;
     a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;
     a.eps = d->eps;
+    a.G = kernel_groups(d);
     return launched(m3::launch_chunk_states(a, d->io == M3_BF16, stream), "m3_layer_chunk_states");
 }
 
@@ -731,7 +763,7 @@ m3_status m3_layer_backward(const m3_dims* d, const void* x, const void* B, cons
         return fail(M3_E_UNSUPPORTED, "m3_layer_backward: chunk must be 0 or %lld for these dims",
                     (long long)lay.Q);
     const size_t es = io_size(d);
-    const size_t nX = (size_t)(b * L * H * R * P) * es, nBC = (size_t)(b * L * H * R * N) * es;
+    const size_t nX = (size_t)(b * L * H * R * P) * es, nBC = (size_t)(b * L * bc_groups(d) * R * N) * es;
     const size_t nStep = (size_t)(b * L * H) * es, nA = (size_t)H * 4;
     const size_t nTh = (size_t)(b * L * H * (N / 2)) * es, nPhi = (size_t)(b * H * (N / 2)) * 4;
     const size_t nY = (size_t)(b * L * H * (w_out ? 1 : R) * P) * es, nH = (size_t)(b * H * N * P) * 4;
@@ -792,6 +824,11 @@ m3_status m3_layer_backward(const m3_dims* d, const void* x, const void* B, cons
     a.b = b; a.L = L; a.H = (int)H; a.N = (int)N; a.P = (int)P; a.R = (int)R;
     a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;
     a.eps = d->eps;
+    a.G = kernel_groups(d);
+    if (a.G > 0) {
+        a.ws_dB = (char*)workspace + lay.gB_off;
+        a.ws_dC = (char*)workspace + lay.gC_off;
+    }
     return launched(m3::launch_backward(a, d->io == M3_BF16, stream), "m3_layer_backward");
 }
 

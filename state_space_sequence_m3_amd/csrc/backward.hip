@@ -133,16 +133,20 @@ __global__ __launch_bounds__(NIB * 64, 1) void chunk_states_kernel(BackwardArgs 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
-    const int64_t bh = blockIdx.x;
+    // heads that share raw B and C run on one XCD (consecutive items), so its L2 serves the group
+    const int64_t bh = a.G > 0 && a.G < a.H ? xcd_item(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
     const int64_t b = bh / a.H;
     const int h = (int)(bh % a.H);
     const int H = a.H;
     const int64_t L = a.L, nchunk = (L + Q - 1) / Q;
     const float Alog2 = a.A[h] * kLog2e;
     const int64_t row_bh = b * L * H + h;
-    const int64_t HRN = (int64_t)H * R * N, HRP = (int64_t)H * R * P, HK = (int64_t)H * K;
+    // raw B rows: the head's own, or its group slot's (GS slots per step, SBC elements per step)
+    const int GS = bc_slots(H, a.G);
+    const int64_t row_bc = b * L * GS + bc_slot(h, H, a.G);
+    const int64_t SBC = (int64_t)GS * R * N, HRP = (int64_t)H * R * P, HK = (int64_t)H * K;
     const T* Xg = (const T*)a.x + row_bh * R * P;
-    const T* Bg = (const T*)a.B + row_bh * R * N;
+    const T* Bg = (const T*)a.B + row_bc * R * N;
     const T* dtg = (const T*)a.dt + row_bh;
     const T* lamg = (const T*)a.lam + row_bh;
     const T* thg = (const T*)a.theta + row_bh * K;
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(NIB * 64, 1) void chunk_states_kernel(BackwardArgs 
     const int rC = iC0 & (R - 1);
     auto offC = [&](int k) {
         const int i = iC0 + k * RKC;
-        return (uint32_t)(((i >> RL2) * (int)HRN + (i & (R - 1)) * N + cC0 * VE) * (int)sizeof(T));
+        return (uint32_t)(((i >> RL2) * (int)SBC + (i & (R - 1)) * N + cC0 * VE) * (int)sizeof(T));
     };
     auto offX = [&](int k) {
         const int i = iX0 + k * RKX;
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(NIB * 64, 1) void chunk_states_kernel(BackwardArgs 
         // ---- loads
         uint4 rb[MAXC], rx[MAXX];
         {
-            const rsrc_t dB = make_rsrc(Bg + t0 * HRN, tail_bytes(t0, HRN, (int64_t)R * N));
+            const rsrc_t dB = make_rsrc(Bg + t0 * SBC, tail_bytes(t0, SBC, (int64_t)R * N));
             const rsrc_t dX = make_rsrc(Xg + t0 * HRP, tail_bytes(t0, HRP, (int64_t)R * P));
 #pragma unroll
             for (int k = 0; k < MAXC; ++k)
@@ -382,26 +386,35 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
-    const int64_t bh = blockIdx.x;
+    // heads that share raw B and C run on one XCD (consecutive items), so its L2 serves the group
+    const int64_t bh = a.G > 0 && a.G < a.H ? xcd_item(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
     const int64_t b = bh / a.H;
     const int h = (int)(bh % a.H);
     const int H = a.H;
     const int64_t L = a.L, nchunk = (L + Q - 1) / Q;
     const float A = a.A[h], Alog2 = A * kLog2e;
     const int64_t row_bh = b * L * H + h;
-    const int64_t HRN = (int64_t)H * R * N, HRP = (int64_t)H * R * P, HK = (int64_t)H * K;
+    // raw B and C rows: the head's own, or its group slot's (GS slots per step, SBC elements per
+    // step); their gradient rows have the same layout
+    const int GS = bc_slots(H, a.G);
+    const int64_t row_bc = b * L * GS + bc_slot(h, H, a.G);
+    const int64_t SBC = (int64_t)GS * R * N, HRP = (int64_t)H * R * P, HK = (int64_t)H * K;
     const bool mix = a.w_out != nullptr;
     const int64_t ystep = mix ? (int64_t)H * P : HRP, yrow = mix ? P : (int64_t)R * P;
     const T* Xg = (const T*)a.x + row_bh * R * P;
-    const T* Bg = (const T*)a.B + row_bh * R * N;
-    const T* Cg = (const T*)a.C + row_bh * R * N;
+    const T* Bg = (const T*)a.B + row_bc * R * N;
+    const T* Cg = (const T*)a.C + row_bc * R * N;
     const T* dtg = (const T*)a.dt + row_bh;
     const T* lamg = (const T*)a.lam + row_bh;
     const T* thg = (const T*)a.theta + row_bh * K;
     const T* dyg = (const T*)a.dy + row_bh * yrow;
     T* dXg = (T*)a.dx + row_bh * R * P;
-    T* dBg = (T*)a.dB + row_bh * R * N;
-    T* dCg = (T*)a.dC + row_bh * R * N;
+    // dB, dC rows: the call's outputs (one slot per head), or, with head groups, this head's
+    // plane of the workspace (plane h mod H/G, each plane in the grouped layout), which
+    // group_sum_kernel adds up per group afterwards
+    const int64_t plane = a.ws_dB ? (int64_t)(h % (H / GS)) * a.b * L * GS * R * N : 0;
+    T* dBg = (a.ws_dB ? (T*)a.ws_dB + plane : (T*)a.dB) + row_bc * R * N;
+    T* dCg = (a.ws_dC ? (T*)a.ws_dC + plane : (T*)a.dC) + row_bc * R * N;
     T* ddtg = (T*)a.ddt + row_bh;
     T* dlamg = (T*)a.dlam + row_bh;
     T* dthg = (T*)a.dtheta + row_bh * K;
@@ -490,7 +503,7 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
         const int wrow = 16 * wave + l16;   // this lane's chunk row in the wave-owned row block
         auto offC = [&](int k) {
             const int i = iC0 + k * RKC;
-            return (uint32_t)(((i >> RL2) * (int)HRN + (i & (R - 1)) * N + cC0 * VE) * (int)sizeof(T));
+            return (uint32_t)(((i >> RL2) * (int)SBC + (i & (R - 1)) * N + cC0 * VE) * (int)sizeof(T));
         };
         auto offX = [&](int k) {
             const int i = iX0 + k * RKX;
@@ -504,8 +517,8 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
         // ================= S1: loads ===================================================
         uint4 rb[MAXC], rc[MAXC], rx[MAXX], ry[MAXX], rs[MAXS];
         {
-            const uint32_t nbc = tail_bytes(t0, HRN, (int64_t)R * N);
-            const rsrc_t dB = make_rsrc(Bg + t0 * HRN, nbc), dC = make_rsrc(Cg + t0 * HRN, nbc);
+            const uint32_t nbc = tail_bytes(t0, SBC, (int64_t)R * N);
+            const rsrc_t dB = make_rsrc(Bg + t0 * SBC, nbc), dC = make_rsrc(Cg + t0 * SBC, nbc);
             const rsrc_t dX = make_rsrc(Xg + t0 * HRP, tail_bytes(t0, HRP, (int64_t)R * P));
             const rsrc_t dYr = make_rsrc(dyg + t0 * ystep, tail_bytes(t0, ystep, yrow));
             const rsrc_t dS = make_rsrc((const T*)a.ws_states + (bh * nchunk + c) * (int64_t)P * N,
@@ -902,8 +915,8 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
         // The raw B and C rows are read again for the adjoint below (the first read left them in
         // L2): holding them from S1 through the products took registers that then spilled.
         {
-            const uint32_t nbc = tail_bytes(t0, HRN, (int64_t)R * N);
-            const rsrc_t dB = make_rsrc(Bg + t0 * HRN, nbc), dC = make_rsrc(Cg + t0 * HRN, nbc);
+            const uint32_t nbc = tail_bytes(t0, SBC, (int64_t)R * N);
+            const rsrc_t dB = make_rsrc(Bg + t0 * SBC, nbc), dC = make_rsrc(Cg + t0 * SBC, nbc);
 #pragma unroll
             for (int k = 0; k < MAXC; ++k) {
                 const bool in = S::FULLC || iC0 + k * RKC < QR;
@@ -920,8 +933,8 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
 
         // ================= S7: rotation and BCNorm adjoint per row =====================
         {
-            const uint32_t nbc = tail_bytes(t0, HRN, (int64_t)R * N);
-            const rsrc_t dBo = make_rsrc(dBg + t0 * HRN, nbc), dCo = make_rsrc(dCg + t0 * HRN, nbc);
+            const uint32_t nbc = tail_bytes(t0, SBC, (int64_t)R * N);
+            const rsrc_t dBo = make_rsrc(dBg + t0 * SBC, nbc), dCo = make_rsrc(dCg + t0 * SBC, nbc);
 #pragma unroll
             for (int k = 0; k < MAXC; ++k) {
                 const int i = iC0 + k * RKC;
@@ -1266,6 +1279,30 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(BackwardArgs a) {
     }
 }
 
+// Head groups: dB and dC of each group slot are the sums of the H / G per-head planes, added in
+// fp32 in plane order (the same order on every run).  One 16-byte vector per thread and step of
+// a grid-stride loop; blockIdx.y picks B (0) or C (1).
+template <typename T>
+__global__ __launch_bounds__(256) void group_sum_kernel(BackwardArgs a) {
+    constexpr int VE = 16 / (int)sizeof(T);
+    const int planes = a.H / a.G;
+    const int64_t n = a.b * a.L * a.G * a.R * a.N;   // elements per plane (R N is a multiple of 16)
+    const T* src = (const T*)(blockIdx.y == 0 ? a.ws_dB : a.ws_dC);
+    T* dst = (T*)(blockIdx.y == 0 ? a.dB : a.dC);
+    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n / VE; v += (int64_t)gridDim.x * 256) {
+        float acc[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+        for (int j = 0; j < planes; ++j) {
+            float f[VE];
+            unpack16(*(const uint4*)(src + j * n + v * VE), f, T{});
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[e] += f[e];
+        }
+        *(uint4*)(dst + v * VE) = pack16(acc, T{});
+    }
+}
+
 template <typename T, int N, int P, int NIB, int R>
 hipError_t launch_nipr(const BackwardArgs& a, bool states_only, hipStream_t s) {
     const dim3 grid((unsigned)(a.b * a.H)), block(NIB * 64);
@@ -1276,6 +1313,11 @@ hipError_t launch_nipr(const BackwardArgs& a, bool states_only, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)a.H), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    const int64_t vecs = a.ws_dB ? a.b * a.L * a.G * R * N / (16 / (int64_t)sizeof(T)) : 0;
+    if (e != hipSuccess || vecs == 0) return e;
+    const unsigned blocks = (unsigned)((vecs + 255) / 256 < 2048 ? (vecs + 255) / 256 : 2048);
+    hipLaunchKernelGGL(group_sum_kernel<T>, dim3(blocks, 2), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -169,7 +169,8 @@ template <typename T, int N, int NW>
 __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) {
     constexpr int LPR = N / 8, RPW = 64 / LPR, K = N / 2;
     __shared__ float wsum[NW][K];
-    const int64_t id = blockIdx.x;
+    // heads that share raw B and C run on one XCD (consecutive items), so its L2 serves the group
+    const int64_t id = a.G > 0 && a.G < a.H ? xcd_item(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
     const int seg = (int)(id % a.nseg);
     const int64_t bh = id / a.nseg;
     const int64_t b = bh / a.H;
@@ -253,12 +254,16 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
     }
 
     // walk the quarter, RPW rows rho = (t - w0) * R + r at a time; row rho of this wave lives at
-    // (rho / R) * H * R * N + (rho % R) * N past the (b, w0, h) row
+    // (rho / R) * H * R * N + (rho % R) * N past the (b, w0, h) row of the outputs, and at
+    // (rho / R) * GS * R * N + (rho % R) * N past the (b, w0, slot) row of raw B and C (GS = G
+    // head slots, H when every head has its own)
     const int64_t nrows = (w1 - w0) * R;
     const int64_t row_w0 = (b * a.L + w0) * a.H + h;
-    const int64_t HRN = (int64_t)a.H * R * N, HK = (int64_t)a.H * K;
-    const T* Bq = (const T*)a.B + row_w0 * R * N + 8 * c;
-    const T* Cq = (const T*)a.C + row_w0 * R * N + 8 * c;
+    const int GS = bc_slots(a.H, a.G);
+    const int64_t row_in = (b * a.L + w0) * GS + bc_slot(h, a.H, a.G);
+    const int64_t HRN = (int64_t)a.H * R * N, SBC = (int64_t)GS * R * N, HK = (int64_t)a.H * K;
+    const T* Bq = (const T*)a.B + row_in * R * N + 8 * c;
+    const T* Cq = (const T*)a.C + row_in * R * N + 8 * c;
     T* Bo = (T*)a.Bbar + row_w0 * R * N + 8 * c;
     T* Co = (T*)a.Cbar + row_w0 * R * N + 8 * c;
     const T* thq = (const T*)a.theta + row_w0 * K + 4 * c;
@@ -286,7 +291,7 @@ __global__ __launch_bounds__(NW * 64) void bcnorm_rope_kernel(BcnormRopeArgs a) 
     const Pos plast = {nrows32 > 0 ? (nrows32 - 1) / R : 0, nrows32 > 0 ? (nrows32 - 1) % R : 0};
     auto load_block = [&](int rho0, Pos p, int slot) {
         const Pos u = rho0 + j < nrows32 ? p : plast;
-        const int64_t o = (int64_t)u.tl * HRN + u.r * N;
+        const int64_t o = (int64_t)u.tl * SBC + u.r * N;
         nB[slot] = RW::ld8s(Bq + o);
         nC[slot] = RW::ld8s(Cq + o);
         nT[slot] = RW::ld4s(thq + (int64_t)u.tl * HK);

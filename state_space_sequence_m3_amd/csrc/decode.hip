@@ -46,8 +46,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeArgs a) 
     const int tid = threadIdx.x;
 
     const T* Bp = (const T*)a.Bbar_prev + bh * R * N;
-    const T* Bt = (const T*)a.Bbar + bh * R * N;
-    const T* Ct = (const T*)a.Cbar + bh * R * N;
+    // the token's B and C: per head, or (fused, head groups) the raw rows of the head's slot
+    const int64_t rowBC = FUSED ? (bh / a.H) * bc_slots(a.H, a.G) + bc_slot(h, a.H, a.G) : bh;
+    const T* Bt = (const T*)a.Bbar + rowBC * R * N;
+    const T* Ct = (const T*)a.Cbar + rowBC * R * N;
     const T* xp = (const T*)a.x_prev + bh * R * P;
     const T* xt = (const T*)a.x + bh * R * P;
     float4* hp = (float4*)(a.h + bh * (int64_t)N * P);
@@ -315,8 +317,10 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(FUS
         const bool ok = qq < npairs;
         const int64_t bh = ok ? qq : 0;
         const rsrc_t rsBp = make_rsrc((const T*)a.Bbar_prev + bh * R * N, ok ? R * N * ES : 0);
-        const rsrc_t rsB = make_rsrc((const T*)a.Bbar + bh * R * N, ok ? R * N * ES : 0);
-        const rsrc_t rsC = make_rsrc((const T*)a.Cbar + bh * R * N, ok ? R * N * ES : 0);
+        // the token's B and C: per head, or (fused, head groups) the raw rows of the head's slot
+        const int64_t rowBC = FUSED ? (bh / H) * bc_slots(H, a.G) + bc_slot(h, H, a.G) : bh;
+        const rsrc_t rsB = make_rsrc((const T*)a.Bbar + rowBC * R * N, ok ? R * N * ES : 0);
+        const rsrc_t rsC = make_rsrc((const T*)a.Cbar + rowBC * R * N, ok ? R * N * ES : 0);
         const rsrc_t rsXp = make_rsrc((const T*)a.x_prev + bh * R * P, ok ? R * P * ES : 0);
         const rsrc_t rsX = make_rsrc((const T*)a.x + bh * R * P, ok ? R * P * ES : 0);
         rdt = buffer_load_bits(make_rsrc((const T*)a.dt + bh, ok ? ES : 0), 0, T{});

@@ -33,6 +33,8 @@ struct DecodeArgs {
     void* Bbar_out = nullptr;    // [b, H, R, N] the token's rotated B (next step's Bbar_prev)
     int bcnorm = 0;
     float eps = 0.f;
+    // raw B and C hold G head slots: head h reads slot h / (H / G) (0: one slot per head)
+    int G = 0;
 };
 
 struct BcnormRopeArgs {
@@ -55,6 +57,8 @@ struct BcnormRopeArgs {
     int nseg;             // segments per (b, h)
     int bcnorm;
     float eps;
+    // raw B and C hold G head slots: head h reads slot h / (H / G) (0: one slot per head)
+    int G = 0;
 };
 
 struct PrefillArgs {
@@ -105,6 +109,9 @@ struct PrefillArgs {
     const float* seg_phi = nullptr;  // fused: angle-segment start angles [b, H, nsegA, parts, N/2] (radians)
     int64_t angle_seglen = 0;        // steps per angle segment (seglen or a divisor of it)
     int angle_parts = 0;             // start angles per angle segment
+    // fused layer only: raw B and C hold G head slots, head h reads slot h / (H / G) (0: one slot
+    // per head); the heads of a group are then laid out on one XCD (see xcd_block)
+    int G = 0;
 };
 
 // Gradients of the fused layer core (m3_layer_chunk_states / m3_layer_backward).  B and C are raw
@@ -157,6 +164,12 @@ struct BackwardArgs {
     int H, N, P, R;
     int bcnorm;
     float eps;
+    // raw B and C hold G head slots, head h reads slot h / (H / G) (0: one slot per head).  With
+    // G < H the backward kernel writes each head's dB, dC rows to ws_dB, ws_dC ([b, L, H, R, N]
+    // io) and group_sum adds each group's heads into dB, dC.
+    int G = 0;
+    void* ws_dB = nullptr;
+    void* ws_dC = nullptr;
 };
 
 bool backward_supported(int N, int P, int R);

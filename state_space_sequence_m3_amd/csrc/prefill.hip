@@ -123,8 +123,10 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // a split sequence: pass 1 runs segments 0 .. nseg-2 of each (b, h) (end states only), pass 2
     // all of them
     const int segs = a.pass == 1 ? a.nseg - 1 : a.nseg;
-    const int64_t bh = a.pass ? (int64_t)blockIdx.x / segs : (int64_t)blockIdx.x;
-    const int seg = a.pass ? (int)(blockIdx.x % (unsigned)segs) : 0;
+    // heads that share raw B and C run on one XCD (consecutive items), so its L2 serves the group
+    const int64_t item = a.G > 0 && a.G < a.H ? xcd_item(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
+    const int64_t bh = a.pass ? item / segs : item;
+    const int seg = a.pass ? (int)(item % segs) : 0;
     const int64_t b = bh / a.H;
     const int h = (int)(bh % a.H);
     const int H = a.H, R = a.R, Q = a.Q;
@@ -153,10 +155,14 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const float Alog2 = a.A[h] * kLog2e;
     // (b, t = 0, h) bases; step t of this (b, h) is t * H rows further
     const int64_t row_bh = t_first * H + h;
-    const int64_t HRN = (int64_t)H * R * N, HRP = (int64_t)H * R * P;
+    // B and C rows: per head (Bbar, Cbar), or the raw rows of the head's group slot (fused);
+    // SBC = B or C elements per step
+    const int GS = bc_slots(H, a.G);
+    const int64_t row_bc = t_first * GS + bc_slot(h, H, a.G);
+    const int64_t SBC = (int64_t)GS * R * N, HRP = (int64_t)H * R * P;
     const T* Xg = (const T*)a.x + row_bh * R * P;
-    const T* Bg = (const T*)a.Bbar + row_bh * R * N;
-    const T* Cg = (const T*)a.Cbar + row_bh * R * N;
+    const T* Bg = (const T*)a.Bbar + row_bc * R * N;
+    const T* Cg = (const T*)a.Cbar + row_bc * R * N;
     const T* dtg = (const T*)a.dt + row_bh;
     const T* lamg = (const T*)a.lam + row_bh;
     const float* hin = nullptr;
@@ -185,10 +191,10 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // ---- staging: this thread moves 16-byte vectors k = 0, 1, ... of each tile.  Vector k is
     // chunk row i = i0 + k * RK (row (t, r) = (i >> rl2, i & rmask)), 16-byte column c0.
     const int iC0 = tid / VPN, cC0 = tid % VPN, iX0 = tid / VPP, cX0 = tid % VPP;
-    const int HRN32 = (int)HRN, HRP32 = (int)HRP;
+    const int SBC32 = (int)SBC, HRP32 = (int)HRP;
     auto offC = [&](int k) {
         const int i = iC0 + k * RKC;
-        return (uint32_t)(((i >> rl2) * HRN32 + (i & rmask) * N + cC0 * VE) * (int)sizeof(T));
+        return (uint32_t)(((i >> rl2) * SBC32 + (i & rmask) * N + cC0 * VE) * (int)sizeof(T));
     };
     auto offX = [&](int k) {
         const int i = iX0 + k * RKX;
@@ -199,8 +205,8 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     uint4 rc[NBUF][MAXC], rb[NBUF][MAXC], rx[NBUF][MAXX];
     typedef typename IoBits<T>::type Bits;
     Bits nd[NBUF], nl[NBUF], ndn[NBUF], nln[NBUF];   // dt, lambda at t and t + 1 (io bits; the last wave uses them)
-    const rsrc_t dCs = make_rsrc(Cg, states_only ? 0u : seq_bytes(HRN, (int64_t)R * N));
-    const rsrc_t dBs = make_rsrc(Bg, seq_bytes(HRN, (int64_t)R * N));
+    const rsrc_t dCs = make_rsrc(Cg, states_only ? 0u : seq_bytes(SBC, (int64_t)R * N));
+    const rsrc_t dBs = make_rsrc(Bg, seq_bytes(SBC, (int64_t)R * N));
     const rsrc_t dXs = make_rsrc(Xg, seq_bytes(HRP, (int64_t)R * P));
     const rsrc_t dDs = make_rsrc(dtg, seq_bytes(H, 1));
     const rsrc_t dLs = make_rsrc(lamg, seq_bytes(H, 1));
@@ -208,13 +214,13 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     auto load_chunk = [&](int64_t c, int set, int part = -1) {
         const int64_t t0 = c * Q;
         if (!STATES && (part < 0 || part == 0)) {
-            const uint32_t o = step_off(t0, HRN);
+            const uint32_t o = step_off(t0, SBC);
 #pragma unroll
             for (int k = 0; k < MAXC; ++k)
                 if (FULLC || iC0 + k * RKC < QR) rc[set][k] = buffer_load16_stream(dCs, offC(k) + o);
         }
         if (part < 0 || part == 1) {
-            const uint32_t o = step_off(t0, HRN);
+            const uint32_t o = step_off(t0, SBC);
 #pragma unroll
             for (int k = 0; k < MAXC; ++k)
                 if (FULLC || iC0 + k * RKC < QR) rb[set][k] = buffer_load16_stream(dBs, offC(k) + o);
@@ -744,7 +750,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             for (int e = tid; e < R * N; e += NT) {
                 T v;
                 if (FUSED) v = sB[lb * TB + (tlast * R + e / N) * LDB + e % N];   // rotated here only
-                else v = Bg[(L - 1) * HRN + e];
+                else v = Bg[(L - 1) * SBC + e];
                 Blast[e] = v;
             }
         }

@@ -22,6 +22,9 @@ theta, then the decode-state tensors.
 
 Mamba-2 mode (the ``mamba2`` workloads) sets lam = 1 and theta = 0 after the draws, with BCNorm
 and biases off: the same kernels then run the exponential-Euler recurrence without rotation.
+
+Head-group workloads (``groups`` = G > 0) draw raw B and C with G head slots instead of H (same
+distribution); every other tensor stays per head.
 """
 from __future__ import annotations
 
@@ -48,7 +51,13 @@ class Workload:
     theta_std: float = 1.0
     decode_steps: int = 0
     mamba2: bool = False  # Mamba-2 mode: lambda = 1 (exponential-Euler step) and theta = 0
+    groups: int = 0       # head slots of raw B and C, shared by groups of H / G heads (0: per head)
     note: str = field(default="", compare=False)
+
+    @property
+    def bc_heads(self) -> int:
+        """Head slots of raw B and C: G, or H when every head has its own."""
+        return self.groups if self.groups else self.nheads
 
     @property
     def torch_io(self):
@@ -74,6 +83,15 @@ WORKLOADS = {
                                False, decode_steps=256, note="b128 H64 P64 N128 R1, 256 steps"),
     "decode_b128_r4": Workload("decode_b128_r4", 128, 1, 64, 64, 128, 4, 1, "bf16", True, True,
                                True, decode_steps=256, note="b128 H64 P64 N128 R4, 256 steps"),
+    "siso_g1_b8_l2048": Workload("siso_g1_b8_l2048", 8, 2048, 64, 64, 128, 1, 64, "bf16", True, True,
+                                 False, groups=1,
+                                 note="SISO b8 L2048 with raw B and C shared by all 64 heads (G = 1)"),
+    "mimo4_g1_b8_l2048": Workload("mimo4_g1_b8_l2048", 8, 2048, 64, 64, 128, 4, 16, "bf16", True, True,
+                                  True, groups=1,
+                                  note="MIMO R4 b8 L2048 with raw B and C shared by all 64 heads (G = 1)"),
+    "mimo4_g8_b8_l2048": Workload("mimo4_g8_b8_l2048", 8, 2048, 64, 64, 128, 4, 16, "bf16", True, True,
+                                  True, groups=8,
+                                  note="MIMO R4 b8 L2048 with raw B and C shared by groups of 8 heads"),
     "long_mimo4_b1_l16384": Workload("long_mimo4_b1_l16384", 1, 16384, 64, 64, 128, 4, 16, "bf16",
                                      True, True, True, theta_std=math.pi, decode_steps=512,
                                      note="b1 L16384 H64 R4 Q16, theta std pi, then 512 decode steps"),
@@ -113,15 +131,15 @@ def make_params(w: Workload, g, device, normw: bool = False) -> dict:
 def make_sequence(w: Workload, g, device, lead: tuple) -> dict:
     """Per-step tensors with leading dims ``lead`` (e.g. (b, L) for prefill, (steps, b) for decode).
 
-    x [*lead, H, R, P], B, C [*lead, H, R, N], dt, lam [*lead, H], theta [*lead, H, N/2], all in
-    the workload's io dtype.
+    x [*lead, H, R, P], B, C [*lead, G, R, N] (G = H unless the workload shares them across head
+    groups), dt, lam [*lead, H], theta [*lead, H, N/2], all in the workload's io dtype.
     """
     H, R, N, P = w.nheads, w.rank, w.dstate, w.headdim
     io = w.torch_io
     out = {}
     out["x"] = _normal(g, (*lead, H, R, P), device).to(io)
-    out["B"] = _normal(g, (*lead, H, R, N), device).to(io)
-    out["C"] = _normal(g, (*lead, H, R, N), device).to(io)
+    out["B"] = _normal(g, (*lead, w.bc_heads, R, N), device).to(io)
+    out["C"] = _normal(g, (*lead, w.bc_heads, R, N), device).to(io)
     out["dt"] = torch.nn.functional.softplus(_normal(g, (*lead, H), device) - 1.0).to(io)
     out["lam"] = torch.sigmoid(_normal(g, (*lead, H), device)).to(io)
     out["theta"] = _normal(g, (*lead, H, N // 2), device, w.theta_std).to(io)

@@ -37,7 +37,7 @@ class M3Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
                 ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("rank", ctypes.c_int64),
                 ("chunk", ctypes.c_int64), ("io", ctypes.c_int32), ("flags", ctypes.c_uint32),
-                ("eps", ctypes.c_float)]
+                ("eps", ctypes.c_float), ("ngroups", ctypes.c_int64)]
 
 
 class M3Error(RuntimeError):
@@ -144,9 +144,18 @@ def _tensor(t, name, shape, dtype, device):
 
 
 def make_dims(batch, seqlen, nheads, headdim, dstate, rank, chunk=0, io=M3_BF16, bcnorm=True,
-              eps=1e-5) -> M3Dims:
+              eps=1e-5, groups=0) -> M3Dims:
+    """``groups`` = G head slots of raw B and C (heads share them in groups of H / G); 0 = one
+    per head."""
     return M3Dims(batch, seqlen, nheads, headdim, dstate, rank, chunk, io,
-                  M3_BCNORM if bcnorm else 0, eps)
+                  M3_BCNORM if bcnorm else 0, eps, groups)
+
+
+def _groups(H, G):
+    """The dims field for raw B and C with G head slots and H heads (0 when G == H)."""
+    if G < 1 or H % G != 0:
+        raise ValueError("B and C have %d head slots, which must divide the %d heads" % (G, H))
+    return 0 if G == H else G
 
 
 def bcnorm_rope_workspace_bytes(dims: M3Dims) -> int:
@@ -164,13 +173,16 @@ def layer_prefill_workspace_bytes(dims: M3Dims) -> int:
 def m3_bcnorm_rope(B, C, dt, theta, normw_B=None, normw_C=None, bias_B=None, bias_C=None,
                    phi_in=None, Bbar=None, Cbar=None, phi_out=None, bcnorm=True, eps=1e-5,
                    workspace=None, stream=None):
-    """BCNorm + bias + cumulative rotation.  B, C: [b, L, H, R, N]; returns (Bbar, Cbar, phi_out)."""
+    """BCNorm + bias + cumulative rotation.  B, C: [b, L, G, R, N] raw (G = H, or head slots
+    shared by groups of H / G heads; H is taken from dt); returns (Bbar, Cbar, phi_out) with
+    Bbar, Cbar [b, L, H, R, N]."""
     lib = load()
-    b, L, H, R, N = B.shape
+    b, L, G, R, N = B.shape
+    H = dt.shape[2]
     dev, io = B.device, B.dtype
     f32 = torch.float32
-    _tensor(B, "B", (b, L, H, R, N), io, dev)
-    _tensor(C, "C", (b, L, H, R, N), io, dev)
+    _tensor(B, "B", (b, L, G, R, N), io, dev)
+    _tensor(C, "C", (b, L, G, R, N), io, dev)
     _tensor(dt, "dt", (b, L, H), io, dev)
     _tensor(theta, "theta", (b, L, H, N // 2), io, dev)
     _tensor(normw_B, "normw_B", (H, N), f32, dev)
@@ -178,12 +190,13 @@ def m3_bcnorm_rope(B, C, dt, theta, normw_B=None, normw_C=None, bias_B=None, bia
     _tensor(bias_B, "bias_B", (H, R, N), f32, dev)
     _tensor(bias_C, "bias_C", (H, R, N), f32, dev)
     _tensor(phi_in, "phi_in", (b, H, N // 2), f32, dev)
-    Bbar = torch.empty_like(B) if Bbar is None else _tensor(Bbar, "Bbar", B.shape, io, dev)
-    Cbar = torch.empty_like(C) if Cbar is None else _tensor(Cbar, "Cbar", C.shape, io, dev)
+    oshape = (b, L, H, R, N)
+    Bbar = torch.empty(oshape, dtype=io, device=dev) if Bbar is None else _tensor(Bbar, "Bbar", oshape, io, dev)
+    Cbar = torch.empty(oshape, dtype=io, device=dev) if Cbar is None else _tensor(Cbar, "Cbar", oshape, io, dev)
     if phi_out is None:
         phi_out = torch.empty((b, H, N // 2), dtype=f32, device=dev)
     _tensor(phi_out, "phi_out", (b, H, N // 2), f32, dev)
-    dims = make_dims(b, L, H, 0, N, R, 0, _io_code(io), bcnorm, eps)
+    dims = make_dims(b, L, H, 0, N, R, 0, _io_code(io), bcnorm, eps, _groups(H, G))
     need = bcnorm_rope_workspace_bytes(dims)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -246,16 +259,17 @@ def m3_layer_prefill(x, B, C, dt, theta, A, lam, normw_B=None, normw_C=None, bia
                      bias_C=None, w_out=None, phi_in=None, h_in=None, Bbar_prev=None, x_prev=None,
                      y=None, h_out=None, phi_out=None, Bbar_last=None, x_last=None, chunk=0,
                      bcnorm=True, eps=1e-5, workspace=None, stream=None):
-    """m3_bcnorm_rope + m3_prefill in one pass.  x: [b, L, H, R, P]; raw B, C: [b, L, H, R, N].
-    A workspace of layer_prefill_workspace_bytes is allocated when none is given (it lets few
-    long sequences run split into segments).  Returns (y, h_out, phi_out)."""
+    """m3_bcnorm_rope + m3_prefill in one pass.  x: [b, L, H, R, P]; raw B, C: [b, L, G, R, N]
+    (G = H, or head slots shared by groups of H / G heads).  A workspace of
+    layer_prefill_workspace_bytes is allocated when none is given (it lets few long sequences
+    run split into segments).  Returns (y, h_out, phi_out)."""
     lib = load()
     b, L, H, R, P = x.shape
-    N = B.shape[-1]
+    G, N = B.shape[2], B.shape[-1]
     dev, io = x.device, x.dtype
     f32 = torch.float32
-    _tensor(B, "B", (b, L, H, R, N), io, dev)
-    _tensor(C, "C", (b, L, H, R, N), io, dev)
+    _tensor(B, "B", (b, L, G, R, N), io, dev)
+    _tensor(C, "C", (b, L, G, R, N), io, dev)
     _tensor(dt, "dt", (b, L, H), io, dev)
     _tensor(theta, "theta", (b, L, H, N // 2), io, dev)
     _tensor(lam, "lam", (b, L, H), io, dev)
@@ -279,7 +293,7 @@ def m3_layer_prefill(x, B, C, dt, theta, A, lam, normw_B=None, normw_C=None, bia
     _tensor(phi_out, "phi_out", (b, H, N // 2), f32, dev)
     _tensor(Bbar_last, "Bbar_last", (b, H, R, N), io, dev)
     _tensor(x_last, "x_last", (b, H, R, P), io, dev)
-    dims = make_dims(b, L, H, P, N, R, chunk, _io_code(io), bcnorm, eps)
+    dims = make_dims(b, L, H, P, N, R, chunk, _io_code(io), bcnorm, eps, _groups(H, G))
     workspace, ws_bytes = _workspace(workspace, layer_prefill_workspace_bytes(dims), dev)
     _check(lib.m3_layer_prefill(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(theta),
                                 _ptr(normw_B), _ptr(normw_C), _ptr(bias_B), _ptr(bias_C), _ptr(A),
@@ -316,17 +330,19 @@ def m3_decode_step(h, Bbar_prev, x_prev, x, Bbar, Cbar, dt, A, lam, w_out=None, 
 def m3_layer_decode_step(h, phi, Bbar_prev, x_prev, x, B, C, dt, theta, A, lam, normw_B=None,
                          normw_C=None, bias_B=None, bias_C=None, w_out=None, y=None, Bbar_out=None,
                          bcnorm=True, eps=1e-5, stream=None):
-    """Rotation + one decode token: h [b, H, N, P] and phi [b, H, N/2] updated in place.
-    Returns (y, Bbar_out); Bbar_out is the next step's Bbar_prev."""
+    """Rotation + one decode token: h [b, H, N, P] and phi [b, H, N/2] updated in place; raw B,
+    C [b, G, R, N] (G = H, or head slots shared by groups of H / G heads).
+    Returns (y, Bbar_out); Bbar_out [b, H, R, N] is the next step's Bbar_prev."""
     lib = load()
     b, H, N, P = h.shape
     R = x.shape[2]
+    G = B.shape[1]
     dev, io = h.device, x.dtype
     f32 = torch.float32
     _tensor(h, "h", (b, H, N, P), f32, dev)
     _tensor(phi, "phi", (b, H, N // 2), f32, dev)
     for name, t, shp in (("Bbar_prev", Bbar_prev, (b, H, R, N)), ("x_prev", x_prev, (b, H, R, P)),
-                         ("x", x, (b, H, R, P)), ("B", B, (b, H, R, N)), ("C", C, (b, H, R, N)),
+                         ("x", x, (b, H, R, P)), ("B", B, (b, G, R, N)), ("C", C, (b, G, R, N)),
                          ("dt", dt, (b, H)), ("theta", theta, (b, H, N // 2)), ("lam", lam, (b, H))):
         _tensor(t, name, shp, io, dev)
     _tensor(A, "A", (H,), f32, dev)
@@ -340,7 +356,7 @@ def m3_layer_decode_step(h, phi, Bbar_prev, x_prev, x, B, C, dt, theta, A, lam, 
     if Bbar_out is None:
         Bbar_out = torch.empty((b, H, R, N), dtype=io, device=dev)
     _tensor(Bbar_out, "Bbar_out", (b, H, R, N), io, dev)
-    dims = make_dims(b, 1, H, P, N, R, 0, _io_code(io), bcnorm, eps)
+    dims = make_dims(b, 1, H, P, N, R, 0, _io_code(io), bcnorm, eps, _groups(H, G))
     _check(lib.m3_layer_decode_step(ctypes.byref(dims), _ptr(h), _ptr(phi), _ptr(Bbar_prev),
                                     _ptr(x_prev), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(theta),
                                     _ptr(normw_B), _ptr(normw_C), _ptr(bias_B), _ptr(bias_C),
@@ -353,18 +369,18 @@ def m3_layer_prefill_varlen(cu_seqlens, x, B, C, dt, theta, A, lam, normw_B=None
                             bias_B=None, bias_C=None, w_out=None, phi_in=None, h_in=None,
                             Bbar_prev=None, x_prev=None, y=None, h_out=None, phi_out=None,
                             Bbar_last=None, x_last=None, chunk=0, bcnorm=True, eps=1e-5, stream=None):
-    """m3_layer_prefill over a packed batch: x [T, H, R, P], B, C [T, H, R, N], ...; sequence s is
+    """m3_layer_prefill over a packed batch: x [T, H, R, P], B, C [T, G, R, N], ...; sequence s is
     tokens cu_seqlens[s]:cu_seqlens[s+1] (int32 device tensor of b + 1 offsets).
     Returns (y, h_out, phi_out)."""
     lib = load()
     T, H, R, P = x.shape
-    N = B.shape[-1]
+    G, N = B.shape[1], B.shape[-1]
     b = cu_seqlens.numel() - 1
     dev, io = x.device, x.dtype
     f32 = torch.float32
     _tensor(cu_seqlens, "cu_seqlens", (b + 1,), torch.int32, dev)
-    _tensor(B, "B", (T, H, R, N), io, dev)
-    _tensor(C, "C", (T, H, R, N), io, dev)
+    _tensor(B, "B", (T, G, R, N), io, dev)
+    _tensor(C, "C", (T, G, R, N), io, dev)
     _tensor(dt, "dt", (T, H), io, dev)
     _tensor(theta, "theta", (T, H, N // 2), io, dev)
     _tensor(lam, "lam", (T, H), io, dev)
@@ -388,7 +404,7 @@ def m3_layer_prefill_varlen(cu_seqlens, x, B, C, dt, theta, A, lam, normw_B=None
     _tensor(phi_out, "phi_out", (b, H, N // 2), f32, dev)
     _tensor(Bbar_last, "Bbar_last", (b, H, R, N), io, dev)
     _tensor(x_last, "x_last", (b, H, R, P), io, dev)
-    dims = make_dims(b, T, H, P, N, R, chunk, _io_code(io), bcnorm, eps)
+    dims = make_dims(b, T, H, P, N, R, chunk, _io_code(io), bcnorm, eps, _groups(H, G))
     _check(lib.m3_layer_prefill_varlen(ctypes.byref(dims), _ptr(cu_seqlens), _ptr(x), _ptr(B), _ptr(C),
                                        _ptr(dt), _ptr(theta), _ptr(normw_B), _ptr(normw_C), _ptr(bias_B),
                                        _ptr(bias_C), _ptr(A), _ptr(lam), _ptr(w_out), _ptr(phi_in),
@@ -409,14 +425,14 @@ def layer_backward_workspace_bytes(dims: M3Dims) -> int:
 def m3_layer_chunk_states(x, B, dt, theta, A, lam, normw_B=None, bias_B=None, phi_in=None, h_in=None,
                           Bbar_prev=None, x_prev=None, states=None, phis=None, bcnorm=True, eps=1e-5,
                           stream=None):
-    """Entry state and angle of every backward chunk.  Returns (states [b, H, nchunk, P, N] io,
-    phis [b, H, nchunk, N/2] f32) and the chunk length in steps."""
+    """Entry state and angle of every backward chunk (raw B: [b, L, G, R, N]).  Returns (states
+    [b, H, nchunk, P, N] io, phis [b, H, nchunk, N/2] f32) and the chunk length in steps."""
     lib = load()
     b, L, H, R, P = x.shape
-    N = B.shape[-1]
+    G, N = B.shape[2], B.shape[-1]
     dev, io = x.device, x.dtype
     f32 = torch.float32
-    _tensor(B, "B", (b, L, H, R, N), io, dev)
+    _tensor(B, "B", (b, L, G, R, N), io, dev)
     _tensor(dt, "dt", (b, L, H), io, dev)
     _tensor(theta, "theta", (b, L, H, N // 2), io, dev)
     _tensor(lam, "lam", (b, L, H), io, dev)
@@ -427,7 +443,7 @@ def m3_layer_chunk_states(x, B, dt, theta, A, lam, normw_B=None, bias_B=None, ph
     _tensor(h_in, "h_in", (b, H, N, P), f32, dev)
     _tensor(Bbar_prev, "Bbar_prev", (b, H, R, N), io, dev)
     _tensor(x_prev, "x_prev", (b, H, R, P), io, dev)
-    dims = make_dims(b, L, H, P, N, R, 0, _io_code(io), bcnorm, eps)
+    dims = make_dims(b, L, H, P, N, R, 0, _io_code(io), bcnorm, eps, _groups(H, G))
     Q = layer_backward_chunk(dims)
     if Q == 0:
         raise M3Error(M3_E_UNSUPPORTED, "no backward kernel for N=%d P=%d R=%d" % (N, P, R))
@@ -452,14 +468,15 @@ def m3_layer_backward(x, B, C, dt, theta, A, lam, dy, normw_B=None, normw_C=None
     """Gradients of m3_layer_prefill.  ``dy`` has y's shape; dh_out [b, H, N, P] and dphi_out
     [b, H, N/2] are optional (zero).  Returns a dict keyed by input name (x, B, C, dt, theta, A,
     lam, normw_B, normw_C, bias_B, bias_C, w_out, phi_in, h_in, Bbar_prev, x_prev); ``grads`` may
-    supply preallocated output tensors under those names."""
+    supply preallocated output tensors under those names.  Raw B, C: [b, L, G, R, N]; their
+    gradients have the same layout (summed over each group's heads)."""
     lib = load()
     b, L, H, R, P = x.shape
-    N = B.shape[-1]
+    G, N = B.shape[2], B.shape[-1]
     dev, io = x.device, x.dtype
     f32 = torch.float32
-    _tensor(B, "B", (b, L, H, R, N), io, dev)
-    _tensor(C, "C", (b, L, H, R, N), io, dev)
+    _tensor(B, "B", (b, L, G, R, N), io, dev)
+    _tensor(C, "C", (b, L, G, R, N), io, dev)
     _tensor(dt, "dt", (b, L, H), io, dev)
     _tensor(theta, "theta", (b, L, H, N // 2), io, dev)
     _tensor(lam, "lam", (b, L, H), io, dev)
@@ -478,7 +495,7 @@ def m3_layer_backward(x, B, C, dt, theta, A, lam, dy, normw_B=None, normw_C=None
     _tensor(dh_out, "dh_out", (b, H, N, P), f32, dev)
     _tensor(dphi_out, "dphi_out", (b, H, N // 2), f32, dev)
     carry = Bbar_prev is not None and x_prev is not None
-    spec = {"x": ((b, L, H, R, P), io), "B": ((b, L, H, R, N), io), "C": ((b, L, H, R, N), io),
+    spec = {"x": ((b, L, H, R, P), io), "B": ((b, L, G, R, N), io), "C": ((b, L, G, R, N), io),
             "dt": ((b, L, H), io), "theta": ((b, L, H, N // 2), io), "A": ((H,), f32),
             "lam": ((b, L, H), io), "normw_B": ((H, N), f32), "normw_C": ((H, N), f32),
             "bias_B": ((H, R, N), f32), "bias_C": ((H, R, N), f32), "phi_in": ((b, H, N // 2), f32),
@@ -496,7 +513,7 @@ def m3_layer_backward(x, B, C, dt, theta, A, lam, dy, normw_B=None, normw_C=None
     grads.setdefault("w_out", None)
     grads.setdefault("Bbar_prev", None)
     grads.setdefault("x_prev", None)
-    dims = make_dims(b, L, H, P, N, R, 0, _io_code(io), bcnorm, eps)
+    dims = make_dims(b, L, H, P, N, R, 0, _io_code(io), bcnorm, eps, _groups(H, G))
     need = layer_backward_workspace_bytes(dims)
     if need == 0:
         raise M3Error(M3_E_UNSUPPORTED, "no backward kernel for N=%d P=%d R=%d" % (N, P, R))

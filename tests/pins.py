@@ -415,8 +415,11 @@ def check_split_carry(lib=None):
 #     pass; the gradient of the forward definition is what the backward computes, and a central
 #     difference of the forward (O(h^2) truncation, h = 1e-5) reaches it by another route.
 # ---------------------------------------------------------------------------------------------
-def _grad_case(seed, R, mix, bcnorm, carry, weights):
+def _grad_case(seed, R, mix, bcnorm, carry, weights, groups=0):
     c = _rand_case(seed, L=6, R=R, N=4, P=3, H=2, b=2, carry=carry)
+    if groups:   # raw B and C shared by the heads: the first `groups` head slots are kept
+        c["B"] = c["B"][:, :, :groups].copy()
+        c["C"] = c["C"][:, :, :groups].copy()
     r = _rng(seed + 1000)
     H, N, P = 2, 4, 3
     if weights:
@@ -437,10 +440,11 @@ def _objective(c, cot, mix, bcnorm, lib):
 
 def check_layer_gradients_fd(lib=None):
     step = 1e-5
-    for seed, R, mix, bcnorm, carry, weights in [(91, 2, True, True, True, True),
-                                                 (92, 1, False, False, False, False),
-                                                 (93, 3, False, True, True, False)]:
-        c = _grad_case(seed, R, mix, bcnorm, carry, weights)
+    for seed, R, mix, bcnorm, carry, weights, groups in [(91, 2, True, True, True, True, 0),
+                                                         (92, 1, False, False, False, False, 0),
+                                                         (93, 3, False, True, True, False, 0),
+                                                         (94, 2, True, True, True, True, 1)]:
+        c = _grad_case(seed, R, mix, bcnorm, carry, weights, groups)
         b, L, H, _, P = c["x"].shape
         N = c["B"].shape[-1]
         r = _rng(seed + 2000)
@@ -468,6 +472,67 @@ def check_layer_gradients_fd(lib=None):
             assert err <= 1e-6 * scale, (seed, name, err, scale)
 
 
+# ---------------------------------------------------------------------------------------------
+# 12. Head groups: raw B and C in G < H slots, slot s shared by heads s H/G .. (s+1) H/G - 1.  The
+#     pages define B and C per head, so each head of a group must get exactly what a one-head
+#     call with its slot's rows gives.  Reached here by slicing every per-head input at h and the
+#     B, C slot at h G / H for a separate one-head call.
+# ---------------------------------------------------------------------------------------------
+_HEAD_AXIS = {"x": 2, "dt": 2, "lam": 2, "theta": 2, "A": 0, "h_in": 1, "Bbar_prev": 1,
+              "x_prev": 1, "phi_in": 1, "bias_B": 0, "bias_C": 0, "normw_B": 0, "normw_C": 0,
+              "w_out": 0}
+
+
+def check_head_groups(lib=None):
+    b, L, H, G, R, N, P = 2, 9, 4, 2, 2, 6, 3
+    c = _rand_case(101, L=L, R=R, N=N, P=P, H=H, b=b)
+    r = _rng(1101)
+    c["B"] = r.standard_normal((b, L, G, R, N))
+    c["C"] = r.standard_normal((b, L, G, R, N))
+    c["bias_B"] = 0.5 * r.standard_normal((H, R, N))
+    c["bias_C"] = 0.5 * r.standard_normal((H, R, N))
+    c["normw_B"] = 1.0 + 0.3 * r.standard_normal((H, N))
+    c["normw_C"] = 1.0 + 0.3 * r.standard_normal((H, N))
+    c["w_out"] = r.standard_normal((H, R, P))
+    out = oracle.layer(c, mix=True, lib=lib)
+    assert out["y"].shape == (b, L, H, P) and out["Bbar"].shape == (b, L, H, R, N)
+    for h in range(H):
+        slot = (h * G) // H
+        one = {k: np.take(v, [h], axis=_HEAD_AXIS[k]) for k, v in c.items() if k in _HEAD_AXIS}
+        one["B"] = c["B"][:, :, slot:slot + 1]
+        one["C"] = c["C"][:, :, slot:slot + 1]
+        ref = oracle.layer(one, mix=True, lib=lib)
+        assert np.abs(out["y"][:, :, h:h + 1] - ref["y"]).max() <= 1e-13 * np.abs(ref["y"]).max()
+        assert np.abs(out["h_out"][:, h:h + 1] - ref["h_out"]).max() <= 1e-13 * np.abs(ref["h_out"]).max()
+        assert np.abs(out["Bbar_last"][:, h:h + 1] - ref["Bbar_last"]).max() <= 1e-13
+    # gradients of the shared rows: central differences of the forward (two groups of two heads,
+    # so a sum over the wrong heads shows)
+    d = _rand_case(102, L=4, R=1, N=4, P=2, H=H, b=1)
+    r = _rng(1102)
+    d["B"] = r.standard_normal((1, 4, G, 1, 4))
+    d["C"] = r.standard_normal((1, 4, G, 1, 4))
+    d["bias_B"] = 0.5 * r.standard_normal((H, 1, 4))
+    d["bias_C"] = 0.5 * r.standard_normal((H, 1, 4))
+    cot = {"y": r.standard_normal((1, 4, H, 1, 2)), "h": r.standard_normal((1, H, 4, 2)),
+           "phi": r.standard_normal((1, H, 2))}
+    grads = oracle.layer_backward(d, cot["y"], cot["h"], cot["phi"], mix=False, lib=lib)
+    step = 1e-5
+    for name in ("B", "C"):
+        flat = d[name].reshape(-1)
+        fd = np.empty(flat.size)
+        for i in range(flat.size):
+            keep = flat[i]
+            flat[i] = keep + step
+            fp = _objective(d, cot, False, True, lib)
+            flat[i] = keep - step
+            fm = _objective(d, cot, False, True, lib)
+            flat[i] = keep
+            fd[i] = (fp - fm) / (2 * step)
+        got = grads[name].reshape(-1)
+        assert grads[name].shape == d[name].shape
+        assert np.abs(got - fd).max() <= 1e-6 * max(1.0, float(np.abs(fd).max())), name
+
+
 ALL_CHECKS = [
     check_masked_matrix_form,
     check_lambda_one_is_euler,
@@ -482,4 +547,5 @@ ALL_CHECKS = [
     check_bcnorm_invariants,
     check_split_carry,
     check_layer_gradients_fd,
+    check_head_groups,
 ]

@@ -334,3 +334,48 @@ def test_layer_chunk_states_errors():
     q = list(p)
     q[12] = q[0]
     assert lib.m3_layer_chunk_states(ctypes.byref(d), *q, None) == m3scan.M3_E_ALIAS
+
+
+def test_head_groups_validation():
+    """dims->ngroups: 0 or a divisor of nheads; only the calls that take raw B and C accept G < H
+    (m3_prefill and m3_decode_step take per-head Bbar and Cbar)."""
+    lib = m3scan.load()
+    assert ctypes.sizeof(m3scan.M3Dims) == 80
+    p = _ptrs(22)
+    for i in (5, 6, 7, 8, 11, 12, 13, 14, 15, 19, 20, 21):
+        p[i] = None
+    layer = lambda dims: lib.m3_layer_prefill(ctypes.byref(dims), *p, 0, None)
+    base = dict(nheads=4, chunk=32)
+    assert layer(_dims(groups=3, **base)) == m3scan.M3_E_DIMS            # 3 does not divide 4
+    assert "ngroups" in m3scan.last_error()
+    assert layer(_dims(groups=8, **base)) == m3scan.M3_E_DIMS            # more slots than heads
+    assert layer(_dims(groups=-1, **base)) == m3scan.M3_E_DIMS
+    for g in (0, 1, 2, 4):                                               # valid: stops at the device
+        assert layer(_dims(groups=g, **base)) == m3scan.M3_E_NODEVICE
+    assert _prefill(_dims(groups=2, nheads=4), _prefill_args()) == m3scan.M3_E_DIMS
+    assert "per-head" in m3scan.last_error()
+    assert _prefill(_dims(groups=4, nheads=4), _prefill_args()) == m3scan.M3_E_NODEVICE
+    dec = _ptrs(11)
+    dec[9] = None
+    assert lib.m3_decode_step(ctypes.byref(_dims(seqlen=1, nheads=4, groups=1)), *dec, None) == m3scan.M3_E_DIMS
+    # raw B, C of G slots are smaller than per-head ones: an output right after a G-slot B is legal
+    dims = _dims(groups=1, **base)
+    q = list(p)
+    nB = 2 * 8 * 1 * 1 * 128 * 2                                         # b L G R N bf16
+    q[16] = P(q[1].value + nB)                                           # y just past B
+    assert layer(dims) == m3scan.M3_E_NODEVICE
+    assert lib.m3_layer_prefill(ctypes.byref(dims), *q, 0, None) == m3scan.M3_E_NODEVICE
+    q[16] = P(q[1].value + nB - 16)                                      # y overlapping B's end
+    assert lib.m3_layer_prefill(ctypes.byref(dims), *q, 0, None) == m3scan.M3_E_ALIAS
+
+
+def test_head_groups_backward_workspace():
+    """With G < H the backward workspace adds per-head dB and dC rows (b L H R N io each)."""
+    d = _dims(seqlen=130, nheads=4)
+    g = _dims(seqlen=130, nheads=4, groups=2)
+    r = lambda n: (n + 255) // 256 * 256
+    per_head = 2 * 130 * 4 * 1 * 128 * 2
+    assert m3scan.layer_backward_workspace_bytes(g) == m3scan.layer_backward_workspace_bytes(d) + 2 * r(per_head)
+    assert m3scan.layer_backward_workspace_bytes(_dims(seqlen=130, nheads=4, groups=4)) == \
+        m3scan.layer_backward_workspace_bytes(d)
+    assert m3scan.layer_backward_workspace_bytes(_dims(nheads=4, groups=3)) == 0

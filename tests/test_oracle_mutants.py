@@ -6,6 +6,7 @@ wrong sign, a wrong index or operand), built on the CPU into a temporary library
 the pins are sharp enough to catch each kind of mistake, not that the oracle is right (that is
 what ``test_oracle_pins.py`` checks).
 """
+import numpy as np
 import pytest
 
 import oracle
@@ -78,3 +79,23 @@ def test_mutant_is_caught(tmp_path, name, old, new):
         except AssertionError:
             failed.append(check.__name__)
     assert failed, "no pin caught mutant " + name
+
+
+# Planted mistakes in the oracle's head-group layer (Python): expanding the slots in the wrong
+# order (slot h mod G instead of h // (H / G)) and summing the gradients over the wrong heads.
+def _tiled_expansion(v, H):
+    v = oracle._f64(v)
+    return np.tile(v, (1, 1, H // v.shape[2], 1, 1))
+
+
+def _strided_fold(g, G):
+    b, L, H, R, N = g.shape
+    return g.reshape(b, L, H // G, G, R, N).sum(axis=2)
+
+
+@pytest.mark.parametrize("name,fn", [("heads_from_groups", _tiled_expansion),
+                                     ("groups_from_heads", _strided_fold)])
+def test_group_mutant_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(oracle, name, fn)
+    with pytest.raises(AssertionError):
+        pins.check_head_groups()
