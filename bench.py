@@ -12,7 +12,7 @@ every input) on the SISO and MIMO workloads, the
 roofline of the dominant kernel measured live with HIP events on the launch stream, and the fp64
 oracle's throughput on a bounded sample of the same prefill workload on the host cores.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 100] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -83,12 +83,13 @@ def bcnorm_bytes_per_token_head(w) -> int:
     return es * (4 * R * N + N // 2 + 1)
 
 
-def layer_bytes_per_token_head(w) -> int:
-    """m3_layer_prefill: x, raw B and C, theta, dt, lam read once, y written once."""
+def layer_bytes_per_token_head(w) -> float:
+    """m3_layer_prefill: x, raw B and C, theta, dt, lam read once, y written once.  Raw B and C
+    shared by groups of heads are read once per group: a share G / H of them per head."""
     es = 2 if w.io == "bf16" else 4
     R, N, P = w.rank, w.dstate, w.headdim
     y = P if w.mix else R * P
-    return es * (R * P + 2 * R * N + N // 2 + 2 + y)
+    return es * (R * P + 2 * R * N * w.bc_heads / w.nheads + N // 2 + 2 + y)
 
 
 def prefill_flops_per_token_head(w) -> int:
@@ -180,7 +181,7 @@ def time_layer(w, inp, chunk, steps, warmup, dev):
     stream = torch.cuda.current_stream()
     # the sequence-split workspace (few long sequences), allocated once outside the timed region
     dims = m3scan.make_dims(b, L, H, P, N, R, chunk, m3scan.M3_BF16 if w.io == "bf16" else m3scan.M3_F32,
-                            w.bcnorm)
+                            w.bcnorm, groups=w.groups)
     need = m3scan.layer_prefill_workspace_bytes(dims)
     ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else False
 
@@ -488,7 +489,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the GPU reaches its steady clocks after ~20 ms of sustained work: 100 steps of the SISO step
+    # (~25 ms) before the timed ones; with 3 the first timed steps ran ~10% slow
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -572,6 +575,20 @@ def main():
                 entry["m3_prefill"] = {"ms": ms_p, "tokens/s": wv.batch * wv.seqlen / (ms_p / 1e3),
                                        "GB/s": pb / ms_p / 1e6, "hbm_frac": pb / ms_p / 1e6 / HBM_PEAK_GBS}
             variants[vname] = entry
+            del inpv
+            torch.cuda.empty_cache()
+        # raw B and C shared by groups of heads (G = 1: all 64 heads; G = 8: groups of 8)
+        for vname in ("siso_g1_b8_l2048", "mimo4_g1_b8_l2048", "mimo4_g8_b8_l2048"):
+            wv = inputs.WORKLOADS[vname]
+            inpv = inputs.make_prefill_inputs(wv, seed=0, device=dev)
+            thv = wv.batch * wv.seqlen * wv.nheads
+            ms_l = time_layer(wv, inpv, LAYER_CHUNK_ROWS // wv.rank, args.steps, args.warmup, dev)
+            lb = thv * layer_bytes_per_token_head(wv) + wv.batch * wv.nheads * wv.dstate * (wv.headdim + 1) * 4
+            lf = thv * prefill_flops_per_token_head(wv.with_(chunk=LAYER_CHUNK_ROWS // wv.rank))
+            variants[vname] = {"m3_layer_prefill": {
+                "ms": ms_l, "tokens/s": wv.batch * wv.seqlen / (ms_l / 1e3), "groups": wv.groups,
+                "GB/s": lb / ms_l / 1e6, "hbm_frac": lb / ms_l / 1e6 / HBM_PEAK_GBS,
+                "TFLOP/s": lf / ms_l / 1e9, "mfma_frac": lf / ms_l / 1e9 / BF16_MFMA_PEAK_TFLOPS}}
             del inpv
             torch.cuda.empty_cache()
         variants["siso_varlen_packed"] = time_varlen(w, args.steps, args.warmup, dev)
