@@ -533,6 +533,40 @@ def check_head_groups(lib=None):
         assert np.abs(got - fd).max() <= 1e-6 * max(1.0, float(np.abs(fd).max())), name
 
 
+# ---------------------------------------------------------------------------------------------
+# 13. Two readings written out (the pages leave them open): the MIMO output mixing
+#     y[p] = sum_r w_out[h, r, p] Y[r, p] (papernotes key design 3 gives x_t as P x R; the mixing
+#     back to P is the reading) and BCNorm's eps, added to the mean square under the square root.
+#     Each is checked against its definition by another route: the unmixed outputs weighted and
+#     summed here, and the closed form of a constant vector, c w / sqrt(c^2 + eps).
+# ---------------------------------------------------------------------------------------------
+def check_output_mixing(lib=None):
+    c = _rand_case(111, L=7, R=3, N=4, P=5, H=2, b=2)
+    r = _rng(1111)
+    w_out = r.standard_normal((2, 3, 5))
+    c["w_out"] = w_out
+    mixed = oracle.layer(c, mix=True, lib=lib)["y"]                  # [b, L, H, P]
+    ranks = oracle.layer(c, mix=False, lib=lib)["y"]                 # [b, L, H, R, P]
+    ref = np.zeros_like(mixed)
+    for h in range(2):
+        for rr in range(3):
+            ref[:, :, h, :] += w_out[h, rr, :] * ranks[:, :, h, rr, :]
+    assert np.abs(mixed - ref).max() <= 1e-13 * np.abs(ref).max()
+
+
+def check_bcnorm_eps(lib=None):
+    L, N = 3, 8
+    dt = np.full((1, L, 1), 0.3)
+    th0 = np.zeros((1, L, 1, N // 2))
+    w = np.linspace(0.5, 1.5, N).reshape(1, N)
+    for cval, eps in ((0.7, 1e-5), (0.7, 0.49), (-2.0, 3.0), (1e-3, 1e-5)):
+        B = np.full((1, L, 1, 1, N), cval)
+        Bb, Cb, _ = oracle.bcnorm_rope(B, -B, dt, th0, normw_B=w, normw_C=w, eps=eps, lib=lib)
+        want = cval * w[0] / math.sqrt(cval * cval + eps)
+        assert np.abs(Bb[0, :, 0, 0] - want).max() <= 1e-14
+        assert np.abs(Cb[0, :, 0, 0] + want).max() <= 1e-14
+
+
 ALL_CHECKS = [
     check_masked_matrix_form,
     check_lambda_one_is_euler,
@@ -548,4 +582,6 @@ ALL_CHECKS = [
     check_split_carry,
     check_layer_gradients_fd,
     check_head_groups,
+    check_output_mixing,
+    check_bcnorm_eps,
 ]

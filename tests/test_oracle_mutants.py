@@ -36,6 +36,10 @@ MUTANTS = [
     ("h_in_ignored", "g[i] = h_in ? h_in[(ib * H + h) * NP + i] : 0.0;", "g[i] = 0.0;"),
     ("carried_input_ignored", "if (Bbar_prev && x_prev) {", "if (0) {"),
     ("rank_sum_dropped", "u[n * P + p] += bt[n] * xt[p];", "u[n * P + p] = bt[n] * xt[p];"),
+    ("mix_weight_of_rank_zero", "acc += w_out[(h * R + r) * P + p] * Y[r * P + p];",
+     "acc += w_out[(h * R) * P + p] * Y[r * P + p];"),
+    ("eps_outside_sqrt", "const double inv = 1.0 / sqrt(ms + eps);",
+     "const double inv = 1.0 / (sqrt(ms) + eps);"),
     ("pair_swapped_in_rotation", "out[2 * k + 1] = -s * v[2 * k] + c * v[2 * k + 1];",
      "out[2 * k + 1] = -s * v[2 * k + 1] + c * v[2 * k];"),
     # gradients
