@@ -502,8 +502,8 @@ def main():
                     help="only time a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the layer core has no cross-GPU step, and this build "
-              "runs on a single MI355X (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU: the layer core has no cross-GPU step, and its throughput "
+              "is measured on a single MI355X (requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

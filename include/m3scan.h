@@ -63,7 +63,7 @@ typedef enum {
     M3_E_DIMS = 2,        /* a size is negative, odd where it must be even, or inconsistent */
     M3_E_ALIGN = 3,       /* a pointer violates the alignment rule above                    */
     M3_E_DTYPE = 4,       /* dims->io is not M3_F32 or M3_BF16                             */
-    M3_E_UNSUPPORTED = 5, /* valid, but outside the shapes this build has kernels for       */
+    M3_E_UNSUPPORTED = 5, /* valid, but outside the shapes the library has kernels for     */
     M3_E_NODEVICE = 6,    /* no current HIP device, or it is not gfx950                     */
     M3_E_LAUNCH = 7,      /* the HIP runtime refused a kernel launch                        */
     M3_E_WORKSPACE = 8,   /* workspace NULL or smaller than *_workspace_bytes returned      */
@@ -132,7 +132,7 @@ typedef struct {
  *   workspace   device scratch of m3_bcnorm_rope_workspace_bytes(dims) bytes (may be NULL
  *               when that is 0)
  * phi_out may be the same buffer as phi_in (decode carries the angle in place); no other
- * output may overlap an input.  This build has kernels for N in {16, 32, 64, 128, 256} and
+ * output may overlap an input.  The library has kernels for N in {16, 32, 64, 128, 256} and
  * 1 <= R <= 64; other shapes return M3_E_UNSUPPORTED.
  */
 m3_status m3_bcnorm_rope(const m3_dims* dims, const void* B, const void* C, const void* dt,
@@ -185,7 +185,7 @@ size_t m3_bcnorm_rope_workspace_bytes(const m3_dims* dims);
  * sequence's rows of a tensor span less than 2^31 bytes: (L + 3 chunk) * H * R * max(N, P) * io
  * size < 2^31, else M3_E_DIMS (the kernel addresses a sequence with 32-bit offsets; a longer
  * sequence is split into calls, which the carried state and last step make exact).
- * dims->chunk * R must be 16, 32, 48 or 64.  This build has kernels for (N, P) in {(16,16),
+ * dims->chunk * R must be 16, 32, 48 or 64.  The library has kernels for (N, P) in {(16,16),
  * (64,64), (128,64)} and R in {1, 2, 4, 8, 16} dividing 16; other shapes return
  * M3_E_UNSUPPORTED.
  */
@@ -216,7 +216,7 @@ size_t m3_prefill_workspace_bytes(const m3_dims* dims);
  * Arguments are those of the two calls, with the same shapes, optionality and meaning; Bbar_last
  * receives the rotated Bbar of the last step, as m3_prefill would return it.  dims->chunk = 0
  * picks 32 / R steps per chunk.  h_out may be the h_in buffer and phi_out the phi_in buffer;
- * no other output may overlap an input.  This build has kernels for (N, P) in {(16, 16),
+ * no other output may overlap an input.  The library has kernels for (N, P) in {(16, 16),
  * (64, 64), (128, 64)}, R in {1, 2, 4, 8, 16} and chunk * R in {16, 32, 64};
  * other shapes return M3_E_UNSUPPORTED.  The sequence length limit of m3_prefill applies (with
  * the angle carried as phi_in / phi_out when a sequence is split).  The workspace (optional,
