@@ -546,6 +546,9 @@ def main():
     w = inputs.WORKLOADS["siso_b8_l2048"]
     inp = inputs.make_prefill_inputs(w, seed=0, device=dev)
     kernels = path_stats(w, inp, LAYER_CHUNK_ROWS)
+    # the practical ceiling of this GPU's memory system in the same run: a plain 1 GiB device copy
+    copy = copy_probe(1 << 30, 10, 10, dev)
+    torch.cuda.empty_cache()
     ms_step = kernels["m3_layer_prefill"]["ms"]
     tokens = w.batch * w.seqlen
     mimo = None
@@ -619,7 +622,8 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4),
                 "traffic": recorded_traffic(kname, w.name),
                 "algorithmic_bytes_per_launch": kd["bytes"], "avg_launch_ms": round(kd["ms"], 5),
-                "mfma_tflops": round(kd["TFLOP/s"], 1), "mfma_frac_of_bf16_peak": round(kd["mfma_frac"], 4)}
+                "mfma_tflops": round(kd["TFLOP/s"], 1), "mfma_frac_of_bf16_peak": round(kd["mfma_frac"], 4),
+                "copy_GB/s": round(copy["GB/s"], 1), "frac_of_copy": round(kd["GB/s"] / copy["GB/s"], 4)}
 
     decode = None
     if not args.no_decode:
