@@ -148,18 +148,28 @@ __global__ __launch_bounds__(64 * kParts) void angle_partial_kernel(BcnormRopeAr
 }
 
 // Quarter sums -> quarter start angles (exclusive scan, phi_in added), in place; the inclusive
-// total is the final angle phi_out.
+// total is the final angle phi_out.  A thread reads a block of kScanBlk quarter sums before it
+// writes any back: a load that follows a store to the same array waits for it, so one value at a
+// time would cost a memory round trip per quarter.
+constexpr int kScanBlk = 8;
 __global__ void angle_scan_kernel(BcnormRopeArgs a) {
     const int K = a.N / 2;
     const int64_t bh = blockIdx.x;
     const int64_t nq = (int64_t)a.nseg * kParts;
     for (int k = threadIdx.x; k < K; k += blockDim.x) {
         float run = a.phi_in ? wrap_angle(a.phi_in[bh * K + k]) : 0.0f;
-        for (int64_t s = 0; s < nq; ++s) {
-            float* p = a.seg_phi + (bh * nq + s) * K + k;
-            const float v = *p;
-            *p = run;
-            run = wrap_angle(run + v);
+        float* col = a.seg_phi + bh * nq * K + k;
+        for (int64_t s0 = 0; s0 < nq; s0 += kScanBlk) {
+            float v[kScanBlk];
+#pragma unroll
+            for (int i = 0; i < kScanBlk; ++i) v[i] = s0 + i < nq ? col[(s0 + i) * K] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < kScanBlk; ++i) {
+                if (s0 + i < nq) {
+                    col[(s0 + i) * K] = run;
+                    run = wrap_angle(run + v[i]);
+                }
+            }
         }
         a.phi_out[bh * K + k] = run;
     }

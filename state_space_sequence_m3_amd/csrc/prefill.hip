@@ -778,9 +778,10 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 // the one the scan adds for a carried (Bbar_prev, x_prev).  kCombineElems state elements per
 // workgroup (4 per thread, kept in registers along the chain).
 constexpr int kCombineElems = 1024;
-template <typename T>
+constexpr int kCombineBlk = 8;   // segments whose inputs are read ahead of the chain
+template <typename T, int R>
 __global__ __launch_bounds__(256) void segment_combine_kernel(PrefillArgs a) {
-    const int N = a.N, P = a.P, R = a.R, H = a.H;
+    const int N = a.N, P = a.P, H = a.H;
     const int64_t NP = (int64_t)N * P;
     const int G = (int)((NP + kCombineElems - 1) / kCombineElems);
     const int64_t bh = blockIdx.x / G, b = bh / H;
@@ -792,21 +793,43 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(PrefillArgs a) {
         el[j] = (int64_t)part * kCombineElems + threadIdx.x + 256 * j;
         gp[j] = el[j] < NP ? a.ws_state[bh * a.nseg * NP + el[j]] : 0.f;   // segment 0: already true
     }
-    for (int s = 1; s + 1 < a.nseg; ++s) {
-        const float decay = exp2f(a.ws_l2[bh * a.nseg + s]);
-        const int64_t row0 = (b * a.L + s * a.seglen) * H + h;   // step t0 of this head
-        const float c0 = (1.0f - load_f32((const T*)a.lam + row0)) * load_f32((const T*)a.dt + row0);
-        const T* Bp = (const T*)a.ws_bbar + (bh * a.nseg + s - 1) * (int64_t)(R * N);
-        const T* xp = (const T*)a.x + (row0 - H) * R * P;
-        float* gs = a.ws_state + (bh * a.nseg + s) * NP;
+    // Segments in blocks of kCombineBlk: every input of a block (decays, c0, the carried-in
+    // outer products u, the segments' own end states) is read before any result is written back,
+    // since a load that follows a store to the workspace waits for it; only the chain through gp
+    // is sequential.
+    for (int s0 = 1; s0 + 1 < a.nseg; s0 += kCombineBlk) {
+        float decay[kCombineBlk], c0[kCombineBlk], u[kCombineBlk][4], own[kCombineBlk][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (el[j] >= NP) continue;
-            const int n = (int)(el[j] / P), p = (int)(el[j] % P);
-            float u = 0.f;
-            for (int r = 0; r < R; ++r) u = fmaf(load_f32(Bp + r * N + n), load_f32(xp + r * P + p), u);
-            gp[j] = fmaf(decay, fmaf(c0, u, gp[j]), gs[el[j]]);
-            gs[el[j]] = gp[j];
+        for (int i = 0; i < kCombineBlk; ++i) {
+            const int s = s0 + i + 1 < a.nseg ? s0 + i : s0;   // past the last one: unused
+            decay[i] = exp2f(a.ws_l2[bh * a.nseg + s]);
+            const int64_t row0 = (b * a.L + s * a.seglen) * H + h;   // step t0 of this head
+            c0[i] = (1.0f - load_f32((const T*)a.lam + row0)) * load_f32((const T*)a.dt + row0);
+            const T* Bp = (const T*)a.ws_bbar + (bh * a.nseg + s - 1) * (int64_t)(R * N);
+            const T* xp = (const T*)a.x + (row0 - H) * R * P;
+            const float* gs = a.ws_state + (bh * a.nseg + s) * NP;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                u[i][j] = 0.f;
+                own[i][j] = 0.f;
+                if (el[j] >= NP) continue;
+                const int n = (int)(el[j] / P), p = (int)(el[j] % P);
+#pragma unroll
+                for (int r = 0; r < R; ++r) u[i][j] = fmaf(load_f32(Bp + r * N + n), load_f32(xp + r * P + p), u[i][j]);
+                own[i][j] = gs[el[j]];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kCombineBlk; ++i) {
+            const int s = s0 + i;
+            if (s + 1 >= a.nseg) break;
+            float* gs = a.ws_state + (bh * a.nseg + s) * NP;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (el[j] >= NP) continue;
+                gp[j] = fmaf(decay[i], fmaf(c0[i], u[i][j], gp[j]), own[i][j]);
+                gs[el[j]] = gp[j];
+            }
         }
     }
 }
@@ -865,14 +888,23 @@ hipError_t launch_layer(const PrefillArgs& a, bool bf16_io, hipStream_t s) {
     return bf16_io ? launch_t<bf16, true>(a, s) : launch_t<float, true>(a, s);
 }
 
+template <typename T>
+hipError_t launch_combine_t(const PrefillArgs& a, dim3 grid, hipStream_t s) {
+    switch (a.R) {   // the ranks as a constant: the loads of a block of segments go out together
+        case 1: hipLaunchKernelGGL((segment_combine_kernel<T, 1>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((segment_combine_kernel<T, 2>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((segment_combine_kernel<T, 4>), grid, dim3(256), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((segment_combine_kernel<T, 8>), grid, dim3(256), 0, s, a); break;
+        case 16: hipLaunchKernelGGL((segment_combine_kernel<T, 16>), grid, dim3(256), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_segment_combine(const PrefillArgs& a, bool bf16_io, hipStream_t s) {
     const int64_t G = ((int64_t)a.N * a.P + kCombineElems - 1) / kCombineElems;
     const dim3 grid((unsigned)(a.b * a.H * G));
-    if (bf16_io)
-        hipLaunchKernelGGL(segment_combine_kernel<bf16>, grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(segment_combine_kernel<float>, grid, dim3(256), 0, s, a);
-    return hipGetLastError();
+    return bf16_io ? launch_combine_t<bf16>(a, grid, s) : launch_combine_t<float>(a, grid, s);
 }
 
 }  // namespace m3
