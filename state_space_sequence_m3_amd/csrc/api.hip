@@ -237,7 +237,14 @@ hipError_t run_split(m3::PrefillArgs a, const SplitPlan& sp, void* ws, bool fuse
         a.angle_parts = m3::bcnorm_rope_parts();
     }
     a.pass = 1;
-    if (e == hipSuccess) e = fused ? m3::launch_layer(a, bf16, s) : m3::launch_prefill(a, bf16, s);
+    {
+        // the states-only pass stages no C and computes no y, so its per-chunk fixed work weighs
+        // more: the fused call runs it on 64-row chunks (its end states do not depend on the
+        // chunk; 1.2% off the b1 L16384 MIMO call)
+        m3::PrefillArgs a1 = a;
+        if (fused && 64 % a.R == 0 && m3::layer_supported(a.N, a.P, a.R, 64, bf16)) a1.Q = 64 / a.R;
+        if (e == hipSuccess) e = fused ? m3::launch_layer(a1, bf16, s) : m3::launch_prefill(a1, bf16, s);
+    }
     if (e == hipSuccess && sp.nseg > 2) e = m3::launch_segment_combine(a, bf16, s);
     a.pass = 2;
     if (e == hipSuccess) e = fused ? m3::launch_layer(a, bf16, s) : m3::launch_prefill(a, bf16, s);
