@@ -26,6 +26,8 @@ SPLIT_CASES = [
     ("bf16", 1, 4096, 2, 64, 64, 1, 32, 32, False, False),   # N = 64, segments of 1024
     ("bf16", 2, 3500, 1, 64, 128, 2, 8, 32, True, True),     # b = 2, 16-row fused chunks
     ("bf16", 3, 2100, 1, 64, 128, 1, 16, 16, False, True),   # b = 3, chunk 16 in both calls
+    ("bf16", 1, 12288, 1, 64, 128, 1, 32, 64, False, True),  # 12 segments: the chaining runs
+                                                              # two blocks of segments
 ]
 
 
