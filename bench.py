@@ -380,10 +380,11 @@ def time_decode(w, steps, warmup, dev):
 def backward_bytes_per_token_head(w) -> int:
     """Compulsory HBM bytes of m3_layer_backward per (token, head): the forward inputs x, B, C, dt,
     lam, theta and the cotangent dy read once, the gradients dx, dB, dC, ddt, dlam, dtheta written
-    once.  The chunk states the call saves and reads back are its own intermediates (excluded)."""
+    once.  The chunk states the call saves and reads back are its own intermediates (excluded).
+    Raw B and C shared by groups of heads (and their gradients) count G / H per head."""
     es = 2 if w.io == "bf16" else 4
     R, N, P = w.rank, w.dstate, w.headdim
-    io = R * P + 2 * R * N + 2 + N // 2
+    io = R * P + 2 * R * N * w.bc_heads / w.nheads + 2 + N // 2
     return es * (2 * io + (P if w.mix else R * P))
 
 
@@ -410,7 +411,7 @@ def time_backward(w, steps, warmup, dev):
                                      inp["lam"], cot["dy"], inp["normw_B"], inp["normw_C"], inp["bias_B"],
                                      inp["bias_C"], mixw, bcnorm=w.bcnorm)
     dims = m3scan.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, 0,
-                            m3scan._io_code(w.torch_io), w.bcnorm)
+                            m3scan._io_code(w.torch_io), w.bcnorm, groups=w.groups)
     ws = torch.empty(m3scan.layer_backward_workspace_bytes(dims), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -655,7 +656,8 @@ def main():
     backward = None
     if not args.no_backward:
         backward = {}
-        for bname in ("siso_b8_l2048",) + (() if args.no_mimo else ("mimo4_b8_l2048",)):
+        # the last: raw B and C shared by all heads (dB, dC summed over the heads by a second kernel)
+        for bname in ("siso_b8_l2048",) + (() if args.no_mimo else ("mimo4_b8_l2048", "siso_g1_b8_l2048")):
             wb = inputs.WORKLOADS[bname]
             t = time_backward(wb, args.steps, args.warmup, dev)
             thb = wb.batch * wb.seqlen * wb.nheads
