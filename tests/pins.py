@@ -567,6 +567,53 @@ def check_bcnorm_eps(lib=None):
         assert np.abs(Cb[0, :, 0, 0] + want).max() <= 1e-14
 
 
+# ---------------------------------------------------------------------------------------------
+# 14. Decode = the layer core one token at a time (aipaper section 4.1 Proposition 1 is a step
+#     recurrence; decode carries its state, angle and previous-token factors from step to step).
+#     k chained ``oracle.decode_step`` calls must give the outputs of one ``oracle.layer`` call
+#     over the same k steps, and leave behind its final state, angle, last rotated B and last x.
+#     Without BCNorm or bias the chained outputs must also equal the complex-frame reference of
+#     check 6 (aipaper Propositions 2-3), a route that does not go through ``oracle.layer``.
+# ---------------------------------------------------------------------------------------------
+def _decode_chain(c, mix, bcnorm, lib):
+    """Run c's L steps through oracle.decode_step one token at a time; returns (ys, state)."""
+    L = c["x"].shape[1]
+    consts = {k: c[k] for k in ("A", "normw_B", "normw_C", "bias_B", "bias_C", "w_out") if k in c}
+    state = {"h": c["h_in"], "phi": c["phi_in"], "Bbar_prev": c["Bbar_prev"], "x_prev": c["x_prev"]}
+    ys = []
+    for t in range(L):
+        tok = {k: c[k][:, t] for k in ("x", "B", "C", "dt", "lam", "theta")}
+        y, state = oracle.decode_step(state, tok, consts, bcnorm=bcnorm, mix=mix, lib=lib)
+        ys.append(y)
+    return np.stack(ys, axis=1), state
+
+
+def check_decode_chain(lib=None):
+    c = _rand_case(121, L=9, R=2, N=6, P=3, H=2, b=2)
+    r = _rng(1121)
+    c["normw_B"] = 1.0 + 0.3 * r.standard_normal((2, 6))
+    c["normw_C"] = 1.0 + 0.3 * r.standard_normal((2, 6))
+    c["bias_B"] = 0.5 * r.standard_normal((2, 2, 6))
+    c["bias_C"] = 0.5 * r.standard_normal((2, 2, 6))
+    c["w_out"] = r.standard_normal((2, 2, 3))
+    full = oracle.layer(c, mix=True, lib=lib)
+    ys, st = _decode_chain(c, True, True, lib)
+    tol = lambda ref: 1e-12 * max(1.0, float(np.abs(ref).max()))
+    assert np.abs(ys - full["y"]).max() <= tol(full["y"]), "decode outputs"
+    assert np.abs(st["h"] - full["h_out"]).max() <= tol(full["h_out"]), "decode state"
+    assert np.abs(st["phi"] - full["phi_out"]).max() <= 1e-12, "decode angle"
+    assert np.abs(st["Bbar_prev"] - full["Bbar_last"]).max() <= tol(full["Bbar_last"]), "decode last Bbar"
+    assert np.abs(st["x_prev"] - full["x_last"]).max() == 0.0, "decode last x"
+    # no BCNorm, no bias, unmixed: against the complex-valued recurrence
+    d = _rand_case(122, L=11, R=2, N=8, P=3)
+    ys, st = _decode_chain(d, False, False, lib)
+    ref, hz, Phi = _complex_reference(d, (d["B"][0, :, 0], d["C"][0, :, 0]))
+    assert np.abs(ys[0, :, 0] - ref).max() <= 1e-12 * np.abs(ref).max(), "decode vs complex frame"
+    gz = st["h"][0, 0, 0::2] + 1j * st["h"][0, 0, 1::2]
+    assert np.abs(np.exp(1j * Phi)[:, None] * gz - hz).max() <= 1e-12 * np.abs(hz).max()
+    assert np.abs(st["phi"][0, 0] - Phi).max() <= 1e-12
+
+
 ALL_CHECKS = [
     check_masked_matrix_form,
     check_lambda_one_is_euler,
@@ -584,4 +631,5 @@ ALL_CHECKS = [
     check_head_groups,
     check_output_mixing,
     check_bcnorm_eps,
+    check_decode_chain,
 ]

@@ -103,3 +103,38 @@ def test_group_mutant_is_caught(monkeypatch, name, fn):
     monkeypatch.setattr(oracle, name, fn)
     with pytest.raises(AssertionError):
         pins.check_head_groups()
+
+
+# Planted wiring mistakes in the oracle's decode step (Python): the carry it hands to the next
+# token.  Each wraps the real step and then corrupts one carried field, as a mistake in mapping
+# the layer's outputs back into the state would.
+_REAL_DECODE = oracle.decode_step
+
+
+def _stale_bbar(state, tok, consts, **kw):
+    y, new = _REAL_DECODE(state, tok, consts, **kw)
+    return y, dict(new, Bbar_prev=state["Bbar_prev"])
+
+
+def _unadvanced_phi(state, tok, consts, **kw):
+    y, new = _REAL_DECODE(state, tok, consts, **kw)
+    return y, dict(new, phi=state["phi"])
+
+
+def _stale_x(state, tok, consts, **kw):
+    y, new = _REAL_DECODE(state, tok, consts, **kw)
+    return y, dict(new, x_prev=state["x_prev"])
+
+
+def _unrotated_bbar(state, tok, consts, **kw):
+    # the raw B (normalised and biased, not rotated) carried instead of the rotated one
+    y, new = _REAL_DECODE(state, tok, consts, **kw)
+    return y, dict(new, Bbar_prev=oracle._f64(tok["B"]))
+
+
+@pytest.mark.parametrize("fn", [_stale_bbar, _unadvanced_phi, _stale_x, _unrotated_bbar],
+                         ids=lambda f: f.__name__.lstrip("_"))
+def test_decode_wiring_mutant_is_caught(monkeypatch, fn):
+    monkeypatch.setattr(oracle, "decode_step", fn)
+    with pytest.raises(AssertionError):
+        pins.check_decode_chain()
