@@ -40,8 +40,11 @@
  *    M3_OK means "validated and enqueued"; faults during execution surface at the caller's
  *    next synchronisation.  Calls on one stream run in order.
  *  - Errors.  A non-OK status leaves every output untouched and sets a message readable with
- *    m3_last_error() on the calling thread.  Numeric values are not validated (dt <= 0, A > 0,
- *    NaN or Inf simply propagate).
+ *    m3_last_error() on the calling thread.  Numeric values live in device memory and are not
+ *    validated.  The kernels assume that the decay never grows, i.e. dt * A <= 0 at every step
+ *    (dt > 0 after softplus and A <= 0, as the method defines them): the chunked kernels clamp
+ *    the exponent of each decay factor exp(A * sum of dt) at 0, so with dt * A > 0 their results
+ *    are not those of the recurrence (no error is reported).  NaN and Inf propagate.
  *  - Device.  The current HIP device must be a gfx950 GPU, else M3_E_NODEVICE.
  *  - Threads.  Calls from several host threads are safe; calls that write the same buffers
  *    must be ordered by the caller.

@@ -532,8 +532,10 @@ m3_status m3_prefill(const m3_dims* d, const void* x, const void* Bbar, const vo
                        {h_in, 1, "h_in"}};
     if ((s = check_align(a16, 6, 16)) != M3_OK) return s;
     const Buf aes[] = {{dt, 1, "dt"}, {lam, 1, "lam"}, {Bbar_prev, 1, "Bbar_prev"}, {x_prev, 1, "x_prev"},
-                       {Bbar_last, 1, "Bbar_last"}, {x_last, 1, "x_last"}, {A, 1, "A"}, {w_out, 1, "w_out"}};
-    if ((s = check_align(aes, 8, es)) != M3_OK) return s;
+                       {Bbar_last, 1, "Bbar_last"}, {x_last, 1, "x_last"}};
+    if ((s = check_align(aes, 6, es)) != M3_OK) return s;
+    const Buf a4[] = {{A, 1, "A"}, {w_out, 1, "w_out"}};
+    if ((s = check_align(a4, 2, 4)) != M3_OK) return s;
     const Buf ins[] = {{x, nX, "x"}, {Bbar, nBC, "Bbar"}, {Cbar, nBC, "Cbar"}, {dt, nStep, "dt"}, {A, nA, "A"},
                        {lam, nStep, "lam"}, {w_out, nWo, "w_out"}, {Bbar_prev, nBp, "Bbar_prev"},
                        {x_prev, nXp, "x_prev"}};
@@ -612,9 +614,10 @@ m3_status m3_decode_step(const m3_dims* d, float* h, const void* Bbar_prev, cons
                     (long long)N, (long long)P, (long long)R);
     if (!aligned(h, 16)) return fail(M3_E_ALIGN, "h is not 16-byte aligned");
     const Buf aes[] = {{Bbar_prev, 1, "Bbar_prev"}, {x_prev, 1, "x_prev"}, {x, 1, "x"}, {Bbar, 1, "Bbar"},
-                       {Cbar, 1, "Cbar"}, {dt, 1, "dt"}, {lam, 1, "lam"}, {y, 1, "y"}, {A, 1, "A"},
-                       {w_out, 1, "w_out"}};
-    if ((s = check_align(aes, 10, es)) != M3_OK) return s;
+                       {Cbar, 1, "Cbar"}, {dt, 1, "dt"}, {lam, 1, "lam"}, {y, 1, "y"}};
+    if ((s = check_align(aes, 8, es)) != M3_OK) return s;
+    const Buf a4[] = {{A, 1, "A"}, {w_out, 1, "w_out"}};
+    if ((s = check_align(a4, 2, 4)) != M3_OK) return s;
     const Buf ins[] = {{Bbar_prev, nBp, "Bbar_prev"}, {x_prev, nXp, "x_prev"}, {x, nXp, "x"}, {Bbar, nBp, "Bbar"},
                        {Cbar, nBp, "Cbar"}, {dt, nStep, "dt"}, {A, nA, "A"}, {lam, nStep, "lam"},
                        {w_out, nWo, "w_out"}};

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "m3_mapping.h"
+
 namespace m3 {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -168,20 +170,5 @@ __device__ __forceinline__ uint32_t clamp_bytes(int64_t n) {
 __device__ __forceinline__ float wrap_angle(float a) { return a - kTwoPi * rintf(a * kInvTwoPi); }
 // The same for an angle in turns (revolutions): reduced to [-1/2, 1/2].
 __device__ __forceinline__ float wrap_turns(float a) { return a - rintf(a); }
-
-// Raw B and C with G head slots shared by groups of H / G consecutive heads: the slot of head h,
-// and the slots per step (G = 0: one slot per head).
-__device__ __forceinline__ int bc_slot(int h, int H, int G) { return G > 0 ? h / (H / G) : h; }
-__device__ __forceinline__ int bc_slots(int H, int G) { return G > 0 ? G : H; }
-
-// XCD-aware order of a grid's work items.  The dispatcher hands workgroup i to XCD i mod 8, each
-// XCD with its own L2; this maps workgroup i to item (i mod 8) * n/8 + i / 8, so that every XCD
-// takes one contiguous range of items in order (n a multiple of 8, else the identity).
-// Neighbouring items, such as the heads of a group that read the same raw B and C, then meet in
-// one L2.
-constexpr int kXcds = 8;
-__device__ __forceinline__ int64_t xcd_item(int64_t i, int64_t n) {
-    return n % kXcds == 0 ? (i % kXcds) * (n / kXcds) + i / kXcds : i;
-}
 
 }  // namespace m3

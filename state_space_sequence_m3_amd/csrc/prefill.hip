@@ -168,8 +168,13 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const float* hin = nullptr;
     const T* Bprev = nullptr;
     const T* xprev = nullptr;
+    // Split sequences and a carry updated in place (h_out == h_in): the last segment of pass 2
+    // writes h_out while segment 0 of the same launch may not have read h_in yet (nothing orders
+    // the workgroups).  Pass 1's segment 0 therefore saves h_in in the state slot of the last
+    // segment, which neither pass 1 nor the chaining uses, and pass 2's segment 0 reads it there.
+    float* hin_copy = a.pass && a.h_in ? a.ws_state + (bh * a.nseg + a.nseg - 1) * (int64_t)(N * P) : nullptr;
     if (own_carry) {
-        hin = a.h_in ? a.h_in + bh * (int64_t)(N * P) : nullptr;
+        hin = a.pass == 2 ? hin_copy : (a.h_in ? a.h_in + bh * (int64_t)(N * P) : nullptr);
         Bprev = a.Bbar_prev ? (const T*)a.Bbar_prev + bh * (int64_t)(R * N) : nullptr;
         xprev = a.x_prev ? (const T*)a.x_prev + bh * (int64_t)(R * P) : nullptr;
     } else if (a.pass == 2) {
@@ -286,9 +291,11 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // chunk), read first: without pipelining prev == out.  Chunk 0 starts from phi_in (radians).
     const int kcol = wave * KWL + (lane & (KWL - 1)), run = lane / KWL;
     // angle carried in (radians): the call's, or the segment's start angle from the angle pass
+    // (a split sequence takes every segment's start angle from the angle pass, segment 0's too:
+    // phi_out may be the phi_in buffer, and the last segment writes it)
     const float* phin = nullptr;
     if (FUSED) {
-        if (own_carry) {
+        if (a.pass == 0) {
             phin = a.phi_in ? a.phi_in + bh * K : nullptr;
         } else {
             const int64_t nsegA = (a.L + a.angle_seglen - 1) / a.angle_seglen;
@@ -448,6 +455,12 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
         for (int m = 0; m < 4; ++m)
             st[nb][m] = hin ? hin[(16 * nb + 4 * g + m) * P + pcol] : 0.f;
+    if (a.pass == 1 && own_carry && hin_copy) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) hin_copy[(16 * nb + 4 * g + m) * P + pcol] = st[nb][m];
+    }
     if (Bprev && xprev && L > 0) {
         const float c0 = (1.0f - load_f32(lamg)) * load_f32(dtg);
         for (int r = 0; r < R; ++r) {

@@ -109,6 +109,26 @@ def test_prefill_misaligned():
     assert _prefill(_dims(), p) == m3scan.M3_E_ALIGN
 
 
+def test_fp32_pointers_need_four_byte_alignment():
+    """A and w_out are fp32 in every call: a 2-byte-aligned pointer is refused even when the io
+    type is bf16 (2-byte elements)."""
+    p = _prefill_args()
+    p[4] = P(ALIGNED + 4 * (1 << 24) + 2)            # A
+    assert _prefill(_dims(), p) == m3scan.M3_E_ALIGN and "A" in m3scan.last_error()
+    p = _prefill_args()
+    p[6] = P(ALIGNED + 6 * (1 << 24) + 2)            # w_out
+    assert _prefill(_dims(), p) == m3scan.M3_E_ALIGN and "w_out" in m3scan.last_error()
+    lib = m3scan.load()
+    q = _ptrs(11)                                     # h, Bbar_prev, x_prev, x, Bbar, Cbar, dt, A, lam, w_out, y
+    call = lambda qq: lib.m3_decode_step(ctypes.byref(_dims(seqlen=1)), *qq, None)
+    r = list(q)
+    r[7] = P(q[7].value + 2)
+    assert call(r) == m3scan.M3_E_ALIGN and "A" in m3scan.last_error()
+    r = list(q)
+    r[9] = P(q[9].value + 2)
+    assert call(r) == m3scan.M3_E_ALIGN and "w_out" in m3scan.last_error()
+
+
 def test_prefill_output_overlapping_input():
     p = _prefill_args()
     p[10] = p[0]    # y on top of x
