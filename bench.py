@@ -4,15 +4,23 @@
 One step = one pass of the layer core (BCNorm + bias + rotation, then the chunked scan) over one
 batch of the SISO workload (b=8, L=2048, H=64, P=64, N=128, R=1, bf16 io, fp32 state) through
 m3_layer_prefill, which does both in one kernel (chunk 32).  `value` is prefill tokens/s (b * L
-tokens per step).  The same line times the two-call path (m3_bcnorm_rope then m3_prefill, chunk
-64) for comparison, the MIMO R=4 workload through both paths, decode throughput on the B=128
-decode workloads (R=1 and R=4: m3_layer_decode_step per token, and the two-call path
-m3_bcnorm_rope with L=1 then m3_decode_step), the backward pass (m3_layer_backward: gradients of
-every input) on the SISO and MIMO workloads, the
-roofline of the dominant kernel measured live with HIP events on the launch stream, and the fp64
-oracle's throughput on a bounded sample of the same prefill workload on the host cores.
+tokens per step).  The same line carries:
+  * the two-call path (m3_bcnorm_rope then m3_prefill, chunk 64) and the MIMO R=4 workload
+    through both paths;
+  * the comparison grid of the kernel-time table (Mamba-2 mode / SISO / MIMO R=4, fp32 / bf16,
+    d_state 64 / 128) through the fused call;
+  * decode steps/s on the B=128 workloads (state 268 MB) and on B=512 (state 1.07 GB, four times
+    the 256 MB Infinity Cache, so every step streams its state from DRAM), R=1 and R=4, through
+    m3_layer_decode_step and through the two calls (m3_bcnorm_rope L=1 + m3_decode_step);
+  * head groups, packed variable-length prefill, the long-context split, small-batch decode from
+    HIP graphs, and the backward pass;
+  * the roofline of the step's kernel measured live with HIP events on the launch stream, a plain
+    1 GiB copy timed in the same run, and the fp64 oracle's throughput on bounded samples of the
+    workloads on the host cores.
+Every timed loop runs its warm-up steps and then at least WARM_S seconds of the same work before
+the timed steps (the GPU's clocks ramp over the first tens of milliseconds of work).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 100] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 20] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -32,6 +40,7 @@ from state_space_sequence_m3_amd import inputs, m3scan  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 MFMA, TFLOP/s
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X fp32 (matrix and vector), TFLOP/s
 
 
 KERNEL_SOURCES = {
@@ -116,6 +125,23 @@ def layer_decode_bytes_per_head(w) -> int:
     return 2 * N * P * 4 + 2 * (N // 2) * 4 + es * (4 * R * N + 2 * R * P + 2 + N // 2 + y)
 
 
+# The GPU reaches its steady clocks only after some tens of milliseconds of sustained work: every
+# timed loop below first runs its `warmup` steps, then keeps running the same step until at least
+# WARM_S seconds of work have passed since the warm-up began (untimed), then times its steps.
+WARM_S = 0.25
+
+
+def warm_up(step, warmup):
+    t_start = time.perf_counter()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    while time.perf_counter() - t_start < WARM_S:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+
+
 def time_prefill(w, steps, warmup, dev, inp=None, scan_only=False):
     """The two-call path: m3_bcnorm_rope then m3_prefill (chunk w.chunk).  With scan_only the
     rotation call is left out and m3_prefill reads the raw B and C (Mamba-2 mode)."""
@@ -150,9 +176,7 @@ def time_prefill(w, steps, warmup, dev, inp=None, scan_only=False):
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, warmup)
     # whole-step timing: K steps between two events
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -191,9 +215,7 @@ def time_layer(w, inp, chunk, steps, warmup, dev):
                                 inp["bias_C"], inp["w_out"] if w.mix else None, y=y, h_out=h,
                                 phi_out=phi, chunk=chunk, bcnorm=w.bcnorm, workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, warmup)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
@@ -204,11 +226,16 @@ def time_layer(w, inp, chunk, steps, warmup, dev):
     return t0.elapsed_time(t1) / steps
 
 
+# Decode tokens come from a ring of this many distinct seeded tokens (step s uses token s mod
+# TOKEN_RING): the state, read and written every step, is what the step moves; the tokens only
+# need to be distinct and realistic, not 256 + warm-up different ones.
+TOKEN_RING = 32
+
+
 def time_layer_decode(w, steps, warmup, dev):
     """`steps` consecutive decode tokens through m3_layer_decode_step (rotation + decode in one
     launch), HIP-event timed on the launch stream."""
-    total = steps + warmup
-    dinp = inputs.make_decode_inputs(w, seed=0, steps=total, device=dev)
+    dinp = inputs.make_decode_inputs(w, seed=0, steps=TOKEN_RING, device=dev)
     toks, st = dinp["tokens"], dinp["state"]
     b, H, R, N, P = w.batch, w.nheads, w.rank, w.dstate, w.headdim
     h, phi = st["h"], st["phi"]
@@ -216,24 +243,25 @@ def time_layer_decode(w, steps, warmup, dev):
     y = torch.empty((b, H, P) if w.mix else (b, H, R, P), dtype=w.torch_io, device=dev)
     stream = torch.cuda.current_stream()
     xprev = st["x_prev"]
+    count = 0
 
-    def tok(s):
-        nonlocal xprev
-        Bprev, Bcur = bufs[s % 2], bufs[(s + 1) % 2]
+    def tok():
+        nonlocal xprev, count
+        s = count % TOKEN_RING
+        Bprev, Bcur = bufs[count % 2], bufs[(count + 1) % 2]
         m3scan.m3_layer_decode_step(h, phi, Bprev, xprev, toks["x"][s], toks["B"][s], toks["C"][s],
                                     toks["dt"][s], toks["theta"][s], dinp["A"], toks["lam"][s], None,
                                     None, dinp["bias_B"], dinp["bias_C"],
                                     dinp["w_out"] if w.mix else None, y=y, Bbar_out=Bcur)
         xprev = toks["x"][s]
+        count += 1
 
-    for s in range(warmup):
-        tok(s)
-    torch.cuda.synchronize()
+    warm_up(tok, warmup)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for k in range(steps):
-        tok(warmup + k)
+    for _ in range(steps):
+        tok()
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
@@ -261,9 +289,7 @@ def time_varlen(w, steps, warmup, dev):
                                        inp["bias_C"], None, y=y.view(T, w.nheads, w.rank, w.headdim),
                                        chunk=LAYER_CHUNK_ROWS // w.rank)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, warmup)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -332,8 +358,7 @@ def time_small_batch_decode(w, steps, dev, graph_steps=16):
 
 def time_decode(w, steps, warmup, dev):
     """`steps` consecutive decode tokens (bcnorm_rope L=1 + decode_step each), HIP-event timed."""
-    total = steps + warmup
-    dinp = inputs.make_decode_inputs(w, seed=0, steps=total, device=dev)
+    dinp = inputs.make_decode_inputs(w, seed=0, steps=TOKEN_RING, device=dev)
     toks, st = dinp["tokens"], dinp["state"]
     b, H, R, N, P = w.batch, w.nheads, w.rank, w.dstate, w.headdim
     h, phi = st["h"], st["phi"]
@@ -343,9 +368,10 @@ def time_decode(w, steps, warmup, dev):
     stream = torch.cuda.current_stream()
     xprev = st["x_prev"]
 
-    def tok(s, ev=None):
+    def tok(c, ev=None):
         nonlocal xprev
-        Bprev, Bcur = bufs[s % 2], bufs[(s + 1) % 2]
+        s = c % TOKEN_RING
+        Bprev, Bcur = bufs[c % 2], bufs[(c + 1) % 2]
         if ev is not None:
             ev[0].record(stream)
         m3scan.m3_bcnorm_rope(toks["B"][s].unsqueeze(1), toks["C"][s].unsqueeze(1),
@@ -360,15 +386,20 @@ def time_decode(w, steps, warmup, dev):
             ev[2].record(stream)
         xprev = toks["x"][s]
 
-    for s in range(warmup):
-        tok(s)
-    torch.cuda.synchronize()
+    count = 0
+
+    def next_tok():
+        nonlocal count
+        tok(count)
+        count += 1
+
+    warm_up(next_tok, warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for k in range(steps):
-        tok(warmup + k, evs[k])
+        tok(count + k, evs[k])
     t1.record(stream)
     torch.cuda.synchronize()
     ms_tok = t0.elapsed_time(t1) / steps
@@ -426,9 +457,7 @@ def time_backward(w, steps, warmup, dev):
 
     out = {}
     for name, fn in (("m3_layer_backward", step), ("m3_layer_chunk_states", states)):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, warmup)
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
@@ -470,9 +499,7 @@ def copy_probe(nbytes: int, steps: int, warmup: int, dev):
     the reference against which the FETCH_SIZE / WRITE_SIZE counters are scaled."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).normal_()
     dst = torch.empty_like(src)
-    for _ in range(warmup):
-        dst.copy_(src)
-    torch.cuda.synchronize()
+    warm_up(lambda: dst.copy_(src), warmup)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -486,13 +513,92 @@ def copy_probe(nbytes: int, steps: int, warmup: int, dev):
             "ms": ms, "GB/s": moved / ms / 1e6, "hbm_frac": moved / ms / 1e6 / HBM_PEAK_GBS}
 
 
+def grid_entry(wv, inpv, steps, warmup, dev):
+    """One cell of the comparison grid: m3_layer_prefill (and, in Mamba-2 mode, m3_prefill on
+    the raw B and C, which are already the scan's inputs there)."""
+    thv = wv.batch * wv.seqlen * wv.nheads
+    rows = LAYER_CHUNK_ROWS
+    ms_l = time_layer(wv, inpv, rows // wv.rank, steps, warmup, dev)
+    wl = wv.with_(chunk=rows // wv.rank)
+    lb = thv * layer_bytes_per_token_head(wv) + wv.batch * wv.nheads * wv.dstate * (wv.headdim + 1) * 4
+    lf = thv * prefill_flops_per_token_head(wl)
+    peak = BF16_MFMA_PEAK_TFLOPS if wv.io == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    entry = {"workload": wv.name, "m3_layer_prefill": {
+        "ms": ms_l, "tokens/s": wv.batch * wv.seqlen / (ms_l / 1e3), "chunk": wl.chunk,
+        "GB/s": lb / ms_l / 1e6, "hbm_frac": lb / ms_l / 1e6 / HBM_PEAK_GBS,
+        "TFLOP/s": lf / ms_l / 1e9, "mfma_frac": lf / ms_l / 1e9 / peak}}
+    if wv.mamba2:
+        _, _, _, ms_p = time_prefill(wv, steps, warmup, dev, inpv, scan_only=True)
+        pb = thv * prefill_bytes_per_token_head(wv) + wv.batch * wv.nheads * wv.dstate * wv.headdim * 4
+        entry["m3_prefill"] = {"ms": ms_p, "tokens/s": wv.batch * wv.seqlen / (ms_p / 1e3), "chunk": wv.chunk,
+                               "GB/s": pb / ms_p / 1e6, "hbm_frac": pb / ms_p / 1e6 / HBM_PEAK_GBS}
+    return entry
+
+
+def time_grid(steps, warmup, dev):
+    """The kernel-time comparison grid of the aipaper.cc summary (section 6.2, Table 3): Mamba-2
+    mode, SISO and MIMO R = 4, each in fp32 and bf16 io at d_state 64 and 128, on the b8 L2048
+    H64 P64 layer, all through the same fused kernel."""
+    out = {}
+    for (mode, io, n), name in inputs.TABLE3_GRID.items():
+        wv = inputs.WORKLOADS[name]
+        inpv = inputs.make_prefill_inputs(wv, seed=0, device=dev)
+        out["%s/%s/N%d" % (mode, io, n)] = grid_entry(wv, inpv, steps, warmup, dev)
+        del inpv
+        torch.cuda.empty_cache()
+    return out
+
+
+def more_cpu_baselines(w, inp):
+    """The unchanged oracle on bounded samples of the other workloads (on the host's OpenMP
+    threads), and on one thread for the SISO workload: MIMO prefill (one head of every batch
+    row), one decode step of the whole b128 batch (R = 1 and R = 4), and the long-context prefill
+    on two heads (the full 16384 steps)."""
+    import oracle
+    out = {}
+
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    threads = oracle.num_threads()
+    # SISO on one thread: 4 (batch, head) pairs, full length
+    host = {k: (None if v is None else (v[:1, :, :4] if k in ("x", "B", "C", "dt", "lam", "theta") else v[:4]).cpu())
+            for k, v in inp.items()}
+    oracle.set_num_threads(1)
+    try:
+        secs = timed(lambda: oracle.layer(host, bcnorm=w.bcnorm, mix=w.mix))
+    finally:
+        oracle.set_num_threads(threads)
+    out["siso_b8_l2048_one_thread"] = {
+        "value": 4 * w.seqlen / w.nheads / secs, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": "4 (batch, head) pairs x %d steps, %.2f s" % (w.seqlen, secs)}
+    for name, heads in (("mimo4_b8_l2048", 1), ("long_mimo4_b1_l16384", 2)):
+        wv = inputs.WORKLOADS[name]
+        g = inputs.make_prefill_inputs(wv.with_(nheads=heads), seed=0)
+        secs = timed(lambda: oracle.layer(g, bcnorm=wv.bcnorm, mix=wv.mix))
+        out[name] = {"value": wv.batch * heads * wv.seqlen / wv.nheads / secs, "unit": "tokens/s",
+                     "cores": threads, "kind": "oracle",
+                     "sample": "%d (batch, head) pairs x %d steps, %.2f s; tokens = pairs * L / H"
+                               % (wv.batch * heads, wv.seqlen, secs)}
+    for name in ("decode_b128_r1", "decode_b128_r4"):
+        wd = inputs.WORKLOADS[name]
+        dinp = inputs.make_decode_inputs(wd, seed=0, steps=1)
+        tok = {k: v[0] for k, v in dinp["tokens"].items()}
+        consts = {"A": dinp["A"], "bias_B": dinp["bias_B"], "bias_C": dinp["bias_C"], "w_out": dinp["w_out"]}
+        secs = timed(lambda: oracle.decode_step(dinp["state"], tok, consts, mix=wd.mix))
+        out[name] = {"value": 1.0 / secs, "unit": "steps/s", "cores": threads, "kind": "oracle",
+                     "sample": "one decode step of all %d (batch, head) pairs, %.3f s" % (wd.batch * wd.nheads, secs)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # the GPU reaches its steady clocks after ~20 ms of sustained work: 100 steps of the SISO step
-    # (~25 ms) before the timed ones; with 3 the first timed steps ran ~10% slow
-    ap.add_argument("--warmup", type=int, default=100)
+    # untimed steps before the timed ones (followed by WARM_S seconds of the same work)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -563,24 +669,10 @@ def main():
     # same kernels: the fused call (chunk 32) and the plain scan (chunk 64; in Mamba-2 mode the raw
     # B and C are already Bbar and Cbar, so the scan alone is the whole layer core)
     variants = None
+    table3 = None
     if not args.no_mimo:
+        table3 = time_grid(args.steps, args.warmup, dev)
         variants = {}
-        for vname in ("mamba2_siso_b8_l2048", "siso_n64_b8_l2048"):
-            wv = inputs.WORKLOADS[vname]
-            inpv = inputs.make_prefill_inputs(wv, seed=0, device=dev)
-            thv = wv.batch * wv.seqlen * wv.nheads
-            ms_l = time_layer(wv, inpv, LAYER_CHUNK_ROWS // wv.rank, args.steps, args.warmup, dev)
-            lb = thv * layer_bytes_per_token_head(wv) + wv.batch * wv.nheads * wv.dstate * (wv.headdim + 1) * 4
-            entry = {"m3_layer_prefill": {"ms": ms_l, "tokens/s": wv.batch * wv.seqlen / (ms_l / 1e3),
-                                          "GB/s": lb / ms_l / 1e6, "hbm_frac": lb / ms_l / 1e6 / HBM_PEAK_GBS}}
-            if wv.mamba2:
-                _, _, _, ms_p = time_prefill(wv, args.steps, args.warmup, dev, inpv, scan_only=True)
-                pb = thv * prefill_bytes_per_token_head(wv) + wv.batch * wv.nheads * wv.dstate * wv.headdim * 4
-                entry["m3_prefill"] = {"ms": ms_p, "tokens/s": wv.batch * wv.seqlen / (ms_p / 1e3),
-                                       "GB/s": pb / ms_p / 1e6, "hbm_frac": pb / ms_p / 1e6 / HBM_PEAK_GBS}
-            variants[vname] = entry
-            del inpv
-            torch.cuda.empty_cache()
         # raw B and C shared by groups of heads (G = 1: all 64 heads; G = 8: groups of 8)
         for vname in ("siso_g1_b8_l2048", "mimo4_g1_b8_l2048", "mimo4_g8_b8_l2048"):
             wv = inputs.WORKLOADS[vname]
@@ -629,7 +721,7 @@ def main():
     decode = None
     if not args.no_decode:
         decode = {}
-        for name in ("decode_b128_r1", "decode_b128_r4"):
+        for name in ("decode_b128_r1", "decode_b128_r4", "decode_b512_r1", "decode_b512_r4"):
             wd = inputs.WORKLOADS[name]
             ms_fused = time_layer_decode(wd, args.decode_steps, args.warmup, dev)
             ms_tok, ms_dbc, ms_dec = time_decode(wd, args.decode_steps, args.warmup, dev)
@@ -639,6 +731,8 @@ def main():
                             "layer_decode_step_GB/s": fbytes / ms_fused / 1e6,
                             "layer_decode_step_hbm_frac": fbytes / ms_fused / 1e6 / HBM_PEAK_GBS,
                             "layer_decode_step_bytes": fbytes,
+                            "layer_decode_step_frac_of_copy": fbytes / ms_fused / 1e6 / copy["GB/s"],
+                            "state_bytes": wd.batch * wd.nheads * wd.dstate * wd.headdim * 4,
                             "two_calls": {"steps_per_s": 1e3 / ms_tok, "ms_per_step": ms_tok,
                                           "decode_step_ms": ms_dec, "bcnorm_rope_ms": ms_dbc,
                                           "decode_step_GB/s": dbytes / ms_dec / 1e6,
@@ -672,12 +766,15 @@ def main():
                                "chunk_rows": rows}
 
     cpu = None
+    cpu_more = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, inp, args.cpu_heads)
+        cpu_more = more_cpu_baselines(w, inp)
 
     line = {
         "metric": "prefill tokens/s and B=128 decode steps/s per Mamba-3 layer; % of roofline",
         "value": tokens / (ms_step / 1e3),
+        "warm_s": WARM_S,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -696,7 +793,9 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "cpu_baselines": cpu_more,
         "mimo4_b8_l2048": mimo,
+        "table3_grid": table3,
         "variants": variants,
         "decode": decode,
         "backward": backward,

@@ -68,6 +68,8 @@ def _bind(path: str):
     lib.m3o_bcnorm_rope_backward.argtypes = [_I64] * 5 + [ctypes.c_int, ctypes.c_double] + [_D] * 21
     lib.m3o_num_threads.restype = ctypes.c_int
     lib.m3o_num_threads.argtypes = []
+    lib.m3o_set_num_threads.restype = None
+    lib.m3o_set_num_threads.argtypes = [ctypes.c_int]
     return lib
 
 
@@ -96,6 +98,11 @@ def _ptr(a):
 def num_threads() -> int:
     """OpenMP threads the oracle uses (OMP_NUM_THREADS, else the cores it may run on)."""
     return int(_load().m3o_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for the oracle's later calls (the arithmetic does not depend on it)."""
+    _load().m3o_set_num_threads(int(n))
 
 
 def heads_from_groups(v, H):

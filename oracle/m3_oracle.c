@@ -233,6 +233,17 @@ int m3o_num_threads(void)
 #endif
 }
 
+/* Threads of later parallel loops (n >= 1); used to time the oracle on one host core. */
+void m3o_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Gradients of m3o_scan (the adjoint of each step of the recurrence above, taken in reverse
  * order; nothing here is chunked or reordered).  Given dy (same layout as y) and dh_out (NULL =

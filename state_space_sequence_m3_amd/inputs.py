@@ -92,10 +92,37 @@ WORKLOADS = {
     "mimo4_g8_b8_l2048": Workload("mimo4_g8_b8_l2048", 8, 2048, 64, 64, 128, 4, 16, "bf16", True, True,
                                   True, groups=8,
                                   note="MIMO R4 b8 L2048 with raw B and C shared by groups of 8 heads"),
+    # decode with a state of 1.07 GB, four times the 256 MB Infinity Cache: every step streams the
+    # state from DRAM (the b128 state, 268 MB, can be partly served by that cache)
+    "decode_b512_r1": Workload("decode_b512_r1", 512, 1, 64, 64, 128, 1, 1, "bf16", True, True,
+                               False, decode_steps=256, note="b512 H64 P64 N128 R1, 256 steps"),
+    "decode_b512_r4": Workload("decode_b512_r4", 512, 1, 64, 64, 128, 4, 1, "bf16", True, True,
+                               True, decode_steps=256, note="b512 H64 P64 N128 R4, 256 steps"),
     "long_mimo4_b1_l16384": Workload("long_mimo4_b1_l16384", 1, 16384, 64, 64, 128, 4, 16, "bf16",
                                      True, True, True, theta_std=math.pi, decode_steps=512,
                                      note="b1 L16384 H64 R4 Q16, theta std pi, then 512 decode steps"),
 }
+
+# The comparison grid of the kernel-time table on the aipaper.cc summary (section 6.2, Table 3):
+# Mamba-2 mode, SISO and MIMO R = 4, each with fp32 and bf16 io and d_state 64 and 128, on the b8
+# L2048 H64 P64 layer shape.  Keyed by (mode, io, N).
+def _grid():
+    base = {"mamba2": WORKLOADS["mamba2_siso_b8_l2048"], "siso": WORKLOADS["siso_b8_l2048"],
+            "mimo4": WORKLOADS["mimo4_b8_l2048"]}
+    grid = {}
+    for mode, w0 in base.items():
+        for io in ("f32", "bf16"):
+            for n in (64, 128):
+                suffix = ("" if n == 128 else "_n64") + ("" if io == "bf16" else "_f32")
+                name = w0.name.replace("_b8", suffix + "_b8") if suffix else w0.name
+                if name not in WORKLOADS:
+                    WORKLOADS[name] = w0.with_(name=name, io=io, dstate=n,
+                                               note="%s, %s io, d_state %d (comparison grid)" % (mode, io, n))
+                grid[(mode, io, n)] = name
+    return grid
+
+
+TABLE3_GRID = _grid()
 
 
 def _gen(seed: int, device) -> torch.Generator:

@@ -121,3 +121,57 @@ def test_split_workspace_too_small_is_rejected():
     with pytest.raises(m3scan.M3Error) as e:
         _layer(d, w, 32, False, workspace=small)
     assert e.value.status == m3scan.M3_E_WORKSPACE
+
+
+_HEAD_AXIS = {"x": 2, "dt": 2, "lam": 2, "theta": 2, "A": 0, "h_in": 1, "Bbar_prev": 1,
+              "x_prev": 1, "phi_in": 1, "bias_B": 0, "bias_C": 0, "normw_B": 0, "normw_C": 0,
+              "w_out": 0}
+
+
+def _oracle_heads(inp, heads, G, H, mix):
+    """oracle.layer on the listed heads only: each head with its own inputs and its group's raw B
+    and C rows (slot h // (H / G))."""
+    sub = {k: v.index_select(_HEAD_AXIS[k], torch.tensor(heads)) for k, v in inp.items()
+           if k in _HEAD_AXIS and v is not None}
+    slots = torch.tensor([h // (H // G) for h in heads])
+    sub["B"] = inp["B"].index_select(2, slots)
+    sub["C"] = inp["C"].index_select(2, slots)
+    return oracle.layer(sub, bcnorm=True, mix=mix)
+
+
+def test_split_in_place_carry_with_reordered_segments():
+    """The in-place carry (h_out = h_in, phi_out = phi_in) on a split whose segments run out of
+    order: 100 (b, h) pairs in 6 segments (pass 2: 600 workgroups, more than the 512 the GPU holds
+    at once; 6 does not divide 600 / 8 = 75), heads in 25 groups of 4, so the grouped launch
+    reorders its workgroups XCD by XCD and some pairs' segment 0 starts after their last segment
+    has written h_out.  Sampled heads (among them 12, whose segment 0 runs in block 576 and last
+    segment in block 17) against the oracle; then m3_prefill with its state in place, on the same
+    shape per head."""
+    H, G, L = 100, 25, 6144
+    w = inputs.Workload("split_inplace", 1, L, H, 64, 128, 1, 32, "bf16", True, True, False, 1.0, groups=G)
+    dims = m3scan.make_dims(1, L, H, 64, 128, 1, 32, m3scan.M3_BF16, groups=G)
+    need = m3scan.layer_prefill_workspace_bytes(dims)
+    assert need > 0, "the split is not used"
+    inp = inputs.make_prefill_inputs(w, seed=85, normw=True, carry=True)
+    d = to_dev(inp, DEV)
+    h = d["h_in"].clone()
+    phi = d["phi_in"].clone()
+    y, _, _ = _layer(dict(d, h_in=h, phi_in=phi), w, 32, False, h_out=h, phi_out=phi)
+    torch.cuda.synchronize()
+    heads = [0, 12, 13, 50, 87, 99]
+    ref = _oracle_heads(inp, heads, G, H, False)
+    hs = torch.tensor(heads, device=DEV)
+    assert rel_err(y.index_select(2, hs), ref["y"]) <= TOL["bf16"]
+    assert rel_err(h.index_select(1, hs), ref["h_out"]) <= TOL["bf16"]
+    assert angle_err(phi.index_select(1, hs), ref["phi_out"]) <= 1e-3
+    # m3_prefill (per-head rotated B and C), state in place, 64-step chunks: 600 workgroups again
+    Bb, Cb, _ = m3scan.m3_bcnorm_rope(d["B"], d["C"], d["dt"], d["theta"], d["normw_B"], d["normw_C"],
+                                      d["bias_B"], d["bias_C"], d["phi_in"])
+    pd = m3scan.make_dims(1, L, H, 64, 128, 1, 64, m3scan.M3_BF16)
+    assert m3scan.prefill_workspace_bytes(pd) > 0, "the split is not used"
+    h2 = d["h_in"].clone()
+    y2, _ = m3scan.m3_prefill(d["x"], Bb, Cb, d["dt"], d["A"], d["lam"], None, h2, d["Bbar_prev"],
+                              d["x_prev"], h_out=h2, chunk=64)
+    torch.cuda.synchronize()
+    assert rel_err(y2.index_select(2, hs), ref["y"]) <= TOL["bf16"]
+    assert rel_err(h2.index_select(1, hs), ref["h_out"]) <= TOL["bf16"]

@@ -67,6 +67,15 @@ def _fused_layer(d, w):
     ("mimo4_b8_l2048", [(0, 5), (6, 40)]),
     ("mamba2_siso_b8_l2048", [(1, 2), (7, 60)]),
     ("siso_n64_b8_l2048", [(2, 9), (5, 33)]),
+    # the rest of the comparison grid (Mamba-2 mode / SISO / MIMO R = 4 x fp32 / bf16 x N 64 / 128)
+    ("mimo4_n64_b8_l2048", [(1, 7)]),
+    ("mamba2_siso_n64_b8_l2048", [(6, 21)]),
+    ("siso_f32_b8_l2048", [(2, 11)]),
+    ("siso_n64_f32_b8_l2048", [(7, 0)]),
+    ("mimo4_f32_b8_l2048", [(4, 50)]),
+    ("mimo4_n64_f32_b8_l2048", [(3, 63)]),
+    ("mamba2_siso_f32_b8_l2048", [(0, 30)]),
+    ("mamba2_siso_n64_f32_b8_l2048", [(5, 44)]),
 ])
 @pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 def test_prefill_workload_sampled(name, pairs, fused):
@@ -117,6 +126,9 @@ def _decode_steps(w, dinp, steps, mix, h, phi, Bprev, xprev, consts_dev, toks, f
 @pytest.mark.parametrize("name,pairs", [
     ("decode_b128_r1", [(0, 0), (77, 31), (127, 63)]),
     ("decode_b128_r4", [(5, 2), (120, 60)]),
+    # a state four times the Infinity Cache (the DRAM-bound decode lines of the benchmark)
+    ("decode_b512_r1", [(0, 0), (511, 63)]),
+    ("decode_b512_r4", [(300, 7)]),
 ])
 @pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 def test_decode_workload_sampled(name, pairs, fused):
