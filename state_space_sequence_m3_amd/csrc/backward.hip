@@ -56,12 +56,21 @@ namespace m3 {
 
 namespace {
 
-template <typename T, int N_, int P_, int NIB_, int R_>
+// WPB waves share each 16-row block of a chunk (the backward pass runs WPB = 2: two waves per
+// SIMD, each with half of the row block's column blocks and half of the state tiles).
+template <typename T, int N_, int P_, int NIB_, int R_, int WPB_ = 1>
 struct Shape {
-    static constexpr int N = N_, P = P_, NIB = NIB_, R = R_;
-    static constexpr int NW = NIB, NT = 64 * NW, QR = 16 * NIB, Q = QR / R;
+    static constexpr int N = N_, P = P_, NIB = NIB_, R = R_, WPB = WPB_;
+    static constexpr int NW = NIB * WPB, NT = 64 * NW, QR = 16 * NIB, Q = QR / R;
     static constexpr int RL2 = R == 1 ? 0 : (R == 2 ? 1 : 2);
     static constexpr int NB = N / 16, PB = P / 16, PPW = PB / NW;
+    // a wave's share of a row block's column work: PBH of the P blocks, NBH of the N blocks
+    static constexpr int PBH = PB / WPB, NBH = NB / WPB;
+    // a wave's tiles of the N x P state (cotangent): SCW column blocks of SRW row blocks each,
+    // column group wave % NCG, row group wave / NCG
+    static constexpr int SCW = PB >= NW ? PB / NW : 1, NCG = PB / SCW, SRW = NB / (NW / NCG);
+    static_assert(PB % WPB == 0 && NB % WPB == 0, "column blocks per wave");
+    static_assert(NCG * SCW == PB && (NW / NCG) * SRW == NB && NW % NCG == 0, "state tiles per wave");
     static constexpr int PADT = Mma<T>::PADT;
     static constexpr int LDB = N + PADT, LDX = P + PADT, LDS = N + PADT, LDM = QR + PADT;
     static constexpr int VE = 16 / (int)sizeof(T), VPN = N / VE, VPP = P / VE;
@@ -81,7 +90,6 @@ struct Shape {
     // after the products the region holds the fp32 gradient rows and the per-row angle gradients
     static constexpr int OFF_FB = 0, OFF_FC = QR * LDF * 4, OFF_FPHI = 2 * QR * LDF * 4,
                          ALIAS = OFF_FPHI + QR * LDD * 4, FINAL = N * (P + 4) * 4;
-    static_assert(PB % NW == 0, "state column blocks per wave");
     static_assert(NT % VPN == 0 && NT % VPP == 0 && RKC % R == 0 && RKX % R == 0, "staging layout");
     static_assert(NVT >= 1 && NVT * TPV <= NT && TPV <= 64 && (TPV & (TPV - 1)) == 0, "angle scan layout");
     static_assert(ALIAS <= TILES && FINAL <= TILES, "aliased LDS");
@@ -119,6 +127,7 @@ __global__ __launch_bounds__(NIB * 64, 1) void chunk_states_kernel(BackwardArgs 
     using MM = Mma<T>;
     using F = typename MM::frag;
     constexpr int NW = S::NW, NT = S::NT, QR = S::QR, Q = S::Q, RL2 = S::RL2, NB = S::NB, PPW = S::PPW;
+    static_assert(S::WPB == 1 && S::PB % NW == 0, "state column blocks per wave");
     constexpr int LDB = S::LDB, LDX = S::LDX, VE = S::VE, VPN = S::VPN, VPP = S::VPP;
     constexpr int RKC = S::RKC, RKX = S::RKX, MAXC = S::MAXC, MAXX = S::MAXX;
     constexpr int K = S::K, VT = S::VT, NVT = S::NVT, TPV = S::TPV, SPT = S::SPT, LDPHI = S::LDPHI;
@@ -347,13 +356,13 @@ __global__ __launch_bounds__(NIB * 64, 1) void chunk_states_kernel(BackwardArgs 
     }
 }
 
-template <typename T, int N, int P, int NIB, int R>
-__global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
-    using S = Shape<T, N, P, NIB, R>;
+template <typename T, int N, int P, int NIB, int R, int WPB>
+__global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArgs a) {
+    using S = Shape<T, N, P, NIB, R, WPB>;
     using MM = Mma<T>;
     using F = typename MM::frag;
-    constexpr int NW = S::NW, NT = S::NT, QR = S::QR, Q = S::Q, RL2 = S::RL2, NB = S::NB, PB = S::PB,
-                  PPW = S::PPW;
+    constexpr int NW = S::NW, NT = S::NT, QR = S::QR, Q = S::Q, RL2 = S::RL2, NB = S::NB, PB = S::PB;
+    constexpr int PBH = S::PBH, NBH = S::NBH, SCW = S::SCW, SRW = S::SRW, NCG = S::NCG;
     constexpr int LDB = S::LDB, LDX = S::LDX, LDS = S::LDS, LDM = S::LDM, VE = S::VE, VPN = S::VPN,
                   VPP = S::VPP;
     constexpr int RKC = S::RKC, RKX = S::RKX, MAXC = S::MAXC, MAXX = S::MAXX, MAXS = S::MAXS;
@@ -378,7 +387,7 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
     __shared__ __align__(16) float rL2[64], rEl[64], rGam[64], rMu[64], rW[64];
     __shared__ float rEnd[2];   // l_end (log2 units), exp(l_end)
     // per-row partial gradients (per wave where several waves add to a row)
-    __shared__ __align__(16) float pMu[NW * 64], pLi[NW * 64], pGam[NW * 64], rDw[64], rDlo[64];
+    __shared__ __align__(16) float pMu[NW * 64], pLi[NW * 64], pGam[NW * 64], rDw[WPB * 64], rDlo[WPB * 64];
     __shared__ float pSS[NW], red[NW];
     __shared__ __align__(16) float rotdd[NVT * 64];
     __shared__ __align__(16) float sWt[2 * N], sBias[2 * R * N], sWo[R * P];
@@ -386,6 +395,9 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
+    // row block rbw of the chunk (16 rows), half hf of its column work; state tiles: column group
+    // cg, row group rg
+    const int rbw = wave % NIB, hf = wave / NIB, cg = wave % NCG, rg = wave / NCG;
     // heads that share raw B and C run on one XCD (consecutive items), so its L2 serves the group
     const int64_t bh = a.G > 0 && a.G < a.H ? xcd_item(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
     const int64_t b = bh / a.H;
@@ -450,16 +462,17 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
 #pragma unroll
     for (int e = 0; e < VT; ++e) dcarry[e] = scanner && a.dphi_out ? a.dphi_out[bh * K + tv * VT + e] : 0.f;
 
-    // ---- state cotangent (starts at dh_out): wave w owns columns p in blocks w * PPW ..
-    floatx4 st[PPW][NB];
+    // ---- state cotangent (starts at dh_out): the wave's tiles, column blocks cg SCW + j of row
+    // blocks rg SRW + i
+    floatx4 st[SCW][SRW];
 #pragma unroll
-    for (int j = 0; j < PPW; ++j)
+    for (int j = 0; j < SCW; ++j)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int i = 0; i < SRW; ++i)
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const int p = 16 * (wave * PPW + j) + l16;
-                st[j][nb][m] = a.dh_out ? a.dh_out[(bh * N + 16 * nb + 4 * g + m) * P + p] : 0.f;
+                const int p = 16 * (cg * SCW + j) + l16, n = 16 * (rg * SRW + i) + 4 * g + m;
+                st[j][i][m] = a.dh_out ? a.dh_out[(bh * N + n) * P + p] : 0.f;
             }
 
     // per-thread sums over the sequence: BCNorm weight and bias gradients of the thread's columns
@@ -467,9 +480,9 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
     float accW[2][VE], accBias[2][VE];
 #pragma unroll
     for (int e = 0; e < VE; ++e) accW[0][e] = accW[1][e] = accBias[0][e] = accBias[1][e] = 0.f;
-    floatx4 accMix[PB];
+    floatx4 accMix[PBH];
 #pragma unroll
-    for (int pb = 0; pb < PB; ++pb) accMix[pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int pb = 0; pb < PBH; ++pb) accMix[pb] = floatx4{0.f, 0.f, 0.f, 0.f};
     float dA_acc = 0.f;
     float pend_ddt = 0.f, pend_dlam = 0.f;   // the scalar wave: gradients of the step after the chunk
 
@@ -500,7 +513,7 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
         const int rC = iC0 & (R - 1);
         const int tv = tid / TPV, tj = tid % TPV;
         const bool scanner = tid < NVT * TPV;
-        const int wrow = 16 * wave + l16;   // this lane's chunk row in the wave-owned row block
+        const int wrow = 16 * rbw + l16;   // this lane's chunk row in the wave's row block
         auto offC = [&](int k) {
             const int i = iC0 + k * RKC;
             return (uint32_t)(((i >> RL2) * (int)SBC + (i & (R - 1)) * N + cC0 * VE) * (int)sizeof(T));
@@ -568,13 +581,13 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
             nln = buffer_load_bits(dL, o1, T{});
         }
         // dy of the lane's rows and columns for the mixing-weight gradient
-        uint4 dyv[PB];
+        uint4 dyv[PBH];
         if (mix) {
             const rsrc_t dYr = make_rsrc(dyg + t0 * ystep, tail_bytes(t0, ystep, yrow));
             const int t = wrow >> RL2;
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb) {
-                const uint32_t off = (uint32_t)((t * H * P + 16 * pb + 4 * g) * (int)sizeof(T));
+            for (int pb = 0; pb < PBH; ++pb) {
+                const uint32_t off = (uint32_t)((t * H * P + 16 * (hf * PBH + pb) + 4 * g) * (int)sizeof(T));
                 if constexpr (sizeof(T) == 2) {
                     const uint2 u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(dYr, (int)off, 0, 0));
                     dyv[pb] = make_uint4(u.x, u.y, 0u, 0u);
@@ -624,10 +637,10 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
             if (S::FULLS || p < P) *(uint4*)(sSt + p * LDS + cC0 * VE) = rs[k];
         }
 #pragma unroll
-        for (int j = 0; j < PPW; ++j) {
-            const int p = 16 * (wave * PPW + j) + l16;
+        for (int j = 0; j < SCW; ++j) {
+            const int p = 16 * (cg * SCW + j) + l16;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) MM::st(sDSt + p * LDS + 16 * nb + 4 * g, MM::pack(st[j][nb]));
+            for (int i = 0; i < SRW; ++i) MM::st(sDSt + p * LDS + 16 * (rg * SRW + i) + 4 * g, MM::pack(st[j][i]));
         }
         const float cd = bits_to_f32(nd), cl = bits_to_f32(nl), cdn = bits_to_f32(ndn), cln = bits_to_f32(nln);
         if (wave == NW - 1) {
@@ -738,59 +751,63 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
                 for (int m = 0; m < 4; ++m) pMu[wave * 64 + s0 + m] += emu[m];
             }
         }
-        // dX^T (rows p, columns s in this wave's block): first the state part w_s dS_out^T Bbar^T
-        floatx4 dxa[PB];
+        // dX^T (rows p in this wave's column blocks, columns s in its row block): first the state
+        // part w_s dS_out^T Bbar^T
+        floatx4 dxa[PBH];
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb) {
+        for (int pb = 0; pb < PBH; ++pb) {
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NB; ++kb)
-                acc = MM::mma(MM::ldk(sDSt + (16 * pb + l16) * LDS + 16 * kb + 4 * g),
+                acc = MM::mma(MM::ldk(sDSt + (16 * (hf * PBH + pb) + l16) * LDS + 16 * kb + 4 * g),
                               MM::ldk(sB + wrow * LDB + 16 * kb + 4 * g), acc);
             const float ws = rW[wrow];
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[m] *= ws;
             dxa[pb] = acc;
         }
-        // dBbar^T (rows n, columns s = this wave's rows): Z = dS_out X^T, dw_s = Bbar_s . Z_s
-        floatx4 dba[NB];
+        // dBbar^T (rows n in this wave's half, columns s = the row block): Z = dS_out X^T,
+        // dw_s = Bbar_s . Z_s (this half's share; the halves are added in the scalar step)
+        floatx4 dba[NBH];
         {
             float dw = 0.f;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
+            for (int nb = 0; nb < NBH; ++nb) {
+                const int nbg = hf * NBH + nb;
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < PB; ++kb)
-                    acc = MM::mma(MM::ldt(sDSt + (16 * kb + 4 * g) * LDS + 16 * nb, LDS, l16),
+                    acc = MM::mma(MM::ldt(sDSt + (16 * kb + 4 * g) * LDS + 16 * nbg, LDS, l16),
                                   MM::ldk(sX + wrow * LDX + 16 * kb + 4 * g), acc);
-                const floatx4 bv = MM::unpack(MM::ldk(sB + wrow * LDB + 16 * nb + 4 * g));
+                const floatx4 bv = MM::unpack(MM::ldk(sB + wrow * LDB + 16 * nbg + 4 * g));
 #pragma unroll
                 for (int m = 0; m < 4; ++m) dw = fmaf(bv[m], acc[m], dw);
                 dba[nb] = acc;
             }
             dw += shfl_xor(dw, 16);
             dw += shfl_xor(dw, 32);
-            if (g == 0) rDw[wrow] = dw;
+            if (g == 0) rDw[hf * 64 + wrow] = dw;
             const float ws = rW[wrow];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int nb = 0; nb < NBH; ++nb)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) dba[nb][m] *= ws;
         }
         // dCbar^T (rows n, columns i = this wave's rows): exp(l_i) S_in dY_i, and
         // dl_i += Cbar_i . that
-        floatx4 dca[NB];
+        floatx4 dca[NBH];
         {
             const float el = rEl[wrow];
             float dlo = 0.f;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
+            for (int nb = 0; nb < NBH; ++nb) {
+                const int nbg = hf * NBH + nb;
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < PB; ++kb)
-                    acc = MM::mma(MM::ldt(sSt + (16 * kb + 4 * g) * LDS + 16 * nb, LDS, l16),
+                    acc = MM::mma(MM::ldt(sSt + (16 * kb + 4 * g) * LDS + 16 * nbg, LDS, l16),
                                   MM::ldk(sDY + wrow * LDX + 16 * kb + 4 * g), acc);
-                const floatx4 cv = MM::unpack(MM::ldk(sC + wrow * LDB + 16 * nb + 4 * g));
+                const floatx4 cv = MM::unpack(MM::ldk(sC + wrow * LDB + 16 * nbg + 4 * g));
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     acc[m] *= el;
@@ -800,35 +817,36 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
             }
             dlo += shfl_xor(dlo, 16);
             dlo += shfl_xor(dlo, 32);
-            if (g == 0) rDlo[wrow] = dlo;
+            if (g == 0) rDlo[hf * 64 + wrow] = dlo;
         }
-        // recomputed Y^T (rows p, columns i = this wave's rows), state part, when mixing
-        floatx4 ya[PB];
+        // recomputed Y^T (rows p in this wave's column blocks, columns i = the row block), state
+        // part, when mixing
+        floatx4 ya[PBH];
         if (mix) {
             const float el = rEl[wrow];
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb) {
+            for (int pb = 0; pb < PBH; ++pb) {
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NB; ++kb)
-                    acc = MM::mma(MM::ldk(sSt + (16 * pb + l16) * LDS + 16 * kb + 4 * g),
+                    acc = MM::mma(MM::ldk(sSt + (16 * (hf * PBH + pb) + l16) * LDS + 16 * kb + 4 * g),
                                   MM::ldk(sC + wrow * LDB + 16 * kb + 4 * g), acc);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) acc[m] *= el;
                 ya[pb] = acc;
             }
         }
-        // <dS_out, S_in> over this wave's state columns
+        // <dS_out, S_in> over this wave's state tiles
         {
             float ss = 0.f;
 #pragma unroll
-            for (int j = 0; j < PPW; ++j) {
-                const int p = 16 * (wave * PPW + j) + l16;
+            for (int j = 0; j < SCW; ++j) {
+                const int p = 16 * (cg * SCW + j) + l16;
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const floatx4 sv = MM::unpack(MM::ldk(sSt + p * LDS + 16 * nb + 4 * g));
+                for (int i = 0; i < SRW; ++i) {
+                    const floatx4 sv = MM::unpack(MM::ldk(sSt + p * LDS + 16 * (rg * SRW + i) + 4 * g));
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) ss = fmaf(st[j][nb][m], sv[m], ss);
+                    for (int m = 0; m < 4; ++m) ss = fmaf(st[j][i][m], sv[m], ss);
                 }
             }
             ss = group_sum(ss, 64);
@@ -839,36 +857,36 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
         // ================= S5: products with the masked score tiles; state cotangent ===
         // dX^T += dY^T M1 (i blocks at or after this wave's s block)
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb)
+        for (int pb = 0; pb < PBH; ++pb)
 #pragma unroll
             for (int ib = 0; ib < NIB; ++ib)
-                if (ib >= wave)
-                    dxa[pb] = MM::mma(MM::ldt(sDY + (16 * ib + 4 * g) * LDX + 16 * pb, LDX, l16),
-                                      MM::ldt(sM1 + (16 * ib + 4 * g) * LDM + 16 * wave, LDM, l16), dxa[pb]);
+                if (ib >= rbw)
+                    dxa[pb] = MM::mma(MM::ldt(sDY + (16 * ib + 4 * g) * LDX + 16 * (hf * PBH + pb), LDX, l16),
+                                      MM::ldt(sM1 + (16 * ib + 4 * g) * LDM + 16 * rbw, LDM, l16), dxa[pb]);
         // dBbar^T += Cbar^T dS
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NBH; ++nb)
 #pragma unroll
             for (int ib = 0; ib < NIB; ++ib)
-                if (ib >= wave)
-                    dba[nb] = MM::mma(MM::ldt(sC + (16 * ib + 4 * g) * LDB + 16 * nb, LDB, l16),
-                                      MM::ldt(sDS + (16 * ib + 4 * g) * LDM + 16 * wave, LDM, l16), dba[nb]);
+                if (ib >= rbw)
+                    dba[nb] = MM::mma(MM::ldt(sC + (16 * ib + 4 * g) * LDB + 16 * (hf * NBH + nb), LDB, l16),
+                                      MM::ldt(sDS + (16 * ib + 4 * g) * LDM + 16 * rbw, LDM, l16), dba[nb]);
         // dCbar^T += Bbar^T dS^T (s blocks at or before this wave's i block)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NBH; ++nb)
 #pragma unroll
             for (int sb = 0; sb < NIB; ++sb)
-                if (sb <= wave)
-                    dca[nb] = MM::mma(MM::ldt(sB + (16 * sb + 4 * g) * LDB + 16 * nb, LDB, l16),
+                if (sb <= rbw)
+                    dca[nb] = MM::mma(MM::ldt(sB + (16 * sb + 4 * g) * LDB + 16 * (hf * NBH + nb), LDB, l16),
                                       MM::ldk(sDS + wrow * LDM + 16 * sb + 4 * g), dca[nb]);
         // recomputed Y^T += X^T M1^T; mixing-weight gradient sum_t Y[t, r, p] dy[t, p]
         if (mix) {
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb) {
+            for (int pb = 0; pb < PBH; ++pb) {
 #pragma unroll
                 for (int sb = 0; sb < NIB; ++sb)
-                    if (sb <= wave)
-                        ya[pb] = MM::mma(MM::ldt(sX + (16 * sb + 4 * g) * LDX + 16 * pb, LDX, l16),
+                    if (sb <= rbw)
+                        ya[pb] = MM::mma(MM::ldt(sX + (16 * sb + 4 * g) * LDX + 16 * (hf * PBH + pb), LDX, l16),
                                          MM::ldk(sM1 + wrow * LDM + 16 * sb + 4 * g), ya[pb]);
                 float f[VE];
                 unpack16(dyv[pb], f, T{});
@@ -880,8 +898,8 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
         {
             const float dec = rEnd[1];
 #pragma unroll
-            for (int j = 0; j < PPW; ++j) {
-                const int pb = wave * PPW + j;
+            for (int j = 0; j < SCW; ++j) {
+                const int pb = cg * SCW + j;
                 F yb[NIB];
 #pragma unroll
                 for (int ib = 0; ib < NIB; ++ib) {
@@ -892,12 +910,13 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
                     yb[ib] = MM::pack(yv);
                 }
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
+                for (int i = 0; i < SRW; ++i) {
+                    const int nb = rg * SRW + i;
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) st[j][nb][m] *= dec;
+                    for (int m = 0; m < 4; ++m) st[j][i][m] *= dec;
 #pragma unroll
                     for (int ib = 0; ib < NIB; ++ib)
-                        st[j][nb] = MM::mma(MM::ldt(sC + (16 * ib + 4 * g) * LDB + 16 * nb, LDB, l16), yb[ib], st[j][nb]);
+                        st[j][i] = MM::mma(MM::ldt(sC + (16 * ib + 4 * g) * LDB + 16 * nb, LDB, l16), yb[ib], st[j][i]);
                 }
             }
         }
@@ -906,8 +925,9 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
             const rsrc_t dXo = make_rsrc(dXg + t0 * HRP, tail_bytes(t0, HRP, (int64_t)R * P));
             const int tl = wrow >> RL2, r = wrow & (R - 1);
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
-                store4(dXo, (uint32_t)((tl * (int)HRP + r * P + 16 * pb + 4 * g) * (int)sizeof(T)), dxa[pb], T{});
+            for (int pb = 0; pb < PBH; ++pb)
+                store4(dXo, (uint32_t)((tl * (int)HRP + r * P + 16 * (hf * PBH + pb) + 4 * g) * (int)sizeof(T)), dxa[pb],
+                       T{});
         }
         __syncthreads();   // (4)
 
@@ -925,9 +945,9 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
             }
         }
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            *(floatx4*)(fB + wrow * LDF + 16 * nb + 4 * g) = dba[nb];
-            *(floatx4*)(fC + wrow * LDF + 16 * nb + 4 * g) = dca[nb];
+        for (int nb = 0; nb < NBH; ++nb) {
+            *(floatx4*)(fB + wrow * LDF + 16 * (hf * NBH + nb) + 4 * g) = dba[nb];
+            *(floatx4*)(fC + wrow * LDF + 16 * (hf * NBH + nb) + 4 * g) = dca[nb];
         }
         __syncthreads();   // (5)
 
@@ -1073,8 +1093,11 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
                         GM += pGam[w * 64 + row];
                         LI += pLi[w * 64 + row];
                     }
-                    DW += rDw[row];
-                    LI += rDlo[row];
+#pragma unroll
+                    for (int hh = 0; hh < WPB; ++hh) {
+                        DW += rDw[hh * 64 + row];
+                        LI += rDlo[hh * 64 + row];
+                    }
                 }
             }
             const float d = live ? cd : 0.f, lm = live ? cl : 0.f;
@@ -1137,12 +1160,12 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
     // ---- after the first chunk: carried-in inputs, step 0, outputs -------------------------
     // dh_in = dS_{-1}
 #pragma unroll
-    for (int j = 0; j < PPW; ++j)
+    for (int j = 0; j < SCW; ++j)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int i = 0; i < SRW; ++i)
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-                a.dh_in[(bh * N + 16 * nb + 4 * g + m) * P + 16 * (wave * PPW + j) + l16] = st[j][nb][m];
+                a.dh_in[(bh * N + 16 * (rg * SRW + i) + 4 * g + m) * P + 16 * (cg * SCW + j) + l16] = st[j][i][m];
     float dc0 = 0.f;
     const bool carry_in = a.Bbar_prev && a.x_prev && L > 0;
     if (carry_in) {
@@ -1150,11 +1173,12 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
         float* fS = (float*)tiles;
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < PPW; ++j)
+        for (int j = 0; j < SCW; ++j)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int i = 0; i < SRW; ++i)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) fS[(16 * nb + 4 * g + m) * (P + 4) + 16 * (wave * PPW + j) + l16] = st[j][nb][m];
+                for (int m = 0; m < 4; ++m)
+                    fS[(16 * (rg * SRW + i) + 4 * g + m) * (P + 4) + 16 * (cg * SCW + j) + l16] = st[j][i][m];
         __syncthreads();
         const float c0 = (1.0f - load_f32(lamg)) * load_f32(dtg);
         const T* Bp = (const T*)a.Bbar_prev + bh * R * N;
@@ -1232,7 +1256,7 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
         if (mix) {
             // lanes l16 = r, r + R, ... of a row group hold the same (r, p): sum them
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
+            for (int pb = 0; pb < PBH; ++pb)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     float v = accMix[pb][m];
@@ -1245,9 +1269,9 @@ __global__ __launch_bounds__(NIB * 64, 1) void backward_kernel(BackwardArgs a) {
             for (int w = 0; w < NW; ++w) {
                 if (wave == w && l16 < R) {
 #pragma unroll
-                    for (int pb = 0; pb < PB; ++pb)
+                    for (int pb = 0; pb < PBH; ++pb)
 #pragma unroll
-                        for (int m = 0; m < 4; ++m) fmix[l16 * P + 16 * pb + 4 * g + m] += accMix[pb][m];
+                        for (int m = 0; m < 4; ++m) fmix[l16 * P + 16 * (hf * PBH + pb) + 4 * g + m] += accMix[pb][m];
                 }
                 __syncthreads();
             }
@@ -1303,13 +1327,18 @@ __global__ __launch_bounds__(256) void group_sum_kernel(BackwardArgs a) {
     }
 }
 
+// waves per 16-row block of the backward kernel: two where the column blocks split evenly (two
+// waves per SIMD), one for the 16 x 16 shape
+template <int N, int P> constexpr int backward_wpb() { return (N / 16) % 2 == 0 && (P / 16) % 2 == 0 ? 2 : 1; }
+
 template <typename T, int N, int P, int NIB, int R>
 hipError_t launch_nipr(const BackwardArgs& a, bool states_only, hipStream_t s) {
     const dim3 grid((unsigned)(a.b * a.H)), block(NIB * 64);
     hipLaunchKernelGGL((chunk_states_kernel<T, N, P, NIB, R>), grid, block, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || states_only) return e;
-    hipLaunchKernelGGL((backward_kernel<T, N, P, NIB, R>), grid, block, 0, s, a);
+    constexpr int WPB = backward_wpb<N, P>();
+    hipLaunchKernelGGL((backward_kernel<T, N, P, NIB, R, WPB>), grid, dim3(NIB * WPB * 64), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)a.H), dim3(256), 0, s, a);
