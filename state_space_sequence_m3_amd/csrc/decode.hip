@@ -267,7 +267,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeArgs a) 
 //
 // LDS: per parity, Bbar_prev, Bbar, Cbar as [n][r] (one LDS read serves every rank of a row) and
 // x_prev, x as [r][p]; per parity, the Y partial sums [wave][r][p]; the head constants.
-template <typename T, int N, int P, int R, bool FUSED>
+// NTS: the states of the call are far larger than the last-level cache, so every step streams
+// them from DRAM: their loads and stores are non-temporal (a read-modify-write stream in place
+// moves ~10% more that way; for states the cache can partly hold, the default policy is faster).
+template <typename T, int N, int P, int R, bool FUSED, bool NTS>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(FUSED && R == 4 ? 3 : 4))) void decode_stream_kernel(DecodeArgs a) {
     constexpr int NT = kDecThreads, K = N / 2;
     constexpr int NQ = N * P / (4 * NT);                 // float4 of state per thread per pair
@@ -361,7 +364,9 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(FUS
         }
         const rsrc_t rsH = make_rsrc(a.h + bh * (int64_t)(N * P), ok ? N * P * 4 : 0);
 #pragma unroll
-        for (int k = 0; k < NQ; ++k) g[k] = buffer_load16(rsH, (uint32_t)(tid + NT * k) * 16);
+        for (int k = 0; k < NQ; ++k)
+            g[k] = NTS ? buffer_load16_stream(rsH, (uint32_t)(tid + NT * k) * 16)
+                       : buffer_load16(rsH, (uint32_t)(tid + NT * k) * 16);
     };
 
     // ---- stage a pair's token vectors into LDS buffer `par`; returns its step scalars
@@ -499,7 +504,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(FUS
                 for (int r = 0; r < R; ++r) v = fmaf(bt[r], xg[r][j], fmaf(bp[r], xb[r][j], v));
                 g[j] = v;
             }
-            buffer_store16(rsH, (uint32_t)(tid + NT * k) * 16,
+            (NTS ? buffer_store16_stream : buffer_store16)(rsH, (uint32_t)(tid + NT * k) * 16,
                            make_uint4(__float_as_uint(g[0]), __float_as_uint(g[1]), __float_as_uint(g[2]),
                                       __float_as_uint(g[3])));
 #pragma unroll
@@ -592,15 +597,25 @@ inline int64_t stream_grid(int64_t npairs, int H, int resident) {
     return g;
 }
 
-template <typename T, int N, int P, int R, bool FUSED>
-hipError_t launch_stream(const DecodeArgs& a, hipStream_t s, bool& done) {
+// states larger than this stream from DRAM on every step (the last-level cache is 256 MB)
+constexpr int64_t kStreamStateBytes = (int64_t)512 << 20;
+
+template <typename T, int N, int P, int R, bool FUSED, bool NTS>
+hipError_t launch_stream_nts(const DecodeArgs& a, hipStream_t s, bool& done) {
     static std::atomic<int> cache[kMaxDevices];
-    auto kern = decode_stream_kernel<T, N, P, R, FUSED>;
+    auto kern = decode_stream_kernel<T, N, P, R, FUSED, NTS>;
     const int64_t grid = stream_grid(a.b * a.H, a.H, resident_workgroups(kern, cache));
     done = grid > 0;
     if (!done) return hipSuccess;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDecThreads), 0, s, a);
     return hipGetLastError();
+}
+
+template <typename T, int N, int P, int R, bool FUSED>
+hipError_t launch_stream(const DecodeArgs& a, hipStream_t s, bool& done) {
+    const bool nts = a.b * a.H * (int64_t)N * P * 4 > kStreamStateBytes;
+    return nts ? launch_stream_nts<T, N, P, R, FUSED, true>(a, s, done)
+               : launch_stream_nts<T, N, P, R, FUSED, false>(a, s, done);
 }
 
 template <typename T, int N, int P, bool FUSED>

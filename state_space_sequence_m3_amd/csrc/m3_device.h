@@ -148,6 +148,10 @@ __device__ __forceinline__ void buffer_store8(rsrc_t r, uint32_t off, uint2 v) {
 __device__ __forceinline__ void buffer_store16(rsrc_t r, uint32_t off, uint4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
 }
+// non-temporal store (data not read again soon through this cache level)
+__device__ __forceinline__ void buffer_store16_stream(rsrc_t r, uint32_t off, uint4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 2);
+}
 // one io element as raw bits (loaded now, converted where it is used, so the load need not be
 // waited for at once); past the descriptor's end it reads as zero
 template <typename T> struct IoBits;
