@@ -128,7 +128,7 @@ def layer_decode_bytes_per_head(w) -> int:
 # The GPU reaches its steady clocks only after some tens of milliseconds of sustained work: every
 # timed loop below first runs its `warmup` steps, then keeps running the same step until at least
 # WARM_S seconds of work have passed since the warm-up began (untimed), then times its steps.
-WARM_S = 0.25
+WARM_S = float(os.environ.get("M3_BENCH_WARM_S", "0.25"))
 
 
 def warm_up(step, warmup):
