@@ -413,6 +413,35 @@ m3_status m3_layer_backward(const m3_dims* dims, const void* x, const void* B, c
                             float* dh_in, void* dBbar_prev, void* dx_prev, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * m3_layer_prefill_noalloc -- m3_layer_prefill for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * For: those callers.  Arguments, results and errors are those of m3_layer_prefill without the
+ * workspace: where m3_layer_prefill would split few long sequences into segments (when
+ * m3_layer_prefill_workspace_bytes(dims) > 0), this call uses a device array the library holds
+ * instead of a caller workspace.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).
+ *   - Limit.  The array holds M3_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, enough for the split of
+ *     b = 1, L = 16384, H = 64, R = 4, N = 128, P = 64 (about 18 MB).  Dims whose split needs more
+ *     return M3_E_WORKSPACE (call m3_layer_prefill with a workspace instead).  Dims that do not
+ *     split use no scratch.
+ *   - Sharing.  Every call on one GPU uses that GPU's one array, whose contents persist from
+ *     call to call (each call writes every scratch element before reading it; nothing needs to
+ *     start at zero).  Calls that may run at the same time on one GPU (on different streams, or
+ *     from several host threads without ordering) race on the array: the caller must order them.
+ *   - Memory.  Each GPU the library runs on holds its copy of the array from the library's load
+ *     until the process ends.
+ */
+#define M3_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+m3_status m3_layer_prefill_noalloc(const m3_dims* dims, const void* x, const void* B, const void* C,
+                                   const void* dt, const void* theta, const float* normw_B,
+                                   const float* normw_C, const float* bias_B, const float* bias_C,
+                                   const float* A, const void* lam, const float* w_out,
+                                   const float* phi_in, const float* h_in, const void* Bbar_prev,
+                                   const void* x_prev, void* y, float* h_out, float* phi_out,
+                                   void* Bbar_last, void* x_last, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

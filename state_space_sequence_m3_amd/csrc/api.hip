@@ -842,4 +842,71 @@ m3_status m3_layer_backward(const m3_dims* d, const void* x, const void* B, cons
     return launched(m3::launch_backward(a, d->io == M3_BF16, stream), "m3_layer_backward");
 }
 
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// m3_layer_prefill_noalloc: m3_layer_prefill whose sequence-split workspace is a library-held
+// device array instead of caller memory, for callers that cannot allocate (code under graph
+// capture, serving loops).  The array lives in this file's code object: each GPU the library
+// runs on holds its own copy (kNoAllocScratchBytes) from the module's load until the process
+// ends.  Host code never uses the array's name as a device address; its address on each device
+// is taken once with hipGetSymbolAddress, with that device current, and kept per device.
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = M3_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kScratchDevices = 256;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+
+// the scratch array's address on the current device, taken once per device (with that device
+// current) and kept
+m3_status scratch_on_current_device(const char* fn, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices)
+        return fail(M3_E_NODEVICE, "%s: no current HIP device", fn);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(M3_E_LAUNCH, "%s: cannot get the scratch array's address on device %d: %s", fn, dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return M3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_layer_prefill_noalloc(const m3_dims* d, const void* x, const void* B, const void* C,
+                                   const void* dt, const void* theta, const float* normw_B,
+                                   const float* normw_C, const float* bias_B, const float* bias_C,
+                                   const float* A, const void* lam, const float* w_out,
+                                   const float* phi_in, const float* h_in, const void* Bbar_prev,
+                                   const void* x_prev, void* y, float* h_out, float* phi_out,
+                                   void* Bbar_last, void* x_last, hipStream_t stream) {
+    const char* fn = "m3_layer_prefill_noalloc";
+    m3_status s = check_common_dims(d);
+    if (s != M3_OK) return s;
+    // the workspace m3_layer_prefill would take for these dims on this device (0: no split)
+    const size_t need = m3_layer_prefill_workspace_bytes(d);
+    if (need > kNoAllocScratchBytes)
+        return fail(M3_E_WORKSPACE,
+                    "%s: these dims split each sequence and need %zu bytes of scratch; the library holds %zu "
+                    "(call m3_layer_prefill with a workspace instead)",
+                    fn, need, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) {
+        if ((s = check_device()) != M3_OK) return s;
+        if ((s = scratch_on_current_device(fn, &ws)) != M3_OK) return s;
+    }
+    return layer_prefill(d, false, nullptr, x, B, C, dt, theta, normw_B, normw_C, bias_B, bias_C, A, lam, w_out,
+                         phi_in, h_in, Bbar_prev, x_prev, y, h_out, phi_out, Bbar_last, x_last, ws, need, stream, fn);
+}
+
 }  // extern "C"

@@ -30,7 +30,9 @@ EXPORTED = ["m3_bcnorm_rope", "m3_bcnorm_rope_workspace_bytes", "m3_prefill",
             "m3_layer_prefill_varlen",
             "m3_decode_step",
             "m3_layer_decode_step", "m3_layer_backward_chunk", "m3_layer_chunk_states",
-            "m3_layer_backward_workspace_bytes", "m3_layer_backward", "m3_last_error", "m3_version"]
+            "m3_layer_backward_workspace_bytes", "m3_layer_backward", "m3_last_error", "m3_version",
+            "m3_layer_prefill_noalloc"]
+NOALLOC_SCRATCH_BYTES = 32 << 20   # M3_NOALLOC_SCRATCH_BYTES
 
 
 class M3Dims(ctypes.Structure):
@@ -74,6 +76,8 @@ def load(path: str = LIB_PATH):
             lib.m3_layer_prefill_workspace_bytes.argtypes = [_DIMS]
             lib.m3_layer_prefill.restype = ctypes.c_int
             lib.m3_layer_prefill.argtypes = [_DIMS] + [_P] * 22 + [ctypes.c_size_t, _P]
+            lib.m3_layer_prefill_noalloc.restype = ctypes.c_int
+            lib.m3_layer_prefill_noalloc.argtypes = [_DIMS] + [_P] * 21 + [_P]
             lib.m3_layer_prefill_varlen.restype = ctypes.c_int
             lib.m3_layer_prefill_varlen.argtypes = [_DIMS] + [_P] * 22 + [_P]
             lib.m3_layer_decode_step.restype = ctypes.c_int
@@ -300,6 +304,53 @@ def m3_layer_prefill(x, B, C, dt, theta, A, lam, normw_B=None, normw_C=None, bia
                                 _ptr(lam), _ptr(w_out), _ptr(phi_in), _ptr(h_in), _ptr(Bbar_prev),
                                 _ptr(x_prev), _ptr(y), _ptr(h_out), _ptr(phi_out), _ptr(Bbar_last),
                                 _ptr(x_last), _ptr(workspace), ws_bytes, _stream(stream)))
+    return y, h_out, phi_out
+
+
+def m3_layer_prefill_noalloc(x, B, C, dt, theta, A, lam, normw_B=None, normw_C=None, bias_B=None,
+                             bias_C=None, w_out=None, phi_in=None, h_in=None, Bbar_prev=None,
+                             x_prev=None, y=None, h_out=None, phi_out=None, Bbar_last=None,
+                             x_last=None, chunk=0, bcnorm=True, eps=1e-5, stream=None):
+    """m3_layer_prefill without a workspace argument: a split of few long sequences uses the
+    library's own device scratch array (M3_NOALLOC_SCRATCH_BYTES per GPU).  The library itself
+    allocates nothing; outputs not passed are allocated here (pass them all for an allocation-free
+    call).  Returns (y, h_out, phi_out)."""
+    lib = load()
+    b, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[-1]
+    dev, io = x.device, x.dtype
+    f32 = torch.float32
+    _tensor(B, "B", (b, L, G, R, N), io, dev)
+    _tensor(C, "C", (b, L, G, R, N), io, dev)
+    _tensor(dt, "dt", (b, L, H), io, dev)
+    _tensor(theta, "theta", (b, L, H, N // 2), io, dev)
+    _tensor(lam, "lam", (b, L, H), io, dev)
+    _tensor(A, "A", (H,), f32, dev)
+    _tensor(normw_B, "normw_B", (H, N), f32, dev)
+    _tensor(normw_C, "normw_C", (H, N), f32, dev)
+    _tensor(bias_B, "bias_B", (H, R, N), f32, dev)
+    _tensor(bias_C, "bias_C", (H, R, N), f32, dev)
+    _tensor(w_out, "w_out", (H, R, P), f32, dev)
+    _tensor(phi_in, "phi_in", (b, H, N // 2), f32, dev)
+    _tensor(h_in, "h_in", (b, H, N, P), f32, dev)
+    _tensor(Bbar_prev, "Bbar_prev", (b, H, R, N), io, dev)
+    _tensor(x_prev, "x_prev", (b, H, R, P), io, dev)
+    yshape = (b, L, H, P) if w_out is not None else (b, L, H, R, P)
+    y = torch.empty(yshape, dtype=io, device=dev) if y is None else _tensor(y, "y", yshape, io, dev)
+    if h_out is None:
+        h_out = torch.empty((b, H, N, P), dtype=f32, device=dev)
+    _tensor(h_out, "h_out", (b, H, N, P), f32, dev)
+    if phi_out is None:
+        phi_out = torch.empty((b, H, N // 2), dtype=f32, device=dev)
+    _tensor(phi_out, "phi_out", (b, H, N // 2), f32, dev)
+    _tensor(Bbar_last, "Bbar_last", (b, H, R, N), io, dev)
+    _tensor(x_last, "x_last", (b, H, R, P), io, dev)
+    dims = make_dims(b, L, H, P, N, R, chunk, _io_code(io), bcnorm, eps, _groups(H, G))
+    _check(lib.m3_layer_prefill_noalloc(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(theta),
+                                        _ptr(normw_B), _ptr(normw_C), _ptr(bias_B), _ptr(bias_C), _ptr(A),
+                                        _ptr(lam), _ptr(w_out), _ptr(phi_in), _ptr(h_in), _ptr(Bbar_prev),
+                                        _ptr(x_prev), _ptr(y), _ptr(h_out), _ptr(phi_out), _ptr(Bbar_last),
+                                        _ptr(x_last), _stream(stream)))
     return y, h_out, phi_out
 
 

@@ -399,3 +399,27 @@ def test_head_groups_backward_workspace():
     assert m3scan.layer_backward_workspace_bytes(_dims(seqlen=130, nheads=4, groups=4)) == \
         m3scan.layer_backward_workspace_bytes(d)
     assert m3scan.layer_backward_workspace_bytes(_dims(nheads=4, groups=3)) == 0
+
+
+def test_noalloc_rejects_a_split_beyond_its_scratch():
+    """m3_layer_prefill_noalloc: dims whose sequence split needs more than the library's scratch
+    array are refused before any device work (the split plan assumes 256 compute units when no
+    device answers)."""
+    lib = m3scan.load()
+    # 500 (b, h) pairs, 2 segments of 1024 steps: 32.8 MB of states + rotated B + angles > 32 MiB
+    d = _dims(batch=2, seqlen=2048, nheads=250, rank=4, chunk=8)
+    assert m3scan.layer_prefill_workspace_bytes(d) > m3scan.NOALLOC_SCRATCH_BYTES
+    # x, B, C, dt, theta, normw_B, normw_C, bias_B, bias_C, A, lam, w_out, phi_in, h_in, Bbar_prev,
+    # x_prev, y, h_out, phi_out, Bbar_last, x_last
+    p = _ptrs(21)
+    for i in (5, 6, 7, 8, 11, 12, 13, 14, 15, 19, 20):   # optional pointers
+        p[i] = None
+    st = lib.m3_layer_prefill_noalloc(ctypes.byref(d), *p, None)
+    assert st == m3scan.M3_E_WORKSPACE and "scratch" in m3scan.last_error()
+    # a call that does not split needs no scratch: it gets past the size check (and then stops at
+    # the device check here)
+    small = _dims(batch=8, seqlen=64, nheads=64, rank=1, chunk=32)
+    assert m3scan.layer_prefill_workspace_bytes(small) == 0
+    st = lib.m3_layer_prefill_noalloc(ctypes.byref(small), *p, None)
+    if not os.path.exists("/dev/kfd"):
+        assert st == m3scan.M3_E_NODEVICE
