@@ -71,8 +71,12 @@ struct Shape {
     static constexpr int SCW = PB >= NW ? PB / NW : 1, NCG = PB / SCW, SRW = NB / (NW / NCG);
     static_assert(PB % WPB == 0 && NB % WPB == 0, "column blocks per wave");
     static_assert(NCG * SCW == PB && (NW / NCG) * SRW == NB && NW % NCG == 0, "state tiles per wave");
-    static constexpr int PADT = Mma<T>::PADT;
+    static constexpr int PADT = Mma<T>::PADT, PADK = Mma<T>::PADK;
     static constexpr int LDB = N + PADT, LDX = P + PADT, LDS = N + PADT, LDM = QR + PADT;
+    // the backward kernel reads most of its tiles both along K and transposed, and no row padding
+    // serves both without bank conflicts: the tiles read mostly along K (Bbar, Cbar, x, dY and the
+    // entry state) take the K padding, the state cotangent and the score tiles the transposed one
+    static constexpr int LDBK = N + PADK, LDXK = P + PADK, LDSK = N + PADK;
     static constexpr int VE = 16 / (int)sizeof(T), VPN = N / VE, VPP = P / VE;
     static constexpr int RKC = NT / VPN, RKX = NT / VPP;
     static constexpr int MAXC = (QR + RKC - 1) / RKC, MAXX = (QR + RKX - 1) / RKX;
@@ -82,11 +86,12 @@ struct Shape {
     static constexpr int K = N / 2, VT = VE, NVT = K / VT;
     static constexpr int TPV0 = NT / NVT, TPV = Q < TPV0 ? Q : TPV0, SPT = Q / TPV;
     static constexpr int LDPHI = K + 4, LDF = N + 4, LDD = K + 4;
-    // byte offsets of the tiles in the shared tile region
-    static constexpr int SZB = QR * LDB * (int)sizeof(T), SZX = QR * LDX * (int)sizeof(T);
-    static constexpr int SZS = P * LDS * (int)sizeof(T), SZM = QR * LDM * (int)sizeof(T);
+    // byte offsets of the backward kernel's tiles in its shared tile region
+    static constexpr int SZB = QR * LDBK * (int)sizeof(T), SZX = QR * LDXK * (int)sizeof(T);
+    static constexpr int SZSK = P * LDSK * (int)sizeof(T), SZS = P * LDS * (int)sizeof(T);
+    static constexpr int SZM = QR * LDM * (int)sizeof(T);
     static constexpr int OFF_B = 0, OFF_C = SZB, OFF_X = 2 * SZB, OFF_Y = OFF_X + SZX, OFF_S = OFF_Y + SZX,
-                         OFF_DS = OFF_S + SZS, OFF_M1 = OFF_DS + SZS, OFF_DSC = OFF_M1 + SZM, TILES = OFF_DSC + SZM;
+                         OFF_DS = OFF_S + SZSK, OFF_M1 = OFF_DS + SZS, OFF_DSC = OFF_M1 + SZM, TILES = OFF_DSC + SZM;
     // after the products the region holds the fp32 gradient rows and the per-row angle gradients
     static constexpr int OFF_FB = 0, OFF_FC = QR * LDF * 4, OFF_FPHI = 2 * QR * LDF * 4,
                          ALIAS = OFF_FPHI + QR * LDD * 4, FINAL = N * (P + 4) * 4;
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
     using F = typename MM::frag;
     constexpr int NW = S::NW, NT = S::NT, QR = S::QR, Q = S::Q, RL2 = S::RL2, NB = S::NB, PB = S::PB;
     constexpr int PBH = S::PBH, NBH = S::NBH, SCW = S::SCW, SRW = S::SRW, NCG = S::NCG;
-    constexpr int LDB = S::LDB, LDX = S::LDX, LDS = S::LDS, LDM = S::LDM, VE = S::VE, VPN = S::VPN,
+    constexpr int LDB = S::LDBK, LDX = S::LDXK, LDSS = S::LDSK, LDS = S::LDS, LDM = S::LDM, VE = S::VE, VPN = S::VPN,
                   VPP = S::VPP;
     constexpr int RKC = S::RKC, RKX = S::RKX, MAXC = S::MAXC, MAXX = S::MAXX, MAXS = S::MAXS;
     constexpr int K = S::K, VT = S::VT, NVT = S::NVT, TPV = S::TPV, SPT = S::SPT, LDPHI = S::LDPHI,
@@ -634,7 +639,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
             const int p = iC0 + k * RKC;
-            if (S::FULLS || p < P) *(uint4*)(sSt + p * LDS + cC0 * VE) = rs[k];
+            if (S::FULLS || p < P) *(uint4*)(sSt + p * LDSS + cC0 * VE) = rs[k];
         }
 #pragma unroll
         for (int j = 0; j < SCW; ++j) {
@@ -805,7 +810,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < PB; ++kb)
-                    acc = MM::mma(MM::ldt(sSt + (16 * kb + 4 * g) * LDS + 16 * nbg, LDS, l16),
+                    acc = MM::mma(MM::ldt(sSt + (16 * kb + 4 * g) * LDSS + 16 * nbg, LDSS, l16),
                                   MM::ldk(sDY + wrow * LDX + 16 * kb + 4 * g), acc);
                 const floatx4 cv = MM::unpack(MM::ldk(sC + wrow * LDB + 16 * nbg + 4 * g));
 #pragma unroll
@@ -829,7 +834,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NB; ++kb)
-                    acc = MM::mma(MM::ldk(sSt + (16 * (hf * PBH + pb) + l16) * LDS + 16 * kb + 4 * g),
+                    acc = MM::mma(MM::ldk(sSt + (16 * (hf * PBH + pb) + l16) * LDSS + 16 * kb + 4 * g),
                                   MM::ldk(sC + wrow * LDB + 16 * kb + 4 * g), acc);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) acc[m] *= el;
@@ -844,7 +849,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                 const int p = 16 * (cg * SCW + j) + l16;
 #pragma unroll
                 for (int i = 0; i < SRW; ++i) {
-                    const floatx4 sv = MM::unpack(MM::ldk(sSt + p * LDS + 16 * (rg * SRW + i) + 4 * g));
+                    const floatx4 sv = MM::unpack(MM::ldk(sSt + p * LDSS + 16 * (rg * SRW + i) + 4 * g));
 #pragma unroll
                     for (int m = 0; m < 4; ++m) ss = fmaf(st[j][i][m], sv[m], ss);
                 }

@@ -68,7 +68,8 @@ namespace {
 // STATES: pass 1 of a split sequence, which needs only each segment's end state: no C is read
 // or staged, and the score tiles, masks, outputs and stores of y are left out (the chunk's
 // barrier stays, it orders the staging buffers).
-template <typename T, int N, int P, int NIB, bool FUSED, bool STATES = false>
+// PAIR (fused, ranks R >= 2): each thread stages two neighbouring rows of one step (see rowC).
+template <typename T, int N, int P, int NIB, bool FUSED, bool STATES = false, bool PAIR = false>
 __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) {
     using MM = Mma<T>;
     using F = typename MM::frag;
@@ -197,8 +198,13 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // chunk row i = i0 + k * RK (row (t, r) = (i >> rl2, i & rmask)), 16-byte column c0.
     const int iC0 = tid / VPN, cC0 = tid % VPN, iX0 = tid / VPP, cX0 = tid % VPP;
     const int SBC32 = (int)SBC, HRP32 = (int)HRP;
+    // With ranks (R >= 2) and a chunk of two staging steps, the fused kernel gives each thread two
+    // neighbouring rows, 2 iC0 and 2 iC0 + 1: two ranks of one step, which share their rotation
+    // angles, so the sine and cosine are taken once for both (the rows of MIMO are 4 per step).
+    constexpr bool pair_rows = PAIR && FUSED && MAXC == 2 && FULLC;
+    auto rowC = [&](int k) { return pair_rows ? 2 * iC0 + k : iC0 + k * RKC; };
     auto offC = [&](int k) {
-        const int i = iC0 + k * RKC;
+        const int i = rowC(k);
         return (uint32_t)(((i >> rl2) * SBC32 + (i & rmask) * N + cC0 * VE) * (int)sizeof(T));
     };
     auto offX = [&](int k) {
@@ -222,13 +228,13 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             const uint32_t o = step_off(t0, SBC);
 #pragma unroll
             for (int k = 0; k < MAXC; ++k)
-                if (FULLC || iC0 + k * RKC < QR) rc[set][k] = buffer_load16_stream(dCs, offC(k) + o);
+                if (FULLC || rowC(k) < QR) rc[set][k] = buffer_load16_stream(dCs, offC(k) + o);
         }
         if (part < 0 || part == 1) {
             const uint32_t o = step_off(t0, SBC);
 #pragma unroll
             for (int k = 0; k < MAXC; ++k)
-                if (FULLC || iC0 + k * RKC < QR) rb[set][k] = buffer_load16_stream(dBs, offC(k) + o);
+                if (FULLC || rowC(k) < QR) rb[set][k] = buffer_load16_stream(dBs, offC(k) + o);
         }
         if (part < 0 || part == 2) {
             const uint32_t o = step_off(t0, HRP);
@@ -341,19 +347,18 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // one after the other to keep few values live; they share the row's angles.
     const float invN = 1.0f / (float)N;
     const bool has_w = a.bcnorm && (a.normw_B || a.normw_C);
-    auto stage_bc = [&](int set, int k, int i, int buf) {
-        const int t = i >> rl2, r = i & rmask;
-        const int n0 = cC0 * VE;
-        // angles first (LDS read + hardware sin/cos, independent of the rest)
-        float cs[VE / 2], sn[VE / 2];
-        {
-            const float* ph = sPhi + buf * TPH + t * LDPHI + n0 / 2;
+    // the angles of row i's step for this thread's pairs (LDS read + hardware sin/cos, in turns)
+    auto row_angles = [&](int i, int buf, float (&cs)[VE / 2], float (&sn)[VE / 2]) {
+        const float* ph = sPhi + buf * TPH + (i >> rl2) * LDPHI + cC0 * VE / 2;
 #pragma unroll
-            for (int q = 0; q < VE / 2; ++q) {   // angles in turns
-                sn[q] = __builtin_amdgcn_sinf(ph[q]);
-                cs[q] = __builtin_amdgcn_cosf(ph[q]);
-            }
+        for (int q = 0; q < VE / 2; ++q) {
+            sn[q] = __builtin_amdgcn_sinf(ph[q]);
+            cs[q] = __builtin_amdgcn_cosf(ph[q]);
         }
+    };
+    auto stage_bc = [&](int set, int k, int i, int buf, const float (&cs)[VE / 2], const float (&sn)[VE / 2]) {
+        const int r = i & rmask;
+        const int n0 = cC0 * VE;
         float sc[2] = {1.f, 1.f};
         if (a.bcnorm) {   // RMS over the row's N values, spread over VPN consecutive lanes
             constexpr int NR = STATES ? 1 : 2;   // rows normalised: B (and C)
@@ -430,10 +435,20 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     constexpr int NITEM = MAXC + MAXX + 1;
     auto stage_item = [&](int j, int set, int buf) {
         if (j < MAXC) {
-            const int i = iC0 + j * RKC;
+            const int i = rowC(j);
             if (FULLC || i < QR) {
                 if (FUSED) {
-                    stage_bc(set, j, i, buf);
+                    float cs[VE / 2], sn[VE / 2];
+                    if constexpr (pair_rows) {   // both rows (one step) in the first item, one set of angles
+                        if (j == 0) {
+                            row_angles(i, buf, cs, sn);
+                            stage_bc(set, 0, i, buf, cs, sn);
+                            stage_bc(set, 1, i + 1, buf, cs, sn);
+                        }
+                    } else {
+                        row_angles(i, buf, cs, sn);
+                        stage_bc(set, j, i, buf, cs, sn);
+                    }
                 } else {
                     if (!STATES) *(uint4*)(sC + buf * TC + i * LDC + cC0 * VE) = rc[set][j];
                     *(uint4*)(sB + buf * TB + i * LDB + cC0 * VE) = rb[set][j];
@@ -855,7 +870,13 @@ hipError_t launch_nps(const PrefillArgs& a, hipStream_t s) {
     const size_t dyn = FUSED ? (size_t)(2 * N + 2 * a.R * N) * sizeof(float) : 0;
     switch (a.Q * a.R) {
         case 16: hipLaunchKernelGGL((prefill_kernel<T, N, P, 1, FUSED, STATES>), grid, block, dyn, s, a); break;
-        case 32: hipLaunchKernelGGL((prefill_kernel<T, N, P, 2, FUSED, STATES>), grid, block, dyn, s, a); break;
+        case 32:
+            // fused with ranks: two rows of one step per staging thread (angles taken once)
+            if (FUSED && a.R >= 2)
+                hipLaunchKernelGGL((prefill_kernel<T, N, P, 2, FUSED, STATES, true>), grid, block, dyn, s, a);
+            else
+                hipLaunchKernelGGL((prefill_kernel<T, N, P, 2, FUSED, STATES>), grid, block, dyn, s, a);
+            break;
         case 48:
             if (FUSED || STATES) return hipErrorInvalidValue;   // never split (48 does not divide 512)
             hipLaunchKernelGGL((prefill_kernel<T, N, P, 3, false>), grid, block, 0, s, a);
