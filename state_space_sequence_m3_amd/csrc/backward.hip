@@ -975,7 +975,16 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                     __sincosf(ph[q], &sn[q], &cs[q]);
                     dph[q] = 0.f;
                 }
-                float dvb[2][VE], sdot[2];
+                // With vn = v / RMS (the normalised raw row), vb = vn w + bias and dvb = R(Phi) dout
+                // (the rotation undone): the angle cotangent of a pair is dvb0 vb1 - dvb1 vb0
+                // (the rotation's derivative is the rotation by a further quarter turn, which
+                // commutes with it), and the BCNorm adjoint is dv = (w dvb - vn <w dvb, vn> / N) / RMS.
+                // The 16-bit instances take that factored form; the fp32 ones keep the earlier form
+                // (the pair cotangent from the rotated row, 1/RMS cubed on the raw row), since the
+                // factored form compiled for fp32 at N = 128, R = 4 gave wrong dB rows in the
+                // chunk's second row block, with this step's own code found correct.
+                constexpr bool kFactored = sizeof(T) == 2;
+                float dvb[2][VE], vn[2][VE], sdot[2];
 #pragma unroll
                 for (int which = 0; which < 2; ++which) {
                     const float* src = (which == 0 ? fB : fC) + ii * LDF + cC0 * VE;
@@ -987,26 +996,51 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                         dout[which][e + 2] = d4[2];
                         dout[which][e + 3] = d4[3];
                     }
-                    const float* ww = sWt + which * N + cC0 * VE;
-                    float vb[VE];
-                    norm_bias<T, VE>(v[which], inv[k][which], ww, sBias + (which * R + rC) * N + cC0 * VE, has_w, vb);
+                    const float* ww = sWt + which * N + cC0 * VE;   // 1 without weights
+                    const float* bb = sBias + (which * R + rC) * N + cC0 * VE;
+                    const float iv = inv[k][which];
                     float sd = 0.f;
+                    if constexpr (kFactored) {
 #pragma unroll
-                    for (int q = 0; q < VE / 2; ++q) {
-                        const float x0 = vb[2 * q], x1 = vb[2 * q + 1];
-                        const float o0 = fmaf(cs[q], x0, sn[q] * x1), o1 = fmaf(cs[q], x1, -sn[q] * x0);
-                        const float d0 = dout[which][2 * q], d1 = dout[which][2 * q + 1];
-                        dvb[which][2 * q] = fmaf(cs[q], d0, -sn[q] * d1);
-                        dvb[which][2 * q + 1] = fmaf(sn[q], d0, cs[q] * d1);
-                        dph[q] += fmaf(d0, o1, -d1 * o0);
-                    }
-#pragma unroll
-                    for (int e = 0; e < VE; ++e) {
-                        if (in) {
-                            accBias[which][e] += dvb[which][e];
-                            accW[which][e] = fmaf(dvb[which][e], v[which][e] * inv[k][which], accW[which][e]);
+                        for (int q = 0; q < VE / 2; ++q) {
+                            const float n0 = v[which][2 * q] * iv, n1 = v[which][2 * q + 1] * iv;
+                            vn[which][2 * q] = n0;
+                            vn[which][2 * q + 1] = n1;
+                            const float x0 = fmaf(n0, ww[2 * q], bb[2 * q]), x1 = fmaf(n1, ww[2 * q + 1], bb[2 * q + 1]);
+                            const float d0 = dout[which][2 * q], d1 = dout[which][2 * q + 1];
+                            const float e0 = fmaf(cs[q], d0, -sn[q] * d1), e1 = fmaf(sn[q], d0, cs[q] * d1);
+                            dvb[which][2 * q] = e0;
+                            dvb[which][2 * q + 1] = e1;
+                            dph[q] += fmaf(e0, x1, -e1 * x0);
                         }
-                        sd = fmaf(dvb[which][e] * ww[e], v[which][e], sd);
+#pragma unroll
+                        for (int e = 0; e < VE; ++e) {
+                            if (in) {
+                                accBias[which][e] += dvb[which][e];
+                                accW[which][e] = fmaf(dvb[which][e], vn[which][e], accW[which][e]);
+                            }
+                            sd = fmaf(dvb[which][e] * ww[e], vn[which][e], sd);
+                        }
+                    } else {
+                        float vb[VE];
+                        norm_bias<T, VE>(v[which], iv, ww, bb, has_w, vb);
+#pragma unroll
+                        for (int q = 0; q < VE / 2; ++q) {
+                            const float x0 = vb[2 * q], x1 = vb[2 * q + 1];
+                            const float o0 = fmaf(cs[q], x0, sn[q] * x1), o1 = fmaf(cs[q], x1, -sn[q] * x0);
+                            const float d0 = dout[which][2 * q], d1 = dout[which][2 * q + 1];
+                            dvb[which][2 * q] = fmaf(cs[q], d0, -sn[q] * d1);
+                            dvb[which][2 * q + 1] = fmaf(sn[q], d0, cs[q] * d1);
+                            dph[q] += fmaf(d0, o1, -d1 * o0);
+                        }
+#pragma unroll
+                        for (int e = 0; e < VE; ++e) {
+                            if (in) {
+                                accBias[which][e] += dvb[which][e];
+                                accW[which][e] = fmaf(dvb[which][e], v[which][e] * iv, accW[which][e]);
+                            }
+                            sd = fmaf(dvb[which][e] * ww[e], v[which][e], sd);
+                        }
                     }
                     sdot[which] = sd;
                 }
@@ -1019,10 +1053,17 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                 for (int which = 0; which < 2; ++which) {
                     float dv[VE];
                     if (a.bcnorm) {
-                        const float iv = inv[k][which], c3 = iv * iv * iv * invN * sdot[which];
+                        const float iv = inv[k][which];
                         const float* ww = sWt + which * N + cC0 * VE;
+                        if constexpr (kFactored) {
+                            const float sN = sdot[which] * invN;
 #pragma unroll
-                        for (int e = 0; e < VE; ++e) dv[e] = fmaf(ww[e] * iv, dvb[which][e], -c3 * v[which][e]);
+                            for (int e = 0; e < VE; ++e) dv[e] = iv * fmaf(-vn[which][e], sN, ww[e] * dvb[which][e]);
+                        } else {
+                            const float c3 = iv * iv * iv * invN * sdot[which];
+#pragma unroll
+                            for (int e = 0; e < VE; ++e) dv[e] = fmaf(ww[e] * iv, dvb[which][e], -c3 * v[which][e]);
+                        }
                     } else {
 #pragma unroll
                         for (int e = 0; e < VE; ++e) dv[e] = dvb[which][e];
