@@ -44,8 +44,8 @@ FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X fp32 (matrix and vector), TFLOP/s
 
 
 KERNEL_SOURCES = {
-    "prefill_kernel<bf16,128,64,4>": ("prefill.hip", "m3_device.h", "m3_launch.h", "m3_mma.h"),
-    "prefill_kernel<bf16,128,64,2,fused>": ("prefill.hip", "m3_device.h", "m3_launch.h", "m3_mma.h"),
+    "prefill_kernel<bf16,128,64,4>": ("prefill.hip", "m3_device.h", "m3_mapping.h", "m3_launch.h", "m3_mma.h"),
+    "prefill_kernel<bf16,128,64,2,fused>": ("prefill.hip", "m3_device.h", "m3_mapping.h", "m3_launch.h", "m3_mma.h"),
 }
 LAYER_CHUNK_ROWS = 32   # chunk * R rows per tile of the fused kernel
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_core_siso_b8_l2048_hbm_traffic.md")
