@@ -98,6 +98,9 @@ struct Shape {
     static_assert(NT % VPN == 0 && NT % VPP == 0 && RKC % R == 0 && RKX % R == 0, "staging layout");
     static_assert(NVT >= 1 && NVT * TPV <= NT && TPV <= 64 && (TPV & (TPV - 1)) == 0, "angle scan layout");
     static_assert(ALIAS <= TILES && FINAL <= TILES, "aliased LDS");
+    // the score tiles (L o S, L o dP) lie past the gradient rows: their upper triangle, zeroed once
+    // before the chunk loop, stays zero
+    static_assert(ALIAS <= OFF_M1, "score tiles outside the aliased region");
     static_assert(R == 1 || R == 2 || R == 4, "rank");
 };
 
@@ -400,6 +403,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
+    constexpr bool kAllBlocks = sizeof(T) == 4;   // see the score-tile zeroing below
     // row block rbw of the chunk (16 rows), half hf of its column work; state tiles: column group
     // cg, row group rg
     const int rbw = wave % NIB, hf = wave / NIB, cg = wave % NCG, rg = wave / NCG;
@@ -450,6 +454,15 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
         sBias[e] = bias ? bias[h * R * N + rn] : 0.f;
     }
     for (int e = tid; e < NW * 64; e += NT) pMu[e] = pLi[e] = pGam[e] = 0.f;
+    // fp32: the products that take a row block's score tiles run over every block, those above
+    // the diagonal included, which S4 never writes and which therefore hold zeros.  Skipping those
+    // blocks by a branch on the wave's row block let the compiler copy an accumulator out of its
+    // MFMA chain at the join with too few wait states on the skipping path (an 8-pass fp32 MFMA
+    // needs about ten), which then read it before the chain's last product had landed.  The bf16
+    // instances keep the branches (their compiled code has no such read; a host test scans the
+    // compiled kernels for it).
+    if constexpr (kAllBlocks)
+        for (int e = tid; e < 2 * S::SZM / 4; e += NT) ((uint32_t*)(tiles + S::OFF_M1))[e] = 0u;
 
     // ---- staging layout (B, C, state rows: vectors of rows iC0 + k RKC; x, dY: iX0 + k RKX); the
     // chunk loop derives it and its row offsets from the thread index itself, the sums after the
@@ -865,7 +878,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
         for (int pb = 0; pb < PBH; ++pb)
 #pragma unroll
             for (int ib = 0; ib < NIB; ++ib)
-                if (ib >= rbw)
+                if (kAllBlocks || ib >= rbw)   // fp32: every block (zero tiles past the triangle)
                     dxa[pb] = MM::mma(MM::ldt(sDY + (16 * ib + 4 * g) * LDX + 16 * (hf * PBH + pb), LDX, l16),
                                       MM::ldt(sM1 + (16 * ib + 4 * g) * LDM + 16 * rbw, LDM, l16), dxa[pb]);
         // dBbar^T += Cbar^T dS
@@ -873,7 +886,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
         for (int nb = 0; nb < NBH; ++nb)
 #pragma unroll
             for (int ib = 0; ib < NIB; ++ib)
-                if (ib >= rbw)
+                if (kAllBlocks || ib >= rbw)   // fp32: every block (zero tiles past the triangle)
                     dba[nb] = MM::mma(MM::ldt(sC + (16 * ib + 4 * g) * LDB + 16 * (hf * NBH + nb), LDB, l16),
                                       MM::ldt(sDS + (16 * ib + 4 * g) * LDM + 16 * rbw, LDM, l16), dba[nb]);
         // dCbar^T += Bbar^T dS^T (s blocks at or before this wave's i block)
@@ -881,7 +894,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
         for (int nb = 0; nb < NBH; ++nb)
 #pragma unroll
             for (int sb = 0; sb < NIB; ++sb)
-                if (sb <= rbw)
+                if (kAllBlocks || sb <= rbw)   // fp32: every block (zero tiles past the triangle)
                     dca[nb] = MM::mma(MM::ldt(sB + (16 * sb + 4 * g) * LDB + 16 * (hf * NBH + nb), LDB, l16),
                                       MM::ldk(sDS + wrow * LDM + 16 * sb + 4 * g), dca[nb]);
         // recomputed Y^T += X^T M1^T; mixing-weight gradient sum_t Y[t, r, p] dy[t, p]
@@ -890,7 +903,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
             for (int pb = 0; pb < PBH; ++pb) {
 #pragma unroll
                 for (int sb = 0; sb < NIB; ++sb)
-                    if (sb <= rbw)
+                    if (kAllBlocks || sb <= rbw)   // fp32: every block (zero tiles past the triangle)
                         ya[pb] = MM::mma(MM::ldt(sX + (16 * sb + 4 * g) * LDX + 16 * (hf * PBH + pb), LDX, l16),
                                          MM::ldk(sM1 + wrow * LDM + 16 * sb + 4 * g), ya[pb]);
                 float f[VE];
@@ -979,11 +992,6 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                 // (the rotation undone): the angle cotangent of a pair is dvb0 vb1 - dvb1 vb0
                 // (the rotation's derivative is the rotation by a further quarter turn, which
                 // commutes with it), and the BCNorm adjoint is dv = (w dvb - vn <w dvb, vn> / N) / RMS.
-                // The 16-bit instances take that factored form; the fp32 ones keep the earlier form
-                // (the pair cotangent from the rotated row, 1/RMS cubed on the raw row), since the
-                // factored form compiled for fp32 at N = 128, R = 4 gave wrong dB rows in the
-                // chunk's second row block, with this step's own code found correct.
-                constexpr bool kFactored = sizeof(T) == 2;
                 float dvb[2][VE], vn[2][VE], sdot[2];
 #pragma unroll
                 for (int which = 0; which < 2; ++which) {
@@ -1000,47 +1008,25 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                     const float* bb = sBias + (which * R + rC) * N + cC0 * VE;
                     const float iv = inv[k][which];
                     float sd = 0.f;
-                    if constexpr (kFactored) {
 #pragma unroll
-                        for (int q = 0; q < VE / 2; ++q) {
-                            const float n0 = v[which][2 * q] * iv, n1 = v[which][2 * q + 1] * iv;
-                            vn[which][2 * q] = n0;
-                            vn[which][2 * q + 1] = n1;
-                            const float x0 = fmaf(n0, ww[2 * q], bb[2 * q]), x1 = fmaf(n1, ww[2 * q + 1], bb[2 * q + 1]);
-                            const float d0 = dout[which][2 * q], d1 = dout[which][2 * q + 1];
-                            const float e0 = fmaf(cs[q], d0, -sn[q] * d1), e1 = fmaf(sn[q], d0, cs[q] * d1);
-                            dvb[which][2 * q] = e0;
-                            dvb[which][2 * q + 1] = e1;
-                            dph[q] += fmaf(e0, x1, -e1 * x0);
-                        }
+                    for (int q = 0; q < VE / 2; ++q) {
+                        const float n0 = v[which][2 * q] * iv, n1 = v[which][2 * q + 1] * iv;
+                        vn[which][2 * q] = n0;
+                        vn[which][2 * q + 1] = n1;
+                        const float x0 = fmaf(n0, ww[2 * q], bb[2 * q]), x1 = fmaf(n1, ww[2 * q + 1], bb[2 * q + 1]);
+                        const float d0 = dout[which][2 * q], d1 = dout[which][2 * q + 1];
+                        const float e0 = fmaf(cs[q], d0, -sn[q] * d1), e1 = fmaf(sn[q], d0, cs[q] * d1);
+                        dvb[which][2 * q] = e0;
+                        dvb[which][2 * q + 1] = e1;
+                        dph[q] += fmaf(e0, x1, -e1 * x0);
+                    }
 #pragma unroll
-                        for (int e = 0; e < VE; ++e) {
-                            if (in) {
-                                accBias[which][e] += dvb[which][e];
-                                accW[which][e] = fmaf(dvb[which][e], vn[which][e], accW[which][e]);
-                            }
-                            sd = fmaf(dvb[which][e] * ww[e], vn[which][e], sd);
+                    for (int e = 0; e < VE; ++e) {
+                        if (in) {
+                            accBias[which][e] += dvb[which][e];
+                            accW[which][e] = fmaf(dvb[which][e], vn[which][e], accW[which][e]);
                         }
-                    } else {
-                        float vb[VE];
-                        norm_bias<T, VE>(v[which], iv, ww, bb, has_w, vb);
-#pragma unroll
-                        for (int q = 0; q < VE / 2; ++q) {
-                            const float x0 = vb[2 * q], x1 = vb[2 * q + 1];
-                            const float o0 = fmaf(cs[q], x0, sn[q] * x1), o1 = fmaf(cs[q], x1, -sn[q] * x0);
-                            const float d0 = dout[which][2 * q], d1 = dout[which][2 * q + 1];
-                            dvb[which][2 * q] = fmaf(cs[q], d0, -sn[q] * d1);
-                            dvb[which][2 * q + 1] = fmaf(sn[q], d0, cs[q] * d1);
-                            dph[q] += fmaf(d0, o1, -d1 * o0);
-                        }
-#pragma unroll
-                        for (int e = 0; e < VE; ++e) {
-                            if (in) {
-                                accBias[which][e] += dvb[which][e];
-                                accW[which][e] = fmaf(dvb[which][e], v[which][e] * iv, accW[which][e]);
-                            }
-                            sd = fmaf(dvb[which][e] * ww[e], v[which][e], sd);
-                        }
+                        sd = fmaf(dvb[which][e] * ww[e], vn[which][e], sd);
                     }
                     sdot[which] = sd;
                 }
@@ -1055,15 +1041,9 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                     if (a.bcnorm) {
                         const float iv = inv[k][which];
                         const float* ww = sWt + which * N + cC0 * VE;
-                        if constexpr (kFactored) {
-                            const float sN = sdot[which] * invN;
+                        const float sN = sdot[which] * invN;
 #pragma unroll
-                            for (int e = 0; e < VE; ++e) dv[e] = iv * fmaf(-vn[which][e], sN, ww[e] * dvb[which][e]);
-                        } else {
-                            const float c3 = iv * iv * iv * invN * sdot[which];
-#pragma unroll
-                            for (int e = 0; e < VE; ++e) dv[e] = fmaf(ww[e] * iv, dvb[which][e], -c3 * v[which][e]);
-                        }
+                        for (int e = 0; e < VE; ++e) dv[e] = iv * fmaf(-vn[which][e], sN, ww[e] * dvb[which][e]);
                     } else {
 #pragma unroll
                         for (int e = 0; e < VE; ++e) dv[e] = dvb[which][e];

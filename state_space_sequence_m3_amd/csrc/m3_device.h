@@ -64,16 +64,25 @@ __device__ __forceinline__ float wave_scan_add(float v) {
     v += dpp_move<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
     return v;
 }
-// Sum over aligned groups of R lanes (R = 1, 2, 4, 8 or 16) inside each row of 16 lanes, with DPP
-// moves only: quad_perm swaps inside quads, then half-row and row mirrors, each of which pairs two
-// groups that already hold uniform partial sums.
+// Sum over aligned groups of R lanes (R = 1, 2, ..., 64): inside each row of 16 lanes with DPP
+// moves (quad_perm swaps inside quads, then half-row and row mirrors, each of which pairs two
+// groups that already hold uniform partial sums); across rows with gfx950's swaps, which applied
+// to (v, v) return both rows of a pair (v_permlane16_swap: rows (0, 0, 2, 2) and (1, 1, 3, 3);
+// v_permlane32_swap: rows (0, 1, 0, 1) and (2, 3, 2, 3)), so their sum is the pair's in every
+// lane, in VALU (no LDS crossbar), and the same value an exchange of the partners would give.
 __device__ __forceinline__ float group_sum(float v, int R) {
     if (R >= 2) v += dpp_move<0xB1, 0xf>(v);    // quad_perm [1, 0, 3, 2]
     if (R >= 4) v += dpp_move<0x4E, 0xf>(v);    // quad_perm [2, 3, 0, 1]
     if (R >= 8) v += dpp_move<0x141, 0xf>(v);   // row_half_mirror
     if (R >= 16) v += dpp_move<0x140, 0xf>(v);  // row_mirror
-    if (R >= 32) v += __shfl_xor(v, 16, 64);
-    if (R >= 64) v += __shfl_xor(v, 32, 64);
+    if (R >= 32) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+    if (R >= 64) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
     return v;
 }
 // Inclusive prefix sum inside aligned groups of W lanes (W a power of two, at most 64).  Inside a
