@@ -668,12 +668,20 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
             const float l2end = lane_value(l2, Q - 1);
             const float el = fast_exp2(l2);
             const float w = fast_exp2(fminf(l2end - l2, 0.f)) * mu;
-            const int ts = lane >> RL2;
-            rL2[lane] = shfl(l2, ts);
-            rGam[lane] = shfl(gam, ts);
-            rMu[lane] = shfl(mu, ts);
-            rEl[lane] = shfl(el, ts);
-            rW[lane] = shfl(w, ts);
+            if constexpr (R == 1) {   // row = step
+                rL2[lane] = l2;
+                rGam[lane] = gam;
+                rMu[lane] = mu;
+                rEl[lane] = el;
+                rW[lane] = w;
+            } else {                  // row s holds step s >> RL2
+                const int ts = lane >> RL2;
+                rL2[lane] = shfl(l2, ts);
+                rGam[lane] = shfl(gam, ts);
+                rMu[lane] = shfl(mu, ts);
+                rEl[lane] = shfl(el, ts);
+                rW[lane] = shfl(w, ts);
+            }
             if (lane == 0) {
                 rEnd[0] = l2end;
                 rEnd[1] = fast_exp2(l2end);
