@@ -366,12 +366,13 @@ m3_status layer_prefill(const m3_dims* d, bool packed, const int32_t* cu_seqlens
 }
 
 
-// backward pass: chunk and workspace layout (states, angles, per-(b, h) partial sums, each
-// starting on a 256-byte boundary)
+// backward pass: chunk and workspace layout (states, angles, per-(b, h) partial sums, per-chunk
+// step sums, each starting on a 256-byte boundary)
 struct BwdLayout {
     int64_t Q = 0, nchunk = 0;
     int rec = 0;
-    size_t st_bytes = 0, phi_off = 0, phi_bytes = 0, part_off = 0, part_bytes = 0, total = 0;
+    size_t st_bytes = 0, phi_off = 0, phi_bytes = 0, part_off = 0, part_bytes = 0, sc_off = 0, sc_bytes = 0;
+    size_t total = 0;
     // head groups: per-head dB and dC rows (H / G planes of the grouped layout each)
     size_t gB_off = 0, gC_off = 0, g_bytes = 0;
 };
@@ -394,7 +395,9 @@ bool bwd_layout(const m3_dims* d, BwdLayout* o) {
     o->phi_bytes = (size_t)(b * H * o->nchunk * (N / 2)) * 4;
     o->part_off = o->phi_off + round256(o->phi_bytes);
     o->part_bytes = (size_t)(b * H * o->rec) * 4;
-    o->total = o->part_off + round256(o->part_bytes);
+    o->sc_off = o->part_off + round256(o->part_bytes);
+    o->sc_bytes = (size_t)(b * H * o->nchunk * (5 * o->Q + 3)) * 4;
+    o->total = o->sc_off + round256(o->sc_bytes);
     if (kernel_groups(d) > 0) {
         o->g_bytes = (size_t)(b * d->seqlen * H * R * N) * io_size(d);
         o->gB_off = o->total;
@@ -830,6 +833,7 @@ m3_status m3_layer_backward(const m3_dims* d, const void* x, const void* B, cons
     a.ws_states = workspace;
     a.ws_phi = (float*)((char*)workspace + lay.phi_off);
     a.ws_part = (float*)((char*)workspace + lay.part_off);
+    a.ws_scal = (float*)((char*)workspace + lay.sc_off);
     a.rec = lay.rec;
     a.b = b; a.L = L; a.H = (int)H; a.N = (int)N; a.P = (int)P; a.R = (int)R;
     a.bcnorm = (d->flags & M3_BCNORM) ? 1 : 0;

@@ -33,7 +33,7 @@
 // rotated output, the RMS norm's Jacobian, and the angle's reverse prefix sum gives dtheta and the
 // rotation's share of d(dt).
 //
-// Mapping on gfx950.  Two kernels per call (plus a small reduction):
+// Mapping on gfx950.  Three kernels per call (plus a small reduction):
 //   chunk_states_kernel  one workgroup per (b, h) walks the chunks forward with the state in MFMA
 //                        accumulators (as the forward prefill does) and writes each chunk's
 //                        entry state S_in (io type, transposed [P][N]) and entry angle (fp32) to a
@@ -45,7 +45,10 @@
 //                        elementwise rotation / norm adjoint runs on the gradient tiles after they
 //                        are moved to LDS in fp32.  Per-(b, h) sums of the per-head parameters'
 //                        gradients go to the workspace and are reduced over the batch in a fixed
-//                        order (deterministic).
+//                        order (deterministic).  Each chunk's per-step sums of the scalar
+//                        gradients' terms go to the workspace too:
+//   step_grads_kernel    turns them into d(dt), d(lambda) and dA, every chunk independently, so
+//                        that serial per-step work stays off the backward kernel's chunk chain.
 #include <type_traits>
 
 #include "m3_device.h"
@@ -98,6 +101,10 @@ struct Shape {
     static_assert(NT % VPN == 0 && NT % VPP == 0 && RKC % R == 0 && RKX % R == 0, "staging layout");
     static_assert(NVT >= 1 && NVT * TPV <= NT && TPV <= 64 && (TPV & (TPV - 1)) == 0, "angle scan layout");
     static_assert(ALIAS <= TILES && FINAL <= TILES, "aliased LDS");
+    // bf16 tiles of 64- or 128-element rows are stored unpadded with their 8-byte pieces permuted
+    // per row (tile_off), which serves both the reads along K and the transposed reads without bank
+    // conflicts; the other shapes keep the padded rows above (the tile sizes cover both).
+    static constexpr bool SWZ = sizeof(T) == 2 && (N == 64 || N == 128) && P == 64 && QR == 64;
     // the score tiles (L o S, L o dP) lie past the gradient rows: their upper triangle, zeroed once
     // before the chunk loop, stays zero
     static_assert(ALIAS <= OFF_M1, "score tiles outside the aliased region");
@@ -364,6 +371,48 @@ __global__ __launch_bounds__(NIB * 64, 1) void chunk_states_kernel(BackwardArgs 
     }
 }
 
+// Element offset of (row, col) in a bf16 tile of LD = 64 or 128 elements a row, stored unpadded
+// with the row's 8-byte pieces (4 elements, col / 4) permuted by an XOR with
+//   s(row) = 4 (row % 8) + 2 (row / 8 % 2)            (128-element rows, 32 pieces: one row per
+//                                                      256-byte line of the 64 banks)
+//   s(row) = 4 (row / 2 % 4) + 2 (row / 8 % 2)        (64-element rows, 16 pieces: two rows a line)
+// The 32 lanes that one cycle serves read, along K, 16 rows x 2 pieces and, transposed, 8 rows x
+// 4 pieces (a 16-row block and a 4-piece-aligned column): both land on 32 distinct piece slots.
+// s is even, so the two pieces of a 16-byte store stay adjacent.  col is a multiple of 4.
+// Transposed 16-bit read of one lane's 4 x 16-bit piece at p (the swizzled tiles give each lane
+// its own address: the four rows a lane gathers are not a fixed stride apart).
+__device__ __forceinline__ Mma<bf16>::frag ldt_lane_bf16(const bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(lds_char*)p);
+}
+
+// Element (row, col) of a 16-bit LDS tile with LD elements per row.  Unswizzled (SWZ false) the
+// rows are padded (LD includes the padding).  Swizzled, rows are unpadded and the row's 8-byte
+// pieces (4 elements; piece q covers columns 4q .. 4q + 3) are permuted: piece q is stored at
+// q ^ s(row).  LDS has 64 four-byte banks, i.e. 32 eight-byte bank pairs; an unpadded 128-element
+// row starts on pair 0, a 64-element row on pair 0 or 16.  The products read two patterns: along
+// K (16 rows x pieces 2g', 2g' + 1 per half-wave) and transposed (8 rows x 4 consecutive pieces per
+// half-wave).  s(row) = 4 (row mod 8) + 2 ((row / 8) mod 2) for 128-element rows and
+// 4 ((row / 2) mod 4) + 2 ((row / 8) mod 2) for 64-element rows sends both patterns to 32 distinct
+// pairs, so neither conflicts; s is even, so a 16-byte write (pieces 2q', 2q' + 1) stays one
+// contiguous 16-byte store.
+template <bool SWZ, int LD>
+__device__ __forceinline__ int tile_off(int row, int col) {
+    if constexpr (!SWZ) {
+        return row * LD + col;
+    } else {
+        static_assert(LD == 64 || LD == 128, "swizzled row length");
+        const int s = LD == 128 ? 4 * (row & 7) + 2 * ((row >> 3) & 1) : 4 * ((row >> 1) & 3) + 2 * ((row >> 3) & 1);
+        return row * LD + (((col >> 2) ^ s) << 2);
+    }
+}
+// transposed fragment read of rows row0 .. row0 + 3 of each lane group (the caller's row0
+// includes 4 g), columns col0 ..
+template <bool SWZ, int LD, typename T>
+__device__ __forceinline__ typename Mma<T>::frag tile_ldt(const T* tile, int row0, int col0, int l16) {
+    if constexpr (SWZ) return ldt_lane_bf16(tile + tile_off<true, LD>(row0 + (l16 >> 2), col0 + 4 * (l16 & 3)));
+    else return Mma<T>::ldt(tile + row0 * LD + col0, LD, l16);
+}
+
 template <typename T, int N, int P, int NIB, int R, int WPB>
 __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArgs a) {
     using S = Shape<T, N, P, NIB, R, WPB>;
@@ -371,8 +420,9 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
     using F = typename MM::frag;
     constexpr int NW = S::NW, NT = S::NT, QR = S::QR, Q = S::Q, RL2 = S::RL2, NB = S::NB, PB = S::PB;
     constexpr int PBH = S::PBH, NBH = S::NBH, SCW = S::SCW, SRW = S::SRW, NCG = S::NCG;
-    constexpr int LDB = S::LDBK, LDX = S::LDXK, LDSS = S::LDSK, LDS = S::LDS, LDM = S::LDM, VE = S::VE, VPN = S::VPN,
-                  VPP = S::VPP;
+    constexpr bool SWZ = S::SWZ;   // see tile_off
+    constexpr int LDB = SWZ ? N : S::LDBK, LDX = SWZ ? P : S::LDXK, LDSS = SWZ ? N : S::LDSK, LDS = SWZ ? N : S::LDS,
+                  LDM = SWZ ? QR : S::LDM, VE = S::VE, VPN = S::VPN, VPP = S::VPP;
     constexpr int RKC = S::RKC, RKX = S::RKX, MAXC = S::MAXC, MAXX = S::MAXX, MAXS = S::MAXS;
     constexpr int K = S::K, VT = S::VT, NVT = S::NVT, TPV = S::TPV, SPT = S::SPT, LDPHI = S::LDPHI,
                   LDF = S::LDF, LDD = S::LDD;
@@ -436,8 +486,6 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
     const int64_t plane = a.ws_dB ? (int64_t)(h % (H / GS)) * a.b * L * GS * R * N : 0;
     T* dBg = (a.ws_dB ? (T*)a.ws_dB + plane : (T*)a.dB) + row_bc * R * N;
     T* dCg = (a.ws_dC ? (T*)a.ws_dC + plane : (T*)a.dC) + row_bc * R * N;
-    T* ddtg = (T*)a.ddt + row_bh;
-    T* dlamg = (T*)a.dlam + row_bh;
     T* dthg = (T*)a.dtheta + row_bh * K;
     auto tail_bytes = [&](int64_t t0, int64_t step, int64_t row) {
         return clamp_bytes(((L - t0 - 1) * step + row) * (int64_t)sizeof(T));
@@ -501,8 +549,6 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
     floatx4 accMix[PBH];
 #pragma unroll
     for (int pb = 0; pb < PBH; ++pb) accMix[pb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float dA_acc = 0.f;
-    float pend_ddt = 0.f, pend_dlam = 0.f;   // the scalar wave: gradients of the step after the chunk
 
     const float invN = 1.0f / (float)N;
     const bool has_w = a.bcnorm && (a.normw_B || a.normw_C);
@@ -638,27 +684,27 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
         for (int k = 0; k < MAXX; ++k) {
             const int i = iX0 + k * RKX;
             if (!(S::FULLX || i < QR)) continue;
-            *(uint4*)(sX + i * LDX + cX0 * VE) = rx[k];
+            *(uint4*)(sX + tile_off<SWZ, LDX>(i, cX0 * VE)) = rx[k];
             if (mix) {
                 float f[VE];
                 unpack16(ry[k], f, T{});
 #pragma unroll
                 for (int e = 0; e < VE; ++e) f[e] *= sWo[(i & (R - 1)) * P + cX0 * VE + e];
-                *(uint4*)(sDY + i * LDX + cX0 * VE) = pack16(f, T{});
+                *(uint4*)(sDY + tile_off<SWZ, LDX>(i, cX0 * VE)) = pack16(f, T{});
             } else {
-                *(uint4*)(sDY + i * LDX + cX0 * VE) = ry[k];
+                *(uint4*)(sDY + tile_off<SWZ, LDX>(i, cX0 * VE)) = ry[k];
             }
         }
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
             const int p = iC0 + k * RKC;
-            if (S::FULLS || p < P) *(uint4*)(sSt + p * LDSS + cC0 * VE) = rs[k];
+            if (S::FULLS || p < P) *(uint4*)(sSt + tile_off<SWZ, LDSS>(p, cC0 * VE)) = rs[k];
         }
 #pragma unroll
         for (int j = 0; j < SCW; ++j) {
             const int p = 16 * (cg * SCW + j) + l16;
 #pragma unroll
-            for (int i = 0; i < SRW; ++i) MM::st(sDSt + p * LDS + 16 * (rg * SRW + i) + 4 * g, MM::pack(st[j][i]));
+            for (int i = 0; i < SRW; ++i) MM::st(sDSt + tile_off<SWZ, LDS>(p, 16 * (rg * SRW + i) + 4 * g), MM::pack(st[j][i]));
         }
         const float cd = bits_to_f32(nd), cl = bits_to_f32(nl), cdn = bits_to_f32(ndn), cln = bits_to_f32(nln);
         if (wave == NW - 1) {
@@ -716,7 +762,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                     vb[2 * q] = fmaf(cs[q], x0, sn[q] * x1);
                     vb[2 * q + 1] = fmaf(cs[q], x1, -sn[q] * x0);
                 }
-                *(uint4*)((which == 0 ? sB : sC) + i * LDB + cC0 * VE) = pack16(vb, T{});
+                *(uint4*)((which == 0 ? sB : sC) + tile_off<SWZ, LDB>(i, cC0 * VE)) = pack16(vb, T{});
             }
         }
         __syncthreads();   // (2)
@@ -730,12 +776,12 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
             floatx4 sv = {0.f, 0.f, 0.f, 0.f}, dv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NB; ++kb)
-                sv = MM::mma(MM::ldk(sB + (16 * sb + l16) * LDB + 16 * kb + 4 * g),
-                             MM::ldk(sC + (16 * ib + l16) * LDB + 16 * kb + 4 * g), sv);
+                sv = MM::mma(MM::ldk(sB + tile_off<SWZ, LDB>(16 * sb + l16, 16 * kb + 4 * g)),
+                             MM::ldk(sC + tile_off<SWZ, LDB>(16 * ib + l16, 16 * kb + 4 * g)), sv);
 #pragma unroll
             for (int kb = 0; kb < PB; ++kb)
-                dv = MM::mma(MM::ldk(sX + (16 * sb + l16) * LDX + 16 * kb + 4 * g),
-                             MM::ldk(sDY + (16 * ib + l16) * LDX + 16 * kb + 4 * g), dv);
+                dv = MM::mma(MM::ldk(sX + tile_off<SWZ, LDX>(16 * sb + l16, 16 * kb + 4 * g)),
+                             MM::ldk(sDY + tile_off<SWZ, LDX>(16 * ib + l16, 16 * kb + 4 * g)), dv);
             const int i = 16 * ib + l16, s0 = 16 * sb + 4 * g;
             const int ti = i >> RL2;
             const float l2i = rL2[i], gi = rGam[i];
@@ -758,8 +804,8 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                 li = fmaf(mus[m], E, li);
                 gsum += diag ? dl : 0.f;
             }
-            MM::st(sM1 + i * LDM + s0, MM::pack(m1));
-            MM::st(sDS + i * LDM + s0, MM::pack(ds));
+            MM::st(sM1 + tile_off<SWZ, LDM>(i, s0), MM::pack(m1));
+            MM::st(sDS + tile_off<SWZ, LDM>(i, s0), MM::pack(ds));
             // row i: sums over s (m in the lane, then the four lane groups)
             li += shfl_xor(li, 16);
             li += shfl_xor(li, 32);
@@ -785,8 +831,8 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NB; ++kb)
-                acc = MM::mma(MM::ldk(sDSt + (16 * (hf * PBH + pb) + l16) * LDS + 16 * kb + 4 * g),
-                              MM::ldk(sB + wrow * LDB + 16 * kb + 4 * g), acc);
+                acc = MM::mma(MM::ldk(sDSt + tile_off<SWZ, LDS>(16 * (hf * PBH + pb) + l16, 16 * kb + 4 * g)),
+                              MM::ldk(sB + tile_off<SWZ, LDB>(wrow, 16 * kb + 4 * g)), acc);
             const float ws = rW[wrow];
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[m] *= ws;
@@ -803,9 +849,9 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < PB; ++kb)
-                    acc = MM::mma(MM::ldt(sDSt + (16 * kb + 4 * g) * LDS + 16 * nbg, LDS, l16),
-                                  MM::ldk(sX + wrow * LDX + 16 * kb + 4 * g), acc);
-                const floatx4 bv = MM::unpack(MM::ldk(sB + wrow * LDB + 16 * nbg + 4 * g));
+                    acc = MM::mma(tile_ldt<SWZ, LDS>(sDSt, 16 * kb + 4 * g, 16 * nbg, l16),
+                                  MM::ldk(sX + tile_off<SWZ, LDX>(wrow, 16 * kb + 4 * g)), acc);
+                const floatx4 bv = MM::unpack(MM::ldk(sB + tile_off<SWZ, LDB>(wrow, 16 * nbg + 4 * g)));
 #pragma unroll
                 for (int m = 0; m < 4; ++m) dw = fmaf(bv[m], acc[m], dw);
                 dba[nb] = acc;
@@ -831,9 +877,9 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < PB; ++kb)
-                    acc = MM::mma(MM::ldt(sSt + (16 * kb + 4 * g) * LDSS + 16 * nbg, LDSS, l16),
-                                  MM::ldk(sDY + wrow * LDX + 16 * kb + 4 * g), acc);
-                const floatx4 cv = MM::unpack(MM::ldk(sC + wrow * LDB + 16 * nbg + 4 * g));
+                    acc = MM::mma(tile_ldt<SWZ, LDSS>(sSt, 16 * kb + 4 * g, 16 * nbg, l16),
+                                  MM::ldk(sDY + tile_off<SWZ, LDX>(wrow, 16 * kb + 4 * g)), acc);
+                const floatx4 cv = MM::unpack(MM::ldk(sC + tile_off<SWZ, LDB>(wrow, 16 * nbg + 4 * g)));
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     acc[m] *= el;
@@ -855,8 +901,8 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NB; ++kb)
-                    acc = MM::mma(MM::ldk(sSt + (16 * (hf * PBH + pb) + l16) * LDSS + 16 * kb + 4 * g),
-                                  MM::ldk(sC + wrow * LDB + 16 * kb + 4 * g), acc);
+                    acc = MM::mma(MM::ldk(sSt + tile_off<SWZ, LDSS>(16 * (hf * PBH + pb) + l16, 16 * kb + 4 * g)),
+                                  MM::ldk(sC + tile_off<SWZ, LDB>(wrow, 16 * kb + 4 * g)), acc);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) acc[m] *= el;
                 ya[pb] = acc;
@@ -870,7 +916,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                 const int p = 16 * (cg * SCW + j) + l16;
 #pragma unroll
                 for (int i = 0; i < SRW; ++i) {
-                    const floatx4 sv = MM::unpack(MM::ldk(sSt + p * LDSS + 16 * (rg * SRW + i) + 4 * g));
+                    const floatx4 sv = MM::unpack(MM::ldk(sSt + tile_off<SWZ, LDSS>(p, 16 * (rg * SRW + i) + 4 * g)));
 #pragma unroll
                     for (int m = 0; m < 4; ++m) ss = fmaf(st[j][i][m], sv[m], ss);
                 }
@@ -887,24 +933,24 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
 #pragma unroll
             for (int ib = 0; ib < NIB; ++ib)
                 if (kAllBlocks || ib >= rbw)   // fp32: every block (zero tiles past the triangle)
-                    dxa[pb] = MM::mma(MM::ldt(sDY + (16 * ib + 4 * g) * LDX + 16 * (hf * PBH + pb), LDX, l16),
-                                      MM::ldt(sM1 + (16 * ib + 4 * g) * LDM + 16 * rbw, LDM, l16), dxa[pb]);
+                    dxa[pb] = MM::mma(tile_ldt<SWZ, LDX>(sDY, 16 * ib + 4 * g, 16 * (hf * PBH + pb), l16),
+                                      tile_ldt<SWZ, LDM>(sM1, 16 * ib + 4 * g, 16 * rbw, l16), dxa[pb]);
         // dBbar^T += Cbar^T dS
 #pragma unroll
         for (int nb = 0; nb < NBH; ++nb)
 #pragma unroll
             for (int ib = 0; ib < NIB; ++ib)
                 if (kAllBlocks || ib >= rbw)   // fp32: every block (zero tiles past the triangle)
-                    dba[nb] = MM::mma(MM::ldt(sC + (16 * ib + 4 * g) * LDB + 16 * (hf * NBH + nb), LDB, l16),
-                                      MM::ldt(sDS + (16 * ib + 4 * g) * LDM + 16 * rbw, LDM, l16), dba[nb]);
+                    dba[nb] = MM::mma(tile_ldt<SWZ, LDB>(sC, 16 * ib + 4 * g, 16 * (hf * NBH + nb), l16),
+                                      tile_ldt<SWZ, LDM>(sDS, 16 * ib + 4 * g, 16 * rbw, l16), dba[nb]);
         // dCbar^T += Bbar^T dS^T (s blocks at or before this wave's i block)
 #pragma unroll
         for (int nb = 0; nb < NBH; ++nb)
 #pragma unroll
             for (int sb = 0; sb < NIB; ++sb)
                 if (kAllBlocks || sb <= rbw)   // fp32: every block (zero tiles past the triangle)
-                    dca[nb] = MM::mma(MM::ldt(sB + (16 * sb + 4 * g) * LDB + 16 * (hf * NBH + nb), LDB, l16),
-                                      MM::ldk(sDS + wrow * LDM + 16 * sb + 4 * g), dca[nb]);
+                    dca[nb] = MM::mma(tile_ldt<SWZ, LDB>(sB, 16 * sb + 4 * g, 16 * (hf * NBH + nb), l16),
+                                      MM::ldk(sDS + tile_off<SWZ, LDM>(wrow, 16 * sb + 4 * g)), dca[nb]);
         // recomputed Y^T += X^T M1^T; mixing-weight gradient sum_t Y[t, r, p] dy[t, p]
         if (mix) {
 #pragma unroll
@@ -912,8 +958,8 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
 #pragma unroll
                 for (int sb = 0; sb < NIB; ++sb)
                     if (kAllBlocks || sb <= rbw)   // fp32: every block (zero tiles past the triangle)
-                        ya[pb] = MM::mma(MM::ldt(sX + (16 * sb + 4 * g) * LDX + 16 * (hf * PBH + pb), LDX, l16),
-                                         MM::ldk(sM1 + wrow * LDM + 16 * sb + 4 * g), ya[pb]);
+                        ya[pb] = MM::mma(tile_ldt<SWZ, LDX>(sX, 16 * sb + 4 * g, 16 * (hf * PBH + pb), l16),
+                                         MM::ldk(sM1 + tile_off<SWZ, LDM>(wrow, 16 * sb + 4 * g)), ya[pb]);
                 float f[VE];
                 unpack16(dyv[pb], f, T{});
 #pragma unroll
@@ -929,7 +975,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                 F yb[NIB];
 #pragma unroll
                 for (int ib = 0; ib < NIB; ++ib) {
-                    floatx4 yv = MM::unpack(MM::ldt(sDY + (16 * ib + 4 * g) * LDX + 16 * pb, LDX, l16));
+                    floatx4 yv = MM::unpack(tile_ldt<SWZ, LDX>(sDY, 16 * ib + 4 * g, 16 * pb, l16));
                     const floatx4 el = *(const floatx4*)(rEl + 16 * ib + 4 * g);
 #pragma unroll
                     for (int m = 0; m < 4; ++m) yv[m] *= el[m];
@@ -942,7 +988,7 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
                     for (int m = 0; m < 4; ++m) st[j][i][m] *= dec;
 #pragma unroll
                     for (int ib = 0; ib < NIB; ++ib)
-                        st[j][i] = MM::mma(MM::ldt(sC + (16 * ib + 4 * g) * LDB + 16 * nb, LDB, l16), yb[ib], st[j][i]);
+                        st[j][i] = MM::mma(tile_ldt<SWZ, LDB>(sC, 16 * ib + 4 * g, 16 * nb, l16), yb[ib], st[j][i]);
                 }
             }
         }
@@ -1113,81 +1159,44 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
         }
         __syncthreads();   // (7)
 
-        // ================= S9: per-step scalar gradients (last wave, lane = step) ======
-        if (wave == NW - 1) {
-            const bool live = lane < Q;
-            float MU = 0.f, DW = 0.f, GM = 0.f, LI = 0.f;
-            if (live) {
+        // ================= S9: per-step sums of the chunk's row partials -> workspace =====
+        // record [MU, GM, LI, DW, ROT][step], then ss: the per-step scalar gradients that need
+        // them run afterwards in step_grads_kernel, off this kernel's chunk chain.  Each thread
+        // zeroes the partials it read for the next chunk.
+        {
+            float* rec = a.ws_scal + (bh * nchunk + c) * (5 * Q + 3);
+            for (int e = tid; e <= 5 * Q; e += NT) {
+                const int k = e / Q, s = e - k * Q;
+                float acc = 0.f;
+                if (k == 5) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int row = lane * R + r;
+                    for (int w = 0; w < NW; ++w) acc += pSS[w];
+                } else if (k == 4) {
 #pragma unroll
-                    for (int w = 0; w < NW; ++w) {
-                        MU += pMu[w * 64 + row];
-                        GM += pGam[w * 64 + row];
-                        LI += pLi[w * 64 + row];
-                    }
+                    for (int v2 = 0; v2 < NVT; ++v2) acc += rotdd[v2 * 64 + s];
+                } else {
 #pragma unroll
-                    for (int hh = 0; hh < WPB; ++hh) {
-                        DW += rDw[hh * 64 + row];
-                        LI += rDlo[hh * 64 + row];
+                    for (int r = 0; r < R; ++r) {
+                        const int row = s * R + r;
+                        if (k == 3) {
+#pragma unroll
+                            for (int hh = 0; hh < WPB; ++hh) acc += rDw[hh * 64 + row];
+                        } else {
+                            float* part = k == 0 ? pMu : k == 1 ? pGam : pLi;
+#pragma unroll
+                            for (int w = 0; w < NW; ++w) {
+                                acc += part[w * 64 + row];
+                                part[w * 64 + row] = 0.f;
+                            }
+                            if (k == 2) {
+#pragma unroll
+                                for (int hh = 0; hh < WPB; ++hh) acc += rDlo[hh * 64 + row];
+                            }
+                        }
                     }
                 }
+                rec[e] = acc;
             }
-            const float d = live ? cd : 0.f, lm = live ? cl : 0.f;
-            const float l2 = rL2[lane * R < 64 ? lane * R : 0];
-            const float mu = live ? rMu[lane * R] : 0.f, wv = live ? rW[lane * R] : 0.f;
-            const float ed = live ? fast_exp2(fminf(rEnd[0] - l2, 0.f)) : 0.f;
-            const float dmu = MU + ed * DW;
-            float dl = LI - mu * MU - wv * DW;
-            float lend = wave_scan_add(wv * DW);   // sum_s w_s dw_s (inclusive; lane 63 = total)
-            lend = lane_value(lend, 63);
-            float ss = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) ss += pSS[w];
-            lend += rEnd[1] * ss;
-            if (lane == Q - 1) dl += lend;
-            dl = live ? dl : 0.f;
-            const float pre = wave_scan_add(dl);
-            const float suf = lane_value(pre, 63) - pre + dl;
-            float rot = 0.f;
-            if (live) {
-#pragma unroll
-                for (int v2 = 0; v2 < NVT; ++v2) rot += rotdd[v2 * 64 + lane];
-            }
-            const float gsum = GM + dmu;
-            const float dmu_prev = shfl_up(dmu, 1);
-            float ddt = fmaf(A, suf, fmaf(lm, gsum, rot));
-            float dlam = d * gsum;
-            if (lane >= 1) {
-                ddt = fmaf(1.0f - lm, dmu_prev, ddt);
-                dlam = fmaf(-d, dmu_prev, dlam);
-            }
-            dA_acc = fmaf(d, suf, dA_acc);
-            // mu of the chunk's last step reaches the next step (first step of chunk c + 1)
-            const float dmu_last = lane_value(dmu, Q - 1);
-            const float lam_n = lane_value(cln, Q - 1), dt_n = lane_value(cdn, Q - 1);
-            pend_ddt = fmaf(1.0f - lam_n, dmu_last, pend_ddt);
-            pend_dlam = fmaf(-dt_n, dmu_last, pend_dlam);
-            const rsrc_t dDo = make_rsrc(ddtg + t0 * H, tail_bytes(t0, H, 1));
-            const rsrc_t dLo = make_rsrc(dlamg + t0 * H, tail_bytes(t0, H, 1));
-            // lanes 1..Q-1 store their steps; lane 0 stores the pending step t0 + Q (when the
-            // sequence has it) and its own step becomes the pending one
-            const bool st_now = lane == 0 ? c + 1 < nchunk : lane < Q;
-            const float vd = lane == 0 ? pend_ddt : ddt, vl = lane == 0 ? pend_dlam : dlam;
-            const uint32_t off = st_now ? (uint32_t)((lane == 0 ? Q : lane) * H * (int)sizeof(T)) : 0x80000000u;
-            if constexpr (sizeof(T) == 2) {
-                __builtin_amdgcn_raw_buffer_store_b16(bf16_bits_rne(vd), dDo, (int)off, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b16(bf16_bits_rne(vl), dLo, (int)off, 0, 0);
-            } else {
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vd), dDo, (int)off, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vl), dLo, (int)off, 0, 0);
-            }
-            pend_ddt = lane_value(ddt, 0);
-            pend_dlam = lane_value(dlam, 0);
-            // partial arrays start from zero for the next chunk
-#pragma unroll
-            for (int w = 0; w < NW; ++w) pMu[w * 64 + lane] = pLi[w * 64 + lane] = pGam[w * 64 + lane] = 0.f;
         }
     }
 
@@ -1242,16 +1251,9 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
         for (int e = tid; e < R * N; e += NT)
             if (a.dBbar_prev) ((T*)a.dBbar_prev)[bh * R * N + e] = T{};
     }
-    if (wave == NW - 1) {
-        if (L > 0 && lane == 0) {
-            // step 0: c_0 = (1 - lambda_0) dt_0 weighs the carried-in input
-            const float d0 = load_f32(dtg), l0 = load_f32(lamg);
-            ddtg[0] = from_f32<T>(fmaf(1.0f - l0, dc0, pend_ddt));
-            dlamg[0] = from_f32<T>(fmaf(-d0, dc0, pend_dlam));
-        }
-        const float dA_tot = group_sum(dA_acc, 64);
-        if (lane == 0) a.ws_part[bh * a.rec] = dA_tot;
-    }
+    // the carried-in input's share of mu's gradient before step 0 (c_0 = (1 - lambda_0) dt_0
+    // weighs it), for step_grads_kernel: slot 5 Q + 1 of the first chunk's record
+    if (tid == 0 && nchunk > 0) a.ws_scal[bh * nchunk * (5 * Q + 3) + 5 * Q + 1] = dc0;
     // angle cotangent before the first step
     if (scanner && tj == 0) {
 #pragma unroll
@@ -1314,16 +1316,137 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
     }
 }
 
-// Sums of the per-(b, h) partial records over the batch, in batch order.
-__global__ __launch_bounds__(256) void reduce_partials_kernel(BackwardArgs a) {
+// Per-step scalar gradients d(dt) and d(lambda) and each chunk's share of dA, from the step sums
+// the backward kernel leaves per chunk (record [MU, GM, LI, DW, ROT][Q], ss, and in the first
+// chunk's record the carried-in input's dmu before step 0).  For each step t of a chunk:
+//   dmu_t  = MU_t + exp(l_end - l_t) DW_t
+//   dl_t   = LI_t - mu_t MU_t - w_t DW_t  (+ sum_s w_s DW_s + exp(l_end) ss at the last step)
+//   d(dt)_t  = A sum_{t' >= t} dl_t' + lambda_t (GM_t + dmu_t) + ROT_t + (1 - lambda_t) dmu_{t-1}
+//   dlam_t   = dt_t (GM_t + dmu_t) - dt_t dmu_{t-1}
+//   dA_chunk = sum_t dt_t sum_{t' >= t} dl_t'
+// with l_t, mu_t and w_t recomputed from dt, lambda and A as the backward kernel forms them.  The
+// previous step's dmu comes from the lane below; for a chunk's first step from the previous
+// chunk's last step (whose decay to its chunk end is exp(0) = 1), or, at step 0, the carried-in
+// input's.  No chunk depends on another's result.  One workgroup per (chunk, block of 64 heads,
+// batch): dt and lambda of the chunk's steps (and the step after) for the 64 heads are read as
+// whole rows into LDS, each of the 16 waves takes 4 heads (lane = step; their record values
+// loaded first) and writes its gradients back over its heads' columns, and the gradient rows are
+// stored whole: per-head columns would
+// read and write 2-byte pieces of lines that 64 workgroups share.  The dA share goes to slot
+// 5 Q + 2 of the chunk's record; reduce_partials_kernel adds the shares.
+constexpr int kStepWaves = 16;
+
+template <typename T>
+__global__ __launch_bounds__(64 * kStepWaves) void step_grads_kernel(BackwardArgs a, int Q) {
+    extern __shared__ float step_tiles[];   // dt, lambda: [Q + 1][64] each
+    float* sd = step_tiles;
+    float* sl = step_tiles + (Q + 1) * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t c = blockIdx.x, b = blockIdx.z;
+    const int hb = (int)blockIdx.y * 64, H = a.H;
+    const int64_t L = a.L, nchunk = (L + Q - 1) / Q, t0 = c * Q;
+    const int REC = 5 * Q + 3;
+    const T* dtg = (const T*)a.dt + b * L * H;
+    const T* lamg = (const T*)a.lam + b * L * H;
+    const bool live = lane < Q;
+    // the wave's heads j = wave + 16 k: their record values are loaded for all four heads first
+    constexpr int HPW = 64 / kStepWaves;
+    float MU[HPW], GM[HPW], LI[HPW], DW[HPW], ROT[HPW], SS[HPW], PREV[HPW];
+#pragma unroll
+    for (int k = 0; k < HPW; ++k) {
+        const int h = hb + wave + kStepWaves * k;
+        const bool on = h < H;
+        const float* rec = a.ws_scal + ((b * H + (on ? h : 0)) * nchunk + c) * REC;
+        MU[k] = on && live ? rec[lane] : 0.f;
+        GM[k] = on && live ? rec[Q + lane] : 0.f;
+        LI[k] = on && live ? rec[2 * Q + lane] : 0.f;
+        DW[k] = on && live ? rec[3 * Q + lane] : 0.f;
+        ROT[k] = on && live ? rec[4 * Q + lane] : 0.f;
+        SS[k] = on ? rec[5 * Q] : 0.f;
+        PREV[k] = !on ? 0.f : c > 0 ? rec[Q - 1 - REC] + rec[4 * Q - 1 - REC] : rec[5 * Q + 1];
+    }
+    for (int e = tid; e < (Q + 1) * 64; e += 64 * kStepWaves) {
+        const int st = e >> 6, j = e & 63;
+        const int64_t t = t0 + st;
+        const bool in = t < L && hb + j < H;
+        sd[e] = in ? load_f32(dtg + t * H + hb + j) : 0.f;
+        sl[e] = in ? load_f32(lamg + t * H + hb + j) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < HPW; ++k) {
+        const int j = wave + kStepWaves * k, h = hb + j;
+        if (h >= H) break;
+        const float A = a.A[h], Alog2 = A * kLog2e;
+        const float cd = live ? sd[lane * 64 + j] : 0.f, cl = live ? sl[lane * 64 + j] : 0.f;
+        const float cdn = live ? sd[(lane + 1) * 64 + j] : 0.f, cln = live ? sl[(lane + 1) * 64 + j] : 0.f;
+        const float l2 = wave_scan_add(cd * Alog2);
+        const float gam = cl * cd;
+        const float mu = gam + (1.0f - cln) * cdn;
+        const float l2end = lane_value(l2, Q - 1);
+        const float ed = live ? fast_exp2(fminf(l2end - l2, 0.f)) : 0.f;
+        const float wv = ed * mu;
+        const float dmu = MU[k] + ed * DW[k];
+        float dl = LI[k] - mu * MU[k] - wv * DW[k];
+        const float lend = lane_value(wave_scan_add(wv * DW[k]), 63) + fast_exp2(l2end) * SS[k];
+        if (lane == Q - 1) dl += lend;
+        dl = live ? dl : 0.f;
+        const float pre = wave_scan_add(dl);
+        const float suf = lane_value(pre, 63) - pre + dl;
+        const float gsum = GM[k] + dmu;
+        const float up = shfl_up(dmu, 1);
+        const float prev = lane == 0 ? PREV[k] : up;
+        float ddt = fmaf(A, suf, fmaf(cl, gsum, ROT[k]));
+        float dlam = cd * gsum;
+        ddt = fmaf(1.0f - cl, prev, ddt);
+        dlam = fmaf(-cd, prev, dlam);
+        const float dA = group_sum(cd * suf, 64);
+        if (lane == 0) a.ws_scal[((b * H + h) * nchunk + c) * REC + 5 * Q + 2] = dA;
+        if (live) {   // this wave's own column: read above, by this lane
+            sd[lane * 64 + j] = ddt;
+            sl[lane * 64 + j] = dlam;
+        }
+    }
+    __syncthreads();
+    T* ddtg = (T*)a.ddt + b * L * H;
+    T* dlamg = (T*)a.dlam + b * L * H;
+    for (int e = tid; e < Q * 64; e += 64 * kStepWaves) {
+        const int st = e >> 6, j = e & 63;
+        const int64_t t = t0 + st;
+        if (t < L && hb + j < H) {
+            ddtg[t * H + hb + j] = from_f32<T>(sd[e]);
+            dlamg[t * H + hb + j] = from_f32<T>(sl[e]);
+        }
+    }
+}
+
+// Sums of the per-(b, h) partial records over the batch, in batch order; dA from the per-chunk
+// shares (thread j adds shares j, j + 256, ... of the (batch, chunk) list, then a fixed tree over
+// the threads: the same order on every run).
+__global__ __launch_bounds__(256) void reduce_partials_kernel(BackwardArgs a, int Q) {
     const int h = blockIdx.x;
     const int R = a.R, P = a.P, N = a.N;
-    for (int e = threadIdx.x; e < a.rec; e += 256) {
+    {
+        __shared__ float red[256];
+        const int64_t nchunk = (a.L + Q - 1) / Q, n = a.b * nchunk;
+        const int REC = 5 * Q + 3;
+        float acc = 0.f;
+        for (int64_t i = threadIdx.x; i < n; i += 256) {
+            const int64_t bb = i / nchunk, cc = i - bb * nchunk;
+            acc += a.ws_scal[((bb * a.H + h) * nchunk + cc) * REC + 5 * Q + 2];
+        }
+        red[threadIdx.x] = acc;
+        __syncthreads();
+        for (int w = 128; w > 0; w >>= 1) {
+            if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) a.dA[h] = red[0];
+    }
+    for (int e = threadIdx.x + 1; e < a.rec; e += 256) {
         float acc = 0.f;
         for (int64_t b = 0; b < a.b; ++b) acc += a.ws_part[(b * a.H + h) * a.rec + e];
-        if (e == 0) {
-            a.dA[h] = acc;
-        } else if (e < 1 + R * P) {
+        if (e < 1 + R * P) {
             if (a.dw_out) a.dw_out[h * R * P + (e - 1)] = acc;
         } else if (e < 1 + R * P + 2 * N) {
             const int f = e - 1 - R * P;
@@ -1368,6 +1491,7 @@ template <int N, int P> constexpr int backward_wpb() { return (N / 16) % 2 == 0 
 template <typename T, int N, int P, int NIB, int R>
 hipError_t launch_nipr(const BackwardArgs& a, bool states_only, hipStream_t s) {
     const dim3 grid((unsigned)(a.b * a.H)), block(NIB * 64);
+    if (!states_only && a.b > 65535) return hipErrorInvalidValue;   // step_grads_kernel's grid z
     hipLaunchKernelGGL((chunk_states_kernel<T, N, P, NIB, R>), grid, block, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || states_only) return e;
@@ -1375,7 +1499,15 @@ hipError_t launch_nipr(const BackwardArgs& a, bool states_only, hipStream_t s) {
     hipLaunchKernelGGL((backward_kernel<T, N, P, NIB, R, WPB>), grid, dim3(NIB * WPB * 64), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)a.H), dim3(256), 0, s, a);
+    constexpr int Q = Shape<T, N, P, NIB, R, WPB>::Q;
+    const int64_t nchunk = (a.L + Q - 1) / Q;
+    if (nchunk > 0) {
+        const dim3 sgrid((unsigned)nchunk, (unsigned)((a.H + 63) / 64), (unsigned)a.b);
+        hipLaunchKernelGGL(step_grads_kernel<T>, sgrid, dim3(64 * kStepWaves), 2 * (Q + 1) * 64 * sizeof(float), s, a, Q);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)a.H), dim3(256), 0, s, a, Q);
     e = hipGetLastError();
     const int64_t vecs = a.ws_dB ? a.b * a.L * a.G * R * N / (16 / (int64_t)sizeof(T)) : 0;
     if (e != hipSuccess || vecs == 0) return e;

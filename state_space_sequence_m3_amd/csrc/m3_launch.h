@@ -155,10 +155,12 @@ struct BackwardArgs {
     void* dBbar_prev;
     void* dx_prev;
     // workspace: chunk-entry states [b, H, nchunk, P, N] (io type), entry angles
-    // [b, H, nchunk, N/2], per-(b, h) partial sums [b, H, rec]
+    // [b, H, nchunk, N/2], per-(b, h) partial sums [b, H, rec], per-chunk step sums and dA share
+    // [b, H, nchunk, 5 Q + 3] (f32; see step_grads_kernel)
     void* ws_states;
     float* ws_phi;
     float* ws_part;
+    float* ws_scal;
     int rec;              // 1 + R P + 2 N + 2 R N
     int64_t b, L;
     int H, N, P, R;

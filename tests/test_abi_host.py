@@ -302,12 +302,14 @@ def test_layer_backward_sizes():
     assert m3scan.layer_backward_chunk(_dims(rank=4)) == 16
     assert m3scan.layer_backward_chunk(_dims(io=m3scan.M3_F32)) == 32
     assert m3scan.layer_backward_chunk(_dims(rank=8)) == 0
-    # states (3 chunks) + angles + per-(b, h) partial sums, each rounded up to 256 bytes
+    # states (3 chunks) + angles + per-(b, h) partial sums + per-chunk step sums (5 per step and
+    # 3 per chunk), each rounded up to 256 bytes
     st = 2 * 3 * 3 * 64 * 128 * 2
     ph = 2 * 3 * 3 * 64 * 4
     part = 2 * 3 * (1 + 64 + 2 * 128 + 2 * 128) * 4
+    steps = 2 * 3 * 3 * (5 * 64 + 3) * 4
     r = lambda n: (n + 255) // 256 * 256
-    assert m3scan.layer_backward_workspace_bytes(d) == r(st) + r(ph) + r(part)
+    assert m3scan.layer_backward_workspace_bytes(d) == r(st) + r(ph) + r(part) + r(steps)
     assert m3scan.layer_backward_workspace_bytes(_dims(rank=8)) == 0
 
 

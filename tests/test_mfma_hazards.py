@@ -11,7 +11,10 @@ follows the fall-through and taken-branch paths to the first instruction that us
 registers (other than a dependent MFMA taking them as its accumulator, which the hardware orders).
 Each opcode's required distance is taken from the compiler's own choice on paths without a taken
 branch (the smallest distance it leaves there); a path through a taken branch that is shorter
-fails.  No GPU is needed.
+fails.  A path on which the execution mask is known to be zero (an s_cbranch_execz taken, or an
+s_cbranch_execnz not taken, and no write of exec since) runs VALU instructions on no lanes, so
+those are not uses there; instructions that ignore the mask (MFMA, v_readlane, v_readfirstlane,
+v_writelane) still are.  No GPU is needed.
 """
 from __future__ import annotations
 
@@ -87,6 +90,13 @@ def _use(op, ops, dst):
     return None
 
 
+_EXEC_FREE = ("v_mfma", "v_readlane", "v_readfirstlane", "v_writelane")   # run whatever exec holds
+
+
+def _writes_exec(op, ops):
+    return "saveexec" in op or (op.startswith("s_") and bool(ops) and ops[0] == "exec")
+
+
 def _distances(ins, labels):
     """(mfma opcode, distance, through a taken branch) for each MFMA and each path to a use."""
     found = []
@@ -94,9 +104,9 @@ def _distances(ins, labels):
         if not op.startswith("v_mfma"):
             continue
         dst = _regs(ops[0])
-        stack = [(i + 1, 0, False, frozenset())]
+        stack = [(i + 1, 0, False, False, frozenset())]
         while stack:
-            k, dist, taken, seen = stack.pop()
+            k, dist, taken, exec_zero, seen = stack.pop()
             while k < len(ins) and dist < WINDOW:
                 o, oo = ins[k]
                 if o == "s_endpgm":
@@ -106,16 +116,23 @@ def _distances(ins, labels):
                     k += 1
                     continue
                 u = _use(o, oo, dst)
+                if u == "use" and exec_zero and not o.startswith(_EXEC_FREE):
+                    u = None   # no lane runs it
                 if u == "use":
                     found.append((op, dist, taken))
                 if u is not None:
                     break
+                if _writes_exec(o, oo):
+                    exec_zero = False
                 if o.startswith("s_cbranch") or o == "s_branch":
                     tgt = labels.get(oo[0]) if oo else None
                     if tgt is not None and (k, tgt) not in seen:
-                        stack.append((tgt, dist + 1, True, seen | {(k, tgt)}))
+                        stack.append((tgt, dist + 1, True, exec_zero or o == "s_cbranch_execz",
+                                      seen | {(k, tgt)}))
                     if o == "s_branch":
                         break
+                    if o == "s_cbranch_execnz":
+                        exec_zero = True   # falling through: exec is zero
                 dist += 1
                 k += 1
     return found
