@@ -41,6 +41,9 @@ BWD_CASES = [
     ("bf16", 2, 129, 2, 64, 128, 1, False, False, False, False, False),  # no BCNorm, no bias
     ("bf16", 1, 200, 2, 64, 64, 1, True, True, True, False, True),     # N = 64
     ("bf16", 1, 40, 2, 64, 128, 1, True, True, True, False, True),     # shorter than one chunk
+    # more than 64 heads: the per-step gradients run per block of 64 heads (a partial second one)
+    ("f32", 1, 70, 66, 16, 16, 1, True, True, True, False, True),
+    ("bf16", 2, 100, 65, 64, 64, 1, True, True, True, False, True),
 ]
 
 
