@@ -1351,33 +1351,50 @@ __global__ __launch_bounds__(64 * kStepWaves) void step_grads_kernel(BackwardArg
     const bool live = lane < Q;
     // the wave's heads j = wave + 16 k: their record values are loaded for all four heads first
     constexpr int HPW = 64 / kStepWaves;
-    float MU[HPW], GM[HPW], LI[HPW], DW[HPW], ROT[HPW], SS[HPW], PREV[HPW];
+    float MU[HPW], GM[HPW], LI[HPW], DW[HPW], ROT[HPW], SS[HPW], PA[HPW], PB[HPW], AH[HPW];
+    const int ls = live ? lane : 0;   // every load in bounds; lanes past the chunk are masked at use
 #pragma unroll
     for (int k = 0; k < HPW; ++k) {
         const int h = hb + wave + kStepWaves * k;
-        const bool on = h < H;
-        const float* rec = a.ws_scal + ((b * H + (on ? h : 0)) * nchunk + c) * REC;
-        MU[k] = on && live ? rec[lane] : 0.f;
-        GM[k] = on && live ? rec[Q + lane] : 0.f;
-        LI[k] = on && live ? rec[2 * Q + lane] : 0.f;
-        DW[k] = on && live ? rec[3 * Q + lane] : 0.f;
-        ROT[k] = on && live ? rec[4 * Q + lane] : 0.f;
-        SS[k] = on ? rec[5 * Q] : 0.f;
-        PREV[k] = !on ? 0.f : c > 0 ? rec[Q - 1 - REC] + rec[4 * Q - 1 - REC] : rec[5 * Q + 1];
+        const float* rec = a.ws_scal + ((b * H + (h < H ? h : 0)) * nchunk + c) * REC;
+        AH[k] = a.A[h < H ? h : 0];
+        MU[k] = rec[ls];
+        GM[k] = rec[Q + ls];
+        LI[k] = rec[2 * Q + ls];
+        DW[k] = rec[3 * Q + ls];
+        ROT[k] = rec[4 * Q + ls];
+        SS[k] = rec[5 * Q];
+        PA[k] = c > 0 ? rec[Q - 1 - REC] : rec[5 * Q + 1];
+        PB[k] = c > 0 ? rec[4 * Q - 1 - REC] : 0.f;
     }
-    for (int e = tid; e < (Q + 1) * 64; e += 64 * kStepWaves) {
-        const int st = e >> 6, j = e & 63;
+    // the dt and lambda rows (at most 65 x 64 values: Q <= 64), all loads issued before any use
+    constexpr int TL = (65 * 64 + 64 * kStepWaves - 1) / (64 * kStepWaves);
+    typedef typename IoBits<T>::type Bits;
+    Bits vd[TL], vl[TL];
+    bool vin[TL];
+#pragma unroll
+    for (int i = 0; i < TL; ++i) {   // unconditional loads of in-bounds addresses, masked below
+        const int e = tid + i * 64 * kStepWaves, st = e >> 6, j = e & 63;
         const int64_t t = t0 + st;
-        const bool in = t < L && hb + j < H;
-        sd[e] = in ? load_f32(dtg + t * H + hb + j) : 0.f;
-        sl[e] = in ? load_f32(lamg + t * H + hb + j) : 0.f;
+        vin[i] = e < (Q + 1) * 64 && t < L && hb + j < H;
+        const int64_t o = vin[i] ? t * H + hb + j : 0;
+        vd[i] = *(const Bits*)(dtg + o);
+        vl[i] = *(const Bits*)(lamg + o);
+    }
+#pragma unroll
+    for (int i = 0; i < TL; ++i) {
+        const int e = tid + i * 64 * kStepWaves;
+        if (e < (Q + 1) * 64) {
+            sd[e] = vin[i] ? bits_to_f32(vd[i]) : 0.f;
+            sl[e] = vin[i] ? bits_to_f32(vl[i]) : 0.f;
+        }
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < HPW; ++k) {
         const int j = wave + kStepWaves * k, h = hb + j;
         if (h >= H) break;
-        const float A = a.A[h], Alog2 = A * kLog2e;
+        const float A = AH[k], Alog2 = A * kLog2e;
         const float cd = live ? sd[lane * 64 + j] : 0.f, cl = live ? sl[lane * 64 + j] : 0.f;
         const float cdn = live ? sd[(lane + 1) * 64 + j] : 0.f, cln = live ? sl[(lane + 1) * 64 + j] : 0.f;
         const float l2 = wave_scan_add(cd * Alog2);
@@ -1386,17 +1403,19 @@ __global__ __launch_bounds__(64 * kStepWaves) void step_grads_kernel(BackwardArg
         const float l2end = lane_value(l2, Q - 1);
         const float ed = live ? fast_exp2(fminf(l2end - l2, 0.f)) : 0.f;
         const float wv = ed * mu;
-        const float dmu = MU[k] + ed * DW[k];
-        float dl = LI[k] - mu * MU[k] - wv * DW[k];
-        const float lend = lane_value(wave_scan_add(wv * DW[k]), 63) + fast_exp2(l2end) * SS[k];
+        const float mu_s = live ? MU[k] : 0.f, gm_s = live ? GM[k] : 0.f, li_s = live ? LI[k] : 0.f;
+        const float dw_s = live ? DW[k] : 0.f, rot_s = live ? ROT[k] : 0.f;
+        const float dmu = mu_s + ed * dw_s;
+        float dl = li_s - mu * mu_s - wv * dw_s;
+        const float lend = lane_value(wave_scan_add(wv * dw_s), 63) + fast_exp2(l2end) * SS[k];
         if (lane == Q - 1) dl += lend;
         dl = live ? dl : 0.f;
         const float pre = wave_scan_add(dl);
         const float suf = lane_value(pre, 63) - pre + dl;
-        const float gsum = GM[k] + dmu;
+        const float gsum = gm_s + dmu;
         const float up = shfl_up(dmu, 1);
-        const float prev = lane == 0 ? PREV[k] : up;
-        float ddt = fmaf(A, suf, fmaf(cl, gsum, ROT[k]));
+        const float prev = lane == 0 ? PA[k] + PB[k] : up;
+        float ddt = fmaf(A, suf, fmaf(cl, gsum, rot_s));
         float dlam = cd * gsum;
         ddt = fmaf(1.0f - cl, prev, ddt);
         dlam = fmaf(-cd, prev, dlam);
@@ -1431,6 +1450,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(BackwardArgs a, in
         const int64_t nchunk = (a.L + Q - 1) / Q, n = a.b * nchunk;
         const int REC = 5 * Q + 3;
         float acc = 0.f;
+#pragma unroll 4
         for (int64_t i = threadIdx.x; i < n; i += 256) {
             const int64_t bb = i / nchunk, cc = i - bb * nchunk;
             acc += a.ws_scal[((bb * a.H + h) * nchunk + cc) * REC + 5 * Q + 2];
@@ -1445,6 +1465,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(BackwardArgs a, in
     }
     for (int e = threadIdx.x + 1; e < a.rec; e += 256) {
         float acc = 0.f;
+#pragma unroll 8
         for (int64_t b = 0; b < a.b; ++b) acc += a.ws_part[(b * a.H + h) * a.rec + e];
         if (e < 1 + R * P) {
             if (a.dw_out) a.dw_out[h * R * P + (e - 1)] = acc;
