@@ -1334,13 +1334,15 @@ __global__ __launch_bounds__(NIB * WPB * 64, 1) void backward_kernel(BackwardArg
 // stored whole: per-head columns would
 // read and write 2-byte pieces of lines that 64 workgroups share.  The dA share goes to slot
 // 5 Q + 2 of the chunk's record; reduce_partials_kernel adds the shares.
-constexpr int kStepWaves = 16;
+constexpr int kStepWaves = 16, kStepLd = 65;
 
 template <typename T>
 __global__ __launch_bounds__(64 * kStepWaves) void step_grads_kernel(BackwardArgs a, int Q) {
-    extern __shared__ float step_tiles[];   // dt, lambda: [Q + 1][64] each
+    // dt, lambda: [Q + 1][65] each (rows of 65 floats: a head's column, read with lane = step,
+    // then falls in 64 different banks; rows of 64 would put the whole column in one bank)
+    extern __shared__ float step_tiles[];
     float* sd = step_tiles;
-    float* sl = step_tiles + (Q + 1) * 64;
+    float* sl = step_tiles + (Q + 1) * kStepLd;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t c = blockIdx.x, b = blockIdx.z;
     const int hb = (int)blockIdx.y * 64, H = a.H;
@@ -1385,8 +1387,9 @@ __global__ __launch_bounds__(64 * kStepWaves) void step_grads_kernel(BackwardArg
     for (int i = 0; i < TL; ++i) {
         const int e = tid + i * 64 * kStepWaves;
         if (e < (Q + 1) * 64) {
-            sd[e] = vin[i] ? bits_to_f32(vd[i]) : 0.f;
-            sl[e] = vin[i] ? bits_to_f32(vl[i]) : 0.f;
+            const int o = (e >> 6) * kStepLd + (e & 63);
+            sd[o] = vin[i] ? bits_to_f32(vd[i]) : 0.f;
+            sl[o] = vin[i] ? bits_to_f32(vl[i]) : 0.f;
         }
     }
     __syncthreads();
@@ -1395,8 +1398,8 @@ __global__ __launch_bounds__(64 * kStepWaves) void step_grads_kernel(BackwardArg
         const int j = wave + kStepWaves * k, h = hb + j;
         if (h >= H) break;
         const float A = AH[k], Alog2 = A * kLog2e;
-        const float cd = live ? sd[lane * 64 + j] : 0.f, cl = live ? sl[lane * 64 + j] : 0.f;
-        const float cdn = live ? sd[(lane + 1) * 64 + j] : 0.f, cln = live ? sl[(lane + 1) * 64 + j] : 0.f;
+        const float cd = live ? sd[lane * kStepLd + j] : 0.f, cl = live ? sl[lane * kStepLd + j] : 0.f;
+        const float cdn = live ? sd[(lane + 1) * kStepLd + j] : 0.f, cln = live ? sl[(lane + 1) * kStepLd + j] : 0.f;
         const float l2 = wave_scan_add(cd * Alog2);
         const float gam = cl * cd;
         const float mu = gam + (1.0f - cln) * cdn;
@@ -1422,8 +1425,8 @@ __global__ __launch_bounds__(64 * kStepWaves) void step_grads_kernel(BackwardArg
         const float dA = group_sum(cd * suf, 64);
         if (lane == 0) a.ws_scal[((b * H + h) * nchunk + c) * REC + 5 * Q + 2] = dA;
         if (live) {   // this wave's own column: read above, by this lane
-            sd[lane * 64 + j] = ddt;
-            sl[lane * 64 + j] = dlam;
+            sd[lane * kStepLd + j] = ddt;
+            sl[lane * kStepLd + j] = dlam;
         }
     }
     __syncthreads();
@@ -1433,8 +1436,8 @@ __global__ __launch_bounds__(64 * kStepWaves) void step_grads_kernel(BackwardArg
         const int st = e >> 6, j = e & 63;
         const int64_t t = t0 + st;
         if (t < L && hb + j < H) {
-            ddtg[t * H + hb + j] = from_f32<T>(sd[e]);
-            dlamg[t * H + hb + j] = from_f32<T>(sl[e]);
+            ddtg[t * H + hb + j] = from_f32<T>(sd[st * kStepLd + j]);
+            dlamg[t * H + hb + j] = from_f32<T>(sl[st * kStepLd + j]);
         }
     }
 }
@@ -1524,7 +1527,7 @@ hipError_t launch_nipr(const BackwardArgs& a, bool states_only, hipStream_t s) {
     const int64_t nchunk = (a.L + Q - 1) / Q;
     if (nchunk > 0) {
         const dim3 sgrid((unsigned)nchunk, (unsigned)((a.H + 63) / 64), (unsigned)a.b);
-        hipLaunchKernelGGL(step_grads_kernel<T>, sgrid, dim3(64 * kStepWaves), 2 * (Q + 1) * 64 * sizeof(float), s, a, Q);
+        hipLaunchKernelGGL(step_grads_kernel<T>, sgrid, dim3(64 * kStepWaves), 2 * (Q + 1) * kStepLd * sizeof(float), s, a, Q);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
