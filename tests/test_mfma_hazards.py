@@ -161,3 +161,40 @@ def test_no_mfma_result_used_early_after_a_taken_branch(assembly):
     bad = [(n, op, d, straight[op]) for n, op, d in branched if op in straight and d < straight[op]]
     assert not bad, "MFMA results used too early after a taken branch (kernel, opcode, distance, " \
                     "straight-line minimum): %s" % sorted(set(bad))[:10]
+
+
+def _scan(lines):
+    """Straight-line minimum and branched distances of a hand-written instruction list."""
+    ins, labels = [], {}
+    for line in lines:
+        if line.endswith(":"):
+            labels[line[:-1]] = len(ins)
+            continue
+        op = line.split()[0]
+        ins.append((op, [o.strip() for o in line[len(op):].split(",")] if len(line) > len(op) else []))
+    return _distances(ins, labels)
+
+
+def test_scanner_rules_on_written_cases():
+    mfma = "v_mfma_f32_16x16x16_bf16 v[0:3], v[4:5], v[6:7], v[0:3]"
+    # straight line: a use four instructions after the MFMA
+    assert _scan([mfma, "v_mov_b32 v8, v9", "v_mov_b32 v8, v9", "s_nop 1", "v_add_f32 v10, v0, v1"]) == \
+        [("v_mfma_f32_16x16x16_bf16", 4, False)]
+    # a taken branch to a use: found through the branch, at its distance
+    found = _scan([mfma, "s_cbranch_scc1 .L1", "s_nop 7", "v_add_f32 v10, v0, v1", ".L1:", "v_add_f32 v11, v2, v3"])
+    assert ("v_mfma_f32_16x16x16_bf16", 1, True) in found
+    # exec known zero (execz taken): VALU instructions run on no lanes and are not uses ...
+    found = _scan([mfma, "s_cbranch_execz .L1", "s_nop 7", "v_add_f32 v10, v0, v1", ".L1:",
+                   "v_mov_b32 v2, v9", "s_endpgm"])
+    assert all(not taken for _, _, taken in found)
+    # ... but instructions that ignore exec are, and so is any VALU use once exec is written again
+    found = _scan([mfma, "s_cbranch_execz .L1", "s_nop 7", "v_add_f32 v10, v0, v1", ".L1:",
+                   "v_readlane_b32 s4, v1, 0", "s_endpgm"])
+    assert ("v_mfma_f32_16x16x16_bf16", 1, True) in found
+    found = _scan([mfma, "s_cbranch_execz .L1", "s_nop 7", "v_add_f32 v10, v0, v1", ".L1:",
+                   "s_or_b64 exec, exec, s[6:7]", "v_mov_b32 v2, v9", "s_endpgm"])
+    assert ("v_mfma_f32_16x16x16_bf16", 2, True) in found
+    # falling through an execnz branch leaves exec zero as well: only the taken path's use counts
+    found = _scan([mfma, "s_cbranch_execnz .L1", "v_mov_b32 v2, v9", "s_endpgm", ".L1:", "s_nop 7",
+                   "v_mov_b32 v2, v9"])
+    assert found == [("v_mfma_f32_16x16x16_bf16", 9, True)]
