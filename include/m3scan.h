@@ -223,9 +223,15 @@ size_t m3_prefill_workspace_bytes(const m3_dims* dims);
  * (64, 64), (128, 64)}, R in {1, 2, 4, 8, 16} and chunk * R in {16, 32, 64};
  * other shapes return M3_E_UNSUPPORTED.  The sequence length limit of m3_prefill applies (with
  * the angle carried as phi_in / phi_out when a sequence is split).  The workspace (optional,
- * m3_layer_prefill_workspace_bytes(dims) bytes, 16-byte aligned) enables the sequence split of
- * m3_prefill; the segments' start angles then come from the sums of dt * theta per 512 steps, as
- * m3_bcnorm_rope computes them.  Workspace errors as m3_prefill.
+ * m3_layer_prefill_workspace_bytes(dims) bytes, 16-byte aligned) enables a sequence split for
+ * the same dims as m3_prefill's, run differently: every segment runs at once, y included, the
+ * later ones from a zero carry; the chaining kernel gives each segment's true carry (and h_out);
+ * then each later segment's first steps run again from its true carry, in whole chunks, until
+ * the carry's decay from the segment's start, exp(A sum of dt), has stayed below 2^-48 (a
+ * segment whose carry never decays that far is rerun whole).  The y left from the zero-carry run
+ * past that point lacks only the carry's share, below 2^-48 of the carried state's contribution
+ * (2^-24 below float rounding).  The segments' start angles come from the sums of dt * theta per
+ * 512 steps, as m3_bcnorm_rope computes them.  Workspace errors as m3_prefill.
  */
 m3_status m3_layer_prefill(const m3_dims* dims, const void* x, const void* B, const void* C,
                            const void* dt, const void* theta, const float* normw_B,

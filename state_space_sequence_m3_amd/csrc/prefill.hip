@@ -69,6 +69,12 @@ namespace {
 // or staged, and the score tiles, masks, outputs and stores of y are left out (the chunk's
 // barrier stays, it orders the staging buffers).
 // PAIR (fused, ranks R >= 2): each thread stages two neighbouring rows of one step (see rowC).
+// A split sequence's later segments run first from a zero carry (pass 3).  The carried-in
+// state's share of y at step t of a segment is that state times 2^{l2}, l2 the log2 decay from the
+// segment's start through t; once l2 < -kFixLog2 for the rest of the segment the share is below
+// 2^-48 of the state, 2^-24 below float rounding, and pass 4 reruns only the steps before.
+constexpr float kFixLog2 = 48.0f;
+
 template <typename T, int N, int P, int NIB, bool FUSED, bool STATES = false, bool PAIR = false>
 __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) {
     using MM = Mma<T>;
@@ -121,13 +127,13 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
-    // a split sequence: pass 1 runs segments 0 .. nseg-2 of each (b, h) (end states only), pass 2
-    // all of them
-    const int segs = a.pass == 1 ? a.nseg - 1 : a.nseg;
+    // a split sequence: pass 1 runs segments 0 .. nseg-2 of each (b, h) (end states only), passes
+    // 2 and 3 all of them, pass 4 segments 1 .. nseg-1 (their first ws_fix steps)
+    const int segs = a.pass == 1 || a.pass == 4 ? a.nseg - 1 : a.nseg;
     // heads that share raw B and C run on one XCD (consecutive items), so its L2 serves the group
     const int64_t item = a.G > 0 && a.G < a.H ? xcd_item(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
     const int64_t bh = a.pass ? item / segs : item;
-    const int seg = a.pass ? (int)(item % segs) : 0;
+    const int seg = a.pass ? (int)(item % segs) + (a.pass == 4 ? 1 : 0) : 0;
     const int64_t b = bh / a.H;
     const int h = (int)(bh % a.H);
     const int H = a.H, R = a.R, Q = a.Q;
@@ -145,12 +151,13 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     if (a.pass) {
         t_first += seg * a.seglen;
         L = min(a.seglen, a.L - seg * a.seglen);
+        if (a.pass == 4) L = min(L, (int64_t)a.ws_fix[bh * a.nseg + seg]);
     }
     // pass 1 needs only the segment's end state: no C is read and no y stored
     const bool states_only = STATES || a.pass == 1;
-    // carried in: the call's carry (no split, or segment 0), none (the later segments in pass 1),
-    // or the previous segment's combined end state and its last step (the later segments in
-    // pass 2)
+    // carried in: the call's carry (no split, or segment 0), none (the later segments in passes
+    // 1 and 3), or the previous segment's combined end state and its last step (the later
+    // segments in passes 2 and 4)
     const bool own_carry = seg == 0;
     const int64_t nchunk = (L + Q - 1) / Q;
     const float Alog2 = a.A[h] * kLog2e;
@@ -173,12 +180,14 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // writes h_out while segment 0 of the same launch may not have read h_in yet (nothing orders
     // the workgroups).  Pass 1's segment 0 therefore saves h_in in the state slot of the last
     // segment, which neither pass 1 nor the chaining uses, and pass 2's segment 0 reads it there.
-    float* hin_copy = a.pass && a.h_in ? a.ws_state + (bh * a.nseg + a.nseg - 1) * (int64_t)(N * P) : nullptr;
+    // (Pass 3 writes no h_out, so its segment 0 reads h_in directly.)
+    float* hin_copy = (a.pass == 1 || a.pass == 2) && a.h_in ? a.ws_state + (bh * a.nseg + a.nseg - 1) * (int64_t)(N * P)
+                                                          : nullptr;
     if (own_carry) {
         hin = a.pass == 2 ? hin_copy : (a.h_in ? a.h_in + bh * (int64_t)(N * P) : nullptr);
         Bprev = a.Bbar_prev ? (const T*)a.Bbar_prev + bh * (int64_t)(R * N) : nullptr;
         xprev = a.x_prev ? (const T*)a.x_prev + bh * (int64_t)(R * P) : nullptr;
-    } else if (a.pass == 2) {
+    } else if (a.pass == 2 || a.pass == 4) {
         hin = a.ws_state + (bh * a.nseg + seg - 1) * (int64_t)(N * P);
         Bprev = (const T*)a.ws_bbar + (bh * a.nseg + seg - 1) * (int64_t)(R * N);
         xprev = Xg - HRP;   // step t_first - 1 of this head
@@ -400,7 +409,11 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // the last wave (the one with the fewest score tiles): the chunk's per-step scalars (lane =
     // step) -> per-row copies in LDS.  Lanes past the chunk only add to later lanes of the scan,
     // which are never read.
-    float l2sum = 0.f;   // STATES: the segment's log2 decay, sum of the chunks' (last wave)
+    float l2sum = 0.f;   // STATES, pass 3: the segment's log2 decay, sum of the chunks' (last wave)
+    // pass 3 (last wave): chunks staged so far, and how many of them have a step whose log2 decay
+    // from the segment's start (the carried-in state's factor in y) is above -kFixLog2; a chunk's
+    // 64 lanes include the step after it (a conservative superset)
+    int staged_chunks = 0, fix_chunks = 0;
     auto stage_scalars = [&](float d, float lm, float dn63, float lmn63, int buf) {
         // dt, lambda of step t + 1: the next lane's, lane 63's own load (the shuffles run in every
         // lane: a lane reading an inactive lane would get zero)
@@ -411,7 +424,11 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         const float gam = lm * d;
         const float mu = gam + (1.0f - lmn) * dn;
         const float l2end = lane_value(l2, Q - 1);
-        if (STATES) l2sum += l2end;
+        if (a.pass == 3) {
+            ++staged_chunks;
+            if (__any(l2sum + l2 >= -kFixLog2)) fix_chunks = staged_chunks;
+        }
+        if (STATES || a.pass == 3) l2sum += l2end;
         const float el = fast_exp2(l2);
         const float w = fast_exp2(fminf(l2end - l2, 0.f)) * mu;
         float* o = rL2 + buf * 64;
@@ -755,15 +772,20 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 
     // ---- outputs: final state and the last step's (Bbar, x) ------------------------------
     // no split: the call's; pass 1: the segment's end state and last Bbar row, into the
-    // workspace; pass 2: the call's, from the last segment only
-    const bool last_seg = a.pass != 2 || seg == a.nseg - 1;
-    float* hout = a.pass == 1 ? a.ws_state + (bh * a.nseg + seg) * (int64_t)(N * P)
-                              : (last_seg ? a.h_out + bh * (int64_t)(N * P) : nullptr);
-    T* Blast = a.pass == 1 ? (T*)a.ws_bbar + (bh * a.nseg + seg) * (int64_t)(R * N)
-                           : (last_seg && a.Bbar_last ? (T*)a.Bbar_last + bh * (int64_t)(R * N) : nullptr);
-    T* xlast = a.pass != 1 && last_seg && a.x_last ? (T*)a.x_last + bh * (int64_t)(R * P) : nullptr;
-    float* phout = FUSED && a.pass != 1 && last_seg && a.phi_out ? a.phi_out + bh * K : nullptr;
-    if (STATES && wave == NW - 1 && lane == 0) a.ws_l2[bh * a.nseg + seg] = l2sum;
+    // workspace; pass 2: the call's, from the last segment only; pass 3: the segment's end state
+    // into the workspace, its last Bbar row there too except in the last segment, which writes
+    // the call's Bbar_last, x_last and phi_out (h_out comes from segment_combine); pass 4: none
+    const bool last_seg = a.pass == 0 || a.pass == 1 || seg == a.nseg - 1;
+    const bool ws_out = a.pass == 1 || a.pass == 3;
+    float* hout = ws_out ? a.ws_state + (bh * a.nseg + seg) * (int64_t)(N * P)
+                         : (a.pass != 4 && last_seg ? a.h_out + bh * (int64_t)(N * P) : nullptr);
+    T* Blast = a.pass == 1 || (a.pass == 3 && !last_seg) ? (T*)a.ws_bbar + (bh * a.nseg + seg) * (int64_t)(R * N)
+               : (a.pass != 4 && last_seg && a.Bbar_last ? (T*)a.Bbar_last + bh * (int64_t)(R * N) : nullptr);
+    T* xlast = a.pass != 1 && a.pass != 4 && last_seg && a.x_last ? (T*)a.x_last + bh * (int64_t)(R * P) : nullptr;
+    float* phout = FUSED && a.pass != 1 && a.pass != 4 && last_seg && a.phi_out ? a.phi_out + bh * K : nullptr;
+    if ((STATES || a.pass == 3) && wave == NW - 1 && lane == 0) a.ws_l2[bh * a.nseg + seg] = l2sum;
+    if (a.pass == 3 && wave == NW - 1 && lane == 0)
+        a.ws_fix[bh * a.nseg + seg] = (int)min((int64_t)fix_chunks * Q, L);
     if (hout) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -797,9 +819,9 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     }
 }
 
-// Between the passes of a split sequence: the true end state of segment s (1 <= s <= nseg - 2)
-// is its local end state (from zero, pass 1) plus the carried state that enters it, decayed over
-// the segment:
+// Between the passes of a split sequence: the true end state of segment s (1 <= s <= nseg - 2;
+// after pass 3 also s = nseg - 1, whose result is the call's h_out) is its local end state (from
+// zero, passes 1 and 3) plus the carried state that enters it, decayed over the segment:
 //   g_end(s) = g_local(s) + 2^{l2(s)} (g_end(s - 1) + c_{t0} Bbar_{t0-1}^T x_{t0-1})
 // with l2(s) = log2 e * A * sum_{t in s} dt_t (saved by pass 1), t0 the segment's first step and
 // c_{t0} = (1 - lambda_{t0}) dt_{t0}: the recurrence is linear in its carry, and the carry term is
@@ -825,11 +847,12 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(PrefillArgs a) {
     // outer products u, the segments' own end states) is read before any result is written back,
     // since a load that follows a store to the workspace waits for it; only the chain through gp
     // is sequential.
-    for (int s0 = 1; s0 + 1 < a.nseg; s0 += kCombineBlk) {
+    const int last = a.pass == 3 ? a.nseg : a.nseg - 1;   // segments chained: 1 .. last - 1
+    for (int s0 = 1; s0 < last; s0 += kCombineBlk) {
         float decay[kCombineBlk], c0[kCombineBlk], u[kCombineBlk][4], own[kCombineBlk][4];
 #pragma unroll
         for (int i = 0; i < kCombineBlk; ++i) {
-            const int s = s0 + i + 1 < a.nseg ? s0 + i : s0;   // past the last one: unused
+            const int s = s0 + i < last ? s0 + i : s0;   // past the last one: unused
             decay[i] = exp2f(a.ws_l2[bh * a.nseg + s]);
             const int64_t row0 = (b * a.L + s * a.seglen) * H + h;   // step t0 of this head
             c0[i] = (1.0f - load_f32((const T*)a.lam + row0)) * load_f32((const T*)a.dt + row0);
@@ -850,8 +873,8 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < kCombineBlk; ++i) {
             const int s = s0 + i;
-            if (s + 1 >= a.nseg) break;
-            float* gs = a.ws_state + (bh * a.nseg + s) * NP;
+            if (s >= last) break;
+            float* gs = s + 1 < a.nseg ? a.ws_state + (bh * a.nseg + s) * NP : a.h_out + bh * NP;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if (el[j] >= NP) continue;
@@ -864,7 +887,7 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(PrefillArgs a) {
 
 template <typename T, int N, int P, bool FUSED, bool STATES>
 hipError_t launch_nps(const PrefillArgs& a, hipStream_t s) {
-    const int64_t per_bh = a.pass == 0 ? 1 : (a.pass == 1 ? a.nseg - 1 : a.nseg);
+    const int64_t per_bh = a.pass == 0 ? 1 : (a.pass == 1 || a.pass == 4 ? a.nseg - 1 : a.nseg);
     const dim3 grid((unsigned)(a.b * a.H * per_bh)), block(P / 16 * 64);
     // fused: BCNorm weights and biases in dynamic LDS
     const size_t dyn = FUSED ? (size_t)(2 * N + 2 * a.R * N) * sizeof(float) : 0;
@@ -887,9 +910,12 @@ hipError_t launch_nps(const PrefillArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// passes 1 and 2 split m3_prefill, passes 3 and 4 the fused call
 template <typename T, int N, int P, bool FUSED>
 hipError_t launch_np(const PrefillArgs& a, hipStream_t s) {
-    return a.pass == 1 ? launch_nps<T, N, P, FUSED, true>(a, s) : launch_nps<T, N, P, FUSED, false>(a, s);
+    if (FUSED ? a.pass == 1 || a.pass == 2 : a.pass >= 3) return hipErrorInvalidValue;
+    if constexpr (FUSED) return launch_nps<T, N, P, true, false>(a, s);
+    else return a.pass == 1 ? launch_nps<T, N, P, false, true>(a, s) : launch_nps<T, N, P, false, false>(a, s);
 }
 
 template <typename T, bool FUSED>

@@ -1,6 +1,9 @@
 """GPU parity of the sequence split of m3_prefill and m3_layer_prefill: with few (b, h) pairs and
-long sequences, and a workspace, each sequence runs as segments in parallel (pass 1 from zero
-carries, a chaining kernel, pass 2 from the true carries).  Checked against the fp64 oracle's
+long sequences, and a workspace, each sequence runs as segments in parallel.  m3_prefill: pass 1
+(end states from zero carries), a chaining kernel, pass 2 (every segment from its true carry).
+m3_layer_prefill: pass 3 (every segment, y included, the later ones from zero carries), the
+chaining, pass 4 (each later segment's first steps again from its true carry, until the carry's
+share of y has decayed by 2^-48).  Checked against the fp64 oracle's
 layer core over the whole sequence, with carries in, ragged last segments and 2-4 segments (so
 that the chaining runs); the same call run in one pass is checked against the oracle too.
 Every call goes through the C ABI (via the ctypes binding).  Tolerances are those of
@@ -109,6 +112,54 @@ def test_split_layer_prefill_in_place_carry():
     assert rel_err(y, ref["y"]) <= TOL["bf16"]
     assert rel_err(h, ref["h_out"]) <= TOL["bf16"]
     assert angle_err(phi, ref["phi_out"]) <= 1e-3
+
+
+def test_split_rerun_lengths():
+    """Pass 4's rerun length per segment, from the log2 decay l2(t) = log2(e) A sum_{s <= t} dt_s
+    counted from the segment's start: whole 16-step chunks up to the last chunk whose first step
+    still has l2 >= -48 (the decay is monotone here, so that step is the chunk's largest).  Three
+    heads at the extremes: A = -1e-4 (the carry never decays: every segment is rerun whole),
+    A = -40 (gone within a chunk) and A = -16 with dt = 4 at each segment's first step (gone at
+    that step: nothing is rerun).  The recorded lengths are read back from the workspace, and y,
+    h_out and phi_out checked against the oracle."""
+    L, H, P, N, R, Q = 4100, 3, 64, 128, 2, 16
+    w = _wl("bf16", 1, L, H, P, N, R, Q, True)
+    inp = inputs.make_prefill_inputs(w, seed=86, normw=True, carry=True)
+    inp["A"] = torch.tensor([-1e-4, -40.0, -16.0], dtype=torch.float32)
+    # 3 pairs on 256 compute units: 4100 steps in segments of 1536 (a multiple of 512, at least
+    # 1024 steps each): 1536, 1536, 1028
+    seglen, nseg = 1536, 3
+    for s in range(1, nseg):
+        inp["dt"][0, s * seglen, 2] = 4.0
+    r = lambda n: (n + 255) // 256 * 256
+    off_fix = r(H * nseg * N * P * 4) + r(H * nseg * R * N * 2) + r(H * nseg * 4)
+    need = m3scan.layer_prefill_workspace_bytes(_dims(w, Q))
+    assert need == off_fix + r(H * nseg * 4) + r(H * nseg * 4 * (N // 2) * 4) + r(H * (N // 2) * 4), \
+        "the split plan differs from the one this test assumes"
+    d = to_dev(inp, DEV)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    y, h, phi = _layer(d, w, Q, True, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.layer(inp, bcnorm=True, mix=True)
+    assert rel_err(y, ref["y"]) <= TOL["bf16"]
+    assert rel_err(h, ref["h_out"]) <= TOL["bf16"]
+    assert angle_err(phi, ref["phi_out"]) <= 1e-3
+    fix = ws[off_fix:off_fix + H * nseg * 4].view(torch.int32).view(H, nseg).cpu()
+    dt = inp["dt"][0].double()
+    for hh in range(H):
+        for s in range(nseg):
+            t0, t1 = s * seglen, min((s + 1) * seglen, L)
+            l2 = torch.cumsum(dt[t0:t1, hh] * float(inp["A"][hh]) * 1.4426950408889634, 0)
+            firsts = l2[::Q]
+            # a chunk whose first step sits within 1e-3 of the threshold may go either way in fp32
+            lo = [c + 1 for c in range(len(firsts)) if firsts[c] >= -48 + 1e-3]
+            hi = [c + 1 for c in range(len(firsts)) if firsts[c] >= -48 - 1e-3]
+            lo = min(max(lo, default=0) * Q, t1 - t0)
+            hi = min(max(hi, default=0) * Q, t1 - t0)
+            assert lo <= int(fix[hh, s]) <= hi, (hh, s, int(fix[hh, s]), lo, hi)
+    assert fix[0].tolist() == [1536, 1536, 1028]
+    assert fix[1].tolist() == [Q, Q, Q]
+    assert fix[2, 1:].tolist() == [0, 0]
 
 
 def test_split_workspace_too_small_is_rejected():
