@@ -177,11 +177,16 @@ size_t m3_bcnorm_rope_workspace_bytes(const m3_dims* dims);
  *   workspace   m3_prefill_workspace_bytes(dims) bytes, 16-byte aligned, or NULL        optional
  * With a workspace, a call with few (b, h) pairs (fewer than two per compute unit) and long
  * sequences splits each sequence into segments of a multiple of 512 steps that run in parallel:
- * pass 1 gives every segment's end state from a zero carry (segment 0 from the call's carry),
- * a small kernel chains them (the recurrence is linear in its carry: the end state of segment s
- * is its own end state plus the incoming state decayed by exp(A sum of dt over the segment)),
- * and pass 2 reruns segments 1, 2, ... from their true carries.  The results are those of one
- * pass up to rounding order.  m3_prefill_workspace_bytes returns 0 when no split would be used;
+ * pass 1 runs every segment in full, y included, segment 0 from the call's carry and the others
+ * from a zero carry; a small kernel chains the segments' end states into true ones and h_out
+ * (the recurrence is linear in its carry: the end state of segment s is its own end state plus
+ * the incoming state decayed by exp(A sum of dt over the segment)); pass 2 reruns the first steps
+ * of segments 1, 2, ... from their true carries, in whole chunks, until the carry's decay from
+ * the segment's start, exp(A sum of dt), has stayed below 2^-48 (a segment whose carry never
+ * decays that far is rerun whole).  The y left from the zero-carry run past that point lacks only
+ * the carry's share, below 2^-48 of the carried state's contribution (2^-24 below float
+ * rounding); the other results are those of one pass up to rounding order.
+ * m3_prefill_workspace_bytes returns 0 when no split would be used;
  * with NULL the call always runs one pass per sequence.  A non-NULL workspace smaller than the
  * returned size is M3_E_WORKSPACE; one that overlaps any argument is M3_E_ALIAS.
  * Any L >= 0 is accepted (L = 0 copies the carried state to the outputs), as long as one
@@ -223,15 +228,10 @@ size_t m3_prefill_workspace_bytes(const m3_dims* dims);
  * (64, 64), (128, 64)}, R in {1, 2, 4, 8, 16} and chunk * R in {16, 32, 64};
  * other shapes return M3_E_UNSUPPORTED.  The sequence length limit of m3_prefill applies (with
  * the angle carried as phi_in / phi_out when a sequence is split).  The workspace (optional,
- * m3_layer_prefill_workspace_bytes(dims) bytes, 16-byte aligned) enables a sequence split for
- * the same dims as m3_prefill's, run differently: every segment runs at once, y included, the
- * later ones from a zero carry; the chaining kernel gives each segment's true carry (and h_out);
- * then each later segment's first steps run again from its true carry, in whole chunks, until
- * the carry's decay from the segment's start, exp(A sum of dt), has stayed below 2^-48 (a
- * segment whose carry never decays that far is rerun whole).  The y left from the zero-carry run
- * past that point lacks only the carry's share, below 2^-48 of the carried state's contribution
- * (2^-24 below float rounding).  The segments' start angles come from the sums of dt * theta per
- * 512 steps, as m3_bcnorm_rope computes them.  Workspace errors as m3_prefill.
+ * m3_layer_prefill_workspace_bytes(dims) bytes, 16-byte aligned) enables the sequence split of
+ * m3_prefill, for the same dims and with the same passes; the segments' start angles come from
+ * the sums of dt * theta per 512 steps, as m3_bcnorm_rope computes them.  Workspace errors as
+ * m3_prefill.
  */
 m3_status m3_layer_prefill(const m3_dims* dims, const void* x, const void* B, const void* C,
                            const void* dt, const void* theta, const float* normw_B,

@@ -156,7 +156,7 @@ int device_cus() {
 // few to give every compute unit two workgroups, each sequence is cut into segments of a
 // multiple of 512 steps (at least 1024 each) that run in parallel, then are chained (see
 // PrefillArgs).  Workspace: the segments' end states, the rotated Bbar of their last steps, their
-// log2 decays and, fused, the steps of each segment to rerun, the start angles of each segment's
+// log2 decays, the steps of each segment to rerun and, fused, the start angles of each segment's
 // quarters (m3_bcnorm_rope's angle kernels over the same segments) and a final-angle scratch row.
 struct SplitPlan {
     int nseg = 1;
@@ -185,10 +185,9 @@ SplitPlan split_plan(const m3_dims* d, int64_t Q, bool fused, bool packed) {
     sp.off_state = 0;
     sp.off_bbar = align256((size_t)(pairs * nseg * N * P) * 4);
     sp.off_l2 = sp.off_bbar + align256((size_t)(pairs * nseg * R * N) * es);
-    sp.total = sp.off_l2 + align256((size_t)(pairs * nseg) * 4);
+    sp.off_fix = sp.off_l2 + align256((size_t)(pairs * nseg) * 4);
+    sp.total = sp.off_fix + align256((size_t)(pairs * nseg) * 4);
     if (fused) {
-        sp.off_fix = sp.total;
-        sp.total = sp.off_fix + align256((size_t)(pairs * nseg) * 4);
         sp.nsegA = nseg;   // the angle pass sums dt * theta over the same segments
         sp.off_phi = sp.total;
         sp.off_phiend = sp.off_phi + align256((size_t)(pairs * sp.nsegA * m3::bcnorm_rope_parts() * (N / 2)) * 4);
@@ -210,10 +209,9 @@ m3_status check_split_workspace(const SplitPlan& sp, const void* ws, size_t ws_b
     return M3_OK;
 }
 
-// A split prefill.  m3_prefill: pass 1 (end states), chaining, pass 2 (every segment from its
-// true carry).  m3_layer_prefill: the angle pass, pass 3 (every segment, the later ones from zero),
-// chaining (which also gives h_out), pass 4 (the later segments' first steps again, from their
-// true carry, until the carry's share of y has decayed below float rounding)
+// A split prefill (fused: after the angle pass): pass 1 (every segment, the later ones from
+// zero), chaining (which also gives h_out), pass 2 (the later segments' first steps again, from
+// their true carry, until the carry's share of y has decayed below float rounding)
 hipError_t run_split(m3::PrefillArgs a, const SplitPlan& sp, void* ws, bool fused, bool bf16, hipStream_t s) {
     char* w = (char*)ws;
     a.nseg = sp.nseg;
@@ -221,6 +219,7 @@ hipError_t run_split(m3::PrefillArgs a, const SplitPlan& sp, void* ws, bool fuse
     a.ws_state = (float*)(w + sp.off_state);
     a.ws_bbar = w + sp.off_bbar;
     a.ws_l2 = (float*)(w + sp.off_l2);
+    a.ws_fix = (int*)(w + sp.off_fix);
     hipError_t e = hipSuccess;
     if (fused) {
         m3::BcnormRopeArgs g{};
@@ -240,19 +239,15 @@ hipError_t run_split(m3::PrefillArgs a, const SplitPlan& sp, void* ws, bool fuse
         a.seg_phi = g.seg_phi;
         a.angle_seglen = g.seglen;
         a.angle_parts = m3::bcnorm_rope_parts();
-        a.ws_fix = (int*)(w + sp.off_fix);
-        a.pass = 3;
-        if (e == hipSuccess) e = m3::launch_layer(a, bf16, s);
-        if (e == hipSuccess) e = m3::launch_segment_combine(a, bf16, s);
-        a.pass = 4;
-        if (e == hipSuccess) e = m3::launch_layer(a, bf16, s);
-        return e;
     }
+    auto run = [&](const m3::PrefillArgs& pa) {
+        return fused ? m3::launch_layer(pa, bf16, s) : m3::launch_prefill(pa, bf16, s);
+    };
     a.pass = 1;
-    if (e == hipSuccess) e = m3::launch_prefill(a, bf16, s);
-    if (e == hipSuccess && sp.nseg > 2) e = m3::launch_segment_combine(a, bf16, s);
+    if (e == hipSuccess) e = run(a);
+    if (e == hipSuccess) e = m3::launch_segment_combine(a, bf16, s);
     a.pass = 2;
-    if (e == hipSuccess) e = m3::launch_prefill(a, bf16, s);
+    if (e == hipSuccess) e = run(a);
     return e;
 }
 

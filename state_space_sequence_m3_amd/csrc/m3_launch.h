@@ -95,26 +95,20 @@ struct PrefillArgs {
     const int32_t* cu_seqlens = nullptr;
     int64_t T = 0;
     // Sequence split (few (b, h) pairs, long sequences): each sequence is cut into nseg segments
-    // of seglen steps.  pass 0 = no split.
-    // m3_prefill: pass 1 runs segments 0 .. nseg-2 at once for their end states only (segment 0
-    // from the call's carry, the others from zero; no C is read, no y computed): the end states
-    // and the rotated Bbar of their last steps go to the workspace.  segment_combine turns the
-    // end states into true ones, and pass 2 runs every segment from its true carry, writing y and,
-    // in the last segment, the call's outputs.
-    // m3_layer_prefill: pass 3 runs every segment at once, segment 0 from the call's carry and the
-    // others from zero, writing y, each segment's end state, last rotated Bbar, log2 decay and
-    // ws_fix (the steps from the segment's start after which the carried-in state's share of y,
-    // which decays as 2^l2, stays below 2^-48 of its size), and in the last segment the call's
-    // angle and last-step outputs; segment_combine chains the end states (and writes h_out); pass
-    // 4 reruns the first ws_fix steps of segments 1 .. nseg-1 from their true carry, writing y
-    // only.  The re-read is then the carry's decay length rather than the whole sequence.
+    // of seglen steps.  pass 0 = no split.  pass 1 runs every segment at once, segment 0 from the
+    // call's carry and the others from zero, writing y, each segment's end state, last rotated
+    // Bbar, log2 decay and ws_fix (the steps from the segment's start after which the carried-in
+    // state's share of y, which decays as 2^l2, stays below 2^-48 of its size), and in the last
+    // segment the call's angle and last-step outputs; segment_combine chains the end states (and
+    // writes h_out); pass 2 reruns the first ws_fix steps of segments 1 .. nseg-1 from their true
+    // carry, writing y only.
     int pass = 0;
     int nseg = 1;
     int64_t seglen = 0;
     float* ws_state = nullptr;       // [b, H, nseg, N, P] end state of each segment
     void* ws_bbar = nullptr;         // [b, H, nseg, R, N] io, rotated Bbar of each segment's last step
     float* ws_l2 = nullptr;          // [b, H, nseg] log2 decay of each segment (log2 e A sum of dt)
-    int* ws_fix = nullptr;           // [b, H, nseg] pass 3 -> pass 4: steps of each segment to rerun
+    int* ws_fix = nullptr;           // [b, H, nseg] pass 1 -> pass 2: steps of each segment to rerun
     const float* seg_phi = nullptr;  // fused: angle-segment start angles [b, H, nsegA, parts, N/2] (radians)
     int64_t angle_seglen = 0;        // steps per angle segment (seglen or a divisor of it)
     int angle_parts = 0;             // start angles per angle segment

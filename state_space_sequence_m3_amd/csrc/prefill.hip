@@ -65,17 +65,14 @@ namespace {
 // remains.  The raw loads of chunk c + 2 are issued at the start of chunk c into the register set
 // of that parity, so they have a whole chunk to arrive.  Tiles of 48 or 64 rows do not fit twice
 // in LDS and run the same steps with two barriers per chunk.
-// STATES: pass 1 of a split sequence, which needs only each segment's end state: no C is read
-// or staged, and the score tiles, masks, outputs and stores of y are left out (the chunk's
-// barrier stays, it orders the staging buffers).
 // PAIR (fused, ranks R >= 2): each thread stages two neighbouring rows of one step (see rowC).
-// A split sequence's later segments run first from a zero carry (pass 3).  The carried-in
+// A split sequence's later segments run first from a zero carry (pass 1).  The carried-in
 // state's share of y at step t of a segment is that state times 2^{l2}, l2 the log2 decay from the
 // segment's start through t; once l2 < -kFixLog2 for the rest of the segment the share is below
-// 2^-48 of the state, 2^-24 below float rounding, and pass 4 reruns only the steps before.
+// 2^-48 of the state, 2^-24 below float rounding, and pass 2 reruns only the steps before.
 constexpr float kFixLog2 = 48.0f;
 
-template <typename T, int N, int P, int NIB, bool FUSED, bool STATES = false, bool PAIR = false>
+template <typename T, int N, int P, int NIB, bool FUSED, bool PAIR = false>
 __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) {
     using MM = Mma<T>;
     using F = typename MM::frag;
@@ -127,13 +124,13 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
-    // a split sequence: pass 1 runs segments 0 .. nseg-2 of each (b, h) (end states only), passes
-    // 2 and 3 all of them, pass 4 segments 1 .. nseg-1 (their first ws_fix steps)
-    const int segs = a.pass == 1 || a.pass == 4 ? a.nseg - 1 : a.nseg;
+    // a split sequence: pass 1 runs every segment of each (b, h), pass 2 segments 1 .. nseg-1
+    // (their first ws_fix steps)
+    const int segs = a.pass == 2 ? a.nseg - 1 : a.nseg;
     // heads that share raw B and C run on one XCD (consecutive items), so its L2 serves the group
     const int64_t item = a.G > 0 && a.G < a.H ? xcd_item(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
     const int64_t bh = a.pass ? item / segs : item;
-    const int seg = a.pass ? (int)(item % segs) + (a.pass == 4 ? 1 : 0) : 0;
+    const int seg = a.pass ? (int)(item % segs) + (a.pass == 2 ? 1 : 0) : 0;
     const int64_t b = bh / a.H;
     const int h = (int)(bh % a.H);
     const int H = a.H, R = a.R, Q = a.Q;
@@ -151,13 +148,10 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     if (a.pass) {
         t_first += seg * a.seglen;
         L = min(a.seglen, a.L - seg * a.seglen);
-        if (a.pass == 4) L = min(L, (int64_t)a.ws_fix[bh * a.nseg + seg]);
+        if (a.pass == 2) L = min(L, (int64_t)a.ws_fix[bh * a.nseg + seg]);
     }
-    // pass 1 needs only the segment's end state: no C is read and no y stored
-    const bool states_only = STATES || a.pass == 1;
-    // carried in: the call's carry (no split, or segment 0), none (the later segments in passes
-    // 1 and 3), or the previous segment's combined end state and its last step (the later
-    // segments in passes 2 and 4)
+    // carried in: the call's carry (no split, or segment 0), none (the later segments in pass 1),
+    // or the previous segment's chained end state and its last step (pass 2)
     const bool own_carry = seg == 0;
     const int64_t nchunk = (L + Q - 1) / Q;
     const float Alog2 = a.A[h] * kLog2e;
@@ -176,18 +170,13 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const float* hin = nullptr;
     const T* Bprev = nullptr;
     const T* xprev = nullptr;
-    // Split sequences and a carry updated in place (h_out == h_in): the last segment of pass 2
-    // writes h_out while segment 0 of the same launch may not have read h_in yet (nothing orders
-    // the workgroups).  Pass 1's segment 0 therefore saves h_in in the state slot of the last
-    // segment, which neither pass 1 nor the chaining uses, and pass 2's segment 0 reads it there.
-    // (Pass 3 writes no h_out, so its segment 0 reads h_in directly.)
-    float* hin_copy = (a.pass == 1 || a.pass == 2) && a.h_in ? a.ws_state + (bh * a.nseg + a.nseg - 1) * (int64_t)(N * P)
-                                                          : nullptr;
+    // (A split writes h_out only in the chaining kernel, after pass 1's segment 0 has read h_in,
+    // so the carry may be updated in place.)
     if (own_carry) {
-        hin = a.pass == 2 ? hin_copy : (a.h_in ? a.h_in + bh * (int64_t)(N * P) : nullptr);
+        hin = a.h_in ? a.h_in + bh * (int64_t)(N * P) : nullptr;
         Bprev = a.Bbar_prev ? (const T*)a.Bbar_prev + bh * (int64_t)(R * N) : nullptr;
         xprev = a.x_prev ? (const T*)a.x_prev + bh * (int64_t)(R * P) : nullptr;
-    } else if (a.pass == 2 || a.pass == 4) {
+    } else if (a.pass == 2) {
         hin = a.ws_state + (bh * a.nseg + seg - 1) * (int64_t)(N * P);
         Bprev = (const T*)a.ws_bbar + (bh * a.nseg + seg - 1) * (int64_t)(R * N);
         xprev = Xg - HRP;   // step t_first - 1 of this head
@@ -225,7 +214,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     uint4 rc[NBUF][MAXC], rb[NBUF][MAXC], rx[NBUF][MAXX];
     typedef typename IoBits<T>::type Bits;
     Bits nd[NBUF], nl[NBUF], ndn[NBUF], nln[NBUF];   // dt, lambda at t and t + 1 (io bits; the last wave uses them)
-    const rsrc_t dCs = make_rsrc(Cg, states_only ? 0u : seq_bytes(SBC, (int64_t)R * N));
+    const rsrc_t dCs = make_rsrc(Cg, seq_bytes(SBC, (int64_t)R * N));
     const rsrc_t dBs = make_rsrc(Bg, seq_bytes(SBC, (int64_t)R * N));
     const rsrc_t dXs = make_rsrc(Xg, seq_bytes(HRP, (int64_t)R * P));
     const rsrc_t dDs = make_rsrc(dtg, seq_bytes(H, 1));
@@ -233,7 +222,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // part: 0 = Cbar rows, 1 = Bbar rows, 2 = x rows, 3 = step scalars; -1 = all
     auto load_chunk = [&](int64_t c, int set, int part = -1) {
         const int64_t t0 = c * Q;
-        if (!STATES && (part < 0 || part == 0)) {
+        if (part < 0 || part == 0) {
             const uint32_t o = step_off(t0, SBC);
 #pragma unroll
             for (int k = 0; k < MAXC; ++k)
@@ -370,7 +359,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         const int n0 = cC0 * VE;
         float sc[2] = {1.f, 1.f};
         if (a.bcnorm) {   // RMS over the row's N values, spread over VPN consecutive lanes
-            constexpr int NR = STATES ? 1 : 2;   // rows normalised: B (and C)
+            constexpr int NR = 2;   // rows normalised: B and C
             float q2[2] = {0.f, 0.f};
 #pragma unroll
             for (int which = 0; which < NR; ++which) q2[which] = sumsq16(which == 0 ? rb[set][k] : rc[set][k], T{});
@@ -384,7 +373,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
                 sc[which] = __builtin_amdgcn_rsqf(fmaxf(fmaf(q2[which], invN, a.eps), 1e-30f));
         }
 #pragma unroll
-        for (int which = 0; which < (STATES ? 1 : 2); ++which) {
+        for (int which = 0; which < 2; ++which) {
             float x[VE];
             unpack16(which == 0 ? rb[set][k] : rc[set][k], x, T{});
             const float* bw = sBias + (which * R + r) * N + n0;
@@ -409,8 +398,8 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // the last wave (the one with the fewest score tiles): the chunk's per-step scalars (lane =
     // step) -> per-row copies in LDS.  Lanes past the chunk only add to later lanes of the scan,
     // which are never read.
-    float l2sum = 0.f;   // STATES, pass 3: the segment's log2 decay, sum of the chunks' (last wave)
-    // pass 3 (last wave): chunks staged so far, and how many of them have a step whose log2 decay
+    float l2sum = 0.f;   // pass 1: the segment's log2 decay, sum of the chunks' (last wave)
+    // pass 1 (last wave): chunks staged so far, and how many of them have a step whose log2 decay
     // from the segment's start (the carried-in state's factor in y) is above -kFixLog2; a chunk's
     // 64 lanes include the step after it (a conservative superset)
     int staged_chunks = 0, fix_chunks = 0;
@@ -424,11 +413,11 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         const float gam = lm * d;
         const float mu = gam + (1.0f - lmn) * dn;
         const float l2end = lane_value(l2, Q - 1);
-        if (a.pass == 3) {
+        if (a.pass == 1) {
             ++staged_chunks;
             if (__any(l2sum + l2 >= -kFixLog2)) fix_chunks = staged_chunks;
         }
-        if (STATES || a.pass == 3) l2sum += l2end;
+        if (a.pass == 1) l2sum += l2end;
         const float el = fast_exp2(l2);
         const float w = fast_exp2(fminf(l2end - l2, 0.f)) * mu;
         float* o = rL2 + buf * 64;
@@ -467,7 +456,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
                         stage_bc(set, j, i, buf, cs, sn);
                     }
                 } else {
-                    if (!STATES) *(uint4*)(sC + buf * TC + i * LDC + cC0 * VE) = rc[set][j];
+                    *(uint4*)(sC + buf * TC + i * LDC + cC0 * VE) = rc[set][j];
                     *(uint4*)(sB + buf * TB + i * LDB + cC0 * VE) = rb[set][j];
                 }
             }
@@ -487,12 +476,6 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
         for (int m = 0; m < 4; ++m)
             st[nb][m] = hin ? hin[(16 * nb + 4 * g + m) * P + pcol] : 0.f;
-    if (a.pass == 1 && own_carry && hin_copy) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) hin_copy[(16 * nb + 4 * g + m) * P + pcol] = st[nb][m];
-    }
     if (Bprev && xprev && L > 0) {
         const float c0 = (1.0f - load_f32(lamg)) * load_f32(dtg);
         for (int r = 0; r < R; ++r) {
@@ -508,7 +491,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     const bool mix = a.w_out != nullptr;
     T* yg = (T*)a.y + row_bh * (mix ? P : (int64_t)R * P);
     const int64_t ystep = mix ? (int64_t)H * P : HRP, yrow = mix ? P : (int64_t)R * P;
-    const rsrc_t dYs = make_rsrc(yg, states_only ? 0u : seq_bytes(ystep, yrow));
+    const rsrc_t dYs = make_rsrc(yg, seq_bytes(ystep, yrow));
     floatx4 wo = {1.f, 1.f, 1.f, 1.f};          // mixing weights for this lane's (r, 4 columns)
     if (mix) {
         const int r = l16 & rmask;
@@ -574,14 +557,12 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         // two blocks' worth.
         F fc[2][NIB], fsb[2][NSLOT], fsc[2][NSLOT], fbt[2][NIB];
         auto fetch = [&](int k, int s) {
-            if constexpr (!STATES) {
 #pragma unroll
-                for (int ib = 0; ib < NIB; ++ib) fc[s][ib] = MM::ldk(tC + 16 * ib * LDC + 16 * k);
+            for (int ib = 0; ib < NIB; ++ib) fc[s][ib] = MM::ldk(tC + 16 * ib * LDC + 16 * k);
 #pragma unroll
-                for (int j = 0; j < NSLOT; ++j) {
-                    fsb[s][j] = MM::ldk(pSB[j] + buf * TB + 16 * k);
-                    fsc[s][j] = MM::ldk(pSC[j] + buf * TC + 16 * k);
-                }
+            for (int j = 0; j < NSLOT; ++j) {
+                fsb[s][j] = MM::ldk(pSB[j] + buf * TB + 16 * k);
+                fsc[s][j] = MM::ldk(pSC[j] + buf * TC + 16 * k);
             }
 #pragma unroll
             for (int sb = 0; sb < NIB; ++sb) fbt[s][sb] = MM::ldt(tBt + 16 * sb * LDB + 16 * k, LDB, l16);
@@ -593,15 +574,13 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
             __builtin_amdgcn_sched_barrier(0);
             if (k + 1 < NB) fetch(k + 1, s ^ 1);
             hook(k);
-            if constexpr (!STATES) {
-                // state part of Y^T, K block k (state rows 16k.., before the update)
-                const F sa = MM::pack(st[k]);
+            // state part of Y^T, K block k (state rows 16k.., before the update)
+            const F sa = MM::pack(st[k]);
 #pragma unroll
-                for (int ib = 0; ib < NIB; ++ib) y[ib] = MM::mma(sa, fc[s][ib], y[ib]);
-                // this wave's S^T tiles
+            for (int ib = 0; ib < NIB; ++ib) y[ib] = MM::mma(sa, fc[s][ib], y[ib]);
+            // this wave's S^T tiles
 #pragma unroll
-                for (int j = 0; j < NSLOT; ++j) acc[j] = MM::mma(fsb[s][j], fsc[s][j], acc[j]);
-            }
+            for (int j = 0; j < NSLOT; ++j) acc[j] = MM::mma(fsb[s][j], fsc[s][j], acc[j]);
             // state rows of N block k
 #pragma unroll
             for (int m = 0; m < 4; ++m) st[k][m] *= dec;
@@ -610,7 +589,6 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         }
         __builtin_amdgcn_sched_barrier(0);
         after_part1();
-        if constexpr (!STATES) {
         // mask the score tiles: lane holds S^T[s = 16 sb + 4 g + m][i = 16 ib + l16]
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
@@ -637,9 +615,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
             for (int m = 0; m < 4; ++m) y[ib][m] *= el;
         }
-        }
         __syncthreads();
-        if constexpr (STATES) return;
 
         // ---- part 2: Y^T += X^T M^T, mixing, stores --------------------------------------
 #pragma unroll
@@ -771,21 +747,20 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     }
 
     // ---- outputs: final state and the last step's (Bbar, x) ------------------------------
-    // no split: the call's; pass 1: the segment's end state and last Bbar row, into the
-    // workspace; pass 2: the call's, from the last segment only; pass 3: the segment's end state
-    // into the workspace, its last Bbar row there too except in the last segment, which writes
-    // the call's Bbar_last, x_last and phi_out (h_out comes from segment_combine); pass 4: none
-    const bool last_seg = a.pass == 0 || a.pass == 1 || seg == a.nseg - 1;
-    const bool ws_out = a.pass == 1 || a.pass == 3;
-    float* hout = ws_out ? a.ws_state + (bh * a.nseg + seg) * (int64_t)(N * P)
-                         : (a.pass != 4 && last_seg ? a.h_out + bh * (int64_t)(N * P) : nullptr);
-    T* Blast = a.pass == 1 || (a.pass == 3 && !last_seg) ? (T*)a.ws_bbar + (bh * a.nseg + seg) * (int64_t)(R * N)
-               : (a.pass != 4 && last_seg && a.Bbar_last ? (T*)a.Bbar_last + bh * (int64_t)(R * N) : nullptr);
-    T* xlast = a.pass != 1 && a.pass != 4 && last_seg && a.x_last ? (T*)a.x_last + bh * (int64_t)(R * P) : nullptr;
-    float* phout = FUSED && a.pass != 1 && a.pass != 4 && last_seg && a.phi_out ? a.phi_out + bh * K : nullptr;
-    if ((STATES || a.pass == 3) && wave == NW - 1 && lane == 0) a.ws_l2[bh * a.nseg + seg] = l2sum;
-    if (a.pass == 3 && wave == NW - 1 && lane == 0)
+    // no split: the call's; pass 1: the segment's end state into the workspace, its last Bbar
+    // row there too except in the last segment, which writes the call's Bbar_last, x_last and
+    // phi_out (h_out comes from segment_combine); pass 2: none
+    const bool last_seg = a.pass == 0 || seg == a.nseg - 1;
+    float* hout = a.pass == 1 ? a.ws_state + (bh * a.nseg + seg) * (int64_t)(N * P)
+                              : (a.pass == 0 ? a.h_out + bh * (int64_t)(N * P) : nullptr);
+    T* Blast = a.pass == 1 && !last_seg ? (T*)a.ws_bbar + (bh * a.nseg + seg) * (int64_t)(R * N)
+               : (a.pass != 2 && last_seg && a.Bbar_last ? (T*)a.Bbar_last + bh * (int64_t)(R * N) : nullptr);
+    T* xlast = a.pass != 2 && last_seg && a.x_last ? (T*)a.x_last + bh * (int64_t)(R * P) : nullptr;
+    float* phout = FUSED && a.pass != 2 && last_seg && a.phi_out ? a.phi_out + bh * K : nullptr;
+    if (a.pass == 1 && wave == NW - 1 && lane == 0) {
+        a.ws_l2[bh * a.nseg + seg] = l2sum;
         a.ws_fix[bh * a.nseg + seg] = (int)min((int64_t)fix_chunks * Q, L);
+    }
     if (hout) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -819,9 +794,9 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     }
 }
 
-// Between the passes of a split sequence: the true end state of segment s (1 <= s <= nseg - 2;
-// after pass 3 also s = nseg - 1, whose result is the call's h_out) is its local end state (from
-// zero, passes 1 and 3) plus the carried state that enters it, decayed over the segment:
+// Between the passes of a split sequence: the true end state of segment s (1 <= s <= nseg - 1;
+// the last one's is the call's h_out) is its local end state (from zero, pass 1) plus the carried
+// state that enters it, decayed over the segment:
 //   g_end(s) = g_local(s) + 2^{l2(s)} (g_end(s - 1) + c_{t0} Bbar_{t0-1}^T x_{t0-1})
 // with l2(s) = log2 e * A * sum_{t in s} dt_t (saved by pass 1), t0 the segment's first step and
 // c_{t0} = (1 - lambda_{t0}) dt_{t0}: the recurrence is linear in its carry, and the carry term is
@@ -847,7 +822,7 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(PrefillArgs a) {
     // outer products u, the segments' own end states) is read before any result is written back,
     // since a load that follows a store to the workspace waits for it; only the chain through gp
     // is sequential.
-    const int last = a.pass == 3 ? a.nseg : a.nseg - 1;   // segments chained: 1 .. last - 1
+    const int last = a.nseg;   // segments chained: 1 .. last - 1
     for (int s0 = 1; s0 < last; s0 += kCombineBlk) {
         float decay[kCombineBlk], c0[kCombineBlk], u[kCombineBlk][4], own[kCombineBlk][4];
 #pragma unroll
@@ -885,37 +860,29 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(PrefillArgs a) {
     }
 }
 
-template <typename T, int N, int P, bool FUSED, bool STATES>
-hipError_t launch_nps(const PrefillArgs& a, hipStream_t s) {
-    const int64_t per_bh = a.pass == 0 ? 1 : (a.pass == 1 || a.pass == 4 ? a.nseg - 1 : a.nseg);
+template <typename T, int N, int P, bool FUSED>
+hipError_t launch_np(const PrefillArgs& a, hipStream_t s) {
+    const int64_t per_bh = a.pass == 0 ? 1 : (a.pass == 2 ? a.nseg - 1 : a.nseg);
     const dim3 grid((unsigned)(a.b * a.H * per_bh)), block(P / 16 * 64);
     // fused: BCNorm weights and biases in dynamic LDS
     const size_t dyn = FUSED ? (size_t)(2 * N + 2 * a.R * N) * sizeof(float) : 0;
     switch (a.Q * a.R) {
-        case 16: hipLaunchKernelGGL((prefill_kernel<T, N, P, 1, FUSED, STATES>), grid, block, dyn, s, a); break;
+        case 16: hipLaunchKernelGGL((prefill_kernel<T, N, P, 1, FUSED>), grid, block, dyn, s, a); break;
         case 32:
             // fused with ranks: two rows of one step per staging thread (angles taken once)
             if (FUSED && a.R >= 2)
-                hipLaunchKernelGGL((prefill_kernel<T, N, P, 2, FUSED, STATES, true>), grid, block, dyn, s, a);
+                hipLaunchKernelGGL((prefill_kernel<T, N, P, 2, FUSED, true>), grid, block, dyn, s, a);
             else
-                hipLaunchKernelGGL((prefill_kernel<T, N, P, 2, FUSED, STATES>), grid, block, dyn, s, a);
+                hipLaunchKernelGGL((prefill_kernel<T, N, P, 2, FUSED>), grid, block, dyn, s, a);
             break;
         case 48:
-            if (FUSED || STATES) return hipErrorInvalidValue;   // never split (48 does not divide 512)
+            if (FUSED || a.pass) return hipErrorInvalidValue;   // never split (48 does not divide 512)
             hipLaunchKernelGGL((prefill_kernel<T, N, P, 3, false>), grid, block, 0, s, a);
             break;
-        case 64: hipLaunchKernelGGL((prefill_kernel<T, N, P, 4, FUSED, STATES>), grid, block, dyn, s, a); break;
+        case 64: hipLaunchKernelGGL((prefill_kernel<T, N, P, 4, FUSED>), grid, block, dyn, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
-}
-
-// passes 1 and 2 split m3_prefill, passes 3 and 4 the fused call
-template <typename T, int N, int P, bool FUSED>
-hipError_t launch_np(const PrefillArgs& a, hipStream_t s) {
-    if (FUSED ? a.pass == 1 || a.pass == 2 : a.pass >= 3) return hipErrorInvalidValue;
-    if constexpr (FUSED) return launch_nps<T, N, P, true, false>(a, s);
-    else return a.pass == 1 ? launch_nps<T, N, P, false, true>(a, s) : launch_nps<T, N, P, false, false>(a, s);
 }
 
 template <typename T, bool FUSED>

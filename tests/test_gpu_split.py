@@ -1,9 +1,8 @@
 """GPU parity of the sequence split of m3_prefill and m3_layer_prefill: with few (b, h) pairs and
-long sequences, and a workspace, each sequence runs as segments in parallel.  m3_prefill: pass 1
-(end states from zero carries), a chaining kernel, pass 2 (every segment from its true carry).
-m3_layer_prefill: pass 3 (every segment, y included, the later ones from zero carries), the
-chaining, pass 4 (each later segment's first steps again from its true carry, until the carry's
-share of y has decayed by 2^-48).  Checked against the fp64 oracle's
+long sequences, and a workspace, each sequence runs as segments in parallel: pass 1 (every
+segment, y included, the later ones from zero carries), a chaining kernel, pass 2 (each later
+segment's first steps again from its true carry, until the carry's share of y has decayed by
+2^-48).  Checked against the fp64 oracle's
 layer core over the whole sequence, with carries in, ragged last segments and 2-4 segments (so
 that the chaining runs); the same call run in one pass is checked against the oracle too.
 Every call goes through the C ABI (via the ctypes binding).  Tolerances are those of
@@ -115,13 +114,13 @@ def test_split_layer_prefill_in_place_carry():
 
 
 def test_split_rerun_lengths():
-    """Pass 4's rerun length per segment, from the log2 decay l2(t) = log2(e) A sum_{s <= t} dt_s
+    """Pass 2's rerun length per segment, from the log2 decay l2(t) = log2(e) A sum_{s <= t} dt_s
     counted from the segment's start: whole 16-step chunks up to the last chunk whose first step
     still has l2 >= -48 (the decay is monotone here, so that step is the chunk's largest).  Three
     heads at the extremes: A = -1e-4 (the carry never decays: every segment is rerun whole),
     A = -40 (gone within a chunk) and A = -16 with dt = 4 at each segment's first step (gone at
     that step: nothing is rerun).  The recorded lengths are read back from the workspace, and y,
-    h_out and phi_out checked against the oracle."""
+    h_out and phi_out checked against the oracle, through m3_layer_prefill and m3_prefill."""
     L, H, P, N, R, Q = 4100, 3, 64, 128, 2, 16
     w = _wl("bf16", 1, L, H, P, N, R, Q, True)
     inp = inputs.make_prefill_inputs(w, seed=86, normw=True, carry=True)
@@ -145,21 +144,34 @@ def test_split_rerun_lengths():
     assert rel_err(h, ref["h_out"]) <= TOL["bf16"]
     assert angle_err(phi, ref["phi_out"]) <= 1e-3
     fix = ws[off_fix:off_fix + H * nseg * 4].view(torch.int32).view(H, nseg).cpu()
+    # the same split through m3_prefill (its workspace ends after the rerun lengths)
+    Bb, Cb, _ = m3scan.m3_bcnorm_rope(d["B"], d["C"], d["dt"], d["theta"], d["normw_B"], d["normw_C"],
+                                      d["bias_B"], d["bias_C"], d["phi_in"])
+    need2 = m3scan.prefill_workspace_bytes(_dims(w, Q))
+    assert need2 == off_fix + r(H * nseg * 4)
+    ws2 = torch.empty(need2, dtype=torch.uint8, device=DEV)
+    y2, h2 = m3scan.m3_prefill(d["x"], Bb, Cb, d["dt"], d["A"], d["lam"], d["w_out"], d["h_in"],
+                               d["Bbar_prev"], d["x_prev"], chunk=Q, workspace=ws2)
+    torch.cuda.synchronize()
+    assert rel_err(y2, ref["y"]) <= TOL["bf16"]
+    assert rel_err(h2, ref["h_out"]) <= TOL["bf16"]
+    fix2 = ws2[off_fix:off_fix + H * nseg * 4].view(torch.int32).view(H, nseg).cpu()
     dt = inp["dt"][0].double()
-    for hh in range(H):
-        for s in range(nseg):
-            t0, t1 = s * seglen, min((s + 1) * seglen, L)
-            l2 = torch.cumsum(dt[t0:t1, hh] * float(inp["A"][hh]) * 1.4426950408889634, 0)
-            firsts = l2[::Q]
-            # a chunk whose first step sits within 1e-3 of the threshold may go either way in fp32
-            lo = [c + 1 for c in range(len(firsts)) if firsts[c] >= -48 + 1e-3]
-            hi = [c + 1 for c in range(len(firsts)) if firsts[c] >= -48 - 1e-3]
-            lo = min(max(lo, default=0) * Q, t1 - t0)
-            hi = min(max(hi, default=0) * Q, t1 - t0)
-            assert lo <= int(fix[hh, s]) <= hi, (hh, s, int(fix[hh, s]), lo, hi)
-    assert fix[0].tolist() == [1536, 1536, 1028]
-    assert fix[1].tolist() == [Q, Q, Q]
-    assert fix[2, 1:].tolist() == [0, 0]
+    for f in (fix, fix2):
+        for hh in range(H):
+            for s in range(nseg):
+                t0, t1 = s * seglen, min((s + 1) * seglen, L)
+                l2 = torch.cumsum(dt[t0:t1, hh] * float(inp["A"][hh]) * 1.4426950408889634, 0)
+                firsts = l2[::Q]
+                # a chunk whose first step sits within 1e-3 of the threshold may go either way in fp32
+                lo = [c + 1 for c in range(len(firsts)) if firsts[c] >= -48 + 1e-3]
+                hi = [c + 1 for c in range(len(firsts)) if firsts[c] >= -48 - 1e-3]
+                lo = min(max(lo, default=0) * Q, t1 - t0)
+                hi = min(max(hi, default=0) * Q, t1 - t0)
+                assert lo <= int(f[hh, s]) <= hi, (hh, s, int(f[hh, s]), lo, hi)
+        assert f[0].tolist() == [1536, 1536, 1028]
+        assert f[1].tolist() == [Q, Q, Q]
+        assert f[2, 1:].tolist() == [0, 0]
 
 
 def test_split_workspace_too_small_is_rejected():
@@ -192,10 +204,11 @@ def _oracle_heads(inp, heads, G, H, mix):
 
 def test_split_in_place_carry_with_reordered_segments():
     """The in-place carry (h_out = h_in, phi_out = phi_in) on a split whose segments run out of
-    order: 100 (b, h) pairs in 6 segments (pass 2: 600 workgroups, more than the 512 the GPU holds
+    order: 100 (b, h) pairs in 6 segments (pass 1: 600 workgroups, more than the 512 the GPU holds
     at once; 6 does not divide 600 / 8 = 75), heads in 25 groups of 4, so the grouped launch
     reorders its workgroups XCD by XCD and some pairs' segment 0 starts after their last segment
-    has written h_out.  Sampled heads (among them 12, whose segment 0 runs in block 576 and last
+    has finished (a pass that wrote h_out or phi_out would have overwritten the carry before
+    segment 0 read it).  Sampled heads (among them 12, whose segment 0 runs in block 576 and last
     segment in block 17) against the oracle; then m3_prefill with its state in place, on the same
     shape per head."""
     H, G, L = 100, 25, 6144

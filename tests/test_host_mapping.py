@@ -2,10 +2,11 @@
 launches use (csrc/m3_mapping.h, compiled here with the host compiler, no GPU).
 
 The map must be a permutation of the grid's items: every (b, h, segment) item runs exactly once.
-It also reorders the items, so the segments of one sequence are not dispatched in order: the
-split prefill's pass 2 can therefore not rely on segment 0 starting before the last segment ends
-(why pass 2 reads the carried-in state from the workspace, not from h_in, which the last segment
-may overwrite when h_out is the h_in buffer)."""
+It also reorders the items, so the segments of one sequence are not dispatched in order: no
+segment of a split prefill's pass may rely on segment 0 starting before the last segment ends
+(why no segment of a pass writes h_out or phi_out while segment 0 of the same pass may still
+read h_in or phi_in from the same buffer: h_out comes from the chaining kernel between the
+passes, and every segment takes its start angle from the angle pass)."""
 from __future__ import annotations
 
 import os
@@ -30,7 +31,7 @@ int main() {
             if (it < 0 || it >= n || seen[it]++) { std::printf("BAD %ld %ld\n", n, i); return 1; }
         }
     }
-    // 100 (b, h) pairs in 6 segments (pass 2 of a split sequence): the blocks that run segment 0
+    // 100 (b, h) pairs in 6 segments (pass 1 of a split sequence): the blocks that run segment 0
     // and the last segment of pair 12
     const long n = 600, segs = 6, bh = 12;
     long first = -1, last = -1;
