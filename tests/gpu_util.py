@@ -39,6 +39,24 @@ def per_head_rel_err(gpu, ref, head_axis_from_end):
     return worst
 
 
+def per_step_rel_err(gpu, ref, axis, floor=1e-2):
+    """Worst over the steps along `axis` of max|gpu_t - ref_t| / max|ref_t|, where a step whose
+    reference is below `floor` times the largest one is measured against that floor instead (a
+    step whose output is near zero, e.g. where Cbar_t . Bbar_t nearly cancels, has no relative
+    scale of its own: its absolute error is the usual one)."""
+    g = to_np(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    assert np.isfinite(g).all()
+    g, r = np.moveaxis(g, axis, 0), np.moveaxis(r, axis, 0)
+    big = np.abs(r).max()
+    worst = 0.0
+    for t in range(r.shape[0]):
+        s = max(np.abs(r[t]).max(), floor * big, 1e-300)
+        worst = max(worst, float(np.abs(g[t] - r[t]).max() / s))
+    return worst
+
+
 def angle_err(gpu_phi, ref_phi):
     d = to_np(gpu_phi) - np.asarray(ref_phi, dtype=np.float64)
     d = (d + math.pi) % (2 * math.pi) - math.pi

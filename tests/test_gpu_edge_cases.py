@@ -28,7 +28,7 @@ import torch
 
 import oracle
 import pins
-from gpu_util import TOL, angle_err, rel_err, to_np
+from gpu_util import TOL, angle_err, per_step_rel_err, rel_err, to_np
 from state_space_sequence_m3_amd import m3scan
 
 pytestmark = pytest.mark.gpu
@@ -95,21 +95,6 @@ def _decode_chain(d, bcnorm, mix):
     return torch.stack(ys, 1), h, phi
 
 
-def _per_step_err(gpu, ref, floor=1e-2):
-    """Worst over steps of max|gpu_t - ref_t| / max|ref_t|, with steps whose reference is below
-    `floor` times the largest one measured against that floor instead (a step whose output is
-    near zero has no relative scale of its own)."""
-    g, r = to_np(gpu), np.asarray(ref, dtype=np.float64)
-    assert g.shape == r.shape, (g.shape, r.shape)
-    assert np.isfinite(g).all()
-    big = np.abs(r).max()
-    worst = 0.0
-    for t in range(r.shape[1]):
-        s = max(np.abs(r[:, t]).max(), floor * big, 1e-300)
-        worst = max(worst, float(np.abs(g[:, t] - r[:, t]).max() / s))
-    return worst
-
-
 def _cotangents(inp, mix, seed):
     rng = np.random.default_rng(seed)
     b, L, H, R, P = inp["x"].shape
@@ -168,7 +153,7 @@ def _check_all_paths(inp, io, chunk, bcnorm=False, mix=False, decode=True, backw
     if decode:
         y3, h3, phi3 = _decode_chain(d, bcnorm, mix)
         torch.cuda.synchronize()
-        results["m3_layer_decode_step"] = (_per_step_err(y3, ref["y"]), rel_err(h3, ref["h_out"]),
+        results["m3_layer_decode_step"] = (per_step_rel_err(y3, ref["y"], 1), rel_err(h3, ref["h_out"]),
                                             angle_err(phi3, ref["phi_out"]))
     print({k: tuple("%.2e" % e for e in v) if isinstance(v, tuple) else "%.2e" % v
            for k, v in results.items()}, flush=True)

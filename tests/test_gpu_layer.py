@@ -65,7 +65,8 @@ def test_layer_parity(case):
     ref = oracle.layer(inp, bcnorm=bcnorm, mix=mix)
     tol = TOL[io]
     assert rel_err(y, ref["y"]) <= tol
-    assert per_head_rel_err(y, ref["y"], 2 if mix else 3) <= 2 * tol
+    ph = per_head_rel_err(y, ref["y"], 2 if mix else 3)
+    assert ph <= tol, ph
     assert rel_err(h, ref["h_out"]) <= tol
     assert angle_err(phi, ref["phi_out"]) <= (1e-3 if io == "bf16" else 1e-4)
     assert rel_err(Blast, ref["Bbar_last"]) <= tol

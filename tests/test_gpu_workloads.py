@@ -6,9 +6,16 @@ approximately).  Inputs are drawn on the device with a seeded generator; the sam
 copied to the host for the oracle.
 
 Errors are normwise per output tensor, max|gpu - ref| / max|ref|; for decode the output tensor is
-y over all decode steps of the run.  (A single step's y can be far below its typical size when
-Cbar_t . Bbar_t nearly cancels; its absolute error is then the usual one, set by the bf16 rounding
-of Bbar and Cbar, so a per-step ratio is not a meaningful measure there.)
+y over all decode steps of the run, and each step's y is also judged on its own: its error
+against its own largest value, or against a floor of the run's largest where the step's y is
+smaller than that (a single step's y can be far below its typical size when the sum over the
+state rows nearly cancels; its absolute error is then the usual one).  The floor is 1% for
+m3_layer_decode_step and 10% for m3_bcnorm_rope + m3_decode_step, whose rotated Bbar and Cbar are
+rounded to bf16 between the two calls: that rounding (2^-9 of each element) reaches y_t through a
+sum over the N state rows and the state built from the rounded Bbar, and leaves an absolute error
+of about 1e-3 of the run's largest y in a cancelling step (1.1e-3 at worst over the sampled
+pairs), so 1% would judge rounding as failure.  A step that is wrong (a stale or missing carry, a
+skipped update) is off by the order of its own size and fails either bar.
 """
 from __future__ import annotations
 
@@ -17,7 +24,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import TOL, angle_err, rel_err, to_np
+from gpu_util import TOL, angle_err, per_step_rel_err, rel_err, to_np
 from state_space_sequence_m3_amd import inputs, m3scan
 
 pytestmark = pytest.mark.gpu
@@ -63,8 +70,8 @@ def _fused_layer(d, w):
 
 
 @pytest.mark.parametrize("name,pairs", [
-    ("siso_b8_l2048", [(0, 0), (3, 17), (7, 63)]),
-    ("mimo4_b8_l2048", [(0, 5), (6, 40)]),
+    ("siso_b8_l2048", [(0, 0), (1, 31), (2, 46), (3, 17), (5, 8), (7, 63)]),
+    ("mimo4_b8_l2048", [(0, 5), (2, 62), (4, 23), (6, 40)]),
     ("mamba2_siso_b8_l2048", [(1, 2), (7, 60)]),
     ("siso_n64_b8_l2048", [(2, 9), (5, 33)]),
     # the rest of the comparison grid (Mamba-2 mode / SISO / MIMO R = 4 x fp32 / bf16 x N 64 / 128)
@@ -124,11 +131,11 @@ def _decode_steps(w, dinp, steps, mix, h, phi, Bprev, xprev, consts_dev, toks, f
 
 
 @pytest.mark.parametrize("name,pairs", [
-    ("decode_b128_r1", [(0, 0), (77, 31), (127, 63)]),
-    ("decode_b128_r4", [(5, 2), (120, 60)]),
+    ("decode_b128_r1", [(0, 0), (40, 50), (77, 31), (127, 63)]),
+    ("decode_b128_r4", [(5, 2), (64, 33), (99, 9), (120, 60)]),
     # a state four times the Infinity Cache (the DRAM-bound decode lines of the benchmark)
-    ("decode_b512_r1", [(0, 0), (511, 63)]),
-    ("decode_b512_r4", [(300, 7)]),
+    ("decode_b512_r1", [(0, 0), (255, 12), (511, 63)]),
+    ("decode_b512_r4", [(100, 44), (300, 7), (511, 0)]),
 ])
 @pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 def test_decode_workload_sampled(name, pairs, fused):
@@ -142,6 +149,8 @@ def test_decode_workload_sampled(name, pairs, fused):
     ys, _, _ = _decode_steps(w, dinp, steps, w.mix, h, phi, st["Bbar_prev"].clone(),
                              st["x_prev"].clone(), dinp, dinp["tokens"], fused=fused)
     torch.cuda.synchronize()
+    floor = 1e-2 if fused else 1e-1
+    step_errs = []
     for bi, hi in pairs:
         consts = {"A": dinp["A"][hi:hi + 1].cpu(), "bias_B": dinp["bias_B"][hi:hi + 1].cpu(),
                   "bias_C": dinp["bias_C"][hi:hi + 1].cpu(),
@@ -153,12 +162,15 @@ def test_decode_workload_sampled(name, pairs, fused):
             tok = {k: dinp["tokens"][k][s, bi:bi + 1, hi:hi + 1].cpu() for k in SEQ_KEYS}
             ry, state = oracle.decode_step(state, tok, consts, mix=w.mix)
             rys.append(ry)
-        # y over all decode steps is one output tensor: normwise error over the whole of it
+        # y over all decode steps is one output tensor: normwise error over the whole of it, and
+        # step by step
         yg = torch.stack([y[bi:bi + 1, hi:hi + 1] for y in ys], 0)
         err = rel_err(yg, np.stack(rys, 0))
         assert err <= TOL[w.io], (bi, hi, err)
+        step_errs.append((bi, hi, per_step_rel_err(yg, np.stack(rys, 0), 0, floor)))
         assert rel_err(h[bi:bi + 1, hi:hi + 1], state["h"]) <= TOL[w.io]
         assert angle_err(phi[bi:bi + 1, hi:hi + 1], state["phi"]) <= 1e-3
+    assert max(e for _, _, e in step_errs) <= TOL[w.io], step_errs
 
 
 def test_long_context_prefill_then_decode_sampled():
@@ -193,8 +205,11 @@ def test_long_context_prefill_then_decode_sampled():
             tok = {k: toks[k][s, 0:1, hi:hi + 1].cpu() for k in SEQ_KEYS}
             ry, state = oracle.decode_step(state, tok, consts, mix=True)
             rys.append(ry)
-        err = rel_err(torch.stack([y[:, hi:hi + 1] for y in ys], 0), np.stack(rys, 0))
+        yg = torch.stack([y[:, hi:hi + 1] for y in ys], 0)
+        err = rel_err(yg, np.stack(rys, 0))
         assert err <= TOL["bf16"], (hi, err)
+        serr = per_step_rel_err(yg, np.stack(rys, 0), 0)
+        assert serr <= TOL["bf16"], (hi, serr)
         assert rel_err(h[:, hi:hi + 1], state["h"]) <= TOL["bf16"]
         assert angle_err(phi[:, hi:hi + 1], state["phi"]) <= 1e-3
 
@@ -210,7 +225,7 @@ def test_long_context_layer_prefill_sampled():
     y, h, phi = m3scan.m3_layer_prefill(inp["x"], inp["B"], inp["C"], inp["dt"], inp["theta"], inp["A"],
                                         inp["lam"], None, None, inp["bias_B"], inp["bias_C"], inp["w_out"])
     torch.cuda.synchronize()
-    for hi in (3, 58):
+    for hi in (3, 20, 47, 58):
         ref = oracle.layer(_slice_pair(inp, 0, hi), mix=True)
         assert rel_err(y[:, :, hi:hi + 1], ref["y"]) <= TOL["bf16"], hi
         assert rel_err(h[:, hi:hi + 1], ref["h_out"]) <= TOL["bf16"], hi
