@@ -229,9 +229,11 @@ size_t m3_prefill_workspace_bytes(const m3_dims* dims);
  * other shapes return M3_E_UNSUPPORTED.  The sequence length limit of m3_prefill applies (with
  * the angle carried as phi_in / phi_out when a sequence is split).  The workspace (optional,
  * m3_layer_prefill_workspace_bytes(dims) bytes, 16-byte aligned) enables the sequence split of
- * m3_prefill, for the same dims and with the same passes; the segments' start angles come from
- * the sums of dt * theta per 512 steps, as m3_bcnorm_rope computes them.  Workspace errors as
- * m3_prefill.
+ * m3_prefill, for the same dims and with the same passes.  The later segments' first pass also
+ * starts from angle zero (y depends only on the differences of the angles inside a segment when
+ * the carried state is zero); the chaining adds up the segments' angle sums into true start
+ * angles and turns the end states and last Bbar rows by them (the call's Bbar_last is thereby
+ * rounded to the io type twice).  Workspace errors as m3_prefill.
  */
 m3_status m3_layer_prefill(const m3_dims* dims, const void* x, const void* B, const void* C,
                            const void* dt, const void* theta, const float* normw_B,

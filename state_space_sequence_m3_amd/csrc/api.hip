@@ -156,12 +156,12 @@ int device_cus() {
 // few to give every compute unit two workgroups, each sequence is cut into segments of a
 // multiple of 512 steps (at least 1024 each) that run in parallel, then are chained (see
 // PrefillArgs).  Workspace: the segments' end states, the rotated Bbar of their last steps, their
-// log2 decays, the steps of each segment to rerun and, fused, the start angles of each segment's
-// quarters (m3_bcnorm_rope's angle kernels over the same segments) and a final-angle scratch row.
+// log2 decays, the steps of each segment to rerun and, fused, each segment's end angle from the
+// first pass and its true start angle.
 struct SplitPlan {
     int nseg = 1;
-    int64_t seglen = 0, nsegA = 0;
-    size_t off_state = 0, off_bbar = 0, off_l2 = 0, off_fix = 0, off_phi = 0, off_phiend = 0, total = 0;
+    int64_t seglen = 0;
+    size_t off_state = 0, off_bbar = 0, off_l2 = 0, off_fix = 0, off_phiend = 0, off_phi = 0, total = 0;
 };
 constexpr int64_t kSplitAlign = 512, kSplitMin = 1024;
 
@@ -188,10 +188,9 @@ SplitPlan split_plan(const m3_dims* d, int64_t Q, bool fused, bool packed) {
     sp.off_fix = sp.off_l2 + align256((size_t)(pairs * nseg) * 4);
     sp.total = sp.off_fix + align256((size_t)(pairs * nseg) * 4);
     if (fused) {
-        sp.nsegA = nseg;   // the angle pass sums dt * theta over the same segments
-        sp.off_phi = sp.total;
-        sp.off_phiend = sp.off_phi + align256((size_t)(pairs * sp.nsegA * m3::bcnorm_rope_parts() * (N / 2)) * 4);
-        sp.total = sp.off_phiend + align256((size_t)(pairs * (N / 2)) * 4);
+        sp.off_phiend = sp.total;
+        sp.off_phi = sp.off_phiend + align256((size_t)(pairs * nseg * (N / 2)) * 4);
+        sp.total = sp.off_phi + align256((size_t)(pairs * nseg * (N / 2)) * 4);
     }
     return sp;
 }
@@ -209,9 +208,10 @@ m3_status check_split_workspace(const SplitPlan& sp, const void* ws, size_t ws_b
     return M3_OK;
 }
 
-// A split prefill (fused: after the angle pass): pass 1 (every segment, the later ones from
-// zero), chaining (which also gives h_out), pass 2 (the later segments' first steps again, from
-// their true carry, until the carry's share of y has decayed below float rounding)
+// A split prefill: pass 1 (every segment; the later ones from zero state and, fused, zero
+// angle), chaining (true start angles, entering states, h_out, Bbar_last, phi_out), pass 2 (the
+// later segments' first steps again, from their entering state, until the carry's share of y has
+// decayed below float rounding)
 hipError_t run_split(m3::PrefillArgs a, const SplitPlan& sp, void* ws, bool fused, bool bf16, hipStream_t s) {
     char* w = (char*)ws;
     a.nseg = sp.nseg;
@@ -220,31 +220,13 @@ hipError_t run_split(m3::PrefillArgs a, const SplitPlan& sp, void* ws, bool fuse
     a.ws_bbar = w + sp.off_bbar;
     a.ws_l2 = (float*)(w + sp.off_l2);
     a.ws_fix = (int*)(w + sp.off_fix);
-    hipError_t e = hipSuccess;
-    if (fused) {
-        m3::BcnormRopeArgs g{};
-        g.dt = a.dt;
-        g.theta = a.theta;
-        g.phi_in = a.phi_in;
-        g.seg_phi = (float*)(w + sp.off_phi);
-        g.phi_out = (float*)(w + sp.off_phiend);
-        g.b = a.b;
-        g.L = a.L;
-        g.H = a.H;
-        g.N = a.N;
-        g.R = a.R;
-        g.seglen = sp.seglen;
-        g.nseg = (int)sp.nsegA;
-        e = m3::launch_segment_angles(g, bf16, s);
-        a.seg_phi = g.seg_phi;
-        a.angle_seglen = g.seglen;
-        a.angle_parts = m3::bcnorm_rope_parts();
-    }
+    a.ws_phiend = fused ? (float*)(w + sp.off_phiend) : nullptr;
+    a.seg_phi = fused ? (float*)(w + sp.off_phi) : nullptr;
     auto run = [&](const m3::PrefillArgs& pa) {
         return fused ? m3::launch_layer(pa, bf16, s) : m3::launch_prefill(pa, bf16, s);
     };
     a.pass = 1;
-    if (e == hipSuccess) e = run(a);
+    hipError_t e = run(a);
     if (e == hipSuccess) e = m3::launch_segment_combine(a, bf16, s);
     a.pass = 2;
     if (e == hipSuccess) e = run(a);

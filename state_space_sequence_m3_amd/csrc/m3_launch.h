@@ -96,22 +96,25 @@ struct PrefillArgs {
     int64_t T = 0;
     // Sequence split (few (b, h) pairs, long sequences): each sequence is cut into nseg segments
     // of seglen steps.  pass 0 = no split.  pass 1 runs every segment at once, segment 0 from the
-    // call's carry and the others from zero, writing y, each segment's end state, last rotated
-    // Bbar, log2 decay and ws_fix (the steps from the segment's start after which the carried-in
-    // state's share of y, which decays as 2^l2, stays below 2^-48 of its size), and in the last
-    // segment the call's angle and last-step outputs; segment_combine chains the end states (and
-    // writes h_out); pass 2 reruns the first ws_fix steps of segments 1 .. nseg-1 from their true
-    // carry, writing y only.
+    // call's carry (state, last step, angle) and the others from zero, writing y, each segment's
+    // end state, last Bbar row, log2 decay, end angle (fused) and ws_fix (the steps from the
+    // segment's start after which the carried-in state's share of y, which decays as 2^l2, stays
+    // below 2^-48 of its size), and the call's x_last from the last segment; segment_combine
+    // chains the end angles into true start angles, turns the later segments' end states and
+    // Bbar rows to them, chains the end states (leaving in each segment's slot the state that
+    // enters the next one), and writes h_out, Bbar_last and phi_out; pass 2 reruns the first
+    // ws_fix steps of segments 1 .. nseg-1 from their entering state and true start angle,
+    // writing y only.
     int pass = 0;
     int nseg = 1;
     int64_t seglen = 0;
-    float* ws_state = nullptr;       // [b, H, nseg, N, P] end state of each segment
-    void* ws_bbar = nullptr;         // [b, H, nseg, R, N] io, rotated Bbar of each segment's last step
+    float* ws_state = nullptr;       // [b, H, nseg, N, P] end state of each segment (pass 1)
+    void* ws_bbar = nullptr;         // [b, H, nseg, R, N] io, Bbar of each segment's last step (pass 1)
     float* ws_l2 = nullptr;          // [b, H, nseg] log2 decay of each segment (log2 e A sum of dt)
     int* ws_fix = nullptr;           // [b, H, nseg] pass 1 -> pass 2: steps of each segment to rerun
-    const float* seg_phi = nullptr;  // fused: angle-segment start angles [b, H, nsegA, parts, N/2] (radians)
-    int64_t angle_seglen = 0;        // steps per angle segment (seglen or a divisor of it)
-    int angle_parts = 0;             // start angles per angle segment
+    float* ws_phiend = nullptr;      // fused: [b, H, nseg, N/2] end angle of each segment in pass 1
+                                     // (radians; segment 0 true, the others from zero)
+    float* seg_phi = nullptr;        // fused: [b, H, nseg, N/2] true start angle of each segment
     // fused layer only: raw B and C hold G head slots, head h reads slot h / (H / G) (0: one slot
     // per head); the heads of a group are then laid out on one XCD (see xcd_block)
     int G = 0;
@@ -196,10 +199,7 @@ hipError_t launch_prefill(const PrefillArgs& a, bool bf16_io, hipStream_t s);
 
 bool layer_supported(int N, int P, int R, int QR, bool bf16_io);
 hipError_t launch_layer(const PrefillArgs& a, bool bf16_io, hipStream_t s);
-// between the two passes of a split sequence: true end states of segments 1 .. nseg-2
+// between the two passes of a split sequence: true start angles, end states and last Bbar rows
 hipError_t launch_segment_combine(const PrefillArgs& a, bool bf16_io, hipStream_t s);
-// the start angle of every angle segment (seg_phi) and the final angle: the first two kernels of
-// m3_bcnorm_rope alone
-hipError_t launch_segment_angles(const BcnormRopeArgs& a, bool bf16_io, hipStream_t s);
 
 }  // namespace m3

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         if (a.pass == 2) L = min(L, (int64_t)a.ws_fix[bh * a.nseg + seg]);
     }
     // carried in: the call's carry (no split, or segment 0), none (the later segments in pass 1),
-    // or the previous segment's chained end state and its last step (pass 2)
+    // or the chained state entering the segment (pass 2)
     const bool own_carry = seg == 0;
     const int64_t nchunk = (L + Q - 1) / Q;
     const float Alog2 = a.A[h] * kLog2e;
@@ -177,9 +177,8 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
         Bprev = a.Bbar_prev ? (const T*)a.Bbar_prev + bh * (int64_t)(R * N) : nullptr;
         xprev = a.x_prev ? (const T*)a.x_prev + bh * (int64_t)(R * P) : nullptr;
     } else if (a.pass == 2) {
+        // the state entering the segment, the previous step's term included (the chaining adds it)
         hin = a.ws_state + (bh * a.nseg + seg - 1) * (int64_t)(N * P);
-        Bprev = (const T*)a.ws_bbar + (bh * a.nseg + seg - 1) * (int64_t)(R * N);
-        xprev = Xg - HRP;   // step t_first - 1 of this head
     }
     const int pcol = 16 * wave + l16;            // this lane's column of P in MFMA tiles
     // One buffer descriptor per stream over this sequence: from step 0 of this (b, h) to the end
@@ -294,17 +293,16 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     // on the last step's angle.  The carried angle is the last row of buffer `prev` (the previous
     // chunk), read first: without pipelining prev == out.  Chunk 0 starts from phi_in (radians).
     const int kcol = wave * KWL + (lane & (KWL - 1)), run = lane / KWL;
-    // angle carried in (radians): the call's, or the segment's start angle from the angle pass
-    // (a split sequence takes every segment's start angle from the angle pass, segment 0's too:
-    // phi_out may be the phi_in buffer, and the last segment writes it)
+    // angle carried in (radians): the call's (no split, and segment 0 of pass 1), none (the
+    // later segments of pass 1: their angles run from zero), or the segment's true start angle
+    // from the chaining (pass 2).  A pass-1 segment from zero has the y of its true angles (y
+    // depends on differences of the angles in a segment only, and on the carried state, which is
+    // zero there); its end state and last Bbar row come out rotated back by its start angle,
+    // which the chaining applies.
     const float* phin = nullptr;
     if (FUSED) {
-        if (a.pass == 0) {
-            phin = a.phi_in ? a.phi_in + bh * K : nullptr;
-        } else {
-            const int64_t nsegA = (a.L + a.angle_seglen - 1) / a.angle_seglen;
-            phin = a.seg_phi + (bh * nsegA + seg * (a.seglen / a.angle_seglen)) * a.angle_parts * (int64_t)K;
-        }
+        if (a.pass == 0 || (a.pass == 1 && seg == 0)) phin = a.phi_in ? a.phi_in + bh * K : nullptr;
+        else if (a.pass == 2) phin = a.seg_phi + (bh * a.nseg + seg) * (int64_t)K;
     }
     auto scan = [&](int64_t c, int out, int prev) {
         if (!FUSED) return;
@@ -747,16 +745,18 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     }
 
     // ---- outputs: final state and the last step's (Bbar, x) ------------------------------
-    // no split: the call's; pass 1: the segment's end state into the workspace, its last Bbar
-    // row there too except in the last segment, which writes the call's Bbar_last, x_last and
-    // phi_out (h_out comes from segment_combine); pass 2: none
+    // no split: the call's; pass 1: the segment's end state, last Bbar row and (fused) end angle
+    // into the workspace, and the call's x_last from the last segment (segment_combine writes
+    // h_out, Bbar_last and phi_out); pass 2: none
     const bool last_seg = a.pass == 0 || seg == a.nseg - 1;
     float* hout = a.pass == 1 ? a.ws_state + (bh * a.nseg + seg) * (int64_t)(N * P)
                               : (a.pass == 0 ? a.h_out + bh * (int64_t)(N * P) : nullptr);
-    T* Blast = a.pass == 1 && !last_seg ? (T*)a.ws_bbar + (bh * a.nseg + seg) * (int64_t)(R * N)
-               : (a.pass != 2 && last_seg && a.Bbar_last ? (T*)a.Bbar_last + bh * (int64_t)(R * N) : nullptr);
+    T* Blast = a.pass == 1 ? (T*)a.ws_bbar + (bh * a.nseg + seg) * (int64_t)(R * N)
+               : (a.pass == 0 && a.Bbar_last ? (T*)a.Bbar_last + bh * (int64_t)(R * N) : nullptr);
     T* xlast = a.pass != 2 && last_seg && a.x_last ? (T*)a.x_last + bh * (int64_t)(R * P) : nullptr;
-    float* phout = FUSED && a.pass != 2 && last_seg && a.phi_out ? a.phi_out + bh * K : nullptr;
+    float* phout = !FUSED ? nullptr
+                   : (a.pass == 1 ? a.ws_phiend + (bh * a.nseg + seg) * (int64_t)K
+                                  : (a.pass == 0 && a.phi_out ? a.phi_out + bh * K : nullptr));
     if (a.pass == 1 && wave == NW - 1 && lane == 0) {
         a.ws_l2[bh * a.nseg + seg] = l2sum;
         a.ws_fix[bh * a.nseg + seg] = (int)min((int64_t)fix_chunks * Q, L);
@@ -794,67 +794,152 @@ __global__ __launch_bounds__(P / 16 * 64, 2) void prefill_kernel(PrefillArgs a) 
     }
 }
 
-// Between the passes of a split sequence: the true end state of segment s (1 <= s <= nseg - 1;
-// the last one's is the call's h_out) is its local end state (from zero, pass 1) plus the carried
-// state that enters it, decayed over the segment:
+// Between the passes of a split sequence.  Angles (fused calls): segment 1 starts at segment 0's
+// end angle from pass 1 (segment 0 ran at its true angles) and segment s + 1 at segment s's start
+// plus the angle sum segment s formed from zero in pass 1; a segment that ran from angle 0 has
+// its end state and last Bbar row off by a rotation by its start angle, and rotations of a pair
+// add, so turning each (2k, 2k + 1) row pair by pair k's start angle gives the true ones.  States:
+// the true end state of segment s (1 <= s <= nseg - 1; the last one is the call's h_out) is its
+// own end state (from zero, turned) plus the carried state that enters it, decayed over the
+// segment:
 //   g_end(s) = g_local(s) + 2^{l2(s)} (g_end(s - 1) + c_{t0} Bbar_{t0-1}^T x_{t0-1})
 // with l2(s) = log2 e * A * sum_{t in s} dt_t (saved by pass 1), t0 the segment's first step and
 // c_{t0} = (1 - lambda_{t0}) dt_{t0}: the recurrence is linear in its carry, and the carry term is
-// the one the scan adds for a carried (Bbar_prev, x_prev).  kCombineElems state elements per
-// workgroup (4 per thread, kept in registers along the chain).
-constexpr int kCombineElems = 1024;
+// the one the scan adds for a carried (Bbar_prev, x_prev).  The state entering segment s,
+// g_end(s - 1) + c_{t0} Bbar_{t0-1}^T x_{t0-1}, replaces g_end(s - 1) in the workspace: pass 2
+// starts segment s from it.  Each thread carries row pairs (2k, 2k + 1) of one state column p,
+// kCombinePairs (row pair, column) items per workgroup (two per thread, in registers along the
+// chain).  Pair k's true start angles and the call's Bbar_last and phi_out come from the first
+// workgroup of each (b, h) at the end.
+constexpr int kCombinePairs = 512;
 constexpr int kCombineBlk = 8;   // segments whose inputs are read ahead of the chain
+// (x0, x1) turned by the angle with cosine cs and sine sn, as the staging rotates a row pair
+__device__ __forceinline__ void turn_pair(float cs, float sn, float& x0, float& x1) {
+    const float a = x0, b = x1;
+    x0 = fmaf(cs, a, sn * b);
+    x1 = fmaf(cs, b, -sn * a);
+}
 template <typename T, int R>
 __global__ __launch_bounds__(256) void segment_combine_kernel(PrefillArgs a) {
-    const int N = a.N, P = a.P, H = a.H;
-    const int64_t NP = (int64_t)N * P;
-    const int G = (int)((NP + kCombineElems - 1) / kCombineElems);
+    const int N = a.N, P = a.P, H = a.H, K = N / 2, nseg = a.nseg;
+    const int64_t NP = (int64_t)N * P, KP = (int64_t)K * P;
+    const int G = (int)((KP + kCombinePairs - 1) / kCombinePairs);
     const int64_t bh = blockIdx.x / G, b = bh / H;
     const int h = (int)(bh % H), part = (int)(blockIdx.x % G);
-    float gp[4];
-    int64_t el[4];
+    const bool fused = a.ws_phiend != nullptr;
+    const T* bb = (const T*)a.ws_bbar + bh * nseg * (int64_t)(R * N);
+    const float* phe = fused ? a.ws_phiend + bh * nseg * (int64_t)K : nullptr;
+    const float* gst = a.ws_state + bh * nseg * NP;
+    bool on[2];
+    int kk[2], pp[2];
+    float g0[2], g1[2];
+    float ph[2], php[2];   // fused: start angles of the block's first segment and of the one before
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        el[j] = (int64_t)part * kCombineElems + threadIdx.x + 256 * j;
-        gp[j] = el[j] < NP ? a.ws_state[bh * a.nseg * NP + el[j]] : 0.f;   // segment 0: already true
+    for (int j = 0; j < 2; ++j) {
+        const int64_t e = (int64_t)part * kCombinePairs + threadIdx.x + 256 * j;
+        on[j] = e < KP;
+        kk[j] = on[j] ? (int)(e / P) : 0;
+        pp[j] = on[j] ? (int)(e % P) : 0;
+        g0[j] = on[j] ? gst[(2 * kk[j]) * P + pp[j]] : 0.f;   // segment 0: already true
+        g1[j] = on[j] ? gst[(2 * kk[j] + 1) * P + pp[j]] : 0.f;
+        ph[j] = fused ? phe[kk[j]] : 0.f;                        // segment 1 starts where 0 ended
+        php[j] = 0.f;                                            // (segment 0's Bbar row is true)
     }
-    // Segments in blocks of kCombineBlk: every input of a block (decays, c0, the carried-in
-    // outer products u, the segments' own end states) is read before any result is written back,
-    // since a load that follows a store to the workspace waits for it; only the chain through gp
-    // is sequential.
-    const int last = a.nseg;   // segments chained: 1 .. last - 1
-    for (int s0 = 1; s0 < last; s0 += kCombineBlk) {
-        float decay[kCombineBlk], c0[kCombineBlk], u[kCombineBlk][4], own[kCombineBlk][4];
+    // Segments in blocks of kCombineBlk: every input of a block (decays, c0, angle sums, the
+    // carried-in outer products u, the segments' own end states) is read before any result is
+    // written back, since a load that follows a store to the workspace waits for it; only the
+    // chain through g is sequential.
+    for (int s0 = 1; s0 < nseg; s0 += kCombineBlk) {
+        float decay[kCombineBlk], c0[kCombineBlk], ua[kCombineBlk][2], ub[kCombineBlk][2];
+        float oa[kCombineBlk][2], ob[kCombineBlk][2], ang[kCombineBlk + 1][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) ang[0][j] = ph[j];
 #pragma unroll
         for (int i = 0; i < kCombineBlk; ++i) {
-            const int s = s0 + i < last ? s0 + i : s0;   // past the last one: unused
-            decay[i] = exp2f(a.ws_l2[bh * a.nseg + s]);
+            const int s = s0 + i < nseg ? s0 + i : s0;   // past the last one: unused
+            decay[i] = exp2f(a.ws_l2[bh * nseg + s]);
             const int64_t row0 = (b * a.L + s * a.seglen) * H + h;   // step t0 of this head
             c0[i] = (1.0f - load_f32((const T*)a.lam + row0)) * load_f32((const T*)a.dt + row0);
-            const T* Bp = (const T*)a.ws_bbar + (bh * a.nseg + s - 1) * (int64_t)(R * N);
+            const T* Bp = bb + (s - 1) * (int64_t)(R * N);
             const T* xp = (const T*)a.x + (row0 - H) * R * P;
-            const float* gs = a.ws_state + (bh * a.nseg + s) * NP;
+            const float* gs = gst + s * NP;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                u[i][j] = 0.f;
-                own[i][j] = 0.f;
-                if (el[j] >= NP) continue;
-                const int n = (int)(el[j] / P), p = (int)(el[j] % P);
+            for (int j = 0; j < 2; ++j) {
+                // the next segment's start angle: this one's plus its own sum from zero
+                ang[i + 1][j] = fused ? wrap_angle(ang[i][j] + phe[s * K + kk[j]]) : 0.f;
+                float u0 = 0.f, u1 = 0.f;
 #pragma unroll
-                for (int r = 0; r < R; ++r) u[i][j] = fmaf(load_f32(Bp + r * N + n), load_f32(xp + r * P + p), u[i][j]);
-                own[i][j] = gs[el[j]];
+                for (int r = 0; r < R; ++r) {
+                    const float xv = load_f32(xp + r * P + pp[j]);
+                    u0 = fmaf(load_f32(Bp + r * N + 2 * kk[j]), xv, u0);
+                    u1 = fmaf(load_f32(Bp + r * N + 2 * kk[j] + 1), xv, u1);
+                }
+                float v0 = gs[(2 * kk[j]) * P + pp[j]], v1 = gs[(2 * kk[j] + 1) * P + pp[j]];
+                if (fused) {
+                    float sn, cs;
+                    // the previous segment's Bbar row ran from its start angle's zero (the sum over
+                    // ranks commutes with the pair's rotation; segment 0's row is already true)
+                    if (s > 1) {
+                        __sincosf(i == 0 ? php[j] : ang[i - 1][j], &sn, &cs);
+                        turn_pair(cs, sn, u0, u1);
+                    }
+                    __sincosf(ang[i][j], &sn, &cs);
+                    turn_pair(cs, sn, v0, v1);
+                }
+                ua[i][j] = u0;
+                ub[i][j] = u1;
+                oa[i][j] = v0;
+                ob[i][j] = v1;
             }
         }
 #pragma unroll
         for (int i = 0; i < kCombineBlk; ++i) {
             const int s = s0 + i;
-            if (s >= last) break;
-            float* gs = s + 1 < a.nseg ? a.ws_state + (bh * a.nseg + s) * NP : a.h_out + bh * NP;
+            if (s >= nseg) break;
+            float* gin = a.ws_state + (bh * nseg + s - 1) * NP;   // read in an earlier block
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (el[j] >= NP) continue;
-                gp[j] = fmaf(decay[i], fmaf(c0[i], u[i][j], gp[j]), own[i][j]);
-                gs[el[j]] = gp[j];
+            for (int j = 0; j < 2; ++j) {
+                if (!on[j]) continue;
+                const float c0a = fmaf(c0[i], ua[i][j], g0[j]), c0b = fmaf(c0[i], ub[i][j], g1[j]);
+                gin[(2 * kk[j]) * P + pp[j]] = c0a;
+                gin[(2 * kk[j] + 1) * P + pp[j]] = c0b;
+                g0[j] = fmaf(decay[i], c0a, oa[i][j]);
+                g1[j] = fmaf(decay[i], c0b, ob[i][j]);
+                if (s + 1 == nseg) {
+                    a.h_out[bh * NP + (2 * kk[j]) * P + pp[j]] = g0[j];
+                    a.h_out[bh * NP + (2 * kk[j] + 1) * P + pp[j]] = g1[j];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            php[j] = ang[kCombineBlk - 1][j];
+            ph[j] = ang[kCombineBlk][j];
+        }
+    }
+    // The first workgroup of the (b, h), one thread per row pair k: the true start angles of
+    // segments 1 .. nseg-1 (pass 2 reads them), the call's phi_out and its Bbar_last (the last
+    // segment's row turned by that segment's start angle: its second rounding to the io type).
+    if (part != 0) return;
+    for (int k = threadIdx.x; k < K; k += blockDim.x) {
+        float sn = 0.f, cs = 1.f;
+        if (fused) {
+            float phs = phe[k];   // start angle of segment 1
+            for (int s = 1; s < nseg; ++s) {
+                a.seg_phi[(bh * nseg + s) * K + k] = phs;
+                if (s + 1 < nseg) phs = wrap_angle(phs + phe[s * K + k]);
+            }
+            __sincosf(phs, &sn, &cs);
+            if (a.phi_out) a.phi_out[bh * K + k] = wrap_angle(phs + phe[(nseg - 1) * K + k]);
+        }
+        if (a.Bbar_last) {
+            const T* src = bb + (nseg - 1) * (int64_t)(R * N);
+            T* dst = (T*)a.Bbar_last + bh * (int64_t)(R * N);
+            for (int r = 0; r < R; ++r) {
+                float v0 = load_f32(src + r * N + 2 * k), v1 = load_f32(src + r * N + 2 * k + 1);
+                turn_pair(cs, sn, v0, v1);
+                dst[r * N + 2 * k] = from_f32<T>(v0);
+                dst[r * N + 2 * k + 1] = from_f32<T>(v1);
             }
         }
     }
@@ -929,7 +1014,7 @@ hipError_t launch_combine_t(const PrefillArgs& a, dim3 grid, hipStream_t s) {
 }
 
 hipError_t launch_segment_combine(const PrefillArgs& a, bool bf16_io, hipStream_t s) {
-    const int64_t G = ((int64_t)a.N * a.P + kCombineElems - 1) / kCombineElems;
+    const int64_t G = ((int64_t)(a.N / 2) * a.P + kCombinePairs - 1) / kCombinePairs;
     const dim3 grid((unsigned)(a.b * a.H * G));
     return bf16_io ? launch_combine_t<bf16>(a, grid, s) : launch_combine_t<float>(a, grid, s);
 }

@@ -133,7 +133,7 @@ def test_split_rerun_lengths():
     r = lambda n: (n + 255) // 256 * 256
     off_fix = r(H * nseg * N * P * 4) + r(H * nseg * R * N * 2) + r(H * nseg * 4)
     need = m3scan.layer_prefill_workspace_bytes(_dims(w, Q))
-    assert need == off_fix + r(H * nseg * 4) + r(H * nseg * 4 * (N // 2) * 4) + r(H * (N // 2) * 4), \
+    assert need == off_fix + r(H * nseg * 4) + 2 * r(H * nseg * (N // 2) * 4), \
         "the split plan differs from the one this test assumes"
     d = to_dev(inp, DEV)
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
