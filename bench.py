@@ -705,7 +705,9 @@ def main():
             "two_calls": {"ms": ms_s4, "tokens/s": toks4 / (ms_s4 / 1e3), "bcnorm_rope_ms": ms_b4,
                           "chunk": wl4.chunk},
             "m3_prefill": {"ms": ms_p4, "GB/s": pb4 / ms_p4 / 1e6, "hbm_frac": pb4 / ms_p4 / 1e6 / HBM_PEAK_GBS},
-            "how": "sequence split into segments run in parallel (64 (b, h) pairs)"}
+            "how": "sequence split into segments run in parallel (64 (b, h) pairs): every segment once, "
+                   "the end states (and, fused, angles) chained, then each later segment's first steps "
+                   "again from its true carry"}
         del inp4
         torch.cuda.empty_cache()
     # the step is one kernel: the fused layer kernel
