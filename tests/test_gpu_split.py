@@ -30,6 +30,7 @@ SPLIT_CASES = [
     ("bf16", 3, 2100, 1, 64, 128, 1, 16, 16, False, True),   # b = 3, chunk 16 in both calls
     ("bf16", 1, 12288, 1, 64, 128, 1, 32, 64, False, True),  # 12 segments: the chaining runs
                                                               # two blocks of segments
+    ("bf16", 1, 3000, 2, 64, 64, 8, 4, 8, True, True),       # R = 8: 4- and 8-step chunks
 ]
 
 
