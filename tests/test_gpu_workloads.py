@@ -103,6 +103,28 @@ def test_prefill_workload_sampled(name, pairs, fused):
         assert angle_err(phi[bi:bi + 1, hi:hi + 1], ref["phi_out"]) <= 1e-3
 
 
+
+@pytest.mark.parametrize("name,pairs", [
+    ("siso_b8_l2048", [(0, 3), (4, 27), (6, 58)]),
+    ("mimo4_b8_l2048", [(1, 12), (5, 49), (7, 33)]),
+    ("long_mimo4_b1_l16384", [(0, 17)]),
+])
+def test_two_calls_bench_chunk_sampled(name, pairs):
+    """m3_bcnorm_rope + m3_prefill on chunks of 32 rows (chunk * R = 32), the launch configuration
+    bench.py times for the two-call path (the long-context workload: its sequence split)."""
+    w = inputs.WORKLOADS[name]
+    wc = w.with_(chunk=32 // w.rank)
+    print("workload", name, "two calls, chunk", wc.chunk, flush=True)
+    inp = inputs.make_prefill_inputs(w, seed=2, device=DEV, carry=True)
+    _, _, y, h, phi = _layer(inp, wc)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all() and torch.isfinite(h).all()
+    for bi, hi in pairs:
+        ref = oracle.layer(_slice_pair(inp, bi, hi), bcnorm=w.bcnorm, mix=w.mix)
+        assert rel_err(y[bi:bi + 1, :, hi:hi + 1], ref["y"]) <= TOL[w.io], (bi, hi)
+        assert rel_err(h[bi:bi + 1, hi:hi + 1], ref["h_out"]) <= TOL[w.io], (bi, hi)
+        assert angle_err(phi[bi:bi + 1, hi:hi + 1], ref["phi_out"]) <= 1e-3
+
 def _decode_steps(w, dinp, steps, mix, h, phi, Bprev, xprev, consts_dev, toks, fused=False):
     """`steps` tokens, each m3_bcnorm_rope (L = 1) + m3_decode_step, or with `fused` one
     m3_layer_decode_step; the rotated-B buffers are swapped between steps."""
